@@ -1,0 +1,166 @@
+"""CPU oracle for dynamic block-sparse video attention -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP library
+and never imports it.
+
+The arithmetic lives in ``oracle.c`` (plain fp64 loops, OpenMP over rows);
+this module only marshals NumPy arrays.  What each step computes, and the
+readings taken where the NABLA summary page ("NABLA: Neighborhood Adaptive
+Block-Level Attention", section "Methodologie : NABLA") is silent, are stated
+in ``oracle.c``.
+
+Pinned by ``tests/test_oracle_pins.py`` (closed forms, brute force on tiny
+grids, invariants, a hand-derived golden case); no function here is
+unpinned.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+TOKENS_PER_BLOCK = 64
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (fp64, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+                               _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I = ctypes.c_int64
+        D = ctypes.c_double
+        lib.oracle_pool.argtypes = [P, I, I, I, P]
+        lib.oracle_select_rows.argtypes = [P, P, I, I, I, P, I, D, P, I, I, I, I, I, I, P, P, P]
+        lib.oracle_attention_rows.argtypes = [P, P, P, I, I, I, P, P, P, I, D, P, P, P]
+        for f in (lib.oracle_pool, lib.oracle_select_rows, lib.oracle_attention_rows):
+            f.restype = None
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32(x) -> np.ndarray:
+    """Exact float32 copy of a tensor/array (bf16 and f32 widen exactly)."""
+    if hasattr(x, "detach"):
+        import torch
+        x = x.detach().to("cpu", torch.float32).numpy()
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / float(np.sqrt(head_dim))
+
+
+def pool(x, tpb: int = TOKENS_PER_BLOCK) -> np.ndarray:
+    """Block means: x [..., N, d] -> [..., N/tpb, d] in fp64."""
+    x = _f32(x)
+    *lead, n, d = x.shape
+    if n % tpb:
+        raise ValueError("token count must be a whole number of blocks")
+    nblk = int(np.prod(lead, dtype=np.int64)) * (n // tpb)
+    out = np.empty((nblk, d), dtype=np.float64)
+    _load().oracle_pool(_ptr(x), nblk, tpb, d, _ptr(out))
+    return out.reshape(*lead, n // tpb, d)
+
+
+def select_rows(qbar: np.ndarray, kbar: np.ndarray, heads: int, block_grid: Sequence[int],
+                thresholds, window=(-1, -1, -1), scale: Optional[float] = None,
+                rows: Optional[np.ndarray] = None, stats: bool = False):
+    """Reduced map, CDF cut and window for the listed rows.
+
+    qbar, kbar: pooled [B, H, nB, d] (fp64).  thresholds: scalar or [H].
+    Returns ``keep`` [nrows, nB] uint8 (bit 0: CDF rule, bit 1: window) and,
+    with ``stats``, the probabilities ``p`` and the exclusive CDF mass ``E``.
+    """
+    qbar = np.ascontiguousarray(qbar, dtype=np.float64)
+    kbar = np.ascontiguousarray(kbar, dtype=np.float64)
+    *lead, nB, d = qbar.shape
+    bh = int(np.prod(lead, dtype=np.int64))
+    nT, nTy, nTx = (int(g) for g in block_grid)
+    if nT * nTy * nTx != nB:
+        raise ValueError("block grid does not match the number of blocks")
+    thr = np.broadcast_to(np.asarray(thresholds, dtype=np.float64), (heads,)).copy()
+    if not np.all(thr > 0):
+        raise ValueError("thresholds must be > 0")
+    if rows is None:
+        rows = np.arange(bh * nB, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    keep = np.zeros((len(rows), nB), dtype=np.uint8)
+    p = np.empty((len(rows), nB), dtype=np.float64) if stats else None
+    E = np.empty((len(rows), nB), dtype=np.float64) if stats else None
+    sc = default_scale(d) if scale is None else float(scale)
+    wt, wh, ww = (int(w) for w in window)
+    _load().oracle_select_rows(_ptr(qbar), _ptr(kbar), heads, nB, d, _ptr(rows), len(rows), sc,
+                               _ptr(thr), nT, nTy, nTx, wt, wh, ww, _ptr(keep), _ptr(p), _ptr(E))
+    if stats:
+        return keep, p, E
+    return keep
+
+
+def csr_from_mask(mask: np.ndarray):
+    """Dense boolean block mask [rows, nB] -> (row_ptr int64 [rows+1], col_idx int32), ascending columns."""
+    mask = np.asarray(mask).astype(bool)
+    counts = mask.sum(axis=1)
+    row_ptr = np.zeros(mask.shape[0] + 1, dtype=np.int64)
+    np.cumsum(counts, out=row_ptr[1:])
+    col_idx = np.nonzero(mask)[1].astype(np.int32)
+    return row_ptr, col_idx
+
+
+def select(q, k, heads: int, block_grid, thresholds, window=(-1, -1, -1), scale=None):
+    """Full selection for every row: returns (mask bool [B*H*nB, nB], row_ptr, col_idx)."""
+    qbar = pool(q)
+    kbar = pool(k)
+    keep = select_rows(qbar, kbar, heads, block_grid, thresholds, window, scale)
+    mask = keep != 0
+    row_ptr, col_idx = csr_from_mask(mask)
+    return mask, row_ptr, col_idx
+
+
+def attention_rows(q, k, v, row_ptr, col_idx, rows, scale: Optional[float] = None,
+                   tpb: int = TOKENS_PER_BLOCK, weights: bool = False):
+    """Exact attention of every token of the listed query-block rows over its kept tiles.
+
+    q, k, v: [B, H, N, d]; row_ptr/col_idx: CSR over rows r = bh * nB + i.
+    Returns out [nrows, tpb, d] fp64 and lse [nrows, tpb] (natural log), plus
+    the per-token weight sums with ``weights``.
+    """
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    *lead, n, d = q.shape
+    nB = n // tpb
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    rp = np.ascontiguousarray(row_ptr, dtype=np.int64)
+    ci = np.ascontiguousarray(col_idx, dtype=np.int32)
+    out = np.empty((len(rows), tpb, d), dtype=np.float64)
+    lse = np.empty((len(rows), tpb), dtype=np.float64)
+    ws = np.empty((len(rows), tpb), dtype=np.float64) if weights else None
+    sc = default_scale(d) if scale is None else float(scale)
+    _load().oracle_attention_rows(_ptr(q), _ptr(k), _ptr(v), nB, tpb, d, _ptr(rp), _ptr(ci),
+                                  _ptr(rows), len(rows), sc, _ptr(out), _ptr(lse), _ptr(ws))
+    if weights:
+        return out, lse, ws
+    return out, lse

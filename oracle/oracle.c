@@ -1,0 +1,217 @@
+/*
+ * CPU oracle for dynamic block-sparse video attention -- TEST INFRASTRUCTURE.
+ *
+ * Plain, slow, obviously correct fp64 loops.  Only the test-suite, the smoke
+ * check and the benchmark's CPU-baseline leg use this file; the product path
+ * never links or calls it, and it shares no code with the HIP library.
+ *
+ * What it computes follows the NABLA summary page ("NABLA: Neighborhood
+ * Adaptive Block-Level Attention", section "Methodologie : NABLA"):
+ *   - Sous-echantillonnage: Q and K are mean-pooled per block of tokens;
+ *   - Attention Reduite: a full attention map (softmax over every key block)
+ *     is computed on the pooled vectors;
+ *   - Seuil CDF: per row of that map, blocks are kept by the cumulative
+ *     distribution against the threshold thr;
+ *   - Expansion: the block mask says which 64x64 token tiles are computed;
+ *   - Integration Hybride avec STA: the final mask is the union of the
+ *     content mask and a static sliding-tile window (M = M_nabla OR M_STA);
+ * followed by exact softmax attention of every query token over the tokens of
+ * its kept key blocks.
+ *
+ * Readings taken where the page is silent (each restated in the design notes):
+ *   - pooled scores use the same scale as the attention, 1/sqrt(d) by default;
+ *   - the softmax of the reduced map runs over all key blocks, no causal mask;
+ *   - CDF rule: blocks are ordered by probability descending, ties broken by
+ *     the lower block index; with E(j) the mass of the blocks strictly before
+ *     j, block j is kept iff E(j) < thr.  This is the page's "cumulative
+ *     probability above 1 - thr" counted from the small end, and it keeps the
+ *     block that makes the mass reach thr;
+ *   - thr >= 1 keeps every block (the literal rule could drop blocks whose
+ *     probability underflows, which would not be dense attention);
+ *   - the window is a box of radius (wt, wh, ww) in block coordinates,
+ *     clipped at the grid edges, without wrap or shift;
+ *   - a query row with no kept block gives O = 0 and LSE = -inf.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC oracle.c -o liboracle.so -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Sous-echantillonnage: xbar[b][c] = (1/tpb) * sum over the tpb tokens of block b of x[token][c]. */
+void oracle_pool(const float *x, int64_t nblocks, int64_t tpb, int64_t d, double *xbar)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nblocks; ++b) {
+        for (int64_t c = 0; c < d; ++c) {
+            double s = 0.0;
+            for (int64_t t = 0; t < tpb; ++t)
+                s += (double)x[(b * tpb + t) * d + c];
+            xbar[b * d + c] = s / (double)tpb;
+        }
+    }
+}
+
+typedef struct {
+    double p;
+    int64_t j;
+} prob_idx;
+
+/* Order for the CDF: larger probability first, then lower block index. */
+static int by_prob_desc(const void *a, const void *b)
+{
+    const prob_idx *x = (const prob_idx *)a, *y = (const prob_idx *)b;
+    if (x->p > y->p) return -1;
+    if (x->p < y->p) return 1;
+    return (x->j < y->j) ? -1 : (x->j > y->j);
+}
+
+/*
+ * Attention Reduite + Seuil CDF + union with the window, for a list of rows.
+ *
+ * qbar, kbar: pooled vectors [BH][nB][d] (fp64).  A row index r = bh * nB + i
+ * names query block i of batch-head bh; its head is bh % H.
+ * keep[k][j] (k-th listed row) receives bit 0 when the CDF rule keeps j and
+ * bit 1 when the window contains j.  p_out / E_out (optional, [nrows][nB])
+ * receive the row's probabilities and the exclusive mass E(j) in CDF order.
+ */
+void oracle_select_rows(const double *qbar, const double *kbar, int64_t H, int64_t nB, int64_t d,
+                        const int64_t *rows, int64_t nrows, double scale, const double *thr_head,
+                        int64_t nT, int64_t nTy, int64_t nTx, int64_t wt, int64_t wh, int64_t ww,
+                        uint8_t *keep, double *p_out, double *E_out)
+{
+    (void)nT;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)nB);
+        prob_idx *ord = (prob_idx *)malloc(sizeof(prob_idx) * (size_t)nB);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t k = 0; k < nrows; ++k) {
+            const int64_t r = rows[k];
+            const int64_t bh = r / nB, i = r % nB;
+            const double thr = thr_head[bh % H];
+            const double *qi = qbar + (bh * nB + i) * d;
+            uint8_t *kr = keep + k * nB;
+
+            /* reduced attention map row: scaled dot products, then a softmax over all key blocks */
+            double mx = -INFINITY;
+            for (int64_t j = 0; j < nB; ++j) {
+                const double *kj = kbar + (bh * nB + j) * d;
+                double acc = 0.0;
+                for (int64_t c = 0; c < d; ++c) acc += qi[c] * kj[c];
+                s[j] = acc * scale;
+                if (s[j] > mx) mx = s[j];
+            }
+            double z = 0.0;
+            for (int64_t j = 0; j < nB; ++j) {
+                s[j] = exp(s[j] - mx);
+                z += s[j];
+            }
+            for (int64_t j = 0; j < nB; ++j) s[j] /= z;
+
+            /* CDF: walk the blocks from the most probable; keep while the mass before is below thr */
+            for (int64_t j = 0; j < nB; ++j) {
+                ord[j].p = s[j];
+                ord[j].j = j;
+            }
+            qsort(ord, (size_t)nB, sizeof(prob_idx), by_prob_desc);
+            double before = 0.0;
+            for (int64_t n = 0; n < nB; ++n) {
+                const int64_t j = ord[n].j;
+                kr[j] = (thr >= 1.0 || before < thr) ? 1 : 0;
+                if (E_out) E_out[k * nB + j] = before;
+                before += ord[n].p;
+            }
+            if (p_out)
+                for (int64_t j = 0; j < nB; ++j) p_out[k * nB + j] = s[j];
+
+            /* static window around the query block, in block coordinates (t, y, x) */
+            if (wt >= 0 && wh >= 0 && ww >= 0) {
+                const int64_t ti = i / (nTy * nTx), yi = (i / nTx) % nTy, xi = i % nTx;
+                for (int64_t j = 0; j < nB; ++j) {
+                    const int64_t tj = j / (nTy * nTx), yj = (j / nTx) % nTy, xj = j % nTx;
+                    if (llabs(tj - ti) <= wt && llabs(yj - yi) <= wh && llabs(xj - xi) <= ww)
+                        kr[j] |= 2;
+                }
+            }
+        }
+        free(s);
+        free(ord);
+    }
+}
+
+/*
+ * Exact attention over the kept tiles (Expansion): for every token n of query
+ * block i, softmax over all tokens of the key blocks listed in the CSR row of
+ * (bh, i), then the weighted sum of V.
+ *
+ * q, k, v: [BH][nB*tpb][d] float32 (the exact values the GPU sees).
+ * row_ptr/col_idx: CSR over rows r = bh * nB + i.  For each listed row, out
+ * receives [tpb][d] fp64 and lse [tpb] the natural-log normaliser
+ * log(sum_m exp(scale * q_n . k_m)).  An empty row yields O = 0, LSE = -inf.
+ * w_sum (optional, [nrows][tpb]) receives the sum of the row's softmax weights.
+ */
+void oracle_attention_rows(const float *q, const float *k, const float *v, int64_t nB, int64_t tpb,
+                           int64_t d, const int64_t *row_ptr, const int32_t *col_idx,
+                           const int64_t *rows, int64_t nrows, double scale,
+                           double *out, double *lse, double *w_sum)
+{
+    const int64_t N = nB * tpb;
+#pragma omp parallel
+    {
+        double *logit = (double *)malloc(sizeof(double) * (size_t)N);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 1) collapse(2)
+        for (int64_t kr = 0; kr < nrows; ++kr) {
+            for (int64_t t = 0; t < tpb; ++t) {
+                const int64_t r = rows[kr];
+                const int64_t bh = r / nB, i = r % nB;
+                const float *qn = q + (bh * N + i * tpb + t) * d;
+                const int64_t beg = row_ptr[r], end = row_ptr[r + 1];
+                double *o = out + (kr * tpb + t) * d;
+                const int64_t m_count = (end - beg) * tpb;
+                if (m_count == 0) {
+                    for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+                    lse[kr * tpb + t] = -INFINITY;
+                    if (w_sum) w_sum[kr * tpb + t] = 0.0;
+                    continue;
+                }
+                double mx = -INFINITY;
+                int64_t m = 0;
+                for (int64_t e = beg; e < end; ++e) {
+                    const int64_t j = col_idx[e];
+                    for (int64_t u = 0; u < tpb; ++u, ++m) {
+                        const float *km = k + (bh * N + j * tpb + u) * d;
+                        double a = 0.0;
+                        for (int64_t c = 0; c < d; ++c) a += (double)qn[c] * (double)km[c];
+                        logit[m] = a * scale;
+                        if (logit[m] > mx) mx = logit[m];
+                    }
+                }
+                double z = 0.0;
+                for (int64_t mm = 0; mm < m_count; ++mm) {
+                    logit[mm] = exp(logit[mm] - mx);
+                    z += logit[mm];
+                }
+                for (int64_t c = 0; c < d; ++c) acc[c] = 0.0;
+                double wsum = 0.0;
+                m = 0;
+                for (int64_t e = beg; e < end; ++e) {
+                    const int64_t j = col_idx[e];
+                    for (int64_t u = 0; u < tpb; ++u, ++m) {
+                        const float *vm = v + (bh * N + j * tpb + u) * d;
+                        const double w = logit[m] / z;
+                        wsum += w;
+                        for (int64_t c = 0; c < d; ++c) acc[c] += w * (double)vm[c];
+                    }
+                }
+                for (int64_t c = 0; c < d; ++c) o[c] = acc[c];
+                lse[kr * tpb + t] = mx + log(z);
+                if (w_sum) w_sum[kr * tpb + t] = wsum;
+            }
+        }
+        free(logit);
+        free(acc);
+    }
+}

@@ -1,0 +1,341 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Closed forms, a hand-derived worked example, brute force on tiny grids and
+invariants, chosen so that a dropped term, a wrong sign, index or scale, or a
+transposed operand in ``oracle.c`` fails at least one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import brute
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "dyadic_cdf.txt")
+
+
+def _rand(shape, seed, scale=1.0):
+    return (np.random.default_rng(seed).standard_normal(shape) * scale).astype(np.float32)
+
+
+# ---------------------------------------------------------------- pooling
+
+def test_pool_constant_and_ramp():
+    # constant tokens pool to the constant; a ramp over the 64 tokens pools to its midpoint
+    x = np.zeros((2, 128, 4), np.float32)
+    x[:, :64, 0] = 3.25
+    x[:, 64:, 1] = np.arange(64, dtype=np.float32)
+    x[:, :, 2] = np.arange(128, dtype=np.float32)[None, :] * 0.5
+    xb = oracle.pool(x)
+    assert xb.shape == (2, 2, 4)
+    assert np.all(xb[:, 0, 0] == 3.25) and np.all(xb[:, 1, 0] == 0)
+    assert np.all(xb[:, 1, 1] == 31.5) and np.all(xb[:, 0, 1] == 0)
+    assert np.allclose(xb[:, 0, 2], 0.5 * 31.5) and np.allclose(xb[:, 1, 2], 0.5 * 95.5)
+
+
+def test_pool_matches_reshape_mean():
+    x = _rand((3, 5 * 64, 16), 1)
+    ref = x.astype(np.float64).reshape(3, 5, 64, 16).mean(axis=2)
+    assert np.allclose(oracle.pool(x), ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- CDF rule
+
+def _golden_cases():
+    cases = []
+    for line in open(GOLDEN):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        parts = line.split()
+        ns = [int(t) for t in parts[1:5]]
+        cases.append((parts[0], ns, float(parts[5]), [int(t) for t in parts[6].split(",")]))
+    return cases
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: f"{c[0]}-{c[2]}")
+def test_golden_dyadic(case):
+    _, ns, thr, kept = case
+    d = 64
+    q = np.zeros((1, 1, 4 * 64, d), np.float32)
+    k = np.zeros((1, 1, 4 * 64, d), np.float32)
+    q[..., 0] = 8.0
+    for j, n in enumerate(ns):
+        k[0, 0, 64 * j:64 * (j + 1), 0] = math.log(2.0) * n
+    keep, p, E = oracle.select_rows(oracle.pool(q), oracle.pool(k), 1, (1, 1, 4), thr, stats=True)
+    expect_p = np.array([2.0 ** n for n in ns]) / sum(2.0 ** n for n in ns)
+    assert np.allclose(p[0], expect_p, rtol=1e-6)
+    got = sorted(np.nonzero(keep[0] & 1)[0].tolist())
+    assert got == kept
+
+
+@pytest.mark.parametrize("nB,thr", [(16, 0.9), (16, 0.5), (7, 0.3), (480, 0.905), (3840, 0.7001), (5, 1.0), (33, 0.999)])
+def test_uniform_scores_keep_ceil(nB, thr):
+    # Q = 0 makes every reduced score 0, so p = 1/nB and E = k/nB in index order:
+    # the rule keeps the ceil(thr * nB) lowest indices.  Cases where thr * nB is a whole number
+    # but 1/nB is not dyadic are left out: there E == thr up to the last bit of the running sum.
+    d = 8
+    q = np.zeros((1, 1, nB * 64, d), np.float32)
+    k = _rand((1, 1, nB * 64, d), 2)
+    keep = oracle.select_rows(oracle.pool(q), oracle.pool(k), 1, (1, 1, nB), thr)
+    expect = min(nB, math.ceil(thr * nB - 1e-12))
+    if thr >= 1:
+        expect = nB
+    kept = np.nonzero(keep[0] & 1)[0]
+    assert len(kept) == expect
+    assert np.array_equal(kept, np.arange(expect))
+
+
+def test_one_hot_and_small_threshold():
+    # one key block far above the rest: p_max ~ 1 > thr, so only it is kept;
+    # a tiny threshold keeps only the argmax whatever the spread
+    nB, d = 12, 16
+    q = np.zeros((1, 1, nB * 64, d), np.float32)
+    q[..., 0] = 1.0
+    k = np.zeros((1, 1, nB * 64, d), np.float32)
+    k[0, 0, 5 * 64:6 * 64, 0] = 200.0
+    keep = oracle.select_rows(oracle.pool(q), oracle.pool(k), 1, (1, 1, nB), 0.9)
+    assert np.nonzero(keep[0])[0].tolist() == [5]
+    kr = _rand((1, 1, nB * 64, d), 3)
+    qr = _rand((1, 1, nB * 64, d), 4)
+    qb, kb = oracle.pool(qr), oracle.pool(kr)
+    keep, p, _ = oracle.select_rows(qb, kb, 1, (1, 1, nB), 1e-9, stats=True)
+    for r in range(nB):
+        assert np.nonzero(keep[r])[0].tolist() == [int(np.argmax(p[r]))]
+
+
+def test_two_block_sigmoid_closed_form():
+    # two key blocks with reduced scores c0, c1: p0 = 1 / (1 + exp(c1 - c0)); checks the 1/sqrt(d) scale
+    d = 16
+    q = np.zeros((1, 1, 128, d), np.float32)
+    k = np.zeros((1, 1, 128, d), np.float32)
+    q[..., 3] = 2.0
+    k[0, 0, :64, 3] = 1.5
+    k[0, 0, 64:, 3] = -0.5
+    _, p, _ = oracle.select_rows(oracle.pool(q), oracle.pool(k), 1, (1, 1, 2), 0.5, stats=True)
+    c0, c1 = 2.0 * 1.5 / 4.0, 2.0 * -0.5 / 4.0
+    assert abs(p[0, 0] - 1.0 / (1.0 + math.exp(c1 - c0))) < 1e-14
+    # an explicit scale overrides the default
+    _, p2, _ = oracle.select_rows(oracle.pool(q), oracle.pool(k), 1, (1, 1, 2), 0.5, scale=1.0, stats=True)
+    assert abs(p2[0, 0] - 1.0 / (1.0 + math.exp(-4.0))) < 1e-14
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_cdf_matches_pairwise_bruteforce(seed):
+    # random tiny heads; the sorted walk of the oracle must equal the sort-free O(n^2) definition,
+    # and its probabilities must equal a NumPy softmax of NumPy matmul scores of the pooled vectors
+    rng = np.random.default_rng(100 + seed)
+    H, nB, d = 3, int(rng.integers(2, 40)), 16
+    amp = float(rng.choice([0.3, 3.0, 30.0]))
+    q = _rand((1, H, nB * 64, d), seed, amp)
+    k = _rand((1, H, nB * 64, d), seed + 50, amp)
+    thr = rng.uniform(0.05, 0.99, size=H)
+    qb, kb = oracle.pool(q), oracle.pool(k)
+    keep, p, E = oracle.select_rows(qb, kb, H, (1, 1, nB), thr, stats=True)
+    for h in range(H):
+        s = (qb[0, h] @ kb[0, h].T) / math.sqrt(d)
+        ref_p = np.exp(s - s.max(axis=1, keepdims=True))
+        ref_p /= ref_p.sum(axis=1, keepdims=True)
+        assert np.allclose(p[h * nB:(h + 1) * nB], ref_p, rtol=1e-12, atol=1e-300)
+        for i in range(nB):
+            r = h * nB + i
+            assert np.array_equal(keep[r] & 1, brute.cdf_keep_pairwise(p[r], thr[h]).astype(np.uint8))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_kept_mass_and_minimality(seed):
+    H, nB, d = 2, 64, 32
+    q = _rand((1, H, nB * 64, d), 10 + seed, 2.0)
+    k = _rand((1, H, nB * 64, d), 20 + seed, 2.0)
+    thr = [0.3, 0.85]
+    keep, p, _ = oracle.select_rows(oracle.pool(q), oracle.pool(k), H, (1, 1, nB), thr, stats=True)
+    for r in range(H * nB):
+        t = thr[r // nB]
+        kp = p[r][(keep[r] & 1) != 0]
+        assert kp.sum() >= t - 1e-12                  # enough mass
+        assert kp.sum() - kp.min() < t + 1e-12        # dropping the smallest kept block falls short
+        # every dropped block is no more probable than every kept one
+        dp = p[r][(keep[r] & 1) == 0]
+        if dp.size:
+            assert dp.max() <= kp.min()
+
+
+def test_threshold_one_keeps_underflowed_blocks():
+    # thr >= 1 keeps everything, even blocks whose probability underflows to 0
+    nB, d = 6, 4
+    q = np.zeros((1, 1, nB * 64, d), np.float32)
+    q[..., 0] = 1.0
+    k = np.zeros((1, 1, nB * 64, d), np.float32)
+    k[0, 0, :64, 0] = 3000.0
+    keep, p, _ = oracle.select_rows(oracle.pool(q), oracle.pool(k), 1, (1, 1, nB), 1.0, stats=True)
+    assert np.all(p[0, 1:] == 0.0)
+    assert np.all(keep == 1)
+    keep2 = oracle.select_rows(oracle.pool(q), oracle.pool(k), 1, (1, 1, nB), 1.5)
+    assert np.all(keep2 == 1)
+
+
+def test_invalid_threshold_rejected():
+    qb = np.zeros((1, 1, 2, 4))
+    with pytest.raises(ValueError):
+        oracle.select_rows(qb, qb, 1, (1, 1, 2), 0.0)
+    with pytest.raises(ValueError):
+        oracle.select_rows(qb, qb, 1, (1, 1, 2), float("nan"))
+
+
+def test_key_block_permutation_permutes_mask():
+    # relabelling key blocks relabels the mask columns (random data: no exact ties)
+    H, nB, d = 1, 24, 16
+    q = _rand((1, H, nB * 64, d), 7, 3.0)
+    k = _rand((1, H, nB * 64, d), 8, 3.0)
+    perm = np.random.default_rng(9).permutation(nB)
+    kp = k.reshape(1, H, nB, 64, d)[:, :, perm].reshape(1, H, nB * 64, d)
+    qb = oracle.pool(q)
+    a = oracle.select_rows(qb, oracle.pool(k), H, (1, 1, nB), 0.6)
+    b = oracle.select_rows(qb, oracle.pool(kp), H, (1, 1, nB), 0.6)
+    assert np.array_equal(a[:, perm], b)
+
+
+# ---------------------------------------------------------------- window
+
+@pytest.mark.parametrize("grid,win", [((3, 4, 5), (1, 1, 1)), ((4, 6, 10), (1, 1, 1)), ((2, 3, 3), (0, 1, 2)),
+                                      ((5, 2, 7), (2, 0, 1))])
+def test_window_counts(grid, win):
+    nB = int(np.prod(grid))
+    d = 4
+    q = np.zeros((1, 1, nB * 64, d), np.float32)
+    k = np.zeros((1, 1, nB * 64, d), np.float32)
+    keep = oracle.select_rows(oracle.pool(q), oracle.pool(k), 1, grid, 1e-6, window=win)
+    nT, nTy, nTx = grid
+    for i in range(nB):
+        wmask = (keep[i] & 2) != 0
+        assert wmask.sum() == brute.window_count(i, grid, win)
+        assert wmask[i]
+        t, y, x = i // (nTy * nTx), (i // nTx) % nTy, i % nTx
+        for j in np.nonzero(wmask)[0]:
+            tj, yj, xj = j // (nTy * nTx), (j // nTx) % nTy, j % nTx
+            assert abs(tj - t) <= win[0] and abs(yj - y) <= win[1] and abs(xj - x) <= win[2]
+    if grid == (4, 6, 10) and win == (1, 1, 1):
+        interior = (1 * 6 + 2) * 10 + 3
+        assert (keep[interior] & 2).astype(bool).sum() == 27
+        assert (keep[0] & 2).astype(bool).sum() == 8
+
+
+# ---------------------------------------------------------------- attention
+
+def _full_csr(rows, nB):
+    return oracle.csr_from_mask(np.ones((rows, nB), bool))
+
+
+@pytest.mark.parametrize("d", [16, 64])
+def test_threshold_one_equals_dense_attention(d):
+    H, nB = 2, 5
+    q = _rand((1, H, nB * 64, d), 31, 1.5)
+    k = _rand((1, H, nB * 64, d), 32, 1.5)
+    v = _rand((1, H, nB * 64, d), 33)
+    mask, rp, ci = oracle.select(q, k, H, (1, 1, nB), 1.0)
+    assert mask.all()
+    out, lse = oracle.attention_rows(q, k, v, rp, ci, np.arange(H * nB))
+    sc = 1.0 / math.sqrt(d)
+    for h in range(H):
+        ref, ref_lse = brute.dense_attention(q[0, h], k[0, h], v[0, h], sc)
+        assert np.abs(out[h * nB:(h + 1) * nB].reshape(-1, d) - ref).max() < 1e-12
+        assert np.abs(lse[h * nB:(h + 1) * nB].reshape(-1) - ref_lse).max() < 1e-12
+        # and the library routine agrees (torch's fp64 scaled-dot-product attention)
+        t = torch.nn.functional.scaled_dot_product_attention(
+            *(torch.from_numpy(x[0, h].astype(np.float64))[None] for x in (q, k, v)))
+        assert np.abs(out[h * nB:(h + 1) * nB].reshape(-1, d) - t[0].numpy()).max() < 1e-12
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_tile_walk_matches_token_mask_bruteforce(seed):
+    rng = np.random.default_rng(seed)
+    H, nB, d = 2, 6, 32
+    q = _rand((1, H, nB * 64, d), 40 + seed, 2.0)
+    k = _rand((1, H, nB * 64, d), 50 + seed, 2.0)
+    v = _rand((1, H, nB * 64, d), 60 + seed)
+    mask = rng.random((H * nB, nB)) < 0.45
+    mask[3] = False                                   # one empty row
+    rp, ci = oracle.csr_from_mask(mask)
+    out, lse, ws = oracle.attention_rows(q, k, v, rp, ci, np.arange(H * nB), weights=True)
+    sc = 1.0 / math.sqrt(d)
+    for h in range(H):
+        ref, ref_lse = brute.token_mask_attention(q[0, h], k[0, h], v[0, h], mask[h * nB:(h + 1) * nB], sc)
+        got = out[h * nB:(h + 1) * nB].reshape(-1, d)
+        assert np.abs(got - ref).max() < 1e-12
+        gl = lse[h * nB:(h + 1) * nB].reshape(-1)
+        assert np.array_equal(np.isinf(gl), np.isinf(ref_lse))
+        fin = np.isfinite(ref_lse)
+        assert np.abs(gl[fin] - ref_lse[fin]).max() < 1e-12
+    nonempty = mask.any(axis=1)
+    assert np.abs(ws[nonempty] - 1.0).max() < 1e-12        # each row's weights sum to 1
+    assert np.all(out[3] == 0) and np.all(np.isneginf(lse[3]))
+
+
+def test_constant_values_give_constant_output_and_order_invariance():
+    H, nB, d = 1, 8, 16
+    q = _rand((1, H, nB * 64, d), 70, 3.0)
+    k = _rand((1, H, nB * 64, d), 71, 3.0)
+    v = np.broadcast_to(np.linspace(-2, 2, d, dtype=np.float32), (1, H, nB * 64, d)).copy()
+    mask = np.random.default_rng(72).random((nB, nB)) < 0.5
+    mask[:, 0] = True
+    rp, ci = oracle.csr_from_mask(mask)
+    out, _ = oracle.attention_rows(q, k, v, rp, ci, np.arange(nB))
+    assert np.abs(out - v[0, 0, 0]).max() < 1e-12
+    # the order in which a row's tiles are walked does not change the result
+    v2 = _rand((1, H, nB * 64, d), 73)
+    a, la = oracle.attention_rows(q, k, v2, rp, ci, np.arange(nB))
+    ci_rev = ci.copy()
+    for r in range(nB):
+        ci_rev[rp[r]:rp[r + 1]] = ci[rp[r]:rp[r + 1]][::-1]
+    b, lb = oracle.attention_rows(q, k, v2, rp, ci_rev, np.arange(nB))
+    assert np.abs(a - b).max() < 1e-12 and np.abs(la - lb).max() < 1e-12
+
+
+def test_linearity_in_values():
+    H, nB, d = 1, 4, 16
+    q = _rand((1, H, nB * 64, d), 80, 2.0)
+    k = _rand((1, H, nB * 64, d), 81, 2.0)
+    v1 = _rand((1, H, nB * 64, d), 82)
+    v2 = _rand((1, H, nB * 64, d), 83)
+    rp, ci = _full_csr(nB, nB)
+    rows = np.arange(nB)
+    o1, _ = oracle.attention_rows(q, k, v1, rp, ci, rows)
+    o2, _ = oracle.attention_rows(q, k, v2, rp, ci, rows)
+    o3, _ = oracle.attention_rows(q, k, (2 * v1 - 3 * v2).astype(np.float32), rp, ci, rows)
+    assert np.abs(o3 - (2 * o1 - 3 * o2)).max() < 1e-5   # fp32 rounding of 2 v1 - 3 v2
+
+
+def test_single_block_grid_is_dense():
+    d = 32
+    q = _rand((1, 1, 64, d), 90, 2.0)
+    k = _rand((1, 1, 64, d), 91, 2.0)
+    v = _rand((1, 1, 64, d), 92)
+    mask, rp, ci = oracle.select(q, k, 1, (1, 1, 1), 0.01)
+    assert mask.all()
+    out, _ = oracle.attention_rows(q, k, v, rp, ci, [0])
+    ref, _ = brute.dense_attention(q[0, 0], k[0, 0], v[0, 0], 1 / math.sqrt(d))
+    assert np.abs(out[0] - ref).max() < 1e-12
+
+
+def test_batch_and_head_indexing():
+    # two batches x two heads with different data: each (b, h) must use its own slice
+    B, H, nB, d = 2, 2, 3, 16
+    q = _rand((B, H, nB * 64, d), 95, 2.0)
+    k = _rand((B, H, nB * 64, d), 96, 2.0)
+    v = _rand((B, H, nB * 64, d), 97)
+    thr = [0.5, 0.95]
+    mask, rp, ci = oracle.select(q, k, H, (1, 1, nB), thr)
+    out, _ = oracle.attention_rows(q, k, v, rp, ci, np.arange(B * H * nB))
+    for b in range(B):
+        for h in range(H):
+            bh = b * H + h
+            m1, rp1, ci1 = oracle.select(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], 1, (1, 1, nB), thr[h])
+            assert np.array_equal(mask[bh * nB:(bh + 1) * nB], m1)
+            o1, _ = oracle.attention_rows(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                                          rp1, ci1, np.arange(nB))
+            assert np.array_equal(out[bh * nB:(bh + 1) * nB], o1)
