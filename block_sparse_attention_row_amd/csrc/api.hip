@@ -1,0 +1,240 @@
+// C-ABI entry points of libsparse_attn: argument checks, workspace layout and
+// kernel launches on the caller's stream.  Every check runs on the host
+// before any HIP call, so a rejected call touches neither the device nor the
+// outputs.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sparse_attn.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+using namespace sattn;
+
+constexpr int64_t kAlign = 256;
+constexpr int kSelectMaxLds = 65536;
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+struct Dims {
+    int64_t B, H, D, N, nB, nBp, nW, rows;
+    int32_t nT, nTy, nTx;
+};
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Validates the shape and derives the sizes; returns a status.
+int32_t check_shape(const sparse_attn_shape *s, Dims *d) {
+    if (!s) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (s->batch < 1 || s->heads < 1 || s->grid_t < 1 || s->grid_h < 1 || s->grid_w < 1 || s->tile_t < 1 ||
+        s->tile_h < 1 || s->tile_w < 1)
+        return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (s->dtype != SPARSE_ATTN_F32 && s->dtype != SPARSE_ATTN_BF16) return SPARSE_ATTN_UNSUPPORTED;
+    if (s->head_dim != 64 && s->head_dim != 128) return SPARSE_ATTN_UNSUPPORTED;
+    if ((int64_t)s->tile_t * s->tile_h * s->tile_w != 64) return SPARSE_ATTN_UNSUPPORTED;
+    if (s->grid_t % s->tile_t || s->grid_h % s->tile_h || s->grid_w % s->tile_w) return SPARSE_ATTN_UNSUPPORTED;
+    if (!isfinite(s->scale)) return SPARSE_ATTN_INVALID_ARGUMENT;
+    d->B = s->batch;
+    d->H = s->heads;
+    d->D = s->head_dim;
+    d->nT = s->grid_t / s->tile_t;
+    d->nTy = s->grid_h / s->tile_h;
+    d->nTx = s->grid_w / s->tile_w;
+    d->N = (int64_t)s->grid_t * s->grid_h * s->grid_w;
+    d->nB = (int64_t)d->nT * d->nTy * d->nTx;
+    d->nBp = align_up(d->nB, 64);
+    d->nW = d->nBp / 64;
+    d->rows = d->B * d->H * d->nB;
+    // row_ptr / col_idx are int32: the worst-case nnz must fit.
+    if (d->rows > INT32_MAX / d->nB) return SPARSE_ATTN_UNSUPPORTED;
+    return SPARSE_ATTN_OK;
+}
+
+float effective_scale(const sparse_attn_shape *s) {
+    return s->scale != 0.f ? s->scale : (float)(1.0 / sqrt((double)s->head_dim));
+}
+
+struct Layout {
+    int64_t thr, qbar, kbar, bits, counts, total;
+};
+
+Layout layout(const Dims &d) {
+    Layout l;
+    int64_t off = 0;
+    l.thr = off;
+    off = align_up(off + 4 * d.H, kAlign);
+    l.qbar = off;
+    off = align_up(off + 4 * d.B * d.H * d.nB * d.D, kAlign);
+    l.kbar = off;
+    off = align_up(off + 4 * d.B * d.H * d.nB * d.D, kAlign);
+    l.bits = off;
+    off = align_up(off + 8 * d.rows * d.nW, kAlign);
+    l.counts = off;
+    off = align_up(off + 4 * d.rows, kAlign);
+    l.total = off;
+    return l;
+}
+
+bool bad_thr(float t) { return !(t > 0.f); }   // also rejects NaN
+
+int32_t rows_per_group(const Dims &d) {
+    int32_t R = 16;
+    while (R > 1 && (int64_t)R * d.nBp * 4 + 4 * 256 * 4 > kSelectMaxLds) R >>= 1;
+    while (R > 4 && d.B * d.H * ((d.nB + R - 1) / R) < 1024) R >>= 1;
+    return R;
+}
+
+int32_t emit_csr(const Dims &d, uint64_t *bits, int32_t *counts, int32_t *row_ptr, int32_t *col_idx,
+                 hipStream_t st) {
+    if (launch_scan(counts, d.rows, row_ptr, st)) return SPARSE_ATTN_HIP_ERROR;
+    if (launch_emit(bits, row_ptr, d.rows, (int32_t)d.nW, col_idx, st)) return SPARSE_ATTN_HIP_ERROR;
+    return SPARSE_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sparse_attn_version(void) { return SPARSE_ATTN_VERSION; }
+
+const char *sparse_attn_status_string(int32_t status) {
+    switch (status) {
+    case SPARSE_ATTN_OK: return "ok";
+    case SPARSE_ATTN_INVALID_ARGUMENT: return "invalid argument";
+    case SPARSE_ATTN_UNSUPPORTED: return "unsupported dtype, head_dim, tile or size";
+    case SPARSE_ATTN_CAPACITY: return "col_idx capacity below the worst case B*H*nB*nB";
+    case SPARSE_ATTN_WORKSPACE: return "workspace smaller than sparse_attn_workspace_size";
+    case SPARSE_ATTN_HIP_ERROR: return "HIP kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int64_t sparse_attn_csr_capacity(const sparse_attn_shape *shape) {
+    Dims d;
+    const int32_t st = check_shape(shape, &d);
+    if (st) return st;
+    return d.rows * d.nB;
+}
+
+int64_t sparse_attn_workspace_size(const sparse_attn_shape *shape) {
+    Dims d;
+    const int32_t st = check_shape(shape, &d);
+    if (st) return st;
+    return layout(d).total;
+}
+
+int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_select_params *params, const void *q,
+                           const void *k, int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity,
+                           void *workspace, int64_t workspace_bytes, void *stream) {
+    Dims d;
+    int32_t st = check_shape(shape, &d);
+    if (st) return st;
+    if (!params || !q || !k || !row_ptr || !col_idx || !workspace) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(row_ptr, 4) || !aligned(col_idx, 4) ||
+        !aligned(workspace, 16))
+        return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (d.nBp * 4 + 4 * 256 * 4 > kSelectMaxLds) return SPARSE_ATTN_UNSUPPORTED;
+    if (bad_thr(params->threshold)) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (params->head_thresholds)
+        for (int64_t h = 0; h < d.H; ++h)
+            if (bad_thr(params->head_thresholds[h])) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (col_capacity < d.rows * d.nB) return SPARSE_ATTN_CAPACITY;
+    const Layout L = layout(d);
+    if (workspace_bytes < L.total) return SPARSE_ATTN_WORKSPACE;
+
+    hipStream_t s = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    float *thr = (float *)(ws + L.thr);
+    float *qbar = (float *)(ws + L.qbar);
+    float *kbar = (float *)(ws + L.kbar);
+    uint64_t *bits = (uint64_t *)(ws + L.bits);
+    int32_t *counts = (int32_t *)(ws + L.counts);
+
+    {
+        float tmp[ThrChunk::kMax];
+        for (int64_t h0 = 0; h0 < d.H; h0 += ThrChunk::kMax) {
+            const int n = (int)((d.H - h0) < ThrChunk::kMax ? (d.H - h0) : ThrChunk::kMax);
+            for (int i = 0; i < n; ++i)
+                tmp[i] = params->head_thresholds ? params->head_thresholds[h0 + i] : params->threshold;
+            if (launch_fill_thresholds(tmp, n, thr + h0, s)) return SPARSE_ATTN_HIP_ERROR;
+        }
+    }
+    if (launch_pool(q, k, qbar, kbar, d.B * d.H * d.nB, shape->dtype, (int)d.D, s)) return SPARSE_ATTN_HIP_ERROR;
+
+    SelectArgs a;
+    a.qbar = qbar;
+    a.kbar = kbar;
+    a.thr = thr;
+    a.bits = bits;
+    a.counts = counts;
+    a.R = rows_per_group(d);
+    a.groups_per_head = (int32_t)((d.nB + a.R - 1) / a.R);
+    a.n_groups = d.B * d.H * a.groups_per_head;
+    a.H = (int32_t)d.H;
+    a.nB = (int32_t)d.nB;
+    a.nBp = (int32_t)d.nBp;
+    a.nTy = d.nTy;
+    a.nTx = d.nTx;
+    a.window = params->win_t >= 0 && params->win_h >= 0 && params->win_w >= 0;
+    a.wt = params->win_t;
+    a.wh = params->win_h;
+    a.ww = params->win_w;
+    a.scale_log2 = effective_scale(shape) * kLog2e;
+    if (launch_select(a, (int)d.D, s)) return SPARSE_ATTN_HIP_ERROR;
+    return emit_csr(d, bits, counts, row_ptr, col_idx, s);
+}
+
+int32_t sparse_attn_forward(const sparse_attn_shape *shape, const void *q, const void *k, const void *v,
+                            const int32_t *row_ptr, const int32_t *col_idx, int64_t col_count, void *out,
+                            float *lse, void *workspace, int64_t workspace_bytes, void *stream) {
+    Dims d;
+    int32_t st = check_shape(shape, &d);
+    if (st) return st;
+    if (!q || !k || !v || !row_ptr || !out || !workspace) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (col_count < 0 || (col_count > 0 && !col_idx)) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(row_ptr, 4) ||
+        !aligned(col_idx, 4) || !aligned(lse, 4) || !aligned(workspace, 16))
+        return SPARSE_ATTN_INVALID_ARGUMENT;
+    const Layout L = layout(d);
+    if (workspace_bytes < L.total) return SPARSE_ATTN_WORKSPACE;
+
+    AttnArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.row_ptr = row_ptr;
+    a.col_idx = col_idx;
+    a.col_count = col_count;
+    a.out = out;
+    a.lse = lse;
+    a.rows = d.rows;
+    a.nB = (int32_t)d.nB;
+    a.scale_log2 = effective_scale(shape) * kLog2e;
+    if (launch_attention(a, shape->dtype, (int)d.D, (hipStream_t)stream)) return SPARSE_ATTN_HIP_ERROR;
+    return SPARSE_ATTN_OK;
+}
+
+int32_t sparse_attn_mask_to_csr(const sparse_attn_shape *shape, const uint8_t *block_mask, int32_t *row_ptr,
+                                int32_t *col_idx, int64_t col_capacity, void *workspace, int64_t workspace_bytes,
+                                void *stream) {
+    Dims d;
+    int32_t st = check_shape(shape, &d);
+    if (st) return st;
+    if (!block_mask || !row_ptr || !col_idx || !workspace) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (!aligned(row_ptr, 4) || !aligned(col_idx, 4) || !aligned(workspace, 16)) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (col_capacity < d.rows * d.nB) return SPARSE_ATTN_CAPACITY;
+    const Layout L = layout(d);
+    if (workspace_bytes < L.total) return SPARSE_ATTN_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    uint64_t *bits = (uint64_t *)(ws + L.bits);
+    int32_t *counts = (int32_t *)(ws + L.counts);
+    if (launch_mask_bits(block_mask, d.rows, (int32_t)d.nB, (int32_t)d.nW, bits, counts, s))
+        return SPARSE_ATTN_HIP_ERROR;
+    return emit_csr(d, bits, counts, row_ptr, col_idx, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Device-side helpers shared by the gfx950 kernels of libsparse_attn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sattn {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+constexpr int kTokensPerBlock = 64;
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// bf16 <-> fp32 as raw 16-bit patterns (bf16 is the upper half of an fp32).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 with round-to-nearest-even, two values packed in one dword
+// (a in the low half).  NaN inputs do not occur on these paths.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+    ua += 0x7fffu + ((ua >> 16) & 1u);
+    ub += 0x7fffu + ((ub >> 16) & 1u);
+    return (ua >> 16) | (ub & 0xffff0000u);
+}
+
+template <typename T> struct DType;
+template <> struct DType<float> { static constexpr int code = 0; };
+template <> struct DType<__bf16> { static constexpr int code = 1; };
+
+// Wave-wide reductions over 64 lanes (results in every lane).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    return v;
+}
+
+// Bijective mapping of a flat work index so that the workgroups the hardware
+// sends to one XCD (dispatch is round-robin over the 8 XCDs) receive a
+// contiguous range of work items: neighbouring rows then share that XCD's L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t n) {
+    constexpr int64_t kXcd = 8;
+    const int64_t x = bid % kXcd, k = bid / kXcd;
+    const int64_t per = n / kXcd, rem = n % kXcd;
+    return x * per + (x < rem ? x : rem) + k;
+}
+
+}  // namespace sattn

@@ -1,0 +1,168 @@
+/*
+ * sparse_attn.h -- C-ABI of the MI355X (gfx950) dynamic block-sparse
+ * self-attention library (libsparse_attn.so).
+ *
+ * What the library computes follows the NABLA summary page ("NABLA:
+ * Neighborhood Adaptive Block-Level Attention", section "Methodologie :
+ * NABLA"): tokens of a latent video grid T x H x W arrive in tile-major order
+ * (item "Reordonnancement des Jetons", fractal flattening: one 1 x 8 x 8 tile
+ * of 64 tokens per block), Q and K are mean-pooled per block
+ * ("Sous-echantillonnage"), a softmax attention map is taken over the pooled
+ * blocks ("Attention Reduite"), each of its rows is cut by the CDF threshold
+ * ("Seuil CDF"), optionally united with a static sliding-tile window
+ * ("Integration Hybride avec STA", M = M_nabla OR M_STA), and exact softmax
+ * attention is then run over the kept 64 x 64 tiles only ("Expansion").
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense row-major [B, H, N, d] with N = grid_t*grid_h*grid_w;
+ *     block b of a head is tokens [64 b, 64 b + 64).  Element type is given
+ *     by shape->dtype (fp32 or bf16); q, k, v and out share it.
+ *   - All pointers named as device pointers must point to device memory (or
+ *     memory the device can address) and be 16-byte aligned.  Host pointers
+ *     are read during the call only and are not retained.
+ *   - The caller owns every buffer.  The library allocates and frees nothing
+ *     and keeps no state between calls; scratch space comes in through
+ *     `workspace` (see sparse_attn_workspace_size).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and runs asynchronously: no call synchronises the host.  Concurrent
+ *     calls are safe as long as they do not share output or workspace
+ *     buffers.
+ *   - Return value: SPARSE_ATTN_OK (0) or a negative status.  Every argument
+ *     is checked on the host before anything is enqueued, so a call that
+ *     fails a check launches nothing and writes nothing.  SPARSE_ATTN_HIP_ERROR
+ *     reports a launch failure (work enqueued before it may have run).
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPARSE_ATTN_VERSION 10000 /* 1.0.0 */
+
+/* element types */
+#define SPARSE_ATTN_F32 0
+#define SPARSE_ATTN_BF16 1
+
+/* status codes */
+#define SPARSE_ATTN_OK 0
+#define SPARSE_ATTN_INVALID_ARGUMENT (-1) /* null/misaligned pointer, bad size, bad threshold   */
+#define SPARSE_ATTN_UNSUPPORTED (-2)      /* dtype, head_dim or tile not implemented            */
+#define SPARSE_ATTN_CAPACITY (-3)         /* col_idx shorter than the worst case B*H*nB*nB      */
+#define SPARSE_ATTN_WORKSPACE (-4)        /* workspace smaller than sparse_attn_workspace_size  */
+#define SPARSE_ATTN_HIP_ERROR (-5)        /* a kernel launch failed                             */
+
+/*
+ * Problem shape.  head_dim must be 64 or 128; the tile must hold 64 tokens
+ * (only 1 x 8 x 8 is implemented) and divide the grid exactly.  scale is the
+ * softmax scale of both the pooled scores and the attention; 0 means
+ * 1/sqrt(head_dim).
+ */
+typedef struct sparse_attn_shape {
+    int32_t batch, heads, head_dim;
+    int32_t grid_t, grid_h, grid_w;
+    int32_t tile_t, tile_h, tile_w;
+    int32_t dtype;
+    float scale;
+} sparse_attn_shape;
+
+/*
+ * Selection parameters.
+ *   threshold        CDF mass to keep per query block, in (0, 1]; values >= 1
+ *                    keep every block.  NaN or <= 0 is rejected.
+ *   head_thresholds  optional HOST array [heads] overriding `threshold` per
+ *                    head (same rules), or NULL.  At most 1024 heads.
+ *   win_t/h/w        radii, in blocks, of the static window united with the
+ *                    CDF mask: key block j is also kept when |dt| <= win_t,
+ *                    |dy| <= win_h and |dx| <= win_w between the block
+ *                    coordinates of query and key (clipped at the grid edges,
+ *                    no wrap).  Any negative radius turns the window off.
+ */
+typedef struct sparse_attn_select_params {
+    float threshold;
+    const float *head_thresholds;
+    int32_t win_t, win_h, win_w;
+} sparse_attn_select_params;
+
+/* Library version (SPARSE_ATTN_VERSION of the build). */
+int32_t sparse_attn_version(void);
+
+/* Static text for a status code (never NULL). */
+const char *sparse_attn_status_string(int32_t status);
+
+/*
+ * Worst-case number of kept blocks, B*H*nB*nB, i.e. the col_idx length
+ * sparse_attn_select and sparse_attn_mask_to_csr require.  Negative status
+ * if the shape is invalid or the worst case does not fit in int32.
+ */
+int64_t sparse_attn_csr_capacity(const sparse_attn_shape *shape);
+
+/*
+ * Bytes of device workspace needed by every entry point for this shape
+ * (one size serves select, forward and mask_to_csr).  Negative status if
+ * the shape is invalid.
+ */
+int64_t sparse_attn_workspace_size(const sparse_attn_shape *shape);
+
+/*
+ * Dynamic block selection (pooling, reduced attention map, CDF cut, window
+ * union) emitted as a CSR block list.
+ *
+ *   q, k        device, [B, H, N, d] in shape->dtype, tile-major tokens.
+ *   row_ptr     device, int32 [B*H*nB + 1], written: row r = (b*H + h)*nB + i
+ *               owns col_idx[row_ptr[r] .. row_ptr[r+1]); row_ptr[0] = 0 and
+ *               row_ptr[B*H*nB] = nnz (left on the device, not returned).
+ *   col_idx     device, int32 [col_capacity]; entries [0, nnz) are written,
+ *               strictly ascending key-block indices within each row.
+ *   col_capacity  must be >= sparse_attn_csr_capacity(shape).
+ *   workspace   device, >= sparse_attn_workspace_size(shape) bytes; its
+ *               contents on entry do not matter.
+ * Ties in the CDF order go to the lower key-block index.
+ */
+int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_select_params *params,
+                           const void *q, const void *k, int32_t *row_ptr, int32_t *col_idx,
+                           int64_t col_capacity, void *workspace, int64_t workspace_bytes,
+                           void *stream);
+
+/*
+ * Block-sparse attention forward over a CSR block list (from
+ * sparse_attn_select, sparse_attn_mask_to_csr or the caller).
+ *
+ *   q, k, v     device, [B, H, N, d] in shape->dtype.
+ *   row_ptr     device, int32 [B*H*nB + 1], non-decreasing, row_ptr[0] = 0.
+ *   col_idx     device, int32 [col_count]; each row's entries are key-block
+ *               indices in [0, nB) without repeats (any order).  Entries
+ *               outside [0, nB) are skipped; row ends beyond col_count are
+ *               clipped to col_count.
+ *   out         device, [B, H, N, d] in shape->dtype: for each query token,
+ *               softmax(scale * q k^T) v over the tokens of the row's key
+ *               blocks.  A row with no block gives zeros.
+ *   lse         optional device fp32 [B, H, N] (natural-log log-sum-exp of
+ *               the scaled logits; -inf for an empty row), or NULL.
+ *   workspace   device, >= sparse_attn_workspace_size(shape) bytes.
+ */
+int32_t sparse_attn_forward(const sparse_attn_shape *shape, const void *q, const void *k, const void *v,
+                            const int32_t *row_ptr, const int32_t *col_idx, int64_t col_count,
+                            void *out, float *lse, void *workspace, int64_t workspace_bytes,
+                            void *stream);
+
+/*
+ * External block mask to CSR (the path that accepts a caller's mask, e.g. a
+ * static window or a mask reused from an earlier step).
+ *
+ *   block_mask  device, uint8 [B, H, nB, nB]; nonzero = keep key block j for
+ *               query block i.
+ *   row_ptr, col_idx, col_capacity, workspace: as in sparse_attn_select.
+ */
+int32_t sparse_attn_mask_to_csr(const sparse_attn_shape *shape, const uint8_t *block_mask,
+                                int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity,
+                                void *workspace, int64_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

@@ -1,0 +1,180 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C-ABI binding
+and compare it with the CPU oracle.
+
+Mask rule (selection).  Where GPU and oracle disagree on block j of a row,
+with p, E the oracle's probabilities and exclusive CDF mass and c the
+oracle's crossing block (the last block it keeps in CDF order):
+  R1  excused if |E(j) - thr| <= 1e-4;
+  R2  excused if |p_j - p_c| <= 1e-5 * p_c (a rank swap of near-equal blocks
+      at the cut);
+window blocks are never excused.  On rows that disagree, the GPU's kept set
+must still hold mass >= thr - 1e-4 and stay minimal (mass minus its smallest
+block < thr + 1e-4) when the window is off.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+import oracle
+from block_sparse_attention_row_amd import binding as B
+from block_sparse_attention_row_amd.synth import Workload
+
+R1_BAND = 1e-4
+R2_REL = 1e-5
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+LSE_TOL = {"bf16": 2e-3, "f32": 1e-4}
+
+
+def to_device(*ts):
+    return [t.to("cuda") for t in ts]
+
+
+def shape_for(wl: Workload) -> B.Shape:
+    return B.make_shape(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.dtype, 0.0, wl.tile)
+
+
+def check_csr(row_ptr: np.ndarray, col_idx: np.ndarray, nB: int):
+    """Structural validity of a CSR block list; returns the dense mask."""
+    rows = len(row_ptr) - 1
+    assert row_ptr[0] == 0
+    assert np.all(np.diff(row_ptr) >= 0)
+    nnz = int(row_ptr[-1])
+    cols = col_idx[:nnz]
+    assert np.all((cols >= 0) & (cols < nB))
+    mask = np.zeros((rows, nB), dtype=bool)
+    r = np.repeat(np.arange(rows), np.diff(row_ptr))
+    # strictly ascending within each row
+    same = r[1:] == r[:-1]
+    assert np.all(cols[1:][same] > cols[:-1][same])
+    mask[r, cols] = True
+    return mask
+
+
+def gpu_select(wl: Workload, q, k, thr, window=None, bufs=None):
+    shape = shape_for(wl)
+    win = wl.window if window is None else window
+    head_thr = None if wl.head_threshold_range is None else [float(x) for x in thr]
+    rp, ci = B.sparse_attn_select(shape, q, k, threshold=float(np.float32(wl.threshold)),
+                                  head_thresholds=head_thr, window=win, buffers=bufs)
+    torch.cuda.synchronize()
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    nnz = int(rp_h[-1])
+    ci_h = ci[:nnz].cpu().numpy()
+    return rp_h, ci_h
+
+
+@dataclass
+class MaskReport:
+    rows: int
+    diff_rows: int
+    diff_blocks: int
+    r1: int
+    r2: int
+    unexcused: int
+    window_missing: int
+    invariant_fail: int
+
+
+def compare_masks(gpu_mask: np.ndarray, keep: np.ndarray, qbar, kbar, wl: Workload, thr: np.ndarray,
+                  window=None) -> MaskReport:
+    """gpu_mask, keep: [rows, nB]; keep is the oracle's (bit0 CDF, bit1 window)."""
+    win = wl.window if window is None else window
+    nB = keep.shape[1]
+    oracle_mask = keep != 0
+    diff = np.nonzero((gpu_mask != oracle_mask).any(axis=1))[0]
+    r1 = r2 = unexc = wmiss = inv = nblk = 0
+    if len(diff):
+        kk, p, E = oracle.select_rows(qbar, kbar, wl.heads, wl.block_grid, thr.astype(np.float64), win,
+                                      rows=diff, stats=True)
+        window_on = all(w >= 0 for w in win)
+        for n, r in enumerate(diff):
+            t = float(thr[(r // nB) % wl.heads])
+            cdf = (kk[n] & 1) != 0
+            if t >= 1.0:
+                pc = None
+            else:
+                c = int(np.argmax(np.where(cdf, E[n], -1.0)))
+                pc = p[n, c]
+            for j in np.nonzero(gpu_mask[r] != oracle_mask[r])[0]:
+                nblk += 1
+                if kk[n, j] & 2:
+                    wmiss += 1
+                    continue
+                if abs(E[n, j] - t) <= R1_BAND:
+                    r1 += 1
+                elif pc is not None and abs(p[n, j] - pc) <= R2_REL * pc:
+                    r2 += 1
+                else:
+                    unexc += 1
+            if not window_on and t < 1.0:
+                kp = p[n][gpu_mask[r]]
+                if not (kp.sum() >= t - R1_BAND and kp.sum() - kp.min() < t + R1_BAND):
+                    inv += 1
+    return MaskReport(gpu_mask.shape[0], len(diff), nblk, r1, r2, unexc, wmiss, inv)
+
+
+def oracle_select_full(wl: Workload, q, k, thr):
+    qbar = oracle.pool(q)
+    kbar = oracle.pool(k)
+    keep = oracle.select_rows(qbar, kbar, wl.heads, wl.block_grid, thr.astype(np.float64), wl.window)
+    return qbar, kbar, keep
+
+
+def gpu_forward(wl: Workload, q, k, v, row_ptr, col_idx, want_lse=True):
+    shape = shape_for(wl)
+    rp = torch.as_tensor(np.asarray(row_ptr, dtype=np.int32)).cuda()
+    ci = torch.as_tensor(np.asarray(col_idx, dtype=np.int32)).cuda()
+    if ci.numel() == 0:
+        ci = torch.zeros(1, dtype=torch.int32, device="cuda")[:0]
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=q.device)
+    B.sparse_attn_forward(shape, q, k, v, rp, ci, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def compare_rows(wl: Workload, out, lse, q, k, v, row_ptr, col_idx, rows):
+    """Max |GPU - oracle| of output and LSE over the listed query-block rows."""
+    ref, ref_lse = oracle.attention_rows(q, k, v, row_ptr, col_idx, rows)
+    nB = wl.blocks
+    o = out.float().cpu().reshape(-1, nB, 64, wl.head_dim)
+    l = lse.cpu().reshape(-1, nB, 64)
+    rows = np.asarray(rows)
+    got = o[rows // nB, rows % nB].numpy().astype(np.float64)
+    got_l = l[rows // nB, rows % nB].numpy().astype(np.float64)
+    assert np.isfinite(got).all(), "non-finite output"
+    err = float(np.abs(got - ref).max()) if got.size else 0.0
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isneginf(got_l), ~fin)
+    lerr = float(np.abs(got_l[fin] - ref_lse[fin]).max()) if fin.any() else 0.0
+    return err, lerr
+
+
+def sample_rows(wl: Workload, thr: np.ndarray, n_heads=2, n_blocks=32, seed=1):
+    rng = np.random.default_rng(seed)
+    if wl.head_threshold_range is not None:
+        heads = [int(np.argmin(thr)), int(np.argmax(thr))]
+    else:
+        heads = sorted(rng.choice(wl.heads, size=min(n_heads, wl.heads), replace=False).tolist())
+    rows = []
+    for h in heads:
+        blocks = np.sort(rng.choice(wl.blocks, size=min(n_blocks, wl.blocks), replace=False))
+        rows.extend((h * wl.blocks + blocks).tolist())        # batch 0
+    return np.array(rows, dtype=np.int64)
+
+
+def flops_kept(nnz: int, d: int) -> float:
+    return 4.0 * 64 * 64 * d * nnz
+
+
+def fmt(rep: MaskReport) -> str:
+    return (f"rows={rep.rows} diff_rows={rep.diff_rows} diff_blocks={rep.diff_blocks} R1={rep.r1} R2={rep.r2} "
+            f"unexcused={rep.unexcused} window_missing={rep.window_missing} invariant_fail={rep.invariant_fail}")
+
+
+def scale_of(d: int) -> float:
+    return 1.0 / math.sqrt(d)

@@ -1,0 +1,156 @@
+"""Host-side checks of the C-ABI (no GPU needed: every rejected call returns
+before any HIP call, and the size queries are pure host code)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_row_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(sparse_attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_exported_set():
+    assert _declared() == sorted(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert B.sparse_attn_version() == 10000
+    for st in (0, -1, -2, -3, -4, -5):
+        assert B.status_string(st) and B.status_string(st) != "unknown status"
+    assert B.status_string(-99) == "unknown status"
+
+
+def _shape(**kw):
+    base = dict(batch=1, heads=12, head_dim=128, grid=(20, 32, 48), dtype="bf16")
+    base.update(kw)
+    return B.make_shape(base["batch"], base["heads"], base["head_dim"], base["grid"], base["dtype"],
+                        base.get("scale", 0.0), base.get("tile", (1, 8, 8)))
+
+
+def test_capacity_and_workspace_formulas():
+    s = _shape()
+    nB = 20 * 4 * 6
+    assert nB == 480
+    rows = 12 * nB
+    assert B.sparse_attn_csr_capacity(s) == rows * nB
+    nbp = 512
+    expect = 0
+    al = lambda x: (x + 255) // 256 * 256
+    expect = al(expect + 4 * 12)
+    expect = al(expect + 4 * rows * 128)
+    expect = al(expect + 4 * rows * 128)
+    expect = al(expect + 8 * rows * (nbp // 64))
+    expect = al(expect + 4 * rows)
+    assert B.sparse_attn_workspace_size(s) == expect
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), B.SPARSE_ATTN_UNSUPPORTED),
+    (dict(dtype=7), B.SPARSE_ATTN_UNSUPPORTED),
+    (dict(grid=(20, 30, 48)), B.SPARSE_ATTN_UNSUPPORTED),          # not a whole number of 8x8 tiles
+    (dict(tile=(1, 4, 8)), B.SPARSE_ATTN_UNSUPPORTED),             # 32-token tile
+    (dict(batch=0), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(heads=-1), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(scale=float("nan")), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(scale=float("inf")), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(heads=4000, grid=(64, 48, 80)), B.SPARSE_ATTN_UNSUPPORTED),  # worst-case nnz overflows int32
+])
+def test_bad_shapes_rejected(kw, status):
+    s = _shape(**kw)
+    assert B.sparse_attn_csr_capacity(s) == status
+    assert B.sparse_attn_workspace_size(s) == status
+
+
+def test_other_64_token_tiles_accepted():
+    s = _shape(tile=(4, 4, 4), grid=(20, 32, 48))
+    assert B.sparse_attn_csr_capacity(s) == (12 * 5 * 8 * 12) * (5 * 8 * 12)
+
+
+# Fake but well-aligned device addresses: every call below must fail its
+# host-side checks before it could dereference or launch anything.
+A = 1 << 20
+
+
+def _select(shape, thr=0.9, head_thr=None, q=A, k=A, rp=A, ci=A, cap=None, ws=A, wsb=None):
+    params = B.SelectParams(thr, head_thr, -1, -1, -1)
+    cap = B.sparse_attn_csr_capacity(shape) if cap is None else cap
+    wsb = B.sparse_attn_workspace_size(shape) if wsb is None else wsb
+    return B.lib().sparse_attn_select(ctypes.byref(shape), ctypes.byref(params), q, k, rp, ci, cap, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(thr=0.0), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(thr=-0.5), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(thr=float("nan")), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(q=None), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(k=A + 8), B.SPARSE_ATTN_INVALID_ARGUMENT),              # misaligned
+    (dict(rp=A + 2), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(ci=None), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(ws=None), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(cap=10), B.SPARSE_ATTN_CAPACITY),
+    (dict(wsb=1024), B.SPARSE_ATTN_WORKSPACE),
+])
+def test_select_rejects_before_launch(kw, status):
+    assert _select(_shape(), **kw) == status
+
+
+def test_select_rejects_bad_head_threshold():
+    arr = (ctypes.c_float * 12)(*([0.9] * 11 + [float("nan")]))
+    assert _select(_shape(), head_thr=ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))) == \
+        B.SPARSE_ATTN_INVALID_ARGUMENT
+
+
+def test_select_rejects_too_many_blocks():
+    s = _shape(heads=1, grid=(256, 64, 64))     # 16,384 blocks: score row does not fit the selection LDS
+    assert _select(s) == B.SPARSE_ATTN_UNSUPPORTED
+
+
+def _forward(shape, q=A, k=A, v=A, rp=A, ci=A, cc=100, out=A, lse=None, ws=A, wsb=None):
+    wsb = B.sparse_attn_workspace_size(shape) if wsb is None else wsb
+    return B.lib().sparse_attn_forward(ctypes.byref(shape), q, k, v, rp, ci, cc, out, lse, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(v=None), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(out=A + 4), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(lse=A + 2), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(cc=-1), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(ci=None, cc=5), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(rp=None), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(wsb=0), B.SPARSE_ATTN_WORKSPACE),
+])
+def test_forward_rejects_before_launch(kw, status):
+    assert _forward(_shape(), **kw) == status
+
+
+def test_forward_rejects_bad_shape():
+    assert _forward(_shape(head_dim=32)) == B.SPARSE_ATTN_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mask=None), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(cap=0), B.SPARSE_ATTN_CAPACITY),
+    (dict(wsb=16), B.SPARSE_ATTN_WORKSPACE),
+    (dict(rp=A + 1), B.SPARSE_ATTN_INVALID_ARGUMENT),
+])
+def test_mask_to_csr_rejects_before_launch(kw, status):
+    s = _shape()
+    cap = kw.get("cap", B.sparse_attn_csr_capacity(s))
+    wsb = kw.get("wsb", B.sparse_attn_workspace_size(s))
+    mask = kw.get("mask", A)
+    rp = kw.get("rp", A)
+    assert B.lib().sparse_attn_mask_to_csr(ctypes.byref(s), mask, rp, A, cap, A, wsb, None) == status

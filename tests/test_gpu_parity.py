@@ -1,0 +1,209 @@
+"""GPU parity: the HIP path (through the C-ABI) against the CPU oracle.
+
+Small workloads (several tiles, ragged block counts, both dtypes and head
+sizes, windows, per-head thresholds, batch > 1) are compared in full; the
+five full-size workloads in test_gpu_workloads.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_attention_row_amd import binding as B
+from block_sparse_attention_row_amd.synth import WORKLOADS, make_inputs, small_workload
+
+from . import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    B.lib()
+
+
+SMALL = [
+    # name, heads, d, block grid, dtype, thr, window, reading, head-thr range, batch
+    ("f32_d64_tiny", 1, 64, (4, 2, 2), "f32", 0.9, (-1, -1, -1), "A", None, 1),
+    ("f32_d128_ragged", 2, 128, (3, 3, 5), "f32", 0.8, (-1, -1, -1), "B", None, 1),
+    ("bf16_d128_ragged", 3, 128, (3, 5, 7), "bf16", 0.85, (-1, -1, -1), "A", None, 1),
+    ("bf16_d128_sparse", 2, 128, (4, 4, 6), "bf16", 0.9, (-1, -1, -1), "B", None, 1),
+    ("bf16_d64_window", 2, 64, (2, 3, 5), "bf16", 0.7, (1, 1, 1), "B", None, 1),
+    ("bf16_d128_window_A", 2, 128, (5, 3, 4), "bf16", 0.8, (1, 1, 1), "A", None, 1),
+    ("bf16_d128_headthr", 4, 128, (2, 4, 9), "bf16", 0.7, (-1, -1, -1), "A", (0.6, 0.8), 2),
+    ("bf16_d128_page", 3, 128, (4, 6, 8), "bf16", 0.9, (-1, -1, -1), "page", None, 1),
+    ("bf16_d128_dense", 2, 128, (2, 3, 3), "bf16", 1.0, (-1, -1, -1), "A", None, 1),
+    ("bf16_d128_one_block", 2, 128, (1, 1, 1), "bf16", 0.5, (-1, -1, -1), "A", None, 1),
+]
+
+
+def _wl(case):
+    name, H, d, bg, dt, thr, win, reading, hr, batch = case
+    wl = small_workload(name, H, d, bg, dt, threshold=thr, window=win, head_threshold_range=hr, seed=7)
+    return wl.with_(batch=batch), reading
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_select_and_forward(case):
+    wl, reading = _wl(case)
+    print(f"\n[case] {wl.name} reading={reading} heads={wl.heads} d={wl.head_dim} blocks={wl.blocks}", flush=True)
+    q, k, v, thr = make_inputs(wl, reading)
+    qd, kd, vd = P.to_device(q, k, v)
+
+    # selection: GPU mask vs oracle mask under the excuse rules
+    rp, ci = P.gpu_select(wl, qd, kd, thr)
+    gmask = P.check_csr(rp, ci, wl.blocks)
+    qbar, kbar, keep = P.oracle_select_full(wl, q, k, thr)
+    rep = P.compare_masks(gmask, keep, qbar, kbar, wl, thr)
+    print(P.fmt(rep), flush=True)
+    assert rep.unexcused == 0 and rep.window_missing == 0 and rep.invariant_fail == 0
+
+    # forward under the oracle's CSR, every row
+    orp, oci = oracle.csr_from_mask(keep != 0)
+    out, lse = P.gpu_forward(wl, qd, kd, vd, orp, oci)
+    rows = np.arange(wl.batch * wl.heads * wl.blocks)
+    err, lerr = P.compare_rows(wl, out, lse, q, k, v, orp, oci, rows)
+    print(f"forward max|err|={err:.3e} lse max|err|={lerr:.3e}", flush=True)
+    tol, ltol = P.TOL[wl.dtype], P.LSE_TOL[wl.dtype]
+    if wl.dtype == "f32" and reading != "A":
+        # Reading B gives logits near 200: a 128-term fp32 dot product of that size carries about
+        # sqrt(d) * ulp(2048) / 2 ~ 7e-4 of rounding (6e-5 after the 1/sqrt(d) scale), which moves
+        # the softmax weights by that relative amount; 1e-3 covers it with margin.  The 1e-4 fp32 bound
+        # is for the specified fp32 workload, whose logits are O(1).
+        tol, ltol = 1e-3, 1e-3
+    assert err <= tol and lerr <= ltol
+
+    # end to end: GPU CSR into GPU forward, on rows where the masks agree
+    out2, lse2 = P.gpu_forward(wl, qd, kd, vd, rp, ci)
+    same = np.nonzero(~(gmask != (keep != 0)).any(axis=1))[0]
+    err2, lerr2 = P.compare_rows(wl, out2, lse2, q, k, v, orp, oci, same)
+    assert err2 <= tol and lerr2 <= ltol
+
+
+def test_threshold_one_is_dense_attention():
+    wl = small_workload("dense", 2, 128, (2, 2, 3), "bf16", threshold=1.0, seed=3)
+    q, k, v, thr = make_inputs(wl, "B")
+    qd, kd, vd = P.to_device(q, k, v)
+    rp, ci = P.gpu_select(wl, qd, kd, thr)
+    gmask = P.check_csr(rp, ci, wl.blocks)
+    assert gmask.all()
+    out, lse = P.gpu_forward(wl, qd, kd, vd, rp, ci)
+    ref = torch.nn.functional.scaled_dot_product_attention(q.double(), k.double(), v.double())
+    assert (out.double().cpu() - ref).abs().max().item() <= P.TOL["bf16"]
+
+
+def test_external_mask_empty_rows_and_roundtrip():
+    wl = small_workload("ext", 2, 128, (2, 3, 4), "bf16", seed=11)
+    q, k, v, _ = make_inputs(wl, "A")
+    qd, kd, vd = P.to_device(q, k, v)
+    rng = np.random.default_rng(5)
+    rows, nB = wl.heads * wl.blocks, wl.blocks
+    mask = rng.random((rows, nB)) < 0.3
+    mask[[0, 7, rows - 1]] = False                  # empty rows
+    mask[3] = True                                  # a full row
+    shape = P.shape_for(wl)
+    mdev = torch.as_tensor(mask.astype(np.uint8)).cuda()
+    rp, ci = B.sparse_attn_mask_to_csr(shape, mdev)
+    torch.cuda.synchronize()
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    ci_h = ci[:int(rp_h[-1])].cpu().numpy()
+    orp, oci = oracle.csr_from_mask(mask)
+    assert np.array_equal(rp_h, orp) and np.array_equal(ci_h, oci)   # integer work: bit-exact
+    out, lse = P.gpu_forward(wl, qd, kd, vd, rp_h, ci_h)
+    err, lerr = P.compare_rows(wl, out, lse, q, k, v, orp, oci, np.arange(rows))
+    assert err <= P.TOL["bf16"] and lerr <= P.LSE_TOL["bf16"]
+    o = out.float().cpu().reshape(rows, 64, -1)
+    assert torch.all(o[[0, 7, rows - 1]] == 0)
+    l = lse.cpu().reshape(rows, 64)
+    assert torch.all(torch.isneginf(l[[0, 7, rows - 1]]))
+
+
+def test_forward_any_column_order_and_skips_bad_columns():
+    wl = small_workload("order", 1, 128, (2, 2, 4), "bf16", seed=13)
+    q, k, v, _ = make_inputs(wl, "B")
+    qd, kd, vd = P.to_device(q, k, v)
+    nB = wl.blocks
+    rng = np.random.default_rng(2)
+    mask = rng.random((nB, nB)) < 0.5
+    mask[:, 0] = True
+    orp, oci = oracle.csr_from_mask(mask)
+    shuf = oci.copy()
+    for r in range(nB):
+        seg = shuf[orp[r]:orp[r + 1]]
+        shuf[orp[r]:orp[r + 1]] = seg[rng.permutation(len(seg))]
+    out_a, lse_a = P.gpu_forward(wl, qd, kd, vd, orp, oci)
+    out_b, lse_b = P.gpu_forward(wl, qd, kd, vd, orp, shuf)
+    err, lerr = P.compare_rows(wl, out_b, lse_b, q, k, v, orp, oci, np.arange(nB))
+    assert err <= P.TOL["bf16"] and lerr <= P.LSE_TOL["bf16"]
+    # columns outside [0, nB) are skipped: insert -1 and nB into every row
+    rp2 = [0]
+    ci2 = []
+    for r in range(nB):
+        ci2 += [-1] + oci[orp[r]:orp[r + 1]].tolist() + [nB + 3]
+        rp2.append(len(ci2))
+    out_c, lse_c = P.gpu_forward(wl, qd, kd, vd, np.array(rp2), np.array(ci2))
+    assert torch.equal(out_c, out_a) and torch.equal(lse_c, lse_a)
+
+
+def test_deterministic_and_no_nan():
+    wl = small_workload("det", 3, 128, (3, 4, 5), "bf16", threshold=0.8, window=(1, 1, 1), seed=17)
+    q, k, v, thr = make_inputs(wl, "A")
+    qd, kd, vd = P.to_device(q, k, v)
+    shape = P.shape_for(wl)
+    bufs = B.alloc_buffers(shape)
+    bufs.col_idx.fill_(-7)
+    results = []
+    for _ in range(2):
+        rp, ci = B.sparse_attn_select(shape, qd, kd, threshold=wl.threshold, window=wl.window, buffers=bufs)
+        rp = rp.clone()
+        ci = ci[:int(rp[-1].item())].clone()
+        out = torch.full_like(qd, float("nan"))
+        lse = torch.full(qd.shape[:3], float("nan"), device="cuda")
+        B.sparse_attn_forward(shape, qd, kd, vd, rp, ci, out=out, lse=lse)
+        torch.cuda.synchronize()
+        results.append((rp.cpu(), ci.cpu(), out.cpu(), lse.cpu()))
+    for a, b in zip(*results):
+        assert torch.equal(a, b)
+    assert not torch.isnan(results[0][2].float()).any() and not torch.isnan(results[0][3]).any()
+
+
+def test_nondefault_scale():
+    wl = small_workload("scale", 2, 64, (2, 2, 3), "f32", threshold=0.75, seed=19)
+    q, k, v, thr = make_inputs(wl, "A")
+    qd, kd, vd = P.to_device(q, k, v)
+    shape = B.make_shape(1, wl.heads, wl.head_dim, wl.grid, "f32", scale=0.5)
+    rp, ci = B.sparse_attn_select(shape, qd, kd, threshold=0.75)
+    torch.cuda.synchronize()
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    gmask = P.check_csr(rp_h, ci[:int(rp_h[-1])].cpu().numpy(), wl.blocks)
+    qbar, kbar = oracle.pool(q), oracle.pool(k)
+    keep = oracle.select_rows(qbar, kbar, wl.heads, wl.block_grid, 0.75, scale=0.5)
+    assert (gmask == (keep != 0)).mean() > 0.999
+    orp, oci = oracle.csr_from_mask(keep != 0)
+    rpd = torch.as_tensor(orp.astype(np.int32)).cuda()
+    cid = torch.as_tensor(oci).cuda()
+    out, lse = B.sparse_attn_forward(shape, qd, kd, vd, rpd, cid, want_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.attention_rows(q, k, v, orp, oci, np.arange(wl.heads * wl.blocks), scale=0.5)
+    got = out.cpu().reshape(-1, 64, wl.head_dim).numpy()
+    assert np.abs(got - ref).max() <= P.TOL["f32"]
+    assert np.abs(lse.cpu().reshape(-1, 64).numpy() - ref_lse).max() <= P.LSE_TOL["f32"]
+
+
+def test_tiny_workload_full():
+    wl = WORKLOADS["tiny_f32"]
+    q, k, v, thr = make_inputs(wl, "A")
+    qd, kd, vd = P.to_device(q, k, v)
+    rp, ci = P.gpu_select(wl, qd, kd, thr)
+    gmask = P.check_csr(rp, ci, wl.blocks)
+    qbar, kbar, keep = P.oracle_select_full(wl, q, k, thr)
+    rep = P.compare_masks(gmask, keep, qbar, kbar, wl, thr)
+    print(P.fmt(rep), flush=True)
+    assert rep.unexcused == 0
+    orp, oci = oracle.csr_from_mask(keep != 0)
+    out, lse = P.gpu_forward(wl, qd, kd, vd, orp, oci)
+    err, lerr = P.compare_rows(wl, out, lse, q, k, v, orp, oci, np.arange(wl.blocks))
+    print(f"tiny forward err={err:.3e} lse={lerr:.3e}", flush=True)
+    assert err <= P.TOL["f32"] and lerr <= P.LSE_TOL["f32"]
