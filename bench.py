@@ -1,0 +1,299 @@
+"""Benchmark of the block-sparse attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+sparse_attn_select (pooling, pooled softmax, CDF cut, CSR) followed by
+sparse_attn_forward (block-sparse flash attention over the kept tiles).
+The workload is the Wan2.1-1.3B-480p-like layer: batch 1, 12 heads, d=128,
+bf16, grid 20x32x48 (30,720 tokens, 480 blocks of 1x8x8), threshold 0.9,
+inputs from the seeded generator (reading A).
+
+Prints one JSON line.  `value` is the effective TFLOP/s of the whole step on
+kept tiles, 4*64*64*d*nnz / t_step.  `roofline` is for the attention
+kernel (MFMA bound, bf16 dense peak 2.5 PFLOP/s), its launch duration taken
+with HIP events on the stream it runs on.  `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py --pmc-summary DIR   # HBM traffic from rocprofv3 --pmc runs
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_wan13b_480p.json")
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_row_amd", "csrc", "attention.hip")
+ATTN_KERNEL = "attn_bf16_kernel"
+COPY_BYTES = 1 << 30
+
+
+def _sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan13b_480p")
+    ap.add_argument("--reading", default="A")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for rocprofv3 counter scaling)")
+    ap.add_argument("--pmc-summary", metavar="DIR", help="summarise rocprofv3 --pmc output and exit")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------- counters
+
+def _read_counter_csv(pattern, counter):
+    """Per-dispatch counter values by kernel name from rocprofv3 counter_collection.csv files."""
+    out = {}
+    for path in glob.glob(pattern, recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row.get("Kernel_Name", "")
+                out.setdefault(name, []).append(float(row["Counter_Value"]))
+    return out
+
+
+def pmc_summary(d):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel, scaled by a 1 GiB copy."""
+    fetch = _read_counter_csv(os.path.join(d, "fetch", "**", "*counter_collection.csv"), "FETCH_SIZE")
+    write = _read_counter_csv(os.path.join(d, "write", "**", "*counter_collection.csv"), "WRITE_SIZE")
+
+    def pick(table, key):
+        vals = [v for n, vs in table.items() if key in n for v in vs]
+        return sum(vals) / len(vals) if vals else None
+
+    copy_key = "elementwise_kernel"
+    cf, cw = pick(fetch, copy_key), pick(write, copy_key)
+    af, aw = pick(fetch, ATTN_KERNEL), pick(write, ATTN_KERNEL)
+    kib = COPY_BYTES / 1024.0
+    rec = {
+        "kernel": ATTN_KERNEL,
+        "attention_source_sha256": _sha(ATTN_SRC),
+        "fetch_kib_per_dispatch": af, "write_kib_per_dispatch": aw,
+        "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_expected_kib": kib,
+        "fetch_scale": (kib / cf) if cf else None, "write_scale": (kib / cw) if cw else None,
+    }
+    if af and aw and cf and cw:
+        rec["hbm_bytes_per_dispatch"] = af * 1024.0 * rec["fetch_scale"] + aw * 1024.0 * rec["write_scale"]
+    print(json.dumps(rec, indent=1))
+    return rec
+
+
+def stored_traffic():
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("attention_source_sha256") != _sha(ATTN_SRC):
+        return None            # kernel changed since the counters were taken
+    return rec.get("hbm_bytes_per_dispatch")
+
+
+# ---------------------------------------------------------------------------- GPU bench
+
+def main():
+    args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the path shards by head with no exchange, see the design notes", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_sparse_attention_row_amd import binding as B
+    from block_sparse_attention_row_amd.synth import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    B.lib()
+    wl = WORKLOADS[args.workload]
+    t0 = time.time()
+    q, k, v, thr = make_inputs(wl, args.reading)
+    print(f"[bench] inputs {wl.name} reading {args.reading} drawn in {time.time() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    shape = B.make_shape(wl.batch, wl.heads, wl.head_dim, wl.grid, wl.dtype, 0.0, wl.tile)
+    bufs = B.alloc_buffers(shape, dev)
+    out = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+    head_thr = None if wl.head_threshold_range is None else [float(x) for x in thr]
+    stream = torch.cuda.current_stream()
+
+    def select():
+        return B.sparse_attn_select(shape, qd, kd, threshold=float(np.float32(wl.threshold)),
+                                    head_thresholds=head_thr, window=wl.window, buffers=bufs, stream=stream)
+
+    def forward(rp, ci):
+        B.sparse_attn_forward(shape, qd, kd, vd, rp, ci, out=out, lse=lse, workspace=bufs.workspace,
+                              stream=stream)
+
+    def step():
+        rp, ci = select()
+        forward(rp, ci)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    nnz = int(bufs.row_ptr[-1].item())
+    rows = wl.batch * wl.heads * wl.blocks
+
+    # timed region: exactly `steps` steps, synchronised on both sides
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        rp, ci = select()
+        ev[i][0].record(stream)
+        forward(rp, ci)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    ms_step = 1000.0 * t_total / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    attn_ms_avg = sum(attn_ms) / len(attn_ms)
+
+    flops = 4.0 * 64 * 64 * wl.head_dim * nnz
+    value = flops / (ms_step * 1e-3) / 1e12
+    attn_tflops = flops / (attn_ms_avg * 1e-3) / 1e12
+
+    # selection alone, each repetition after a 1 GiB sweep so Q and K do not sit in the last-level cache
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    sel_ms = []
+    for _ in range(10):
+        flush.add_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        select()
+        b.record(stream)
+        torch.cuda.synchronize()
+        sel_ms.append(a.elapsed_time(b))
+    sel_ms_med = sorted(sel_ms)[len(sel_ms) // 2]
+    elt = qd.element_size()
+    sel_bytes = 2 * qd.numel() * elt + 4 * (rows + 1) + 4 * nnz
+    sel_gbs = sel_bytes / (sel_ms_med * 1e-3) / 1e9
+
+    # dense reference: the same forward kernel over the full CSR (every tile kept)
+    full_rp = torch.arange(0, rows + 1, dtype=torch.int32, device=dev) * wl.blocks
+    full_ci = torch.arange(wl.blocks, dtype=torch.int32, device=dev).repeat(rows)
+    for _ in range(2):
+        B.sparse_attn_forward(shape, qd, kd, vd, full_rp, full_ci, out=out, lse=lse, workspace=bufs.workspace,
+                              stream=stream)
+    dense_ms = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        B.sparse_attn_forward(shape, qd, kd, vd, full_rp, full_ci, out=out, lse=lse, workspace=bufs.workspace,
+                              stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        dense_ms.append(a.elapsed_time(b))
+    dense_ms_med = sorted(dense_ms)[len(dense_ms) // 2]
+
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    traffic = stored_traffic()
+    rec = {
+        "metric": "effective TFLOP/s on kept tiles (select + forward step)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded smoothed-Gaussian Q, K = Q + noise, Gaussian V)",
+        "config": {
+            "workload": wl.name, "batch": wl.batch, "heads": wl.heads, "head_dim": wl.head_dim,
+            "grid": list(wl.grid), "tokens": wl.tokens, "blocks": wl.blocks, "threshold": wl.threshold,
+            "window": list(wl.window), "reading": args.reading, "nnz_tiles": nnz,
+            "kept_fraction": round(nnz / (rows * wl.blocks), 4),
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+            "kernel": ATTN_KERNEL, "launch_ms": round(attn_ms_avg, 4),
+            "flops_per_launch": flops,
+        },
+        "attention_tflops_pct_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+        "selection": {
+            "ms": round(sel_ms_med, 4), "bytes": sel_bytes, "GB_s": round(sel_gbs, 1),
+            "frac_hbm_peak": round(sel_gbs / PEAK_HBM_GBS, 4),
+        },
+        "dense_forward_ms": round(dense_ms_med, 4),
+        "speedup_vs_dense": {
+            "forward": round(dense_ms_med / attn_ms_avg, 3),
+            "select_plus_forward": round(dense_ms_med / (attn_ms_avg + sel_ms_med), 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl, q, k, v, thr, bufs, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(wl, q, k, v, thr, bufs, target_s):
+    """The CPU oracle timed on a bounded sample of the same workload (rank 0, one GPU)."""
+    import numpy as np
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    rows = wl.batch * wl.heads * wl.blocks
+    rp = bufs.row_ptr.cpu().numpy().astype(np.int64)
+    ci = bufs.col_idx[:int(rp[-1])].cpu().numpy()
+    # time one query block first, then size the sample to about target_s seconds
+    rng = np.random.default_rng(1)
+    order = rng.permutation(rows)
+    t0 = time.perf_counter()
+    oracle.attention_rows(q, k, v, rp, ci, order[:1])
+    per = max(time.perf_counter() - t0, 1e-3)
+    n = int(min(rows, max(2, target_s / per)))
+    sample = order[1:1 + n]
+    t0 = time.perf_counter()
+    oracle.attention_rows(q, k, v, rp, ci, sample)
+    t = time.perf_counter() - t0
+    tiles = int(np.sum(rp[sample + 1] - rp[sample]))
+    tflops = 4.0 * 64 * 64 * wl.head_dim * tiles / t / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle attention over {n} of {rows} query blocks ({tiles} kept tiles, "
+                      f"{t:.1f} s) under the GPU's block list; full-step extrapolation "
+                      f"{t * rows / n:.0f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -36,7 +36,7 @@ int32_t check_shape(const sparse_attn_shape *s, Dims *d) {
     if (s->head_dim != 64 && s->head_dim != 128) return SPARSE_ATTN_UNSUPPORTED;
     if ((int64_t)s->tile_t * s->tile_h * s->tile_w != 64) return SPARSE_ATTN_UNSUPPORTED;
     if (s->grid_t % s->tile_t || s->grid_h % s->tile_h || s->grid_w % s->tile_w) return SPARSE_ATTN_UNSUPPORTED;
-    if (!isfinite(s->scale)) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (!isfinite(s->scale) || s->scale < 0.f) return SPARSE_ATTN_INVALID_ARGUMENT;
     d->B = s->batch;
     d->H = s->heads;
     d->D = s->head_dim;

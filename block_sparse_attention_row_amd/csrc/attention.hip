@@ -28,25 +28,58 @@ namespace sattn {
 
 // ---------------------------------------------------------------------------
 // bf16 inputs, bf16 MFMA (v_mfma_f32_32x32x16_bf16), fp32 accumulation.
-template <int D>
-__global__ __launch_bounds__(128) void attn_bf16_kernel(AttnArgs a) {
-    constexpr int KS = D + 8;        // K row stride in LDS (elements)
-    constexpr int VS = 64 + 8;       // V^T row stride in LDS (elements)
-    constexpr int NDG = D / 8;       // 16-byte column groups per token row
-    constexpr int KCH = 64 * NDG / 128;   // K chunks per thread
-    constexpr int NDT = D / 32;      // 32-wide d tiles of the output
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[64 * KS];
-    __shared__ __attribute__((aligned(16))) __bf16 Vt[D * VS];
+//
+// K and V tiles go from global memory straight into LDS with
+// global_load_lds_dwordx4 (lane p of a wave-wide load lands at M0 + 16 p),
+// row-major, the 16-byte slots of row r XOR-swizzled by r mod (slots per row) so
+// that operand reads of 16 consecutive rows hit 16 different bank groups.  V is
+// read transposed with ds_read_b64_tr_b16: within each 16-lane group, source
+// lane 4e + c names 4 consecutive d of key row e, and output lane i receives the
+// 4 keys at d = i -- the A-operand layout of O^T = V^T P^T.
+//
+// The direct loads are issued from inline asm and waited for explicitly, so the
+// next K streams in during the softmax and P V of the current tile and the next V
+// during the next Q K^T.  Column indices come through the scalar cache.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, hh = lane >> 5, l32 = lane & 31;
+// One wave-wide 16-byte-per-lane load from sbase + voff into LDS at lds_addr + 16 * lane.
+__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, const void *sbase) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+
+template <int D>
+__global__ __launch_bounds__(128, 2) void attn_bf16_kernel(AttnArgs a) {
+    constexpr int ROWB = D * 2;                   // bytes per token row
+    constexpr int SLOTS = ROWB / 16;              // 16-byte slots per row
+    constexpr int RPI = 1024 / ROWB;              // rows written by one wave-wide direct load
+    constexpr int IPW = 32 / RPI;                 // direct loads per wave per tile (each wave: 32 rows)
+    constexpr int NPAT = SLOTS / RPI;             // distinct per-lane swizzle patterns
+    constexpr int NDT = D / 32;                   // 32-wide d tiles of the output
+    static_assert(NPAT * RPI * ROWB == ROWB * SLOTS, "pattern period");
+    __shared__ __attribute__((aligned(1024))) char Ks[64 * ROWB];
+    __shared__ __attribute__((aligned(1024))) char Vs[64 * ROWB];
+
+    const int t = threadIdx.x, lane = t & 63, hh = lane >> 5, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int64_t row = xcd_remap(blockIdx.x, a.rows);
     const int64_t bh = row / a.nB;
     const int64_t N = (int64_t)a.nB * 64;
     const __bf16 *qg = (const __bf16 *)a.q + (bh * N + (row % a.nB) * 64) * D;
-    const __bf16 *kg = (const __bf16 *)a.k + bh * N * D;
-    const __bf16 *vg = (const __bf16 *)a.v + bh * N * D;
+    const char *kg = (const char *)a.k + bh * N * ROWB + 32 * wave * ROWB;
+    const char *vg = (const char *)a.v + bh * N * ROWB + 32 * wave * ROWB;
+    const_i32 *rp = (const_i32 *)a.row_ptr;
+    const_i32 *cidx = (const_i32 *)a.col_idx;
 
-    int64_t beg = a.row_ptr[row], end = a.row_ptr[row + 1];
+    int64_t beg = rp[row], end = rp[row + 1];
     end = end < a.col_count ? end : a.col_count;
     beg = beg < 0 ? 0 : beg;
     const int ntile = end > beg ? (int)(end - beg) : 0;
@@ -56,50 +89,30 @@ __global__ __launch_bounds__(128) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
         qf[c] = *reinterpret_cast<const bf16x8 *>(qg + (32 * wave + l32) * D + 16 * c + 8 * hh);
+    // settle the Q loads here (vmcnt(0) through the builtin, which the compiler's own
+    // wait tracking sees), so that no wait for them lands inside the tile loop, where
+    // it would also wait for the in-flight direct loads
+    __builtin_amdgcn_s_waitcnt(0x0f70);
 
-    // per-thread roles in the tile copy
-    const bool vrole = t < 8 * NDG;
-    const int vdg = t % NDG, vh = (t / NDG) & 1, vkc = t / (2 * NDG);
+    // per-lane source offsets of the direct loads, one per swizzle pattern
+    uint32_t voff[NPAT];
+#pragma unroll
+    for (int j = 0; j < NPAT; ++j) {
+        const int r = RPI * j + lane / SLOTS, sl = lane % SLOTS;
+        voff[j] = r * ROWB + 16 * (sl ^ (r % SLOTS));
+    }
+    const uint32_t ks_base = (uint32_t)(uintptr_t)(lds_char *)Ks + 32 * wave * ROWB;
+    const uint32_t vs_base = (uint32_t)(uintptr_t)(lds_char *)Vs + 32 * wave * ROWB;
+    auto issue = [&](const char *tile, uint32_t lds) {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i)
+            dma16(lds + RPI * i * ROWB, voff[i % NPAT], tile + (i / NPAT) * (NPAT * RPI * ROWB));
+    };
+    // byte offset of element (r, col) in a swizzled tile (col a multiple of 4)
+    auto swz = [](int r, int col) { return r * ROWB + 16 * ((col >> 3) ^ (r % SLOTS)) + 2 * (col & 7); };
 
-    u32x4 kreg[KCH], vreg[8];
-    auto fetch = [&](int col) {
-        const __bf16 *kt = kg + (int64_t)col * 64 * D;
-        const __bf16 *vt = vg + (int64_t)col * 64 * D;
-#pragma unroll
-        for (int it = 0; it < KCH; ++it) {
-            const int c = t + 128 * it;
-            kreg[it] = *reinterpret_cast<const u32x4 *>(kt + (c / NDG) * D + (c % NDG) * 8);
-        }
-        if (vrole) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int key = 16 * vkc + (e < 4 ? 4 * vh + e : 8 + 4 * vh + (e - 4));
-                vreg[e] = *reinterpret_cast<const u32x4 *>(vt + key * D + vdg * 8);
-            }
-        }
-    };
-    auto stash = [&]() {
-#pragma unroll
-        for (int it = 0; it < KCH; ++it) {
-            const int c = t + 128 * it;
-            *reinterpret_cast<u32x4 *>(&Ks[(c / NDG) * KS + (c % NDG) * 8]) = kreg[it];
-        }
-        if (vrole) {
-            // 8 keys x 8 d (16-bit) -> 8 d-rows x 8 keys
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                u32x4 lo, hi;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    lo[m] = __builtin_amdgcn_perm(vreg[2 * m + 1][w], vreg[2 * m][w], 0x05040100u);
-                    hi[m] = __builtin_amdgcn_perm(vreg[2 * m + 1][w], vreg[2 * m][w], 0x07060302u);
-                }
-                const int d0 = vdg * 8 + 2 * w;
-                *reinterpret_cast<u32x4 *>(&Vt[d0 * VS + 16 * vkc + 8 * vh]) = lo;
-                *reinterpret_cast<u32x4 *>(&Vt[(d0 + 1) * VS + 16 * vkc + 8 * vh]) = hi;
-            }
-        }
-    };
+    // transposed-read coordinates for the V operand: group g = lane/16, source lane j = 4e + c
+    const int tr_e = (lane & 15) >> 2, tr_c = lane & 3, tr_g = lane >> 4;
 
     f32x16 acc_o[NDT];
 #pragma unroll
@@ -108,21 +121,24 @@ __global__ __launch_bounds__(128) void attn_bf16_kernel(AttnArgs a) {
         for (int v = 0; v < 16; ++v) acc_o[i][v] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    int e_next = 0;
     auto next_valid = [&](int from) {
-        while (from < ntile && (unsigned)a.col_idx[beg + from] >= (unsigned)a.nB) ++from;
+        while (from < ntile && (unsigned)cidx[beg + from] >= (unsigned)a.nB) ++from;
         return from;
     };
-    e_next = next_valid(0);
-    if (e_next < ntile) fetch(a.col_idx[beg + e_next]);
+    int e_cur = next_valid(0);
+    if (e_cur < ntile) {
+        const int64_t col = cidx[beg + e_cur];
+        issue(kg + col * 64 * ROWB, ks_base);
+        issue(vg + col * 64 * ROWB, vs_base);
+    }
 
-    while (e_next < ntile) {
+    while (e_cur < ntile) {
+        const int e_next = next_valid(e_cur + 1);
+        const bool more = e_next < ntile;
+        const int64_t col_next = more ? cidx[beg + e_next] : 0;
+
+        wait_vmcnt<IPW>();          // this wave's K loads landed (its V loads may still fly)
         __syncthreads();
-        stash();
-        __syncthreads();
-        const int e_cur = e_next;
-        e_next = next_valid(e_cur + 1);
-        if (e_next < ntile) fetch(a.col_idx[beg + e_next]);
 
         // S^T = K Q^T for the two 32-key halves
         f32x16 acc_s[2];
@@ -132,55 +148,68 @@ __global__ __launch_bounds__(128) void attn_bf16_kernel(AttnArgs a) {
             for (int v = 0; v < 16; ++v) acc_s[kt][v] = 0.f;
 #pragma unroll
             for (int c = 0; c < D / 16; ++c) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&Ks[(32 * kt + l32) * KS + 16 * c + 8 * hh]);
+                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + swz(32 * kt + l32, 16 * c + 8 * hh));
                 acc_s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], acc_s[kt], 0, 0, 0);
             }
         }
-        // online softmax in the log2 domain; this lane owns query l32
-        float mt = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                acc_s[kt][v] *= a.scale_log2;
-                mt = fmaxf(mt, acc_s[kt][v]);
-            }
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = exp2f(m_run - m_new);
-        m_run = m_new;
-        float ls = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float p = exp2f(acc_s[kt][v] - m_new);
-                acc_s[kt][v] = p;
-                ls += p;
-            }
-        l_run = l_run * alpha + ls;
-#pragma unroll
-        for (int i = 0; i < NDT; ++i)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc_o[i][v] *= alpha;
+        __syncthreads();            // both waves are done with Ks
+        if (more) issue(kg + col_next * 64 * ROWB, ks_base);
 
-        // O^T += V^T P^T over four 16-key chunks
+        // online softmax; this lane owns query l32.  The running max is kept in raw
+        // dot-product units and only moved when a new score exceeds it by more than
+        // kLazy (in log2 units): in between, P = 2^(s*c - m*c) stays below 2^kLazy and
+        // the output needs no rescaling.  The result is the same softmax.
+        float mt = fmaxf(acc_s[0][0], acc_s[0][1]);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int v = (kt == 0 ? 2 : 0); v < 16; v += 2) mt = fmaxf(mt, fmaxf(acc_s[kt][v], acc_s[kt][v + 1]));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const bool grow = (mt - m_run) * a.scale_log2 > kLazy;
+        if (__ballot(grow)) {
+            const float m_new = grow ? mt : m_run;
+            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * a.scale_log2);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < NDT; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc_o[i][v] *= alpha;
+        }
+        const float mc = m_run * a.scale_log2;
+        bf16x8 pf[4];
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
-            const f32x16 &s = acc_s[kc >> 1];
-            const int b = 8 * (kc & 1);
-            u32x4 pw;
-            pw[0] = pack_bf16x2(s[b + 0], s[b + 1]);
-            pw[1] = pack_bf16x2(s[b + 2], s[b + 3]);
-            pw[2] = pack_bf16x2(s[b + 4], s[b + 5]);
-            pw[3] = pack_bf16x2(s[b + 6], s[b + 7]);
-            const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+            f32x8 pv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[kc >> 1][8 * (kc & 1) + e], a.scale_log2, -mc));
+                pv[e] = p;
+                l_run += p;
+            }
+            pf[kc] = __builtin_convertvector(pv, bf16x8);
+        }
+
+        if (more) wait_vmcnt<IPW>(); else wait_vmcnt<0>();   // this wave's V loads landed
+        __syncthreads();
+
+        // O^T += V^T P^T over four 16-key chunks; slot e of chunk kc is key
+        // 16 kc + (e < 4 ? 4 hh + e : 8 + 4 hh + e - 4), matching the accumulators of P
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-                const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(&Vt[(32 * dt + l32) * VS + 16 * kc + 8 * hh]);
-                acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc_o[dt], 0, 0, 0);
+                const int col = 32 * dt + 16 * (tr_g & 1) + 4 * tr_c;
+                const int r0 = 16 * kc + 4 * (tr_g >> 1) + tr_e;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Vs + swz(r0, col)));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Vs + swz(r0 + 8, col)));
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+                acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], acc_o[dt], 0, 0, 0);
             }
         }
+        __syncthreads();            // both waves are done with Vs
+        if (more) issue(vg + col_next * 64 * ROWB, vs_base);
+        e_cur = e_next;
     }
 
     // epilogue: normalise and store; lane owns query l32, d = 32 dt + 8 rr + 4 hh + {0..3}
@@ -192,12 +221,12 @@ __global__ __launch_bounds__(128) void attn_bf16_kernel(AttnArgs a) {
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-            uint2 w;
-            w.x = pack_bf16x2(acc_o[dt][4 * rr + 0] * inv, acc_o[dt][4 * rr + 1] * inv);
-            w.y = pack_bf16x2(acc_o[dt][4 * rr + 2] * inv, acc_o[dt][4 * rr + 3] * inv);
-            *reinterpret_cast<uint2 *>(og + 32 * dt + 8 * rr + 4 * hh) = w;
+            f32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = acc_o[dt][4 * rr + e] * inv;
+            *reinterpret_cast<bf16x4 *>(og + 32 * dt + 8 * rr + 4 * hh) = __builtin_convertvector(w, bf16x4);
         }
-    if (a.lse && hh == 0) a.lse[qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (a.lse && hh == 0) a.lse[qrow] = l_tot > 0.f ? (m_run * a.scale_log2 + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------

@@ -67,6 +67,7 @@ def test_capacity_and_workspace_formulas():
     (dict(heads=-1), B.SPARSE_ATTN_INVALID_ARGUMENT),
     (dict(scale=float("nan")), B.SPARSE_ATTN_INVALID_ARGUMENT),
     (dict(scale=float("inf")), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(scale=-0.1), B.SPARSE_ATTN_INVALID_ARGUMENT),
     (dict(heads=4000, grid=(64, 48, 80)), B.SPARSE_ATTN_UNSUPPORTED),  # worst-case nnz overflows int32
 ])
 def test_bad_shapes_rejected(kw, status):
