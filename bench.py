@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--reading", default="A")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-CSR reference forward")
+    ap.add_argument("--no-select-timing", action="store_true", help="skip the separate selection timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for rocprofv3 counter scaling)")
     ap.add_argument("--pmc-summary", metavar="DIR", help="summarise rocprofv3 --pmc output and exit")
@@ -188,7 +190,7 @@ def main():
     # selection alone, each repetition after a 1 GiB sweep so Q and K do not sit in the last-level cache
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     sel_ms = []
-    for _ in range(10):
+    for _ in range(0 if args.no_select_timing else 10):
         flush.add_(1.0)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
@@ -196,7 +198,7 @@ def main():
         b.record(stream)
         torch.cuda.synchronize()
         sel_ms.append(a.elapsed_time(b))
-    sel_ms_med = sorted(sel_ms)[len(sel_ms) // 2]
+    sel_ms_med = sorted(sel_ms)[len(sel_ms) // 2] if sel_ms else float("nan")
     elt = qd.element_size()
     sel_bytes = 2 * qd.numel() * elt + 4 * (rows + 1) + 4 * nnz
     sel_gbs = sel_bytes / (sel_ms_med * 1e-3) / 1e9
@@ -204,11 +206,11 @@ def main():
     # dense reference: the same forward kernel over the full CSR (every tile kept)
     full_rp = torch.arange(0, rows + 1, dtype=torch.int32, device=dev) * wl.blocks
     full_ci = torch.arange(wl.blocks, dtype=torch.int32, device=dev).repeat(rows)
-    for _ in range(2):
+    for _ in range(0 if args.no_dense else 2):
         B.sparse_attn_forward(shape, qd, kd, vd, full_rp, full_ci, out=out, lse=lse, workspace=bufs.workspace,
                               stream=stream)
     dense_ms = []
-    for _ in range(5):
+    for _ in range(0 if args.no_dense else 5):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         B.sparse_attn_forward(shape, qd, kd, vd, full_rp, full_ci, out=out, lse=lse, workspace=bufs.workspace,
@@ -216,7 +218,7 @@ def main():
         b.record(stream)
         torch.cuda.synchronize()
         dense_ms.append(a.elapsed_time(b))
-    dense_ms_med = sorted(dense_ms)[len(dense_ms) // 2]
+    dense_ms_med = sorted(dense_ms)[len(dense_ms) // 2] if dense_ms else float("nan")
 
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)

@@ -211,6 +211,8 @@ int32_t sparse_attn_forward(const sparse_attn_shape *shape, const void *q, const
     a.out = out;
     a.lse = lse;
     a.rows = d.rows;
+    a.pairs_per_head = (int32_t)((d.nB + 1) / 2);
+    a.n_pairs = d.B * d.H * a.pairs_per_head;
     a.nB = (int32_t)d.nB;
     a.scale_log2 = effective_scale(shape) * kLog2e;
     if (launch_attention(a, shape->dtype, (int)d.D, (hipStream_t)stream)) return SPARSE_ATTN_HIP_ERROR;

@@ -31,8 +31,11 @@ namespace sattn {
 //
 // K and V tiles go from global memory straight into LDS with
 // global_load_lds_dwordx4 (lane p of a wave-wide load lands at M0 + 16 p),
-// row-major, the 16-byte slots of row r XOR-swizzled by r mod (slots per row) so
-// that operand reads of 16 consecutive rows hit 16 different bank groups.  V is
+// row-major, the 16-byte slots of row r XOR-swizzled by swz_key(r).  The key is
+// chosen for both read patterns: the K operand reads one slot of 16 consecutive
+// rows (the keys of rows r mod 16 must all differ), and a transposed V read
+// takes 4 consecutive slots of 4 consecutive rows (the keys of those rows must
+// move the 4-slot group), so that either fills all 64 banks without conflict.  V is
 // read transposed with ds_read_b64_tr_b16: within each 16-lane group, source
 // lane 4e + c names 4 consecutive d of key row e, and output lane i receives the
 // 4 keys at d = i -- the A-operand layout of O^T = V^T P^T.
@@ -52,67 +55,107 @@ __device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, const vo
                  : "memory", "m0");
 }
 
+// XOR key of the 16-byte slots of tile row r (see above): a bijection on r mod 16
+// for 16-slot rows, and on (r >> 1) mod 8 within each row parity for 8-slot rows
+// (128-byte rows: even and odd rows sit on opposite halves of the banks).
+template <int SLOTS> __device__ __forceinline__ int swz_key(int r) {
+    if constexpr (SLOTS == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef const __attribute__((address_space(4))) int32_t const_i32;
 
 template <int D>
-__global__ __launch_bounds__(128, 2) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     constexpr int ROWB = D * 2;                   // bytes per token row
     constexpr int SLOTS = ROWB / 16;              // 16-byte slots per row
     constexpr int RPI = 1024 / ROWB;              // rows written by one wave-wide direct load
-    constexpr int IPW = 32 / RPI;                 // direct loads per wave per tile (each wave: 32 rows)
-    constexpr int NPAT = SLOTS / RPI;             // distinct per-lane swizzle patterns
+    constexpr int IPW = 16 / RPI;                 // direct loads per wave per tensor (each wave: 16 rows)
     constexpr int NDT = D / 32;                   // 32-wide d tiles of the output
-    static_assert(NPAT * RPI * ROWB == ROWB * SLOTS, "pattern period");
-    __shared__ __attribute__((aligned(1024))) char Ks[64 * ROWB];
-    __shared__ __attribute__((aligned(1024))) char Vs[64 * ROWB];
+    constexpr int TILEB = 64 * ROWB;
+    __shared__ __attribute__((aligned(1024))) char Ks[2 * TILEB];
+    __shared__ __attribute__((aligned(1024))) char Vs[2 * TILEB];
 
     const int t = threadIdx.x, lane = t & 63, hh = lane >> 5, l32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int64_t row = xcd_remap(blockIdx.x, a.rows);
-    const int64_t bh = row / a.nB;
+    const int grp = wave >> 1;                    // 0: first query block of the pair, 1: second
+    const int64_t pair = xcd_remap(blockIdx.x, a.n_pairs);
+    const int64_t bh = pair / a.pairs_per_head;
+    const int i0 = (int)(pair % a.pairs_per_head) * 2;
     const int64_t N = (int64_t)a.nB * 64;
-    const __bf16 *qg = (const __bf16 *)a.q + (bh * N + (row % a.nB) * 64) * D;
-    const char *kg = (const char *)a.k + bh * N * ROWB + 32 * wave * ROWB;
-    const char *vg = (const char *)a.v + bh * N * ROWB + 32 * wave * ROWB;
+    const char *kg = (const char *)a.k + bh * N * ROWB + 16 * wave * ROWB;
+    const char *vg = (const char *)a.v + bh * N * ROWB + 16 * wave * ROWB;
     const_i32 *rp = (const_i32 *)a.row_ptr;
     const_i32 *cidx = (const_i32 *)a.col_idx;
 
-    int64_t beg = rp[row], end = rp[row + 1];
-    end = end < a.col_count ? end : a.col_count;
-    beg = beg < 0 ? 0 : beg;
-    const int ntile = end > beg ? (int)(end - beg) : 0;
+    // CSR ranges of the two rows (the second may not exist when nB is odd)
+    const int64_t rowA = bh * a.nB + i0;
+    const bool hasB = i0 + 1 < a.nB;
+    auto clamp_range = [&](int64_t r, int64_t &b, int64_t &e) {
+        b = rp[r];
+        e = rp[r + 1];
+        e = e < a.col_count ? e : a.col_count;
+        b = b < 0 ? 0 : b;
+        if (e < b) e = b;
+    };
+    int64_t begA, endA, begB = 0, endB = 0;
+    clamp_range(rowA, begA, endA);
+    if (hasB) clamp_range(rowA + 1, begB, endB);
+    const bool has_row = grp == 0 || hasB;
 
-    // Q fragments (B operand of S^T): query 32*wave + l32, d = 16c + 8hh .. +7
+    // Q fragments (B operand of S^T): query 32*(wave&1) + l32 of this wave's block, d = 16c + 8hh .. +7
+    const __bf16 *qg = (const __bf16 *)a.q + (bh * N + (int64_t)(i0 + grp) * 64) * D;
     bf16x8 qf[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
-        qf[c] = *reinterpret_cast<const bf16x8 *>(qg + (32 * wave + l32) * D + 16 * c + 8 * hh);
+        qf[c] = has_row ? *reinterpret_cast<const bf16x8 *>(qg + (32 * (wave & 1) + l32) * D + 16 * c + 8 * hh)
+                        : bf16x8{};
     // settle the Q loads here (vmcnt(0) through the builtin, which the compiler's own
-    // wait tracking sees), so that no wait for them lands inside the tile loop, where
-    // it would also wait for the in-flight direct loads
+    // wait tracking sees), so that no wait for them lands inside the tile loop
     __builtin_amdgcn_s_waitcnt(0x0f70);
 
-    // per-lane source offsets of the direct loads, one per swizzle pattern
-    uint32_t voff[NPAT];
+    // per-lane source offsets of the direct loads (this wave covers rows 16 w .. 16 w + 15)
+    uint32_t voff[IPW];
 #pragma unroll
-    for (int j = 0; j < NPAT; ++j) {
-        const int r = RPI * j + lane / SLOTS, sl = lane % SLOTS;
-        voff[j] = r * ROWB + 16 * (sl ^ (r % SLOTS));
+    for (int j = 0; j < IPW; ++j) {
+        const int r = RPI * j + lane / SLOTS, sl = lane % SLOTS;   // row within the wave's 16 (== row mod 16)
+        voff[j] = r * ROWB + 16 * (sl ^ swz_key<SLOTS>(r));
     }
-    const uint32_t ks_base = (uint32_t)(uintptr_t)(lds_char *)Ks + 32 * wave * ROWB;
-    const uint32_t vs_base = (uint32_t)(uintptr_t)(lds_char *)Vs + 32 * wave * ROWB;
-    auto issue = [&](const char *tile, uint32_t lds) {
+    const uint32_t ks0 = (uint32_t)(uintptr_t)(lds_char *)Ks + 16 * wave * ROWB;
+    const uint32_t vs0 = (uint32_t)(uintptr_t)(lds_char *)Vs + 16 * wave * ROWB;
+    auto issue = [&](int64_t col, int buf) {
 #pragma unroll
-        for (int i = 0; i < IPW; ++i)
-            dma16(lds + RPI * i * ROWB, voff[i % NPAT], tile + (i / NPAT) * (NPAT * RPI * ROWB));
+        for (int i = 0; i < IPW; ++i) dma16(ks0 + buf * TILEB + RPI * i * ROWB, voff[i], kg + col * TILEB);
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) dma16(vs0 + buf * TILEB + RPI * i * ROWB, voff[i], vg + col * TILEB);
     };
     // byte offset of element (r, col) in a swizzled tile (col a multiple of 4)
-    auto swz = [](int r, int col) { return r * ROWB + 16 * ((col >> 3) ^ (r % SLOTS)) + 2 * (col & 7); };
-
-    // transposed-read coordinates for the V operand: group g = lane/16, source lane j = 4e + c
+    auto swz = [](int r, int col) { return r * ROWB + 16 * ((col >> 3) ^ swz_key<SLOTS>(r)) + 2 * (col & 7); };
     const int tr_e = (lane & 15) >> 2, tr_c = lane & 3, tr_g = lane >> 4;
+
+    // merged walk over the two rows' ascending lists: each union tile is loaded once for
+    // the 128 queries of the pair and computed by the waves whose row keeps it
+    constexpr int kNone = 0x7fffffff;
+    int64_t ia = begA, ib = begB;
+    int lastA = -1, lastB = -1;
+    auto peek = [&](int64_t &i, int64_t e, int last) {
+        while (i < e) {
+            const int c = cidx[i];
+            if (c > last && c < a.nB) return c;     // ascending, in range
+            ++i;
+        }
+        return kNone;
+    };
+    auto next_union = [&](int &col, bool &inA, bool &inB) {
+        const int cA = peek(ia, endA, lastA), cB = peek(ib, endB, lastB);
+        col = cA < cB ? cA : cB;
+        inA = cA == col && col != kNone;
+        inB = cB == col && col != kNone;
+        if (inA) { lastA = cA; ++ia; }
+        if (inB) { lastB = cB; ++ib; }
+    };
 
     f32x16 acc_o[NDT];
 #pragma unroll
@@ -121,101 +164,98 @@ __global__ __launch_bounds__(128, 2) void attn_bf16_kernel(AttnArgs a) {
         for (int v = 0; v < 16; ++v) acc_o[i][v] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    auto next_valid = [&](int from) {
-        while (from < ntile && (unsigned)cidx[beg + from] >= (unsigned)a.nB) ++from;
-        return from;
-    };
-    int e_cur = next_valid(0);
-    if (e_cur < ntile) {
-        const int64_t col = cidx[beg + e_cur];
-        issue(kg + col * 64 * ROWB, ks_base);
-        issue(vg + col * 64 * ROWB, vs_base);
+    int col;
+    bool inA, inB;
+    next_union(col, inA, inB);
+    if (col != kNone) issue(col, 0);
+    int buf = 0;
+    while (col != kNone) {
+        int col_n;
+        bool inA_n, inB_n;
+        next_union(col_n, inA_n, inB_n);
+
+        wait_vmcnt<0>();            // this wave's part of the current tile has landed
+        __syncthreads();            // ... and everyone's; everyone is done with the other buffer
+        if (col_n != kNone) issue(col_n, buf ^ 1);
+
+        if (grp ? inB : inA) {
+            const char *K = Ks + buf * TILEB;
+            const char *V = Vs + buf * TILEB;
+            // S^T = K Q^T for the two 32-key halves
+            f32x16 acc_s[2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc_s[kt][v] = 0.f;
+#pragma unroll
+                for (int c = 0; c < D / 16; ++c) {
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(K + swz(32 * kt + l32, 16 * c + 8 * hh));
+                    acc_s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], acc_s[kt], 0, 0, 0);
+                }
+            }
+            // online softmax; this lane owns query l32.  The running max is kept in raw
+            // dot-product units and only moved when a new score exceeds it by more than
+            // kLazy (in log2 units): in between, P = 2^(s*c - m*c) stays below 2^kLazy and
+            // the output needs no rescaling.  The result is the same softmax.
+            float mt = fmaxf(acc_s[0][0], acc_s[0][1]);
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int v = (kt == 0 ? 2 : 0); v < 16; v += 2) mt = fmaxf(mt, fmaxf(acc_s[kt][v], acc_s[kt][v + 1]));
+            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+            const bool grow = (mt - m_run) * a.scale_log2 > kLazy;
+            if (__ballot(grow)) {
+                const float m_new = grow ? mt : m_run;
+                const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * a.scale_log2);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int i = 0; i < NDT; ++i)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc_o[i][v] *= alpha;
+            }
+            const float mc = m_run * a.scale_log2;
+            bf16x8 pf[4];
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) {
+                f32x8 pv;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[kc >> 1][8 * (kc & 1) + e], a.scale_log2, -mc));
+                pf[kc] = __builtin_convertvector(pv, bf16x8);
+                // the row sum takes the same bf16-rounded P that enters P V
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){pf[kc][2 * e], pf[kc][2 * e + 1]}, kOnes2, l_run,
+                                                            false);
+            }
+            // O^T += V^T P^T over four 16-key chunks; slot e of chunk kc is key
+            // 16 kc + (e < 4 ? 4 hh + e : 8 + 4 hh + e - 4), matching the accumulators of P
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    const int cc = 32 * dt + 16 * (tr_g & 1) + 4 * tr_c;
+                    const int r0 = 16 * kc + 4 * (tr_g >> 1) + tr_e;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(V + swz(r0, cc)));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(V + swz(r0 + 8, cc)));
+                    const bf16x8 vf =
+                        __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+                    acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], acc_o[dt], 0, 0, 0);
+                }
+            }
+        }
+        buf ^= 1;
+        col = col_n;
+        inA = inA_n;
+        inB = inB_n;
     }
 
-    while (e_cur < ntile) {
-        const int e_next = next_valid(e_cur + 1);
-        const bool more = e_next < ntile;
-        const int64_t col_next = more ? cidx[beg + e_next] : 0;
-
-        wait_vmcnt<IPW>();          // this wave's K loads landed (its V loads may still fly)
-        __syncthreads();
-
-        // S^T = K Q^T for the two 32-key halves
-        f32x16 acc_s[2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc_s[kt][v] = 0.f;
-#pragma unroll
-            for (int c = 0; c < D / 16; ++c) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + swz(32 * kt + l32, 16 * c + 8 * hh));
-                acc_s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], acc_s[kt], 0, 0, 0);
-            }
-        }
-        __syncthreads();            // both waves are done with Ks
-        if (more) issue(kg + col_next * 64 * ROWB, ks_base);
-
-        // online softmax; this lane owns query l32.  The running max is kept in raw
-        // dot-product units and only moved when a new score exceeds it by more than
-        // kLazy (in log2 units): in between, P = 2^(s*c - m*c) stays below 2^kLazy and
-        // the output needs no rescaling.  The result is the same softmax.
-        float mt = fmaxf(acc_s[0][0], acc_s[0][1]);
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int v = (kt == 0 ? 2 : 0); v < 16; v += 2) mt = fmaxf(mt, fmaxf(acc_s[kt][v], acc_s[kt][v + 1]));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const bool grow = (mt - m_run) * a.scale_log2 > kLazy;
-        if (__ballot(grow)) {
-            const float m_new = grow ? mt : m_run;
-            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * a.scale_log2);
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int i = 0; i < NDT; ++i)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc_o[i][v] *= alpha;
-        }
-        const float mc = m_run * a.scale_log2;
-        bf16x8 pf[4];
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-            f32x8 pv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[kc >> 1][8 * (kc & 1) + e], a.scale_log2, -mc));
-                pv[e] = p;
-                l_run += p;
-            }
-            pf[kc] = __builtin_convertvector(pv, bf16x8);
-        }
-
-        if (more) wait_vmcnt<IPW>(); else wait_vmcnt<0>();   // this wave's V loads landed
-        __syncthreads();
-
-        // O^T += V^T P^T over four 16-key chunks; slot e of chunk kc is key
-        // 16 kc + (e < 4 ? 4 hh + e : 8 + 4 hh + e - 4), matching the accumulators of P
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const int col = 32 * dt + 16 * (tr_g & 1) + 4 * tr_c;
-                const int r0 = 16 * kc + 4 * (tr_g >> 1) + tr_e;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Vs + swz(r0, col)));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Vs + swz(r0 + 8, col)));
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-                acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], acc_o[dt], 0, 0, 0);
-            }
-        }
-        __syncthreads();            // both waves are done with Vs
-        if (more) issue(vg + col_next * 64 * ROWB, vs_base);
-        e_cur = e_next;
-    }
-
+    if (!has_row) return;
     // epilogue: normalise and store; lane owns query l32, d = 32 dt + 8 rr + 4 hh + {0..3}
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int64_t qrow = bh * N + (row % a.nB) * 64 + 32 * wave + l32;
+    const int64_t qrow = bh * N + (int64_t)(i0 + grp) * 64 + 32 * (wave & 1) + l32;
     __bf16 *og = (__bf16 *)a.out + qrow * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -347,11 +387,11 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
 }
 
 int launch_attention(const AttnArgs &a, int dtype, int d, hipStream_t s) {
-    const dim3 grid((unsigned)a.rows), block(128);
+    const dim3 pgrid((unsigned)a.n_pairs), pblock(256), grid((unsigned)a.rows), block(128);
     if (dtype == 1 && d == 128)
-        attn_bf16_kernel<128><<<grid, block, 0, s>>>(a);
+        attn_bf16_kernel<128><<<pgrid, pblock, 0, s>>>(a);
     else if (dtype == 1 && d == 64)
-        attn_bf16_kernel<64><<<grid, block, 0, s>>>(a);
+        attn_bf16_kernel<64><<<pgrid, pblock, 0, s>>>(a);
     else if (dtype == 0 && d == 128)
         attn_f32_kernel<128><<<grid, block, 0, s>>>(a);
     else

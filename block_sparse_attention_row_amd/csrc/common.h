@@ -7,6 +7,7 @@
 namespace sattn {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) float f32x8;
@@ -64,5 +65,8 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t n) {
     const int64_t per = n / kXcd, rem = n % kXcd;
     return x * per + (x < rem ? x : rem) + k;
 }
+
+// (1, 1) in bf16, for row sums with v_dot2_f32_bf16
+#define kOnes2 ((bf16x2){(__bf16)1.0f, (__bf16)1.0f})
 
 }  // namespace sattn

@@ -32,6 +32,8 @@ struct AttnArgs {
     void *out;
     float *lse;               // nullable
     int64_t rows;             // B*H*nB
+    int64_t n_pairs;          // B*H*pairs_per_head (query-block pairs of the bf16 kernel)
+    int32_t pairs_per_head;   // ceil(nB / 2)
     int32_t nB;
     float scale_log2;         // softmax scale * log2(e)
 };

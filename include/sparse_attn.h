@@ -133,10 +133,12 @@ int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_sel
  *
  *   q, k, v     device, [B, H, N, d] in shape->dtype.
  *   row_ptr     device, int32 [B*H*nB + 1], non-decreasing, row_ptr[0] = 0.
- *   col_idx     device, int32 [col_count]; each row's entries are key-block
- *               indices in [0, nB) without repeats (any order).  Entries
- *               outside [0, nB) are skipped; row ends beyond col_count are
- *               clipped to col_count.
+ *   col_idx     device, int32 [col_count]; each row's entries are strictly
+ *               ascending key-block indices in [0, nB) (the order
+ *               sparse_attn_select and sparse_attn_mask_to_csr produce).  An
+ *               entry outside [0, nB) or not above the row's previous accepted
+ *               entry is skipped; row ends beyond col_count are clipped to
+ *               col_count.
  *   out         device, [B, H, N, d] in shape->dtype: for each query token,
  *               softmax(scale * q k^T) v over the tokens of the row's key
  *               blocks.  A row with no block gives zeros.

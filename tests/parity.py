@@ -26,7 +26,10 @@ from block_sparse_attention_row_amd.synth import Workload
 R1_BAND = 1e-4
 R2_REL = 1e-5
 TOL = {"bf16": 2e-2, "f32": 1e-4}
-LSE_TOL = {"bf16": 2e-3, "f32": 1e-4}
+# The bf16 path normalises with the sum of the same bf16-rounded weights that enter
+# P V, so its log-sum-exp carries up to the bf16 unit roundoff 2^-8 ~ 3.9e-3 of
+# relative error in the normaliser; fp32 keeps fp32 weights.
+LSE_TOL = {"bf16": 5e-3, "f32": 1e-4}
 
 
 def to_device(*ts):
