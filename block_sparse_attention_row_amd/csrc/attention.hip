@@ -21,6 +21,8 @@
 //     transpose is done in registers while the tile is copied to LDS);
 //   * the next tile's K and V are fetched into registers while the current
 //     tile is computed.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -67,14 +69,157 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef const __attribute__((address_space(4))) int32_t const_i32;
 
+// Tile geometry of the bf16 kernel.
+template <int D> struct TileGeo {
+    static constexpr int ROWB = D * 2;            // bytes per token row
+    static constexpr int SLOTS = ROWB / 16;       // 16-byte slots per row
+    static constexpr int RPI = 1024 / ROWB;       // rows written by one wave-wide direct load
+    static constexpr int IPW = 16 / RPI;          // direct loads per wave per tensor (each wave: 16 rows)
+    static constexpr int NDT = D / 32;            // 32-wide d tiles of the output
+    static constexpr int TILEB = 64 * ROWB;
+    // byte offset of element (r, col) in a swizzled tile (col a multiple of 4)
+    static __device__ __forceinline__ int swz(int r, int col) {
+        return r * ROWB + 16 * ((col >> 3) ^ swz_key<SLOTS>(r)) + 2 * (col & 7);
+    }
+};
+
+// S^T = K Q^T for the two 32-key halves of a tile (K from LDS).
+template <int D>
+__device__ __forceinline__ void tile_scores(const char *K, const bf16x8 *qf, int l32, int hh, f32x16 *acc_s) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc_s[kt][v] = 0.f;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(K + TileGeo<D>::swz(32 * kt + l32, 16 * c + 8 * hh));
+            acc_s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], acc_s[kt], 0, 0, 0);
+        }
+    }
+}
+
+// Online-softmax bookkeeping for one tile of raw scores; this lane owns one query.
+// The running max is kept in raw dot-product units and only moved when a new score
+// exceeds it by more than kLazy (in log2 units): in between, P = 2^(s*c - m*c) stays
+// below 2^kLazy and the output needs no rescaling.  The result is the same softmax.
+template <int NDT>
+__device__ __forceinline__ void tile_rescale(const f32x16 *acc_s, float c, float &m_run, float &l_run,
+                                             f32x16 *acc_o) {
+    float mt = fmaxf(acc_s[0][0], acc_s[0][1]);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = (kt == 0 ? 2 : 0); v < 16; v += 2) mt = fmaxf(mt, fmaxf(acc_s[kt][v], acc_s[kt][v + 1]));
+    mt = pair_max(mt);
+    const bool grow = (mt - m_run) * c > kLazy;
+    if (__ballot(grow)) {
+        const float m_new = grow ? mt : m_run;
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < NDT; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc_o[i][v] *= alpha;
+    }
+}
+
+// P = 2^(s*c - m*c) as bf16 B operands; the row sum takes the same bf16-rounded P.
+__device__ __forceinline__ void tile_probs(const f32x16 *acc_s, float c, float mc, float &l_run, bf16x8 *pf) {
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+        f32x8 pv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[kc >> 1][8 * (kc & 1) + e], c, -mc));
+        pf[kc] = __builtin_convertvector(pv, bf16x8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            l_run = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){pf[kc][2 * e], pf[kc][2 * e + 1]}, kOnes2, l_run, false);
+    }
+}
+
+// O^T += V^T P^T over four 16-key chunks; slot e of chunk kc is key
+// 16 kc + (e < 4 ? 4 hh + e : 8 + 4 hh + e - 4), matching the accumulators of P.
+// The transposed V reads run two MFMAs ahead of their use.
+template <int D>
+__device__ __forceinline__ bf16x8 v_frag(const char *V, int lane, int kc, int dt) {
+    const int tr_e = (lane & 15) >> 2, tr_c = lane & 3, tr_g = lane >> 4;
+    const int cc = 32 * dt + 16 * (tr_g & 1) + 4 * tr_c;
+    const int r0 = 16 * kc + 4 * (tr_g >> 1) + tr_e;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(V + TileGeo<D>::swz(r0, cc)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(V + TileGeo<D>::swz(r0 + 8, cc)));
+    return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+}
+
+template <int D>
+__device__ __forceinline__ void tile_pv(const char *V, const bf16x8 *pf, int lane, f32x16 *acc_o) {
+    constexpr int NDT = TileGeo<D>::NDT, NM = 4 * NDT;
+    bf16x8 vf[3];
+    vf[0] = v_frag<D>(V, lane, 0, 0);
+    vf[1] = v_frag<D>(V, lane, 1 / NDT, 1 % NDT);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+        if (i + 2 < NM) vf[(i + 2) % 3] = v_frag<D>(V, lane, (i + 2) / NDT, (i + 2) % NDT);
+        acc_o[i % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pf[i / NDT], acc_o[i % NDT], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Scores of the next tile (MFMA) interleaved with the probabilities of the current
+// one (VALU): each score MFMA is grouped with an equal share of the softmax work, and the K reads run two MFMAs ahead.
+template <int D>
+__device__ __forceinline__ void tile_scores_probs(const char *K, const bf16x8 *qf, int l32, int hh, f32x16 *sn,
+                                                  const f32x16 *sc, float c, float mc, float &l_run, bf16x8 *pf) {
+    constexpr int NC = D / 16, NM = 2 * NC;       // score MFMAs per tile
+    constexpr int PER = 32 / NM;                  // probabilities per MFMA group
+    // MFMA i works on key half i & 1 and d chunk i >> 1, so consecutive MFMAs feed
+    // different accumulators and never wait on each other
+    auto kfrag = [&](int i) {
+        const int kt = i & 1, cq = i >> 1;
+        return *reinterpret_cast<const bf16x8 *>(K + TileGeo<D>::swz(32 * kt + l32, 16 * cq + 8 * hh));
+    };
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        sn[0][v] = 0.f;
+        sn[1][v] = 0.f;
+    }
+    bf16x8 kf[3];
+    kf[0] = kfrag(0);
+    kf[1] = kfrag(1);
+    f32x8 pv;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+        if (i + 2 < NM) kf[(i + 2) % 3] = kfrag(i + 2);
+        sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[i >> 1], sn[i & 1], 0, 0, 0);
+        // probabilities PER*i .. PER*i + PER - 1 of the current tile (8 per 16-key chunk)
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = PER * i + u, kc = e >> 3;
+            pv[e & 7] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kc >> 1][8 * (kc & 1) + (e & 7)], c, -mc));
+            if ((e & 7) == 7) {
+                pf[kc] = __builtin_convertvector(pv, bf16x8);
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){pf[kc][2 * w], pf[kc][2 * w + 1]}, kOnes2,
+                                                            l_run, false);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Workgroup of 4 waves = a pair of neighbouring query blocks of one (batch, head);
+// waves 2g and 2g+1 own queries 0-31 and 32-63 of block g.  The pair walks the
+// union of its two ascending CSR rows; each union tile is loaded once and computed
+// by the waves whose row keeps it.  The walk is software-pipelined one tile deep:
+// while the scores of tile j+1 are formed on MFMA, the softmax of tile j runs on
+// the VALU, then P V of tile j follows.  K runs two tiles ahead of use and V one,
+// in two LDS buffers each.
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
-    constexpr int ROWB = D * 2;                   // bytes per token row
-    constexpr int SLOTS = ROWB / 16;              // 16-byte slots per row
-    constexpr int RPI = 1024 / ROWB;              // rows written by one wave-wide direct load
-    constexpr int IPW = 16 / RPI;                 // direct loads per wave per tensor (each wave: 16 rows)
-    constexpr int NDT = D / 32;                   // 32-wide d tiles of the output
-    constexpr int TILEB = 64 * ROWB;
+    using G = TileGeo<D>;
+    constexpr int ROWB = G::ROWB, SLOTS = G::SLOTS, RPI = G::RPI, IPW = G::IPW, NDT = G::NDT, TILEB = G::TILEB;
     __shared__ __attribute__((aligned(1024))) char Ks[2 * TILEB];
     __shared__ __attribute__((aligned(1024))) char Vs[2 * TILEB];
 
@@ -89,6 +234,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     const char *vg = (const char *)a.v + bh * N * ROWB + 16 * wave * ROWB;
     const_i32 *rp = (const_i32 *)a.row_ptr;
     const_i32 *cidx = (const_i32 *)a.col_idx;
+    const float c = a.scale_log2;
 
     // CSR ranges of the two rows (the second may not exist when nB is odd)
     const int64_t rowA = bh * a.nB + i0;
@@ -109,9 +255,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     const __bf16 *qg = (const __bf16 *)a.q + (bh * N + (int64_t)(i0 + grp) * 64) * D;
     bf16x8 qf[D / 16];
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-        qf[c] = has_row ? *reinterpret_cast<const bf16x8 *>(qg + (32 * (wave & 1) + l32) * D + 16 * c + 8 * hh)
-                        : bf16x8{};
+    for (int cq = 0; cq < D / 16; ++cq)
+        qf[cq] = has_row ? *reinterpret_cast<const bf16x8 *>(qg + (32 * (wave & 1) + l32) * D + 16 * cq + 8 * hh)
+                         : bf16x8{};
     // settle the Q loads here (vmcnt(0) through the builtin, which the compiler's own
     // wait tracking sees), so that no wait for them lands inside the tile loop
     __builtin_amdgcn_s_waitcnt(0x0f70);
@@ -125,36 +271,36 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     }
     const uint32_t ks0 = (uint32_t)(uintptr_t)(lds_char *)Ks + 16 * wave * ROWB;
     const uint32_t vs0 = (uint32_t)(uintptr_t)(lds_char *)Vs + 16 * wave * ROWB;
-    auto issue = [&](int64_t col, int buf) {
+    auto issue_k = [&](int64_t col, int buf) {
 #pragma unroll
         for (int i = 0; i < IPW; ++i) dma16(ks0 + buf * TILEB + RPI * i * ROWB, voff[i], kg + col * TILEB);
+    };
+    auto issue_v = [&](int64_t col, int buf) {
 #pragma unroll
         for (int i = 0; i < IPW; ++i) dma16(vs0 + buf * TILEB + RPI * i * ROWB, voff[i], vg + col * TILEB);
     };
-    // byte offset of element (r, col) in a swizzled tile (col a multiple of 4)
-    auto swz = [](int r, int col) { return r * ROWB + 16 * ((col >> 3) ^ swz_key<SLOTS>(r)) + 2 * (col & 7); };
-    const int tr_e = (lane & 15) >> 2, tr_c = lane & 3, tr_g = lane >> 4;
 
-    // merged walk over the two rows' ascending lists: each union tile is loaded once for
-    // the 128 queries of the pair and computed by the waves whose row keeps it
+    // merged walk over the two rows' ascending lists (entries out of range or not
+    // ascending are skipped)
     constexpr int kNone = 0x7fffffff;
     int64_t ia = begA, ib = begB;
     int lastA = -1, lastB = -1;
     auto peek = [&](int64_t &i, int64_t e, int last) {
         while (i < e) {
-            const int c = cidx[i];
-            if (c > last && c < a.nB) return c;     // ascending, in range
+            const int cc = cidx[i];
+            if (cc > last && cc < a.nB) return cc;
             ++i;
         }
         return kNone;
     };
-    auto next_union = [&](int &col, bool &inA, bool &inB) {
+    // next union tile: its column and whether this wave's row keeps it
+    auto next_union = [&](int &col, bool &mine) {
         const int cA = peek(ia, endA, lastA), cB = peek(ib, endB, lastB);
         col = cA < cB ? cA : cB;
-        inA = cA == col && col != kNone;
-        inB = cB == col && col != kNone;
+        const bool inA = cA == col && col != kNone, inB = cB == col && col != kNone;
         if (inA) { lastA = cA; ++ia; }
         if (inB) { lastB = cB; ++ib; }
+        mine = grp ? inB : inA;
     };
 
     f32x16 acc_o[NDT];
@@ -164,96 +310,58 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         for (int v = 0; v < 16; ++v) acc_o[i][v] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    int col;
-    bool inA, inB;
-    next_union(col, inA, inB);
-    if (col != kNone) issue(col, 0);
-    int buf = 0;
-    while (col != kNone) {
-        int col_n;
-        bool inA_n, inB_n;
-        next_union(col_n, inA_n, inB_n);
+    // tiles j (scores pending), j+1 (K resident), j+2 (lookahead)
+    int col0, col1, col2;
+    bool mine0, mine1, mine2;
+    next_union(col0, mine0);
+    next_union(col1, mine1);
+    f32x16 sa[2], sb[2];
+    if (col0 != kNone) {
+        issue_k(col0, 0);
+        issue_v(col0, 0);
+        if (col1 != kNone) issue_k(col1, 1);
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (mine0) tile_scores<D>(Ks, qf, l32, hh, sa);
+    }
+    // One pipeline step for tile j with j & 1 == BJ: the scores of tile j are in sc,
+    // those of tile j+1 go to sn; buffer offsets are compile-time constants.
+    auto step = [&](auto bj_tag, f32x16 *sc, f32x16 *sn) {
+        constexpr int BJ = decltype(bj_tag)::value;
+        next_union(col2, mine2);
+        wait_vmcnt<0>();            // this wave's part of K(j+1) and V(j) has landed
+        __syncthreads();            // ... and everyone's; K(j) and V(j-1) are free
+        if (col2 != kNone) issue_k(col2, BJ);
+        if (col1 != kNone) issue_v(col1, BJ ^ 1);
 
-        wait_vmcnt<0>();            // this wave's part of the current tile has landed
-        __syncthreads();            // ... and everyone's; everyone is done with the other buffer
-        if (col_n != kNone) issue(col_n, buf ^ 1);
-
-        if (grp ? inB : inA) {
-            const char *K = Ks + buf * TILEB;
-            const char *V = Vs + buf * TILEB;
-            // S^T = K Q^T for the two 32-key halves
-            f32x16 acc_s[2];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc_s[kt][v] = 0.f;
-#pragma unroll
-                for (int c = 0; c < D / 16; ++c) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(K + swz(32 * kt + l32, 16 * c + 8 * hh));
-                    acc_s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], acc_s[kt], 0, 0, 0);
-                }
-            }
-            // online softmax; this lane owns query l32.  The running max is kept in raw
-            // dot-product units and only moved when a new score exceeds it by more than
-            // kLazy (in log2 units): in between, P = 2^(s*c - m*c) stays below 2^kLazy and
-            // the output needs no rescaling.  The result is the same softmax.
-            float mt = fmaxf(acc_s[0][0], acc_s[0][1]);
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int v = (kt == 0 ? 2 : 0); v < 16; v += 2) mt = fmaxf(mt, fmaxf(acc_s[kt][v], acc_s[kt][v + 1]));
-            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-            const bool grow = (mt - m_run) * a.scale_log2 > kLazy;
-            if (__ballot(grow)) {
-                const float m_new = grow ? mt : m_run;
-                const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * a.scale_log2);
-                m_run = m_new;
-                l_run *= alpha;
-#pragma unroll
-                for (int i = 0; i < NDT; ++i)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) acc_o[i][v] *= alpha;
-            }
-            const float mc = m_run * a.scale_log2;
-            bf16x8 pf[4];
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) {
-                f32x8 pv;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[kc >> 1][8 * (kc & 1) + e], a.scale_log2, -mc));
-                pf[kc] = __builtin_convertvector(pv, bf16x8);
-                // the row sum takes the same bf16-rounded P that enters P V
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    l_run = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){pf[kc][2 * e], pf[kc][2 * e + 1]}, kOnes2, l_run,
-                                                            false);
-            }
-            // O^T += V^T P^T over four 16-key chunks; slot e of chunk kc is key
-            // 16 kc + (e < 4 ? 4 hh + e : 8 + 4 hh + e - 4), matching the accumulators of P
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    const int cc = 32 * dt + 16 * (tr_g & 1) + 4 * tr_c;
-                    const int r0 = 16 * kc + 4 * (tr_g >> 1) + tr_e;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(V + swz(r0, cc)));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(V + swz(r0 + 8, cc)));
-                    const bf16x8 vf =
-                        __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-                    acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], acc_o[dt], 0, 0, 0);
-                }
-            }
+        float mc = 0.f;
+        if (mine0) {
+            tile_rescale<NDT>(sc, c, m_run, l_run, acc_o);
+            mc = m_run * c;
         }
-        buf ^= 1;
-        col = col_n;
-        inA = inA_n;
-        inB = inB_n;
+        bf16x8 pf[4];
+        if (mine0 && mine1) {
+            tile_scores_probs<D>(Ks + (BJ ^ 1) * TILEB, qf, l32, hh, sn, sc, c, mc, l_run, pf);
+        } else if (mine1) {
+            tile_scores<D>(Ks + (BJ ^ 1) * TILEB, qf, l32, hh, sn);
+        } else if (mine0) {
+            tile_probs(sc, c, mc, l_run, pf);
+        }
+        if (mine0) tile_pv<D>(Vs + BJ * TILEB, pf, lane, acc_o);
+        col0 = col1;
+        mine0 = mine1;
+        col1 = col2;
+        mine1 = mine2;
+    };
+    while (col0 != kNone) {
+        step(std::integral_constant<int, 0>{}, sa, sb);
+        if (col0 == kNone) break;
+        step(std::integral_constant<int, 1>{}, sb, sa);
     }
 
     if (!has_row) return;
     // epilogue: normalise and store; lane owns query l32, d = 32 dt + 8 rr + 4 hh + {0..3}
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int64_t qrow = bh * N + (int64_t)(i0 + grp) * 64 + 32 * (wave & 1) + l32;
     __bf16 *og = (__bf16 *)a.out + qrow * D;
@@ -266,7 +374,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
             for (int e = 0; e < 4; ++e) w[e] = acc_o[dt][4 * rr + e] * inv;
             *reinterpret_cast<bf16x4 *>(og + 32 * dt + 8 * rr + 4 * hh) = __builtin_convertvector(w, bf16x4);
         }
-    if (a.lse && hh == 0) a.lse[qrow] = l_tot > 0.f ? (m_run * a.scale_log2 + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (a.lse && hh == 0) a.lse[qrow] = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -339,7 +447,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
                 acc_s[kt2][v] *= a.scale_log2;
                 mt = fmaxf(mt, acc_s[kt2][v]);
             }
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        mt = pair_max(mt);
         const float m_new = fmaxf(m_run, mt);
         const float alpha = exp2f(m_run - m_new);
         m_run = m_new;

@@ -56,6 +56,16 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
+// Combine each lane with its partner l ^ 32 (v_permlane32_swap: no LDS round trip).
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Bijective mapping of a flat work index so that the workgroups the hardware
 // sends to one XCD (dispatch is round-robin over the 8 XCDs) receive a
 // contiguous range of work items: neighbouring rows then share that XCD's L2.
