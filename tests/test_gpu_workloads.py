@@ -1,0 +1,75 @@
+"""GPU parity at the full sizes of the four video-DiT workloads (plus the tiny
+fp32 one in test_gpu_parity.py), in the launch configuration bench.py times.
+
+Selection: every row of every head is compared with the oracle under the
+mask rule in parity.py.  Attention: sampled query blocks (2 heads x 32 blocks,
+drawn with rng(1); for the jittered-threshold workload the heads with the
+lowest and highest threshold) under the oracle's block list, and the same
+rows under the GPU's own block list where the two masks agree.
+"""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_attention_row_amd import binding as B
+from block_sparse_attention_row_amd.synth import WORKLOADS, make_inputs
+
+from . import parity as P
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+BIG = ["wan13b_480p", "wan14b_720p", "hunyuan_720p", "long_video"]
+
+
+def _log(msg):
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", BIG)
+def test_full_size_workload(name):
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    wl = WORKLOADS[name]
+    _log(f"[case] {name}: drawing inputs ({wl.description})")
+    q, k, v, thr = make_inputs(wl, "A")
+    qd, kd, vd = P.to_device(q, k, v)
+    shape = P.shape_for(wl)
+    bufs = B.alloc_buffers(shape)
+
+    # the GPU path as bench.py runs it: select, then forward on the same buffers
+    head_thr = None if wl.head_threshold_range is None else [float(x) for x in thr]
+    rp, ci = B.sparse_attn_select(shape, qd, kd, threshold=float(np.float32(wl.threshold)),
+                                  head_thresholds=head_thr, window=wl.window, buffers=bufs)
+    out_g = torch.empty_like(qd)
+    lse_g = torch.empty(qd.shape[:3], dtype=torch.float32, device="cuda")
+    B.sparse_attn_forward(shape, qd, kd, vd, rp, ci, out=out_g, lse=lse_g, workspace=bufs.workspace)
+    torch.cuda.synchronize()
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    ci_h = ci[:int(rp_h[-1])].cpu().numpy()
+    gmask = P.check_csr(rp_h, ci_h, wl.blocks)
+    rows = wl.batch * wl.heads * wl.blocks
+    _log(f"GPU done: nnz={int(rp_h[-1])} kept={rp_h[-1] / (rows * wl.blocks):.4f}")
+
+    # exact fp32 copies for the oracle, made once
+    q32, k32, v32 = (t.float().numpy() for t in (q, k, v))
+    qbar, kbar, keep = P.oracle_select_full(wl, q32, k32, thr)
+    rep = P.compare_masks(gmask, keep, qbar, kbar, wl, thr)
+    _log("mask: " + P.fmt(rep))
+    assert rep.unexcused == 0 and rep.window_missing == 0 and rep.invariant_fail == 0
+
+    sample = P.sample_rows(wl, thr)
+    orp, oci = oracle.csr_from_mask(keep != 0)
+    out_o, lse_o = P.gpu_forward(wl, qd, kd, vd, orp, oci)
+    err, lerr = P.compare_rows(wl, out_o, lse_o, q32, k32, v32, orp, oci, sample)
+    _log(f"forward (oracle CSR), {len(sample)} sampled blocks: max|err|={err:.3e} lse max|err|={lerr:.3e}")
+    assert err <= P.TOL[wl.dtype] and lerr <= P.LSE_TOL[wl.dtype]
+
+    agree = sample[~(gmask[sample] != (keep[sample] != 0)).any(axis=1)]
+    err2, lerr2 = P.compare_rows(wl, out_g, lse_g, q32, k32, v32, orp, oci, agree)
+    _log(f"forward (GPU CSR), {len(agree)} sampled blocks with equal masks: max|err|={err2:.3e} "
+         f"lse max|err|={lerr2:.3e}")
+    assert err2 <= P.TOL[wl.dtype] and lerr2 <= P.LSE_TOL[wl.dtype]
