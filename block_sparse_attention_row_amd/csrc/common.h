@@ -56,6 +56,69 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
+// DPP lane moves within 16-lane rows (no LDS round trip); lanes without a source read 0.
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+// Max / sum over the whole wave, returned uniformly (reduced per row with DPP, then
+// the four row results read out with v_readlane).
+__device__ __forceinline__ float wave_max_u(float v) {
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    v = fmaxf(v, dpp<kDppXor2>(v));
+    v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp<kDppMirror>(v));
+    return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_u(float v) {
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    v += dpp<kDppHalfMirror>(v);
+    v += dpp<kDppMirror>(v);
+    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+// Inclusive prefix sum over the 64 lanes (lane order).
+__device__ __forceinline__ float wave_prefix_sum(float v, int lane) {
+    v += dpp<kDppShr1>(v);
+    v += dpp<kDppShr2>(v);
+    v += dpp<kDppShr4>(v);
+    v += dpp<kDppShr8>(v);
+    const float r0 = lane_value(v, 15), r1 = lane_value(v, 31), r2 = lane_value(v, 47);
+    const int row = lane >> 4;
+    return v + (row >= 1 ? r0 : 0.f) + (row >= 2 ? r1 : 0.f) + (row >= 3 ? r2 : 0.f);
+}
+
+template <int CTRL> __device__ __forceinline__ uint32_t dppu(uint32_t v, uint32_t fill) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)v, CTRL, 0xF, 0xF, false);
+}
+// Unsigned min / max over the wave, returned uniformly.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = min(v, dppu<kDppXor1>(v, v));
+    v = min(v, dppu<kDppXor2>(v, v));
+    v = min(v, dppu<kDppHalfMirror>(v, v));
+    v = min(v, dppu<kDppMirror>(v, v));
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return min(min(a, b), min(c, d));
+}
+__device__ __forceinline__ uint32_t wave_max_u32_u(uint32_t v) {
+    v = max(v, dppu<kDppXor1>(v, v));
+    v = max(v, dppu<kDppXor2>(v, v));
+    v = max(v, dppu<kDppHalfMirror>(v, v));
+    v = max(v, dppu<kDppMirror>(v, v));
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return max(max(a, b), max(c, d));
+}
+
 // Combine each lane with its partner l ^ 32 (v_permlane32_swap: no LDS round trip).
 __device__ __forceinline__ float pair_max(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -13,7 +13,7 @@ namespace sattn {
 // External dense uint8 mask [rows][nB] -> bitmask rows + counts; one wave per row.
 __global__ __launch_bounds__(256) void mask_bits_kernel(const uint8_t *__restrict__ mask, int64_t rows, int32_t nB,
                                                         int32_t nW, uint64_t *__restrict__ bits,
-                                                        int32_t *__restrict__ counts) {
+                                                        int32_t *__restrict__ counts, int32_t *__restrict__ chunk_sums) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
@@ -26,84 +26,103 @@ __global__ __launch_bounds__(256) void mask_bits_kernel(const uint8_t *__restric
         count += __popcll(b);
         if (lane == 0) bits[row * nW + e] = b;
     }
-    if (lane == 0) counts[row] = count;
+    if (lane == 0) {
+        counts[row] = count;
+        atomicAdd(chunk_sums + (row >> kEmitRowsLog2), count);
+    }
 }
 
-// row_ptr[r] = sum of counts[0 .. r), row_ptr[rows] = total.  One workgroup:
-// each thread sums a contiguous chunk, the chunk sums are scanned in LDS,
-// then each thread writes its chunk.
-__global__ __launch_bounds__(1024) void scan_kernel(const int32_t *__restrict__ counts, int64_t rows,
-                                                    int32_t *__restrict__ row_ptr) {
-    __shared__ int32_t wave_tot[16];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int64_t per = (rows + 1023) / 1024;
-    const int64_t beg = min(rows, (int64_t)t * per), end = min(rows, beg + per);
-    int32_t s = 0;
-    for (int64_t i = beg; i < end; ++i) s += counts[i];
-    int32_t incl = s;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int32_t v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
-    }
-    if (lane == 63) wave_tot[wave] = incl;
-    __syncthreads();
-    int32_t carry = 0;
-    for (int w = 0; w < wave; ++w) carry += wave_tot[w];
-    int32_t run = carry + incl - s;
-    for (int64_t i = beg; i < end; ++i) {
-        row_ptr[i] = run;
-        run += counts[i];
-    }
-    if (t == 1023) row_ptr[rows] = run;
+__global__ void clear_kernel(int32_t *__restrict__ p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
 }
 
-// Bitmask rows -> col_idx (ascending within a row); one wave per row.
+// Prefix and compaction in one pass, one wave per row.  Workgroup b owns rows
+// 4b .. 4b+3.  The offset of row 4b is the sum of the per-chunk kept counts of the
+// 64-row chunks before its chunk (the selection accumulated those) plus the counts
+// of the rows of its own chunk before it; each wave adds the counts of the rows
+// of the workgroup before its own, writes row_ptr and expands its row's bitmask
+// into ascending col_idx.
+template <int CTRL> __device__ __forceinline__ int dppi(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int wave_sum_i(int s) {
+    s += dppi<0xB1>(s);
+    s += dppi<0x4E>(s);
+    s += dppi<0x141>(s);
+    s += dppi<0x140>(s);
+    return __builtin_amdgcn_readlane(s, 0) + __builtin_amdgcn_readlane(s, 16) + __builtin_amdgcn_readlane(s, 32) +
+           __builtin_amdgcn_readlane(s, 48);
+}
+
 __global__ __launch_bounds__(256) void emit_kernel(const uint64_t *__restrict__ bits,
-                                                   const int32_t *__restrict__ row_ptr, int64_t rows, int32_t nW,
-                                                   int32_t *__restrict__ col_idx) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+                                                   const int32_t *__restrict__ counts,
+                                                   const int32_t *__restrict__ chunk_sums, int64_t rows, int32_t nW,
+                                                   int32_t *__restrict__ row_ptr, int32_t *__restrict__ col_idx) {
+    __shared__ int32_t part[4];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t r0 = (int64_t)blockIdx.x * 4;
+    const int64_t c = r0 >> kEmitRowsLog2;
+    const int64_t c0 = c << kEmitRowsLog2;
+    int32_t s = 0;
+    for (int64_t i = t; i < c; i += 256) s += chunk_sums[i];
+    if (t < r0 - c0) s += counts[c0 + t];
+    const int32_t ws = wave_sum_i(s);
+    if (lane == 0) part[wave] = ws;
+    __syncthreads();
+    const int64_t row = r0 + wave;
     if (row >= rows) return;
-    const uint64_t *b = bits + row * nW;
+    int32_t pos = part[0] + part[1] + part[2] + part[3];
+    for (int w = 0; w < wave; ++w) pos += counts[r0 + w];
+    if (lane == 0) {
+        row_ptr[row] = pos;
+        if (row == rows - 1) row_ptr[rows] = pos + counts[row];
+    }
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int32_t base = row_ptr[row];
+    const uint64_t *b = bits + row * nW;
     for (int w0 = 0; w0 < nW; w0 += 64) {
         const uint64_t mine = (w0 + lane < nW) ? b[w0 + lane] : 0ull;
         const int cnt = __popcll(mine);
         int incl = cnt;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int v = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += v;
+        incl += dppi<0x111>(incl);
+        incl += dppi<0x112>(incl);
+        incl += dppi<0x114>(incl);
+        incl += dppi<0x118>(incl);
+        {
+            const int q0 = __builtin_amdgcn_readlane(incl, 15), q1 = __builtin_amdgcn_readlane(incl, 31),
+                      q2 = __builtin_amdgcn_readlane(incl, 47);
+            const int row16 = lane >> 4;
+            incl += (row16 >= 1 ? q0 : 0) + (row16 >= 2 ? q1 : 0) + (row16 >= 3 ? q2 : 0);
         }
         const int excl = incl - cnt;
         const int nw = min(64, nW - w0);
         for (int e = 0; e < nw; ++e) {
-            const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)mine, e, 64);
-            const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(mine >> 32), e, 64);
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, e);
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine >> 32), e);
             const uint64_t m = ((uint64_t)hi << 32) | lo;
-            const int off = __shfl(excl, e, 64);
-            if ((m >> lane) & 1ull) col_idx[base + off + __popcll(m & lt_mask)] = (w0 + e) * 64 + lane;
+            const int off = __builtin_amdgcn_readlane(excl, e);
+            if ((m >> lane) & 1ull) col_idx[pos + off + __popcll(m & lt_mask)] = (w0 + e) * 64 + lane;
         }
-        base += __shfl(incl, 63, 64);
+        pos += __builtin_amdgcn_readlane(incl, 63);
     }
 }
 
 int launch_mask_bits(const uint8_t *mask, int64_t rows, int32_t nB, int32_t nW, uint64_t *bits, int32_t *counts,
-                     hipStream_t s) {
-    mask_bits_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(mask, rows, nB, nW, bits, counts);
+                     int32_t *chunk_sums, hipStream_t s) {
+    mask_bits_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(mask, rows, nB, nW, bits, counts,
+                                                                            chunk_sums);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_scan(const int32_t *counts, int64_t rows, int32_t *row_ptr, hipStream_t s) {
-    scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(counts, rows, row_ptr);
+int launch_clear(int32_t *p, int64_t n, hipStream_t s) {
+    const int64_t blocks = (n + 255) / 256;
+    clear_kernel<<<dim3((unsigned)(blocks < 1024 ? (blocks > 0 ? blocks : 1) : 1024)), dim3(256), 0, s>>>(p, n);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_emit(const uint64_t *bits, const int32_t *row_ptr, int64_t rows, int32_t nW, int32_t *col_idx,
-                hipStream_t s) {
-    emit_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(bits, row_ptr, rows, nW, col_idx);
+int launch_emit(const uint64_t *bits, const int32_t *counts, const int32_t *chunk_sums, int64_t rows, int32_t nW,
+                int32_t *row_ptr, int32_t *col_idx, hipStream_t s) {
+    emit_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(bits, counts, chunk_sums, rows, nW, row_ptr,
+                                                                       col_idx);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -50,7 +50,7 @@ extern "C" {
 /* status codes */
 #define SPARSE_ATTN_OK 0
 #define SPARSE_ATTN_INVALID_ARGUMENT (-1) /* null/misaligned pointer, bad size, bad threshold   */
-#define SPARSE_ATTN_UNSUPPORTED (-2)      /* dtype, head_dim or tile not implemented            */
+#define SPARSE_ATTN_UNSUPPORTED (-2)      /* dtype, head_dim, tile or size not implemented      */
 #define SPARSE_ATTN_CAPACITY (-3)         /* col_idx shorter than the worst case B*H*nB*nB      */
 #define SPARSE_ATTN_WORKSPACE (-4)        /* workspace smaller than sparse_attn_workspace_size  */
 #define SPARSE_ATTN_HIP_ERROR (-5)        /* a kernel launch failed                             */
@@ -58,8 +58,9 @@ extern "C" {
 /*
  * Problem shape.  head_dim must be 64 or 128; the tile must hold 64 tokens
  * (only 1 x 8 x 8 is implemented) and divide the grid exactly.  scale is the
- * softmax scale of both the pooled scores and the attention; 0 means
- * 1/sqrt(head_dim).
+ * softmax scale of both the pooled scores and the attention; it must be
+ * finite and >= 0, and 0 means 1/sqrt(head_dim).  The worst-case block
+ * count B*H*nB*nB (nB = blocks per head) must fit in int32.
  */
 typedef struct sparse_attn_shape {
     int32_t batch, heads, head_dim;
@@ -120,7 +121,9 @@ int64_t sparse_attn_workspace_size(const sparse_attn_shape *shape);
  *   col_capacity  must be >= sparse_attn_csr_capacity(shape).
  *   workspace   device, >= sparse_attn_workspace_size(shape) bytes; its
  *               contents on entry do not matter.
- * Ties in the CDF order go to the lower key-block index.
+ * Ties in the CDF order go to the lower key-block index.  A row of pooled
+ * scores is held in 64 KB of LDS, so nB <= 16128 blocks per head; larger
+ * grids return SPARSE_ATTN_UNSUPPORTED.
  */
 int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_select_params *params,
                            const void *q, const void *k, int32_t *row_ptr, int32_t *col_idx,

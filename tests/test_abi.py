@@ -55,6 +55,7 @@ def test_capacity_and_workspace_formulas():
     expect = al(expect + 4 * rows * 128)
     expect = al(expect + 8 * rows * (nbp // 64))
     expect = al(expect + 4 * rows)
+    expect = al(expect + 4 * ((rows + 63) // 64))
     assert B.sparse_attn_workspace_size(s) == expect
 
 
@@ -116,7 +117,7 @@ def test_select_rejects_bad_head_threshold():
 
 
 def test_select_rejects_too_many_blocks():
-    s = _shape(heads=1, grid=(256, 64, 64))     # 16,384 blocks: score row does not fit the selection LDS
+    s = _shape(heads=1, grid=(256, 128, 64))    # 32,768 blocks: a score row does not fit the selection LDS
     assert _select(s) == B.SPARSE_ATTN_UNSUPPORTED
 
 
