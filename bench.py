@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-CSR reference forward")
     ap.add_argument("--no-select-timing", action="store_true", help="skip the separate selection timing")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (for rocprofv3 counter scaling)")
+                    help="also run a plain 1 GiB read + 1 GiB write kernel (torch.neg) for rocprofv3 counter scaling")
     ap.add_argument("--pmc-summary", metavar="DIR", help="summarise rocprofv3 --pmc output and exit")
     return ap.parse_args()
 
@@ -85,7 +85,7 @@ def pmc_summary(d):
         vals = [v for n, vs in table.items() if key in n for v in vs]
         return sum(vals) / len(vals) if vals else None
 
-    copy_key = "elementwise_kernel"
+    copy_key = "neg_kernel"            # torch.neg over COPY_BYTES: reads and writes COPY_BYTES once
     cf, cw = pick(fetch, copy_key), pick(write, copy_key)
     af, aw = pick(fetch, ATTN_KERNEL), pick(write, ATTN_KERNEL)
     kib = COPY_BYTES / 1024.0
@@ -224,7 +224,7 @@ def main():
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         for _ in range(2):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
