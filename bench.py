@@ -278,14 +278,16 @@ def cpu_baseline(wl, q, k, v, thr, bufs, target_s):
     rows = wl.batch * wl.heads * wl.blocks
     rp = bufs.row_ptr.cpu().numpy().astype(np.int64)
     ci = bufs.col_idx[:int(rp[-1])].cpu().numpy()
-    # time one query block first, then size the sample to about target_s seconds
+    # time a probe of 64 query blocks (the oracle runs rows in parallel), then size the
+    # sample to about target_s seconds
     rng = np.random.default_rng(1)
     order = rng.permutation(rows)
+    probe = min(64, rows // 2)
     t0 = time.perf_counter()
-    oracle.attention_rows(q, k, v, rp, ci, order[:1])
-    per = max(time.perf_counter() - t0, 1e-3)
-    n = int(min(rows, max(2, target_s / per)))
-    sample = order[1:1 + n]
+    oracle.attention_rows(q, k, v, rp, ci, order[:probe])
+    per = max(time.perf_counter() - t0, 1e-3) / max(probe, 1)
+    n = int(min(rows - probe, max(2, target_s / per)))
+    sample = order[probe:probe + n]
     t0 = time.perf_counter()
     oracle.attention_rows(q, k, v, rp, ci, sample)
     t = time.perf_counter() - t0

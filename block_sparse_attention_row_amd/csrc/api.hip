@@ -15,7 +15,6 @@ namespace {
 using namespace sattn;
 
 constexpr int64_t kAlign = 256;
-constexpr int kSelectMaxLds = 65536;
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -57,12 +56,12 @@ float effective_scale(const sparse_attn_shape *s) {
     return s->scale != 0.f ? s->scale : (float)(1.0 / sqrt((double)s->head_dim));
 }
 
-struct Layout {
-    int64_t thr, qbar, kbar, bits, counts, chunks, scores, total;
-};
+int64_t groups_per_head(const Dims &d) { return (d.nB + kGroupRows - 1) / kGroupRows; }
+int64_t n_groups(const Dims &d) { return d.B * d.H * groups_per_head(d); }
 
-// Score rows go through HBM (instead of LDS) when a 16-row group no longer fits.
-bool big_select(const Dims &d) { return (int64_t)16 * d.nBp * 4 + 8 * 256 * 4 > kSelectMaxLds; }
+struct Layout {
+    int64_t thr, qbar, kbar, bits, counts, groups, total;
+};
 
 Layout layout(const Dims &d) {
     Layout l;
@@ -77,26 +76,18 @@ Layout layout(const Dims &d) {
     off = align_up(off + 8 * d.rows * d.nW, kAlign);
     l.counts = off;
     off = align_up(off + 4 * d.rows, kAlign);
-    l.chunks = off;
-    off = align_up(off + 4 * ((d.rows + kEmitRows - 1) / kEmitRows), kAlign);
-    l.scores = off;
-    if (big_select(d)) off = align_up(off + 4 * d.rows * d.nB, kAlign);
+    l.groups = off;
+    off = align_up(off + 4 * n_groups(d), kAlign);
     l.total = off;
     return l;
 }
 
 bool bad_thr(float t) { return !(t > 0.f); }   // also rejects NaN
 
-// Rows per selection workgroup: a full 16-row MFMA tile when the score rows fit LDS.
-int32_t rows_per_group(const Dims &d) {
-    int32_t R = 16;
-    while (R > 1 && (int64_t)R * d.nBp * 4 + 8 * 256 * 4 > kSelectMaxLds) R >>= 1;
-    return R;
-}
-
-int32_t emit_csr(const Dims &d, uint64_t *bits, int32_t *counts, int32_t *chunks, int32_t *row_ptr,
+int32_t emit_csr(const Dims &d, uint64_t *bits, int32_t *counts, int32_t *groups, int32_t *row_ptr,
                  int32_t *col_idx, hipStream_t st) {
-    if (launch_emit(bits, counts, chunks, d.rows, (int32_t)d.nW, row_ptr, col_idx, st)) return SPARSE_ATTN_HIP_ERROR;
+    if (launch_emit(bits, counts, groups, d.rows, (int32_t)d.nB, (int32_t)d.nW, row_ptr, col_idx, st))
+        return SPARSE_ATTN_HIP_ERROR;
     return SPARSE_ATTN_OK;
 }
 
@@ -142,7 +133,7 @@ int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_sel
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(row_ptr, 4) || !aligned(col_idx, 4) ||
         !aligned(workspace, 16))
         return SPARSE_ATTN_INVALID_ARGUMENT;
-    if ((d.nBp + 256) * 4 > kSelectMaxLds) return SPARSE_ATTN_UNSUPPORTED;   // one score row per wave in LDS
+    if (d.nBp > kSelectMaxBlocks) return SPARSE_ATTN_UNSUPPORTED;   // a row is held in registers
     if (bad_thr(params->threshold)) return SPARSE_ATTN_INVALID_ARGUMENT;
     if (params->head_thresholds)
         for (int64_t h = 0; h < d.H; ++h)
@@ -154,11 +145,11 @@ int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_sel
     hipStream_t s = (hipStream_t)stream;
     char *ws = (char *)workspace;
     float *thr = (float *)(ws + L.thr);
-    float *qbar = (float *)(ws + L.qbar);
-    float *kbar = (float *)(ws + L.kbar);
+    __bf16 *qbar = (__bf16 *)(ws + L.qbar);
+    __bf16 *kbar = (__bf16 *)(ws + L.kbar);
     uint64_t *bits = (uint64_t *)(ws + L.bits);
     int32_t *counts = (int32_t *)(ws + L.counts);
-    int32_t *chunks = (int32_t *)(ws + L.chunks);
+    int32_t *groups = (int32_t *)(ws + L.groups);
 
     // thresholds: the first ThrChunk::kMax travel with the pooling kernel, any others
     // through small fill kernels
@@ -167,8 +158,6 @@ int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_sel
     for (int i = 0; i < side.n_thr; ++i)
         side.thr.v[i] = params->head_thresholds ? params->head_thresholds[i] : params->threshold;
     side.thr_dst = thr;
-    side.chunk_sums = chunks;
-    side.n_chunks = (d.rows + kEmitRows - 1) / kEmitRows;
     for (int64_t h0 = ThrChunk::kMax; h0 < d.H; h0 += ThrChunk::kMax) {
         float tmp[ThrChunk::kMax];
         const int n = (int)((d.H - h0) < ThrChunk::kMax ? (d.H - h0) : ThrChunk::kMax);
@@ -185,10 +174,9 @@ int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_sel
     a.thr = thr;
     a.bits = bits;
     a.counts = counts;
-    a.chunk_sums = chunks;
-    a.R = rows_per_group(d);
-    a.groups_per_head = (int32_t)((d.nB + a.R - 1) / a.R);
-    a.n_groups = d.B * d.H * a.groups_per_head;
+    a.group_sums = groups;
+    a.groups_per_head = (int32_t)groups_per_head(d);
+    a.n_groups = n_groups(d);
     a.H = (int32_t)d.H;
     a.nB = (int32_t)d.nB;
     a.nBp = (int32_t)d.nBp;
@@ -199,13 +187,8 @@ int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_sel
     a.wh = params->win_h;
     a.ww = params->win_w;
     a.scale_log2 = effective_scale(shape) * kLog2e;
-    if (big_select(d)) {
-        a.n_groups = d.rows;
-        if (launch_select_big(a, (int)d.D, (float *)(ws + L.scores), s)) return SPARSE_ATTN_HIP_ERROR;
-    } else if (launch_select(a, (int)d.D, s)) {
-        return SPARSE_ATTN_HIP_ERROR;
-    }
-    return emit_csr(d, bits, counts, chunks, row_ptr, col_idx, s);
+    if (launch_select(a, (int)d.D, s)) return SPARSE_ATTN_HIP_ERROR;
+    return emit_csr(d, bits, counts, groups, row_ptr, col_idx, s);
 }
 
 int32_t sparse_attn_forward(const sparse_attn_shape *shape, const void *q, const void *k, const void *v,
@@ -255,11 +238,10 @@ int32_t sparse_attn_mask_to_csr(const sparse_attn_shape *shape, const uint8_t *b
     char *ws = (char *)workspace;
     uint64_t *bits = (uint64_t *)(ws + L.bits);
     int32_t *counts = (int32_t *)(ws + L.counts);
-    int32_t *chunks = (int32_t *)(ws + L.chunks);
-    if (launch_clear(chunks, (d.rows + kEmitRows - 1) / kEmitRows, s)) return SPARSE_ATTN_HIP_ERROR;
-    if (launch_mask_bits(block_mask, d.rows, (int32_t)d.nB, (int32_t)d.nW, bits, counts, chunks, s))
+    int32_t *groups = (int32_t *)(ws + L.groups);
+    if (launch_mask_bits(block_mask, d.B * d.H, (int32_t)d.nB, (int32_t)d.nW, bits, counts, groups, s))
         return SPARSE_ATTN_HIP_ERROR;
-    return emit_csr(d, bits, counts, chunks, row_ptr, col_idx, s);
+    return emit_csr(d, bits, counts, groups, row_ptr, col_idx, s);
 }
 
 }  // extern "C"

@@ -10,38 +10,45 @@
 
 namespace sattn {
 
-// External dense uint8 mask [rows][nB] -> bitmask rows + counts; one wave per row.
-__global__ __launch_bounds__(256) void mask_bits_kernel(const uint8_t *__restrict__ mask, int64_t rows, int32_t nB,
-                                                        int32_t nW, uint64_t *__restrict__ bits,
-                                                        int32_t *__restrict__ counts, int32_t *__restrict__ chunk_sums) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
-    const uint8_t *m = mask + row * (int64_t)nB;
+// External dense uint8 mask [rows][nB] -> bitmask rows + counts.  Workgroup G owns row
+// group G (16 waves, one row each) and writes the group's total.
+__global__ __launch_bounds__(1024) void mask_bits_kernel(const uint8_t *__restrict__ mask, int32_t nB, int32_t nW,
+                                                         int32_t groups_per_head, uint64_t *__restrict__ bits,
+                                                         int32_t *__restrict__ counts,
+                                                         int32_t *__restrict__ group_sums) {
+    __shared__ int32_t wave_count[kGroupRows];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t G = blockIdx.x;
+    const int64_t bh = G / groups_per_head;
+    const int i = (int)(G % groups_per_head) * kGroupRows + wave;
     int count = 0;
-    for (int e = 0; e < nW; ++e) {
-        const int j = 64 * e + lane;
-        const bool k = j < nB && m[j] != 0;
-        const uint64_t b = __ballot(k);
-        count += __popcll(b);
-        if (lane == 0) bits[row * nW + e] = b;
+    if (i < nB) {
+        const int64_t row = bh * nB + i;
+        const uint8_t *m = mask + row * (int64_t)nB;
+        for (int e = 0; e < nW; ++e) {
+            const int j = 64 * e + lane;
+            const uint64_t b = __ballot(j < nB && m[j] != 0);
+            count += __popcll(b);
+            if (lane == 0) bits[row * nW + e] = b;
+        }
+        if (lane == 0) counts[row] = count;
     }
-    if (lane == 0) {
-        counts[row] = count;
-        atomicAdd(chunk_sums + (row >> kEmitRowsLog2), count);
+    if (lane == 0) wave_count[wave] = count;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t t = 0;
+#pragma unroll
+        for (int w = 0; w < kGroupRows; ++w) t += wave_count[w];
+        group_sums[G] = t;
     }
 }
 
-__global__ void clear_kernel(int32_t *__restrict__ p, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
-}
-
-// Prefix and compaction in one pass, one wave per row.  Workgroup b owns rows
-// 4b .. 4b+3.  The offset of row 4b is the sum of the per-chunk kept counts of the
-// 64-row chunks before its chunk (the selection accumulated those) plus the counts
-// of the rows of its own chunk before it; each wave adds the counts of the rows
-// of the workgroup before its own, writes row_ptr and expands its row's bitmask
-// into ascending col_idx.
+// Prefix and compaction in one pass, one wave per row; workgroup b owns rows
+// 4b .. 4b+3.  The offset of a row is the sum of the totals of the row groups before
+// its own plus the counts of the rows of its group before it: the workgroup sums the
+// totals before the group of its first row once, each wave adds what lies between
+// that and its row, writes row_ptr and expands its row's bitmask into ascending
+// col_idx.
 template <int CTRL> __device__ __forceinline__ int dppi(int v) {
     return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
@@ -56,23 +63,28 @@ __device__ __forceinline__ int wave_sum_i(int s) {
 
 __global__ __launch_bounds__(256) void emit_kernel(const uint64_t *__restrict__ bits,
                                                    const int32_t *__restrict__ counts,
-                                                   const int32_t *__restrict__ chunk_sums, int64_t rows, int32_t nW,
-                                                   int32_t *__restrict__ row_ptr, int32_t *__restrict__ col_idx) {
+                                                   const int32_t *__restrict__ group_sums, int64_t rows, int32_t nB,
+                                                   int32_t nW, int32_t *__restrict__ row_ptr,
+                                                   int32_t *__restrict__ col_idx) {
     __shared__ int32_t part[4];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t gph = (nB + kGroupRows - 1) / kGroupRows;
+    auto group_of = [&](int64_t r) { return (r / nB) * gph + (r % nB) / kGroupRows; };
     const int64_t r0 = (int64_t)blockIdx.x * 4;
-    const int64_t c = r0 >> kEmitRowsLog2;
-    const int64_t c0 = c << kEmitRowsLog2;
+    const int64_t G0 = group_of(r0);
     int32_t s = 0;
-    for (int64_t i = t; i < c; i += 256) s += chunk_sums[i];
-    if (t < r0 - c0) s += counts[c0 + t];
+    for (int64_t g = t; g < G0; g += 256) s += group_sums[g];
     const int32_t ws = wave_sum_i(s);
     if (lane == 0) part[wave] = ws;
     __syncthreads();
     const int64_t row = r0 + wave;
     if (row >= rows) return;
-    int32_t pos = part[0] + part[1] + part[2] + part[3];
-    for (int w = 0; w < wave; ++w) pos += counts[r0 + w];
+    const int64_t G = group_of(row);
+    const int64_t first = (row / nB) * nB + ((row % nB) / kGroupRows) * kGroupRows;   // first row of G
+    int32_t mine = 0;
+    if (lane < G - G0) mine += group_sums[G0 + lane];          // at most 3 groups lie between
+    if (lane < row - first) mine += counts[first + lane];      // at most 15 rows
+    int32_t pos = part[0] + part[1] + part[2] + part[3] + wave_sum_i(mine);
     if (lane == 0) {
         row_ptr[row] = pos;
         if (row == rows - 1) row_ptr[rows] = pos + counts[row];
@@ -80,8 +92,8 @@ __global__ __launch_bounds__(256) void emit_kernel(const uint64_t *__restrict__ 
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const uint64_t *b = bits + row * nW;
     for (int w0 = 0; w0 < nW; w0 += 64) {
-        const uint64_t mine = (w0 + lane < nW) ? b[w0 + lane] : 0ull;
-        const int cnt = __popcll(mine);
+        const uint64_t mine_w = (w0 + lane < nW) ? b[w0 + lane] : 0ull;
+        const int cnt = __popcll(mine_w);
         int incl = cnt;
         incl += dppi<0x111>(incl);
         incl += dppi<0x112>(incl);
@@ -96,8 +108,8 @@ __global__ __launch_bounds__(256) void emit_kernel(const uint64_t *__restrict__ 
         const int excl = incl - cnt;
         const int nw = min(64, nW - w0);
         for (int e = 0; e < nw; ++e) {
-            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, e);
-            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine >> 32), e);
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine_w, e);
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine_w >> 32), e);
             const uint64_t m = ((uint64_t)hi << 32) | lo;
             const int off = __builtin_amdgcn_readlane(excl, e);
             if ((m >> lane) & 1ull) col_idx[pos + off + __popcll(m & lt_mask)] = (w0 + e) * 64 + lane;
@@ -106,22 +118,17 @@ __global__ __launch_bounds__(256) void emit_kernel(const uint64_t *__restrict__ 
     }
 }
 
-int launch_mask_bits(const uint8_t *mask, int64_t rows, int32_t nB, int32_t nW, uint64_t *bits, int32_t *counts,
-                     int32_t *chunk_sums, hipStream_t s) {
-    mask_bits_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(mask, rows, nB, nW, bits, counts,
-                                                                            chunk_sums);
+int launch_mask_bits(const uint8_t *mask, int64_t bh, int32_t nB, int32_t nW, uint64_t *bits, int32_t *counts,
+                     int32_t *group_sums, hipStream_t s) {
+    const int32_t gph = (nB + kGroupRows - 1) / kGroupRows;
+    mask_bits_kernel<<<dim3((unsigned)(bh * gph)), dim3(64 * kGroupRows), 0, s>>>(mask, nB, nW, gph, bits, counts,
+                                                                                 group_sums);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_clear(int32_t *p, int64_t n, hipStream_t s) {
-    const int64_t blocks = (n + 255) / 256;
-    clear_kernel<<<dim3((unsigned)(blocks < 1024 ? (blocks > 0 ? blocks : 1) : 1024)), dim3(256), 0, s>>>(p, n);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-int launch_emit(const uint64_t *bits, const int32_t *counts, const int32_t *chunk_sums, int64_t rows, int32_t nW,
-                int32_t *row_ptr, int32_t *col_idx, hipStream_t s) {
-    emit_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(bits, counts, chunk_sums, rows, nW, row_ptr,
+int launch_emit(const uint64_t *bits, const int32_t *counts, const int32_t *group_sums, int64_t rows, int32_t nB,
+                int32_t nW, int32_t *row_ptr, int32_t *col_idx, hipStream_t s) {
+    emit_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(bits, counts, group_sums, rows, nB, nW, row_ptr,
                                                                        col_idx);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -17,17 +17,15 @@ namespace sattn {
 // ---------------------------------------------------------------------------
 // Pooling.  One wave per (tensor, block): the block is 64*D contiguous
 // elements; each lane streams 16-byte chunks, accumulates in fp32, and the
-// lanes that share a column slice are combined with xor-shuffles.
+// lanes that share a column slice are combined with xor-shuffles.  The fp32
+// mean x is stored as a pair of bf16 values, hi = bf16(x) and lo = bf16(x - hi)
+// (row layout [hi: D][lo: D]), the operand form of the split-bf16 score products.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ q, const T *__restrict__ k,
-                                                   float *__restrict__ qbar, float *__restrict__ kbar,
+                                                   __bf16 *__restrict__ qbar, __bf16 *__restrict__ kbar,
                                                    int64_t nblocks, PoolSide side) {
-    // side jobs for the selection that follows: the first ThrChunk::kMax thresholds and
-    // clearing the per-chunk kept counts
+    // side job for the selection that follows: the first ThrChunk::kMax thresholds
     if (blockIdx.x == 0 && (int)threadIdx.x < side.n_thr) side.thr_dst[threadIdx.x] = side.thr.v[threadIdx.x];
-    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < side.n_chunks;
-         c += (int64_t)gridDim.x * blockDim.x)
-        side.chunk_sums[c] = 0;
     constexpr int VEC = 16 / sizeof(T);
     constexpr int LPR = D / VEC;               // lanes covering one token row
     constexpr int RPW = kWave / LPR;           // token rows per wave-wide load
@@ -38,7 +36,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ q, cons
     if (w >= 2 * nblocks) return;
     const int64_t blk = w >> 1;
     const T *src = (w & 1) ? k : q;
-    float *dst = (w & 1) ? kbar : qbar;
+    __bf16 *dst = (w & 1) ? kbar : qbar;
     const int col = (lane % LPR) * VEC, row0 = lane / LPR;
     const u32x4 *p = reinterpret_cast<const u32x4 *>(src + (blk * kTokensPerBlock + row0) * D + col);
     constexpr int STEP = RPW * D * (int)sizeof(T) / 16;   // u32x4 units between iterations
@@ -70,16 +68,19 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ q, cons
         for (int c = 0; c < VEC; ++c) acc[c] += __shfl_xor(acc[c], o, 64);
     }
     if (lane < LPR) {
-        f32x4 *o = reinterpret_cast<f32x4 *>(dst + blk * D + col);
+        typedef __attribute__((ext_vector_type(VEC))) float fv;
+        typedef __attribute__((ext_vector_type(VEC))) __bf16 bv;
+        fv x;
 #pragma unroll
-        for (int c = 0; c < VEC / 4; ++c) {
-            f32x4 v;
-            v[0] = acc[4 * c] * (1.f / 64.f);
-            v[1] = acc[4 * c + 1] * (1.f / 64.f);
-            v[2] = acc[4 * c + 2] * (1.f / 64.f);
-            v[3] = acc[4 * c + 3] * (1.f / 64.f);
-            o[c] = v;
-        }
+        for (int c = 0; c < VEC; ++c) x[c] = acc[c] * (1.f / 64.f);
+        const bv hi = __builtin_convertvector(x, bv);
+        fv r;
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) r[c] = x[c] - (float)hi[c];
+        const bv lo = __builtin_convertvector(r, bv);
+        __bf16 *o = dst + blk * (2 * D) + col;
+        *reinterpret_cast<bv *>(o) = hi;
+        *reinterpret_cast<bv *>(o + D) = lo;
     }
 }
 
@@ -96,304 +97,287 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Phase 2 for one row, run by one wave: sr holds the row's nB scores (already
-// multiplied by scale*log2(e)) in LDS and is overwritten with e_j; writes the row's
-// kept-block bitmask, its count, and adds the count to its chunk.
-__device__ __forceinline__ void select_row(const SelectArgs &a, float *sr, float *hist, int64_t bh, int i) {
-    const int lane = threadIdx.x & 63;
+// ---------------------------------------------------------------------------
+// Selection.  A workgroup of 16 waves owns 16 consecutive query blocks (rows) of
+// one (batch, head); wave w ends up holding row w in registers, key block
+// j = 64c + lane in s[c].
+//
+// Scores ("Attention Reduite"): S = Qbar Kbar^T * scale * log2(e), in chunks of
+// 256 key blocks.  Per chunk each wave forms a 16 x 16 tile (the 16 rows x its 16
+// keys) with v_mfma_f32_16x16x32_bf16 on the split operands, hi*hi + hi*lo + lo*hi
+// (relative error near 2^-16, fp32 accumulation), and parks it in a double-buffered
+// LDS stage; after one barrier every wave reads its own row's 256 scores back.
+//
+// Cut ("Seuil CDF"), per wave on its register row: e_j = 2^(s_j - max) and their sum
+// Z; then an exact mass-weighted radix select over the fp32 bit patterns of the e_j
+// (positive floats order like their bit patterns) finds the crossing value v* and
+// the mass M strictly above it; the digits start at the highest bit where the row's
+// e_j differ, 8 bits per pass, with the pass histogram in LDS.  A block is kept when
+// e_j > v*, or e_j == v* and M plus the mass of the equal blocks with lower index is
+// below thr * Z: the CDF rule with ties going to the lower index, without
+// normalising the row.  Then the optional box window ("Integration Hybride avec
+// STA"), the row's bitmask, its count and the count of its 64-row chunk.
+constexpr int kSelRows = kGroupRows;    // rows (and waves) per workgroup
+constexpr int kSelChunk = 256;          // key blocks per score chunk (16 waves x 16)
+constexpr int kStageStride = kSelChunk + 4;   // padded: the 16x16 tile stores are conflict-free
+
+template <int D> constexpr int qf_stride() { return 2 * D + 8; }   // bf16; 16 B pad per row
+template <int D> constexpr size_t select_lds_bytes() {
+    return (size_t)kSelRows * qf_stride<D>() * 2 + (size_t)2 * kSelRows * kStageStride * 4 +
+           (size_t)kSelRows * 256 * 4;
+}
+
+// The cut of row i of head bh, run by one wave on its register row s (scaled scores,
+// -inf for padding); writes the row's bitmask and count, and its count to `out`.
+template <int NE>
+__device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], float *hist_all, int64_t bh, int i,
+                                           int nvc, int lane, int32_t &out) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t row = bh * a.nB + i;
-    const int ne = a.nBp / 64;
     const int h = (int)(bh % a.H);
     const float thr = a.thr[h];
     const bool keep_all = !(thr < 1.f);
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int nTyx = a.nTy * a.nTx;
+    uint32_t *list = reinterpret_cast<uint32_t *>(hist_all + wave * 256);   // up to 64 keys of the bracket
 
+    // e_j = 2^(s_j - max) in place (0 for padding), Z, and the smallest positive key
     float mx = -INFINITY;
-    for (int e = 0; e < ne; ++e) {
-        const int j = lane + 64 * e;
-        if (j < a.nB) mx = fmaxf(mx, sr[j]);
-    }
+#pragma unroll
+    for (int c = 0; c < NE; ++c)
+        if (c < nvc) mx = fmaxf(mx, s[c]);
     mx = wave_max_u(mx);
     float z = 0.f;
-    for (int e = 0; e < ne; ++e) {
-        const int j = lane + 64 * e;
-        if (j < a.nB) {
-            const float pe = __builtin_amdgcn_exp2f(sr[j] - mx);
-            sr[j] = pe;
+    uint32_t kmin = 0xffffffffu;
+#pragma unroll
+    for (int c = 0; c < NE; ++c) {
+        if (c < nvc) {
+            const float pe = __builtin_amdgcn_exp2f(s[c] - mx);
+            s[c] = pe;
             z += pe;
+            kmin = min(kmin, __float_as_uint(pe) - 1u);     // padding (0) wraps to the top
         }
     }
     const float thrz = thr * wave_sum_u(z);
 
-    // Radix digits start at the highest bit where the row's keys differ (the bits
-    // above it are common to all keys), so the first histogram spreads over the
-    // row's actual range instead of piling onto one exponent bucket.
-    uint32_t vstar = 0;
+    // Crossing value v* and the mass M strictly above it.  Keys are the fp32 bit
+    // patterns of the e_j (order-preserving for e >= 0).  Bisection over the key
+    // bracket (lo, hi] keeps  mass(key > hi) = Mhi < thr*Z <= mass(key > lo); each step
+    // costs one compare/select/add per element plus a wave sum, and the compare
+    // masks' popcounts track how many elements the bracket holds.  Once at most 64
+    // remain they are compacted to LDS, sorted across the lanes, and the crossing
+    // is read off their prefix sums.
+    uint32_t vstar = 0x3f800000u;
     float M = 0.f;
     if (!keep_all) {
-        uint32_t kmin = 0xffffffffu, kmax = 0u;
-        for (int e = 0; e < ne; ++e) {
-            const int j = lane + 64 * e;
-            if (j < a.nB) {
-                const uint32_t u = __float_as_uint(sr[j]);
-                kmin = min(kmin, u);
-                kmax = max(kmax, u);
-            }
-        }
         kmin = wave_min_u32(kmin);
-        kmax = wave_max_u32_u(kmax);
-        const uint32_t diff = kmin ^ kmax;
-        uint32_t prefix = kmax;            // all keys equal: v* is that key, M = 0
-        if (diff) {
-            int hi = 31 - __builtin_clz(diff);                 // highest differing bit
-            prefix = hi == 31 ? 0u : kmax >> (hi + 1);          // the common upper bits
+        uint32_t lo = kmin, hi = 0x3f800000u;            // every e_j <= 1, the row max is exactly 1
+        float Mhi = 0.f;
+        uint32_t clo = 0, chi = 0;                        // counts of key > lo, key > hi
+#pragma unroll
+        for (int c = 0; c < NE; ++c)
+            if (c < nvc) clo += __popcll(__ballot(__float_as_uint(s[c]) > lo));
 #pragma unroll 1
-            while (hi >= 0) {
-                const int lo = hi >= 7 ? hi - 7 : 0, w = hi - lo + 1;
-                const uint32_t dmask = (1u << w) - 1u;
-                reinterpret_cast<f32x4 *>(hist)[lane] = f32x4{0.f, 0.f, 0.f, 0.f};
-                wave_lds_sync();
-                for (int e = 0; e < ne; ++e) {
-                    const int j = lane + 64 * e;
-                    if (j < a.nB) {
-                        const float pe = sr[j];
-                        const uint32_t u = __float_as_uint(pe);
-                        const bool match = hi == 31 || (u >> (hi + 1)) == prefix;
-                        if (match) atomicAdd(&hist[(u >> lo) & dmask], pe);
-                    }
+        while (clo - chi > 64 && hi - lo > 1) {
+            const uint32_t p = lo + ((hi - lo) >> 1);
+            float acc = 0.f;
+            uint32_t cnt = 0;
+#pragma unroll
+            for (int c = 0; c < NE; ++c) {
+                if (c < nvc) {
+                    const bool gt = __float_as_uint(s[c]) > p;
+                    acc += gt ? s[c] : 0.f;
+                    cnt += __popcll(__ballot(gt));
                 }
-                wave_lds_sync();
-                // lane l takes buckets 4(63-l)+3 .. 4(63-l): lane order is descending bucket order
-                const f32x4 hv = reinterpret_cast<const f32x4 *>(hist)[63 - lane];
-                const float T = (hv[0] + hv[1]) + (hv[2] + hv[3]);
-                const float above = M + (wave_prefix_sum(T, lane) - T);   // mass of the higher buckets
-                // the last lane whose higher buckets stay below thr*Z holds the crossing bucket
-                const uint64_t bal = __ballot(above < thrz);
-                const int L = 63 - __builtin_clzll(bal);   // lane 0 always qualifies: above == M < thr*Z
-                const float c3 = above + hv[3];
-                const float c2 = c3 + hv[2];
-                const float c1 = c2 + hv[1];
-                int sub;
-                float mnew;
-                if (c3 >= thrz) { sub = 3; mnew = above; }
-                else if (c2 >= thrz) { sub = 2; mnew = c3; }
-                else if (c1 >= thrz) { sub = 1; mnew = c2; }
-                else { sub = 0; mnew = c1; }
-                sub = __builtin_amdgcn_readlane(sub, L);
-                mnew = lane_value(mnew, L);
-                prefix = (prefix << w) | (uint32_t)(4 * (63 - L) + sub);
-                M = mnew;
-                wave_lds_sync();
-                hi = lo - 1;
+            }
+            const float A = wave_sum_u(acc);
+            if (A < thrz) {
+                hi = p;
+                Mhi = A;
+                chi = cnt;
+            } else {
+                lo = p;
+                clo = cnt;
             }
         }
-        vstar = prefix;
+        vstar = hi;       // a single key left in the bracket: v* = hi, M = Mhi
+        M = Mhi;
+        if (clo - chi <= 64 && clo > chi) {
+            uint32_t base = 0;
+#pragma unroll
+            for (int c = 0; c < NE; ++c) {
+                if (c < nvc) {
+                    const uint32_t u = __float_as_uint(s[c]);
+                    const bool in = u > lo && u <= hi;
+                    const uint64_t m = __ballot(in);
+                    if (in) {
+                        const uint32_t pos =
+                            base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                        list[pos] = u;
+                    }
+                    base += (uint32_t)__popcll(m);
+                }
+            }
+            wave_lds_sync();
+            const uint32_t n = clo - chi;
+            uint32_t u = (uint32_t)lane < n ? list[lane] : 0u;
+            wave_lds_sync();
+            // bitonic sort of the bracket's keys, descending across the lanes
+#pragma unroll
+            for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+                for (int j = k >> 1; j > 0; j >>= 1) {
+                    const uint32_t o = (uint32_t)__shfl_xor((int)u, j, 64);
+                    const bool desc = (lane & k) == 0 || k == 64;
+                    const bool low = (lane & j) == 0;
+                    u = (low == desc) ? max(u, o) : min(u, o);
+                }
+            }
+            const float e = __uint_as_float(u);
+            const float incl = wave_prefix_sum(e, lane);
+            const uint64_t reach = __ballot((uint32_t)lane < n && Mhi + incl >= thrz);
+            const int L = reach ? __builtin_ctzll(reach) : (int)n - 1;   // rounding may leave thr*Z unreached
+            vstar = (uint32_t)__builtin_amdgcn_readlane((int)u, L);
+            M = Mhi + wave_sum_u(u > vstar ? e : 0.f);
+        }
     }
 
-    // ---- emit: kept = above v*, or tie within thr*Z, or in the window
+    // ---- kept = key above v*, or equal to v* with M + (its rank among the equal
+    //      keys, by index) * v* below thr*Z, or inside the window
+    const int nTyx = a.nTy * a.nTx;
     const int ti = i / nTyx, yi = (i / a.nTx) % a.nTy, xi = i % a.nTx;
     const float vstar_f = __uint_as_float(vstar);
-    int ties_before = 0;
-    int count = 0;
-    uint64_t *brow = a.bits + row * (int64_t)ne;
-    for (int e = 0; e < ne; ++e) {
-        const int j = lane + 64 * e;
-        const bool valid = j < a.nB;
-        bool kept = valid && keep_all;
-        if (!keep_all) {
-            const uint32_t u = valid ? __float_as_uint(sr[j]) : 0u;
-            const bool tie = valid && u == vstar;
-            const uint64_t tb = __ballot(tie);
-            kept = valid && u > vstar;
-            if (tie) {
-                const int rank = ties_before + __popcll(tb & lt_mask);
-                kept = M + (float)rank * vstar_f < thrz;
+    uint32_t ties_before = 0, count = 0, wlo = 0, whi = 0;
+#pragma unroll
+    for (int c = 0; c < NE; ++c) {
+        if (c < nvc) {
+            const int j = 64 * c + lane;
+            uint64_t m;
+            if (keep_all) {
+                m = __ballot(j < a.nB);
+            } else {
+                const uint32_t u = __float_as_uint(s[c]);
+                m = __ballot(u > vstar);
+                const uint64_t tb = __ballot(u == vstar);      // padding (0) never equals v* > 0
+                if (tb) {
+                    const uint32_t rank =
+                        ties_before + __builtin_amdgcn_mbcnt_hi((uint32_t)(tb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)tb, 0u));
+                    m |= __ballot(u == vstar && M + (float)rank * vstar_f < thrz);
+                    ties_before += (uint32_t)__popcll(tb);
+                }
             }
-            ties_before += __popcll(tb);
+            if (a.window) {
+                const int tj = j / nTyx, yj = (j / a.nTx) % a.nTy, xj = j % a.nTx;
+                m |= __ballot(j < a.nB && abs(tj - ti) <= a.wt && abs(yj - yi) <= a.wh && abs(xj - xi) <= a.ww);
+            }
+            count += (uint32_t)__popcll(m);
+            if (lane == c) {
+                wlo = (uint32_t)m;
+                whi = (uint32_t)(m >> 32);
+            }
         }
-        if (a.window && valid) {
-            const int tj = j / nTyx, yj = (j / a.nTx) % a.nTy, xj = j % a.nTx;
-            if (abs(tj - ti) <= a.wt && abs(yj - yi) <= a.wh && abs(xj - xi) <= a.ww) kept = true;
-        }
-        const uint64_t m = __ballot(kept);
-        count += __popcll(m);
-        if (lane == 0) brow[e] = m;
     }
+    if (lane < nvc) a.bits[row * (int64_t)nvc + lane] = ((uint64_t)whi << 32) | wlo;
     if (lane == 0) {
-        a.counts[row] = count;
-        atomicAdd(a.chunk_sums + (row >> kEmitRowsLog2), count);   // integer adds: order does not matter
+        a.counts[row] = (int32_t)count;
+        out = (int32_t)count;
     }
 }
 
-// ---------------------------------------------------------------------------
-// Selection.  A workgroup (8 waves) owns R <= 16 consecutive query blocks of one
-// (batch, head).  Phase 1 computes the R x nB pooled scores with fp32 MFMA
-// (v_mfma_f32_16x16x4_f32; each wave sweeps every eighth 16-column tile) and parks
-// them in LDS, pre-multiplied by scale*log2(e).  Phase 2 gives each wave whole rows:
-// e_j = 2^(s_j - max) in place and their sum Z; then an exact mass-weighted radix
-// select over the fp32 bit patterns of the e_j (positive floats order like their
-// bit patterns) finds the crossing value v* and the mass M strictly above it, in
-// four 8-bit passes whose histograms live in LDS.  A block is kept when e_j > v*,
-// or e_j == v* and M plus the mass of the equal blocks with lower index is below
-// thr * Z.  That is the CDF rule with ties going to the lower index, without
-// normalising the row.  Wave-wide sums and scans use DPP and v_readlane.
-template <int D>
-__global__ __launch_bounds__(512) void select_kernel(SelectArgs a) {
-    extern __shared__ float smem[];
-    float *scores = smem;                                 // [R][nBp]
-    float *hist_all = smem + (size_t)a.R * a.nBp;         // [8][256]
+template <int D, int NE>
+__global__ __launch_bounds__(1024) void select_kernel(SelectArgs a) {
+    static_assert(NE % 4 == 0 && NE <= 64, "NE: register row length in 64-key words");
+    constexpr int KB = D / 32;                     // k-blocks of one 16x16x32 product
+    constexpr bool kPrefetch = NE == 16 || NE == 32;   // registers for the next chunk's operands (NE = 8: two workgroups per CU instead)
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    __bf16 *qf = reinterpret_cast<__bf16 *>(smem_raw);                              // [16][2D+8]
+    float *stage = reinterpret_cast<float *>(smem_raw + (size_t)kSelRows * qf_stride<D>() * 2);  // [2][16][260]
+    float *hist_all = stage + 2 * kSelRows * kStageStride;                          // [16][256]
+
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t g = xcd_remap(blockIdx.x, a.n_groups);
     const int64_t bh = g / a.groups_per_head;
-    const int i0 = (int)(g % a.groups_per_head) * a.R;
-    const int nrows = min(a.R, a.nB - i0);
-    const float *qb = a.qbar + (bh * a.nB) * (int64_t)D;
-    const float *kb = a.kbar + (bh * a.nB) * (int64_t)D;
+    const int i0 = (int)(g % a.groups_per_head) * kSelRows;
+    const int nrows = min(kSelRows, a.nB - i0);
+    const int nvc = a.nBp >> 6;                    // 64-key words in a row
+    const int nch = (a.nB + kSelChunk - 1) / kSelChunk;
+    const __bf16 *qs = a.qbar + (bh * a.nB + i0) * (int64_t)(2 * D);
+    const __bf16 *ks = a.kbar + (bh * a.nB) * (int64_t)(2 * D);
 
-    // ---- phase 1: scores -------------------------------------------------
-    {
-        const int ii = lane & 15, gq = lane >> 4;
-        f32x4 aq[D / 16];
-        const bool qok = ii < nrows;
+    const int ii = lane & 15, kq = lane >> 4;
+    float s[NE];
+    bf16x8 kh[2][KB], kl[2][KB];
+    auto load_k = [&](int cc, int slot) {
+        const int jj = kSelChunk * cc + 16 * wave + ii;
+        const bool ok = jj < a.nB;
+        const __bf16 *kr = ks + (int64_t)(ok ? jj : 0) * (2 * D) + 8 * kq;
 #pragma unroll
-        for (int m = 0; m < D / 16; ++m) {
-            aq[m] = qok ? *reinterpret_cast<const f32x4 *>(qb + (int64_t)(i0 + ii) * D + 16 * m + 4 * gq)
-                        : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < KB; ++kb) {
+            bf16x8 h = *reinterpret_cast<const bf16x8 *>(kr + 32 * kb);
+            bf16x8 l = *reinterpret_cast<const bf16x8 *>(kr + D + 32 * kb);
+            kh[slot][kb] = ok ? h : bf16x8{};
+            kl[slot][kb] = ok ? l : bf16x8{};
         }
-        const int ntiles = a.nBp / 16;
-        for (int ct = wave; ct < ntiles; ct += 8) {
-            const int jj = 16 * ct + ii;
-            const bool kok = jj < a.nB;
-            f32x4 bk[D / 16];
-#pragma unroll
-            for (int m = 0; m < D / 16; ++m) {
-                bk[m] = kok ? *reinterpret_cast<const f32x4 *>(kb + (int64_t)jj * D + 16 * m + 4 * gq)
-                            : f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int m = 0; m < D / 16; ++m) {
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(aq[m][s4], bk[m][s4], acc, 0, 0, 0);
-            }
-            // acc[e] = S[row 4*gq + e][col 16*ct + ii]
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * gq + e;
-                if (r < a.R) scores[(size_t)r * a.nBp + jj] = acc[e] * a.scale_log2;
-            }
+    };
+    load_k(0, 0);     // in flight while the queries are staged
+
+    // ---- the group's pooled queries (hi | lo) into LDS
+    {
+        constexpr int PER_ROW = 2 * D / 4;             // 8-byte pieces per row
+        for (int t = threadIdx.x; t < kSelRows * PER_ROW; t += blockDim.x) {
+            const int r = t / PER_ROW, c = t % PER_ROW;
+            uint2 v = {0u, 0u};
+            if (r < nrows) v = reinterpret_cast<const uint2 *>(qs + (int64_t)r * 2 * D)[c];
+            reinterpret_cast<uint2 *>(qf + r * qf_stride<D>())[c] = v;
         }
     }
     __syncthreads();
 
-    // ---- phase 2: per-row softmax mass, CDF cut, window, bitmask -----------
-    float *hist = hist_all + wave * 256;
-    for (int r = wave; r < nrows; r += 8) select_row(a, scores + (size_t)r * a.nBp, hist, bh, i0 + r);
+    // ---- scores, chunk by chunk, into the register row
+#pragma unroll
+    for (int cc = 0; cc < NE / 4; ++cc) {
+        if (cc < nch) {
+            const int cur = kPrefetch ? (cc & 1) : 0;
+            if (kPrefetch && cc + 1 < nch) load_k(cc + 1, cur ^ 1);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const __bf16 *qrow = qf + ii * qf_stride<D>() + 8 * kq;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const bf16x8 qh = *reinterpret_cast<const bf16x8 *>(qrow + 32 * kb);
+                const bf16x8 ql = *reinterpret_cast<const bf16x8 *>(qrow + D + 32 * kb);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql, kh[cur][kb], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kl[cur][kb], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kh[cur][kb], acc, 0, 0, 0);
+            }
+            if (!kPrefetch && cc + 1 < nch) load_k(cc + 1, 0);
+            // acc[e] = S[row 4*kq + e][key 256*cc + 16*wave + ii]
+            float *st = stage + (cc & 1) * kSelRows * kStageStride;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[(4 * kq + e) * kStageStride + 16 * wave + ii] = acc[e] * a.scale_log2;
+            __syncthreads();
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float v = st[wave * kStageStride + 64 * t + lane];
+                s[4 * cc + t] = kSelChunk * cc + 64 * t + lane < a.nB ? v : -INFINITY;   // padding keys
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) s[4 * cc + t] = -INFINITY;
+        }
+    }
+    __shared__ int32_t wave_count[kSelRows];
+    if (wave < nrows) select_cut<NE>(a, s, hist_all, bh, i0 + wave, nvc, lane, wave_count[wave]);
+    else if (lane == 0) wave_count[wave] = 0;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t t = 0;
+#pragma unroll
+        for (int w = 0; w < kSelRows; ++w) t += wave_count[w];
+        a.group_sums[g] = t;
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Large block counts: the R x nB score rows no longer fit LDS in useful numbers, so
-// the scores take a trip through HBM.  score_gemm_kernel forms S = (Qbar Kbar^T) *
-// scale * log2(e) for a whole head in 64 x 64 tiles per wave, each fp32 operand
-// split into a bf16 high part and a bf16 remainder, with the three products
-// hi*hi + hi*lo + lo*hi on v_mfma_f32_32x32x16_bf16 (relative error near 2^-16 per
-// product, fp32 accumulation); select_scores_kernel then copies one score row per
-// wave into LDS and runs the same per-row cut.
-__device__ __forceinline__ void split_bf16x8(const f32x4 &x0, const f32x4 &x1, bf16x8 &hi, bf16x8 &lo) {
-    f32x8 v = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-    hi = __builtin_convertvector(v, bf16x8);
-    f32x8 r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = v[e] - (float)hi[e];
-    lo = __builtin_convertvector(r, bf16x8);
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void score_gemm_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
-                                                         float *__restrict__ S, int32_t nB, int32_t tiles,
-                                                         int64_t n_wtiles, float scale_log2) {
-    const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
-    const int64_t wt = xcd_remap((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6), n_wtiles);
-    if (wt >= n_wtiles) return;
-    const int64_t per_head = (int64_t)tiles * tiles;
-    const int64_t bh = wt / per_head;
-    const int ti = (int)((wt % per_head) / tiles), tj = (int)(wt % tiles);
-    const float *qb = qbar + bh * nB * (int64_t)D;
-    const float *kb = kbar + bh * nB * (int64_t)D;
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
-    int ri[2], cj[2];
-    bool rok[2], cok[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        ri[u] = 64 * ti + 32 * u + l32;
-        cj[u] = 64 * tj + 32 * u + l32;
-        rok[u] = ri[u] < nB;
-        cok[u] = cj[u] < nB;
-    }
-#pragma unroll 2
-    for (int c = 0; c < D / 16; ++c) {
-        bf16x8 ahi[2], alo[2], bhi[2], blo[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            const float *qa = qb + (int64_t)ri[u] * D + 16 * c + 8 * h;
-            const float *kk = kb + (int64_t)cj[u] * D + 16 * c + 8 * h;
-            const f32x4 a0 = rok[u] ? *reinterpret_cast<const f32x4 *>(qa) : z;
-            const f32x4 a1 = rok[u] ? *reinterpret_cast<const f32x4 *>(qa + 4) : z;
-            const f32x4 b0 = cok[u] ? *reinterpret_cast<const f32x4 *>(kk) : z;
-            const f32x4 b1 = cok[u] ? *reinterpret_cast<const f32x4 *>(kk + 4) : z;
-            split_bf16x8(a0, a1, ahi[u], alo[u]);
-            split_bf16x8(b0, b1, bhi[u], blo[u]);
-        }
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[a], bhi[b], acc[a][b], 0, 0, 0);
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[a], blo[b], acc[a][b], 0, 0, 0);
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[a], bhi[b], acc[a][b], 0, 0, 0);
-            }
-    }
-    // acc[a][b][v] = S[row 64 ti + 32 a + 8 (v/4) + 4 h + v%4][col 64 tj + 32 b + l32]
-    float *Sh = S + bh * nB * (int64_t)nB;
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            if (!cok[b]) continue;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r = 64 * ti + 32 * a + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (r < nB) Sh[(int64_t)r * nB + cj[b]] = acc[a][b][v] * scale_log2;
-            }
-        }
-}
-
-__global__ __launch_bounds__(256) void select_scores_kernel(SelectArgs a, const float *__restrict__ S) {
-    extern __shared__ float smem[];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t rows = a.n_groups;                 // one row per wave here
-    const int64_t row = xcd_remap((int64_t)blockIdx.x * (blockDim.x >> 6) + wave, rows);
-    if (row >= rows) return;
-    float *sr = smem + (size_t)wave * (a.nBp + 256);
-    float *hist = sr + a.nBp;
-    const float *src = S + row * (int64_t)a.nB;
-    for (int j = lane; j < a.nB; j += 64) sr[j] = src[j];
-    wave_lds_sync();
-    select_row(a, sr, hist, row / a.nB, (int)(row % a.nB));
-}
-
-// ---------------------------------------------------------------------------
-int launch_pool(const void *q, const void *k, float *qbar, float *kbar, int64_t nblocks, int dtype, int d,
+int launch_pool(const void *q, const void *k, __bf16 *qbar, __bf16 *kbar, int64_t nblocks, int dtype, int d,
                 const PoolSide &side, hipStream_t s) {
     const int64_t waves = 2 * nblocks;
     const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
@@ -419,32 +403,26 @@ int launch_fill_thresholds(const float *host_thr, int n, float *dst, hipStream_t
     return 0;
 }
 
-int launch_select_big(const SelectArgs &a, int d, float *scores, hipStream_t s) {
-    const int tiles = (a.nB + 63) / 64;
-    const int64_t bh = a.n_groups / a.nB;
-    const int64_t n_wtiles = bh * tiles * tiles;
-    const dim3 g1((unsigned)((n_wtiles + 3) / 4)), b1(256);
-    if (d == 128)
-        score_gemm_kernel<128><<<g1, b1, 0, s>>>(a.qbar, a.kbar, scores, a.nB, tiles, n_wtiles, a.scale_log2);
+template <int D> static void launch_select_d(const SelectArgs &a, hipStream_t s) {
+    const dim3 grid((unsigned)a.n_groups), block(64 * kSelRows);
+    const size_t lds = select_lds_bytes<D>();
+    const int nvc = a.nBp / 64;
+    if (nvc <= 8)
+        select_kernel<D, 8><<<grid, block, lds, s>>>(a);
+    else if (nvc <= 16)
+        select_kernel<D, 16><<<grid, block, lds, s>>>(a);
+    else if (nvc <= 32)
+        select_kernel<D, 32><<<grid, block, lds, s>>>(a);
     else
-        score_gemm_kernel<64><<<g1, b1, 0, s>>>(a.qbar, a.kbar, scores, a.nB, tiles, n_wtiles, a.scale_log2);
-    if (hipGetLastError() != hipSuccess) return -1;
-    // as many rows (waves) per workgroup as 64 KB of LDS holds, up to 4
-    const size_t per_wave = (size_t)(a.nBp + 256) * sizeof(float);
-    int wpg = (int)(65536 / per_wave);
-    wpg = wpg > 4 ? 4 : (wpg < 1 ? 1 : wpg);
-    select_scores_kernel<<<dim3((unsigned)((a.n_groups + wpg - 1) / wpg)), dim3(64 * wpg), wpg * per_wave, s>>>(a,
-                                                                                                          scores);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
+        select_kernel<D, 64><<<grid, block, lds, s>>>(a);
 }
 
 int launch_select(const SelectArgs &a, int d, hipStream_t s) {
-    const size_t lds = ((size_t)a.R * a.nBp + 8 * 256) * sizeof(float);
-    const dim3 grid((unsigned)a.n_groups), block(512);
+    if (a.nBp > kSelectMaxBlocks) return -1;
     if (d == 128)
-        select_kernel<128><<<grid, block, lds, s>>>(a);
+        launch_select_d<128>(a, s);
     else
-        select_kernel<64><<<grid, block, lds, s>>>(a);
+        launch_select_d<64>(a, s);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

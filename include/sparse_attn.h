@@ -122,8 +122,8 @@ int64_t sparse_attn_workspace_size(const sparse_attn_shape *shape);
  *   workspace   device, >= sparse_attn_workspace_size(shape) bytes; its
  *               contents on entry do not matter.
  * Ties in the CDF order go to the lower key-block index.  A row of pooled
- * scores is held in 64 KB of LDS, so nB <= 16128 blocks per head; larger
- * grids return SPARSE_ATTN_UNSUPPORTED.
+ * scores is held in registers, so nB <= 4096 blocks per head (262,144
+ * tokens); larger grids return SPARSE_ATTN_UNSUPPORTED.
  */
 int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_select_params *params,
                            const void *q, const void *k, int32_t *row_ptr, int32_t *col_idx,

@@ -55,7 +55,7 @@ def test_capacity_and_workspace_formulas():
     expect = al(expect + 4 * rows * 128)
     expect = al(expect + 8 * rows * (nbp // 64))
     expect = al(expect + 4 * rows)
-    expect = al(expect + 4 * ((rows + 63) // 64))
+    expect = al(expect + 4 * 12 * ((nB + 15) // 16))     # kept-block totals per 16-row group
     assert B.sparse_attn_workspace_size(s) == expect
 
 
@@ -117,8 +117,10 @@ def test_select_rejects_bad_head_threshold():
 
 
 def test_select_rejects_too_many_blocks():
-    s = _shape(heads=1, grid=(256, 128, 64))    # 32,768 blocks: a score row does not fit the selection LDS
+    s = _shape(heads=1, grid=(65, 64, 64))      # 4,160 blocks: a row no longer fits the selection's registers
     assert _select(s) == B.SPARSE_ATTN_UNSUPPORTED
+    s = _shape(heads=1, grid=(64, 64, 64))      # 4,096 blocks: accepted, fails later on the fake workspace size
+    assert _select(s, wsb=1024) == B.SPARSE_ATTN_WORKSPACE
 
 
 def _forward(shape, q=A, k=A, v=A, rp=A, ci=A, cc=100, out=A, lse=None, ws=A, wsb=None):
