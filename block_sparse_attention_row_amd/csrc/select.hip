@@ -127,66 +127,71 @@ template <int D> constexpr size_t select_lds_bytes() {
            (size_t)kSelRows * 256 * 4;
 }
 
-// The cut of row i of head bh, run by one wave on its register row s (scaled scores,
-// -inf for padding); writes the row's bitmask and count, and its count to `out`.
+// The cut of row i of head bh (threshold thr), run by one wave on its register row s
+// (scaled scores, -inf for padding keys); writes the row's bitmask and count, and
+// its count to `out`.
 template <int NE>
 __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], float *hist_all, int64_t bh, int i,
-                                           int nvc, int lane, int32_t &out) {
+                                           float thr, int lane, int32_t &out) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t row = bh * a.nB + i;
-    const int h = (int)(bh % a.H);
-    const float thr = a.thr[h];
+    const int nvc = a.nBp >> 6;
     const bool keep_all = !(thr < 1.f);
     uint32_t *list = reinterpret_cast<uint32_t *>(hist_all + wave * 256);   // up to 64 keys of the bracket
 
-    // e_j = 2^(s_j - max) in place (0 for padding), Z, and the smallest positive key
+    // e_j = 2^(s_j - max) in place (0 for padding), Z, the smallest positive key and
+    // how many keys are positive
     float mx = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < NE; ++c)
-        if (c < nvc) mx = fmaxf(mx, s[c]);
+    for (int c = 0; c < NE; ++c) mx = fmaxf(mx, s[c]);
     mx = wave_max_u(mx);
     float z = 0.f;
-    uint32_t kmin = 0xffffffffu;
+    uint32_t kmin = 0xffffffffu, npos = 0;
 #pragma unroll
     for (int c = 0; c < NE; ++c) {
-        if (c < nvc) {
-            const float pe = __builtin_amdgcn_exp2f(s[c] - mx);
-            s[c] = pe;
-            z += pe;
-            kmin = min(kmin, __float_as_uint(pe) - 1u);     // padding (0) wraps to the top
-        }
+        const float pe = __builtin_amdgcn_exp2f(s[c] - mx);
+        s[c] = pe;
+        z += pe;
+        kmin = min(kmin, __float_as_uint(pe) - 1u);         // padding (0) wraps to the top
+        npos += (uint32_t)__popcll(__ballot(pe > 0.f));
     }
-    const float thrz = thr * wave_sum_u(z);
+    const float Z = wave_sum_u(z);
+    const float thrz = thr * Z;
 
     // Crossing value v* and the mass M strictly above it.  Keys are the fp32 bit
-    // patterns of the e_j (order-preserving for e >= 0).  Bisection over the key
-    // bracket (lo, hi] keeps  mass(key > hi) = Mhi < thr*Z <= mass(key > lo); each step
-    // costs one compare/select/add per element plus a wave sum, and the compare
-    // masks' popcounts track how many elements the bracket holds.  Once at most 64
-    // remain they are compacted to LDS, sorted across the lanes, and the crossing
-    // is read off their prefix sums.
+    // patterns of the e_j (order-preserving for e >= 0).  The key bracket (lo, hi]
+    // keeps  Mhi = mass(key > hi) < thr*Z <= Mlo = mass(key > lo);  each step splits it
+    // at a pivot and costs one compare/select/add per element plus a wave sum; the
+    // compare masks' popcounts track how many elements the bracket holds.  Pivots
+    // alternate between regula falsi on the values (the mass above a value is linear
+    // in the value when the e_j are spread evenly in log scale) and halving the key
+    // range, which bounds the steps.  Once at most 64 elements remain they are
+    // compacted to LDS, sorted across the lanes, and the crossing is read off their
+    // prefix sums.
     uint32_t vstar = 0x3f800000u;
     float M = 0.f;
     if (!keep_all) {
-        kmin = wave_min_u32(kmin);
-        uint32_t lo = kmin, hi = 0x3f800000u;            // every e_j <= 1, the row max is exactly 1
-        float Mhi = 0.f;
-        uint32_t clo = 0, chi = 0;                        // counts of key > lo, key > hi
-#pragma unroll
-        for (int c = 0; c < NE; ++c)
-            if (c < nvc) clo += __popcll(__ballot(__float_as_uint(s[c]) > lo));
+        uint32_t lo = wave_min_u32(kmin), hi = 0x3f800000u;   // every e_j <= 1, the row max is exactly 1
+        float Mhi = 0.f, Mlo = Z;
+        uint32_t clo = npos, chi = 0;                         // counts of key > lo, key > hi
 #pragma unroll 1
-        while (clo - chi > 64 && hi - lo > 1) {
-            const uint32_t p = lo + ((hi - lo) >> 1);
+        for (int step = 0; clo - chi > 64 && hi - lo > 1; ++step) {
+            uint32_t p;
+            if (step < 2 || (step & 1) == 0) {
+                const float vlo = __uint_as_float(lo), vhi = __uint_as_float(hi);
+                const float f = (thrz - Mhi) / (Mlo - Mhi);
+                p = __float_as_uint(vhi - f * (vhi - vlo));
+                p = min(max(p, lo + 1u), hi - 1u);
+            } else {
+                p = lo + ((hi - lo) >> 1);
+            }
             float acc = 0.f;
             uint32_t cnt = 0;
 #pragma unroll
             for (int c = 0; c < NE; ++c) {
-                if (c < nvc) {
-                    const bool gt = __float_as_uint(s[c]) > p;
-                    acc += gt ? s[c] : 0.f;
-                    cnt += __popcll(__ballot(gt));
-                }
+                const bool gt = __float_as_uint(s[c]) > p;
+                acc += gt ? s[c] : 0.f;
+                cnt += (uint32_t)__popcll(__ballot(gt));
             }
             const float A = wave_sum_u(acc);
             if (A < thrz) {
@@ -195,6 +200,7 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
                 chi = cnt;
             } else {
                 lo = p;
+                Mlo = A;
                 clo = cnt;
             }
         }
@@ -204,17 +210,12 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
             uint32_t base = 0;
 #pragma unroll
             for (int c = 0; c < NE; ++c) {
-                if (c < nvc) {
-                    const uint32_t u = __float_as_uint(s[c]);
-                    const bool in = u > lo && u <= hi;
-                    const uint64_t m = __ballot(in);
-                    if (in) {
-                        const uint32_t pos =
-                            base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                        list[pos] = u;
-                    }
-                    base += (uint32_t)__popcll(m);
-                }
+                const uint32_t u = __float_as_uint(s[c]);
+                const bool in = u > lo && u <= hi;
+                const uint64_t m = __ballot(in);
+                if (in)
+                    list[base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = u;
+                base += (uint32_t)__popcll(m);
             }
             wave_lds_sync();
             const uint32_t n = clo - chi;
@@ -248,31 +249,29 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
     uint32_t ties_before = 0, count = 0, wlo = 0, whi = 0;
 #pragma unroll
     for (int c = 0; c < NE; ++c) {
-        if (c < nvc) {
-            const int j = 64 * c + lane;
-            uint64_t m;
-            if (keep_all) {
-                m = __ballot(j < a.nB);
-            } else {
-                const uint32_t u = __float_as_uint(s[c]);
-                m = __ballot(u > vstar);
-                const uint64_t tb = __ballot(u == vstar);      // padding (0) never equals v* > 0
-                if (tb) {
-                    const uint32_t rank =
-                        ties_before + __builtin_amdgcn_mbcnt_hi((uint32_t)(tb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)tb, 0u));
-                    m |= __ballot(u == vstar && M + (float)rank * vstar_f < thrz);
-                    ties_before += (uint32_t)__popcll(tb);
-                }
+        const int j = 64 * c + lane;
+        uint64_t m;
+        if (keep_all) {
+            m = __ballot(j < a.nB);
+        } else {
+            const uint32_t u = __float_as_uint(s[c]);
+            m = __ballot(u > vstar);
+            const uint64_t tb = __ballot(u == vstar);      // padding (0) never equals v* > 0
+            if (tb) {
+                const uint32_t rank =
+                    ties_before + __builtin_amdgcn_mbcnt_hi((uint32_t)(tb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)tb, 0u));
+                m |= __ballot(u == vstar && M + (float)rank * vstar_f < thrz);
+                ties_before += (uint32_t)__popcll(tb);
             }
-            if (a.window) {
-                const int tj = j / nTyx, yj = (j / a.nTx) % a.nTy, xj = j % a.nTx;
-                m |= __ballot(j < a.nB && abs(tj - ti) <= a.wt && abs(yj - yi) <= a.wh && abs(xj - xi) <= a.ww);
-            }
-            count += (uint32_t)__popcll(m);
-            if (lane == c) {
-                wlo = (uint32_t)m;
-                whi = (uint32_t)(m >> 32);
-            }
+        }
+        if (a.window) {
+            const int tj = j / nTyx, yj = (j / a.nTx) % a.nTy, xj = j % a.nTx;
+            m |= __ballot(j < a.nB && abs(tj - ti) <= a.wt && abs(yj - yi) <= a.wh && abs(xj - xi) <= a.ww);
+        }
+        count += (uint32_t)__popcll(m);
+        if (lane == c) {
+            wlo = (uint32_t)m;
+            whi = (uint32_t)(m >> 32);
         }
     }
     if (lane < nvc) a.bits[row * (int64_t)nvc + lane] = ((uint64_t)whi << 32) | wlo;
@@ -282,11 +281,15 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
     }
 }
 
+// NE = 4 * ceil(nB / 256): the register row length in 64-key words (chunks of 256 keys).
 template <int D, int NE>
 __global__ __launch_bounds__(1024) void select_kernel(SelectArgs a) {
     static_assert(NE % 4 == 0 && NE <= 64, "NE: register row length in 64-key words");
     constexpr int KB = D / 32;                     // k-blocks of one 16x16x32 product
-    constexpr bool kPrefetch = NE == 16 || NE == 32;   // registers for the next chunk's operands (NE = 8: two workgroups per CU instead)
+    constexpr int NCH = NE / 4;                    // score chunks
+    // registers for the next chunk's operands where they fit; at NE <= 8 two
+    // workgroups share a CU instead
+    constexpr bool kPrefetch = NE > 8 && NE <= 32;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     __bf16 *qf = reinterpret_cast<__bf16 *>(smem_raw);                              // [16][2D+8]
     float *stage = reinterpret_cast<float *>(smem_raw + (size_t)kSelRows * qf_stride<D>() * 2);  // [2][16][260]
@@ -294,78 +297,66 @@ __global__ __launch_bounds__(1024) void select_kernel(SelectArgs a) {
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t g = xcd_remap(blockIdx.x, a.n_groups);
-    const int64_t bh = g / a.groups_per_head;
-    const int i0 = (int)(g % a.groups_per_head) * kSelRows;
+    const uint32_t g = (uint32_t)xcd_remap(blockIdx.x, a.n_groups);
+    const uint32_t bh = g / (uint32_t)a.groups_per_head;
+    const int i0 = (int)(g - bh * (uint32_t)a.groups_per_head) * kSelRows;
     const int nrows = min(kSelRows, a.nB - i0);
-    const int nvc = a.nBp >> 6;                    // 64-key words in a row
-    const int nch = (a.nB + kSelChunk - 1) / kSelChunk;
-    const __bf16 *qs = a.qbar + (bh * a.nB + i0) * (int64_t)(2 * D);
-    const __bf16 *ks = a.kbar + (bh * a.nB) * (int64_t)(2 * D);
+    const __bf16 *qs = a.qbar + ((int64_t)bh * a.nB + i0) * (2 * D);
+    const __bf16 *ks = a.kbar + ((int64_t)bh * a.nB) * (2 * D);
+    const float thr = a.thr[bh % (uint32_t)a.H];
+
+    // ---- the group's pooled queries (hi | lo) and chunk 0's keys, loads issued together
+    constexpr int PER_ROW = 2 * D / 4;             // 8-byte pieces per query row
+    const int qr = threadIdx.x / PER_ROW, qc = threadIdx.x % PER_ROW;
+    uint2 qv = {0u, 0u};
+    if (qr < nrows) qv = reinterpret_cast<const uint2 *>(qs + (int64_t)qr * 2 * D)[qc];
 
     const int ii = lane & 15, kq = lane >> 4;
     float s[NE];
     bf16x8 kh[2][KB], kl[2][KB];
+    // keys past nB read row 0 (in bounds); their scores land on padding columns
     auto load_k = [&](int cc, int slot) {
         const int jj = kSelChunk * cc + 16 * wave + ii;
-        const bool ok = jj < a.nB;
-        const __bf16 *kr = ks + (int64_t)(ok ? jj : 0) * (2 * D) + 8 * kq;
+        const __bf16 *kr = ks + (int64_t)(jj < a.nB ? jj : 0) * (2 * D) + 8 * kq;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            bf16x8 h = *reinterpret_cast<const bf16x8 *>(kr + 32 * kb);
-            bf16x8 l = *reinterpret_cast<const bf16x8 *>(kr + D + 32 * kb);
-            kh[slot][kb] = ok ? h : bf16x8{};
-            kl[slot][kb] = ok ? l : bf16x8{};
+            kh[slot][kb] = *reinterpret_cast<const bf16x8 *>(kr + 32 * kb);
+            kl[slot][kb] = *reinterpret_cast<const bf16x8 *>(kr + D + 32 * kb);
         }
     };
-    load_k(0, 0);     // in flight while the queries are staged
-
-    // ---- the group's pooled queries (hi | lo) into LDS
-    {
-        constexpr int PER_ROW = 2 * D / 4;             // 8-byte pieces per row
-        for (int t = threadIdx.x; t < kSelRows * PER_ROW; t += blockDim.x) {
-            const int r = t / PER_ROW, c = t % PER_ROW;
-            uint2 v = {0u, 0u};
-            if (r < nrows) v = reinterpret_cast<const uint2 *>(qs + (int64_t)r * 2 * D)[c];
-            reinterpret_cast<uint2 *>(qf + r * qf_stride<D>())[c] = v;
-        }
-    }
+    load_k(0, 0);
+    if (qr < kSelRows) reinterpret_cast<uint2 *>(qf + qr * qf_stride<D>())[qc] = qv;
     __syncthreads();
 
     // ---- scores, chunk by chunk, into the register row
 #pragma unroll
-    for (int cc = 0; cc < NE / 4; ++cc) {
-        if (cc < nch) {
-            const int cur = kPrefetch ? (cc & 1) : 0;
-            if (kPrefetch && cc + 1 < nch) load_k(cc + 1, cur ^ 1);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const __bf16 *qrow = qf + ii * qf_stride<D>() + 8 * kq;
+    for (int cc = 0; cc < NCH; ++cc) {
+        const int cur = kPrefetch ? (cc & 1) : 0;
+        if (kPrefetch && cc + 1 < NCH) load_k(cc + 1, cur ^ 1);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const __bf16 *qrow = qf + ii * qf_stride<D>() + 8 * kq;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const bf16x8 qh = *reinterpret_cast<const bf16x8 *>(qrow + 32 * kb);
-                const bf16x8 ql = *reinterpret_cast<const bf16x8 *>(qrow + D + 32 * kb);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql, kh[cur][kb], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kl[cur][kb], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kh[cur][kb], acc, 0, 0, 0);
-            }
-            if (!kPrefetch && cc + 1 < nch) load_k(cc + 1, 0);
-            // acc[e] = S[row 4*kq + e][key 256*cc + 16*wave + ii]
-            float *st = stage + (cc & 1) * kSelRows * kStageStride;
+        for (int kb = 0; kb < KB; ++kb) {
+            const bf16x8 qh = *reinterpret_cast<const bf16x8 *>(qrow + 32 * kb);
+            const bf16x8 ql = *reinterpret_cast<const bf16x8 *>(qrow + D + 32 * kb);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql, kh[cur][kb], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kl[cur][kb], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kh[cur][kb], acc, 0, 0, 0);
+        }
+        if (!kPrefetch && cc + 1 < NCH) load_k(cc + 1, 0);
+        // acc[e] = S[row 4*kq + e][key 256*cc + 16*wave + ii]
+        float *st = stage + (cc & 1) * kSelRows * kStageStride;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) st[(4 * kq + e) * kStageStride + 16 * wave + ii] = acc[e] * a.scale_log2;
-            __syncthreads();
+        for (int e = 0; e < 4; ++e) st[(4 * kq + e) * kStageStride + 16 * wave + ii] = acc[e] * a.scale_log2;
+        __syncthreads();
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float v = st[wave * kStageStride + 64 * t + lane];
-                s[4 * cc + t] = kSelChunk * cc + 64 * t + lane < a.nB ? v : -INFINITY;   // padding keys
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) s[4 * cc + t] = -INFINITY;
+        for (int t = 0; t < 4; ++t) {
+            const float v = st[wave * kStageStride + 64 * t + lane];
+            s[4 * cc + t] = kSelChunk * cc + 64 * t + lane < a.nB ? v : -INFINITY;   // padding keys
         }
     }
     __shared__ int32_t wave_count[kSelRows];
-    if (wave < nrows) select_cut<NE>(a, s, hist_all, bh, i0 + wave, nvc, lane, wave_count[wave]);
+    if (wave < nrows) select_cut<NE>(a, s, hist_all, bh, i0 + wave, thr, lane, wave_count[wave]);
     else if (lane == 0) wave_count[wave] = 0;
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -403,26 +394,23 @@ int launch_fill_thresholds(const float *host_thr, int n, float *dst, hipStream_t
     return 0;
 }
 
-template <int D> static void launch_select_d(const SelectArgs &a, hipStream_t s) {
-    const dim3 grid((unsigned)a.n_groups), block(64 * kSelRows);
-    const size_t lds = select_lds_bytes<D>();
-    const int nvc = a.nBp / 64;
-    if (nvc <= 8)
-        select_kernel<D, 8><<<grid, block, lds, s>>>(a);
-    else if (nvc <= 16)
-        select_kernel<D, 16><<<grid, block, lds, s>>>(a);
-    else if (nvc <= 32)
-        select_kernel<D, 32><<<grid, block, lds, s>>>(a);
-    else
-        select_kernel<D, 64><<<grid, block, lds, s>>>(a);
+template <int D, int NCH> static void launch_select_nch(const SelectArgs &a, int nch, hipStream_t s) {
+    if constexpr (NCH <= kSelectMaxBlocks / kSelChunk) {
+        if (nch == NCH) {
+            select_kernel<D, 4 * NCH><<<dim3((unsigned)a.n_groups), dim3(64 * kSelRows), select_lds_bytes<D>(), s>>>(a);
+            return;
+        }
+        launch_select_nch<D, NCH + 1>(a, nch, s);
+    }
 }
 
 int launch_select(const SelectArgs &a, int d, hipStream_t s) {
     if (a.nBp > kSelectMaxBlocks) return -1;
+    const int nch = (a.nB + kSelChunk - 1) / kSelChunk;
     if (d == 128)
-        launch_select_d<128>(a, s);
+        launch_select_nch<128, 1>(a, nch, s);
     else
-        launch_select_d<64>(a, s);
+        launch_select_nch<64, 1>(a, nch, s);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
