@@ -7,8 +7,8 @@
 // NABLA").  The result equals a dense softmax over the tokens of the kept
 // blocks.
 //
-// Layout of the work (one workgroup of 2 waves per query block, 32 queries
-// per wave):
+// Layout of the work (bf16): a workgroup of 4 waves serves a pair of neighbouring
+// query blocks, 32 queries per wave, and walks the union of the two CSR rows;
 //   * the transposed score tile S^T = K Q^T is formed on MFMA with K as the
 //     A operand (from LDS) and Q as the B operand (kept in registers), so that
 //     each lane's accumulators belong to one query: the softmax row max needs
@@ -16,11 +16,11 @@
 //     output is a per-lane scalar;
 //   * O^T += V^T P^T reuses the S^T accumulators directly as the B operand:
 //     the eight accumulators a lane holds for a 16-key chunk are exactly the
-//     eight keys it must supply, provided V^T is stored in LDS with the keys
-//     of each 16-key chunk in the order {0-3, 8-11, 4-7, 12-15} (the
-//     transpose is done in registers while the tile is copied to LDS);
-//   * the next tile's K and V are fetched into registers while the current
-//     tile is computed.
+//     eight keys it must supply, once V is read transposed from LDS in the key
+//     order {0-3, 8-11, 4-7, 12-15} of each 16-key chunk;
+//   * K and V tiles stream from global memory straight into double-buffered LDS
+//     (K two tiles ahead of use, V one), and the scores of tile j+1 are formed
+//     while the softmax of tile j runs on the VALU.
 #include <type_traits>
 
 #include "common.h"
@@ -155,13 +155,15 @@ __device__ __forceinline__ bf16x8 v_frag(const char *V, int lane, int kc, int dt
 template <int D>
 __device__ __forceinline__ void tile_pv(const char *V, const bf16x8 *pf, int lane, f32x16 *acc_o) {
     constexpr int NDT = TileGeo<D>::NDT, NM = 4 * NDT;
-    bf16x8 vf[3];
+    // four-slot ring: the read for MFMA i+2 lands in the slot MFMA i-2 used, so it
+    // can be issued before MFMA i without waiting on MFMA i-1's operand reads
+    bf16x8 vf[4];
     vf[0] = v_frag<D>(V, lane, 0, 0);
     vf[1] = v_frag<D>(V, lane, 1 / NDT, 1 % NDT);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
-        if (i + 2 < NM) vf[(i + 2) % 3] = v_frag<D>(V, lane, (i + 2) / NDT, (i + 2) % NDT);
-        acc_o[i % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 3], pf[i / NDT], acc_o[i % NDT], 0, 0, 0);
+        if (i + 2 < NM) vf[(i + 2) % 4] = v_frag<D>(V, lane, (i + 2) / NDT, (i + 2) % NDT);
+        acc_o[i % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 4], pf[i / NDT], acc_o[i % NDT], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -184,14 +186,14 @@ __device__ __forceinline__ void tile_scores_probs(const char *K, const bf16x8 *q
         sn[0][v] = 0.f;
         sn[1][v] = 0.f;
     }
-    bf16x8 kf[3];
+    bf16x8 kf[4];                                 // four-slot ring, as in tile_pv
     kf[0] = kfrag(0);
     kf[1] = kfrag(1);
     f32x8 pv;
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
-        if (i + 2 < NM) kf[(i + 2) % 3] = kfrag(i + 2);
-        sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 3], qf[i >> 1], sn[i & 1], 0, 0, 0);
+        if (i + 2 < NM) kf[(i + 2) % 4] = kfrag(i + 2);
+        sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % 4], qf[i >> 1], sn[i & 1], 0, 0, 0);
         // probabilities PER*i .. PER*i + PER - 1 of the current tile (8 per 16-key chunk)
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
@@ -233,7 +235,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     const char *kg = (const char *)a.k + bh * N * ROWB + 16 * wave * ROWB;
     const char *vg = (const char *)a.v + bh * N * ROWB + 16 * wave * ROWB;
     const_i32 *rp = (const_i32 *)a.row_ptr;
-    const_i32 *cidx = (const_i32 *)a.col_idx;
     const float c = a.scale_log2;
 
     // CSR ranges of the two rows (the second may not exist when nB is odd)
@@ -281,25 +282,39 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     };
 
     // merged walk over the two rows' ascending lists (entries out of range or not
-    // ascending are skipped)
+    // ascending are skipped).  Each row's upcoming entries sit in a VGPR window (lane
+    // l holds entry base + l) read with v_readlane; the following window is loaded
+    // one window ahead, so the walk never waits on memory.
     constexpr int kNone = 0x7fffffff;
-    int64_t ia = begA, ib = begB;
+    const int32_t *cv = a.col_idx;
+    auto window = [&](int64_t base, int64_t e) { return base + lane < e ? cv[base + lane] : kNone; };
+    int64_t baseA = begA, baseB = begB;
+    int posA = 0, posB = 0;
+    int winA = window(baseA, endA), nxtA = window(baseA + 64, endA);
+    int winB = window(baseB, endB), nxtB = window(baseB + 64, endB);
     int lastA = -1, lastB = -1;
-    auto peek = [&](int64_t &i, int64_t e, int last) {
-        while (i < e) {
-            const int cc = cidx[i];
+    auto peek = [&](int64_t &base, int &pos, int &win, int &nxt, int64_t e, int last) {
+        while (base + pos < e) {
+            if (pos == 64) {
+                base += 64;
+                pos = 0;
+                win = nxt;
+                nxt = window(base + 64, e);
+            }
+            const int cc = __builtin_amdgcn_readlane(win, pos);
             if (cc > last && cc < a.nB) return cc;
-            ++i;
+            ++pos;
         }
         return kNone;
     };
     // next union tile: its column and whether this wave's row keeps it
     auto next_union = [&](int &col, bool &mine) {
-        const int cA = peek(ia, endA, lastA), cB = peek(ib, endB, lastB);
+        const int cA = peek(baseA, posA, winA, nxtA, endA, lastA);
+        const int cB = peek(baseB, posB, winB, nxtB, endB, lastB);
         col = cA < cB ? cA : cB;
         const bool inA = cA == col && col != kNone, inB = cB == col && col != kNone;
-        if (inA) { lastA = cA; ++ia; }
-        if (inB) { lastB = cB; ++ib; }
+        if (inA) { lastA = cA; ++posA; }
+        if (inB) { lastB = cB; ++posB; }
         mine = grp ? inB : inA;
     };
 
@@ -328,8 +343,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     // those of tile j+1 go to sn; buffer offsets are compile-time constants.
     auto step = [&](auto bj_tag, f32x16 *sc, f32x16 *sn) {
         constexpr int BJ = decltype(bj_tag)::value;
-        next_union(col2, mine2);
         wait_vmcnt<0>();            // this wave's part of K(j+1) and V(j) has landed
+        next_union(col2, mine2);    // (after the wait: a window load never waits on tile loads)
         __syncthreads();            // ... and everyone's; K(j) and V(j-1) are free
         if (col2 != kNone) issue_k(col2, BJ);
         if (col1 != kNone) issue_v(col1, BJ ^ 1);
