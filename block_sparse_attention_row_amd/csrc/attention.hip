@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     const int t = threadIdx.x, lane = t & 63, hh = lane >> 5, l32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int grp = wave >> 1;                    // 0: first query block of the pair, 1: second
-    const int64_t pair = xcd_remap(blockIdx.x, a.n_pairs);
+    const int64_t pair = xcd_chunk_remap<256>(blockIdx.x, a.n_pairs);
     const int64_t bh = pair / a.pairs_per_head;
     const int i0 = (int)(pair % a.pairs_per_head) * 2;
     const int64_t N = (int64_t)a.nB * 64;

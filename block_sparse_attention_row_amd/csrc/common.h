@@ -139,6 +139,19 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t n) {
     return x * per + (x < rem ? x : rem) + k;
 }
 
+// Like xcd_remap, but the work items are dealt to the XCDs in runs of C consecutive
+// items, round-robin: every XCD still works on neighbouring items at any moment
+// (they share its L2), while items whose cost drifts along the index (heads with
+// different thresholds) spread evenly over the XCDs.  Items past the last whole
+// round of runs fall back to xcd_remap.  A bijection on [0, n).
+template <int64_t C> __device__ __forceinline__ int64_t xcd_chunk_remap(int64_t bid, int64_t n) {
+    constexpr int64_t kXcd = 8;
+    const int64_t full = n / (kXcd * C) * (kXcd * C);
+    if (bid >= full) return full + xcd_remap(bid - full, n - full);
+    const int64_t x = bid % kXcd, k = bid / kXcd;
+    return (k / C) * (kXcd * C) + x * C + k % C;
+}
+
 // (1, 1) in bf16, for row sums with v_dot2_f32_bf16
 #define kOnes2 ((bf16x2){(__bf16)1.0f, (__bf16)1.0f})
 
