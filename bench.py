@@ -187,11 +187,12 @@ def main():
     value = flops / (ms_step * 1e-3) / 1e12
     attn_tflops = flops / (attn_ms_avg * 1e-3) / 1e12
 
-    # selection alone, each repetition after a 1 GiB sweep so Q and K do not sit in the last-level cache
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    # selection alone, each repetition after a read-only 1 GiB sweep, so that Q and K do
+    # not sit in the last-level cache and no dirty lines are left to write back
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     sel_ms = []
     for _ in range(0 if args.no_select_timing else 10):
-        flush.add_(1.0)
+        flush.sum()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         select()
