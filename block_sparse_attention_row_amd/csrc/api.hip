@@ -59,8 +59,13 @@ float effective_scale(const sparse_attn_shape *s) {
 int64_t groups_per_head(const Dims &d) { return (d.nB + kGroupRows - 1) / kGroupRows; }
 int64_t n_groups(const Dims &d) { return d.B * d.H * groups_per_head(d); }
 
+int64_t n_pairs(const Dims &d) { return d.B * d.H * ((d.nB + 1) / 2); }
+int64_t max_slots(const Dims &d) { return n_pairs(d) * 4 < kMaxSlots ? n_pairs(d) * 4 : kMaxSlots; }
+
 struct Layout {
-    int64_t thr, qbar, kbar, bits, counts, groups, total;
+    int64_t thr, qbar, kbar, bits, counts, groups;                       // selection
+    int64_t items, plan_counts, pair_flag, merge, part_o, part_lse;      // attention row splitting
+    int64_t total;
 };
 
 Layout layout(const Dims &d) {
@@ -78,6 +83,19 @@ Layout layout(const Dims &d) {
     off = align_up(off + 4 * d.rows, kAlign);
     l.groups = off;
     off = align_up(off + 4 * n_groups(d), kAlign);
+    const int64_t ms = max_slots(d);
+    l.items = off;
+    off = align_up(off + (int64_t)sizeof(SplitItem) * ms, kAlign);
+    l.plan_counts = off;
+    off = align_up(off + 16, kAlign);
+    l.pair_flag = off;
+    off = align_up(off + 4 * n_pairs(d), kAlign);
+    l.merge = off;
+    off = align_up(off + 12 * ms, kAlign);
+    l.part_o = off;
+    off = align_up(off + 4 * ms * 2 * 64 * d.D, kAlign);
+    l.part_lse = off;
+    off = align_up(off + 4 * ms * 2 * 64, kAlign);
     l.total = off;
     return l;
 }
@@ -216,9 +234,17 @@ int32_t sparse_attn_forward(const sparse_attn_shape *shape, const void *q, const
     a.lse = lse;
     a.rows = d.rows;
     a.pairs_per_head = (int32_t)((d.nB + 1) / 2);
-    a.n_pairs = d.B * d.H * a.pairs_per_head;
+    a.n_pairs = n_pairs(d);
     a.nB = (int32_t)d.nB;
     a.scale_log2 = effective_scale(shape) * kLog2e;
+    char *ws = (char *)workspace;
+    a.plan.items = (SplitItem *)(ws + L.items);
+    a.plan.counts = (int32_t *)(ws + L.plan_counts);
+    a.plan.pair_flag = (int32_t *)(ws + L.pair_flag);
+    a.plan.merge = (int32_t *)(ws + L.merge);
+    a.plan.part_o = (float *)(ws + L.part_o);
+    a.plan.part_lse = (float *)(ws + L.part_lse);
+    a.plan.max_slots = (int32_t)max_slots(d);
     if (launch_attention(a, shape->dtype, (int)d.D, (hipStream_t)stream)) return SPARSE_ATTN_HIP_ERROR;
     return SPARSE_ATTN_OK;
 }

@@ -228,7 +228,20 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     const int t = threadIdx.x, lane = t & 63, hh = lane >> 5, l32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int grp = wave >> 1;                    // 0: first query block of the pair, 1: second
-    const int64_t pair = xcd_chunk_remap<256>(blockIdx.x, a.n_pairs);
+    // work item: the first max_slots workgroups take the pieces of split pairs (so that
+    // long work starts first), the rest take whole pairs that were not split
+    const int64_t ms = a.plan.max_slots;
+    int64_t pair;
+    SplitItem it = {};
+    const bool split = (int64_t)blockIdx.x < ms;
+    if (split) {
+        if ((int64_t)blockIdx.x >= a.plan.counts[0]) return;
+        it = a.plan.items[blockIdx.x];
+        pair = it.pair;
+    } else {
+        pair = xcd_chunk_remap<256>(blockIdx.x - ms, a.n_pairs);
+        if (a.plan.pair_flag[pair]) return;
+    }
     const int64_t bh = pair / a.pairs_per_head;
     const int i0 = (int)(pair % a.pairs_per_head) * 2;
     const int64_t N = (int64_t)a.nB * 64;
@@ -248,8 +261,33 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         if (e < b) e = b;
     };
     int64_t begA, endA, begB = 0, endB = 0;
-    clamp_range(rowA, begA, endA);
-    if (hasB) clamp_range(rowA + 1, begB, endB);
+    int lastA = -1, lastB = -1;
+    if (split) {
+        begA = it.a0;
+        endA = it.a1;
+        begB = it.b0;
+        endB = it.b1;
+        // the whole-row walk would arrive at the piece with the largest valid column
+        // of the entries before it as its last column
+        auto prefix_max = [&](int64_t from, int64_t to) {
+            int m = -1;
+            for (int64_t i = from + lane; i < to; i += 64) {
+                const int cc = a.col_idx[i];
+                if (cc >= 0 && cc < a.nB) m = cc > m ? cc : m;
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const int u = __shfl_xor(m, o, 64);
+                m = u > m ? u : m;
+            }
+            return __builtin_amdgcn_readfirstlane(m);
+        };
+        lastA = prefix_max(it.ra, begA);
+        lastB = prefix_max(it.rb, begB);
+    } else {
+        clamp_range(rowA, begA, endA);
+        if (hasB) clamp_range(rowA + 1, begB, endB);
+    }
     const bool has_row = grp == 0 || hasB;
 
     // Q fragments (B operand of S^T): query 32*(wave&1) + l32 of this wave's block, d = 16c + 8hh .. +7
@@ -292,7 +330,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     int posA = 0, posB = 0;
     int winA = window(baseA, endA), nxtA = window(baseA + 64, endA);
     int winB = window(baseB, endB), nxtB = window(baseB + 64, endB);
-    int lastA = -1, lastB = -1;
     auto peek = [&](int64_t &base, int &pos, int &win, int &nxt, int64_t e, int last) {
         while (base + pos < e) {
             if (pos == 64) {
@@ -378,6 +415,21 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     // epilogue: normalise and store; lane owns query l32, d = 32 dt + 8 rr + 4 hh + {0..3}
     const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (split) {
+        // piece of a split pair: the normalised partial output and its log2-sum-exp
+        const int q = 32 * (wave & 1) + l32;
+        float *po = a.plan.part_o + ((int64_t)it.slot * 2 + grp) * (D * 64);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) po[(32 * dt + 8 * rr + 4 * hh + e) * 64 + q] = acc_o[dt][4 * rr + e] * inv;
+        if (hh == 0)
+            a.plan.part_lse[((int64_t)it.slot * 2 + grp) * 64 + q] =
+                l_tot > 0.f ? m_run * c + __log2f(l_tot) : -INFINITY;
+        return;
+    }
     const int64_t qrow = bh * N + (int64_t)(i0 + grp) * 64 + 32 * (wave & 1) + l32;
     __bf16 *og = (__bf16 *)a.out + qrow * D;
 #pragma unroll
@@ -390,6 +442,182 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
             *reinterpret_cast<bf16x4 *>(og + 32 * dt + 8 * rr + 4 * hh) = __builtin_convertvector(w, bf16x4);
         }
     if (a.lse && hh == 0) a.lse[qrow] = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// Row splitting: the plan (one workgroup) and the merge of the pieces.
+
+// CSR range of row r, clamped as the attention kernel clamps it.
+__device__ __forceinline__ void row_range(const AttnArgs &a, int64_t r, int64_t &b, int64_t &e) {
+    b = a.row_ptr[r];
+    e = a.row_ptr[r + 1];
+    e = e < a.col_count ? e : a.col_count;
+    b = b < 0 ? 0 : b;
+    if (e < b) e = b;
+}
+__device__ __forceinline__ void pair_ranges(const AttnArgs &a, int64_t p, int64_t &bA, int64_t &eA, int64_t &bB,
+                                            int64_t &eB) {
+    const int64_t bh = p / a.pairs_per_head;
+    const int i0 = (int)(p % a.pairs_per_head) * 2;
+    row_range(a, bh * a.nB + i0, bA, eA);
+    bB = eB = 0;
+    if (i0 + 1 < a.nB) row_range(a, bh * a.nB + i0 + 1, bB, eB);
+}
+
+// Sum over the 1024 threads of the workgroup, returned to every thread.
+__device__ __forceinline__ int64_t block_sum64(int64_t v, int64_t *lds16) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) lds16[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int64_t t = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) t += lds16[w];
+    return t;
+}
+// Exclusive prefix over the 1024 threads (thread order) and the total.
+__device__ __forceinline__ int32_t block_scan32(int32_t v, int32_t *lds16, int32_t &total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+    }
+    __syncthreads();
+    if (lane == 63) lds16[wave] = incl;
+    __syncthreads();
+    int32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        const int32_t x = lds16[w];
+        before += w < wave ? x : 0;
+        tot += x;
+    }
+    total = tot;
+    return before + incl - v;
+}
+
+// Piece length L = max(kMinPiece, total work / resident workgroups), doubled until
+// the pieces fit the partial slots; a pair whose longer row holds est > L tiles is cut
+// into ceil(est / L) pieces, each row split evenly by position.  A piece also records
+// where its rows begin, from which its workgroup recovers the last column the
+// whole-row walk would have taken before the piece (so that both skip the same entries).
+__global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
+    __shared__ int64_t red[16];
+    __shared__ int32_t scan[16];
+    const SplitPlan &P = a.plan;
+    const int t = threadIdx.x;
+    auto est_of = [&](int64_t p) {
+        int64_t bA, eA, bB, eB;
+        pair_ranges(a, p, bA, eA, bB, eB);
+        return max(eA - bA, eB - bB);
+    };
+    int64_t tot = 0;
+    for (int64_t p = t; p < a.n_pairs; p += 1024) tot += est_of(p);
+    tot = block_sum64(tot, red);
+    int64_t L = (tot + kResidentPairs - 1) / kResidentPairs;
+    L = L > kMinPiece ? L : kMinPiece;
+    for (int iter = 0; iter < 48; ++iter) {
+        int64_t need = 0;
+        for (int64_t p = t; p < a.n_pairs; p += 1024) {
+            const int64_t e = est_of(p);
+            if (e > L) need += (e + L - 1) / L;
+        }
+        need = block_sum64(need, red);
+        if (need <= P.max_slots) break;
+        L *= 2;
+    }
+    int32_t base = 0, mbase = 0;
+    for (int64_t p0 = 0; p0 < a.n_pairs; p0 += 1024) {
+        const int64_t p = p0 + t;
+        int64_t bA = 0, eA = 0, bB = 0, eB = 0;
+        int32_t ns = 0;
+        if (p < a.n_pairs) {
+            pair_ranges(a, p, bA, eA, bB, eB);
+            const int64_t e = max(eA - bA, eB - bB);
+            ns = e > L ? (int32_t)((e + L - 1) / L) : 0;
+        }
+        int32_t tot_ns, tot_sp;
+        const int32_t excl = block_scan32(ns, scan, tot_ns);
+        const int32_t mex = block_scan32(ns > 0 ? 1 : 0, scan, tot_sp);
+        if (p < a.n_pairs) {
+            P.pair_flag[p] = ns ? base + excl + 1 : 0;
+            if (ns) {
+                const int32_t first = base + excl;
+                int32_t *me = P.merge + 3 * (int64_t)(mbase + mex);
+                me[0] = (int32_t)p;
+                me[1] = first;
+                me[2] = ns;
+                for (int32_t sI = 0; sI < ns; ++sI) {
+                    SplitItem it;
+                    it.pair = (int32_t)p;
+                    it.slot = first + sI;
+                    it.a0 = (int32_t)(bA + (eA - bA) * sI / ns);
+                    it.a1 = (int32_t)(bA + (eA - bA) * (sI + 1) / ns);
+                    it.ra = (int32_t)bA;
+                    it.b0 = (int32_t)(bB + (eB - bB) * sI / ns);
+                    it.b1 = (int32_t)(bB + (eB - bB) * (sI + 1) / ns);
+                    it.rb = (int32_t)bB;
+                    P.items[first + sI] = it;
+                }
+            }
+        }
+        base += tot_ns;
+        mbase += tot_sp;
+    }
+    if (t == 0) {
+        P.counts[0] = base;
+        P.counts[1] = mbase;
+        P.counts[2] = (int32_t)L;
+    }
+}
+
+// One workgroup per split pair; thread (g, dq, q) combines the pieces of query q of
+// block g for d in quarter dq: O = sum_s 2^(lse_s - lse) O_s with
+// lse = log2 sum_s 2^(lse_s).
+template <int D>
+__global__ __launch_bounds__(512) void merge_kernel(AttnArgs a) {
+    constexpr int DQ = D / 4;
+    const int m = blockIdx.x;
+    if (m >= a.plan.counts[1]) return;
+    const int32_t *me = a.plan.merge + 3 * (int64_t)m;
+    const int64_t pair = me[0];
+    const int first = me[1], ns = me[2];
+    const int t = threadIdx.x, q = t & 63, dq = (t >> 6) & 3, g = t >> 8;
+    const int64_t bh = pair / a.pairs_per_head;
+    const int i0 = (int)(pair % a.pairs_per_head) * 2;
+    if (i0 + g >= a.nB) return;
+    const int64_t N = (int64_t)a.nB * 64;
+    const int64_t qrow = bh * N + (int64_t)(i0 + g) * 64 + q;
+    const float *pl = a.plan.part_lse + ((int64_t)first * 2 + g) * 64 + q;   // piece s at pl[128 s]
+    float mx = -INFINITY;
+    for (int sI = 0; sI < ns; ++sI) mx = fmaxf(mx, pl[128 * sI]);
+    float acc[DQ];
+#pragma unroll
+    for (int e = 0; e < DQ; ++e) acc[e] = 0.f;
+    float ltot = -INFINITY;
+    if (mx != -INFINITY) {              // else no kept tile in any piece: O = 0
+        float sum = 0.f;
+        for (int sI = 0; sI < ns; ++sI) sum += __builtin_amdgcn_exp2f(pl[128 * sI] - mx);
+        ltot = mx + __log2f(sum);
+        for (int sI = 0; sI < ns; ++sI) {
+            const float w = __builtin_amdgcn_exp2f(pl[128 * sI] - ltot);
+            const float *po = a.plan.part_o + (((int64_t)(first + sI) * 2 + g) * D + dq * DQ) * 64 + q;
+#pragma unroll
+            for (int e = 0; e < DQ; ++e) acc[e] += w * po[64 * e];
+        }
+    }
+    bf16x8 *og = reinterpret_cast<bf16x8 *>((__bf16 *)a.out + qrow * D + dq * DQ);
+#pragma unroll
+    for (int e8 = 0; e8 < DQ / 8; ++e8) {
+        f32x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = acc[8 * e8 + e];
+        og[e8] = __builtin_convertvector(v, bf16x8);
+    }
+    if (a.lse && dq == 0) a.lse[qrow] = mx == -INFINITY ? -INFINITY : ltot * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -510,12 +738,18 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
 }
 
 int launch_attention(const AttnArgs &a, int dtype, int d, hipStream_t s) {
-    const dim3 pgrid((unsigned)a.n_pairs), pblock(256), grid((unsigned)a.rows), block(128);
-    if (dtype == 1 && d == 128)
-        attn_bf16_kernel<128><<<pgrid, pblock, 0, s>>>(a);
-    else if (dtype == 1 && d == 64)
-        attn_bf16_kernel<64><<<pgrid, pblock, 0, s>>>(a);
-    else if (dtype == 0 && d == 128)
+    const dim3 pgrid((unsigned)(a.plan.max_slots + a.n_pairs)), pblock(256), grid((unsigned)a.rows), block(128);
+    const dim3 mgrid((unsigned)a.plan.max_slots), mblock(512);
+    if (dtype == 1) {
+        plan_kernel<<<1, 1024, 0, s>>>(a);
+        if (d == 128) {
+            attn_bf16_kernel<128><<<pgrid, pblock, 0, s>>>(a);
+            merge_kernel<128><<<mgrid, mblock, 0, s>>>(a);
+        } else {
+            attn_bf16_kernel<64><<<pgrid, pblock, 0, s>>>(a);
+            merge_kernel<64><<<mgrid, mblock, 0, s>>>(a);
+        }
+    } else if (dtype == 0 && d == 128)
         attn_f32_kernel<128><<<grid, block, 0, s>>>(a);
     else
         attn_f32_kernel<64><<<grid, block, 0, s>>>(a);

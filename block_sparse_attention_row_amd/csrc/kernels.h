@@ -41,6 +41,29 @@ struct SelectArgs {
     float scale_log2;         // softmax scale * log2(e)
 };
 
+// Row splitting of the bf16 attention.  Pairs of query blocks whose rows hold more
+// than L tiles are cut into pieces of at most about L tiles (by position in each
+// row); pieces run first, write normalised partial outputs and their log-sum-exp
+// to partial slots, and a merge kernel combines them.  L follows the total work
+// over the workgroups resident at once, so that no work item outlasts the rest.
+struct SplitItem {
+    int32_t pair, slot;          // query-block pair, partial slot
+    int32_t a0, a1, ra;          // row A entries [a0, a1); the row's first entry ra
+    int32_t b0, b1, rb;          // row B likewise (b0 == b1 when the pair has no row B)
+};
+constexpr int kResidentPairs = 512;   // attention workgroups resident at once (256 CUs x 2)
+constexpr int kMinPiece = 64;         // shortest piece (tiles)
+constexpr int kMaxSlots = 512;        // partial slots at most
+struct SplitPlan {
+    SplitItem *items;        // [max_slots] pieces, in pair order
+    int32_t *counts;         // [0] pieces, [1] split pairs, [2] piece length L
+    int32_t *pair_flag;      // [n_pairs] 0: not split, else first slot + 1
+    int32_t *merge;          // [max_slots][3] pair, first slot, pieces (one entry per split pair)
+    float *part_o;           // [max_slots][2 blocks][D][64 queries] normalised partial outputs
+    float *part_lse;         // [max_slots][2 blocks][64] partial log2-sum-exp (scaled-score units)
+    int32_t max_slots;
+};
+
 struct AttnArgs {
     const void *q, *k, *v;
     const int32_t *row_ptr, *col_idx;
@@ -52,6 +75,7 @@ struct AttnArgs {
     int32_t pairs_per_head;   // ceil(nB / 2)
     int32_t nB;
     float scale_log2;         // softmax scale * log2(e)
+    SplitPlan plan;           // bf16 path only
 };
 
 int launch_pool(const void *q, const void *k, __bf16 *qbar, __bf16 *kbar, int64_t nblocks, int dtype, int d,
@@ -62,6 +86,6 @@ int launch_mask_bits(const uint8_t *mask, int64_t bh, int32_t nB, int32_t nW, ui
                      int32_t *group_sums, hipStream_t s);
 int launch_emit(const uint64_t *bits, const int32_t *counts, const int32_t *group_sums, int64_t rows, int32_t nB,
                 int32_t nW, int32_t *row_ptr, int32_t *col_idx, hipStream_t s);
-int launch_attention(const AttnArgs &a, int dtype, int d, hipStream_t s);
+int launch_attention(const AttnArgs &a, int dtype, int d, hipStream_t s);   // bf16: plan, attention, merge
 
 }  // namespace sattn

@@ -56,6 +56,14 @@ def test_capacity_and_workspace_formulas():
     expect = al(expect + 8 * rows * (nbp // 64))
     expect = al(expect + 4 * rows)
     expect = al(expect + 4 * 12 * ((nB + 15) // 16))     # kept-block totals per 16-row group
+    pairs = 12 * ((nB + 1) // 2)
+    slots = min(512, 4 * pairs)                           # attention row splitting
+    expect = al(expect + 32 * slots)                      # pieces
+    expect = al(expect + 16)                              # plan counts
+    expect = al(expect + 4 * pairs)                       # per-pair split flags
+    expect = al(expect + 12 * slots)                      # merge list
+    expect = al(expect + 4 * slots * 2 * 64 * 128)        # partial outputs (fp32)
+    expect = al(expect + 4 * slots * 2 * 64)              # partial log-sum-exp
     assert B.sparse_attn_workspace_size(s) == expect
 
 

@@ -144,6 +144,45 @@ def test_forward_skips_out_of_order_and_out_of_range_columns():
     assert torch.equal(out_c, out_a) and torch.equal(lse_c, lse_a)
 
 
+def test_long_rows_are_split_and_merged():
+    """Rows far longer than the rest are cut into pieces merged by log-sum-exp weights
+    (pieces of at least 64 tiles, so rows of 105 blocks split in two).  An odd block
+    count leaves the last pair of each head with a single row."""
+    wl = small_workload("split", 2, 128, (7, 3, 5), "bf16", seed=23)
+    q, k, v, _ = make_inputs(wl, "B")
+    qd, kd, vd = P.to_device(q, k, v)
+    nB = wl.blocks
+    assert nB == 105
+    rows = wl.heads * nB
+    rng = np.random.default_rng(3)
+    mask = np.zeros((rows, nB), dtype=bool)
+    mask[np.arange(rows), np.arange(rows) % nB] = True
+    mask[np.arange(rows), rng.integers(0, nB, rows)] = True
+    long_rows = [0, 1, 50, nB - 1, nB + 51, 2 * nB - 1]
+    mask[long_rows] = rng.random((len(long_rows), nB)) < 0.97
+    orp, oci = oracle.csr_from_mask(mask)
+    out, lse = P.gpu_forward(wl, qd, kd, vd, orp, oci)
+    err, lerr = P.compare_rows(wl, out, lse, q, k, v, orp, oci, np.arange(rows))
+    assert err <= P.TOL["bf16"] and lerr <= P.LSE_TOL["bf16"]
+    # repeated, descending and out-of-range entries every few positions of the long rows
+    # (so that they straddle the piece boundaries) are skipped as in a whole-row walk
+    rp2, ci2 = [0], []
+    for r in range(rows):
+        seg = oci[orp[r]:orp[r + 1]].tolist()
+        if r in long_rows:
+            junk = []
+            for n, cc in enumerate(seg):
+                junk.append(cc)
+                if n % 7 == 3:
+                    junk += [cc, max(cc - 3, 0), -2, nB + 7]
+            seg = junk
+        ci2 += seg
+        rp2.append(len(ci2))
+    out_c, lse_c = P.gpu_forward(wl, qd, kd, vd, np.array(rp2), np.array(ci2))
+    err, lerr = P.compare_rows(wl, out_c, lse_c, q, k, v, orp, oci, np.arange(rows))
+    assert err <= P.TOL["bf16"] and lerr <= P.LSE_TOL["bf16"]
+
+
 def test_deterministic_and_no_nan():
     wl = small_workload("det", 3, 128, (3, 4, 5), "bf16", threshold=0.8, window=(1, 1, 1), seed=17)
     q, k, v, thr = make_inputs(wl, "A")
