@@ -147,7 +147,12 @@ int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_sel
  *               blocks.  A row with no block gives zeros.
  *   lse         optional device fp32 [B, H, N] (natural-log log-sum-exp of
  *               the scaled logits; -inf for an empty row), or NULL.
- *   workspace   device, >= sparse_attn_workspace_size(shape) bytes.
+ *   workspace   device, >= sparse_attn_workspace_size(shape) bytes; its
+ *               contents on entry do not matter.  In bf16 the call plans the
+ *               work first: pairs of query blocks whose rows are much longer
+ *               than the average share are cut into pieces that are merged by
+ *               their log-sum-exp, so that no single row holds the GPU up.
+ * Calls that share one workspace must not overlap on different streams.
  */
 int32_t sparse_attn_forward(const sparse_attn_shape *shape, const void *q, const void *k, const void *v,
                             const int32_t *row_ptr, const int32_t *col_idx, int64_t col_count,
