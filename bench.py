@@ -204,6 +204,21 @@ def main():
     sel_bytes = 2 * qd.numel() * elt + 4 * (rows + 1) + 4 * nnz
     sel_gbs = sel_bytes / (sel_ms_med * 1e-3) / 1e9
 
+    # token reordering raster -> tile-major of Q (a data-movement kernel: read + write)
+    reo = torch.empty_like(qd)
+    reo_ms = []
+    for _ in range(0 if args.no_select_timing else 5):
+        flush.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        B.sparse_attn_to_tiles(shape, qd, reo, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        reo_ms.append(a.elapsed_time(b))
+    reo_ms_med = sorted(reo_ms)[len(reo_ms) // 2] if reo_ms else float("nan")
+    reo_gbs = 2 * qd.numel() * elt / (reo_ms_med * 1e-3) / 1e9
+    del reo
+
     # dense reference: the same forward kernel over the full CSR (every tile kept)
     full_rp = torch.arange(0, rows + 1, dtype=torch.int32, device=dev) * wl.blocks
     full_ci = torch.arange(wl.blocks, dtype=torch.int32, device=dev).repeat(rows)
@@ -260,6 +275,8 @@ def main():
             "ms": round(sel_ms_med, 4), "bytes": sel_bytes, "GB_s": round(sel_gbs, 1),
             "frac_hbm_peak": round(sel_gbs / PEAK_HBM_GBS, 4),
         },
+        "reorder_to_tiles": {"ms": round(reo_ms_med, 4), "GB_s": round(reo_gbs, 1),
+                             "frac_hbm_peak": round(reo_gbs / PEAK_HBM_GBS, 4)},
         "dense_forward_ms": round(dense_ms_med, 4),
         "speedup_vs_dense": {
             "forward": round(dense_ms_med / attn_ms_avg, 3),

@@ -33,6 +33,8 @@ EXPORTED = (
     "sparse_attn_select",
     "sparse_attn_forward",
     "sparse_attn_mask_to_csr",
+    "sparse_attn_to_tiles",
+    "sparse_attn_from_tiles",
 )
 
 
@@ -87,6 +89,9 @@ def lib():
         L.sparse_attn_forward.restype = ctypes.c_int32
         L.sparse_attn_mask_to_csr.argtypes = [SP, P, P, P, I64, P, I64, P]
         L.sparse_attn_mask_to_csr.restype = ctypes.c_int32
+        for name in ("sparse_attn_to_tiles", "sparse_attn_from_tiles"):
+            getattr(L, name).argtypes = [SP, P, P, P]
+            getattr(L, name).restype = ctypes.c_int32
         _lib = L
     return _lib
 
@@ -204,3 +209,21 @@ def sparse_attn_mask_to_csr(shape: Shape, block_mask, buffers: Optional[Buffers]
                                        bufs.workspace.numel(), _stream(stream))
     _check(st, "sparse_attn_mask_to_csr")
     return bufs.row_ptr, bufs.col_idx
+
+
+def sparse_attn_to_tiles(shape: Shape, src, dst=None, stream=None):
+    """Raster-ordered [B, H, N, d] -> tile-major (a new tensor unless dst is given)."""
+    import torch
+    dst = torch.empty_like(src) if dst is None else dst
+    _check(lib().sparse_attn_to_tiles(ctypes.byref(shape), _ptr(src), _ptr(dst), _stream(stream)),
+           "sparse_attn_to_tiles")
+    return dst
+
+
+def sparse_attn_from_tiles(shape: Shape, src, dst=None, stream=None):
+    """Tile-major [B, H, N, d] -> raster order (a new tensor unless dst is given)."""
+    import torch
+    dst = torch.empty_like(src) if dst is None else dst
+    _check(lib().sparse_attn_from_tiles(ctypes.byref(shape), _ptr(src), _ptr(dst), _stream(stream)),
+           "sparse_attn_from_tiles")
+    return dst

@@ -270,4 +270,35 @@ int32_t sparse_attn_mask_to_csr(const sparse_attn_shape *shape, const uint8_t *b
     return emit_csr(d, bits, counts, groups, row_ptr, col_idx, s);
 }
 
+static int32_t reorder(const sparse_attn_shape *shape, const void *src, void *dst, void *stream, int inverse) {
+    Dims d;
+    int32_t st = check_shape(shape, &d);
+    if (st) return st;
+    if (!src || !dst || src == dst) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (!aligned(src, 16) || !aligned(dst, 16)) return SPARSE_ATTN_INVALID_ARGUMENT;
+    const int64_t rowb = d.D * (shape->dtype == SPARSE_ATTN_BF16 ? 2 : 4);
+    ReorderArgs a;
+    a.nB = (int32_t)d.nB;
+    a.nTy = d.nTy;
+    a.nTx = d.nTx;
+    a.tt = shape->tile_t;
+    a.th = shape->tile_h;
+    a.tw = shape->tile_w;
+    a.gh = shape->grid_h;
+    a.gw = shape->grid_w;
+    a.row_log2 = 0;
+    while ((16LL << a.row_log2) < rowb) ++a.row_log2;
+    a.inverse = inverse;
+    if (launch_reorder(src, dst, a, d.B * d.H * d.nB, (hipStream_t)stream)) return SPARSE_ATTN_HIP_ERROR;
+    return SPARSE_ATTN_OK;
+}
+
+int32_t sparse_attn_to_tiles(const sparse_attn_shape *shape, const void *src, void *dst, void *stream) {
+    return reorder(shape, src, dst, stream, 0);
+}
+
+int32_t sparse_attn_from_tiles(const sparse_attn_shape *shape, const void *src, void *dst, void *stream) {
+    return reorder(shape, src, dst, stream, 1);
+}
+
 }  // extern "C"

@@ -78,6 +78,15 @@ struct AttnArgs {
     SplitPlan plan;           // bf16 path only
 };
 
+struct ReorderArgs {
+    int32_t nB, nTy, nTx;          // blocks per head, block grid (t implied)
+    int32_t tt, th, tw;            // tile
+    int32_t gh, gw;                // token grid height and width
+    int32_t row_log2;              // log2 of the 16-byte pieces per token row
+    int32_t inverse;               // 0: raster -> tile-major, 1: tile-major -> raster
+};
+int launch_reorder(const void *src, void *dst, const ReorderArgs &a, int64_t tiles, hipStream_t s);
+
 int launch_pool(const void *q, const void *k, __bf16 *qbar, __bf16 *kbar, int64_t nblocks, int dtype, int d,
                 const PoolSide &side, hipStream_t s);
 int launch_fill_thresholds(const float *host_thr, int n, float *dst, hipStream_t s);

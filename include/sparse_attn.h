@@ -171,6 +171,22 @@ int32_t sparse_attn_mask_to_csr(const sparse_attn_shape *shape, const uint8_t *b
                                 int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity,
                                 void *workspace, int64_t workspace_bytes, void *stream);
 
+/*
+ * Token reordering between raster order and the tile-major order the calls above
+ * take (the "Fractal Flattening" item of the NABLA summary page, section
+ * "Methodologie : NABLA": the tokens of each spatial patch are made contiguous;
+ * with 64-token tiles this is one level of tiling).
+ *
+ *   src, dst    device, [B, H, N, d] in shape->dtype; distinct, not overlapping.
+ *   raster      token (t, y, x) at index (t * grid_h + y) * grid_w + x.
+ *   tile-major  block b = (bt * nTy + by) * nTx + bx holds tokens [64 b, 64 b + 64):
+ *               the tile_t x tile_h x tile_w tile at (bt, by, bx), row-major inside.
+ * sparse_attn_to_tiles: raster -> tile-major; sparse_attn_from_tiles: the inverse.
+ * The grid must divide into whole tiles (SPARSE_ATTN_UNSUPPORTED otherwise).
+ */
+int32_t sparse_attn_to_tiles(const sparse_attn_shape *shape, const void *src, void *dst, void *stream);
+int32_t sparse_attn_from_tiles(const sparse_attn_shape *shape, const void *src, void *dst, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -121,6 +121,40 @@ def select_rows(qbar: np.ndarray, kbar: np.ndarray, heads: int, block_grid: Sequ
     return keep
 
 
+def tile_order(grid: Sequence[int], tile: Sequence[int]) -> np.ndarray:
+    """perm[i] = raster index of the token at tile-major position i.
+
+    NABLA summary page, section "Methodologie : NABLA", item "Fractal Flattening":
+    the tokens of each spatial patch are made contiguous.  Raster token (t, y, x) sits
+    at (t * H + y) * W + x; tile-major position i belongs to block b = i // V
+    (V = tile volume), b = (bt * nTy + by) * nTx + bx, and is the (i mod V)-th token of
+    that tile in row-major order.
+    """
+    T, H, W = (int(g) for g in grid)
+    tt, th, tw = (int(s) for s in tile)
+    vol = tt * th * tw
+    nTy, nTx = H // th, W // tw
+    i = np.arange(T * H * W, dtype=np.int64)
+    b, u = i // vol, i % vol
+    bt, by, bx = b // (nTy * nTx), (b // nTx) % nTy, b % nTx
+    ut, uy, ux = u // (th * tw), (u // tw) % th, u % tw
+    return ((bt * tt + ut) * H + (by * th + uy)) * W + (bx * tw + ux)
+
+
+def to_tiles(x, grid, tile) -> np.ndarray:
+    """Raster-ordered [..., N, d] -> tile-major (same dtype, exact)."""
+    a = x.numpy() if hasattr(x, "numpy") else np.asarray(x)
+    return a[..., tile_order(grid, tile), :]
+
+
+def from_tiles(x, grid, tile) -> np.ndarray:
+    """Tile-major [..., N, d] -> raster order (the inverse of to_tiles)."""
+    a = x.numpy() if hasattr(x, "numpy") else np.asarray(x)
+    out = np.empty_like(a)
+    out[..., tile_order(grid, tile), :] = a
+    return out
+
+
 def csr_from_mask(mask: np.ndarray):
     """Dense boolean block mask [rows, nB] -> (row_ptr int64 [rows+1], col_idx int32), ascending columns."""
     mask = np.asarray(mask).astype(bool)

@@ -166,3 +166,14 @@ def test_mask_to_csr_rejects_before_launch(kw, status):
     mask = kw.get("mask", A)
     rp = kw.get("rp", A)
     assert B.lib().sparse_attn_mask_to_csr(ctypes.byref(s), mask, rp, A, cap, A, wsb, None) == status
+
+
+@pytest.mark.parametrize("fn", ["sparse_attn_to_tiles", "sparse_attn_from_tiles"])
+def test_reorder_rejects_before_launch(fn):
+    f = getattr(B.lib(), fn)
+    s = _shape()
+    assert f(ctypes.byref(s), A, A, None) == B.SPARSE_ATTN_INVALID_ARGUMENT          # same buffer
+    assert f(ctypes.byref(s), A, A + 8, None) == B.SPARSE_ATTN_INVALID_ARGUMENT      # misaligned
+    assert f(ctypes.byref(s), None, A, None) == B.SPARSE_ATTN_INVALID_ARGUMENT
+    bad = _shape(grid=(20, 30, 48))                                                  # partial tiles
+    assert f(ctypes.byref(bad), A, A + 4096, None) == B.SPARSE_ATTN_UNSUPPORTED

@@ -183,6 +183,24 @@ def test_long_rows_are_split_and_merged():
     assert err <= P.TOL["bf16"] and lerr <= P.LSE_TOL["bf16"]
 
 
+@pytest.mark.parametrize("dtype,d,grid,tile", [("bf16", 128, (3, 16, 24), (1, 8, 8)),
+                                                 ("f32", 64, (4, 8, 16), (2, 4, 8)),
+                                                 ("bf16", 64, (2, 32, 8), (1, 8, 8))])
+def test_token_reorder_matches_oracle(dtype, d, grid, tile):
+    """Raster <-> tile-major reordering is a permutation: bit-exact against the oracle."""
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    gen = torch.Generator().manual_seed(6)
+    x = torch.randn((2, 3, grid[0] * grid[1] * grid[2], d), generator=gen).to(tdt)
+    shape = B.make_shape(2, 3, d, grid, dtype, 0.0, tile)
+    xd = x.cuda()
+    y = B.sparse_attn_to_tiles(shape, xd)
+    z = B.sparse_attn_from_tiles(shape, y)
+    torch.cuda.synchronize()
+    ref = oracle.to_tiles(x.float(), grid, tile)
+    assert np.array_equal(y.float().cpu().numpy(), ref)
+    assert torch.equal(z.cpu(), x)
+
+
 def test_deterministic_and_no_nan():
     wl = small_workload("det", 3, 128, (3, 4, 5), "bf16", threshold=0.8, window=(1, 1, 1), seed=17)
     q, k, v, thr = make_inputs(wl, "A")

@@ -339,3 +339,38 @@ def test_batch_and_head_indexing():
             o1, _ = oracle.attention_rows(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
                                           rp1, ci1, np.arange(nB))
             assert np.array_equal(out[bh * nB:(bh + 1) * nB], o1)
+
+
+# ---------------------------------------------------------------- token reordering
+
+@pytest.mark.parametrize("grid,tile", [((2, 16, 24), (1, 8, 8)), ((4, 8, 8), (2, 4, 8)), ((3, 8, 16), (1, 8, 8))])
+def test_tile_order_groups_each_tile_row_major(grid, tile):
+    """Block b holds exactly the tokens of tile b, in row-major order inside the tile."""
+    T, H, W = grid
+    tt, th, tw = tile
+    perm = oracle.tile_order(grid, tile)
+    assert np.array_equal(np.sort(perm), np.arange(T * H * W))          # a permutation
+    t, y, x = perm // (H * W), (perm // W) % H, perm % W
+    vol = tt * th * tw
+    nTy, nTx = H // th, W // tw
+    for b in range(T * H * W // vol):
+        sl = slice(vol * b, vol * (b + 1))
+        assert np.all(t[sl] // tt == b // (nTy * nTx))
+        assert np.all(y[sl] // th == (b // nTx) % nTy)
+        assert np.all(x[sl] // tw == b % nTx)
+        key = (t[sl] % tt) * (th * tw) + (y[sl] % th) * tw + x[sl] % tw
+        assert np.array_equal(key, np.arange(vol))
+
+
+def test_tile_order_round_trip_and_input_generator():
+    """from_tiles inverts to_tiles, and to_tiles agrees with the input generator's own
+    tile-major permutation (written separately, with reshapes)."""
+    import torch
+    from block_sparse_attention_row_amd.synth import tile_major
+    grid, tile = (3, 16, 24), (1, 8, 8)
+    rng = np.random.default_rng(4)
+    field = rng.standard_normal((2, 3, 5) + grid).astype(np.float32)       # [B, H, d, T, Hh, W]
+    x = np.ascontiguousarray(field.reshape(2, 3, 5, -1).transpose(0, 1, 3, 2))   # raster tokens [B, H, N, d]
+    y = oracle.to_tiles(x, grid, tile)
+    assert np.array_equal(oracle.from_tiles(y, grid, tile), x)
+    assert np.array_equal(y, tile_major(torch.from_numpy(field), grid, tile).numpy())
