@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-CSR reference forward")
     ap.add_argument("--no-select-timing", action="store_true", help="skip the separate selection timing")
+    ap.add_argument("--dense-steps", type=int, default=0,
+                    help="denoising schedule: this many leading steps run dense (no selection)")
+    ap.add_argument("--reselect-every", type=int, default=1,
+                    help="denoising schedule: select every K steps and reuse the block list in between")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB read + 1 GiB write kernel (torch.neg) for rocprofv3 counter scaling")
     ap.add_argument("--pmc-summary", metavar="DIR", help="summarise rocprofv3 --pmc output and exit")
@@ -220,8 +224,8 @@ def main():
     del reo
 
     # dense reference: the same forward kernel over the full CSR (every tile kept)
-    full_rp = torch.arange(0, rows + 1, dtype=torch.int32, device=dev) * wl.blocks
-    full_ci = torch.arange(wl.blocks, dtype=torch.int32, device=dev).repeat(rows)
+    full_bufs = B.alloc_buffers(shape, dev)
+    full_rp, full_ci = B.sparse_attn_full_csr(shape, full_bufs, stream=stream)
     for _ in range(0 if args.no_dense else 2):
         B.sparse_attn_forward(shape, qd, kd, vd, full_rp, full_ci, out=out, lse=lse, workspace=bufs.workspace,
                               stream=stream)
@@ -243,6 +247,29 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+
+    # optional denoising schedule: dense warm-up steps, then a selection every K steps
+    # whose block list the steps in between reuse
+    sched = None
+    if args.dense_steps > 0 or args.reselect_every > 1:
+        K = max(1, args.reselect_every)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        tiles = 0
+        rp_s, ci_s = None, None
+        for i in range(args.steps):
+            if i < args.dense_steps:
+                forward(full_rp, full_ci)
+                tiles += rows * wl.blocks
+            else:
+                if (i - args.dense_steps) % K == 0:
+                    rp_s, ci_s = select()
+                forward(rp_s, ci_s)
+                tiles += nnz
+        torch.cuda.synchronize()
+        t_s = (time.perf_counter() - t0) / args.steps
+        sched = {"dense_steps": args.dense_steps, "reselect_every": K, "ms_per_step": round(1e3 * t_s, 4),
+                 "TFLOP_s": round(4.0 * 64 * 64 * wl.head_dim * tiles / args.steps / t_s / 1e12, 2)}
 
     traffic = stored_traffic()
     rec = {
@@ -283,6 +310,8 @@ def main():
             "select_plus_forward": round(dense_ms_med / (attn_ms_avg + sel_ms_med), 3),
         },
     }
+    if sched is not None:
+        rec["denoise_schedule"] = sched
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, q, k, v, thr, bufs, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

@@ -33,6 +33,7 @@ EXPORTED = (
     "sparse_attn_select",
     "sparse_attn_forward",
     "sparse_attn_mask_to_csr",
+    "sparse_attn_full_csr",
     "sparse_attn_to_tiles",
     "sparse_attn_from_tiles",
 )
@@ -89,6 +90,8 @@ def lib():
         L.sparse_attn_forward.restype = ctypes.c_int32
         L.sparse_attn_mask_to_csr.argtypes = [SP, P, P, P, I64, P, I64, P]
         L.sparse_attn_mask_to_csr.restype = ctypes.c_int32
+        L.sparse_attn_full_csr.argtypes = [SP, P, P, I64, P]
+        L.sparse_attn_full_csr.restype = ctypes.c_int32
         for name in ("sparse_attn_to_tiles", "sparse_attn_from_tiles"):
             getattr(L, name).argtypes = [SP, P, P, P]
             getattr(L, name).restype = ctypes.c_int32
@@ -208,6 +211,15 @@ def sparse_attn_mask_to_csr(shape: Shape, block_mask, buffers: Optional[Buffers]
                                        _ptr(bufs.col_idx), bufs.col_idx.numel(), _ptr(bufs.workspace),
                                        bufs.workspace.numel(), _stream(stream))
     _check(st, "sparse_attn_mask_to_csr")
+    return bufs.row_ptr, bufs.col_idx
+
+
+def sparse_attn_full_csr(shape: Shape, buffers: Optional[Buffers] = None, device=None, stream=None):
+    """The dense block list (every query block keeps every key block) -> (row_ptr, col_idx)."""
+    bufs = buffers or alloc_buffers(shape, device or "cuda")
+    st = lib().sparse_attn_full_csr(ctypes.byref(shape), _ptr(bufs.row_ptr), _ptr(bufs.col_idx), bufs.col_idx.numel(),
+                                    _stream(stream))
+    _check(st, "sparse_attn_full_csr")
     return bufs.row_ptr, bufs.col_idx
 
 

@@ -270,6 +270,18 @@ int32_t sparse_attn_mask_to_csr(const sparse_attn_shape *shape, const uint8_t *b
     return emit_csr(d, bits, counts, groups, row_ptr, col_idx, s);
 }
 
+int32_t sparse_attn_full_csr(const sparse_attn_shape *shape, int32_t *row_ptr, int32_t *col_idx,
+                             int64_t col_capacity, void *stream) {
+    Dims d;
+    int32_t st = check_shape(shape, &d);
+    if (st) return st;
+    if (!row_ptr || !col_idx) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (!aligned(row_ptr, 4) || !aligned(col_idx, 4)) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (col_capacity < d.rows * d.nB) return SPARSE_ATTN_CAPACITY;
+    if (launch_full_csr(d.rows, (int32_t)d.nB, row_ptr, col_idx, (hipStream_t)stream)) return SPARSE_ATTN_HIP_ERROR;
+    return SPARSE_ATTN_OK;
+}
+
 static int32_t reorder(const sparse_attn_shape *shape, const void *src, void *dst, void *stream, int inverse) {
     Dims d;
     int32_t st = check_shape(shape, &d);

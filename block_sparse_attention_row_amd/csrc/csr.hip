@@ -118,6 +118,24 @@ __global__ __launch_bounds__(256) void emit_kernel(const uint64_t *__restrict__ 
     }
 }
 
+// Every row keeps every key block: row_ptr[r] = r * nB, col_idx = 0 .. nB-1 per row.
+__global__ void full_csr_kernel(int64_t rows, int32_t nB, int32_t *__restrict__ row_ptr,
+                                int32_t *__restrict__ col_idx) {
+    const int64_t n = rows * nB;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        col_idx[i] = (int32_t)(i % nB);
+    for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r <= rows; r += (int64_t)gridDim.x * blockDim.x)
+        row_ptr[r] = (int32_t)(r * nB);
+}
+
+int launch_full_csr(int64_t rows, int32_t nB, int32_t *row_ptr, int32_t *col_idx, hipStream_t s) {
+    const int64_t n = rows * nB;
+    int64_t blocks = (n + 255) / 256;
+    blocks = blocks < 1 ? 1 : (blocks > 4096 ? 4096 : blocks);
+    full_csr_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(rows, nB, row_ptr, col_idx);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_mask_bits(const uint8_t *mask, int64_t bh, int32_t nB, int32_t nW, uint64_t *bits, int32_t *counts,
                      int32_t *group_sums, hipStream_t s) {
     const int32_t gph = (nB + kGroupRows - 1) / kGroupRows;

@@ -93,6 +93,7 @@ int launch_fill_thresholds(const float *host_thr, int n, float *dst, hipStream_t
 int launch_select(const SelectArgs &a, int d, hipStream_t s);
 int launch_mask_bits(const uint8_t *mask, int64_t bh, int32_t nB, int32_t nW, uint64_t *bits, int32_t *counts,
                      int32_t *group_sums, hipStream_t s);
+int launch_full_csr(int64_t rows, int32_t nB, int32_t *row_ptr, int32_t *col_idx, hipStream_t s);
 int launch_emit(const uint64_t *bits, const int32_t *counts, const int32_t *group_sums, int64_t rows, int32_t nB,
                 int32_t nW, int32_t *row_ptr, int32_t *col_idx, hipStream_t s);
 int launch_attention(const AttnArgs &a, int dtype, int d, hipStream_t s);   // bf16: plan, attention, merge

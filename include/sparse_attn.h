@@ -172,6 +172,17 @@ int32_t sparse_attn_mask_to_csr(const sparse_attn_shape *shape, const uint8_t *b
                                 void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * The dense block list: every query block keeps every key block (row r holds
+ * 0 .. nB-1 at col_idx[r * nB ...]).  For dense warm-up steps or layers in a
+ * denoising loop, where the selection is skipped or its block list is reused
+ * for several steps (the pages' schedules that keep the first steps or blocks
+ * dense and amortise the selection over later steps).
+ *   row_ptr, col_idx, col_capacity: as in sparse_attn_select.
+ */
+int32_t sparse_attn_full_csr(const sparse_attn_shape *shape, int32_t *row_ptr, int32_t *col_idx,
+                             int64_t col_capacity, void *stream);
+
+/*
  * Token reordering between raster order and the tile-major order the calls above
  * take (the "Fractal Flattening" item of the NABLA summary page, section
  * "Methodologie : NABLA": the tokens of each spatial patch are made contiguous;

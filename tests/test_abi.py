@@ -177,3 +177,12 @@ def test_reorder_rejects_before_launch(fn):
     assert f(ctypes.byref(s), None, A, None) == B.SPARSE_ATTN_INVALID_ARGUMENT
     bad = _shape(grid=(20, 30, 48))                                                  # partial tiles
     assert f(ctypes.byref(bad), A, A + 4096, None) == B.SPARSE_ATTN_UNSUPPORTED
+
+
+def test_full_csr_rejects_before_launch():
+    f = B.lib().sparse_attn_full_csr
+    s = _shape()
+    cap = B.sparse_attn_csr_capacity(s)
+    assert f(ctypes.byref(s), A, A, cap - 1, None) == B.SPARSE_ATTN_CAPACITY
+    assert f(ctypes.byref(s), None, A, cap, None) == B.SPARSE_ATTN_INVALID_ARGUMENT
+    assert f(ctypes.byref(s), A, A + 2, cap, None) == B.SPARSE_ATTN_INVALID_ARGUMENT

@@ -201,6 +201,24 @@ def test_token_reorder_matches_oracle(dtype, d, grid, tile):
     assert torch.equal(z.cpu(), x)
 
 
+def test_full_csr_is_the_dense_block_list():
+    """The dense block list equals the oracle's CSR of an all-true mask (integer work:
+    bit-exact), and attention over it is dense attention."""
+    wl = small_workload("full", 2, 64, (2, 3, 3), "bf16", seed=29)
+    shape = P.shape_for(wl)
+    rows, nB = wl.heads * wl.blocks, wl.blocks
+    rp, ci = B.sparse_attn_full_csr(shape)
+    torch.cuda.synchronize()
+    orp, oci = oracle.csr_from_mask(np.ones((rows, nB), dtype=bool))
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    assert np.array_equal(rp_h, orp) and np.array_equal(ci[:int(rp_h[-1])].cpu().numpy(), oci)
+    q, k, v, _ = make_inputs(wl, "A")
+    qd, kd, vd = P.to_device(q, k, v)
+    out, lse = P.gpu_forward(wl, qd, kd, vd, rp_h, ci[:int(rp_h[-1])].cpu().numpy())
+    err, lerr = P.compare_rows(wl, out, lse, q, k, v, orp, oci, np.arange(rows))
+    assert err <= P.TOL["bf16"] and lerr <= P.LSE_TOL["bf16"]
+
+
 def test_deterministic_and_no_nan():
     wl = small_workload("det", 3, 128, (3, 4, 5), "bf16", threshold=0.8, window=(1, 1, 1), seed=17)
     q, k, v, thr = make_inputs(wl, "A")
