@@ -53,7 +53,8 @@ def _load():
         lib.oracle_pool.argtypes = [P, I, I, I, P]
         lib.oracle_select_rows.argtypes = [P, P, I, I, I, P, I, D, P, I, I, I, I, I, I, P, P, P]
         lib.oracle_attention_rows.argtypes = [P, P, P, I, I, I, P, P, P, I, D, P, P, P]
-        for f in (lib.oracle_pool, lib.oracle_select_rows, lib.oracle_attention_rows):
+        lib.oracle_attention_backward.argtypes = [P, P, P, P, I, I, I, I, P, P, D, P, P, P]
+        for f in (lib.oracle_pool, lib.oracle_select_rows, lib.oracle_attention_rows, lib.oracle_attention_backward):
             f.restype = None
         _lib = lib
     return _lib
@@ -119,6 +120,26 @@ def select_rows(qbar: np.ndarray, kbar: np.ndarray, heads: int, block_grid: Sequ
     if stats:
         return keep, p, E
     return keep
+
+
+def attention_backward(q, k, v, dout, row_ptr, col_idx, scale: Optional[float] = None,
+                       tpb: int = TOKENS_PER_BLOCK):
+    """Gradients (dq, dk, dv) [B, H, N, d] fp64 of the block-sparse attention for the
+    upstream gradient dout, from their definition (see oracle.c).  row_ptr/col_idx: a
+    valid CSR (ascending, in-range columns) over rows r = bh * nB + i."""
+    q, k, v, g = _f32(q), _f32(k), _f32(v), _f32(dout)
+    *lead, n, d = q.shape
+    BH = int(np.prod(lead)) if lead else 1
+    nB = n // tpb
+    rp = np.ascontiguousarray(row_ptr, dtype=np.int64)
+    ci = np.ascontiguousarray(col_idx, dtype=np.int32)
+    dq = np.empty(q.shape, dtype=np.float64)
+    dk = np.empty(q.shape, dtype=np.float64)
+    dv = np.empty(q.shape, dtype=np.float64)
+    sc = default_scale(d) if scale is None else float(scale)
+    _load().oracle_attention_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), BH, nB, tpb, d, _ptr(rp), _ptr(ci), sc,
+                                      _ptr(dq), _ptr(dk), _ptr(dv))
+    return dq, dk, dv
 
 
 def tile_order(grid: Sequence[int], tile: Sequence[int]) -> np.ndarray:

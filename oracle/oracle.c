@@ -215,3 +215,86 @@ void oracle_attention_rows(const float *q, const float *k, const float *v, int64
         free(acc);
     }
 }
+
+/*
+ * Gradients of the block-sparse attention (the backward of the computation
+ * above, for NABLA's training use: "Methodologie : NABLA" and the training
+ * results of the NABLA summary page).  With P the softmax weights of query
+ * token n over the tokens of its kept blocks and O_n = sum_m P_nm v_m, for an
+ * upstream gradient dO:
+ *   dV_m = sum_n P_nm dO_n
+ *   dP_nm = dO_n . v_m,  D_n = dO_n . O_n,  dS_nm = P_nm (dP_nm - D_n)
+ *   dQ_n = scale sum_m dS_nm k_m,  dK_m = scale sum_n dS_nm q_n.
+ * One head at a time (heads in parallel); within a head the rows are visited in
+ * order, so the sums over n are in a fixed order.  Outputs are fp64 [BH][N][d].
+ */
+void oracle_attention_backward(const float *q, const float *k, const float *v, const float *dout, int64_t BH,
+                               int64_t nB, int64_t tpb, int64_t d, const int64_t *row_ptr,
+                               const int32_t *col_idx, double scale, double *dq, double *dk, double *dv)
+{
+    const int64_t N = nB * tpb;
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * (size_t)N);
+        double *o = (double *)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bh = 0; bh < BH; ++bh) {
+            const float *qh = q + bh * N * d, *kh = k + bh * N * d, *vh = v + bh * N * d, *gh = dout + bh * N * d;
+            double *dqh = dq + bh * N * d, *dkh = dk + bh * N * d, *dvh = dv + bh * N * d;
+            for (int64_t x = 0; x < N * d; ++x) dqh[x] = dkh[x] = dvh[x] = 0.0;
+            for (int64_t i = 0; i < nB; ++i) {
+                const int64_t r = bh * nB + i, beg = row_ptr[r], end = row_ptr[r + 1];
+                const int64_t mc = (end - beg) * tpb;
+                if (mc == 0) continue;
+                for (int64_t t = 0; t < tpb; ++t) {
+                    const int64_t n = i * tpb + t;
+                    const float *qn = qh + n * d, *gn = gh + n * d;
+                    /* weights P_nm over the kept tokens, in kept order */
+                    double mx = -INFINITY;
+                    int64_t m = 0;
+                    for (int64_t e = beg; e < end; ++e)
+                        for (int64_t u = 0; u < tpb; ++u, ++m) {
+                            const float *km = kh + (col_idx[e] * tpb + u) * d;
+                            double a = 0.0;
+                            for (int64_t c = 0; c < d; ++c) a += (double)qn[c] * (double)km[c];
+                            w[m] = a * scale;
+                            if (w[m] > mx) mx = w[m];
+                        }
+                    double z = 0.0;
+                    for (int64_t mm = 0; mm < mc; ++mm) {
+                        w[mm] = exp(w[mm] - mx);
+                        z += w[mm];
+                    }
+                    for (int64_t mm = 0; mm < mc; ++mm) w[mm] /= z;
+                    /* O_n and D_n */
+                    for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+                    m = 0;
+                    for (int64_t e = beg; e < end; ++e)
+                        for (int64_t u = 0; u < tpb; ++u, ++m) {
+                            const float *vm = vh + (col_idx[e] * tpb + u) * d;
+                            for (int64_t c = 0; c < d; ++c) o[c] += w[m] * (double)vm[c];
+                        }
+                    double Dn = 0.0;
+                    for (int64_t c = 0; c < d; ++c) Dn += (double)gn[c] * o[c];
+                    /* dV, dP, dS, dQ, dK */
+                    m = 0;
+                    for (int64_t e = beg; e < end; ++e)
+                        for (int64_t u = 0; u < tpb; ++u, ++m) {
+                            const int64_t mt = col_idx[e] * tpb + u;
+                            const float *vm = vh + mt * d, *km = kh + mt * d;
+                            double dp = 0.0;
+                            for (int64_t c = 0; c < d; ++c) dp += (double)gn[c] * (double)vm[c];
+                            const double ds = w[m] * (dp - Dn);
+                            for (int64_t c = 0; c < d; ++c) {
+                                dvh[mt * d + c] += w[m] * (double)gn[c];
+                                dqh[n * d + c] += scale * ds * (double)km[c];
+                                dkh[mt * d + c] += scale * ds * (double)qn[c];
+                            }
+                        }
+                }
+            }
+        }
+        free(w);
+        free(o);
+    }
+}

@@ -374,3 +374,61 @@ def test_tile_order_round_trip_and_input_generator():
     y = oracle.to_tiles(x, grid, tile)
     assert np.array_equal(oracle.from_tiles(y, grid, tile), x)
     assert np.array_equal(y, tile_major(torch.from_numpy(field), grid, tile).numpy())
+
+
+# ---------------------------------------------------------------- gradients
+
+def _loss(q, k, v, g, mask, scale, tpb):
+    """sum(g * O) with O from the token-masked brute force (fp64), per head."""
+    tot = 0.0
+    for h in range(q.shape[0]):
+        o, _ = brute.token_mask_attention(q[h], k[h], v[h], mask[h], scale, tpb)
+        tot += float(np.sum(g[h] * o))
+    return tot
+
+
+def test_backward_matches_finite_differences():
+    """Every gradient entry of a tiny case against central differences of
+    sum(dO * O), O from the token-masked brute force (a separate route)."""
+    rng = np.random.default_rng(8)
+    H, nB, tpb, d = 2, 3, 4, 5
+    N = nB * tpb
+    q, k, v, g = (rng.standard_normal((H, N, d)).astype(np.float32) for _ in range(4))
+    mask = rng.random((H, nB, nB)) < 0.6
+    mask[:, np.arange(nB), np.arange(nB)] = True
+    mask[1, 2] = False                                  # an empty row
+    scale = 0.7
+    rp, ci = oracle.csr_from_mask(mask.reshape(H * nB, nB))
+    dq, dk, dv = oracle.attention_backward(q[None], k[None], v[None], g[None], rp, ci, scale=scale, tpb=tpb)
+    q64, k64, v64, g64 = (x.astype(np.float64) for x in (q, k, v, g))
+    h = 1e-6
+    for name, x, grad in (("q", q64, dq[0]), ("k", k64, dk[0]), ("v", v64, dv[0])):
+        num = np.empty_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            args = {"q": q64, "k": k64, "v": v64}
+            args[name] = xp
+            lp = _loss(args["q"], args["k"], args["v"], g64, mask, scale, tpb)
+            args[name] = xm
+            lm = _loss(args["q"], args["k"], args["v"], g64, mask, scale, tpb)
+            num[idx] = (lp - lm) / (2 * h)
+        assert np.abs(num - grad).max() <= 1e-6 * max(1.0, np.abs(num).max()), name
+
+
+def test_backward_zero_outside_the_kept_blocks():
+    """Key blocks kept by no query block get no dK, dV; empty query rows get no dQ."""
+    rng = np.random.default_rng(9)
+    nB, tpb, d = 4, 8, 6
+    N = nB * tpb
+    q, k, v, g = (rng.standard_normal((1, 1, N, d)).astype(np.float32) for _ in range(4))
+    mask = np.zeros((nB, nB), dtype=bool)
+    mask[0, [0, 2]] = True
+    mask[2, [2]] = True
+    mask[3, [0]] = True                                 # row 1 empty; key block 1 and 3 unused
+    rp, ci = oracle.csr_from_mask(mask)
+    dq, dk, dv = oracle.attention_backward(q, k, v, g, rp, ci, tpb=tpb)
+    for b in (1, 3):
+        assert np.all(dk[0, 0, b * tpb:(b + 1) * tpb] == 0) and np.all(dv[0, 0, b * tpb:(b + 1) * tpb] == 0)
+    assert np.all(dq[0, 0, tpb:2 * tpb] == 0)
+    assert np.abs(dq).max() > 0 and np.abs(dk).max() > 0 and np.abs(dv).max() > 0
