@@ -53,7 +53,7 @@ def _load():
         lib.oracle_pool.argtypes = [P, I, I, I, P]
         lib.oracle_select_rows.argtypes = [P, P, I, I, I, P, I, D, P, I, I, I, I, I, I, P, P, P]
         lib.oracle_attention_rows.argtypes = [P, P, P, I, I, I, P, P, P, I, D, P, P, P]
-        lib.oracle_attention_backward.argtypes = [P, P, P, P, I, I, I, I, P, P, D, P, P, P]
+        lib.oracle_attention_backward.argtypes = [P, P, P, P, P, I, I, I, I, P, P, D, P, P, P]
         for f in (lib.oracle_pool, lib.oracle_select_rows, lib.oracle_attention_rows, lib.oracle_attention_backward):
             f.restype = None
         _lib = lib
@@ -123,11 +123,16 @@ def select_rows(qbar: np.ndarray, kbar: np.ndarray, heads: int, block_grid: Sequ
 
 
 def attention_backward(q, k, v, dout, row_ptr, col_idx, scale: Optional[float] = None,
-                       tpb: int = TOKENS_PER_BLOCK):
+                       tpb: int = TOKENS_PER_BLOCK, out=None):
     """Gradients (dq, dk, dv) [B, H, N, d] fp64 of the block-sparse attention for the
     upstream gradient dout, from their definition (see oracle.c).  row_ptr/col_idx: a
-    valid CSR (ascending, in-range columns) over rows r = bh * nB + i."""
+    valid CSR (ascending, in-range columns) over rows r = bh * nB + i.  `out`: the
+    forward output as stored (e.g. rounded to bf16), used for D = dO . O; None
+    recomputes it in fp64."""
     q, k, v, g = _f32(q), _f32(k), _f32(v), _f32(dout)
+    o = None if out is None else _f32(out)
+    if o is not None and o.shape != q.shape:
+        raise ValueError("out must have the shape of q")
     *lead, n, d = q.shape
     BH = int(np.prod(lead)) if lead else 1
     nB = n // tpb
@@ -137,7 +142,7 @@ def attention_backward(q, k, v, dout, row_ptr, col_idx, scale: Optional[float] =
     dk = np.empty(q.shape, dtype=np.float64)
     dv = np.empty(q.shape, dtype=np.float64)
     sc = default_scale(d) if scale is None else float(scale)
-    _load().oracle_attention_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), BH, nB, tpb, d, _ptr(rp), _ptr(ci), sc,
+    _load().oracle_attention_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o), BH, nB, tpb, d, _ptr(rp), _ptr(ci), sc,
                                       _ptr(dq), _ptr(dk), _ptr(dv))
     return dq, dk, dv
 

@@ -225,12 +225,16 @@ void oracle_attention_rows(const float *q, const float *k, const float *v, int64
  *   dV_m = sum_n P_nm dO_n
  *   dP_nm = dO_n . v_m,  D_n = dO_n . O_n,  dS_nm = P_nm (dP_nm - D_n)
  *   dQ_n = scale sum_m dS_nm k_m,  dK_m = scale sum_n dS_nm q_n.
+ * D_n is the product of dO_n with the forward output.  A caller that holds that
+ * output, rounded as it was stored, passes it as `out` [BH][N][d] and D_n uses it;
+ * with out == NULL, O_n is recomputed here in fp64.
  * One head at a time (heads in parallel); within a head the rows are visited in
  * order, so the sums over n are in a fixed order.  Outputs are fp64 [BH][N][d].
  */
-void oracle_attention_backward(const float *q, const float *k, const float *v, const float *dout, int64_t BH,
-                               int64_t nB, int64_t tpb, int64_t d, const int64_t *row_ptr,
-                               const int32_t *col_idx, double scale, double *dq, double *dk, double *dv)
+void oracle_attention_backward(const float *q, const float *k, const float *v, const float *dout,
+                               const float *out, int64_t BH, int64_t nB, int64_t tpb, int64_t d,
+                               const int64_t *row_ptr, const int32_t *col_idx, double scale, double *dq,
+                               double *dk, double *dv)
 {
     const int64_t N = nB * tpb;
 #pragma omp parallel
@@ -274,6 +278,8 @@ void oracle_attention_backward(const float *q, const float *k, const float *v, c
                             const float *vm = vh + (col_idx[e] * tpb + u) * d;
                             for (int64_t c = 0; c < d; ++c) o[c] += w[m] * (double)vm[c];
                         }
+                    if (out)
+                        for (int64_t c = 0; c < d; ++c) o[c] = (double)out[(bh * N + n) * d + c];
                     double Dn = 0.0;
                     for (int64_t c = 0; c < d; ++c) Dn += (double)gn[c] * o[c];
                     /* dV, dP, dS, dQ, dK */

@@ -432,3 +432,35 @@ def test_backward_zero_outside_the_kept_blocks():
         assert np.all(dk[0, 0, b * tpb:(b + 1) * tpb] == 0) and np.all(dv[0, 0, b * tpb:(b + 1) * tpb] == 0)
     assert np.all(dq[0, 0, tpb:2 * tpb] == 0)
     assert np.abs(dq).max() > 0 and np.abs(dk).max() > 0 and np.abs(dv).max() > 0
+
+
+def test_backward_with_stored_output():
+    """D = dO . O uses the caller's stored output when given.  Shifting O by delta
+    shifts D by dO . delta, which leaves dV unchanged and moves dQ_n by
+    -scale (dO_n . delta_n) sum_m P_nm k_m (closed form; P k from the brute force
+    with k as the values)."""
+    rng = np.random.default_rng(10)
+    H, nB, tpb, d = 2, 3, 4, 5
+    N = nB * tpb
+    q, k, v, g = (rng.standard_normal((H, N, d)).astype(np.float32) for _ in range(4))
+    mask = rng.random((H, nB, nB)) < 0.6
+    mask[:, np.arange(nB), np.arange(nB)] = True
+    scale = 0.6
+    rp, ci = oracle.csr_from_mask(mask.reshape(H * nB, nB))
+    ref = oracle.attention_backward(q[None], k[None], v[None], g[None], rp, ci, scale=scale, tpb=tpb)
+    o = np.stack([brute.token_mask_attention(q[h].astype(np.float64), k[h].astype(np.float64),
+                                             v[h].astype(np.float64), mask[h], scale, tpb)[0] for h in range(H)])
+    same = oracle.attention_backward(q[None], k[None], v[None], g[None], rp, ci, scale=scale, tpb=tpb,
+                                     out=o[None].astype(np.float32))
+    for a, b in zip(same, ref):
+        assert np.abs(a - b).max() <= 1e-6 * np.abs(b).max()
+    delta = rng.standard_normal((H, N, d)).astype(np.float32)
+    shifted = (o.astype(np.float32) + delta)
+    got = oracle.attention_backward(q[None], k[None], v[None], g[None], rp, ci, scale=scale, tpb=tpb,
+                                    out=shifted[None])
+    assert np.array_equal(got[2], same[2])
+    dD = np.sum(g.astype(np.float64) * (shifted.astype(np.float64) - o.astype(np.float32)), axis=-1)   # [H, N]
+    pk = np.stack([brute.token_mask_attention(q[h].astype(np.float64), k[h].astype(np.float64),
+                                              k[h].astype(np.float64), mask[h], scale, tpb)[0] for h in range(H)])
+    expect = same[0][0] - scale * dD[..., None] * pk
+    assert np.abs(got[0][0] - expect).max() <= 1e-9 * np.abs(expect).max()
