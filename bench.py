@@ -54,6 +54,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-CSR reference forward")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-select-timing", action="store_true", help="skip the separate selection timing")
     ap.add_argument("--dense-steps", type=int, default=0,
                     help="denoising schedule: this many leading steps run dense (no selection)")
@@ -223,6 +224,35 @@ def main():
     reo_gbs = 2 * qd.numel() * elt / (reo_ms_med * 1e-3) / 1e9
     del reo
 
+    # backward over the selected block list (bf16): dQ over the rows, dK and dV over the
+    # transposed list; FLOPs counted as the five algorithmic products (S, dP, dV, dQ, dK)
+    bwd = None
+    if wl.dtype == "bf16" and not args.no_backward:
+        rp, ci = select()
+        forward(rp, ci)
+        gen = torch.Generator(device=dev).manual_seed(5)
+        dout = torch.randn(qd.shape, generator=gen, device=dev).to(qd.dtype)
+        grads = tuple(torch.empty_like(qd) for _ in range(3))
+        t_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+
+        def backward():
+            B.sparse_attn_backward(shape, qd, kd, vd, out, lse, dout, rp, ci, workspace=bufs.workspace,
+                                   t_idx=t_idx, stream=stream, grads=grads)
+        backward()
+        bwd_ms = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            backward()
+            b.record(stream)
+            torch.cuda.synchronize()
+            bwd_ms.append(a.elapsed_time(b))
+        bwd_ms_med = sorted(bwd_ms)[len(bwd_ms) // 2]
+        bwd_tf = 2.5 * flops / (bwd_ms_med * 1e-3) / 1e12
+        bwd = {"ms": round(bwd_ms_med, 4), "TFLOP_s": round(bwd_tf, 2),
+               "frac_bf16_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4)}
+        del dout, grads, t_idx
+
     # dense reference: the same forward kernel over the full CSR (every tile kept)
     full_bufs = B.alloc_buffers(shape, dev)
     full_rp, full_ci = B.sparse_attn_full_csr(shape, full_bufs, stream=stream)
@@ -310,6 +340,8 @@ def main():
             "select_plus_forward": round(dense_ms_med / (attn_ms_avg + sel_ms_med), 3),
         },
     }
+    if bwd is not None:
+        rec["backward"] = bwd
     if sched is not None:
         rec["denoise_schedule"] = sched
     if not args.no_cpu_baseline:

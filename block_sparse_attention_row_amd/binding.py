@@ -33,6 +33,7 @@ EXPORTED = (
     "sparse_attn_select",
     "sparse_attn_forward",
     "sparse_attn_mask_to_csr",
+    "sparse_attn_backward",
     "sparse_attn_full_csr",
     "sparse_attn_to_tiles",
     "sparse_attn_from_tiles",
@@ -90,6 +91,8 @@ def lib():
         L.sparse_attn_forward.restype = ctypes.c_int32
         L.sparse_attn_mask_to_csr.argtypes = [SP, P, P, P, I64, P, I64, P]
         L.sparse_attn_mask_to_csr.restype = ctypes.c_int32
+        L.sparse_attn_backward.argtypes = [SP, P, P, P, P, P, P, P, P, I64, P, P, P, P, P, I64, P]
+        L.sparse_attn_backward.restype = ctypes.c_int32
         L.sparse_attn_full_csr.argtypes = [SP, P, P, I64, P]
         L.sparse_attn_full_csr.restype = ctypes.c_int32
         for name in ("sparse_attn_to_tiles", "sparse_attn_from_tiles"):
@@ -212,6 +215,26 @@ def sparse_attn_mask_to_csr(shape: Shape, block_mask, buffers: Optional[Buffers]
                                        bufs.workspace.numel(), _stream(stream))
     _check(st, "sparse_attn_mask_to_csr")
     return bufs.row_ptr, bufs.col_idx
+
+
+def sparse_attn_backward(shape: Shape, q, k, v, out, lse, dout, row_ptr, col_idx, workspace=None, t_idx=None,
+                         stream=None, grads=None):
+    """Gradients (dq, dk, dv) of sparse_attn_forward for the upstream gradient dout
+    (written into `grads` = (dq, dk, dv) when given)."""
+    import torch
+    ws = workspace if workspace is not None else torch.empty(sparse_attn_workspace_size(shape), dtype=torch.uint8,
+                                                              device=q.device)
+    cc = col_idx.numel()
+    t_idx = t_idx if t_idx is not None else torch.empty(max(cc, 1), dtype=torch.int32, device=q.device)
+    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    for g in (dq, dk, dv):
+        if g.shape != q.shape or g.dtype != q.dtype or g.device != q.device or not g.is_contiguous():
+            raise ValueError("gradient outputs must be contiguous tensors like q")
+    st = lib().sparse_attn_backward(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                                    _ptr(row_ptr), _ptr(col_idx), cc, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(t_idx),
+                                    _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "sparse_attn_backward")
+    return dq, dk, dv
 
 
 def sparse_attn_full_csr(shape: Shape, buffers: Optional[Buffers] = None, device=None, stream=None):

@@ -65,6 +65,7 @@ int64_t max_slots(const Dims &d) { return n_pairs(d) * 4 < kMaxSlots ? n_pairs(d
 struct Layout {
     int64_t thr, qbar, kbar, bits, counts, groups;                       // selection
     int64_t items, plan_counts, pair_flag, merge, part_o, part_lse;      // attention row splitting
+    int64_t col_ptr, lse2, dn;                                           // backward
     int64_t total;
 };
 
@@ -96,6 +97,12 @@ Layout layout(const Dims &d) {
     off = align_up(off + 4 * ms * 2 * 64 * d.D, kAlign);
     l.part_lse = off;
     off = align_up(off + 4 * ms * 2 * 64, kAlign);
+    l.col_ptr = off;
+    off = align_up(off + 4 * (d.rows + 1), kAlign);
+    l.lse2 = off;                                   // lse2 then dn: one direct load reaches both
+    off = align_up(off + 4 * d.rows * 64, kAlign);
+    l.dn = off;
+    off = align_up(off + 4 * d.rows * 64, kAlign);
     l.total = off;
     return l;
 }
@@ -268,6 +275,60 @@ int32_t sparse_attn_mask_to_csr(const sparse_attn_shape *shape, const uint8_t *b
     if (launch_mask_bits(block_mask, d.B * d.H, (int32_t)d.nB, (int32_t)d.nW, bits, counts, groups, s))
         return SPARSE_ATTN_HIP_ERROR;
     return emit_csr(d, bits, counts, groups, row_ptr, col_idx, s);
+}
+
+int32_t sparse_attn_backward(const sparse_attn_shape *shape, const void *q, const void *k, const void *v,
+                             const void *out, const float *lse, const void *dout, const int32_t *row_ptr,
+                             const int32_t *col_idx, int64_t col_count, void *dq, void *dk, void *dv,
+                             int32_t *t_idx, void *workspace, int64_t workspace_bytes, void *stream) {
+    Dims d;
+    int32_t st = check_shape(shape, &d);
+    if (st) return st;
+    if (shape->dtype != SPARSE_ATTN_BF16) return SPARSE_ATTN_UNSUPPORTED;
+    if (d.nB > kSelectMaxBlocks) return SPARSE_ATTN_UNSUPPORTED;   // a row's bitmask is held in LDS
+    if (!q || !k || !v || !out || !lse || !dout || !row_ptr || !dq || !dk || !dv || !workspace)
+        return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (col_count < 0 || (col_count > 0 && (!col_idx || !t_idx))) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(dout, 16) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(row_ptr, 4) ||
+        !aligned(col_idx, 4) || !aligned(t_idx, 4) || !aligned(workspace, 16))
+        return SPARSE_ATTN_INVALID_ARGUMENT;
+    const Layout L = layout(d);
+    if (workspace_bytes < L.total) return SPARSE_ATTN_WORKSPACE;
+    char *ws = (char *)workspace;
+    BwdLaunch b;
+    b.args.q = q;
+    b.args.k = k;
+    b.args.v = v;
+    b.args.dout = dout;
+    b.args.lse2 = (float *)(ws + L.lse2);
+    b.args.dn = (float *)(ws + L.dn);
+    b.args.n_pairs = n_pairs(d);
+    b.args.pairs_per_head = (int32_t)((d.nB + 1) / 2);
+    b.args.nB = (int32_t)d.nB;
+    b.args.scale = effective_scale(shape);
+    b.args.scale_log2 = b.args.scale * kLog2e;
+    b.out = out;
+    b.lse = lse;
+    b.lse2 = (float *)(ws + L.lse2);
+    b.dn = (float *)(ws + L.dn);
+    b.row_ptr = row_ptr;
+    b.col_idx = col_idx;
+    b.col_count = col_count;
+    b.bits = (uint64_t *)(ws + L.bits);
+    b.colcount = (int32_t *)(ws + L.counts);
+    b.col_ptr = (int32_t *)(ws + L.col_ptr);
+    b.t_idx = t_idx;
+    b.dq = dq;
+    b.dk = dk;
+    b.dv = dv;
+    b.rows = d.rows;
+    b.BH = d.B * d.H;
+    b.nB = (int32_t)d.nB;
+    b.nW = (int32_t)d.nW;
+    b.d = (int32_t)d.D;
+    if (launch_backward(b, (hipStream_t)stream)) return SPARSE_ATTN_HIP_ERROR;
+    return SPARSE_ATTN_OK;
 }
 
 int32_t sparse_attn_full_csr(const sparse_attn_shape *shape, int32_t *row_ptr, int32_t *col_idx,

@@ -25,78 +25,9 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "tiles.h"
 
 namespace sattn {
-
-// ---------------------------------------------------------------------------
-// bf16 inputs, bf16 MFMA (v_mfma_f32_32x32x16_bf16), fp32 accumulation.
-//
-// K and V tiles go from global memory straight into LDS with
-// global_load_lds_dwordx4 (lane p of a wave-wide load lands at M0 + 16 p),
-// row-major, the 16-byte slots of row r XOR-swizzled by swz_key(r).  The key is
-// chosen for both read patterns: the K operand reads one slot of 16 consecutive
-// rows (the keys of rows r mod 16 must all differ), and a transposed V read
-// takes 4 consecutive slots of 4 consecutive rows (the keys of those rows must
-// move the 4-slot group), so that either fills all 64 banks without conflict.  V is
-// read transposed with ds_read_b64_tr_b16: within each 16-lane group, source
-// lane 4e + c names 4 consecutive d of key row e, and output lane i receives the
-// 4 keys at d = i -- the A-operand layout of O^T = V^T P^T.
-//
-// The direct loads are issued from inline asm and waited for explicitly, so the
-// next K streams in during the softmax and P V of the current tile and the next V
-// during the next Q K^T.  Column indices come through the scalar cache.
-template <int N> __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// One wave-wide 16-byte-per-lane load from sbase + voff into LDS at lds_addr + 16 * lane.
-__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, const void *sbase) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff), "s"(sbase)
-                 : "memory", "m0");
-}
-
-// XOR key of the 16-byte slots of tile row r (see above): a bijection on r mod 16
-// for 16-slot rows, and on (r >> 1) mod 8 within each row parity for 8-slot rows
-// (128-byte rows: even and odd rows sit on opposite halves of the banks).
-template <int SLOTS> __device__ __forceinline__ int swz_key(int r) {
-    if constexpr (SLOTS == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
-    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
-
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) char lds_char;
-typedef const __attribute__((address_space(4))) int32_t const_i32;
-
-// Tile geometry of the bf16 kernel.
-template <int D> struct TileGeo {
-    static constexpr int ROWB = D * 2;            // bytes per token row
-    static constexpr int SLOTS = ROWB / 16;       // 16-byte slots per row
-    static constexpr int RPI = 1024 / ROWB;       // rows written by one wave-wide direct load
-    static constexpr int IPW = 16 / RPI;          // direct loads per wave per tensor (each wave: 16 rows)
-    static constexpr int NDT = D / 32;            // 32-wide d tiles of the output
-    static constexpr int TILEB = 64 * ROWB;
-    // byte offset of element (r, col) in a swizzled tile (col a multiple of 4)
-    static __device__ __forceinline__ int swz(int r, int col) {
-        return r * ROWB + 16 * ((col >> 3) ^ swz_key<SLOTS>(r)) + 2 * (col & 7);
-    }
-};
-
-// S^T = K Q^T for the two 32-key halves of a tile (K from LDS).
-template <int D>
-__device__ __forceinline__ void tile_scores(const char *K, const bf16x8 *qf, int l32, int hh, f32x16 *acc_s) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc_s[kt][v] = 0.f;
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(K + TileGeo<D>::swz(32 * kt + l32, 16 * c + 8 * hh));
-            acc_s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], acc_s[kt], 0, 0, 0);
-        }
-    }
-}
 
 // Online-softmax bookkeeping for one tile of raw scores; this lane owns one query.
 // The running max is kept in raw dot-product units and only moved when a new score
@@ -136,35 +67,6 @@ __device__ __forceinline__ void tile_probs(const f32x16 *acc_s, float c, float m
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             l_run = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){pf[kc][2 * e], pf[kc][2 * e + 1]}, kOnes2, l_run, false);
-    }
-}
-
-// O^T += V^T P^T over four 16-key chunks; slot e of chunk kc is key
-// 16 kc + (e < 4 ? 4 hh + e : 8 + 4 hh + e - 4), matching the accumulators of P.
-// The transposed V reads run two MFMAs ahead of their use.
-template <int D>
-__device__ __forceinline__ bf16x8 v_frag(const char *V, int lane, int kc, int dt) {
-    const int tr_e = (lane & 15) >> 2, tr_c = lane & 3, tr_g = lane >> 4;
-    const int cc = 32 * dt + 16 * (tr_g & 1) + 4 * tr_c;
-    const int r0 = 16 * kc + 4 * (tr_g >> 1) + tr_e;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(V + TileGeo<D>::swz(r0, cc)));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(V + TileGeo<D>::swz(r0 + 8, cc)));
-    return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-}
-
-template <int D>
-__device__ __forceinline__ void tile_pv(const char *V, const bf16x8 *pf, int lane, f32x16 *acc_o) {
-    constexpr int NDT = TileGeo<D>::NDT, NM = 4 * NDT;
-    // four-slot ring: the read for MFMA i+2 lands in the slot MFMA i-2 used, so it
-    // can be issued before MFMA i without waiting on MFMA i-1's operand reads
-    bf16x8 vf[4];
-    vf[0] = v_frag<D>(V, lane, 0, 0);
-    vf[1] = v_frag<D>(V, lane, 1 / NDT, 1 % NDT);
-#pragma unroll
-    for (int i = 0; i < NM; ++i) {
-        if (i + 2 < NM) vf[(i + 2) % 4] = v_frag<D>(V, lane, (i + 2) / NDT, (i + 2) % NDT);
-        acc_o[i % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 4], pf[i / NDT], acc_o[i % NDT], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -476,29 +378,6 @@ __device__ __forceinline__ int64_t block_sum64(int64_t v, int64_t *lds16) {
     for (int w = 0; w < 16; ++w) t += lds16[w];
     return t;
 }
-// Exclusive prefix over the 1024 threads (thread order) and the total.
-__device__ __forceinline__ int32_t block_scan32(int32_t v, int32_t *lds16, int32_t &total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int32_t incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int32_t u = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += u;
-    }
-    __syncthreads();
-    if (lane == 63) lds16[wave] = incl;
-    __syncthreads();
-    int32_t before = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < 16; ++w) {
-        const int32_t x = lds16[w];
-        before += w < wave ? x : 0;
-        tot += x;
-    }
-    total = tot;
-    return before + incl - v;
-}
-
 // Piece length L = max(kMinPiece, total work / resident workgroups), doubled until
 // the pieces fit the partial slots; a pair whose longer row holds est > L tiles is cut
 // into ceil(est / L) pieces, each row split evenly by position.  A piece also records

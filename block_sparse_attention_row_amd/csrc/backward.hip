@@ -1,0 +1,370 @@
+// Block-sparse attention backward (gfx950, bf16 inputs, bf16 MFMA, fp32 accumulation).
+//
+// Gradients of the forward in attention.hip, for the training use of the NABLA
+// summary page ("NABLA: Neighborhood Adaptive Block-Level Attention", sections
+// "Methodologie : NABLA" and the training results).  With P the softmax weights
+// recovered from the forward's log-sum-exp, P_nm = exp(scale q_n.k_m - lse_n), and an
+// upstream gradient dO:
+//   dV = P^T dO,  dP = dO V^T,  D_n = dO_n . O_n,  dS = P o (dP - D),
+//   dQ = scale dS K,  dK = scale dS^T Q.
+// Three passes, each writing whole output rows from one workgroup (no atomics, a
+// fixed summation order):
+//   dQ  a pair of query blocks walks its CSR rows (key tiles streamed into LDS):
+//       S^T = K Q^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T;
+//   dV  a pair of key blocks walks the transposed list (query tiles streamed):
+//       S = Q K^T, P, then dV^T += dO^T P;
+//   dK  likewise: S, P, dP = dO V^T, dS, then dK^T += Q^T dS.
+// Each is the forward's tile machinery with other operands: the streamed tile is
+// the A operand of the scores and, read transposed, of the output product; the
+// pair's own rows sit in registers as the B operand.  The transposed list (for
+// every key block, the query blocks that keep it, ascending) is built from row
+// bitmasks, so it is deterministic and applies the forward's skip rule.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+#include "tiles.h"
+
+namespace sattn {
+
+// ---------------------------------------------------------------------------
+// D_n = dO_n . O_n and lse_n in log2 units, one token per D/8 lanes.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16 *__restrict__ o, const __bf16 *__restrict__ dout,
+                                                       const float *__restrict__ lse, float *__restrict__ lse2,
+                                                       float *__restrict__ dn, int64_t ntok) {
+    constexpr int LPT = D / 8, TPW = 64 / LPT;
+    const int lane = threadIdx.x & 63;
+    const int64_t tok = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW + lane / LPT;
+    float acc = 0.f;
+    if (tok < ntok) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8 *>(o + tok * D + 8 * (lane % LPT));
+        const bf16x8 g = *reinterpret_cast<const bf16x8 *>(dout + tok * D + 8 * (lane % LPT));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += (float)x[e] * (float)g[e];
+    }
+#pragma unroll
+    for (int off = 1; off < LPT; off <<= 1) acc += __shfl_xor(acc, off, 64);
+    if (tok < ntok && lane % LPT == 0) {
+        dn[tok] = acc;
+        lse2[tok] = lse[tok] * kLog2e;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Transposed block list.
+//
+// Row bitmasks with the forward's skip rule: an entry counts when it lies in [0, nB)
+// and above every entry the row accepted before it (a prefix max over the lanes).
+__global__ __launch_bounds__(256) void csr_bits_kernel(const int32_t *__restrict__ row_ptr,
+                                                       const int32_t *__restrict__ col_idx, int64_t col_count,
+                                                       int64_t rows, int32_t nB, int32_t nW,
+                                                       uint64_t *__restrict__ bits) {
+    __shared__ unsigned long long wb[4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+    if (row >= rows) return;
+    if (lane < nW) wb[wave][lane] = 0ull;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int64_t beg = row_ptr[row], end = row_ptr[row + 1];
+    end = end < col_count ? end : col_count;
+    beg = beg < 0 ? 0 : beg;
+    int carry = -1;
+    for (int64_t base = beg; base < end; base += 64) {
+        const int c = base + lane < end ? col_idx[base + lane] : -1;
+        const bool valid = c >= 0 && c < nB;
+        int incl = valid ? c : -1;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(incl, o, 64);
+            if (lane >= o) incl = max(incl, u);
+        }
+        int excl = __shfl_up(incl, 1, 64);
+        excl = max(carry, lane == 0 ? -1 : excl);
+        if (valid && c > excl) atomicOr(&wb[wave][c >> 6], 1ull << (c & 63));
+        carry = max(carry, __shfl(incl, 63, 64));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < nW) bits[row * nW + lane] = wb[wave][lane];
+}
+
+// One wave per (head, 64-column word): lane b owns column 64 w + b.  The rows are
+// taken 64 at a time (lane l loads row r0 + l's word); per bit, a ballot over the
+// lanes gives the rows that keep that column.  COUNT: columns' totals; else the
+// rows are written to their column's list in ascending order.
+template <bool COUNT>
+__global__ __launch_bounds__(256) void csc_pass_kernel(const uint64_t *__restrict__ bits, int64_t BH, int32_t nB,
+                                                       int32_t nW, int32_t *__restrict__ colcount,
+                                                       const int32_t *__restrict__ col_ptr,
+                                                       int32_t *__restrict__ row_idx) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wv >= BH * nW) return;
+    const int64_t bh = wv / nW;
+    const int w = (int)(wv % nW);
+    const int col = 64 * w + lane;
+    const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    int run = 0;                                          // rows found so far for column 64 w + lane
+    const int cp = (!COUNT && col < nB) ? col_ptr[bh * nB + col] : 0;
+    for (int r0 = 0; r0 < nB; r0 += 64) {
+        const uint64_t word = r0 + lane < nB ? bits[(bh * nB + r0 + lane) * nW + w] : 0ull;
+        for (int b = 0; b < 64; ++b) {
+            const bool set = (word >> b) & 1ull;
+            const uint64_t m = __ballot(set);
+            if (!COUNT && set) {
+                const int pos = __builtin_amdgcn_readlane(cp, b) + __builtin_amdgcn_readlane(run, b) +
+                                __popcll(m & lt_mask);
+                row_idx[pos] = r0 + lane;
+            }
+            if (lane == b) run += __popcll(m);
+        }
+    }
+    if (COUNT && col < nB) colcount[bh * nB + col] = run;
+}
+
+// Exclusive prefix of n counts into out[0 .. n] (one workgroup).
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t *__restrict__ in, int64_t n,
+                                                    int32_t *__restrict__ out) {
+    __shared__ int32_t part[16];
+    int32_t carry = 0;
+    for (int64_t b0 = 0; b0 < n; b0 += 1024) {
+        const int64_t i = b0 + threadIdx.x;
+        int32_t total;
+        const int32_t ex = block_scan32(i < n ? in[i] : 0, part, total);
+        if (i < n) out[i] = carry + ex;
+        carry += total;
+    }
+    if (threadIdx.x == 0) out[n] = carry;
+}
+
+// ---------------------------------------------------------------------------
+// The three gradient passes.
+enum BwdMode { kDQ = 0, kDV = 1, kDK = 2 };
+
+template <int D, int MODE>
+__global__ __launch_bounds__(256, 2) void bwd_kernel(BwdArgs a) {
+    using G = TileGeo<D>;
+    constexpr int ROWB = G::ROWB, SLOTS = G::SLOTS, RPI = G::RPI, IPW = G::IPW, NDT = G::NDT, TILEB = G::TILEB;
+    __shared__ __attribute__((aligned(1024))) char T1s[2 * TILEB];
+    __shared__ __attribute__((aligned(1024))) char T2s[2 * TILEB];
+    __shared__ __attribute__((aligned(16))) float aux[2][256];   // per buffer: lse2 [64], D [64] of the streamed block
+
+    const int t = threadIdx.x, lane = t & 63, hh = lane >> 5, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int grp = wave >> 1, half = wave & 1;   // block of the pair, 32-row half of the block
+    const int64_t pair = xcd_chunk_remap<256>(blockIdx.x, a.n_pairs);
+    const int64_t bh = pair / a.pairs_per_head;
+    const int i0 = (int)(pair % a.pairs_per_head) * 2;
+    const int64_t N = (int64_t)a.nB * 64;
+    // streamed tiles: key tiles K, V for dQ; query tiles Q, dO for dV and dK
+    const char *t1g = (const char *)(MODE == kDQ ? a.k : a.q) + bh * N * ROWB + 16 * wave * ROWB;
+    const char *t2g = (const char *)(MODE == kDQ ? a.v : a.dout) + bh * N * ROWB + 16 * wave * ROWB;
+    const float c = a.scale_log2;
+
+    const int64_t rowA = bh * a.nB + i0;
+    const bool hasB = i0 + 1 < a.nB;
+    auto clamp_range = [&](int64_t r, int64_t &b, int64_t &e) {
+        b = a.ptr[r];
+        e = a.ptr[r + 1];
+        e = e < a.idx_count ? e : a.idx_count;
+        b = b < 0 ? 0 : b;
+        if (e < b) e = b;
+    };
+    int64_t begA, endA, begB = 0, endB = 0;
+    clamp_range(rowA, begA, endA);
+    if (hasB) clamp_range(rowA + 1, begB, endB);
+    const bool has_row = grp == 0 || hasB;
+
+    // the pair's own rows, B operands of the score products: queries and dO (dQ), keys
+    // (dV), keys and V (dK); row 32 half + l32 of block i0 + grp, d = 16 cq + 8 hh ..
+    const int64_t own = bh * N + (int64_t)(i0 + grp) * 64 + 32 * half + l32;
+    const __bf16 *o1 = (const __bf16 *)(MODE == kDQ ? a.q : a.k) + own * D;
+    const __bf16 *o2 = (const __bf16 *)(MODE == kDQ ? a.dout : a.v) + own * D;
+    bf16x8 f1[D / 16], f2[D / 16];
+#pragma unroll
+    for (int cq = 0; cq < D / 16; ++cq) {
+        f1[cq] = has_row ? *reinterpret_cast<const bf16x8 *>(o1 + 16 * cq + 8 * hh) : bf16x8{};
+        f2[cq] = (MODE != kDV && has_row) ? *reinterpret_cast<const bf16x8 *>(o2 + 16 * cq + 8 * hh) : bf16x8{};
+    }
+    const float lse2_q = (MODE == kDQ && has_row) ? a.lse2[own] : 0.f;
+    const float d_q = (MODE == kDQ && has_row) ? a.dn[own] : 0.f;
+
+    // merged walk over the two lists (as in the forward)
+    constexpr int kNone = 0x7fffffff;
+    const int32_t *cv = a.idx;
+    auto window = [&](int64_t base, int64_t e) { return base + lane < e ? cv[base + lane] : kNone; };
+    int64_t baseA = begA, baseB = begB;
+    int posA = 0, posB = 0;
+    int winA = window(baseA, endA), nxtA = window(baseA + 64, endA);
+    int winB = window(baseB, endB), nxtB = window(baseB + 64, endB);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    int lastA = -1, lastB = -1;
+    auto peek = [&](int64_t &base, int &pos, int &win, int &nxt, int64_t e, int last) {
+        while (base + pos < e) {
+            if (pos == 64) {
+                base += 64;
+                pos = 0;
+                win = nxt;
+                nxt = window(base + 64, e);
+            }
+            const int cc = __builtin_amdgcn_readlane(win, pos);
+            if (cc > last && cc < a.nB) return cc;
+            ++pos;
+        }
+        return kNone;
+    };
+    auto next_union = [&](int &col, bool &mine) {
+        const int cA = peek(baseA, posA, winA, nxtA, endA, lastA);
+        const int cB = peek(baseB, posB, winB, nxtB, endB, lastB);
+        col = cA < cB ? cA : cB;
+        const bool inA = cA == col && col != kNone, inB = cB == col && col != kNone;
+        if (inA) { lastA = cA; ++posA; }
+        if (inB) { lastB = cB; ++posB; }
+        mine = grp ? inB : inA;
+    };
+
+    // direct loads: this wave covers rows 16 w .. 16 w + 15 of each streamed tile;
+    // for dV and dK wave 0 also brings the block's lse2 and D (lanes 0-15 and 16-31;
+    // lanes 32-63 repeat them into the unused half of the buffer)
+    uint32_t voff[IPW];
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+        const int r = RPI * j + lane / SLOTS, sl = lane % SLOTS;
+        voff[j] = r * ROWB + 16 * (sl ^ swz_key<SLOTS>(r));
+    }
+    const uint32_t t1s0 = (uint32_t)(uintptr_t)(lds_char *)T1s + 16 * wave * ROWB;
+    const uint32_t t2s0 = (uint32_t)(uintptr_t)(lds_char *)T2s + 16 * wave * ROWB;
+    const uint32_t ax0 = (uint32_t)(uintptr_t)(lds_char *)&aux[0][0];
+    const uint32_t aux_voff = (uint32_t)((lane & 31) < 16 ? 16 * (lane & 15)
+                                                           : (uint32_t)((const char *)a.dn - (const char *)a.lse2) +
+                                                                 16 * (lane & 15));
+    auto issue = [&](int64_t col, int buf) {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) dma16(t1s0 + buf * TILEB + RPI * i * ROWB, voff[i], t1g + col * TILEB);
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) dma16(t2s0 + buf * TILEB + RPI * i * ROWB, voff[i], t2g + col * TILEB);
+        if (MODE != kDQ && wave == 0)
+            dma16(ax0 + buf * 1024, aux_voff, (const char *)a.lse2 + (bh * N + col * 64) * 4);
+    };
+
+    f32x16 acc[NDT];
+#pragma unroll
+    for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+
+    int col0, col1;
+    bool mine0, mine1;
+    next_union(col0, mine0);
+    if (col0 != kNone) issue(col0, 0);
+
+    auto step = [&](auto bj_tag) {
+        constexpr int BJ = decltype(bj_tag)::value;
+        wait_vmcnt<0>();            // this wave's part of tile j has landed
+        next_union(col1, mine1);
+        __syncthreads();            // ... and everyone's; the buffers of tile j-1 are free
+        if (col1 != kNone) issue(col1, BJ ^ 1);
+        if (!mine0) return;
+        const char *T1 = T1s + BJ * TILEB, *T2 = T2s + BJ * TILEB;
+        const float *ax = aux[BJ];
+        f32x16 s[2], dp[2];
+        tile_scores<D>(T1, f1, l32, hh, s);
+        if (MODE != kDV) tile_scores<D>(T2, f2, l32, hh, dp);
+        bf16x8 pf[4];
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            f32x4 lo_l, hi_l, lo_d, hi_d;   // lse2, D of the 8 streamed rows of this chunk (dV, dK)
+            if (MODE != kDQ) {
+                lo_l = *reinterpret_cast<const f32x4 *>(ax + 16 * kc + 4 * hh);
+                hi_l = *reinterpret_cast<const f32x4 *>(ax + 16 * kc + 8 + 4 * hh);
+                lo_d = *reinterpret_cast<const f32x4 *>(ax + 64 + 16 * kc + 4 * hh);
+                hi_d = *reinterpret_cast<const f32x4 *>(ax + 64 + 16 * kc + 8 + 4 * hh);
+            }
+            f32x8 pv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = s[kc >> 1][8 * (kc & 1) + e];
+                const float l2 = MODE == kDQ ? lse2_q : (e < 4 ? lo_l[e] : hi_l[e - 4]);
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -l2));
+                if (MODE == kDV) {
+                    pv[e] = p;
+                } else {
+                    const float dd = MODE == kDQ ? d_q : (e < 4 ? lo_d[e] : hi_d[e - 4]);
+                    pv[e] = p * (dp[kc >> 1][8 * (kc & 1) + e] - dd);
+                }
+            }
+            pf[kc] = __builtin_convertvector(pv, bf16x8);
+        }
+        // dQ^T += K^T dS^T (K tile read transposed); dV^T += dO^T P; dK^T += Q^T dS
+        tile_pv<D>(MODE == kDV ? T2 : T1, pf, lane, acc);
+    };
+    while (col0 != kNone) {
+        step(std::integral_constant<int, 0>{});
+        col0 = col1;
+        mine0 = mine1;
+        if (col0 == kNone) break;
+        step(std::integral_constant<int, 1>{});
+        col0 = col1;
+        mine0 = mine1;
+    }
+
+    if (!has_row) return;
+    // lane owns row 32 half + l32 of its block, d = 32 dt + 8 rr + 4 hh + {0..3}
+    const float mult = MODE == kDV ? 1.f : a.scale;
+    __bf16 *og = (__bf16 *)a.grad + own * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            f32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = acc[dt][4 * rr + e] * mult;
+            *reinterpret_cast<bf16x4 *>(og + 32 * dt + 8 * rr + 4 * hh) = __builtin_convertvector(w, bf16x4);
+        }
+}
+
+// ---------------------------------------------------------------------------
+int launch_backward(const BwdLaunch &L, hipStream_t s) {
+    const int64_t ntok = L.rows * 64;
+    const int tpw = 64 / (L.d / 8);
+    const dim3 pg((unsigned)((ntok + 4 * tpw - 1) / (4 * tpw))), pb(256);
+    if (L.d == 128)
+        bwd_prep_kernel<128><<<pg, pb, 0, s>>>((const __bf16 *)L.out, (const __bf16 *)L.args.dout, L.lse, L.lse2, L.dn, ntok);
+    else
+        bwd_prep_kernel<64><<<pg, pb, 0, s>>>((const __bf16 *)L.out, (const __bf16 *)L.args.dout, L.lse, L.lse2, L.dn, ntok);
+    csr_bits_kernel<<<dim3((unsigned)((L.rows + 3) / 4)), dim3(256), 0, s>>>(L.row_ptr, L.col_idx, L.col_count, L.rows,
+                                                                            L.nB, L.nW, L.bits);
+    const int64_t words = L.BH * L.nW;
+    const dim3 wg((unsigned)((words + 3) / 4)), wb(256);
+    csc_pass_kernel<true><<<wg, wb, 0, s>>>(L.bits, L.BH, L.nB, L.nW, L.colcount, nullptr, nullptr);
+    scan_kernel<<<1, 1024, 0, s>>>(L.colcount, L.rows, L.col_ptr);
+    csc_pass_kernel<false><<<wg, wb, 0, s>>>(L.bits, L.BH, L.nB, L.nW, nullptr, L.col_ptr, L.t_idx);
+    BwdArgs csr = L.args, csc = L.args;
+    csr.ptr = L.row_ptr;
+    csr.idx = L.col_idx;
+    csr.idx_count = L.col_count;
+    csr.grad = L.dq;
+    csc.ptr = L.col_ptr;
+    csc.idx = L.t_idx;
+    csc.idx_count = L.col_count;
+    BwdArgs cdv = csc, cdk = csc;
+    cdv.grad = L.dv;
+    cdk.grad = L.dk;
+    const dim3 g((unsigned)L.args.n_pairs), b(256);
+    if (L.d == 128) {
+        bwd_kernel<128, kDQ><<<g, b, 0, s>>>(csr);
+        bwd_kernel<128, kDV><<<g, b, 0, s>>>(cdv);
+        bwd_kernel<128, kDK><<<g, b, 0, s>>>(cdk);
+    } else {
+        bwd_kernel<64, kDQ><<<g, b, 0, s>>>(csr);
+        bwd_kernel<64, kDV><<<g, b, 0, s>>>(cdv);
+        bwd_kernel<64, kDK><<<g, b, 0, s>>>(cdk);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace sattn

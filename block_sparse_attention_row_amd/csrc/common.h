@@ -155,4 +155,27 @@ template <int64_t C> __device__ __forceinline__ int64_t xcd_chunk_remap(int64_t 
 // (1, 1) in bf16, for row sums with v_dot2_f32_bf16
 #define kOnes2 ((bf16x2){(__bf16)1.0f, (__bf16)1.0f})
 
+// Exclusive prefix over the 1024 threads (thread order) and the total.
+__device__ __forceinline__ int32_t block_scan32(int32_t v, int32_t *lds16, int32_t &total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+    }
+    __syncthreads();
+    if (lane == 63) lds16[wave] = incl;
+    __syncthreads();
+    int32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        const int32_t x = lds16[w];
+        before += w < wave ? x : 0;
+        tot += x;
+    }
+    total = tot;
+    return before + incl - v;
+}
+
 }  // namespace sattn

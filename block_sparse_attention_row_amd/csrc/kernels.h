@@ -96,6 +96,33 @@ int launch_mask_bits(const uint8_t *mask, int64_t bh, int32_t nB, int32_t nW, ui
 int launch_full_csr(int64_t rows, int32_t nB, int32_t *row_ptr, int32_t *col_idx, hipStream_t s);
 int launch_emit(const uint64_t *bits, const int32_t *counts, const int32_t *group_sums, int64_t rows, int32_t nB,
                 int32_t nW, int32_t *row_ptr, int32_t *col_idx, hipStream_t s);
+// Backward (bf16).
+struct BwdArgs {
+    const void *q, *k, *v, *dout;
+    const float *lse2, *dn;       // [B*H*N]: the forward's log-sum-exp in log2 units, dO . O
+    const int32_t *ptr, *idx;     // block list walked: CSR (dQ) or its transpose (dV, dK)
+    int64_t idx_count;            // entries of idx
+    void *grad;                   // the gradient this pass writes, bf16 [B, H, N, d]
+    int64_t n_pairs;              // B*H*ceil(nB/2) pairs of blocks
+    int32_t pairs_per_head, nB;
+    float scale_log2, scale;
+};
+struct BwdLaunch {
+    BwdArgs args;                 // fields common to the three passes
+    const void *out;
+    const float *lse;
+    float *lse2, *dn;             // workspace
+    const int32_t *row_ptr, *col_idx;
+    int64_t col_count;
+    uint64_t *bits;               // workspace [rows][nW]
+    int32_t *colcount, *col_ptr;  // workspace [rows], [rows + 1]
+    int32_t *t_idx;               // caller's [col_count]: the transposed list
+    void *dq, *dk, *dv;
+    int64_t rows, BH;
+    int32_t nB, nW, d;
+};
+int launch_backward(const BwdLaunch &L, hipStream_t s);
+
 int launch_attention(const AttnArgs &a, int dtype, int d, hipStream_t s);   // bf16: plan, attention, merge
 
 }  // namespace sattn

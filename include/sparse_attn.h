@@ -172,6 +172,32 @@ int32_t sparse_attn_mask_to_csr(const sparse_attn_shape *shape, const uint8_t *b
                                 void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * Backward of sparse_attn_forward (bf16 only and nB <= 4096; SPARSE_ATTN_UNSUPPORTED
+ * otherwise):
+ * the gradients for training (NABLA summary page, "Methodologie : NABLA" and its
+ * training results).  With P the forward's softmax weights (recovered from lse)
+ * and dO the upstream gradient:
+ *   dV = P^T dO,  dS = P o (dO V^T - rowsum(dO o O)),  dQ = scale dS K,
+ *   dK = scale dS^T Q.
+ *
+ *   q, k, v, out  device, [B, H, N, d] bf16: the forward's inputs and output.
+ *   lse         device fp32 [B, H, N]: the forward's log-sum-exp (required).
+ *   dout        device, [B, H, N, d] bf16: dL/dout.
+ *   row_ptr, col_idx, col_count: the block list the forward used (same rules).
+ *   dq, dk, dv  device, [B, H, N, d] bf16, fully written (zeros where no tile
+ *               reaches a row).
+ *   t_idx       device int32 [col_count], caller-owned scratch: receives the
+ *               transposed block list (for each key block, the query blocks
+ *               that keep it, ascending).
+ *   workspace   as in sparse_attn_forward.
+ * The result is deterministic (no atomics; fixed summation order).
+ */
+int32_t sparse_attn_backward(const sparse_attn_shape *shape, const void *q, const void *k, const void *v,
+                             const void *out, const float *lse, const void *dout, const int32_t *row_ptr,
+                             const int32_t *col_idx, int64_t col_count, void *dq, void *dk, void *dv,
+                             int32_t *t_idx, void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
  * The dense block list: every query block keeps every key block (row r holds
  * 0 .. nB-1 at col_idx[r * nB ...]).  For dense warm-up steps or layers in a
  * denoising loop, where the selection is skipped or its block list is reused

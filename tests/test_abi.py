@@ -64,6 +64,9 @@ def test_capacity_and_workspace_formulas():
     expect = al(expect + 12 * slots)                      # merge list
     expect = al(expect + 4 * slots * 2 * 64 * 128)        # partial outputs (fp32)
     expect = al(expect + 4 * slots * 2 * 64)              # partial log-sum-exp
+    expect = al(expect + 4 * (rows + 1))                  # backward: transposed row pointers
+    expect = al(expect + 4 * rows * 64)                   # backward: lse in log2 units
+    expect = al(expect + 4 * rows * 64)                   # backward: dO . O
     assert B.sparse_attn_workspace_size(s) == expect
 
 
@@ -186,3 +189,21 @@ def test_full_csr_rejects_before_launch():
     assert f(ctypes.byref(s), A, A, cap - 1, None) == B.SPARSE_ATTN_CAPACITY
     assert f(ctypes.byref(s), None, A, cap, None) == B.SPARSE_ATTN_INVALID_ARGUMENT
     assert f(ctypes.byref(s), A, A + 2, cap, None) == B.SPARSE_ATTN_INVALID_ARGUMENT
+
+
+def test_backward_rejects_before_launch():
+    f = B.lib().sparse_attn_backward
+    s = _shape()
+    wsb = B.sparse_attn_workspace_size(s)
+    ok = dict(q=A, k=A, v=A, o=A, lse=A, g=A, rp=A, ci=A, cc=10, dq=A, dk=A, dv=A, ti=A, ws=A, wsb=wsb)
+
+    def call(**kw):
+        x = dict(ok, **kw)
+        return f(ctypes.byref(x.pop("shape", s)), x["q"], x["k"], x["v"], x["o"], x["lse"], x["g"], x["rp"], x["ci"],
+                 x["cc"], x["dq"], x["dk"], x["dv"], x["ti"], x["ws"], x["wsb"], None)
+    assert call(shape=_shape(dtype="f32")) == B.SPARSE_ATTN_UNSUPPORTED
+    assert call(lse=None) == B.SPARSE_ATTN_INVALID_ARGUMENT
+    assert call(ti=None) == B.SPARSE_ATTN_INVALID_ARGUMENT
+    assert call(dk=A + 4) == B.SPARSE_ATTN_INVALID_ARGUMENT
+    assert call(cc=-1) == B.SPARSE_ATTN_INVALID_ARGUMENT
+    assert call(wsb=wsb - 1) == B.SPARSE_ATTN_WORKSPACE

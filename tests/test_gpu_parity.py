@@ -219,6 +219,86 @@ def test_full_csr_is_the_dense_block_list():
     assert err <= P.TOL["bf16"] and lerr <= P.LSE_TOL["bf16"]
 
 
+def _backward_case(wl, reading, mask=None, seed=0):
+    q, k, v, _ = make_inputs(wl, reading)
+    qd, kd, vd = P.to_device(q, k, v)
+    shape = P.shape_for(wl)
+    rows, nB = wl.heads * wl.blocks, wl.blocks
+    if mask is None:
+        qbar, kbar = oracle.pool(q), oracle.pool(k)
+        mask = oracle.select_rows(qbar, kbar, wl.heads, wl.block_grid, float(wl.threshold)) != 0
+    orp, oci = oracle.csr_from_mask(mask)
+    out, lse = P.gpu_forward(wl, qd, kd, vd, orp, oci)
+    gen = torch.Generator().manual_seed(seed)
+    g = torch.randn(q.shape, generator=gen).to(torch.bfloat16)
+    return q, k, v, qd, kd, vd, out, lse, g, shape, orp, oci
+
+
+def _rel_err(got, ref):
+    got = got.float().cpu().numpy().astype(np.float64)
+    return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+@pytest.mark.parametrize("d,grid,thr,reading,seed", [(128, (3, 4, 5), 0.8, "A", 31), (64, (2, 3, 5), 0.9, "B", 37)])
+def test_backward_matches_oracle(d, grid, thr, reading, seed):
+    """dQ, dK, dV against the fp64 oracle under the same block list; the block count
+    is odd, so the last pair of each head has one block."""
+    wl = small_workload("bwd", 2, d, grid, "bf16", threshold=thr, seed=seed)
+    q, k, v, qd, kd, vd, out, lse, g, shape, orp, oci = _backward_case(wl, reading, seed=seed)
+    rpd = torch.as_tensor(orp.astype(np.int32)).cuda()
+    cid = torch.as_tensor(oci).cuda()
+    dq, dk, dv = B.sparse_attn_backward(shape, qd, kd, vd, out, lse, g.cuda(), rpd, cid)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward(q, k, v, g, orp, oci)
+    errs = [_rel_err(x, r) for x, r in ((dq, rq), (dk, rk), (dv, rv))]
+    print(f"backward rel err dq {errs[0]:.3e} dk {errs[1]:.3e} dv {errs[2]:.3e}", flush=True)
+    assert max(errs[:2]) <= P.BWD_TOL_DQK and errs[2] <= P.BWD_TOL_DV
+    # Same stored output on both sides (the oracle's forward, rounded to bf16): what
+    # is left is the kernels' own rounding of P and dS.
+    o_ref, _ = oracle.attention_rows(q, k, v, orp, oci, np.arange(wl.heads * wl.blocks))
+    o_bf = torch.as_tensor(o_ref.reshape(q.shape)).to(torch.bfloat16)
+    dq, dk, dv = B.sparse_attn_backward(shape, qd, kd, vd, o_bf.cuda(), lse, g.cuda(), rpd, cid)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward(q, k, v, g, orp, oci, out=o_bf.float())
+    errs = [_rel_err(x, r) for x, r in ((dq, rq), (dk, rk), (dv, rv))]
+    print(f"backward (same O) rel err dq {errs[0]:.3e} dk {errs[1]:.3e} dv {errs[2]:.3e}", flush=True)
+    assert max(errs[:2]) <= P.BWD_TOL_DQK and errs[2] <= P.BWD_TOL_DV
+
+
+def test_backward_empty_rows_unused_keys_and_skipped_entries():
+    """Empty query rows get dQ = 0, key blocks nobody keeps get dK = dV = 0, and
+    repeated, descending or out-of-range entries change nothing (bit-exact)."""
+    wl = small_workload("bwd2", 2, 128, (3, 3, 3), "bf16", seed=41)
+    nB = wl.blocks
+    rows = wl.heads * nB
+    rng = np.random.default_rng(6)
+    mask = rng.random((rows, nB)) < 0.5
+    mask[:, 4] = False                               # key block 4: unused
+    mask[[0, nB + 7]] = False                        # empty rows
+    mask[1, :] = np.arange(nB) != 4
+    q, k, v, qd, kd, vd, out, lse, g, shape, orp, oci = _backward_case(wl, "A", mask=mask, seed=43)
+    gd = g.cuda()
+    rpd = torch.as_tensor(orp.astype(np.int32)).cuda()
+    cid = torch.as_tensor(oci).cuda()
+    dq, dk, dv = B.sparse_attn_backward(shape, qd, kd, vd, out, lse, gd, rpd, cid)
+    rq, rk, rv = oracle.attention_backward(q, k, v, g, orp, oci)
+    assert max(_rel_err(dq, rq), _rel_err(dk, rk)) <= P.BWD_TOL_DQK and _rel_err(dv, rv) <= P.BWD_TOL_DV
+    dqh = dq.float().cpu().reshape(rows, 64, -1)
+    assert torch.all(dqh[[0, nB + 7]] == 0)
+    dkh, dvh = dk.float().cpu().reshape(rows, 64, -1), dv.float().cpu().reshape(rows, 64, -1)
+    assert torch.all(dkh[[4, nB + 4]] == 0) and torch.all(dvh[[4, nB + 4]] == 0)
+    rp2, ci2 = [0], []
+    for r in range(rows):
+        seg = oci[orp[r]:orp[r + 1]].tolist()
+        ci2 += [-3] + seg[:1] + seg + [nB + 1] + seg[:1]
+        rp2.append(len(ci2))
+    rpd2 = torch.as_tensor(np.array(rp2, dtype=np.int32)).cuda()
+    cid2 = torch.as_tensor(np.array(ci2, dtype=np.int32)).cuda()
+    dq2, dk2, dv2 = B.sparse_attn_backward(shape, qd, kd, vd, out, lse, gd, rpd2, cid2)
+    torch.cuda.synchronize()
+    assert torch.equal(dq2, dq) and torch.equal(dk2, dk) and torch.equal(dv2, dv)
+
+
 def test_deterministic_and_no_nan():
     wl = small_workload("det", 3, 128, (3, 4, 5), "bf16", threshold=0.8, window=(1, 1, 1), seed=17)
     q, k, v, thr = make_inputs(wl, "A")
