@@ -301,7 +301,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         } else if (mine0) {
             tile_probs(sc, c, mc, l_run, pf);
         }
+        // P V is MFMA work only: the wave runs it at raised priority, so that the
+        // SIMD's other wave fills the matrix unit's gaps with its softmax instead of
+        // delaying these MFMAs
+        __builtin_amdgcn_s_setprio(1);
         if (mine0) tile_pv<D>(Vs + BJ * TILEB, pf, lane, acc_o);
+        __builtin_amdgcn_s_setprio(0);
         col0 = col1;
         mine0 = mine1;
         col1 = col2;
