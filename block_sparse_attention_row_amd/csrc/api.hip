@@ -63,7 +63,8 @@ int64_t n_pairs(const Dims &d) { return d.B * d.H * ((d.nB + 1) / 2); }
 int64_t max_slots(const Dims &d) { return n_pairs(d) * 4 < kMaxSlots ? n_pairs(d) * 4 : kMaxSlots; }
 
 struct Layout {
-    int64_t thr, qbar, kbar, bits, counts, groups;                       // selection
+    int64_t thr, kbar, status, ticket;                                   // selection
+    int64_t bits, counts, groups;                                        // external masks
     int64_t items, plan_counts, pair_flag, merge, part_o, part_lse;      // attention row splitting
     int64_t col_ptr, lse2, dn;                                           // backward
     int64_t total;
@@ -74,10 +75,12 @@ Layout layout(const Dims &d) {
     int64_t off = 0;
     l.thr = off;
     off = align_up(off + 4 * d.H, kAlign);
-    l.qbar = off;
-    off = align_up(off + 4 * d.B * d.H * d.nB * d.D, kAlign);
     l.kbar = off;
     off = align_up(off + 4 * d.B * d.H * d.nB * d.D, kAlign);
+    l.status = off;
+    off = align_up(off + 8 * n_groups(d), kAlign);
+    l.ticket = off;
+    off = align_up(off + 16, kAlign);
     l.bits = off;
     off = align_up(off + 8 * d.rows * d.nW, kAlign);
     l.counts = off;
@@ -170,11 +173,9 @@ int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_sel
     hipStream_t s = (hipStream_t)stream;
     char *ws = (char *)workspace;
     float *thr = (float *)(ws + L.thr);
-    __bf16 *qbar = (__bf16 *)(ws + L.qbar);
     __bf16 *kbar = (__bf16 *)(ws + L.kbar);
-    uint64_t *bits = (uint64_t *)(ws + L.bits);
-    int32_t *counts = (int32_t *)(ws + L.counts);
-    int32_t *groups = (int32_t *)(ws + L.groups);
+    uint64_t *status = (uint64_t *)(ws + L.status);
+    uint32_t *ticket = (uint32_t *)(ws + L.ticket);
 
     // thresholds: the first ThrChunk::kMax travel with the pooling kernel, any others
     // through small fill kernels
@@ -183,6 +184,9 @@ int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_sel
     for (int i = 0; i < side.n_thr; ++i)
         side.thr.v[i] = params->head_thresholds ? params->head_thresholds[i] : params->threshold;
     side.thr_dst = thr;
+    side.status = status;
+    side.n_status = n_groups(d);
+    side.ticket = ticket;
     for (int64_t h0 = ThrChunk::kMax; h0 < d.H; h0 += ThrChunk::kMax) {
         float tmp[ThrChunk::kMax];
         const int n = (int)((d.H - h0) < ThrChunk::kMax ? (d.H - h0) : ThrChunk::kMax);
@@ -190,16 +194,17 @@ int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_sel
             tmp[i] = params->head_thresholds ? params->head_thresholds[h0 + i] : params->threshold;
         if (launch_fill_thresholds(tmp, n, thr + h0, s)) return SPARSE_ATTN_HIP_ERROR;
     }
-    if (launch_pool(q, k, qbar, kbar, d.B * d.H * d.nB, shape->dtype, (int)d.D, side, s))
-        return SPARSE_ATTN_HIP_ERROR;
+    if (launch_pool_keys(k, kbar, d.B * d.H * d.nB, shape->dtype, (int)d.D, side, s)) return SPARSE_ATTN_HIP_ERROR;
 
     SelectArgs a;
-    a.qbar = qbar;
+    a.q = q;
     a.kbar = kbar;
     a.thr = thr;
-    a.bits = bits;
-    a.counts = counts;
-    a.group_sums = groups;
+    a.status = status;
+    a.ticket = ticket;
+    a.row_ptr = row_ptr;
+    a.col_idx = col_idx;
+    a.rows = d.rows;
     a.groups_per_head = (int32_t)groups_per_head(d);
     a.n_groups = n_groups(d);
     a.H = (int32_t)d.H;
@@ -212,8 +217,8 @@ int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_sel
     a.wh = params->win_h;
     a.ww = params->win_w;
     a.scale_log2 = effective_scale(shape) * kLog2e;
-    if (launch_select(a, (int)d.D, s)) return SPARSE_ATTN_HIP_ERROR;
-    return emit_csr(d, bits, counts, groups, row_ptr, col_idx, s);
+    if (launch_select(a, (int)d.D, shape->dtype, s)) return SPARSE_ATTN_HIP_ERROR;
+    return SPARSE_ATTN_OK;
 }
 
 int32_t sparse_attn_forward(const sparse_attn_shape *shape, const void *q, const void *k, const void *v,

@@ -39,6 +39,30 @@ template <typename T> struct DType;
 template <> struct DType<float> { static constexpr int code = 0; };
 template <> struct DType<__bf16> { static constexpr int code = 1; };
 
+// Integer wave sums and scans through DPP lane moves.
+template <int CTRL> __device__ __forceinline__ int dppi(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int wave_sum_i(int s) {
+    s += dppi<0xB1>(s);
+    s += dppi<0x4E>(s);
+    s += dppi<0x141>(s);
+    s += dppi<0x140>(s);
+    return __builtin_amdgcn_readlane(s, 0) + __builtin_amdgcn_readlane(s, 16) + __builtin_amdgcn_readlane(s, 32) +
+           __builtin_amdgcn_readlane(s, 48);
+}
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan_i(int v, int lane) {
+    v += dppi<0x111>(v);
+    v += dppi<0x112>(v);
+    v += dppi<0x114>(v);
+    v += dppi<0x118>(v);
+    const int q0 = __builtin_amdgcn_readlane(v, 15), q1 = __builtin_amdgcn_readlane(v, 31),
+              q2 = __builtin_amdgcn_readlane(v, 47);
+    const int row16 = lane >> 4;
+    return v + (row16 >= 1 ? q0 : 0) + (row16 >= 2 ? q1 : 0) + (row16 >= 3 ? q2 : 0);
+}
+
 // Wave-wide reductions over 64 lanes (results in every lane).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -49,18 +49,6 @@ __global__ __launch_bounds__(1024) void mask_bits_kernel(const uint8_t *__restri
 // totals before the group of its first row once, each wave adds what lies between
 // that and its row, writes row_ptr and expands its row's bitmask into ascending
 // col_idx.
-template <int CTRL> __device__ __forceinline__ int dppi(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-__device__ __forceinline__ int wave_sum_i(int s) {
-    s += dppi<0xB1>(s);
-    s += dppi<0x4E>(s);
-    s += dppi<0x141>(s);
-    s += dppi<0x140>(s);
-    return __builtin_amdgcn_readlane(s, 0) + __builtin_amdgcn_readlane(s, 16) + __builtin_amdgcn_readlane(s, 32) +
-           __builtin_amdgcn_readlane(s, 48);
-}
-
 __global__ __launch_bounds__(256) void emit_kernel(const uint64_t *__restrict__ bits,
                                                    const int32_t *__restrict__ counts,
                                                    const int32_t *__restrict__ group_sums, int64_t rows, int32_t nB,
@@ -94,17 +82,7 @@ __global__ __launch_bounds__(256) void emit_kernel(const uint64_t *__restrict__ 
     for (int w0 = 0; w0 < nW; w0 += 64) {
         const uint64_t mine_w = (w0 + lane < nW) ? b[w0 + lane] : 0ull;
         const int cnt = __popcll(mine_w);
-        int incl = cnt;
-        incl += dppi<0x111>(incl);
-        incl += dppi<0x112>(incl);
-        incl += dppi<0x114>(incl);
-        incl += dppi<0x118>(incl);
-        {
-            const int q0 = __builtin_amdgcn_readlane(incl, 15), q1 = __builtin_amdgcn_readlane(incl, 31),
-                      q2 = __builtin_amdgcn_readlane(incl, 47);
-            const int row16 = lane >> 4;
-            incl += (row16 >= 1 ? q0 : 0) + (row16 >= 2 ? q1 : 0) + (row16 >= 3 ? q2 : 0);
-        }
+        const int incl = wave_incl_scan_i(cnt, lane);
         const int excl = incl - cnt;
         const int nw = min(64, nW - w0);
         for (int e = 0; e < nw; ++e) {

@@ -21,18 +21,30 @@ struct PoolSide {
     ThrChunk thr;             // first thresholds, by value
     float *thr_dst;           // [H] (workspace)
     int32_t n_thr;            // thresholds in `thr` (<= ThrChunk::kMax)
+    uint64_t *status;         // look-back words of the selection that follows, zeroed here
+    int64_t n_status;
+    uint32_t *ticket;         // its ticket counter, zeroed here
 };
+
+// Look-back word of a row group: 0 until published, then kStatAgg | the group's
+// kept-block total, finally kStatPre | the inclusive prefix of the totals up to and
+// including the group.  Waits on these words give up after kSpinCap polls (they end
+// in microseconds when every earlier group runs, which the ticket order ensures).
+constexpr uint64_t kStatAgg = 1ull << 62, kStatPre = 2ull << 62, kStatFlags = 3ull << 62;
+constexpr uint32_t kSpinCap = 1u << 22;
 
 // Longest row the selection holds in registers (64 words of 64 key blocks).
 constexpr int kSelectMaxBlocks = 4096;
 
 struct SelectArgs {
-    const __bf16 *qbar;       // [BH*nB][2][D] block means as bf16 pairs (hi, then lo)
-    const __bf16 *kbar;
+    const void *q;            // [BH*N][D] queries in the input dtype (tile-major)
+    const __bf16 *kbar;       // [BH*nB][2][D] key block means as bf16 pairs (hi, then lo)
     const float *thr;         // [H] thresholds (device)
-    uint64_t *bits;           // [BH*nB][nBp/64] kept-block bitmask
-    int32_t *counts;          // [BH*nB] kept blocks per row
-    int32_t *group_sums;      // [n_groups] kept blocks per row group
+    uint64_t *status;         // [n_groups] look-back words (zeroed by the pooling kernel)
+    uint32_t *ticket;         // group ticket counter (zeroed by the pooling kernel)
+    int32_t *row_ptr;         // [rows + 1]
+    int32_t *col_idx;         // [nnz]
+    int64_t rows;             // BH * nB
     int64_t n_groups;         // workgroups = BH * groups_per_head
     int32_t groups_per_head;  // ceil(nB / 16)
     int32_t H, nB, nBp;       // heads, blocks, nB rounded up to 64
@@ -87,10 +99,10 @@ struct ReorderArgs {
 };
 int launch_reorder(const void *src, void *dst, const ReorderArgs &a, int64_t tiles, hipStream_t s);
 
-int launch_pool(const void *q, const void *k, __bf16 *qbar, __bf16 *kbar, int64_t nblocks, int dtype, int d,
-                const PoolSide &side, hipStream_t s);
+int launch_pool_keys(const void *k, __bf16 *kbar, int64_t nblocks, int dtype, int d, const PoolSide &side,
+                     hipStream_t s);
 int launch_fill_thresholds(const float *host_thr, int n, float *dst, hipStream_t s);
-int launch_select(const SelectArgs &a, int d, hipStream_t s);
+int launch_select(const SelectArgs &a, int d, int dtype, hipStream_t s);
 int launch_mask_bits(const uint8_t *mask, int64_t bh, int32_t nB, int32_t nW, uint64_t *bits, int32_t *counts,
                      int32_t *group_sums, hipStream_t s);
 int launch_full_csr(int64_t rows, int32_t nB, int32_t *row_ptr, int32_t *col_idx, hipStream_t s);

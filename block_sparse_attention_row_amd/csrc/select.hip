@@ -1,87 +1,97 @@
-// Block pooling and dynamic block selection (gfx950).
+// Block pooling, dynamic block selection and the CSR of the kept blocks (gfx950).
 //
 // Follows the NABLA summary page ("NABLA: Neighborhood Adaptive Block-Level
 // Attention", section "Methodologie : NABLA"):
-//   pool_kernel   -- "Sous-echantillonnage": mean of each 64-token block of Q and K;
-//   select_kernel -- "Attention Reduite": softmax over the pooled scores of a
-//                    row; "Seuil CDF": keep blocks in descending probability
-//                    while the mass before them is below thr; "Integration
-//                    Hybride avec STA": OR with a static box window.
-// The selection result of a row is a bitmask over key blocks plus its
-// popcount; csr.hip turns those into row_ptr / col_idx.
+//   pool_kernel        -- "Sous-echantillonnage": mean of each 64-token block of K;
+//   select_emit_kernel -- the same mean for the workgroup's own query blocks, then
+//                         "Attention Reduite": softmax over the pooled scores of a
+//                         row; "Seuil CDF": keep blocks in descending probability
+//                         while the mass before them is below thr; "Integration
+//                         Hybride avec STA": OR with a static box window; and the
+//                         "Expansion" into row_ptr / col_idx, whose offsets come
+//                         from a look-back over the groups' totals.
 #include "common.h"
 #include "kernels.h"
 
 namespace sattn {
 
 // ---------------------------------------------------------------------------
-// Pooling.  One wave per (tensor, block): the block is 64*D contiguous
-// elements; each lane streams 16-byte chunks, accumulates in fp32, and the
-// lanes that share a column slice are combined with xor-shuffles.  The fp32
-// mean x is stored as a pair of bf16 values, hi = bf16(x) and lo = bf16(x - hi)
-// (row layout [hi: D][lo: D]), the operand form of the split-bf16 score products.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ q, const T *__restrict__ k,
-                                                   __bf16 *__restrict__ qbar, __bf16 *__restrict__ kbar,
-                                                   int64_t nblocks, PoolSide side) {
-    // side job for the selection that follows: the first ThrChunk::kMax thresholds
-    if (blockIdx.x == 0 && (int)threadIdx.x < side.n_thr) side.thr_dst[threadIdx.x] = side.thr.v[threadIdx.x];
-    constexpr int VEC = 16 / sizeof(T);
-    constexpr int LPR = D / VEC;               // lanes covering one token row
-    constexpr int RPW = kWave / LPR;           // token rows per wave-wide load
-    constexpr int ITER = kTokensPerBlock / RPW;
-    constexpr int BATCH = ITER < 16 ? ITER : 16;
-    const int lane = threadIdx.x & 63;
-    const int64_t w = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
-    if (w >= 2 * nblocks) return;
-    const int64_t blk = w >> 1;
-    const T *src = (w & 1) ? k : q;
-    __bf16 *dst = (w & 1) ? kbar : qbar;
-    const int col = (lane % LPR) * VEC, row0 = lane / LPR;
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(src + (blk * kTokensPerBlock + row0) * D + col);
-    constexpr int STEP = RPW * D * (int)sizeof(T) / 16;   // u32x4 units between iterations
-
-    float acc[VEC];
+// Pooling of one 64-token block by one wave: the block is 64*D contiguous elements;
+// each lane streams 16-byte chunks (BATCH loads in flight), accumulates in fp32, and
+// the lanes that share a column slice are combined with xor-shuffles.  Lanes
+// 0 .. LPR-1 end up with the VEC means of columns col .. col+VEC-1.
+template <typename T, int D, int BATCH> struct BlockPool {
+    static constexpr int VEC = 16 / sizeof(T);
+    static constexpr int LPR = D / VEC;               // lanes covering one token row
+    static constexpr int RPW = kWave / LPR;           // token rows per wave-wide load
+    static constexpr int ITER = kTokensPerBlock / RPW;
+    static constexpr int B = ITER < BATCH ? ITER : BATCH;
+    static __device__ __forceinline__ int col(int lane) { return (lane % LPR) * VEC; }
+    static __device__ __forceinline__ void mean(const T *blk, int lane, float (&x)[VEC]) {
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(blk + (lane / LPR) * D + col(lane));
+        constexpr int STEP = RPW * D * (int)sizeof(T) / 16;   // u32x4 units between iterations
+        float acc[VEC];
 #pragma unroll
-    for (int c = 0; c < VEC; ++c) acc[c] = 0.f;
+        for (int c = 0; c < VEC; ++c) acc[c] = 0.f;
 #pragma unroll
-    for (int b0 = 0; b0 < ITER; b0 += BATCH) {
-        u32x4 buf[BATCH];
+        for (int b0 = 0; b0 < ITER; b0 += B) {
+            u32x4 buf[B];
 #pragma unroll
-        for (int it = 0; it < BATCH; ++it) buf[it] = p[(b0 + it) * STEP];
+            for (int it = 0; it < B; ++it) buf[it] = p[(b0 + it) * STEP];
 #pragma unroll
-        for (int it = 0; it < BATCH; ++it) {
+            for (int it = 0; it < B; ++it) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                if constexpr (sizeof(T) == 2) {
-                    acc[2 * c] += bf16_lo(buf[it][c]);
-                    acc[2 * c + 1] += bf16_hi(buf[it][c]);
-                } else {
-                    acc[c] += __uint_as_float(buf[it][c]);
+                for (int c = 0; c < 4; ++c) {
+                    if constexpr (sizeof(T) == 2) {
+                        acc[2 * c] += bf16_lo(buf[it][c]);
+                        acc[2 * c + 1] += bf16_hi(buf[it][c]);
+                    } else {
+                        acc[c] += __uint_as_float(buf[it][c]);
+                    }
                 }
             }
         }
-    }
 #pragma unroll
-    for (int o = LPR; o < kWave; o <<= 1) {
+        for (int o = LPR; o < kWave; o <<= 1) {
 #pragma unroll
-        for (int c = 0; c < VEC; ++c) acc[c] += __shfl_xor(acc[c], o, 64);
-    }
-    if (lane < LPR) {
-        typedef __attribute__((ext_vector_type(VEC))) float fv;
-        typedef __attribute__((ext_vector_type(VEC))) __bf16 bv;
-        fv x;
+            for (int c = 0; c < VEC; ++c) acc[c] += __shfl_xor(acc[c], o, 64);
+        }
 #pragma unroll
         for (int c = 0; c < VEC; ++c) x[c] = acc[c] * (1.f / 64.f);
-        const bv hi = __builtin_convertvector(x, bv);
-        fv r;
-#pragma unroll
-        for (int c = 0; c < VEC; ++c) r[c] = x[c] - (float)hi[c];
-        const bv lo = __builtin_convertvector(r, bv);
-        __bf16 *o = dst + blk * (2 * D) + col;
-        *reinterpret_cast<bv *>(o) = hi;
-        *reinterpret_cast<bv *>(o + D) = lo;
     }
+    // the fp32 means as bf16 pairs, hi = bf16(x) and lo = bf16(x - hi): the operand
+    // form of the split-bf16 score products ([hi: D][lo: D] per block)
+    static __device__ __forceinline__ void store_split(const float (&x)[VEC], __bf16 *row, int lane) {
+        typedef __attribute__((ext_vector_type(VEC))) float fv;
+        typedef __attribute__((ext_vector_type(VEC))) __bf16 bv;
+        fv xv, r;
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) xv[c] = x[c];
+        const bv hi = __builtin_convertvector(xv, bv);
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) r[c] = xv[c] - (float)hi[c];
+        const bv lo = __builtin_convertvector(r, bv);
+        *reinterpret_cast<bv *>(row + col(lane)) = hi;
+        *reinterpret_cast<bv *>(row + D + col(lane)) = lo;
+    }
+};
+
+// Key block means, one wave per block.  Side jobs for the selection that follows:
+// the first ThrChunk::kMax thresholds, and zeroing its ticket and look-back words.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ k, __bf16 *__restrict__ kbar,
+                                                   int64_t nblocks, PoolSide side) {
+    const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (blockIdx.x == 0 && (int)threadIdx.x < side.n_thr) side.thr_dst[threadIdx.x] = side.thr.v[threadIdx.x];
+    for (int64_t i = gt; i < side.n_status; i += (int64_t)gridDim.x * blockDim.x) side.status[i] = 0;
+    if (gt == 0) *side.ticket = 0u;
+    using P = BlockPool<T, D, 16>;
+    const int lane = threadIdx.x & 63;
+    const int64_t blk = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
+    if (blk >= nblocks) return;
+    float x[P::VEC];
+    P::mean(k + blk * kTokensPerBlock * D, lane, x);
+    if (lane < P::LPR) P::store_split(x, kbar + blk * (2 * D), lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -109,14 +119,13 @@ __device__ __forceinline__ void wave_lds_sync() {
 // LDS stage; after one barrier every wave reads its own row's 256 scores back.
 //
 // Cut ("Seuil CDF"), per wave on its register row: e_j = 2^(s_j - max) and their sum
-// Z; then an exact mass-weighted radix select over the fp32 bit patterns of the e_j
-// (positive floats order like their bit patterns) finds the crossing value v* and
-// the mass M strictly above it; the digits start at the highest bit where the row's
-// e_j differ, 8 bits per pass, with the pass histogram in LDS.  A block is kept when
-// e_j > v*, or e_j == v* and M plus the mass of the equal blocks with lower index is
-// below thr * Z: the CDF rule with ties going to the lower index, without
-// normalising the row.  Then the optional box window ("Integration Hybride avec
-// STA"), the row's bitmask, its count and the count of its 64-row chunk.
+// Z; a pivot search over the fp32 bit patterns of the e_j (positive floats order
+// like their bit patterns) narrows the crossing value v* and the mass M strictly
+// above it, and the last <= 64 candidates are sorted across the lanes.  A block is
+// kept when e_j > v*, or e_j == v* and M plus the mass of the equal blocks with
+// lower index is below thr * Z: the CDF rule with ties going to the lower index,
+// without normalising the row.  Then the optional box window ("Integration Hybride
+// avec STA"), the row's bitmask and its count.
 constexpr int kSelRows = kGroupRows;    // rows (and waves) per workgroup
 constexpr int kSelChunk = 256;          // key blocks per score chunk (16 waves x 16)
 constexpr int kStageStride = kSelChunk + 4;   // padded: the 16x16 tile stores are conflict-free
@@ -127,15 +136,13 @@ template <int D> constexpr size_t select_lds_bytes() {
            (size_t)kSelRows * 256 * 4;
 }
 
-// The cut of row i of head bh (threshold thr), run by one wave on its register row s
-// (scaled scores, -inf for padding keys); writes the row's bitmask and count, and
-// its count to `out`.
+// The cut of row i (threshold thr), run by one wave on its register row s (scaled
+// scores, -inf for padding keys).  Returns the row's bitmask (lane c holds the word
+// of key blocks 64c .. 64c+63) and its count.
 template <int NE>
-__device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], float *hist_all, int64_t bh, int i,
-                                           float thr, int lane, int32_t &out) {
+__device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], float *hist_all, int i, float thr,
+                                           int lane, uint64_t &word, int32_t &count_out) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t row = bh * a.nB + i;
-    const int nvc = a.nBp >> 6;
     const bool keep_all = !(thr < 1.f);
     uint32_t *list = reinterpret_cast<uint32_t *>(hist_all + wave * 256);   // up to 64 keys of the bracket
 
@@ -274,42 +281,76 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
             whi = (uint32_t)(m >> 32);
         }
     }
-    if (lane < nvc) a.bits[row * (int64_t)nvc + lane] = ((uint64_t)whi << 32) | wlo;
-    if (lane == 0) {
-        a.counts[row] = (int32_t)count;
-        out = (int32_t)count;
+    word = ((uint64_t)whi << 32) | wlo;
+    count_out = (int32_t)count;
+}
+
+// Offset of group g in col_idx: decoupled look-back over the groups' look-back words,
+// run by one wave.  The group's total is published first; then the words of the 64
+// groups before the current position are read at once and summed up to the nearest
+// one that carries a prefix; while one of those has published nothing yet the wave
+// polls again.  Every group before g holds an earlier ticket, so it is running or
+// done and publishes its total without waiting on anyone; the polls end.
+__device__ __forceinline__ int64_t group_lookback(uint64_t *status, int64_t g, int64_t total, int lane) {
+    if (lane == 0)
+        __hip_atomic_store(status + g, (g == 0 ? kStatPre : kStatAgg) | (uint64_t)total, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    int64_t base = 0, p = g - 1;
+    uint32_t polls = 0;
+    while (p >= 0) {
+        const int64_t idx = p - lane;
+        const uint64_t w = idx >= 0 ? __hip_atomic_load(status + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                    : kStatPre;
+        const uint64_t f = w & kStatFlags;
+        const uint64_t pre = __ballot(f == kStatPre);
+        const int first = pre ? __builtin_ctzll(pre) : 64;       // nearest group carrying a prefix
+        const uint64_t upto = first >= 63 ? ~0ull : ((2ull << first) - 1);
+        if ((__ballot(f == 0) & upto) && ++polls < kSpinCap) {
+            __builtin_amdgcn_s_sleep(1);
+            continue;
+        }
+        const int v = lane <= first && f != 0 ? (int)(w & ~kStatFlags) : 0;
+        base += wave_sum_i(v);
+        if (first < 64) break;
+        p -= 64;
     }
+    if (lane == 0)
+        __hip_atomic_store(status + g, kStatPre | (uint64_t)(base + total), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return base;
 }
 
 // NE = 4 * ceil(nB / 256): the register row length in 64-key words (chunks of 256 keys).
-template <int D, int NE>
-__global__ __launch_bounds__(1024) void select_kernel(SelectArgs a) {
+// Workgroup = row group taken by ticket (groups start in order).  Wave w pools query
+// block i0 + w into LDS while the first key chunk loads, the waves form the scores
+// chunk by chunk, each cuts its row, wave 0 finds the group's offset by look-back,
+// and each wave writes its row's row_ptr entry and kept columns.
+template <typename T, int D, int NE>
+__global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
     static_assert(NE % 4 == 0 && NE <= 64, "NE: register row length in 64-key words");
     constexpr int KB = D / 32;                     // k-blocks of one 16x16x32 product
     constexpr int NCH = NE / 4;                    // score chunks
     // registers for the next chunk's operands where they fit; at NE <= 8 two
     // workgroups share a CU instead
     constexpr bool kPrefetch = NE > 8 && NE <= 32;
+    using QP = BlockPool<T, D, 8>;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     __bf16 *qf = reinterpret_cast<__bf16 *>(smem_raw);                              // [16][2D+8]
     float *stage = reinterpret_cast<float *>(smem_raw + (size_t)kSelRows * qf_stride<D>() * 2);  // [2][16][260]
     float *hist_all = stage + 2 * kSelRows * kStageStride;                          // [16][256]
+    __shared__ uint32_t s_ticket;
+    __shared__ int32_t wave_count[kSelRows];
+    __shared__ int64_t s_base;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t g = (uint32_t)xcd_remap(blockIdx.x, a.n_groups);
+    if (threadIdx.x == 0) s_ticket = atomicAdd(a.ticket, 1u);
+    __syncthreads();
+    const uint32_t g = __builtin_amdgcn_readfirstlane(s_ticket);
     const uint32_t bh = g / (uint32_t)a.groups_per_head;
     const int i0 = (int)(g - bh * (uint32_t)a.groups_per_head) * kSelRows;
     const int nrows = min(kSelRows, a.nB - i0);
-    const __bf16 *qs = a.qbar + ((int64_t)bh * a.nB + i0) * (2 * D);
     const __bf16 *ks = a.kbar + ((int64_t)bh * a.nB) * (2 * D);
     const float thr = a.thr[bh % (uint32_t)a.H];
-
-    // ---- the group's pooled queries (hi | lo) and chunk 0's keys, loads issued together
-    constexpr int PER_ROW = 2 * D / 4;             // 8-byte pieces per query row
-    const int qr = threadIdx.x / PER_ROW, qc = threadIdx.x % PER_ROW;
-    uint2 qv = {0u, 0u};
-    if (qr < nrows) qv = reinterpret_cast<const uint2 *>(qs + (int64_t)qr * 2 * D)[qc];
 
     const int ii = lane & 15, kq = lane >> 4;
     float s[NE];
@@ -324,8 +365,19 @@ __global__ __launch_bounds__(1024) void select_kernel(SelectArgs a) {
             kl[slot][kb] = *reinterpret_cast<const bf16x8 *>(kr + D + 32 * kb);
         }
     };
+    // ---- the group's pooled queries (hi | lo), one query block per wave
+    {
+        __bf16 *qrow = qf + wave * qf_stride<D>();
+        if (wave < nrows) {
+            float x[QP::VEC];
+            const T *qb = reinterpret_cast<const T *>(a.q) + (((int64_t)bh * a.nB + i0 + wave) * kTokensPerBlock) * D;
+            QP::mean(qb, lane, x);
+            if (lane < QP::LPR) QP::store_split(x, qrow, lane);
+        } else if (lane < 2 * D / 8) {
+            reinterpret_cast<uint4 *>(qrow)[lane] = uint4{0u, 0u, 0u, 0u};
+        }
+    }
     load_k(0, 0);
-    if (qr < kSelRows) reinterpret_cast<uint2 *>(qf + qr * qf_stride<D>())[qc] = qv;
     __syncthreads();
 
     // ---- scores, chunk by chunk, into the register row
@@ -355,31 +407,54 @@ __global__ __launch_bounds__(1024) void select_kernel(SelectArgs a) {
             s[4 * cc + t] = kSelChunk * cc + 64 * t + lane < a.nB ? v : -INFINITY;   // padding keys
         }
     }
-    __shared__ int32_t wave_count[kSelRows];
-    if (wave < nrows) select_cut<NE>(a, s, hist_all, bh, i0 + wave, thr, lane, wave_count[wave]);
-    else if (lane == 0) wave_count[wave] = 0;
+    uint64_t word = 0;
+    int32_t count = 0;
+    if (wave < nrows) select_cut<NE>(a, s, hist_all, i0 + wave, thr, lane, word, count);
+    if (lane == 0) wave_count[wave] = count;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int32_t t = 0;
-#pragma unroll
-        for (int w = 0; w < kSelRows; ++w) t += wave_count[w];
-        a.group_sums[g] = t;
+
+    // ---- offsets: the group's by look-back, then the rows' within the group
+    if (wave == 0) {
+        const int32_t total = wave_sum_i(lane < kSelRows ? wave_count[lane] : 0);
+        const int64_t base = group_lookback(a.status, g, total, lane);
+        if (lane == 0) s_base = base;
+    }
+    __syncthreads();
+    if (wave >= nrows) return;
+    int32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += wave_count[w];
+    const int64_t row = (int64_t)bh * a.nB + i0 + wave;
+    int32_t pos = (int32_t)s_base + before;
+    if (lane == 0) {
+        a.row_ptr[row] = pos;
+        if (row == a.rows - 1) a.row_ptr[a.rows] = pos + count;
+    }
+    // ---- kept columns, ascending: word e of the row sits in lane e
+    const int nvc = a.nBp >> 6;
+    const int cnt = __popcll(word);
+    const int excl = wave_incl_scan_i(cnt, lane) - cnt;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int e = 0; e < nvc; ++e) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)word, e);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(word >> 32), e);
+        const uint64_t m = ((uint64_t)hi << 32) | lo;
+        const int off = __builtin_amdgcn_readlane(excl, e);
+        if ((m >> lane) & 1ull) a.col_idx[pos + off + __popcll(m & lt_mask)] = 64 * e + lane;
     }
 }
 
 // ---------------------------------------------------------------------------
-int launch_pool(const void *q, const void *k, __bf16 *qbar, __bf16 *kbar, int64_t nblocks, int dtype, int d,
-                const PoolSide &side, hipStream_t s) {
-    const int64_t waves = 2 * nblocks;
-    const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+int launch_pool_keys(const void *k, __bf16 *kbar, int64_t nblocks, int dtype, int d, const PoolSide &side,
+                     hipStream_t s) {
+    const dim3 grid((unsigned)((nblocks + 3) / 4)), block(256);
     if (dtype == 1 && d == 128)
-        pool_kernel<__bf16, 128><<<grid, block, 0, s>>>((const __bf16 *)q, (const __bf16 *)k, qbar, kbar, nblocks, side);
+        pool_kernel<__bf16, 128><<<grid, block, 0, s>>>((const __bf16 *)k, kbar, nblocks, side);
     else if (dtype == 1 && d == 64)
-        pool_kernel<__bf16, 64><<<grid, block, 0, s>>>((const __bf16 *)q, (const __bf16 *)k, qbar, kbar, nblocks, side);
+        pool_kernel<__bf16, 64><<<grid, block, 0, s>>>((const __bf16 *)k, kbar, nblocks, side);
     else if (dtype == 0 && d == 128)
-        pool_kernel<float, 128><<<grid, block, 0, s>>>((const float *)q, (const float *)k, qbar, kbar, nblocks, side);
+        pool_kernel<float, 128><<<grid, block, 0, s>>>((const float *)k, kbar, nblocks, side);
     else
-        pool_kernel<float, 64><<<grid, block, 0, s>>>((const float *)q, (const float *)k, qbar, kbar, nblocks, side);
+        pool_kernel<float, 64><<<grid, block, 0, s>>>((const float *)k, kbar, nblocks, side);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -394,23 +469,28 @@ int launch_fill_thresholds(const float *host_thr, int n, float *dst, hipStream_t
     return 0;
 }
 
-template <int D, int NCH> static void launch_select_nch(const SelectArgs &a, int nch, hipStream_t s) {
+template <typename T, int D, int NCH> static void launch_select_nch(const SelectArgs &a, int nch, hipStream_t s) {
     if constexpr (NCH <= kSelectMaxBlocks / kSelChunk) {
         if (nch == NCH) {
-            select_kernel<D, 4 * NCH><<<dim3((unsigned)a.n_groups), dim3(64 * kSelRows), select_lds_bytes<D>(), s>>>(a);
+            select_emit_kernel<T, D, 4 * NCH>
+                <<<dim3((unsigned)a.n_groups), dim3(64 * kSelRows), select_lds_bytes<D>(), s>>>(a);
             return;
         }
-        launch_select_nch<D, NCH + 1>(a, nch, s);
+        launch_select_nch<T, D, NCH + 1>(a, nch, s);
     }
 }
 
-int launch_select(const SelectArgs &a, int d, hipStream_t s) {
+int launch_select(const SelectArgs &a, int d, int dtype, hipStream_t s) {
     if (a.nBp > kSelectMaxBlocks) return -1;
     const int nch = (a.nB + kSelChunk - 1) / kSelChunk;
-    if (d == 128)
-        launch_select_nch<128, 1>(a, nch, s);
+    if (dtype == 1 && d == 128)
+        launch_select_nch<__bf16, 128, 1>(a, nch, s);
+    else if (dtype == 1 && d == 64)
+        launch_select_nch<__bf16, 64, 1>(a, nch, s);
+    else if (dtype == 0 && d == 128)
+        launch_select_nch<float, 128, 1>(a, nch, s);
     else
-        launch_select_nch<64, 1>(a, nch, s);
+        launch_select_nch<float, 64, 1>(a, nch, s);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
