@@ -52,7 +52,7 @@ def _load():
         D = ctypes.c_double
         lib.oracle_pool.argtypes = [P, I, I, I, P]
         lib.oracle_select_rows.argtypes = [P, P, I, I, I, P, I, D, P, I, I, I, I, I, I, P, P, P]
-        lib.oracle_attention_rows.argtypes = [P, P, P, I, I, I, P, P, P, I, D, P, P, P]
+        lib.oracle_attention_rows.argtypes = [P, P, P, I, I, I, P, P, P, P, I, D, P, P, P]
         lib.oracle_attention_backward.argtypes = [P, P, P, P, P, I, I, I, I, P, P, D, P, P, P]
         for f in (lib.oracle_pool, lib.oracle_select_rows, lib.oracle_attention_rows, lib.oracle_attention_backward):
             f.restype = None
@@ -202,16 +202,20 @@ def select(q, k, heads: int, block_grid, thresholds, window=(-1, -1, -1), scale=
 
 
 def attention_rows(q, k, v, row_ptr, col_idx, rows, scale: Optional[float] = None,
-                   tpb: int = TOKENS_PER_BLOCK, weights: bool = False):
+                   tpb: int = TOKENS_PER_BLOCK, weights: bool = False, bias=None):
     """Exact attention of every token of the listed query-block rows over its kept tiles.
 
     q, k, v: [B, H, N, d]; row_ptr/col_idx: CSR over rows r = bh * nB + i.
     Returns out [nrows, tpb, d] fp64 and lse [nrows, tpb] (natural log), plus
-    the per-token weight sums with ``weights``.
+    the per-token weight sums with ``weights``.  ``bias``: optional logit offset per
+    col_idx entry, added to the scaled logits of all keys of that block.
     """
     q, k, v = _f32(q), _f32(k), _f32(v)
     *lead, n, d = q.shape
     nB = n // tpb
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float64)
+    if b is not None and b.shape != np.shape(col_idx):
+        raise ValueError("bias needs one value per col_idx entry")
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     rp = np.ascontiguousarray(row_ptr, dtype=np.int64)
     ci = np.ascontiguousarray(col_idx, dtype=np.int32)
@@ -219,7 +223,7 @@ def attention_rows(q, k, v, row_ptr, col_idx, rows, scale: Optional[float] = Non
     lse = np.empty((len(rows), tpb), dtype=np.float64)
     ws = np.empty((len(rows), tpb), dtype=np.float64) if weights else None
     sc = default_scale(d) if scale is None else float(scale)
-    _load().oracle_attention_rows(_ptr(q), _ptr(k), _ptr(v), nB, tpb, d, _ptr(rp), _ptr(ci),
+    _load().oracle_attention_rows(_ptr(q), _ptr(k), _ptr(v), nB, tpb, d, _ptr(rp), _ptr(ci), _ptr(b),
                                   _ptr(rows), len(rows), sc, _ptr(out), _ptr(lse), _ptr(ws))
     if weights:
         return out, lse, ws

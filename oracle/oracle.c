@@ -151,10 +151,14 @@ void oracle_select_rows(const double *qbar, const double *kbar, int64_t H, int64
  * receives [tpb][d] fp64 and lse [tpb] the natural-log normaliser
  * log(sum_m exp(scale * q_n . k_m)).  An empty row yields O = 0, LSE = -inf.
  * w_sum (optional, [nrows][tpb]) receives the sum of the row's softmax weights.
+ * col_bias (optional, one value per CSR entry) is added to the logits of every
+ * key of that entry's block: the logit offset by which AB-Attention's sampling
+ * ("SIP", section "Les trois techniques d'AB-Attention" of the AB-Attention
+ * page) weighs a kept block by the inverse of its inclusion probability.
  */
 void oracle_attention_rows(const float *q, const float *k, const float *v, int64_t nB, int64_t tpb,
                            int64_t d, const int64_t *row_ptr, const int32_t *col_idx,
-                           const int64_t *rows, int64_t nrows, double scale,
+                           const double *col_bias, const int64_t *rows, int64_t nrows, double scale,
                            double *out, double *lse, double *w_sum)
 {
     const int64_t N = nB * tpb;
@@ -185,7 +189,7 @@ void oracle_attention_rows(const float *q, const float *k, const float *v, int64
                         const float *km = k + (bh * N + j * tpb + u) * d;
                         double a = 0.0;
                         for (int64_t c = 0; c < d; ++c) a += (double)qn[c] * (double)km[c];
-                        logit[m] = a * scale;
+                        logit[m] = a * scale + (col_bias ? col_bias[e] : 0.0);
                         if (logit[m] > mx) mx = logit[m];
                     }
                 }

@@ -464,3 +464,144 @@ def test_backward_with_stored_output():
                                               k[h].astype(np.float64), mask[h], scale, tpb)[0] for h in range(H)])
     expect = same[0][0] - scale * dD[..., None] * pk
     assert np.abs(got[0][0] - expect).max() <= 1e-9 * np.abs(expect).max()
+
+
+# ---------------------------------------------------------------- sampling with inclusion probabilities (SIP)
+
+def test_splitmix64_reference_values():
+    from oracle import sip
+    path = os.path.join(os.path.dirname(__file__), "golden", "splitmix64_seed0.txt")
+    rows = [ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#")]
+    for cnt, hexv in rows:
+        assert int(sip.splitmix64(0, int(cnt))) == int(hexv, 16)
+
+
+def test_uniforms_are_24_bit_and_indexed_by_row_and_block():
+    from oracle import sip
+    u = sip.uniforms(7, 3, 5)
+    assert u.shape == (3, 5) and np.all((u >= 0) & (u < 1))
+    assert np.all(u * 2 ** 24 == np.floor(u * 2 ** 24))
+    # row r, block j is output r * nB + j + 1 of the stream
+    z = int(sip.splitmix64(7, 2 * 5 + 3 + 1))
+    assert u[2, 3] == (z >> 40) * 2.0 ** -24
+    assert np.array_equal(sip.uniforms(7, 2, 5, row0=1), u[1:])
+
+
+def test_inclusion_probabilities_closed_forms():
+    from oracle import sip
+    # uniform scores: pi = k / n everywhere
+    assert np.allclose(sip.inclusion_probabilities(np.full(8, 1 / 8), 3.0), 3 / 8, rtol=0, atol=1e-15)
+    # two blocks, k = 1.5: a >= 2/3 caps the first block (pi = 1, 0.5); below, pi = 1.5 p
+    for a in (0.9, 2 / 3 + 1e-9, 0.6, 0.5):
+        pi = sip.inclusion_probabilities(np.array([a, 1 - a]), 1.5)[0]
+        want = np.array([1.0, 0.5]) if 1.5 * a >= 1 else 1.5 * np.array([a, 1 - a])
+        assert np.allclose(pi, want, rtol=0, atol=1e-12), (a, pi)
+    # p = (1/2, 1/4, 1/8, 1/8), k = 2: c = 2 caps block 0; then c = 1 / (1/2) = 2 for the
+    # rest -> (1, 1/2, 1/4, 1/4)
+    pi = sip.inclusion_probabilities(np.array([0.5, 0.25, 0.125, 0.125]), 2.0)[0]
+    assert np.array_equal(pi, np.array([1.0, 0.5, 0.25, 0.25]))
+    # budget at least the positive count keeps every positive block, never a zero one
+    pi = sip.inclusion_probabilities(np.array([0.7, 0.3, 0.0]), 2.0)[0]
+    assert np.array_equal(pi, np.array([1.0, 1.0, 0.0]))
+
+
+def test_inclusion_probabilities_invariants():
+    from oracle import sip
+    rng = np.random.default_rng(21)
+    p = rng.gamma(0.3, size=(40, 50))
+    p /= p.sum(axis=1, keepdims=True)
+    for k in (1.0, 4.5, 12.0, 49.0):
+        pi = sip.inclusion_probabilities(p, k)
+        assert np.allclose(pi.sum(axis=1), k, rtol=0, atol=1e-9)
+        assert np.all(pi <= 1.0) and np.all(pi >= 0.0)
+        for r in range(p.shape[0]):
+            free = pi[r] < 1.0
+            if free.sum() >= 2:                          # uncapped blocks: pi proportional to p
+                ratio = pi[r][free] / p[r][free]
+                assert np.allclose(ratio, ratio[0], rtol=1e-12)
+                assert p[r][~free].min(initial=np.inf) >= p[r][free].max()   # capped = the largest
+        perm = rng.permutation(p.shape[1])
+        assert np.allclose(sip.inclusion_probabilities(p[:, perm], k), pi[:, perm], rtol=0, atol=1e-12)
+
+
+def test_sampling_frequency_and_horvitz_thompson():
+    """Over many independent rows of the same scores, block j is kept with frequency
+    pi_j, and sum over kept blocks of x_j / pi_j averages to sum_j x_j."""
+    from oracle import sip
+    p = np.array([0.4, 0.2, 0.15, 0.1, 0.08, 0.04, 0.02, 0.01])
+    k = 3.0
+    pi = sip.inclusion_probabilities(p, k)[0]
+    R = 20000
+    u = sip.uniforms(5, R, p.size)
+    keep = u < pi
+    freq = keep.mean(axis=0)
+    sd = np.sqrt(pi * (1 - pi) / R)
+    assert np.all(np.abs(freq - pi) <= 5 * sd + 1e-12)
+    x = np.linspace(1.0, 2.0, p.size)
+    ht = (keep * (x / pi)).sum(axis=1)
+    assert abs(ht.mean() - x.sum()) <= 5 * ht.std() / np.sqrt(R)
+
+
+def test_logit_offset_zero_or_constant_changes_nothing():
+    rng = np.random.default_rng(30)
+    nB, tpb, d = 3, 8, 4
+    N = nB * tpb
+    q, k, v = (rng.standard_normal((1, 1, N, d)).astype(np.float32) for _ in range(3))
+    mask = rng.random((nB, nB)) < 0.7
+    mask[np.arange(nB), np.arange(nB)] = True
+    rp, ci = oracle.csr_from_mask(mask)
+    rows = np.arange(nB)
+    o0, l0 = oracle.attention_rows(q, k, v, rp, ci, rows, tpb=tpb)
+    o1, l1 = oracle.attention_rows(q, k, v, rp, ci, rows, tpb=tpb, bias=np.zeros(len(ci)))
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    # one constant per row: the softmax is unchanged, the LSE moves by it
+    cst = np.repeat(np.array([0.3, -1.2, 2.0]), np.diff(rp))
+    o2, l2 = oracle.attention_rows(q, k, v, rp, ci, rows, tpb=tpb, bias=cst)
+    assert np.allclose(o2, o0, rtol=0, atol=1e-12)
+    assert np.allclose(l2 - l0, np.array([0.3, -1.2, 2.0])[:, None], rtol=0, atol=1e-12)
+
+
+def test_logit_offset_ln_w_equals_w_copies_of_the_block():
+    """An offset ln(w) on a block (w integer) is the block's keys listed w times:
+    checked against token-level brute force on a key set with the copies appended."""
+    rng = np.random.default_rng(31)
+    nB, tpb, d = 3, 4, 5
+    N = nB * tpb
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    mask = np.array([[1, 1, 0], [0, 1, 1], [1, 1, 1]], dtype=bool)
+    w = {(0, 1): 3, (1, 2): 2, (2, 0): 4}                 # (row, block) -> copies
+    rp, ci = oracle.csr_from_mask(mask)
+    bias = np.zeros(len(ci))
+    for r in range(nB):
+        for e in range(rp[r], rp[r + 1]):
+            bias[e] = math.log(w.get((r, int(ci[e])), 1))
+    out, _ = oracle.attention_rows(q[None, None].astype(np.float32), k[None, None].astype(np.float32),
+                                   v[None, None].astype(np.float32), rp, ci, np.arange(nB), tpb=tpb, scale=0.5,
+                                   bias=bias)
+    q32, k32, v32 = (x.astype(np.float32).astype(np.float64) for x in (q, k, v))
+    for r in range(nB):
+        keys, vals = [], []
+        for j in range(nB):
+            if mask[r, j]:
+                for _ in range(w.get((r, j), 1)):
+                    keys.append(k32[j * tpb:(j + 1) * tpb])
+                    vals.append(v32[j * tpb:(j + 1) * tpb])
+        K, V = np.concatenate(keys), np.concatenate(vals)
+        ref, _ = brute.dense_attention(q32[r * tpb:(r + 1) * tpb], K, V, 0.5)
+        assert np.allclose(out[r], ref, rtol=0, atol=1e-12)
+
+
+def test_select_sip_consistency():
+    """The sampled list is u < pi with offsets -ln(pi) of the kept blocks, and a budget
+    of all blocks keeps everything with zero offsets."""
+    from oracle import sip
+    rng = np.random.default_rng(32)
+    q = rng.standard_normal((1, 2, 6 * 64, 8)).astype(np.float32)
+    k = (q + 0.3 * rng.standard_normal(q.shape)).astype(np.float32)
+    keep, rp, ci, bias, pi, u = sip.select_sip(q, k, 2, 2.5, seed=9)
+    assert np.array_equal(keep, u < pi)
+    assert np.allclose(pi.sum(axis=1), 2.5, rtol=0, atol=1e-9)
+    r = np.repeat(np.arange(keep.shape[0]), np.diff(rp))
+    assert np.array_equal(bias, -np.log(pi[r, ci]))
+    keep, rp, ci, bias, pi, u = sip.select_sip(q, k, 2, 6.0, seed=9)
+    assert keep.all() and np.all(bias == 0)
