@@ -13,7 +13,10 @@ more than that):
   * inclusion probabilities pi_j = min(1, c * p_j) with c > 0 chosen so that
     sum_j pi_j equals the budget k (expected kept blocks per row); blocks whose
     c * p_j reaches 1 are the "always kept" ones.  When k is at least the number
-    of blocks with p_j > 0, every such block gets pi_j = 1;
+    of blocks with p_j > 0, every such block gets pi_j = 1.  With m blocks capped,
+    an uncapped block has pi_j = (k - m) p_j / (mass of the uncapped), which is
+    computed from the scores relative to the largest uncapped one so that no
+    probability of the row underflows on the way (p_j is never formed);
   * sampling: independent draws, block j of row r kept iff u_rj < pi_j, where
     u_rj is the top 24 bits of SplitMix64 output number r * nB + j + 1 of the
     stream seeded with `seed`, scaled by 2^-24;
@@ -55,51 +58,68 @@ def uniforms(seed: int, rows: int, nB: int, row0: int = 0) -> np.ndarray:
     return (z >> np.uint64(40)).astype(np.float64) * 2.0 ** -24
 
 
-def pooled_probabilities(q, k, heads: int, scale: Optional[float] = None) -> np.ndarray:
-    """p [B*H*nB, nB]: softmax over key blocks of the pooled scores Qbar_i . Kbar_j * scale."""
+def pooled_scores(q, k, heads: int, scale: Optional[float] = None) -> np.ndarray:
+    """S [B*H*nB, nB]: the pooled scores Qbar_i . Kbar_j * scale (fp64), whose row
+    softmax is NABLA's p_ij."""
     qb, kb = pool(q), pool(k)                      # [B, H, nB, d] fp64
     d = qb.shape[-1]
     sc = default_scale(d) if scale is None else float(scale)
     s = np.einsum("...id,...jd->...ij", qb, kb) * sc
-    s -= s.max(axis=-1, keepdims=True)
-    e = np.exp(s)
-    p = e / e.sum(axis=-1, keepdims=True)
-    return p.reshape(-1, p.shape[-1])
+    return s.reshape(-1, s.shape[-1])
+
+
+def pooled_probabilities(q, k, heads: int, scale: Optional[float] = None) -> np.ndarray:
+    """p [B*H*nB, nB]: the row softmax of pooled_scores."""
+    s = pooled_scores(q, k, heads, scale)
+    e = np.exp(s - s.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def inclusion_probabilities_from_scores(s: np.ndarray, budget: float) -> np.ndarray:
+    """pi = min(1, c p) per row with sum(pi) = budget, p = softmax(s) (module notes).
+
+    For each row, with s sorted descending: try m = 0, 1, ... capped blocks.  The
+    uncapped ones are those after the m-th; with mR the largest of them and
+    E = sum over them of exp(s - mR), an uncapped block gets (budget - m)
+    exp(s_j - mR) / E, and the first m for which the largest uncapped block stays
+    at or below 1 -- budget - m <= E -- fixes the solution.  Scores of -inf are
+    blocks with p = 0: never included.
+    """
+    s = np.atleast_2d(np.asarray(s, dtype=np.float64))
+    pi = np.zeros_like(s)
+    for r in range(s.shape[0]):
+        row = s[r]
+        fin = np.isfinite(row)
+        npos = int(fin.sum())
+        if budget >= npos:
+            pi[r] = fin.astype(np.float64)
+            continue
+        ss = np.sort(row[fin])[::-1]
+        for m in range(npos):
+            mR = ss[m]
+            E = float(np.exp(ss[m:] - mR).sum())
+            K = budget - m
+            if K <= E:
+                pi[r] = np.where(fin, np.minimum(1.0, K * np.exp(np.where(fin, row, mR) - mR) / E), 0.0)
+                break
+    return pi
 
 
 def inclusion_probabilities(p: np.ndarray, budget: float) -> np.ndarray:
-    """pi = min(1, c p) per row with sum(pi) = budget (see the module notes).
-
-    For each row, with p sorted descending: try m = 0, 1, ... capped blocks; c is
-    (budget - m) / (sum of the rest) and the first m whose next block has
-    c * p <= 1 fixes the solution.
-    """
+    """The same for row probabilities p (p = 0 never included)."""
     p = np.atleast_2d(np.asarray(p, dtype=np.float64))
-    pi = np.zeros_like(p)
-    for r in range(p.shape[0]):
-        row = p[r]
-        npos = int(np.count_nonzero(row > 0))
-        if budget >= npos:
-            pi[r] = (row > 0).astype(np.float64)
-            continue
-        ps = np.sort(row)[::-1]
-        tail = np.cumsum(ps[::-1])[::-1]           # tail[m] = sum of ps[m:]
-        for m in range(npos):
-            c = (budget - m) / tail[m]
-            if c * ps[m] <= 1.0:
-                pi[r] = np.minimum(1.0, c * row)
-                break
-    return pi
+    with np.errstate(divide="ignore"):
+        return inclusion_probabilities_from_scores(np.log(p), budget)
 
 
 def select_sip(q, k, heads: int, budget: float, seed: int, scale: Optional[float] = None):
     """The sampled block list: (keep [rows, nB] bool, row_ptr, col_idx, bias per entry,
     pi [rows, nB], u [rows, nB])."""
-    p = pooled_probabilities(q, k, heads, scale)
-    pi = inclusion_probabilities(p, budget)
-    u = uniforms(seed, p.shape[0], p.shape[1])
+    s = pooled_scores(q, k, heads, scale)
+    pi = inclusion_probabilities_from_scores(s, budget)
+    u = uniforms(seed, s.shape[0], s.shape[1])
     keep = u < pi
     row_ptr, col_idx = csr_from_mask(keep)
-    rows = np.repeat(np.arange(p.shape[0]), np.diff(row_ptr))
+    rows = np.repeat(np.arange(s.shape[0]), np.diff(row_ptr))
     bias = -np.log(pi[rows, col_idx])
     return keep, row_ptr, col_idx, bias, pi, u

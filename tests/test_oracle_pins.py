@@ -499,7 +499,7 @@ def test_inclusion_probabilities_closed_forms():
     # p = (1/2, 1/4, 1/8, 1/8), k = 2: c = 2 caps block 0; then c = 1 / (1/2) = 2 for the
     # rest -> (1, 1/2, 1/4, 1/4)
     pi = sip.inclusion_probabilities(np.array([0.5, 0.25, 0.125, 0.125]), 2.0)[0]
-    assert np.array_equal(pi, np.array([1.0, 0.5, 0.25, 0.25]))
+    assert np.allclose(pi, np.array([1.0, 0.5, 0.25, 0.25]), rtol=0, atol=1e-15)
     # budget at least the positive count keeps every positive block, never a zero one
     pi = sip.inclusion_probabilities(np.array([0.7, 0.3, 0.0]), 2.0)[0]
     assert np.array_equal(pi, np.array([1.0, 1.0, 0.0]))
@@ -605,3 +605,21 @@ def test_select_sip_consistency():
     assert np.array_equal(bias, -np.log(pi[r, ci]))
     keep, rp, ci, bias, pi, u = sip.select_sip(q, k, 2, 6.0, seed=9)
     assert keep.all() and np.all(bias == 0)
+
+
+def test_inclusion_probabilities_from_scores_shift_and_range():
+    """pi depends on the scores only through their differences, and blocks far below the
+    row maximum still receive the budget the capped ones leave (no underflow): one
+    dominant block plus three equal ones 2000 nats lower, budget 2 -> (1, 1/3, 1/3, 1/3)."""
+    from oracle import sip
+    s = np.array([[0.0, -2000.0, -2000.0, -2000.0]])
+    pi = sip.inclusion_probabilities_from_scores(s, 2.0)
+    assert np.allclose(pi, [[1.0, 1 / 3, 1 / 3, 1 / 3]], rtol=0, atol=1e-15)
+    rng = np.random.default_rng(33)
+    s = rng.normal(scale=5.0, size=(6, 30))
+    a = sip.inclusion_probabilities_from_scores(s, 7.0)
+    b = sip.inclusion_probabilities_from_scores(s + 123.0, 7.0)
+    assert np.allclose(a, b, rtol=0, atol=1e-12)
+    assert np.allclose(a, sip.inclusion_probabilities(np.exp(s - s.max(1, keepdims=True)) /
+                                                      np.exp(s - s.max(1, keepdims=True)).sum(1, keepdims=True), 7.0),
+                       rtol=0, atol=1e-12)
