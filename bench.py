@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-CSR reference forward")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-sip", action="store_true", help="skip the sampling-selection timing")
+    ap.add_argument("--sip-budget", type=float, default=0.1,
+                    help="sampling selection: expected kept key blocks per row, as a fraction of the blocks")
     ap.add_argument("--no-select-timing", action="store_true", help="skip the separate selection timing")
     ap.add_argument("--dense-steps", type=int, default=0,
                     help="denoising schedule: this many leading steps run dense (no selection)")
@@ -253,6 +256,54 @@ def main():
                "frac_bf16_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4)}
         del dout, grads, t_idx
 
+    # sampling with inclusion probabilities (AB-Attention's SIP) on the same inputs: the
+    # selection (after the cache sweep, like the CDF selection) and the forward with
+    # the Horvitz-Thompson logit offsets over the sampled list
+    sip = None
+    if wl.dtype == "bf16" and not args.no_sip:
+        budget = args.sip_budget * wl.blocks
+        sbufs = B.alloc_buffers(shape, dev)
+        cbias = torch.empty(sbufs.col_idx.numel(), dtype=torch.float32, device=dev)
+
+        def sip_select():
+            return B.sparse_attn_select_sip(shape, qd, kd, budget, seed=2026, buffers=sbufs, col_bias=cbias,
+                                            stream=stream)
+        srp, sci, _ = sip_select()
+        torch.cuda.synchronize()
+        snnz = int(srp[-1].item())
+        sip_ms = []
+        for _ in range(10):
+            flush.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            sip_select()
+            b.record(stream)
+            torch.cuda.synchronize()
+            sip_ms.append(a.elapsed_time(b))
+        sip_ms_med = sorted(sip_ms)[len(sip_ms) // 2]
+        sip_bytes = 2 * qd.numel() * elt + 4 * (rows + 1) + 8 * snnz
+        for _ in range(2):
+            B.sparse_attn_forward_biased(shape, qd, kd, vd, srp, sci, cbias, out=out, lse=lse,
+                                         workspace=bufs.workspace, stream=stream)
+        fw_ms = []
+        for _ in range(10):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            B.sparse_attn_forward_biased(shape, qd, kd, vd, srp, sci, cbias, out=out, lse=lse,
+                                         workspace=bufs.workspace, stream=stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            fw_ms.append(a.elapsed_time(b))
+        fw_ms_med = sorted(fw_ms)[len(fw_ms) // 2]
+        sip_flops = 4.0 * 64 * 64 * wl.head_dim * snnz
+        sip = {"budget_blocks_per_row": budget, "nnz_tiles": snnz, "kept_fraction": round(snnz / (rows * wl.blocks), 4),
+               "select_ms": round(sip_ms_med, 4), "select_GB_s": round(sip_bytes / (sip_ms_med * 1e-3) / 1e9, 1),
+               "select_frac_hbm_peak": round(sip_bytes / (sip_ms_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+               "forward_ms": round(fw_ms_med, 4),
+               "forward_TFLOP_s": round(sip_flops / (fw_ms_med * 1e-3) / 1e12, 2),
+               "forward_frac_bf16_peak": round(sip_flops / (fw_ms_med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del sbufs, cbias
+
     # dense reference: the same forward kernel over the full CSR (every tile kept)
     full_bufs = B.alloc_buffers(shape, dev)
     full_rp, full_ci = B.sparse_attn_full_csr(shape, full_bufs, stream=stream)
@@ -342,6 +393,8 @@ def main():
     }
     if bwd is not None:
         rec["backward"] = bwd
+    if sip is not None:
+        rec["sip"] = sip
     if sched is not None:
         rec["denoise_schedule"] = sched
     if not args.no_cpu_baseline:

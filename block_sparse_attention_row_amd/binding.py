@@ -31,7 +31,9 @@ EXPORTED = (
     "sparse_attn_csr_capacity",
     "sparse_attn_workspace_size",
     "sparse_attn_select",
+    "sparse_attn_select_sip",
     "sparse_attn_forward",
+    "sparse_attn_forward_biased",
     "sparse_attn_mask_to_csr",
     "sparse_attn_backward",
     "sparse_attn_full_csr",
@@ -63,6 +65,10 @@ class SelectParams(ctypes.Structure):
     ]
 
 
+class SipParams(ctypes.Structure):
+    _fields_ = [("budget", ctypes.c_float), ("seed", ctypes.c_uint64)]
+
+
 _lib = None
 
 
@@ -87,8 +93,12 @@ def lib():
         L.sparse_attn_workspace_size.restype = I64
         L.sparse_attn_select.argtypes = [SP, ctypes.POINTER(SelectParams), P, P, P, P, I64, P, I64, P]
         L.sparse_attn_select.restype = ctypes.c_int32
+        L.sparse_attn_select_sip.argtypes = [SP, ctypes.POINTER(SipParams), P, P, P, P, P, I64, P, I64, P]
+        L.sparse_attn_select_sip.restype = ctypes.c_int32
         L.sparse_attn_forward.argtypes = [SP, P, P, P, P, P, I64, P, P, P, I64, P]
         L.sparse_attn_forward.restype = ctypes.c_int32
+        L.sparse_attn_forward_biased.argtypes = [SP, P, P, P, P, P, P, I64, P, P, P, I64, P]
+        L.sparse_attn_forward_biased.restype = ctypes.c_int32
         L.sparse_attn_mask_to_csr.argtypes = [SP, P, P, P, I64, P, I64, P]
         L.sparse_attn_mask_to_csr.restype = ctypes.c_int32
         L.sparse_attn_backward.argtypes = [SP, P, P, P, P, P, P, P, P, I64, P, P, P, P, P, I64, P]
@@ -189,6 +199,24 @@ def sparse_attn_select(shape: Shape, q, k, threshold: float = 0.9,
     return bufs.row_ptr, bufs.col_idx
 
 
+def sparse_attn_select_sip(shape: Shape, q, k, budget: float, seed: int = 0, buffers: Optional[Buffers] = None,
+                           col_bias=None, stream=None):
+    """Sampling with inclusion probabilities; returns (row_ptr, col_idx, col_bias), the
+    first two views of the caller-owned buffers, col_bias fp32 of their capacity."""
+    import torch
+    bufs = buffers or alloc_buffers(shape, q.device)
+    if col_bias is None:
+        col_bias = torch.empty(bufs.col_idx.numel(), dtype=torch.float32, device=q.device)
+    if col_bias.numel() < bufs.col_idx.numel() or col_bias.dtype != torch.float32:
+        raise ValueError("col_bias must be float32 with the capacity of col_idx")
+    params = SipParams(float(budget), int(seed) & 0xFFFFFFFFFFFFFFFF)
+    st = lib().sparse_attn_select_sip(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k),
+                                      _ptr(bufs.row_ptr), _ptr(bufs.col_idx), _ptr(col_bias), bufs.col_idx.numel(),
+                                      _ptr(bufs.workspace), bufs.workspace.numel(), _stream(stream))
+    _check(st, "sparse_attn_select_sip")
+    return bufs.row_ptr, bufs.col_idx, col_bias
+
+
 def sparse_attn_forward(shape: Shape, q, k, v, row_ptr, col_idx, out=None, lse=None, want_lse: bool = False,
                         workspace=None, stream=None):
     """Block-sparse attention; returns out (and lse when requested)."""
@@ -204,6 +232,26 @@ def sparse_attn_forward(shape: Shape, q, k, v, row_ptr, col_idx, out=None, lse=N
                                    col_idx.numel(), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                    _stream(stream))
     _check(st, "sparse_attn_forward")
+    return (out, lse) if (want_lse or lse is not None) else out
+
+
+def sparse_attn_forward_biased(shape: Shape, q, k, v, row_ptr, col_idx, col_bias, out=None, lse=None,
+                               want_lse: bool = False, workspace=None, stream=None):
+    """Block-sparse attention with a logit offset per col_idx entry (fp32 col_bias)."""
+    import torch
+    if col_bias.numel() < col_idx.numel() or col_bias.dtype != torch.float32:
+        raise ValueError("col_bias must be float32 with one value per col_idx entry")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        B, H, N, _ = q.shape
+        lse = torch.empty(B, H, N, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(sparse_attn_workspace_size(shape), dtype=torch.uint8, device=q.device)
+    st = lib().sparse_attn_forward_biased(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr),
+                                          _ptr(col_idx), _ptr(col_bias), col_idx.numel(), _ptr(out), _ptr(lse),
+                                          _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "sparse_attn_forward_biased")
     return (out, lse) if (want_lse or lse is not None) else out
 
 

@@ -221,16 +221,19 @@ int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_sel
     return SPARSE_ATTN_OK;
 }
 
-int32_t sparse_attn_forward(const sparse_attn_shape *shape, const void *q, const void *k, const void *v,
-                            const int32_t *row_ptr, const int32_t *col_idx, int64_t col_count, void *out,
-                            float *lse, void *workspace, int64_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+int32_t forward_impl(const sparse_attn_shape *shape, const void *q, const void *k, const void *v,
+                     const int32_t *row_ptr, const int32_t *col_idx, const float *col_bias, int64_t col_count,
+                     void *out, float *lse, void *workspace, int64_t workspace_bytes, void *stream) {
     Dims d;
     int32_t st = check_shape(shape, &d);
     if (st) return st;
     if (!q || !k || !v || !row_ptr || !out || !workspace) return SPARSE_ATTN_INVALID_ARGUMENT;
     if (col_count < 0 || (col_count > 0 && !col_idx)) return SPARSE_ATTN_INVALID_ARGUMENT;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(row_ptr, 4) ||
-        !aligned(col_idx, 4) || !aligned(lse, 4) || !aligned(workspace, 16))
+        !aligned(col_idx, 4) || !aligned(col_bias, 4) || !aligned(lse, 4) || !aligned(workspace, 16))
         return SPARSE_ATTN_INVALID_ARGUMENT;
     const Layout L = layout(d);
     if (workspace_bytes < L.total) return SPARSE_ATTN_WORKSPACE;
@@ -241,6 +244,7 @@ int32_t sparse_attn_forward(const sparse_attn_shape *shape, const void *q, const
     a.v = v;
     a.row_ptr = row_ptr;
     a.col_idx = col_idx;
+    a.col_bias = col_bias;
     a.col_count = col_count;
     a.out = out;
     a.lse = lse;
@@ -258,6 +262,83 @@ int32_t sparse_attn_forward(const sparse_attn_shape *shape, const void *q, const
     a.plan.part_lse = (float *)(ws + L.part_lse);
     a.plan.max_slots = (int32_t)max_slots(d);
     if (launch_attention(a, shape->dtype, (int)d.D, (hipStream_t)stream)) return SPARSE_ATTN_HIP_ERROR;
+    return SPARSE_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sparse_attn_forward(const sparse_attn_shape *shape, const void *q, const void *k, const void *v,
+                            const int32_t *row_ptr, const int32_t *col_idx, int64_t col_count, void *out,
+                            float *lse, void *workspace, int64_t workspace_bytes, void *stream) {
+    return forward_impl(shape, q, k, v, row_ptr, col_idx, nullptr, col_count, out, lse, workspace, workspace_bytes,
+                        stream);
+}
+
+int32_t sparse_attn_forward_biased(const sparse_attn_shape *shape, const void *q, const void *k, const void *v,
+                                   const int32_t *row_ptr, const int32_t *col_idx, const float *col_bias,
+                                   int64_t col_count, void *out, float *lse, void *workspace,
+                                   int64_t workspace_bytes, void *stream) {
+    if (shape && shape->dtype != SPARSE_ATTN_BF16) return SPARSE_ATTN_UNSUPPORTED;
+    if (col_count > 0 && !col_bias) return SPARSE_ATTN_INVALID_ARGUMENT;
+    // an empty list has no offsets to apply: the plain kernel gives the same result
+    return forward_impl(shape, q, k, v, row_ptr, col_idx, col_count > 0 ? col_bias : nullptr, col_count, out, lse,
+                        workspace, workspace_bytes, stream);
+}
+
+int32_t sparse_attn_select_sip(const sparse_attn_shape *shape, const sparse_attn_sip_params *params, const void *q,
+                               const void *k, int32_t *row_ptr, int32_t *col_idx, float *col_bias,
+                               int64_t col_capacity, void *workspace, int64_t workspace_bytes, void *stream) {
+    Dims d;
+    int32_t st = check_shape(shape, &d);
+    if (st) return st;
+    if (shape->dtype != SPARSE_ATTN_BF16) return SPARSE_ATTN_UNSUPPORTED;
+    if (!params || !q || !k || !row_ptr || !col_idx || !col_bias || !workspace) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(row_ptr, 4) || !aligned(col_idx, 4) || !aligned(col_bias, 4) ||
+        !aligned(workspace, 16))
+        return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (d.nBp > kSelectMaxBlocks) return SPARSE_ATTN_UNSUPPORTED;   // a row is held in registers
+    if (!(params->budget > 0.f) || !(params->budget < INFINITY)) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (col_capacity < d.rows * d.nB) return SPARSE_ATTN_CAPACITY;
+    const Layout L = layout(d);
+    if (workspace_bytes < L.total) return SPARSE_ATTN_WORKSPACE;
+
+    hipStream_t s = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    __bf16 *kbar = (__bf16 *)(ws + L.kbar);
+    uint64_t *status = (uint64_t *)(ws + L.status);
+    uint32_t *ticket = (uint32_t *)(ws + L.ticket);
+    PoolSide side;
+    side.n_thr = 0;
+    side.thr_dst = (float *)(ws + L.thr);
+    side.status = status;
+    side.n_status = n_groups(d);
+    side.ticket = ticket;
+    if (launch_pool_keys(k, kbar, d.B * d.H * d.nB, shape->dtype, (int)d.D, side, s)) return SPARSE_ATTN_HIP_ERROR;
+
+    SelectArgs a = {};
+    a.q = q;
+    a.kbar = kbar;
+    a.thr = (const float *)(ws + L.thr);
+    a.status = status;
+    a.ticket = ticket;
+    a.row_ptr = row_ptr;
+    a.col_idx = col_idx;
+    a.rows = d.rows;
+    a.groups_per_head = (int32_t)groups_per_head(d);
+    a.n_groups = n_groups(d);
+    a.H = (int32_t)d.H;
+    a.nB = (int32_t)d.nB;
+    a.nBp = (int32_t)d.nBp;
+    a.nTy = d.nTy;
+    a.nTx = d.nTx;
+    a.window = 0;
+    a.scale_log2 = effective_scale(shape) * kLog2e;
+    a.budget = params->budget;
+    a.seed = params->seed;
+    a.col_bias = col_bias;
+    if (launch_select_sip(a, (int)d.D, s)) return SPARSE_ATTN_HIP_ERROR;
     return SPARSE_ATTN_OK;
 }
 

@@ -55,6 +55,30 @@ __device__ __forceinline__ void tile_rescale(const f32x16 *acc_s, float c, float
     }
 }
 
+// The same bookkeeping with a logit offset beta (log2 units) on the whole tile:
+// scores are s*c + beta, and the running max M is kept in log2 units.
+template <int NDT>
+__device__ __forceinline__ void tile_rescale_biased(const f32x16 *acc_s, float c, float beta, float &M,
+                                                    float &l_run, f32x16 *acc_o) {
+    float mt = fmaxf(acc_s[0][0], acc_s[0][1]);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = (kt == 0 ? 2 : 0); v < 16; v += 2) mt = fmaxf(mt, fmaxf(acc_s[kt][v], acc_s[kt][v + 1]));
+    mt = __builtin_fmaf(pair_max(mt), c, beta);
+    const bool grow = mt - M > kLazy;
+    if (__ballot(grow)) {
+        const float m_new = grow ? mt : M;
+        const float alpha = __builtin_amdgcn_exp2f(M - m_new);
+        M = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < NDT; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc_o[i][v] *= alpha;
+    }
+}
+
 // P = 2^(s*c - m*c) as bf16 B operands; the row sum takes the same bf16-rounded P.
 __device__ __forceinline__ void tile_probs(const f32x16 *acc_s, float c, float mc, float &l_run, bf16x8 *pf) {
 #pragma unroll
@@ -120,7 +144,11 @@ __device__ __forceinline__ void tile_scores_probs(const char *K, const bf16x8 *q
 // while the scores of tile j+1 are formed on MFMA, the softmax of tile j runs on
 // the VALU, then P V of tile j follows.  K runs two tiles ahead of use and V one,
 // in two LDS buffers each.
-template <int D>
+//
+// BIAS: every block-list entry carries a logit offset (col_bias, natural-log units)
+// that is added to the scores of its tile; the running max is then tracked in log2
+// units, including the offset.
+template <int D, bool BIAS>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     using G = TileGeo<D>;
     constexpr int ROWB = G::ROWB, SLOTS = G::SLOTS, RPI = G::RPI, IPW = G::IPW, NDT = G::NDT, TILEB = G::TILEB;
@@ -212,13 +240,17 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     }
     const uint32_t ks0 = (uint32_t)(uintptr_t)(lds_char *)Ks + 16 * wave * ROWB;
     const uint32_t vs0 = (uint32_t)(uintptr_t)(lds_char *)Vs + 16 * wave * ROWB;
-    auto issue_k = [&](int64_t col, int buf) {
+    // (the column is wave-uniform by construction; readfirstlane states it for the
+    // scalar base operand of the direct load)
+    auto issue_k = [&](int col, int buf) {
+        const int64_t cu = __builtin_amdgcn_readfirstlane(col);
 #pragma unroll
-        for (int i = 0; i < IPW; ++i) dma16(ks0 + buf * TILEB + RPI * i * ROWB, voff[i], kg + col * TILEB);
+        for (int i = 0; i < IPW; ++i) dma16(ks0 + buf * TILEB + RPI * i * ROWB, voff[i], kg + cu * TILEB);
     };
-    auto issue_v = [&](int64_t col, int buf) {
+    auto issue_v = [&](int col, int buf) {
+        const int64_t cu = __builtin_amdgcn_readfirstlane(col);
 #pragma unroll
-        for (int i = 0; i < IPW; ++i) dma16(vs0 + buf * TILEB + RPI * i * ROWB, voff[i], vg + col * TILEB);
+        for (int i = 0; i < IPW; ++i) dma16(vs0 + buf * TILEB + RPI * i * ROWB, voff[i], vg + cu * TILEB);
     };
 
     // merged walk over the two rows' ascending lists (entries out of range or not
@@ -228,17 +260,28 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     constexpr int kNone = 0x7fffffff;
     const int32_t *cv = a.col_idx;
     auto window = [&](int64_t base, int64_t e) { return base + lane < e ? cv[base + lane] : kNone; };
+    // (BIAS) the entries' offsets travel in windows of their own, in step with the columns
+    auto bwindow = [&](int64_t base, int64_t e) {
+        if constexpr (BIAS) return base + lane < e ? a.col_bias[base + lane] : 0.f;
+        else return 0.f;
+    };
     int64_t baseA = begA, baseB = begB;
     int posA = 0, posB = 0;
     int winA = window(baseA, endA), nxtA = window(baseA + 64, endA);
     int winB = window(baseB, endB), nxtB = window(baseB + 64, endB);
-    auto peek = [&](int64_t &base, int &pos, int &win, int &nxt, int64_t e, int last) {
+    float bwinA = bwindow(baseA, endA), bnxtA = bwindow(baseA + 64, endA);
+    float bwinB = bwindow(baseB, endB), bnxtB = bwindow(baseB + 64, endB);
+    auto peek = [&](int64_t &base, int &pos, int &win, int &nxt, float &bwin, float &bnxt, int64_t e, int last) {
         while (base + pos < e) {
             if (pos == 64) {
                 base += 64;
                 pos = 0;
                 win = nxt;
                 nxt = window(base + 64, e);
+                if constexpr (BIAS) {
+                    bwin = bnxt;
+                    bnxt = bwindow(base + 64, e);
+                }
             }
             const int cc = __builtin_amdgcn_readlane(win, pos);
             if (cc > last && cc < a.nB) return cc;
@@ -246,12 +289,20 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         }
         return kNone;
     };
-    // next union tile: its column and whether this wave's row keeps it
-    auto next_union = [&](int &col, bool &mine) {
-        const int cA = peek(baseA, posA, winA, nxtA, endA, lastA);
-        const int cB = peek(baseB, posB, winB, nxtB, endB, lastB);
+    // next union tile: its column, whether this wave's row keeps it, and (BIAS) the
+    // offset of this wave's entry in log2 units
+    auto next_union = [&](int &col, bool &mine, float &beta) {
+        const int cA = peek(baseA, posA, winA, nxtA, bwinA, bnxtA, endA, lastA);
+        const int cB = peek(baseB, posB, winB, nxtB, bwinB, bnxtB, endB, lastB);
         col = cA < cB ? cA : cB;
         const bool inA = cA == col && col != kNone, inB = cB == col && col != kNone;
+        if constexpr (BIAS) {
+            const float bA = inA ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bwinA), posA)) : 0.f;
+            const float bB = inB ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bwinB), posB)) : 0.f;
+            beta = (grp ? bB : bA) * kLog2e;
+        } else {
+            beta = 0.f;
+        }
         if (inA) { lastA = cA; ++posA; }
         if (inB) { lastB = cB; ++posB; }
         mine = grp ? inB : inA;
@@ -262,13 +313,15 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     for (int i = 0; i < NDT; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc_o[i][v] = 0.f;
+    // running max: raw score units, or (BIAS) log2 units including the offsets
     float m_run = -INFINITY, l_run = 0.f;
 
     // tiles j (scores pending), j+1 (K resident), j+2 (lookahead)
     int col0, col1, col2;
     bool mine0, mine1, mine2;
-    next_union(col0, mine0);
-    next_union(col1, mine1);
+    float beta0, beta1, beta2;
+    next_union(col0, mine0, beta0);
+    next_union(col1, mine1, beta1);
     f32x16 sa[2], sb[2];
     if (col0 != kNone) {
         issue_k(col0, 0);
@@ -283,15 +336,20 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     auto step = [&](auto bj_tag, f32x16 *sc, f32x16 *sn) {
         constexpr int BJ = decltype(bj_tag)::value;
         wait_vmcnt<0>();            // this wave's part of K(j+1) and V(j) has landed
-        next_union(col2, mine2);    // (after the wait: a window load never waits on tile loads)
+        next_union(col2, mine2, beta2);   // (after the wait: a window load never waits on tile loads)
         __syncthreads();            // ... and everyone's; K(j) and V(j-1) are free
         if (col2 != kNone) issue_k(col2, BJ);
         if (col1 != kNone) issue_v(col1, BJ ^ 1);
 
         float mc = 0.f;
         if (mine0) {
-            tile_rescale<NDT>(sc, c, m_run, l_run, acc_o);
-            mc = m_run * c;
+            if constexpr (BIAS) {
+                tile_rescale_biased<NDT>(sc, c, beta0, m_run, l_run, acc_o);
+                mc = m_run - beta0;
+            } else {
+                tile_rescale<NDT>(sc, c, m_run, l_run, acc_o);
+                mc = m_run * c;
+            }
         }
         bf16x8 pf[4];
         if (mine0 && mine1) {
@@ -309,8 +367,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         __builtin_amdgcn_s_setprio(0);
         col0 = col1;
         mine0 = mine1;
+        beta0 = beta1;
         col1 = col2;
         mine1 = mine2;
+        beta1 = beta2;
     };
     while (col0 != kNone) {
         step(std::integral_constant<int, 0>{}, sa, sb);
@@ -334,7 +394,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
                 for (int e = 0; e < 4; ++e) po[(32 * dt + 8 * rr + 4 * hh + e) * 64 + q] = acc_o[dt][4 * rr + e] * inv;
         if (hh == 0)
             a.plan.part_lse[((int64_t)it.slot * 2 + grp) * 64 + q] =
-                l_tot > 0.f ? m_run * c + __log2f(l_tot) : -INFINITY;
+                l_tot > 0.f ? (BIAS ? m_run : m_run * c) + __log2f(l_tot) : -INFINITY;
         return;
     }
     const int64_t qrow = bh * N + (int64_t)(i0 + grp) * 64 + 32 * (wave & 1) + l32;
@@ -348,7 +408,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
             for (int e = 0; e < 4; ++e) w[e] = acc_o[dt][4 * rr + e] * inv;
             *reinterpret_cast<bf16x4 *>(og + 32 * dt + 8 * rr + 4 * hh) = __builtin_convertvector(w, bf16x4);
         }
-    if (a.lse && hh == 0) a.lse[qrow] = l_tot > 0.f ? (m_run * c + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (a.lse && hh == 0)
+        a.lse[qrow] = l_tot > 0.f ? ((BIAS ? m_run : m_run * c) + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -626,11 +687,14 @@ int launch_attention(const AttnArgs &a, int dtype, int d, hipStream_t s) {
     const dim3 mgrid((unsigned)a.plan.max_slots), mblock(512);
     if (dtype == 1) {
         plan_kernel<<<1, 1024, 0, s>>>(a);
+        const bool bias = a.col_bias != nullptr;
         if (d == 128) {
-            attn_bf16_kernel<128><<<pgrid, pblock, 0, s>>>(a);
+            if (bias) attn_bf16_kernel<128, true><<<pgrid, pblock, 0, s>>>(a);
+            else attn_bf16_kernel<128, false><<<pgrid, pblock, 0, s>>>(a);
             merge_kernel<128><<<mgrid, mblock, 0, s>>>(a);
         } else {
-            attn_bf16_kernel<64><<<pgrid, pblock, 0, s>>>(a);
+            if (bias) attn_bf16_kernel<64, true><<<pgrid, pblock, 0, s>>>(a);
+            else attn_bf16_kernel<64, false><<<pgrid, pblock, 0, s>>>(a);
             merge_kernel<64><<<mgrid, mblock, 0, s>>>(a);
         }
     } else if (dtype == 0 && d == 128)

@@ -51,6 +51,11 @@ struct SelectArgs {
     int32_t nTy, nTx;         // block grid (t is implied)
     int32_t window, wt, wh, ww;
     float scale_log2;         // softmax scale * log2(e)
+    // sampling with inclusion probabilities (the SIP selection): expected kept blocks
+    // per row, the uniforms' seed, and the offsets written beside col_idx
+    float budget;
+    uint64_t seed;
+    float *col_bias;
 };
 
 // Row splitting of the bf16 attention.  Pairs of query blocks whose rows hold more
@@ -79,6 +84,7 @@ struct SplitPlan {
 struct AttnArgs {
     const void *q, *k, *v;
     const int32_t *row_ptr, *col_idx;
+    const float *col_bias;    // nullable: logit offset per col_idx entry (bf16 path)
     int64_t col_count;
     void *out;
     float *lse;               // nullable
@@ -103,6 +109,7 @@ int launch_pool_keys(const void *k, __bf16 *kbar, int64_t nblocks, int dtype, in
                      hipStream_t s);
 int launch_fill_thresholds(const float *host_thr, int n, float *dst, hipStream_t s);
 int launch_select(const SelectArgs &a, int d, int dtype, hipStream_t s);
+int launch_select_sip(const SelectArgs &a, int d, hipStream_t s);
 int launch_mask_bits(const uint8_t *mask, int64_t bh, int32_t nB, int32_t nW, uint64_t *bits, int32_t *counts,
                      int32_t *group_sums, hipStream_t s);
 int launch_full_csr(int64_t rows, int32_t nB, int32_t *row_ptr, int32_t *col_idx, hipStream_t s);

@@ -285,6 +285,74 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
     count_out = (int32_t)count;
 }
 
+// Uniform in [0, 1) for block j of row r: the top 24 bits of output r * nB + j + 1
+// of the SplitMix64 stream seeded with `seed` (state advanced by the golden gamma,
+// output through the variant-13 murmur3 finaliser), times 2^-24.
+__device__ __forceinline__ float splitmix_uniform(uint64_t seed, uint64_t counter) {
+    uint64_t z = seed + counter * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return (float)(uint32_t)(z >> 40) * 0x1p-24f;
+}
+
+// Sampling with inclusion probabilities ("SIP", AB-Attention page, section "Les
+// trois techniques d'AB-Attention") on row i, run by one wave on its register row s
+// (pooled scores in log2 units, -inf for padding): pi_j = min(1, c p_j) with
+// sum pi = budget, p the row softmax.  The capped blocks are those with s_j >= sigma;
+// with mR the largest uncapped score and E = sum over the uncapped of 2^(s - mR), an
+// uncapped block gets (budget - #capped) 2^(s_j - mR) / E = 2^(s_j - t) with
+// t = mR + log2(E / (budget - #capped)), taken relative to mR so that no
+// probability underflows.  Starting with nothing capped, every block with s_j >= t is
+// capped (sigma = t) and t recomputed, until t lies above every uncapped score (the
+// capped set only grows).  A budget of at least the number of real blocks keeps all
+// of them.  Block j is kept when its uniform is below pi_j.  Returns this lane's
+// bitmask word (as select_cut), the count, sigma and t (sigma = -inf: keep all).
+template <int NE>
+__device__ __forceinline__ void sip_cut(const SelectArgs &a, const float (&s)[NE], int64_t row, int lane,
+                                        uint64_t &word, int32_t &count_out, float &sigma_out, float &t_out) {
+    float sigma = INFINITY, t = INFINITY;
+    if (a.budget < (float)a.nB) {
+        uint32_t ncap = 0;
+        for (int it = 0; it < 64; ++it) {
+            float mr = -INFINITY;
+#pragma unroll
+            for (int c = 0; c < NE; ++c) mr = fmaxf(mr, s[c] < sigma ? s[c] : -INFINITY);
+            mr = wave_max_u(mr);
+            float e = 0.f;
+#pragma unroll
+            for (int c = 0; c < NE; ++c) e += s[c] < sigma ? __builtin_amdgcn_exp2f(s[c] - mr) : 0.f;
+            const float E = wave_sum_u(e);
+            t = mr + __log2f(E / (a.budget - (float)ncap));
+            if (!(t <= mr)) break;                    // the largest uncapped block stays below 1
+            uint32_t cnt = 0;
+#pragma unroll
+            for (int c = 0; c < NE; ++c) cnt += (uint32_t)__popcll(__ballot(s[c] >= t));
+            sigma = t;
+            ncap = cnt;
+        }
+    } else {
+        sigma = -INFINITY;
+    }
+    uint32_t count = 0, wlo = 0, whi = 0;
+#pragma unroll
+    for (int c = 0; c < NE; ++c) {
+        const int j = 64 * c + lane;
+        const float pi = s[c] >= sigma ? 1.f : __builtin_amdgcn_exp2f(s[c] - t);
+        const bool keep = j < a.nB && splitmix_uniform(a.seed, (uint64_t)row * a.nB + j + 1) < pi;
+        const uint64_t m = __ballot(keep);
+        count += (uint32_t)__popcll(m);
+        if (lane == c) {
+            wlo = (uint32_t)m;
+            whi = (uint32_t)(m >> 32);
+        }
+    }
+    word = ((uint64_t)whi << 32) | wlo;
+    count_out = (int32_t)count;
+    sigma_out = sigma;
+    t_out = t;
+}
+
 // Offset of group g in col_idx: decoupled look-back over the groups' look-back words,
 // run by one wave.  The group's total is published first; then the words of the 64
 // groups before the current position are read at once and summed up to the nearest
@@ -324,7 +392,10 @@ __device__ __forceinline__ int64_t group_lookback(uint64_t *status, int64_t g, i
 // block i0 + w into LDS while the first key chunk loads, the waves form the scores
 // chunk by chunk, each cuts its row, wave 0 finds the group's offset by look-back,
 // and each wave writes its row's row_ptr entry and kept columns.
-template <typename T, int D, int NE>
+//
+// MODE 0: NABLA's CDF cut; MODE 1: sampling with inclusion probabilities, which also
+// writes the offset -ln(pi) of every kept block to col_bias.
+template <typename T, int D, int NE, int MODE>
 __global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
     static_assert(NE % 4 == 0 && NE <= 64, "NE: register row length in 64-key words");
     constexpr int KB = D / 32;                     // k-blocks of one 16x16x32 product
@@ -409,7 +480,11 @@ __global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
     }
     uint64_t word = 0;
     int32_t count = 0;
-    if (wave < nrows) select_cut<NE>(a, s, hist_all, i0 + wave, thr, lane, word, count);
+    float sigma = 0.f, tcap = 0.f;
+    if (wave < nrows) {
+        if constexpr (MODE == 0) select_cut<NE>(a, s, hist_all, i0 + wave, thr, lane, word, count);
+        else sip_cut<NE>(a, s, (int64_t)bh * a.nB + i0 + wave, lane, word, count, sigma, tcap);
+    }
     if (lane == 0) wave_count[wave] = count;
     __syncthreads();
 
@@ -434,12 +509,29 @@ __global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
     const int cnt = __popcll(word);
     const int excl = wave_incl_scan_i(cnt, lane) - cnt;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int e = 0; e < nvc; ++e) {
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)word, e);
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(word >> 32), e);
-        const uint64_t m = ((uint64_t)hi << 32) | lo;
-        const int off = __builtin_amdgcn_readlane(excl, e);
-        if ((m >> lane) & 1ull) a.col_idx[pos + off + __popcll(m & lt_mask)] = 64 * e + lane;
+    if constexpr (MODE == 0) {
+        for (int e = 0; e < nvc; ++e) {
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)word, e);
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(word >> 32), e);
+            const uint64_t m = ((uint64_t)hi << 32) | lo;
+            const int off = __builtin_amdgcn_readlane(excl, e);
+            if ((m >> lane) & 1ull) a.col_idx[pos + off + __popcll(m & lt_mask)] = 64 * e + lane;
+        }
+    } else {
+        // the register row is indexed by the word, so the loop runs at compile time
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            if (e >= nvc) break;
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)word, e);
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(word >> 32), e);
+            const uint64_t m = ((uint64_t)hi << 32) | lo;
+            const int off = __builtin_amdgcn_readlane(excl, e);
+            if ((m >> lane) & 1ull) {
+                const int at = pos + off + __popcll(m & lt_mask);
+                a.col_idx[at] = 64 * e + lane;
+                a.col_bias[at] = s[e] >= sigma ? 0.f : (tcap - s[e]) * kLn2;   // -ln(pi)
+            }
+        }
     }
 }
 
@@ -469,14 +561,15 @@ int launch_fill_thresholds(const float *host_thr, int n, float *dst, hipStream_t
     return 0;
 }
 
-template <typename T, int D, int NCH> static void launch_select_nch(const SelectArgs &a, int nch, hipStream_t s) {
+template <typename T, int D, int NCH, int MODE = 0>
+static void launch_select_nch(const SelectArgs &a, int nch, hipStream_t s) {
     if constexpr (NCH <= kSelectMaxBlocks / kSelChunk) {
         if (nch == NCH) {
-            select_emit_kernel<T, D, 4 * NCH>
+            select_emit_kernel<T, D, 4 * NCH, MODE>
                 <<<dim3((unsigned)a.n_groups), dim3(64 * kSelRows), select_lds_bytes<D>(), s>>>(a);
             return;
         }
-        launch_select_nch<T, D, NCH + 1>(a, nch, s);
+        launch_select_nch<T, D, NCH + 1, MODE>(a, nch, s);
     }
 }
 
@@ -491,6 +584,16 @@ int launch_select(const SelectArgs &a, int d, int dtype, hipStream_t s) {
         launch_select_nch<float, 128, 1>(a, nch, s);
     else
         launch_select_nch<float, 64, 1>(a, nch, s);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_select_sip(const SelectArgs &a, int d, hipStream_t s) {
+    if (a.nBp > kSelectMaxBlocks) return -1;
+    const int nch = (a.nB + kSelChunk - 1) / kSelChunk;
+    if (d == 128)
+        launch_select_nch<__bf16, 128, 1, 1>(a, nch, s);
+    else
+        launch_select_nch<__bf16, 64, 1, 1>(a, nch, s);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -130,6 +130,35 @@ int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_sel
                            int64_t col_capacity, void *workspace, int64_t workspace_bytes,
                            void *stream);
 
+/* Parameters of sparse_attn_select_sip. */
+typedef struct {
+    float budget;    /* expected kept key blocks per row, > 0 (>= nB keeps every block) */
+    uint64_t seed;   /* seed of the SplitMix64 stream the draws come from */
+} sparse_attn_sip_params;
+
+/*
+ * Block selection by sampling with inclusion-probability weighting, the second
+ * technique of AB-Attention (AB-Attention page, section "Les trois techniques
+ * d'AB-Attention"), on NABLA's pooled scores: for each row, p_j is the softmax of
+ * the pooled scores over all key blocks (as in sparse_attn_select), the
+ * inclusion probabilities are pi_j = min(1, c p_j) with c such that
+ * sum_j pi_j = budget (the blocks whose c p_j reaches 1 are always kept), and
+ * block j of row r is kept when u < pi_j, where u is the top 24 bits of output
+ * r*nB + j + 1 of the SplitMix64 stream seeded with params->seed, times 2^-24.
+ * Every kept block gets the logit offset -ln(pi_j), for
+ * sparse_attn_forward_biased: the Horvitz-Thompson weight 1/pi_j.
+ *
+ *   q, k, row_ptr, col_idx, col_capacity, workspace: as in sparse_attn_select.
+ *   col_bias    device, fp32 [col_capacity]; entries [0, nnz) are written,
+ *               aligned with col_idx.
+ * bf16 only, nB <= 4096 (SPARSE_ATTN_UNSUPPORTED otherwise); a budget that is
+ * not a finite positive number is SPARSE_ATTN_INVALID_ARGUMENT.
+ */
+int32_t sparse_attn_select_sip(const sparse_attn_shape *shape, const sparse_attn_sip_params *params,
+                               const void *q, const void *k, int32_t *row_ptr, int32_t *col_idx,
+                               float *col_bias, int64_t col_capacity, void *workspace,
+                               int64_t workspace_bytes, void *stream);
+
 /*
  * Block-sparse attention forward over a CSR block list (from
  * sparse_attn_select, sparse_attn_mask_to_csr or the caller).
@@ -158,6 +187,26 @@ int32_t sparse_attn_forward(const sparse_attn_shape *shape, const void *q, const
                             const int32_t *row_ptr, const int32_t *col_idx, int64_t col_count,
                             void *out, float *lse, void *workspace, int64_t workspace_bytes,
                             void *stream);
+
+/*
+ * sparse_attn_forward with a logit offset per block-list entry: the keys of
+ * entry e's block get col_bias[e] added to their scaled logits before the
+ * softmax (numerator and normaliser alike).  This is how AB-Attention's
+ * sampling with inclusion-probability weighting ("SIP", AB-Attention page,
+ * section "Les trois techniques d'AB-Attention") applies its Horvitz-Thompson
+ * weights: offset -ln(pi) makes a block count 1/pi times.
+ *
+ *   col_bias    device, fp32 [col_count], finite values in natural-log units,
+ *               aligned with col_idx (skipped entries' offsets are ignored).
+ *               NULL is allowed only when col_count == 0.
+ *   lse         as in sparse_attn_forward, including the offsets.
+ * Everything else as in sparse_attn_forward.  bf16 only
+ * (SPARSE_ATTN_UNSUPPORTED otherwise).
+ */
+int32_t sparse_attn_forward_biased(const sparse_attn_shape *shape, const void *q, const void *k,
+                                   const void *v, const int32_t *row_ptr, const int32_t *col_idx,
+                                   const float *col_bias, int64_t col_count, void *out, float *lse,
+                                   void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * External block mask to CSR (the path that accepts a caller's mask, e.g. a

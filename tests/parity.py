@@ -152,9 +152,9 @@ def gpu_forward(wl: Workload, q, k, v, row_ptr, col_idx, want_lse=True):
     return out, lse
 
 
-def compare_rows(wl: Workload, out, lse, q, k, v, row_ptr, col_idx, rows):
+def compare_rows(wl: Workload, out, lse, q, k, v, row_ptr, col_idx, rows, bias=None):
     """Max |GPU - oracle| of output and LSE over the listed query-block rows."""
-    ref, ref_lse = oracle.attention_rows(q, k, v, row_ptr, col_idx, rows)
+    ref, ref_lse = oracle.attention_rows(q, k, v, row_ptr, col_idx, rows, bias=bias)
     nB = wl.blocks
     o = out.float().cpu().reshape(-1, nB, 64, wl.head_dim)
     l = lse.cpu().reshape(-1, nB, 64)
@@ -167,6 +167,39 @@ def compare_rows(wl: Workload, out, lse, q, k, v, row_ptr, col_idx, rows):
     assert np.array_equal(np.isneginf(got_l), ~fin)
     lerr = float(np.abs(got_l[fin] - ref_lse[fin]).max()) if fin.any() else 0.0
     return err, lerr
+
+
+def gpu_forward_biased(wl: Workload, q, k, v, row_ptr, col_idx, bias):
+    shape = shape_for(wl)
+    rp = torch.as_tensor(np.asarray(row_ptr, dtype=np.int32)).cuda()
+    ci = torch.as_tensor(np.asarray(col_idx, dtype=np.int32)).cuda()
+    cb = torch.as_tensor(np.asarray(bias, dtype=np.float32)).cuda()
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=q.device)
+    B.sparse_attn_forward_biased(shape, q, k, v, rp, ci, cb, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+# Sampling with inclusion probabilities: the kernels form pi from fp32 exponentials of
+# split-bf16 pooled scores (relative error near 2^-16 of the score, up to ~1e-4 of pi
+# after exponentiation and the normalising constant).  A kept-set difference is
+# excused when the block's uniform lies within SIP_BAND * pi of the oracle's pi; the
+# offsets of blocks kept by both agree to SIP_BIAS_TOL (|d ln pi| ~ |d pi / pi|).
+SIP_BAND = 1e-3
+SIP_BIAS_TOL = 2e-3
+
+
+def compare_sip(rp_g: np.ndarray, ci_g: np.ndarray, cb_g: np.ndarray, keep, pi, u, nB: int):
+    """(differing blocks, unexcused differences, max offset error on common blocks)."""
+    gmask = check_csr(rp_g, ci_g, nB)
+    diff = gmask != keep
+    unexcused = int((diff & ~(np.abs(u - pi) <= SIP_BAND * pi)).sum())
+    rows = np.repeat(np.arange(len(rp_g) - 1), np.diff(rp_g))
+    both = keep[rows, ci_g[:len(rows)]]
+    ref = -np.log(pi[rows, ci_g[:len(rows)]])
+    berr = float(np.abs(cb_g[:len(rows)][both] - ref[both]).max()) if both.any() else 0.0
+    return int(diff.sum()), unexcused, berr
 
 
 def sample_rows(wl: Workload, thr: np.ndarray, n_heads=2, n_blocks=32, seed=1):

@@ -208,3 +208,45 @@ def test_backward_rejects_before_launch():
     assert call(dk=A + 4) == B.SPARSE_ATTN_INVALID_ARGUMENT
     assert call(cc=-1) == B.SPARSE_ATTN_INVALID_ARGUMENT
     assert call(wsb=wsb - 1) == B.SPARSE_ATTN_WORKSPACE
+
+
+def test_forward_biased_rejects_before_launch():
+    f = B.lib().sparse_attn_forward_biased
+    s = _shape()
+    wsb = B.sparse_attn_workspace_size(s)
+
+    def call(shape=None, cb=A, cc=100, ws=A, w=None):
+        return f(ctypes.byref(shape or s), A, A, A, A, A, cb, cc, A, None, ws, wsb if w is None else w, None)
+    assert call(shape=_shape(dtype="f32")) == B.SPARSE_ATTN_UNSUPPORTED
+    assert call(cb=None) == B.SPARSE_ATTN_INVALID_ARGUMENT            # offsets needed for a non-empty list
+    assert call(cb=A + 2) == B.SPARSE_ATTN_INVALID_ARGUMENT           # misaligned
+    assert call(cc=-1) == B.SPARSE_ATTN_INVALID_ARGUMENT
+    assert call(w=16) == B.SPARSE_ATTN_WORKSPACE
+
+
+def _sip(shape, budget=48.0, q=A, k=A, rp=A, ci=A, cb=A, cap=None, wsb=None):
+    params = B.SipParams(budget, 7)
+    cap = B.sparse_attn_csr_capacity(shape) if cap is None else cap
+    wsb = B.sparse_attn_workspace_size(shape) if wsb is None else wsb
+    return B.lib().sparse_attn_select_sip(ctypes.byref(shape), ctypes.byref(params), q, k, rp, ci, cb, cap, A, wsb,
+                                          None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(budget=0.0), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(budget=-3.0), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(budget=float("nan")), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(budget=float("inf")), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(cb=None), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(cb=A + 2), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(q=None), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(cap=10), B.SPARSE_ATTN_CAPACITY),
+    (dict(wsb=1024), B.SPARSE_ATTN_WORKSPACE),
+])
+def test_select_sip_rejects_before_launch(kw, status):
+    assert _sip(_shape(), **kw) == status
+
+
+def test_select_sip_rejects_fp32_and_too_many_blocks():
+    assert _sip(_shape(dtype="f32")) == B.SPARSE_ATTN_UNSUPPORTED
+    assert _sip(_shape(heads=1, grid=(65, 64, 64))) == B.SPARSE_ATTN_UNSUPPORTED

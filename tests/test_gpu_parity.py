@@ -219,6 +219,92 @@ def test_full_csr_is_the_dense_block_list():
     assert err <= P.TOL["bf16"] and lerr <= P.LSE_TOL["bf16"]
 
 
+def _random_offsets(rng, n):
+    """-ln(pi) for inclusion probabilities spread over (0.02, 1]: offsets from 0 to ~3.9."""
+    return -np.log(rng.uniform(0.02, 1.0, n))
+
+
+@pytest.mark.parametrize("d,grid,reading", [(128, (3, 4, 5), "A"), (64, (2, 3, 5), "B")])
+def test_biased_forward_matches_oracle(d, grid, reading):
+    """Attention with a logit offset per block-list entry against the oracle with the
+    same offsets, on a random block list with empty rows."""
+    wl = small_workload("bias", 2, d, grid, "bf16", seed=51)
+    q, k, v, _ = make_inputs(wl, reading)
+    qd, kd, vd = P.to_device(q, k, v)
+    rows, nB = wl.heads * wl.blocks, wl.blocks
+    rng = np.random.default_rng(52)
+    mask = rng.random((rows, nB)) < 0.4
+    mask[[3, nB + 5]] = False
+    orp, oci = oracle.csr_from_mask(mask)
+    bias = _random_offsets(rng, len(oci)).astype(np.float32)
+    out, lse = P.gpu_forward_biased(wl, qd, kd, vd, orp, oci, bias)
+    err, lerr = P.compare_rows(wl, out, lse, q, k, v, orp, oci, np.arange(rows), bias=bias.astype(np.float64))
+    print(f"biased forward d={d}: max|err| {err:.3e} lse {lerr:.3e}", flush=True)
+    assert err <= P.TOL["bf16"] and lerr <= P.LSE_TOL["bf16"]
+    # zero offsets against the plain kernel: the offset path keeps its running max in
+    # log2 units, so the lazy max may move at another tile and P round differently in
+    # bf16; both stay within the output bound of each other
+    out0, lse0 = P.gpu_forward_biased(wl, qd, kd, vd, orp, oci, np.zeros(len(oci), np.float32))
+    out1, lse1 = P.gpu_forward(wl, qd, kd, vd, orp, oci)
+    assert float((out0.float() - out1.float()).abs().max()) <= P.TOL["bf16"]
+    assert torch.equal(torch.isinf(lse0), torch.isinf(lse1))
+    fin = torch.isfinite(lse1)
+    assert float((lse0[fin] - lse1[fin]).abs().max()) <= P.LSE_TOL["bf16"]
+
+
+def test_biased_forward_split_rows():
+    """Offsets on rows long enough to be split into pieces and merged."""
+    wl = small_workload("biassplit", 2, 128, (7, 3, 5), "bf16", seed=53)
+    q, k, v, _ = make_inputs(wl, "A")
+    qd, kd, vd = P.to_device(q, k, v)
+    nB = wl.blocks
+    rows = wl.heads * nB
+    rng = np.random.default_rng(54)
+    mask = np.zeros((rows, nB), dtype=bool)
+    mask[np.arange(rows), np.arange(rows) % nB] = True
+    long_rows = [0, 1, 50, nB + 51]
+    mask[long_rows] = rng.random((len(long_rows), nB)) < 0.97
+    orp, oci = oracle.csr_from_mask(mask)
+    bias = _random_offsets(rng, len(oci)).astype(np.float32)
+    out, lse = P.gpu_forward_biased(wl, qd, kd, vd, orp, oci, bias)
+    err, lerr = P.compare_rows(wl, out, lse, q, k, v, orp, oci, np.arange(rows), bias=bias.astype(np.float64))
+    assert err <= P.TOL["bf16"] and lerr <= P.LSE_TOL["bf16"]
+
+
+@pytest.mark.parametrize("d,grid,budget,reading", [(128, (3, 4, 5), 6.5, "A"), (64, (4, 4, 5), 3.0, "B"),
+                                                   (128, (2, 8, 18), 40.0, "A")])
+def test_sip_selection_matches_oracle(d, grid, budget, reading):
+    """Sampled block lists and their offsets against the oracle (differences only where
+    a block's uniform lies within the stated band of its inclusion probability)."""
+    from oracle import sip
+    wl = small_workload("sip", 2, d, grid, "bf16", seed=55)
+    q, k, _, _ = make_inputs(wl, reading)
+    qd, kd = P.to_device(q, k)
+    shape = P.shape_for(wl)
+    rp, ci, cb = B.sparse_attn_select_sip(shape, qd, kd, budget, seed=1234)
+    torch.cuda.synchronize()
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    nnz = int(rp_h[-1])
+    keep, _, _, _, pi, u = sip.select_sip(q, k, wl.heads, budget, seed=1234)
+    ndiff, unexcused, berr = P.compare_sip(rp_h, ci[:nnz].cpu().numpy(), cb[:nnz].cpu().numpy(), keep, pi, u,
+                                           wl.blocks)
+    print(f"sip d={d} nB={wl.blocks} budget={budget}: kept {nnz} (oracle {int(keep.sum())}), "
+          f"differing {ndiff}, unexcused {unexcused}, max offset err {berr:.2e}", flush=True)
+    assert unexcused == 0 and berr <= P.SIP_BIAS_TOL
+
+
+def test_sip_budget_of_all_blocks_keeps_everything():
+    wl = small_workload("sipall", 1, 64, (2, 3, 3), "bf16", seed=57)
+    q, k, _, _ = make_inputs(wl, "A")
+    qd, kd = P.to_device(q, k)
+    rp, ci, cb = B.sparse_attn_select_sip(P.shape_for(wl), qd, kd, float(wl.blocks), seed=3)
+    torch.cuda.synchronize()
+    nB, rows = wl.blocks, wl.heads * wl.blocks
+    assert np.array_equal(rp.cpu().numpy(), np.arange(rows + 1) * nB)
+    assert np.array_equal(ci[:rows * nB].cpu().numpy(), np.tile(np.arange(nB), rows))
+    assert torch.all(cb[:rows * nB] == 0)
+
+
 def _backward_case(wl, reading, mask=None, seed=0):
     q, k, v, _ = make_inputs(wl, reading)
     qd, kd, vd = P.to_device(q, k, v)

@@ -112,3 +112,36 @@ def _backward_sampled(wl, shape, qd, kd, vd, lse, q32, k32, v32, orp, oci, sampl
         errs.append(float(np.abs(g - ref).max() / np.abs(ref).max()))
     _log(f"backward, {len(rows_s)} sampled rows: rel err dq {errs[0]:.3e} dk {errs[1]:.3e} dv {errs[2]:.3e}")
     assert max(errs[:2]) <= P.BWD_TOL_DQK and errs[2] <= P.BWD_TOL_DV
+
+
+@pytest.mark.timeout(600)
+def test_sip_full_size_480p():
+    """Sampling with inclusion probabilities at full size (budget of 10% of the key
+    blocks, as sparse as the AB-Attention page's runs): every row's sampled set and
+    offsets against the oracle, and the offset forward on sampled rows under the
+    oracle's list."""
+    from oracle import sip
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    wl = WORKLOADS["wan13b_480p"]
+    budget = 0.1 * wl.blocks
+    _log(f"[case] SIP {wl.name} budget {budget}")
+    q, k, v, thr = make_inputs(wl, "A")
+    qd, kd, vd = P.to_device(q, k, v)
+    shape = P.shape_for(wl)
+    rp, ci, cb = B.sparse_attn_select_sip(shape, qd, kd, budget, seed=2026)
+    torch.cuda.synchronize()
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    nnz = int(rp_h[-1])
+    q32, k32, v32 = (t.float().numpy() for t in (q, k, v))
+    keep, orp, oci, obias, pi, u = sip.select_sip(q32, k32, wl.heads, budget, seed=2026)
+    ndiff, unexcused, berr = P.compare_sip(rp_h, ci[:nnz].cpu().numpy(), cb[:nnz].cpu().numpy(), keep, pi, u,
+                                           wl.blocks)
+    _log(f"SIP: kept {nnz} (oracle {int(keep.sum())}, expected {budget * wl.heads * wl.blocks:.0f}), "
+         f"differing {ndiff}, unexcused {unexcused}, max offset err {berr:.2e}")
+    assert unexcused == 0 and berr <= P.SIP_BIAS_TOL
+    sample = P.sample_rows(wl, thr)
+    out, lse = P.gpu_forward_biased(wl, qd, kd, vd, orp, oci, obias.astype(np.float32))
+    err, lerr = P.compare_rows(wl, out, lse, q32, k32, v32, orp, oci, sample, bias=obias)
+    _log(f"offset forward (oracle list), {len(sample)} sampled blocks: max|err|={err:.3e} lse {lerr:.3e}")
+    assert err <= P.TOL[wl.dtype] and lerr <= P.LSE_TOL[wl.dtype]
