@@ -623,3 +623,41 @@ def test_inclusion_probabilities_from_scores_shift_and_range():
     assert np.allclose(a, sip.inclusion_probabilities(np.exp(s - s.max(1, keepdims=True)) /
                                                       np.exp(s - s.max(1, keepdims=True)).sum(1, keepdims=True), 7.0),
                        rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- DynamicRad radial window
+
+def test_radial_radii_by_hand():
+    from oracle import radial
+    # r0 = 4, gamma = 1/2: widths 4, 2, 1, 0.5, 0.25, ... -> radii 4, 2, 1, then skipped
+    assert radial.radii(6, 4.0, 0.5, 0).tolist() == [4, 2, 1, -1, -1, -1]
+    # lambda = 2: skipped frames at even distance keep the co-located block
+    assert radial.radii(7, 4.0, 0.5, 2).tolist() == [4, 2, 1, -1, 0, -1, 0]
+    # r0 below 1: the own frame still keeps its block
+    assert radial.radii(3, 0.5, 0.9, 0).tolist() == [0, -1, -1]
+    # gamma = 1: a constant radius
+    assert radial.radii(4, 2.7, 1.0, 0).tolist() == [2, 2, 2, 2]
+
+
+def test_radial_with_gamma_one_is_a_box_window():
+    """gamma = 1, lambda = 0: the clipped box over all frames and +-floor(r0) tiles,
+    counted by the brute-force window counter."""
+    from oracle import radial
+    grid = (3, 5, 6)
+    m = radial.radial_mask(grid, 1.5, 1.0, 0)
+    for i in range(m.shape[0]):
+        assert m[i].sum() == brute.window_count(i, grid, (grid[0], 1, 1))
+
+
+def test_radial_counts_closed_form_and_symmetry():
+    """An interior block of a large grid keeps (2R(0)+1)^2 + 2 sum_{dt>0} (2R(dt)+1)^2
+    blocks over the frames with R >= 0; the mask is symmetric."""
+    from oracle import radial
+    grid = (9, 13, 13)
+    r0, g, lam = 5.0, 0.6, 3
+    m = radial.radial_mask(grid, r0, g, lam)
+    R = radial.radii(grid[0], r0, g, lam)
+    centre = 4 * 13 * 13 + 6 * 13 + 6
+    want = (2 * R[0] + 1) ** 2 + 2 * sum((2 * R[dt] + 1) ** 2 for dt in range(1, 5) if R[dt] >= 0)
+    assert m[centre].sum() == want
+    assert np.array_equal(m, m.T)
