@@ -35,6 +35,7 @@ EXPORTED = (
     "sparse_attn_forward",
     "sparse_attn_forward_biased",
     "sparse_attn_mask_to_csr",
+    "sparse_attn_radial_csr",
     "sparse_attn_backward",
     "sparse_attn_full_csr",
     "sparse_attn_to_tiles",
@@ -63,6 +64,10 @@ class SelectParams(ctypes.Structure):
         ("head_thresholds", ctypes.POINTER(ctypes.c_float)),
         ("win_t", ctypes.c_int32), ("win_h", ctypes.c_int32), ("win_w", ctypes.c_int32),
     ]
+
+
+class RadialParams(ctypes.Structure):
+    _fields_ = [("r0", ctypes.c_float), ("gamma", ctypes.c_float), ("lambda_", ctypes.c_int32)]
 
 
 class SipParams(ctypes.Structure):
@@ -101,6 +106,8 @@ def lib():
         L.sparse_attn_forward_biased.restype = ctypes.c_int32
         L.sparse_attn_mask_to_csr.argtypes = [SP, P, P, P, I64, P, I64, P]
         L.sparse_attn_mask_to_csr.restype = ctypes.c_int32
+        L.sparse_attn_radial_csr.argtypes = [SP, ctypes.POINTER(RadialParams), P, P, I64, P, I64, P]
+        L.sparse_attn_radial_csr.restype = ctypes.c_int32
         L.sparse_attn_backward.argtypes = [SP, P, P, P, P, P, P, P, P, I64, P, P, P, P, P, I64, P]
         L.sparse_attn_backward.restype = ctypes.c_int32
         L.sparse_attn_full_csr.argtypes = [SP, P, P, I64, P]
@@ -253,6 +260,18 @@ def sparse_attn_forward_biased(shape: Shape, q, k, v, row_ptr, col_idx, col_bias
                                           _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "sparse_attn_forward_biased")
     return (out, lse) if (want_lse or lse is not None) else out
+
+
+def sparse_attn_radial_csr(shape: Shape, r0: float, gamma: float, lam: int = 0, buffers: Optional[Buffers] = None,
+                           device=None, stream=None):
+    """DynamicRad's radial window as a block list -> (row_ptr, col_idx)."""
+    bufs = buffers or alloc_buffers(shape, device or "cuda")
+    params = RadialParams(float(r0), float(gamma), int(lam))
+    st = lib().sparse_attn_radial_csr(ctypes.byref(shape), ctypes.byref(params), _ptr(bufs.row_ptr),
+                                      _ptr(bufs.col_idx), bufs.col_idx.numel(), _ptr(bufs.workspace),
+                                      bufs.workspace.numel(), _stream(stream))
+    _check(st, "sparse_attn_radial_csr")
+    return bufs.row_ptr, bufs.col_idx
 
 
 def sparse_attn_mask_to_csr(shape: Shape, block_mask, buffers: Optional[Buffers] = None, stream=None):

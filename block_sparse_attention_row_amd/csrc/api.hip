@@ -363,6 +363,38 @@ int32_t sparse_attn_mask_to_csr(const sparse_attn_shape *shape, const uint8_t *b
     return emit_csr(d, bits, counts, groups, row_ptr, col_idx, s);
 }
 
+int32_t sparse_attn_radial_csr(const sparse_attn_shape *shape, const sparse_attn_radial_params *params,
+                               int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity, void *workspace,
+                               int64_t workspace_bytes, void *stream) {
+    Dims d;
+    int32_t st = check_shape(shape, &d);
+    if (st) return st;
+    if (!params || !row_ptr || !col_idx || !workspace) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (!aligned(row_ptr, 4) || !aligned(col_idx, 4) || !aligned(workspace, 16)) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (!(params->r0 >= 0.f) || !(params->r0 < INFINITY) || !(params->gamma > 0.f) || !(params->gamma <= 1.f) ||
+        params->lambda < 0)
+        return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (d.nB > kSelectMaxBlocks) return SPARSE_ATTN_UNSUPPORTED;   // the radius table sits in LDS
+    if (col_capacity < d.rows * d.nB) return SPARSE_ATTN_CAPACITY;
+    const Layout L = layout(d);
+    if (workspace_bytes < L.total) return SPARSE_ATTN_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    uint64_t *bits = (uint64_t *)(ws + L.bits);
+    int32_t *counts = (int32_t *)(ws + L.counts);
+    int32_t *groups = (int32_t *)(ws + L.groups);
+    RadialArgs a;
+    a.nT = d.nT;
+    a.nTy = d.nTy;
+    a.nTx = d.nTx;
+    a.r0 = params->r0;
+    a.gamma = params->gamma;
+    a.lambda = params->lambda;
+    if (launch_radial_bits(a, d.B * d.H, (int32_t)d.nB, (int32_t)d.nW, bits, counts, groups, s))
+        return SPARSE_ATTN_HIP_ERROR;
+    return emit_csr(d, bits, counts, groups, row_ptr, col_idx, s);
+}
+
 int32_t sparse_attn_backward(const sparse_attn_shape *shape, const void *q, const void *k, const void *v,
                              const void *out, const float *lse, const void *dout, const int32_t *row_ptr,
                              const int32_t *col_idx, int64_t col_count, void *dq, void *dk, void *dv,

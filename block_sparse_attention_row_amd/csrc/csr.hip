@@ -43,6 +43,62 @@ __global__ __launch_bounds__(1024) void mask_bits_kernel(const uint8_t *__restri
     }
 }
 
+// DynamicRad's radial window (DynamicRad page, section "Methodologie : DynamicRad",
+// items A and B) as row bitmasks + counts, in the layout of mask_bits_kernel.  The
+// width of frame distance dt is r0 * gamma^dt, formed by dt successive fp64
+// multiplications; radius floor(width) while the width is at least 1; a frame below
+// that is skipped unless lambda >= 1 divides dt, which keeps its co-located block;
+// the own frame keeps radius max(floor(r0), 0).  Key block j is kept iff the
+// Chebyshev distance in tiles is within the radius of |t_i - t_j|.
+__global__ __launch_bounds__(1024) void radial_bits_kernel(RadialArgs a, int32_t nB, int32_t nW,
+                                                           int32_t groups_per_head, uint64_t *__restrict__ bits,
+                                                           int32_t *__restrict__ counts,
+                                                           int32_t *__restrict__ group_sums) {
+    __shared__ int32_t wave_count[kGroupRows];
+    __shared__ int32_t radius[kSelectMaxBlocks];      // per frame distance (frames <= blocks)
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int dt = threadIdx.x; dt < a.nT; dt += blockDim.x) {
+        double w = (double)a.r0;
+        for (int u = 0; u < dt; ++u) w = w * (double)a.gamma;
+        int r;
+        if (dt == 0) r = w >= 1.0 ? (int)floor(fmin(w, 1e6)) : 0;
+        else if (w >= 1.0) r = (int)floor(fmin(w, 1e6));
+        else r = (a.lambda >= 1 && dt % a.lambda == 0) ? 0 : -1;
+        radius[dt] = r;
+    }
+    __syncthreads();
+    const int64_t G = blockIdx.x;
+    const int64_t bh = G / groups_per_head;
+    const int i = (int)(G % groups_per_head) * kGroupRows + wave;
+    const int nTyx = a.nTy * a.nTx;
+    int count = 0;
+    if (i < nB) {
+        const int64_t row = bh * nB + i;
+        const int ti = i / nTyx, yi = (i / a.nTx) % a.nTy, xi = i % a.nTx;
+        for (int e = 0; e < nW; ++e) {
+            const int j = 64 * e + lane;
+            bool keep = false;
+            if (j < nB) {
+                const int tj = j / nTyx, yj = (j / a.nTx) % a.nTy, xj = j % a.nTx;
+                const int ds = max(abs(yj - yi), abs(xj - xi));
+                keep = ds <= radius[abs(tj - ti)];
+            }
+            const uint64_t b = __ballot(keep);
+            count += __popcll(b);
+            if (lane == 0) bits[row * nW + e] = b;
+        }
+        if (lane == 0) counts[row] = count;
+    }
+    if (lane == 0) wave_count[wave] = count;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t t = 0;
+#pragma unroll
+        for (int w = 0; w < kGroupRows; ++w) t += wave_count[w];
+        group_sums[G] = t;
+    }
+}
+
 // Prefix and compaction in one pass, one wave per row; workgroup b owns rows
 // 4b .. 4b+3.  The offset of a row is the sum of the totals of the row groups before
 // its own plus the counts of the rows of its group before it: the workgroup sums the
@@ -119,6 +175,14 @@ int launch_mask_bits(const uint8_t *mask, int64_t bh, int32_t nB, int32_t nW, ui
     const int32_t gph = (nB + kGroupRows - 1) / kGroupRows;
     mask_bits_kernel<<<dim3((unsigned)(bh * gph)), dim3(64 * kGroupRows), 0, s>>>(mask, nB, nW, gph, bits, counts,
                                                                                  group_sums);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_radial_bits(const RadialArgs &a, int64_t bh, int32_t nB, int32_t nW, uint64_t *bits, int32_t *counts,
+                       int32_t *group_sums, hipStream_t s) {
+    const int32_t gph = (nB + kGroupRows - 1) / kGroupRows;
+    radial_bits_kernel<<<dim3((unsigned)(bh * gph)), dim3(64 * kGroupRows), 0, s>>>(a, nB, nW, gph, bits, counts,
+                                                                                   group_sums);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -113,6 +113,13 @@ int launch_select_sip(const SelectArgs &a, int d, hipStream_t s);
 int launch_mask_bits(const uint8_t *mask, int64_t bh, int32_t nB, int32_t nW, uint64_t *bits, int32_t *counts,
                      int32_t *group_sums, hipStream_t s);
 int launch_full_csr(int64_t rows, int32_t nB, int32_t *row_ptr, int32_t *col_idx, hipStream_t s);
+struct RadialArgs {
+    int32_t nT, nTy, nTx;     // block grid
+    float r0, gamma;          // width at frame distance 0, decay per frame
+    int32_t lambda;           // long-range sampling period (0: off)
+};
+int launch_radial_bits(const RadialArgs &a, int64_t bh, int32_t nB, int32_t nW, uint64_t *bits, int32_t *counts,
+                       int32_t *group_sums, hipStream_t s);
 int launch_emit(const uint64_t *bits, const int32_t *counts, const int32_t *group_sums, int64_t rows, int32_t nB,
                 int32_t nW, int32_t *row_ptr, int32_t *col_idx, hipStream_t s);
 // Backward (bf16).

@@ -220,6 +220,31 @@ int32_t sparse_attn_mask_to_csr(const sparse_attn_shape *shape, const uint8_t *b
                                 int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity,
                                 void *workspace, int64_t workspace_bytes, void *stream);
 
+/* Parameters of sparse_attn_radial_csr (block-grid units). */
+typedef struct {
+    float r0;        /* window width at frame distance 0, finite, >= 0 */
+    float gamma;     /* width decay per frame of distance, in (0, 1] */
+    int32_t lambda;  /* every lambda-th frame of distance keeps its co-located block; 0 = off */
+} sparse_attn_radial_params;
+
+/*
+ * DynamicRad's radial window (DynamicRad page, section "Methodologie :
+ * DynamicRad", items A and B: a shared candidate set from the decay of
+ * attention with spatial and temporal distance, a decay factor and a long-range
+ * factor) as a CSR block list, the same for every (batch, head).  Width at
+ * frame distance dt: r0 * gamma^dt (dt successive fp64 multiplications);
+ * radius floor(width) while the width is >= 1; a frame whose width is below 1 is
+ * skipped unless lambda >= 1 divides dt, which keeps the co-located block; the
+ * own frame always keeps radius max(floor(r0), 0).  Key block j is kept for
+ * query block i iff max(|dy|, |dx|) in tiles is within the radius of |dt|.
+ *
+ *   row_ptr, col_idx, col_capacity, workspace: as in sparse_attn_mask_to_csr.
+ * nB <= 4096 (SPARSE_ATTN_UNSUPPORTED otherwise).
+ */
+int32_t sparse_attn_radial_csr(const sparse_attn_shape *shape, const sparse_attn_radial_params *params,
+                               int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity,
+                               void *workspace, int64_t workspace_bytes, void *stream);
+
 /*
  * Backward of sparse_attn_forward (bf16 only and nB <= 4096; SPARSE_ATTN_UNSUPPORTED
  * otherwise):

@@ -250,3 +250,22 @@ def test_select_sip_rejects_before_launch(kw, status):
 def test_select_sip_rejects_fp32_and_too_many_blocks():
     assert _sip(_shape(dtype="f32")) == B.SPARSE_ATTN_UNSUPPORTED
     assert _sip(_shape(heads=1, grid=(65, 64, 64))) == B.SPARSE_ATTN_UNSUPPORTED
+
+
+@pytest.mark.parametrize("r0,gamma,lam,status", [
+    (-1.0, 0.5, 0, B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (float("inf"), 0.5, 0, B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (float("nan"), 0.5, 0, B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (2.0, 0.0, 0, B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (2.0, 1.5, 0, B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (2.0, 0.5, -1, B.SPARSE_ATTN_INVALID_ARGUMENT),
+])
+def test_radial_csr_rejects_before_launch(r0, gamma, lam, status):
+    s = _shape()
+    p = B.RadialParams(r0, gamma, lam)
+    cap = B.sparse_attn_csr_capacity(s)
+    assert B.lib().sparse_attn_radial_csr(ctypes.byref(s), ctypes.byref(p), A, A, cap, A,
+                                          B.sparse_attn_workspace_size(s), None) == status
+    ok = B.RadialParams(2.0, 0.5, 0)
+    assert B.lib().sparse_attn_radial_csr(ctypes.byref(s), ctypes.byref(ok), A, A, cap - 1, A,
+                                          B.sparse_attn_workspace_size(s), None) == B.SPARSE_ATTN_CAPACITY

@@ -445,3 +445,24 @@ def test_tiny_workload_full():
     err, lerr = P.compare_rows(wl, out, lse, q, k, v, orp, oci, np.arange(wl.blocks))
     print(f"tiny forward err={err:.3e} lse={lerr:.3e}", flush=True)
     assert err <= P.TOL["f32"] and lerr <= P.LSE_TOL["f32"]
+
+
+@pytest.mark.parametrize("grid,tile,heads,r0,gamma,lam", [
+    ((4, 16, 24), (1, 8, 8), 2, 2.5, 0.6, 0),
+    ((6, 24, 16), (1, 8, 8), 1, 3.0, 0.5, 2),
+    ((20, 32, 48), (1, 8, 8), 3, 4.0, 0.7, 3),      # the 480p block grid
+    ((32, 48, 80), (1, 8, 8), 1, 6.0, 0.8, 4),      # the HunyuanVideo-like block grid
+    ((8, 16, 16), (2, 4, 8), 2, 0.5, 0.9, 1),       # r0 < 1: own block and every frame's co-located one
+])
+def test_radial_csr_matches_oracle(grid, tile, heads, r0, gamma, lam):
+    """DynamicRad's radial window: bit-exact against the oracle's mask, for every head."""
+    from oracle import radial
+    shape = B.make_shape(1, heads, 128, grid, "bf16", 0.0, tile)
+    rp, ci = B.sparse_attn_radial_csr(shape, r0, gamma, lam)
+    torch.cuda.synchronize()
+    block_grid = (grid[0] // tile[0], grid[1] // tile[1], grid[2] // tile[2])
+    m = radial.radial_mask(block_grid, r0, gamma, lam)
+    orp, oci = oracle.csr_from_mask(np.tile(m, (heads, 1)))
+    nnz = int(orp[-1])
+    assert np.array_equal(rp.cpu().numpy(), orp.astype(np.int32))
+    assert np.array_equal(ci[:nnz].cpu().numpy(), oci)
