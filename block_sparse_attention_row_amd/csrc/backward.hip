@@ -7,13 +7,12 @@
 // upstream gradient dO:
 //   dV = P^T dO,  dP = dO V^T,  D_n = dO_n . O_n,  dS = P o (dP - D),
 //   dQ = scale dS K,  dK = scale dS^T Q.
-// Three passes, each writing whole output rows from one workgroup (no atomics, a
+// Two passes, each writing whole output rows from one workgroup (no atomics, a
 // fixed summation order):
-//   dQ  a pair of query blocks walks its CSR rows (key tiles streamed into LDS):
-//       S^T = K Q^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T;
-//   dV  a pair of key blocks walks the transposed list (query tiles streamed):
-//       S = Q K^T, P, then dV^T += dO^T P;
-//   dK  likewise: S, P, dP = dO V^T, dS, then dK^T += Q^T dS.
+//   dQ      a pair of query blocks walks its CSR rows (key tiles streamed into LDS):
+//           S^T = K Q^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T;
+//   dV, dK  a pair of key blocks walks the transposed list (query tiles streamed):
+//           S = Q K^T, P, dP = dO V^T, dS, then dV^T += dO^T P and dK^T += Q^T dS.
 // Each is the forward's tile machinery with other operands: the streamed tile is
 // the A operand of the scores and, read transposed, of the output product; the
 // pair's own rows sit in registers as the B operand.  The transposed list (for
@@ -142,11 +141,14 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// The three gradient passes.
-enum BwdMode { kDQ = 0, kDV = 1, kDK = 2 };
+// The gradient passes: dQ over the block rows, dV and dK together over the transposed list.
+enum BwdMode { kDQ = 0, kDKV = 1 };
 
+// kDKV: dV and dK in one walk of the transposed list (S and dP once per tile, four
+// products; 8% faster at d = 128 than a dV pass and a dK pass that each form S);
+// at d = 128 its two d-wide accumulators take one wave per SIMD.
 template <int D, int MODE>
-__global__ __launch_bounds__(256, 2) void bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, MODE == kDKV && D == 128 ? 1 : 2) void bwd_kernel(BwdArgs a) {
     using G = TileGeo<D>;
     constexpr int ROWB = G::ROWB, SLOTS = G::SLOTS, RPI = G::RPI, IPW = G::IPW, NDT = G::NDT, TILEB = G::TILEB;
     __shared__ __attribute__((aligned(1024))) char T1s[2 * TILEB];
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int cq = 0; cq < D / 16; ++cq) {
         f1[cq] = has_row ? *reinterpret_cast<const bf16x8 *>(o1 + 16 * cq + 8 * hh) : bf16x8{};
-        f2[cq] = (MODE != kDV && has_row) ? *reinterpret_cast<const bf16x8 *>(o2 + 16 * cq + 8 * hh) : bf16x8{};
+        f2[cq] = has_row ? *reinterpret_cast<const bf16x8 *>(o2 + 16 * cq + 8 * hh) : bf16x8{};
     }
     const float lse2_q = (MODE == kDQ && has_row) ? a.lse2[own] : 0.f;
     const float d_q = (MODE == kDQ && has_row) ? a.dn[own] : 0.f;
@@ -251,11 +253,14 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdArgs a) {
             dma16(ax0 + buf * 1024, aux_voff, (const char *)a.lse2 + (bh * N + col * 64) * 4);
     };
 
-    f32x16 acc[NDT];
+    f32x16 acc[NDT], acc2[NDT];     // acc2: dK of the fused pass
 #pragma unroll
     for (int i = 0; i < NDT; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+        for (int v = 0; v < 16; ++v) {
+            acc[i][v] = 0.f;
+            acc2[i][v] = 0.f;
+        }
 
     int col0, col1;
     bool mine0, mine1;
@@ -273,8 +278,8 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdArgs a) {
         const float *ax = aux[BJ];
         f32x16 s[2], dp[2];
         tile_scores<D>(T1, f1, l32, hh, s);
-        if (MODE != kDV) tile_scores<D>(T2, f2, l32, hh, dp);
-        bf16x8 pf[4];
+        tile_scores<D>(T2, f2, l32, hh, dp);
+        bf16x8 pf[4], pf2[4];           // pf2: dS of the fused pass (pf holds P there)
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
             f32x4 lo_l, hi_l, lo_d, hi_d;   // lse2, D of the 8 streamed rows of this chunk (dV, dK)
@@ -284,23 +289,27 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdArgs a) {
                 lo_d = *reinterpret_cast<const f32x4 *>(ax + 64 + 16 * kc + 4 * hh);
                 hi_d = *reinterpret_cast<const f32x4 *>(ax + 64 + 16 * kc + 8 + 4 * hh);
             }
-            f32x8 pv;
+            f32x8 pv, pv2;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float x = s[kc >> 1][8 * (kc & 1) + e];
                 const float l2 = MODE == kDQ ? lse2_q : (e < 4 ? lo_l[e] : hi_l[e - 4]);
                 const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -l2));
-                if (MODE == kDV) {
+                const float dd = MODE == kDQ ? d_q : (e < 4 ? lo_d[e] : hi_d[e - 4]);
+                const float ds = p * (dp[kc >> 1][8 * (kc & 1) + e] - dd);
+                if (MODE == kDKV) {
                     pv[e] = p;
+                    pv2[e] = ds;
                 } else {
-                    const float dd = MODE == kDQ ? d_q : (e < 4 ? lo_d[e] : hi_d[e - 4]);
-                    pv[e] = p * (dp[kc >> 1][8 * (kc & 1) + e] - dd);
+                    pv[e] = ds;
                 }
             }
             pf[kc] = __builtin_convertvector(pv, bf16x8);
+            if (MODE == kDKV) pf2[kc] = __builtin_convertvector(pv2, bf16x8);
         }
         // dQ^T += K^T dS^T (K tile read transposed); dV^T += dO^T P; dK^T += Q^T dS
-        tile_pv<D>(MODE == kDV ? T2 : T1, pf, lane, acc);
+        tile_pv<D>(MODE == kDKV ? T2 : T1, pf, lane, acc);
+        if (MODE == kDKV) tile_pv<D>(T1, pf2, lane, acc2);
     };
     while (col0 != kNone) {
         step(std::integral_constant<int, 0>{});
@@ -314,7 +323,7 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdArgs a) {
 
     if (!has_row) return;
     // lane owns row 32 half + l32 of its block, d = 32 dt + 8 rr + 4 hh + {0..3}
-    const float mult = MODE == kDV ? 1.f : a.scale;
+    const float mult = MODE == kDKV ? 1.f : a.scale;
     __bf16 *og = (__bf16 *)a.grad + own * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -325,6 +334,18 @@ __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdArgs a) {
             for (int e = 0; e < 4; ++e) w[e] = acc[dt][4 * rr + e] * mult;
             *reinterpret_cast<bf16x4 *>(og + 32 * dt + 8 * rr + 4 * hh) = __builtin_convertvector(w, bf16x4);
         }
+    if constexpr (MODE == kDKV) {
+        __bf16 *og2 = (__bf16 *)a.grad2 + own * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                f32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = acc2[dt][4 * rr + e] * a.scale;
+                *reinterpret_cast<bf16x4 *>(og2 + 32 * dt + 8 * rr + 4 * hh) = __builtin_convertvector(w, bf16x4);
+            }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -351,18 +372,16 @@ int launch_backward(const BwdLaunch &L, hipStream_t s) {
     csc.ptr = L.col_ptr;
     csc.idx = L.t_idx;
     csc.idx_count = L.col_count;
-    BwdArgs cdv = csc, cdk = csc;
-    cdv.grad = L.dv;
-    cdk.grad = L.dk;
     const dim3 g((unsigned)L.args.n_pairs), b(256);
+    BwdArgs cdkv = csc;
+    cdkv.grad = L.dv;
+    cdkv.grad2 = L.dk;
     if (L.d == 128) {
         bwd_kernel<128, kDQ><<<g, b, 0, s>>>(csr);
-        bwd_kernel<128, kDV><<<g, b, 0, s>>>(cdv);
-        bwd_kernel<128, kDK><<<g, b, 0, s>>>(cdk);
+        bwd_kernel<128, kDKV><<<g, b, 0, s>>>(cdkv);
     } else {
         bwd_kernel<64, kDQ><<<g, b, 0, s>>>(csr);
-        bwd_kernel<64, kDV><<<g, b, 0, s>>>(cdv);
-        bwd_kernel<64, kDK><<<g, b, 0, s>>>(cdk);
+        bwd_kernel<64, kDKV><<<g, b, 0, s>>>(cdkv);
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

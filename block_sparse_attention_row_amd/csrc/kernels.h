@@ -129,12 +129,13 @@ struct BwdArgs {
     const int32_t *ptr, *idx;     // block list walked: CSR (dQ) or its transpose (dV, dK)
     int64_t idx_count;            // entries of idx
     void *grad;                   // the gradient this pass writes, bf16 [B, H, N, d]
+    void *grad2;                  // second gradient of the fused dV + dK pass (dK; grad is dV)
     int64_t n_pairs;              // B*H*ceil(nB/2) pairs of blocks
     int32_t pairs_per_head, nB;
     float scale_log2, scale;
 };
 struct BwdLaunch {
-    BwdArgs args;                 // fields common to the three passes
+    BwdArgs args;                 // fields common to the gradient passes
     const void *out;
     const float *lse;
     float *lse2, *dn;             // workspace
