@@ -661,3 +661,75 @@ def test_radial_counts_closed_form_and_symmetry():
     want = (2 * R[0] + 1) ** 2 + 2 * sum((2 * R[dt] + 1) ** 2 for dt in range(1, 5) if R[dt] >= 0)
     assert m[centre].sum() == want
     assert np.array_equal(m, m.T)
+
+
+# ---------------------------------------------------------------- intra-block clustering selector (IBCS)
+
+def test_kmeans_recovers_separated_clusters():
+    """Eight tight, well separated groups (sizes 4 .. 32) laid out so that the start
+    positions n*c/8 fall in distinct groups: centroids are the group means and the
+    weights their shares after the first round."""
+    from oracle import ibcs
+    rng = np.random.default_rng(40)
+    sizes = [16] * 8
+    centres = rng.normal(scale=50.0, size=(8, 6))
+    x = np.concatenate([centres[c] + 0.01 * rng.normal(size=(sizes[c], 6)) for c in range(8)])
+    mu, w, gap = ibcs.kmeans(x)
+    starts = np.cumsum([0] + sizes[:-1])
+    for c in range(8):
+        assert np.allclose(mu[c], x[starts[c]:starts[c] + sizes[c]].mean(axis=0), rtol=0, atol=1e-12)
+    assert np.allclose(w, np.array(sizes) / sum(sizes))
+    assert gap > 0.9
+
+
+def test_kmeans_identical_points_and_ties():
+    """All queries equal: every distance ties, everything goes to cluster 0 (lower
+    index), the empty clusters keep their (equal) starting centroids."""
+    from oracle import ibcs
+    x = np.tile(np.array([1.0, -2.0, 0.5]), (128, 1))
+    mu, w, gap = ibcs.kmeans(x)
+    assert np.array_equal(w, np.eye(8)[0]) and np.allclose(mu, x[0]) and gap == 0.0
+
+
+def test_ibcs_reduces_to_nabla_when_a_block_is_constant():
+    """Identical queries inside each 128-token block: one cluster of weight 1 whose
+    centroid is the block mean, so p~ is the softmax of the pooled scores (formed
+    here from the raw tokens, by brute force)."""
+    from oracle import ibcs
+    rng = np.random.default_rng(41)
+    nB, d = 5, 8
+    base = rng.normal(size=(3, d))
+    q = np.repeat(base, 128, axis=0)[: nB * 64][None, None].astype(np.float32)
+    k = rng.normal(size=(1, 1, nB * 64, d)).astype(np.float32)
+    pt, gaps = ibcs.mixture_scores(q, k, 1)
+    kbar = k[0, 0].astype(np.float64).reshape(nB, 64, d).mean(axis=1)
+    for i in range(nB):
+        s = base[i // 2].astype(np.float32).astype(np.float64) @ kbar.T / math.sqrt(d)
+        ref = np.exp(s - s.max()) / np.exp(s - s.max()).sum()
+        assert np.allclose(pt[i], ref, rtol=0, atol=1e-14)
+
+
+def test_ibcs_rows_are_distributions_shared_by_the_pair():
+    from oracle import ibcs
+    rng = np.random.default_rng(42)
+    q = rng.normal(size=(1, 2, 5 * 64, 16)).astype(np.float32)
+    k = rng.normal(size=(1, 2, 5 * 64, 16)).astype(np.float32)
+    pt, gaps = ibcs.mixture_scores(q, k, 2)
+    assert np.allclose(pt.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    for h in range(2):
+        for p in range(2):
+            assert np.array_equal(pt[h * 5 + 2 * p], pt[h * 5 + 2 * p + 1])
+    assert gaps.shape == (2, 3)
+
+
+def test_cdf_keep_against_pairwise_brute_force():
+    from oracle import ibcs
+    rng = np.random.default_rng(43)
+    p = rng.gamma(0.5, size=(30, 17))
+    p[:, 3] = p[:, 5]                               # exact ties
+    p /= p.sum(axis=1, keepdims=True)
+    for thr in (0.3, 0.8, 0.95):
+        keep = ibcs.cdf_keep(p, thr)
+        for r in range(p.shape[0]):
+            assert np.array_equal(keep[r], brute.cdf_keep_pairwise(p[r], thr).astype(bool))
+    assert ibcs.cdf_keep(p, 1.0).all()
