@@ -56,6 +56,7 @@ def parse():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-CSR reference forward")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-sip", action="store_true", help="skip the sampling-selection timing")
+    ap.add_argument("--no-ibcs", action="store_true", help="skip the clustering-selector timing")
     ap.add_argument("--sip-budget", type=float, default=0.1,
                     help="sampling selection: expected kept key blocks per row, as a fraction of the blocks")
     ap.add_argument("--no-select-timing", action="store_true", help="skip the separate selection timing")
@@ -304,6 +305,33 @@ def main():
                "forward_frac_bf16_peak": round(sip_flops / (fw_ms_med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del sbufs, cbias
 
+    # clustering selector (AB-Attention's IBCS) with NABLA's CDF cut, same threshold
+    ibcs = None
+    if wl.dtype == "bf16" and not args.no_ibcs:
+        ibufs = B.alloc_buffers(shape, dev)
+
+        def ibcs_select():
+            return B.sparse_attn_select_ibcs(shape, qd, kd, threshold=float(np.float32(wl.threshold)),
+                                             head_thresholds=head_thr, window=wl.window, buffers=ibufs,
+                                             stream=stream)
+        irp, _ = ibcs_select()
+        torch.cuda.synchronize()
+        innz = int(irp[-1].item())
+        ims = []
+        for _ in range(5):
+            flush.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            ibcs_select()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ims.append(a.elapsed_time(b))
+        ims_med = sorted(ims)[len(ims) // 2]
+        ibytes = 2 * qd.numel() * elt + 4 * (rows + 1) + 4 * innz
+        ibcs = {"ms": round(ims_med, 4), "nnz_tiles": innz, "GB_s": round(ibytes / (ims_med * 1e-3) / 1e9, 1),
+                "frac_hbm_peak": round(ibytes / (ims_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        del ibufs
+
     # dense reference: the same forward kernel over the full CSR (every tile kept)
     full_bufs = B.alloc_buffers(shape, dev)
     full_rp, full_ci = B.sparse_attn_full_csr(shape, full_bufs, stream=stream)
@@ -395,6 +423,8 @@ def main():
         rec["backward"] = bwd
     if sip is not None:
         rec["sip"] = sip
+    if ibcs is not None:
+        rec["ibcs"] = ibcs
     if sched is not None:
         rec["denoise_schedule"] = sched
     if not args.no_cpu_baseline:

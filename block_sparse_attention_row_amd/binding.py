@@ -32,6 +32,7 @@ EXPORTED = (
     "sparse_attn_workspace_size",
     "sparse_attn_select",
     "sparse_attn_select_sip",
+    "sparse_attn_select_ibcs",
     "sparse_attn_forward",
     "sparse_attn_forward_biased",
     "sparse_attn_mask_to_csr",
@@ -100,6 +101,8 @@ def lib():
         L.sparse_attn_select.restype = ctypes.c_int32
         L.sparse_attn_select_sip.argtypes = [SP, ctypes.POINTER(SipParams), P, P, P, P, P, I64, P, I64, P]
         L.sparse_attn_select_sip.restype = ctypes.c_int32
+        L.sparse_attn_select_ibcs.argtypes = [SP, ctypes.POINTER(SelectParams), P, P, P, P, I64, P, I64, P]
+        L.sparse_attn_select_ibcs.restype = ctypes.c_int32
         L.sparse_attn_forward.argtypes = [SP, P, P, P, P, P, I64, P, P, P, I64, P]
         L.sparse_attn_forward.restype = ctypes.c_int32
         L.sparse_attn_forward_biased.argtypes = [SP, P, P, P, P, P, P, I64, P, P, P, I64, P]
@@ -203,6 +206,23 @@ def sparse_attn_select(shape: Shape, q, k, threshold: float = 0.9,
                                   _ptr(bufs.row_ptr), _ptr(bufs.col_idx), bufs.col_idx.numel(),
                                   _ptr(bufs.workspace), bufs.workspace.numel(), _stream(stream))
     _check(st, "sparse_attn_select")
+    return bufs.row_ptr, bufs.col_idx
+
+
+def sparse_attn_select_ibcs(shape: Shape, q, k, threshold: float = 0.9,
+                            head_thresholds: Optional[Sequence[float]] = None, window=(-1, -1, -1),
+                            buffers: Optional[Buffers] = None, stream=None) -> Tuple[object, object]:
+    """The clustering selector with NABLA's CDF cut; returns (row_ptr, col_idx)."""
+    bufs = buffers or alloc_buffers(shape, q.device)
+    ht = None
+    if head_thresholds is not None:
+        arr = (ctypes.c_float * shape.heads)(*[float(x) for x in head_thresholds])
+        ht = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
+    params = SelectParams(float(threshold), ht, *(int(w) for w in window))
+    st = lib().sparse_attn_select_ibcs(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k),
+                                       _ptr(bufs.row_ptr), _ptr(bufs.col_idx), bufs.col_idx.numel(),
+                                       _ptr(bufs.workspace), bufs.workspace.numel(), _stream(stream))
+    _check(st, "sparse_attn_select_ibcs")
     return bufs.row_ptr, bufs.col_idx
 
 

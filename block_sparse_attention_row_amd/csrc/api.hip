@@ -67,8 +67,19 @@ struct Layout {
     int64_t bits, counts, groups;                                        // external masks
     int64_t items, plan_counts, pair_flag, merge, part_o, part_lse;      // attention row splitting
     int64_t col_ptr, lse2, dn;                                           // backward
+    int64_t mix;                                                         // clustering selector rows
     int64_t total;
 };
+
+// The clustering selector keeps one fp32 row per pair of query blocks; heads are
+// processed in chunks so that the rows take at most about 64 MiB.
+int64_t ibcs_row_floats(const Dims &d) { return ((d.nB + 1) / 2) * d.nBp; }
+int64_t ibcs_heads_per_launch(const Dims &d) {
+    const int64_t per_head = 4 * ibcs_row_floats(d);
+    int64_t h = ((int64_t)64 << 20) / (per_head > 0 ? per_head : 1);
+    h = h < 1 ? 1 : h;
+    return h < d.B * d.H ? h : d.B * d.H;
+}
 
 Layout layout(const Dims &d) {
     Layout l;
@@ -106,6 +117,8 @@ Layout layout(const Dims &d) {
     off = align_up(off + 4 * d.rows * 64, kAlign);
     l.dn = off;
     off = align_up(off + 4 * d.rows * 64, kAlign);
+    l.mix = off;
+    off = align_up(off + 4 * ibcs_heads_per_launch(d) * ibcs_row_floats(d), kAlign);
     l.total = off;
     return l;
 }
@@ -339,6 +352,93 @@ int32_t sparse_attn_select_sip(const sparse_attn_shape *shape, const sparse_attn
     a.seed = params->seed;
     a.col_bias = col_bias;
     if (launch_select_sip(a, (int)d.D, s)) return SPARSE_ATTN_HIP_ERROR;
+    return SPARSE_ATTN_OK;
+}
+
+int32_t sparse_attn_select_ibcs(const sparse_attn_shape *shape, const sparse_attn_select_params *params,
+                                const void *q, const void *k, int32_t *row_ptr, int32_t *col_idx,
+                                int64_t col_capacity, void *workspace, int64_t workspace_bytes, void *stream) {
+    Dims d;
+    int32_t st = check_shape(shape, &d);
+    if (st) return st;
+    if (shape->dtype != SPARSE_ATTN_BF16) return SPARSE_ATTN_UNSUPPORTED;
+    if (!params || !q || !k || !row_ptr || !col_idx || !workspace) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(row_ptr, 4) || !aligned(col_idx, 4) ||
+        !aligned(workspace, 16))
+        return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (d.nBp > kSelectMaxBlocks) return SPARSE_ATTN_UNSUPPORTED;   // a row is held in registers
+    if (bad_thr(params->threshold)) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (params->head_thresholds)
+        for (int64_t h = 0; h < d.H; ++h)
+            if (bad_thr(params->head_thresholds[h])) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (col_capacity < d.rows * d.nB) return SPARSE_ATTN_CAPACITY;
+    const Layout L = layout(d);
+    if (workspace_bytes < L.total) return SPARSE_ATTN_WORKSPACE;
+
+    hipStream_t s = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    float *thr = (float *)(ws + L.thr);
+    __bf16 *kbar = (__bf16 *)(ws + L.kbar);
+    uint64_t *status = (uint64_t *)(ws + L.status);
+    uint32_t *ticket = (uint32_t *)(ws + L.ticket);
+    float *rows = (float *)(ws + L.mix);
+    PoolSide side;
+    side.n_thr = (int32_t)(d.H < ThrChunk::kMax ? d.H : ThrChunk::kMax);
+    for (int i = 0; i < side.n_thr; ++i)
+        side.thr.v[i] = params->head_thresholds ? params->head_thresholds[i] : params->threshold;
+    side.thr_dst = thr;
+    side.status = status;
+    side.n_status = n_groups(d);
+    side.ticket = ticket;
+    for (int64_t h0 = ThrChunk::kMax; h0 < d.H; h0 += ThrChunk::kMax) {
+        float tmp[ThrChunk::kMax];
+        const int n = (int)((d.H - h0) < ThrChunk::kMax ? (d.H - h0) : ThrChunk::kMax);
+        for (int i = 0; i < n; ++i)
+            tmp[i] = params->head_thresholds ? params->head_thresholds[h0 + i] : params->threshold;
+        if (launch_fill_thresholds(tmp, n, thr + h0, s)) return SPARSE_ATTN_HIP_ERROR;
+    }
+    if (launch_pool_keys(k, kbar, d.B * d.H * d.nB, shape->dtype, (int)d.D, side, s)) return SPARSE_ATTN_HIP_ERROR;
+
+    IbcsArgs m;
+    m.q = (const __bf16 *)q;
+    m.kbar = kbar;
+    m.rows = rows;
+    m.nB = (int32_t)d.nB;
+    m.nBp = (int32_t)d.nBp;
+    m.pairs_per_head = (int32_t)((d.nB + 1) / 2);
+    m.scale_log2 = effective_scale(shape) * kLog2e;
+    SelectArgs a = {};
+    a.q = q;
+    a.kbar = kbar;
+    a.thr = thr;
+    a.status = status;
+    a.ticket = ticket;
+    a.row_ptr = row_ptr;
+    a.col_idx = col_idx;
+    a.rows = d.rows;
+    a.groups_per_head = (int32_t)groups_per_head(d);
+    a.n_groups = n_groups(d);
+    a.H = (int32_t)d.H;
+    a.nB = (int32_t)d.nB;
+    a.nBp = (int32_t)d.nBp;
+    a.nTy = d.nTy;
+    a.nTx = d.nTx;
+    a.window = params->win_t >= 0 && params->win_h >= 0 && params->win_w >= 0;
+    a.wt = params->win_t;
+    a.wh = params->win_h;
+    a.ww = params->win_w;
+    a.scale_log2 = m.scale_log2;
+    a.mix_rows = rows;
+    // heads in chunks: the rows of a chunk, then its groups' cut (tickets and
+    // look-back words continue across the chunks, so the CSR offsets chain through)
+    const int64_t BH = d.B * d.H, hpl = ibcs_heads_per_launch(d);
+    for (int64_t h0 = 0; h0 < BH; h0 += hpl) {
+        const int64_t nh = BH - h0 < hpl ? BH - h0 : hpl;
+        m.head0 = h0;
+        a.head0 = h0;
+        if (launch_ibcs_mix(m, nh, (int)d.D, s)) return SPARSE_ATTN_HIP_ERROR;
+        if (launch_select_rows(a, nh * groups_per_head(d), s)) return SPARSE_ATTN_HIP_ERROR;
+    }
     return SPARSE_ATTN_OK;
 }
 

@@ -56,7 +56,21 @@ struct SelectArgs {
     float budget;
     uint64_t seed;
     float *col_bias;
+    // the clustering selector (IBCS): log2 of the mixture rows of the heads
+    // [head0, head0 + heads), one row per query-block pair
+    const float *mix_rows;
+    int64_t head0;
 };
+constexpr int kIbcsClusters = 8, kIbcsIters = 4;
+struct IbcsArgs {
+    const __bf16 *q;          // [BH*N][D] queries (bf16, tile-major)
+    const __bf16 *kbar;       // [BH*nB][2][D] key block means (hi | lo)
+    float *rows;              // [heads][pairs][nBp]: log2 of the mixture row of each pair
+    int64_t head0;            // first (batch, head) of this launch
+    int32_t nB, nBp, pairs_per_head;
+    float scale_log2;
+};
+int launch_ibcs_mix(const IbcsArgs &a, int64_t heads, int d, hipStream_t s);
 
 // Row splitting of the bf16 attention.  Pairs of query blocks whose rows hold more
 // than L tiles are cut into pieces of at most about L tiles (by position in each
@@ -110,6 +124,7 @@ int launch_pool_keys(const void *k, __bf16 *kbar, int64_t nblocks, int dtype, in
 int launch_fill_thresholds(const float *host_thr, int n, float *dst, hipStream_t s);
 int launch_select(const SelectArgs &a, int d, int dtype, hipStream_t s);
 int launch_select_sip(const SelectArgs &a, int d, hipStream_t s);
+int launch_select_rows(const SelectArgs &a, int64_t groups, hipStream_t s);
 int launch_mask_bits(const uint8_t *mask, int64_t bh, int32_t nB, int32_t nW, uint64_t *bits, int32_t *counts,
                      int32_t *group_sums, hipStream_t s);
 int launch_full_csr(int64_t rows, int32_t nB, int32_t *row_ptr, int32_t *col_idx, hipStream_t s);

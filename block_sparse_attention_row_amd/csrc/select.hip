@@ -394,7 +394,9 @@ __device__ __forceinline__ int64_t group_lookback(uint64_t *status, int64_t g, i
 // and each wave writes its row's row_ptr entry and kept columns.
 //
 // MODE 0: NABLA's CDF cut; MODE 1: sampling with inclusion probabilities, which also
-// writes the offset -ln(pi) of every kept block to col_bias.
+// writes the offset -ln(pi) of every kept block to col_bias; MODE 2: NABLA's CDF cut
+// on rows given in log2 units (mix_rows, one per pair of query blocks: the
+// clustering selector), with no pooling or scores of its own.
 template <typename T, int D, int NE, int MODE>
 __global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
     static_assert(NE % 4 == 0 && NE <= 64, "NE: register row length in 64-key words");
@@ -425,6 +427,15 @@ __global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
 
     const int ii = lane & 15, kq = lane >> 4;
     float s[NE];
+    if constexpr (MODE == 2) {
+        const int64_t pr = ((int64_t)bh - a.head0) * ((a.nB + 1) / 2) + (i0 + wave) / 2;
+        const float *src = a.mix_rows + pr * a.nBp;
+#pragma unroll
+        for (int c = 0; c < NE; ++c) {
+            const int j = 64 * c + lane;
+            s[c] = (wave < nrows && j < a.nB) ? src[j] : -INFINITY;
+        }
+    } else {
     bf16x8 kh[2][KB], kl[2][KB];
     // keys past nB read row 0 (in bounds); their scores land on padding columns
     auto load_k = [&](int cc, int slot) {
@@ -478,11 +489,12 @@ __global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
             s[4 * cc + t] = kSelChunk * cc + 64 * t + lane < a.nB ? v : -INFINITY;   // padding keys
         }
     }
+    }
     uint64_t word = 0;
     int32_t count = 0;
     float sigma = 0.f, tcap = 0.f;
     if (wave < nrows) {
-        if constexpr (MODE == 0) select_cut<NE>(a, s, hist_all, i0 + wave, thr, lane, word, count);
+        if constexpr (MODE != 1) select_cut<NE>(a, s, hist_all, i0 + wave, thr, lane, word, count);
         else sip_cut<NE>(a, s, (int64_t)bh * a.nB + i0 + wave, lane, word, count, sigma, tcap);
     }
     if (lane == 0) wave_count[wave] = count;
@@ -509,7 +521,7 @@ __global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
     const int cnt = __popcll(word);
     const int excl = wave_incl_scan_i(cnt, lane) - cnt;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    if constexpr (MODE == 0) {
+    if constexpr (MODE != 1) {
         for (int e = 0; e < nvc; ++e) {
             const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)word, e);
             const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(word >> 32), e);
@@ -584,6 +596,168 @@ int launch_select(const SelectArgs &a, int d, int dtype, hipStream_t s) {
         launch_select_nch<float, 128, 1>(a, nch, s);
     else
         launch_select_nch<float, 64, 1>(a, nch, s);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ---------------------------------------------------------------------------
+// The clustering selector's rows (AB-Attention page, section "Les trois techniques
+// d'AB-Attention", first item): one workgroup (8 waves) per pair of query blocks
+// (128 tokens; an odd last block alone).  The pair's queries go to LDS; Lloyd's
+// k-means with 8 clusters and 4 rounds starts from the queries at positions
+// n*c/8: each round assigns every query (one lane each, its query in registers) to
+// the nearest centroid by squared distance, ties to the lower cluster, then moves
+// each centroid to the mean of its queries in query order (an empty cluster keeps
+// its centroid).  The weights are the last assignment's shares.  Wave c then
+// scores centroid c on every key block mean, S = mu_c . Kbar_j * scale (fp32, key
+// means as hi + lo), forms w_c softmax(S) and adds it to the pair's row in LDS, in
+// cluster order; the row is stored in log2 units for the cut.
+template <int D>
+__global__ __launch_bounds__(512) void ibcs_mix_kernel(IbcsArgs a) {
+    constexpr int K = kIbcsClusters;
+    __shared__ __attribute__((aligned(16))) __bf16 qs[128 * D];
+    __shared__ float mu[K * D];
+    __shared__ int32_t asg[128];
+    __shared__ int32_t cnt[K];
+    __shared__ float row[kSelectMaxBlocks];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t pr = blockIdx.x;                                 // pair within this launch
+    const int64_t bh = a.head0 + pr / a.pairs_per_head;
+    const int p = (int)(pr % a.pairs_per_head);
+    const int n = 2 * p + 1 < a.nB ? 128 : 64;
+    const int64_t N = (int64_t)a.nB * 64;
+    const __bf16 *qg = a.q + (bh * N + (int64_t)128 * p) * D;
+    for (int e = t; e < n * D / 8; e += blockDim.x)
+        reinterpret_cast<uint4 *>(qs)[e] = reinterpret_cast<const uint4 *>(qg)[e];
+    __syncthreads();
+    for (int e = t; e < K * D; e += blockDim.x) mu[e] = (float)qs[((n * (e / D)) / K) * D + e % D];
+    float x[D];                                                     // this lane's query (t < n)
+    if (t < n) {
+#pragma unroll
+        for (int dd = 0; dd < D; ++dd) x[dd] = (float)qs[t * D + dd];
+    }
+    __syncthreads();
+    for (int it = 0; it < kIbcsIters; ++it) {
+        if (t < n) {
+            int best = 0;
+            float bd = INFINITY;
+#pragma unroll 1
+            for (int c = 0; c < K; ++c) {
+                float d2 = 0.f;
+#pragma unroll
+                for (int dd = 0; dd < D; ++dd) {
+                    const float df = x[dd] - mu[c * D + dd];
+                    d2 = __builtin_fmaf(df, df, d2);
+                }
+                if (d2 < bd) {
+                    bd = d2;
+                    best = c;
+                }
+            }
+            asg[t] = best;
+        }
+        __syncthreads();
+        // new centroids: thread (c, dd) sums its cluster's queries in query order
+        float nv[(K * D + 511) / 512];
+        int nc[(K * D + 511) / 512];
+#pragma unroll
+        for (int u = 0; u < (K * D + 511) / 512; ++u) {
+            const int e = t + 512 * u;
+            nv[u] = 0.f;
+            nc[u] = 0;
+            if (e < K * D) {
+                const int c = e / D, dd = e % D;
+                float sum = 0.f;
+                int m = 0;
+                for (int q = 0; q < n; ++q)
+                    if (asg[q] == c) {
+                        sum += (float)qs[q * D + dd];
+                        ++m;
+                    }
+                nv[u] = m > 0 ? sum / (float)m : mu[e];
+                nc[u] = m;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < (K * D + 511) / 512; ++u) {
+            const int e = t + 512 * u;
+            if (e < K * D) {
+                mu[e] = nv[u];
+                if (e % D == 0) cnt[e / D] = nc[u];
+            }
+        }
+        __syncthreads();
+    }
+    // wave c: softmax of centroid c over all key blocks (an online pass for the max
+    // and the sum, then a second pass that adds the weighted terms), added to the
+    // pair's row in cluster order
+    const int c = wave;
+    const float wgt = (float)cnt[c] / (float)n;
+    const __bf16 *kb = a.kbar + (bh * a.nB) * (2 * D);
+    const int nvc = a.nBp >> 6;
+    auto score = [&](int j) {
+        const __bf16 *kr = kb + (int64_t)j * (2 * D);
+        float acc = 0.f;
+#pragma unroll
+        for (int d0 = 0; d0 < D; d0 += 8) {
+            const bf16x8 h = *reinterpret_cast<const bf16x8 *>(kr + d0);
+            const bf16x8 l = *reinterpret_cast<const bf16x8 *>(kr + D + d0);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc = __builtin_fmaf(mu[c * D + d0 + u], (float)h[u] + (float)l[u], acc);
+        }
+        return acc * a.scale_log2;
+    };
+    float mx = -INFINITY, z = 0.f;
+    for (int e = 0; e < nvc; ++e) {
+        const int j = 64 * e + lane;
+        if (j < a.nB) {
+            const float v = score(j);
+            if (v > mx) {
+                z = z * __builtin_amdgcn_exp2f(mx - v) + 1.f;
+                mx = v;
+            } else {
+                z += __builtin_amdgcn_exp2f(v - mx);
+            }
+        }
+    }
+    const float gmx = wave_max_u(mx);
+    z = wave_sum_u(mx == -INFINITY ? 0.f : z * __builtin_amdgcn_exp2f(mx - gmx));
+    const float f = wgt / z;
+    for (int cc = 0; cc < K; ++cc) {
+        if (c == cc)
+            for (int e = 0; e < nvc; ++e) {
+                const int j = 64 * e + lane;
+                if (j < a.nB) row[j] = (cc == 0 ? 0.f : row[j]) + f * __builtin_amdgcn_exp2f(score(j) - gmx);
+            }
+        __syncthreads();
+    }
+    float *dst = a.rows + pr * a.nBp;
+    for (int j = t; j < a.nB; j += blockDim.x) dst[j] = row[j] > 0.f ? __log2f(row[j]) : -INFINITY;
+}
+
+int launch_ibcs_mix(const IbcsArgs &a, int64_t heads, int d, hipStream_t s) {
+    const dim3 g((unsigned)(heads * a.pairs_per_head)), b(512);
+    if (d == 128)
+        ibcs_mix_kernel<128><<<g, b, 0, s>>>(a);
+    else
+        ibcs_mix_kernel<64><<<g, b, 0, s>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <int NCH> static void launch_rows_nch(const SelectArgs &a, int64_t groups, int nch, hipStream_t s) {
+    if constexpr (NCH <= kSelectMaxBlocks / kSelChunk) {
+        if (nch == NCH) {
+            select_emit_kernel<__bf16, 128, 4 * NCH, 2>
+                <<<dim3((unsigned)groups), dim3(64 * kSelRows), select_lds_bytes<128>(), s>>>(a);
+            return;
+        }
+        launch_rows_nch<NCH + 1>(a, groups, nch, s);
+    }
+}
+
+int launch_select_rows(const SelectArgs &a, int64_t groups, hipStream_t s) {
+    if (a.nBp > kSelectMaxBlocks) return -1;
+    launch_rows_nch<1>(a, groups, (a.nB + kSelChunk - 1) / kSelChunk, s);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

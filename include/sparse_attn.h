@@ -160,6 +160,26 @@ int32_t sparse_attn_select_sip(const sparse_attn_shape *shape, const sparse_attn
                                int64_t workspace_bytes, void *stream);
 
 /*
+ * Block selection with the intra-block clustering selector, the first technique
+ * of AB-Attention (AB-Attention page, section "Les trois techniques
+ * d'AB-Attention"), cut by NABLA's CDF rule.  Each pair of query blocks
+ * (2p, 2p+1: 128 tokens; an odd last block alone) is clustered by Lloyd's
+ * k-means, 8 clusters and 4 rounds, started from the queries at positions n*c/8
+ * (ties to the lower cluster; an empty cluster keeps its centroid), with weights
+ * equal to the last assignment's shares.  Key block j scores
+ * p~_j = sum_c w_c softmax_j(mu_c . Kbar_j * scale) over all key blocks, and both
+ * blocks of the pair keep the blocks NABLA's CDF rule keeps on p~ (threshold,
+ * per-head thresholds and window as in sparse_attn_select).
+ *
+ *   Arguments as in sparse_attn_select.  bf16 only, nB <= 4096
+ *   (SPARSE_ATTN_UNSUPPORTED otherwise).
+ */
+int32_t sparse_attn_select_ibcs(const sparse_attn_shape *shape, const sparse_attn_select_params *params,
+                                const void *q, const void *k, int32_t *row_ptr, int32_t *col_idx,
+                                int64_t col_capacity, void *workspace, int64_t workspace_bytes,
+                                void *stream);
+
+/*
  * Block-sparse attention forward over a CSR block list (from
  * sparse_attn_select, sparse_attn_mask_to_csr or the caller).
  *

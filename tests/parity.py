@@ -202,6 +202,40 @@ def compare_sip(rp_g: np.ndarray, ci_g: np.ndarray, cb_g: np.ndarray, keep, pi, 
     return int(diff.sum()), unexcused, berr
 
 
+# Clustering selector: the GPU forms centroids as fp32 means and p~ with fp32
+# exponentials of fp32 dot products (key means as hi + lo bf16), so p~ carries
+# about 1e-5 relative error against the fp64 oracle.  The squared distances of the
+# assignment carry ~1e-6 relative error (fp32 sums of 128 squares, centroids that
+# are fp32 means); a pair whose k-means came within IBCS_GAP (relative) of an
+# assignment tie in the oracle may cluster differently: its rows are checked for
+# validity only.  Elsewhere a kept-set
+# difference is excused at the CDF boundary: the mass before the block within
+# IBCS_BAND_E of the threshold, or its p~ within IBCS_BAND_P (relative) of the
+# crossing block's.
+IBCS_GAP = 1e-5
+IBCS_BAND_E = 1e-4
+IBCS_BAND_P = 1e-4
+
+
+def compare_cdf_rows(gmask: np.ndarray, keep: np.ndarray, p: np.ndarray, thr_rows: np.ndarray,
+                     skip: np.ndarray):
+    """(differing blocks, excused, unexcused) over the rows not in `skip`; window-free."""
+    ndiff = nexc = nunx = 0
+    for r in np.nonzero((gmask != keep).any(axis=1) & ~skip)[0]:
+        order = np.argsort(-p[r], kind="stable")
+        before = np.empty(p.shape[1])
+        before[order] = np.concatenate([[0.0], np.cumsum(p[r][order])[:-1]])
+        kept = order[keep[r][order]]
+        pc = p[r][kept[-1]] if len(kept) else 0.0
+        for j in np.nonzero(gmask[r] != keep[r])[0]:
+            ndiff += 1
+            if abs(before[j] - thr_rows[r]) <= IBCS_BAND_E or abs(p[r][j] - pc) <= IBCS_BAND_P * pc:
+                nexc += 1
+            else:
+                nunx += 1
+    return ndiff, nexc, nunx
+
+
 def sample_rows(wl: Workload, thr: np.ndarray, n_heads=2, n_blocks=32, seed=1):
     rng = np.random.default_rng(seed)
     if wl.head_threshold_range is not None:

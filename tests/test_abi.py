@@ -68,6 +68,8 @@ def test_capacity_and_workspace_formulas():
     expect = al(expect + 4 * (rows + 1))                  # backward: transposed row pointers
     expect = al(expect + 4 * rows * 64)                   # backward: lse in log2 units
     expect = al(expect + 4 * rows * 64)                   # backward: dO . O
+    per_head = 4 * ((nB + 1) // 2) * nbp                  # clustering selector: a row per query-block pair
+    expect = al(expect + min(12, max(1, (64 << 20) // per_head)) * per_head)
     assert B.sparse_attn_workspace_size(s) == expect
 
 
@@ -269,3 +271,18 @@ def test_radial_csr_rejects_before_launch(r0, gamma, lam, status):
     ok = B.RadialParams(2.0, 0.5, 0)
     assert B.lib().sparse_attn_radial_csr(ctypes.byref(s), ctypes.byref(ok), A, A, cap - 1, A,
                                           B.sparse_attn_workspace_size(s), None) == B.SPARSE_ATTN_CAPACITY
+
+
+def test_select_ibcs_rejects_before_launch():
+    f = B.lib().sparse_attn_select_ibcs
+    s = _shape()
+    cap = B.sparse_attn_csr_capacity(s)
+    wsb = B.sparse_attn_workspace_size(s)
+    ok = B.SelectParams(0.9, None, -1, -1, -1)
+    assert f(ctypes.byref(_shape(dtype="f32")), ctypes.byref(ok), A, A, A, A, cap, A, wsb, None) == \
+        B.SPARSE_ATTN_UNSUPPORTED
+    bad = B.SelectParams(0.0, None, -1, -1, -1)
+    assert f(ctypes.byref(s), ctypes.byref(bad), A, A, A, A, cap, A, wsb, None) == B.SPARSE_ATTN_INVALID_ARGUMENT
+    assert f(ctypes.byref(s), ctypes.byref(ok), A, A, A, A, cap - 1, A, wsb, None) == B.SPARSE_ATTN_CAPACITY
+    assert f(ctypes.byref(s), ctypes.byref(ok), A, A, A, A, cap, A, wsb - 1, None) == B.SPARSE_ATTN_WORKSPACE
+    assert f(ctypes.byref(s), ctypes.byref(ok), None, A, A, A, cap, A, wsb, None) == B.SPARSE_ATTN_INVALID_ARGUMENT

@@ -305,6 +305,37 @@ def test_sip_budget_of_all_blocks_keeps_everything():
     assert torch.all(cb[:rows * nB] == 0)
 
 
+@pytest.mark.parametrize("d,grid,thr,reading", [(128, (3, 4, 5), 0.8, "A"), (64, (2, 3, 5), 0.9, "B"),
+                                               (128, (2, 8, 18), 0.7, "A")])
+def test_ibcs_selection_matches_oracle(d, grid, thr, reading):
+    """The clustering selector against the oracle: block lists equal except at the CDF
+    boundary, and pairs with near-tied k-means assignments checked for validity."""
+    from oracle import ibcs
+    wl = small_workload("ibcs", 2, d, grid, "bf16", threshold=thr, seed=61)
+    q, k, _, _ = make_inputs(wl, reading)
+    qd, kd = P.to_device(q, k)
+    rp, ci = B.sparse_attn_select_ibcs(P.shape_for(wl), qd, kd, threshold=thr)
+    torch.cuda.synchronize()
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    gmask = P.check_csr(rp_h, ci[:int(rp_h[-1])].cpu().numpy(), wl.blocks)
+    keep, _, _, pt, gaps = ibcs.select_ibcs(q.float().numpy(), k.float().numpy(), wl.heads, thr)
+    nB = wl.blocks
+    pair_of_row = (np.arange(wl.heads * nB) % nB) // 2 + (np.arange(wl.heads * nB) // nB) * ((nB + 1) // 2)
+    skip = gaps.reshape(-1)[pair_of_row] < P.IBCS_GAP
+    ndiff, nexc, nunx = P.compare_cdf_rows(gmask, keep, pt, np.full(len(keep), thr), skip)
+    near_diff = int((gmask[skip] != keep[skip]).sum())
+    # validity on every row: the kept mass reaches the threshold (on the oracle's p~)
+    mass = (pt * gmask).sum(axis=1)
+    print(f"ibcs d={d} nB={nB}: kept {int(gmask.sum())} (oracle {int(keep.sum())}), differing {ndiff}, "
+          f"excused {nexc}, unexcused {nunx}, near-tie rows {int(skip.sum())} (differing there {near_diff})", flush=True)
+    assert nunx == 0
+    assert np.all(mass >= thr - 1e-3)
+    # both blocks of a pair share the row
+    for r in range(0, wl.heads * nB - 1):
+        if (r % nB) % 2 == 0 and (r % nB) + 1 < nB:
+            assert np.array_equal(gmask[r], gmask[r + 1])
+
+
 def _backward_case(wl, reading, mask=None, seed=0):
     q, k, v, _ = make_inputs(wl, reading)
     qd, kd, vd = P.to_device(q, k, v)

@@ -145,3 +145,30 @@ def test_sip_full_size_480p():
     err, lerr = P.compare_rows(wl, out, lse, q32, k32, v32, orp, oci, sample, bias=obias)
     _log(f"offset forward (oracle list), {len(sample)} sampled blocks: max|err|={err:.3e} lse {lerr:.3e}")
     assert err <= P.TOL[wl.dtype] and lerr <= P.LSE_TOL[wl.dtype]
+
+
+@pytest.mark.timeout(600)
+def test_ibcs_full_size_480p():
+    """The clustering selector at full size (480p grid, threshold 0.9): every row's block
+    list against the oracle under the same comparison rule as the small cases."""
+    from oracle import ibcs
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    wl = WORKLOADS["wan13b_480p"]
+    _log(f"[case] IBCS {wl.name} thr {wl.threshold}")
+    q, k, _, _ = make_inputs(wl, "A")
+    qd, kd = P.to_device(q, k)
+    rp, ci = B.sparse_attn_select_ibcs(P.shape_for(wl), qd, kd, threshold=float(np.float32(wl.threshold)))
+    torch.cuda.synchronize()
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    gmask = P.check_csr(rp_h, ci[:int(rp_h[-1])].cpu().numpy(), wl.blocks)
+    thr = float(np.float32(wl.threshold))
+    keep, _, _, pt, gaps = ibcs.select_ibcs(q.float().numpy(), k.float().numpy(), wl.heads, thr)
+    nB = wl.blocks
+    rows = np.arange(wl.heads * nB)
+    skip = gaps.reshape(-1)[(rows % nB) // 2 + (rows // nB) * ((nB + 1) // 2)] < P.IBCS_GAP
+    ndiff, nexc, nunx = P.compare_cdf_rows(gmask, keep, pt, np.full(len(keep), thr), skip)
+    _log(f"IBCS: kept {int(gmask.sum())} (oracle {int(keep.sum())}), differing {ndiff}, excused {nexc}, "
+         f"unexcused {nunx}, near-tie rows {int(skip.sum())} (differing there {int((gmask[skip] != keep[skip]).sum())})")
+    assert nunx == 0
+    assert np.all((pt * gmask).sum(axis=1) >= thr - 1e-3)
