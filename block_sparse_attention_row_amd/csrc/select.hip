@@ -612,9 +612,11 @@ int launch_select(const SelectArgs &a, int d, int dtype, hipStream_t s) {
 // means as hi + lo), forms w_c softmax(S) and adds it to the pair's row in LDS, in
 // cluster order; the row is stored in log2 units for the cut.
 template <int D>
-__global__ __launch_bounds__(512) void ibcs_mix_kernel(IbcsArgs a) {
+__global__ __launch_bounds__(512, 4) void ibcs_mix_kernel(IbcsArgs a) {
     constexpr int K = kIbcsClusters;
-    __shared__ __attribute__((aligned(16))) __bf16 qs[128 * D];
+    // the pair's queries (128 x D bf16), later the staged key means (64 x (D + 1) words)
+    __shared__ __attribute__((aligned(16))) uint32_t qbuf[64 * (D + 1)];
+    __bf16 *qs = reinterpret_cast<__bf16 *>(qbuf);
     __shared__ float mu[K * D];
     __shared__ int32_t asg[128];
     __shared__ int32_t cnt[K];
@@ -626,14 +628,24 @@ __global__ __launch_bounds__(512) void ibcs_mix_kernel(IbcsArgs a) {
     const int n = 2 * p + 1 < a.nB ? 128 : 64;
     const int64_t N = (int64_t)a.nB * 64;
     const __bf16 *qg = a.q + (bh * N + (int64_t)128 * p) * D;
-    for (int e = t; e < n * D / 8; e += blockDim.x)
-        reinterpret_cast<uint4 *>(qs)[e] = reinterpret_cast<const uint4 *>(qg)[e];
+    {
+        // all of this thread's loads in flight before the stores
+        constexpr int PER = 128 * D / 8 / 512;
+        uint4 tmp[PER];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = t + 512 * u;
+            tmp[u] = e < n * D / 8 ? reinterpret_cast<const uint4 *>(qg)[e] : uint4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < PER; ++u) reinterpret_cast<uint4 *>(qs)[t + 512 * u] = tmp[u];
+    }
     __syncthreads();
     for (int e = t; e < K * D; e += blockDim.x) mu[e] = (float)qs[((n * (e / D)) / K) * D + e % D];
-    float x[D];                                                     // this lane's query (t < n)
+    uint32_t x[D / 2];                                              // this lane's query as bf16 pairs (t < n)
     if (t < n) {
 #pragma unroll
-        for (int dd = 0; dd < D; ++dd) x[dd] = (float)qs[t * D + dd];
+        for (int w = 0; w < D / 2; ++w) x[w] = reinterpret_cast<const uint32_t *>(qs)[t * (D / 2) + w];
     }
     __syncthreads();
     for (int it = 0; it < kIbcsIters; ++it) {
@@ -644,9 +656,10 @@ __global__ __launch_bounds__(512) void ibcs_mix_kernel(IbcsArgs a) {
             for (int c = 0; c < K; ++c) {
                 float d2 = 0.f;
 #pragma unroll
-                for (int dd = 0; dd < D; ++dd) {
-                    const float df = x[dd] - mu[c * D + dd];
-                    d2 = __builtin_fmaf(df, df, d2);
+                for (int w = 0; w < D / 2; ++w) {
+                    const float d0 = bf16_lo(x[w]) - mu[c * D + 2 * w], d1 = bf16_hi(x[w]) - mu[c * D + 2 * w + 1];
+                    d2 = __builtin_fmaf(d0, d0, d2);
+                    d2 = __builtin_fmaf(d1, d1, d2);
                 }
                 if (d2 < bd) {
                     bd = d2;
@@ -668,11 +681,12 @@ __global__ __launch_bounds__(512) void ibcs_mix_kernel(IbcsArgs a) {
                 const int c = e / D, dd = e % D;
                 float sum = 0.f;
                 int m = 0;
-                for (int q = 0; q < n; ++q)
-                    if (asg[q] == c) {
-                        sum += (float)qs[q * D + dd];
-                        ++m;
-                    }
+#pragma unroll 16
+                for (int q = 0; q < n; ++q) {
+                    const bool in = asg[q] == c;
+                    sum += in ? (float)qs[q * D + dd] : 0.f;
+                    m += in ? 1 : 0;
+                }
                 nv[u] = m > 0 ? sum / (float)m : mu[e];
                 nc[u] = m;
             }
@@ -690,28 +704,55 @@ __global__ __launch_bounds__(512) void ibcs_mix_kernel(IbcsArgs a) {
     }
     // wave c: softmax of centroid c over all key blocks (an online pass for the max
     // and the sum, then a second pass that adds the weighted terms), added to the
-    // pair's row in cluster order
+    // pair's row in cluster order.  Key means are staged 64 at a time in LDS with
+    // coalesced loads, rows padded to D/2 + 1 words (hi and lo halves as packed
+    // bf16 pairs) so that the lane-per-key reads hit distinct banks.
     const int c = wave;
     const float wgt = (float)cnt[c] / (float)n;
     const __bf16 *kb = a.kbar + (bh * a.nB) * (2 * D);
+    const float *mc = mu + c * D;                                   // this wave's centroid (LDS, broadcast reads)
+    constexpr int KW = D + 1;                                       // words per staged key (hi|lo pairs + pad)
+    uint32_t *kst = qbuf;                                           // the query buffer is free by now
     const int nvc = a.nBp >> 6;
-    auto score = [&](int j) {
-        const __bf16 *kr = kb + (int64_t)j * (2 * D);
+    auto stage = [&](int e) {
+        // 64 key means = 64 * D words: 16-byte loads, all in flight before the stores
+        constexpr int PER = 64 * D / 4 / 512;
+        const uint4 *src = reinterpret_cast<const uint4 *>(kb + (int64_t)(64 * e) * (2 * D));
+        const int nk = a.nB - 64 * e < 64 ? a.nB - 64 * e : 64;
+        uint4 tmp[PER];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int g4 = t + 512 * u;                            // 16-byte piece: key g4 / (D/4)
+            tmp[u] = g4 < nk * D / 4 ? src[g4] : uint4{0u, 0u, 0u, 0u};
+        }
+        __syncthreads();                                           // the previous stage's readers are done
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int g4 = t + 512 * u, key = g4 / (D / 4), w0 = 4 * (g4 % (D / 4));
+            uint32_t *dst = kst + key * KW + w0;
+            dst[0] = tmp[u].x;
+            dst[1] = tmp[u].y;
+            dst[2] = tmp[u].z;
+            dst[3] = tmp[u].w;
+        }
+        __syncthreads();
+    };
+    auto score = [&](int e) {
+        const uint32_t *kr = kst + lane * KW;
         float acc = 0.f;
 #pragma unroll
-        for (int d0 = 0; d0 < D; d0 += 8) {
-            const bf16x8 h = *reinterpret_cast<const bf16x8 *>(kr + d0);
-            const bf16x8 l = *reinterpret_cast<const bf16x8 *>(kr + D + d0);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) acc = __builtin_fmaf(mu[c * D + d0 + u], (float)h[u] + (float)l[u], acc);
+        for (int dd = 0; dd < D; dd += 2) {
+            const uint32_t h = kr[dd / 2], l = kr[D / 2 + dd / 2];
+            acc = __builtin_fmaf(mc[dd], bf16_lo(h) + bf16_lo(l), acc);
+            acc = __builtin_fmaf(mc[dd + 1], bf16_hi(h) + bf16_hi(l), acc);
         }
         return acc * a.scale_log2;
     };
     float mx = -INFINITY, z = 0.f;
     for (int e = 0; e < nvc; ++e) {
-        const int j = 64 * e + lane;
-        if (j < a.nB) {
-            const float v = score(j);
+        stage(e);
+        if (64 * e + lane < a.nB) {
+            const float v = score(e);
             if (v > mx) {
                 z = z * __builtin_amdgcn_exp2f(mx - v) + 1.f;
                 mx = v;
@@ -723,13 +764,15 @@ __global__ __launch_bounds__(512) void ibcs_mix_kernel(IbcsArgs a) {
     const float gmx = wave_max_u(mx);
     z = wave_sum_u(mx == -INFINITY ? 0.f : z * __builtin_amdgcn_exp2f(mx - gmx));
     const float f = wgt / z;
-    for (int cc = 0; cc < K; ++cc) {
-        if (c == cc)
-            for (int e = 0; e < nvc; ++e) {
-                const int j = 64 * e + lane;
-                if (j < a.nB) row[j] = (cc == 0 ? 0.f : row[j]) + f * __builtin_amdgcn_exp2f(score(j) - gmx);
-            }
-        __syncthreads();
+    // second pass: each wave's weighted terms for the staged keys, added in cluster order
+    for (int e = 0; e < nvc; ++e) {
+        stage(e);
+        const int j = 64 * e + lane;
+        const float term = j < a.nB ? f * __builtin_amdgcn_exp2f(score(e) - gmx) : 0.f;
+        for (int cc = 0; cc < K; ++cc) {
+            if (c == cc && j < a.nB) row[j] = (cc == 0 ? 0.f : row[j]) + term;
+            __syncthreads();
+        }
     }
     float *dst = a.rows + pr * a.nBp;
     for (int j = t; j < a.nB; j += blockDim.x) dst[j] = row[j] > 0.f ? __log2f(row[j]) : -INFINITY;
