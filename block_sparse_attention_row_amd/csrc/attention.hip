@@ -29,34 +29,11 @@
 
 namespace sattn {
 
-// Online-softmax bookkeeping for one tile of raw scores; this lane owns one query.
-// The running max is kept in raw dot-product units and only moved when a new score
-// exceeds it by more than kLazy (in log2 units): in between, P = 2^(s*c - m*c) stays
-// below 2^kLazy and the output needs no rescaling.  The result is the same softmax.
-template <int NDT>
-__device__ __forceinline__ void tile_rescale(const f32x16 *acc_s, float c, float &m_run, float &l_run,
-                                             f32x16 *acc_o) {
-    float mt = fmaxf(acc_s[0][0], acc_s[0][1]);
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int v = (kt == 0 ? 2 : 0); v < 16; v += 2) mt = fmaxf(mt, fmaxf(acc_s[kt][v], acc_s[kt][v + 1]));
-    mt = pair_max(mt);
-    const bool grow = (mt - m_run) * c > kLazy;
-    if (__ballot(grow)) {
-        const float m_new = grow ? mt : m_run;
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < NDT; ++i)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc_o[i][v] *= alpha;
-    }
-}
-
-// The same bookkeeping with a logit offset beta (log2 units) on the whole tile:
-// scores are s*c + beta, and the running max M is kept in log2 units.
+// Online-softmax bookkeeping of the kernel with a logit offset beta (log2 units) on
+// each tile: scores are s*c + beta, this lane owns one query, and the running max M
+// (log2 units) only moves when a tile's max exceeds it by more than kLazy: in
+// between, P = 2^(s*c + beta - M) stays below 2^kLazy and the output needs no
+// rescaling.  The result is the same softmax.
 template <int NDT>
 __device__ __forceinline__ void tile_rescale_biased(const f32x16 *acc_s, float c, float beta, float &M,
                                                     float &l_run, f32x16 *acc_o) {
@@ -92,6 +69,35 @@ __device__ __forceinline__ void tile_probs(const f32x16 *acc_s, float c, float m
         for (int e = 0; e < 4; ++e)
             l_run = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){pf[kc][2 * e], pf[kc][2 * e + 1]}, kOnes2, l_run, false);
     }
+}
+
+// The plain kernel forms a tile's P with the running max as it stands and checks
+// the lane's share of the tile's row sum: above 2^16, or not finite (the row's first
+// tile), the max moves to the tile's and the tile's P is formed again.  P stays
+// below 2^16 and the accumulators far from overflow, and the max scan of every
+// tile drops out of the common path.  Returns the share to add to the row sum.
+constexpr float kTileSumCap = 65536.f;
+template <int NDT>
+__device__ __forceinline__ float tile_commit(const f32x16 *acc_s, float c, float &m_run, float &l_run, float lt,
+                                             f32x16 *acc_o, bf16x8 *pf) {
+    if (__ballot(!(lt <= kTileSumCap))) {
+        float mt = fmaxf(acc_s[0][0], acc_s[0][1]);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int v = (kt == 0 ? 2 : 0); v < 16; v += 2) mt = fmaxf(mt, fmaxf(acc_s[kt][v], acc_s[kt][v + 1]));
+        const float m_new = fmaxf(m_run, pair_max(mt));
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < NDT; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc_o[i][v] *= alpha;
+        lt = 0.f;
+        tile_probs(acc_s, c, m_run * c, lt, pf);
+    }
+    return lt;
 }
 
 // Scores of the next tile (MFMA) interleaved with the probabilities of the current
@@ -341,23 +347,27 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         if (col2 != kNone) issue_k(col2, BJ);
         if (col1 != kNone) issue_v(col1, BJ ^ 1);
 
-        float mc = 0.f;
+        // (BIAS: the offset moves the scores tile by tile, so the max is checked first)
+        float mc = 0.f, lt = 0.f;
         if (mine0) {
             if constexpr (BIAS) {
                 tile_rescale_biased<NDT>(sc, c, beta0, m_run, l_run, acc_o);
                 mc = m_run - beta0;
             } else {
-                tile_rescale<NDT>(sc, c, m_run, l_run, acc_o);
                 mc = m_run * c;
             }
         }
         bf16x8 pf[4];
+        float &lacc = BIAS ? l_run : lt;
         if (mine0 && mine1) {
-            tile_scores_probs<D>(Ks + (BJ ^ 1) * TILEB, qf, l32, hh, sn, sc, c, mc, l_run, pf);
+            tile_scores_probs<D>(Ks + (BJ ^ 1) * TILEB, qf, l32, hh, sn, sc, c, mc, lacc, pf);
         } else if (mine1) {
             tile_scores<D>(Ks + (BJ ^ 1) * TILEB, qf, l32, hh, sn);
         } else if (mine0) {
-            tile_probs(sc, c, mc, l_run, pf);
+            tile_probs(sc, c, mc, lacc, pf);
+        }
+        if constexpr (!BIAS) {
+            if (mine0) l_run += tile_commit<NDT>(sc, c, m_run, l_run, lt, acc_o, pf);
         }
         // P V is MFMA work only: the wave runs it at raised priority, so that the
         // SIMD's other wave fills the matrix unit's gaps with its softmax instead of
