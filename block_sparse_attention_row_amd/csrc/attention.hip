@@ -103,16 +103,14 @@ __device__ __forceinline__ float tile_commit(const f32x16 *acc_s, float c, float
 // Scores of the next tile (MFMA) interleaved with the probabilities of the current
 // one (VALU): each score MFMA is grouped with an equal share of the softmax work, and the K reads run two MFMAs ahead.
 template <int D>
-__device__ __forceinline__ void tile_scores_probs(const char *K, const bf16x8 *qf, int l32, int hh, f32x16 *sn,
-                                                  const f32x16 *sc, float c, float mc, float &l_run, bf16x8 *pf) {
+__device__ __forceinline__ void tile_scores_probs(const char *K, const bf16x8 *qf, const FragOffsets<D> &fo,
+                                                  f32x16 *sn, const f32x16 *sc, float c, float mc, float &l_run,
+                                                  bf16x8 *pf) {
     constexpr int NC = D / 16, NM = 2 * NC;       // score MFMAs per tile
     constexpr int PER = 32 / NM;                  // probabilities per MFMA group
     // MFMA i works on key half i & 1 and d chunk i >> 1, so consecutive MFMAs feed
     // different accumulators and never wait on each other
-    auto kfrag = [&](int i) {
-        const int kt = i & 1, cq = i >> 1;
-        return *reinterpret_cast<const bf16x8 *>(K + TileGeo<D>::swz(32 * kt + l32, 16 * cq + 8 * hh));
-    };
+    auto kfrag = [&](int i) { return fo.kfrag(K, i & 1, i >> 1); };
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
         sn[0][v] = 0.f;
@@ -321,6 +319,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         for (int v = 0; v < 16; ++v) acc_o[i][v] = 0.f;
     // running max: raw score units, or (BIAS) log2 units including the offsets
     float m_run = -INFINITY, l_run = 0.f;
+    FragOffsets<D> fo;
+    fo.init(lane);
 
     // tiles j (scores pending), j+1 (K resident), j+2 (lookahead)
     int col0, col1, col2;
@@ -360,9 +360,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         bf16x8 pf[4];
         float &lacc = BIAS ? l_run : lt;
         if (mine0 && mine1) {
-            tile_scores_probs<D>(Ks + (BJ ^ 1) * TILEB, qf, l32, hh, sn, sc, c, mc, lacc, pf);
+            tile_scores_probs<D>(Ks + (BJ ^ 1) * TILEB, qf, fo, sn, sc, c, mc, lacc, pf);
         } else if (mine1) {
-            tile_scores<D>(Ks + (BJ ^ 1) * TILEB, qf, l32, hh, sn);
+            tile_scores_fo<D>(Ks + (BJ ^ 1) * TILEB, qf, fo, sn);
         } else if (mine0) {
             tile_probs(sc, c, mc, lacc, pf);
         }
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         // SIMD's other wave fills the matrix unit's gaps with its softmax instead of
         // delaying these MFMAs
         __builtin_amdgcn_s_setprio(1);
-        if (mine0) tile_pv<D>(Vs + BJ * TILEB, pf, lane, acc_o);
+        if (mine0) tile_pv<D>(Vs + BJ * TILEB, pf, fo, acc_o);
         __builtin_amdgcn_s_setprio(0);
         col0 = col1;
         mine0 = mine1;

@@ -75,6 +75,45 @@ __device__ __forceinline__ bf16x8 v_frag(const char *V, int lane, int kc, int dt
     return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 }
 
+// Per-lane byte offsets of a wave's fragment reads within a tile, formed once.  The
+// swizzle key depends on the row mod 16 only, so a read of another 16-row chunk, of
+// the other 32-key half or of the other tile buffer is one of these plus a
+// compile-time constant, which the LDS read takes as its immediate offset (no
+// address arithmetic per read).  The empty asm keeps each offset whole in a VGPR.
+template <int D> struct FragOffsets {
+    static constexpr int NC = D / 16, NDT = D / 32;
+    uint32_t k[NC];                 // K operand of S^T: row l32, d = 16 c + 8 hh
+    uint32_t vlo[NDT], vhi[NDT];    // transposed V reads of chunk 0, d tile dt: rows r0 and r0 + 8
+    __device__ __forceinline__ void init(int lane) {
+        const int l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            k[c] = (uint32_t)TileGeo<D>::swz(l32, 16 * c + 8 * hh);
+            asm volatile("" : "+v"(k[c]));
+        }
+        const int tr_e = (lane & 15) >> 2, tr_c = lane & 3, tr_g = lane >> 4;
+        const int r0 = 4 * (tr_g >> 1) + tr_e;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const int cc = 32 * dt + 16 * (tr_g & 1) + 4 * tr_c;
+            vlo[dt] = (uint32_t)TileGeo<D>::swz(r0, cc);
+            vhi[dt] = (uint32_t)TileGeo<D>::swz(r0 + 8, cc);
+            asm volatile("" : "+v"(vlo[dt]), "+v"(vhi[dt]));
+        }
+    }
+    // K fragment of key half kt, d chunk c
+    __device__ __forceinline__ bf16x8 kfrag(const char *K, int kt, int c) const {
+        return *reinterpret_cast<const bf16x8 *>(K + 32 * kt * TileGeo<D>::ROWB + k[c]);
+    }
+    // the fragment v_frag(V, lane, kc, dt) reads
+    __device__ __forceinline__ bf16x8 vfrag(const char *V, int kc, int dt) const {
+        const char *base = V + 16 * kc * TileGeo<D>::ROWB;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + vlo[dt]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + vhi[dt]));
+        return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    }
+};
+
 // S^T = K Q^T for the two 32-key halves of a tile (K from LDS).
 template <int D>
 __device__ __forceinline__ void tile_scores(const char *K, const bf16x8 *qf, int l32, int hh, f32x16 *acc_s) {
@@ -90,15 +129,45 @@ __device__ __forceinline__ void tile_scores(const char *K, const bf16x8 *qf, int
     }
 }
 
+// tile_scores through the offset table
+template <int D>
+__device__ __forceinline__ void tile_scores_fo(const char *K, const bf16x8 *qf, const FragOffsets<D> &fo,
+                                               f32x16 *acc_s) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc_s[kt][v] = 0.f;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+            acc_s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fo.kfrag(K, kt, c), qf[c], acc_s[kt], 0, 0, 0);
+    }
+}
+
 // O^T += V^T P^T over four 16-key chunks; slot e of chunk kc is key
 // 16 kc + (e < 4 ? 4 hh + e : 8 + 4 hh + e - 4), matching the accumulators of P.
 // The transposed V reads run two MFMAs ahead of their use.
 
 template <int D>
-__device__ __forceinline__ void tile_pv(const char *V, const bf16x8 *pf, int lane, f32x16 *acc_o) {
+__device__ __forceinline__ void tile_pv(const char *V, const bf16x8 *pf, const FragOffsets<D> &fo, f32x16 *acc_o) {
     constexpr int NDT = TileGeo<D>::NDT, NM = 4 * NDT;
     // four-slot ring: the read for MFMA i+2 lands in the slot MFMA i-2 used, so it
     // can be issued before MFMA i without waiting on MFMA i-1's operand reads
+    bf16x8 vf[4];
+    vf[0] = fo.vfrag(V, 0, 0);
+    vf[1] = fo.vfrag(V, 1 / NDT, 1 % NDT);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+        if (i + 2 < NM) vf[(i + 2) % 4] = fo.vfrag(V, (i + 2) / NDT, (i + 2) % NDT);
+        acc_o[i % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 4], pf[i / NDT], acc_o[i % NDT], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The same with the fragment addresses formed per read (kernels short of VGPRs for
+// the offset table).
+template <int D>
+__device__ __forceinline__ void tile_pv(const char *V, const bf16x8 *pf, int lane, f32x16 *acc_o) {
+    constexpr int NDT = TileGeo<D>::NDT, NM = 4 * NDT;
     bf16x8 vf[4];
     vf[0] = v_frag<D>(V, lane, 0, 0);
     vf[1] = v_frag<D>(V, lane, 1 / NDT, 1 % NDT);
@@ -109,5 +178,6 @@ __device__ __forceinline__ void tile_pv(const char *V, const bf16x8 *pf, int lan
         __builtin_amdgcn_sched_barrier(0);
     }
 }
+
 
 }  // namespace sattn
