@@ -335,7 +335,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         if (col1 != kNone) issue_k(col1, 1);
         wait_vmcnt<0>();
         __syncthreads();
-        if (mine0) tile_scores<D>(Ks, qf, l32, hh, sa);
+        if (mine0) tile_scores<D>(Ks, qf, fo, sa);
     }
     // One pipeline step for tile j with j & 1 == BJ: the scores of tile j are in sc,
     // those of tile j+1 go to sn; buffer offsets are compile-time constants.
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         if (mine0 && mine1) {
             tile_scores_probs<D>(Ks + (BJ ^ 1) * TILEB, qf, fo, sn, sc, c, mc, lacc, pf);
         } else if (mine1) {
-            tile_scores_fo<D>(Ks + (BJ ^ 1) * TILEB, qf, fo, sn);
+            tile_scores<D>(Ks + (BJ ^ 1) * TILEB, qf, fo, sn);
         } else if (mine0) {
             tile_probs(sc, c, mc, lacc, pf);
         }

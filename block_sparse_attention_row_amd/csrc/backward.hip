@@ -253,6 +253,8 @@ __global__ __launch_bounds__(256, MODE == kDKV && D == 128 ? 1 : 2) void bwd_ker
             dma16(ax0 + buf * 1024, aux_voff, (const char *)a.lse2 + (bh * N + col * 64) * 4);
     };
 
+    FragOffsets<D> fo;
+    fo.init(lane);
     f32x16 acc[NDT], acc2[NDT];     // acc2: dK of the fused pass
 #pragma unroll
     for (int i = 0; i < NDT; ++i)
@@ -277,8 +279,8 @@ __global__ __launch_bounds__(256, MODE == kDKV && D == 128 ? 1 : 2) void bwd_ker
         const char *T1 = T1s + BJ * TILEB, *T2 = T2s + BJ * TILEB;
         const float *ax = aux[BJ];
         f32x16 s[2], dp[2];
-        tile_scores<D>(T1, f1, l32, hh, s);
-        tile_scores<D>(T2, f2, l32, hh, dp);
+        tile_scores<D>(T1, f1, fo, s);
+        tile_scores<D>(T2, f2, fo, dp);
         bf16x8 pf[4], pf2[4];           // pf2: dS of the fused pass (pf holds P there)
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
@@ -308,8 +310,8 @@ __global__ __launch_bounds__(256, MODE == kDKV && D == 128 ? 1 : 2) void bwd_ker
             if (MODE == kDKV) pf2[kc] = __builtin_convertvector(pv2, bf16x8);
         }
         // dQ^T += K^T dS^T (K tile read transposed); dV^T += dO^T P; dK^T += Q^T dS
-        tile_pv<D>(MODE == kDKV ? T2 : T1, pf, lane, acc);
-        if (MODE == kDKV) tile_pv<D>(T1, pf2, lane, acc2);
+        tile_pv<D>(MODE == kDKV ? T2 : T1, pf, fo, acc);
+        if (MODE == kDKV) tile_pv<D>(T1, pf2, fo, acc2);
     };
     while (col0 != kNone) {
         step(std::integral_constant<int, 0>{});

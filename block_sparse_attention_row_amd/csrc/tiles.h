@@ -60,21 +60,6 @@ template <int D> struct TileGeo {
 };
 
 
-// O^T-style operand of a 32x32x16 MFMA read transposed from a tile (rows = the
-// summed index): the A operand of X^T Y with X the tile, for 16-row chunk kc and
-// 32-column d tile dt.  Slot e of the fragment is tile row
-// 16 kc + (e < 4 ? 4 hh + e : 8 + 4 hh + e - 4), the row order of the S^T
-// accumulators the B operand takes from.
-template <int D>
-__device__ __forceinline__ bf16x8 v_frag(const char *V, int lane, int kc, int dt) {
-    const int tr_e = (lane & 15) >> 2, tr_c = lane & 3, tr_g = lane >> 4;
-    const int cc = 32 * dt + 16 * (tr_g & 1) + 4 * tr_c;
-    const int r0 = 16 * kc + 4 * (tr_g >> 1) + tr_e;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(V + TileGeo<D>::swz(r0, cc)));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(V + TileGeo<D>::swz(r0 + 8, cc)));
-    return __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-}
-
 // Per-lane byte offsets of a wave's fragment reads within a tile, formed once.  The
 // swizzle key depends on the row mod 16 only, so a read of another 16-row chunk, of
 // the other 32-key half or of the other tile buffer is one of these plus a
@@ -105,7 +90,12 @@ template <int D> struct FragOffsets {
     __device__ __forceinline__ bf16x8 kfrag(const char *K, int kt, int c) const {
         return *reinterpret_cast<const bf16x8 *>(K + 32 * kt * TileGeo<D>::ROWB + k[c]);
     }
-    // the fragment v_frag(V, lane, kc, dt) reads
+    // O^T-style operand of a 32x32x16 MFMA read transposed from a tile (rows = the
+    // summed index): the A operand of X^T Y with X the tile, for 16-row chunk kc and
+    // 32-column d tile dt.  Slot e of the fragment is tile row
+    // 16 kc + (e < 4 ? 4 hh + e : 8 + 4 hh + e - 4), the row order of the S^T
+    // accumulators the B operand takes from.  Its two halves are the transposed
+    // 8-byte reads at rows r0 + 16 kc and r0 + 8 + 16 kc.
     __device__ __forceinline__ bf16x8 vfrag(const char *V, int kc, int dt) const {
         const char *base = V + 16 * kc * TileGeo<D>::ROWB;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + vlo[dt]));
@@ -116,23 +106,7 @@ template <int D> struct FragOffsets {
 
 // S^T = K Q^T for the two 32-key halves of a tile (K from LDS).
 template <int D>
-__device__ __forceinline__ void tile_scores(const char *K, const bf16x8 *qf, int l32, int hh, f32x16 *acc_s) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc_s[kt][v] = 0.f;
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(K + TileGeo<D>::swz(32 * kt + l32, 16 * c + 8 * hh));
-            acc_s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], acc_s[kt], 0, 0, 0);
-        }
-    }
-}
-
-// tile_scores through the offset table
-template <int D>
-__device__ __forceinline__ void tile_scores_fo(const char *K, const bf16x8 *qf, const FragOffsets<D> &fo,
-                                               f32x16 *acc_s) {
+__device__ __forceinline__ void tile_scores(const char *K, const bf16x8 *qf, const FragOffsets<D> &fo, f32x16 *acc_s) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -162,22 +136,5 @@ __device__ __forceinline__ void tile_pv(const char *V, const bf16x8 *pf, const F
         __builtin_amdgcn_sched_barrier(0);
     }
 }
-
-// The same with the fragment addresses formed per read (kernels short of VGPRs for
-// the offset table).
-template <int D>
-__device__ __forceinline__ void tile_pv(const char *V, const bf16x8 *pf, int lane, f32x16 *acc_o) {
-    constexpr int NDT = TileGeo<D>::NDT, NM = 4 * NDT;
-    bf16x8 vf[4];
-    vf[0] = v_frag<D>(V, lane, 0, 0);
-    vf[1] = v_frag<D>(V, lane, 1 / NDT, 1 % NDT);
-#pragma unroll
-    for (int i = 0; i < NM; ++i) {
-        if (i + 2 < NM) vf[(i + 2) % 4] = v_frag<D>(V, lane, (i + 2) / NDT, (i + 2) % NDT);
-        acc_o[i % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % 4], pf[i / NDT], acc_o[i % NDT], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
 
 }  // namespace sattn
