@@ -112,13 +112,15 @@ def pmc_summary(d):
     return rec
 
 
-def stored_traffic():
+def stored_traffic(workload):
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     if rec.get("attention_source_sha256") != _sha(ATTN_SRC):
         return None            # kernel changed since the counters were taken
+    if rec.get("workload") != workload:
+        return None            # the counters were taken on another workload
     return rec.get("hbm_bytes_per_dispatch")
 
 
@@ -381,7 +383,7 @@ def main():
         sched = {"dense_steps": args.dense_steps, "reselect_every": K, "ms_per_step": round(1e3 * t_s, 4),
                  "TFLOP_s": round(4.0 * 64 * 64 * wl.head_dim * tiles / args.steps / t_s / 1e12, 2)}
 
-    traffic = stored_traffic()
+    traffic = stored_traffic(wl.name)
     rec = {
         "metric": "effective TFLOP/s on kept tiles (select + forward step)",
         "value": round(value, 2),
