@@ -601,189 +601,255 @@ int launch_select(const SelectArgs &a, int d, int dtype, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // The clustering selector's rows (AB-Attention page, section "Les trois techniques
-// d'AB-Attention", first item): one workgroup (8 waves) per pair of query blocks
-// (128 tokens; an odd last block alone).  The pair's queries go to LDS; Lloyd's
-// k-means with 8 clusters and 4 rounds starts from the queries at positions
-// n*c/8: each round assigns every query (one lane each, its query in registers) to
-// the nearest centroid by squared distance, ties to the lower cluster, then moves
-// each centroid to the mean of its queries in query order (an empty cluster keeps
-// its centroid).  The weights are the last assignment's shares.  Wave c then
-// scores centroid c on every key block mean, S = mu_c . Kbar_j * scale (fp32, key
-// means as hi + lo), forms w_c softmax(S) and adds it to the pair's row in LDS, in
-// cluster order; the row is stored in log2 units for the cut.
-template <int D>
-__global__ __launch_bounds__(512, 4) void ibcs_mix_kernel(IbcsArgs a) {
-    constexpr int K = kIbcsClusters;
-    // the pair's queries (128 x D bf16), later the staged key means (64 x (D + 1) words)
-    __shared__ __attribute__((aligned(16))) uint32_t qbuf[64 * (D + 1)];
-    __bf16 *qs = reinterpret_cast<__bf16 *>(qbuf);
-    __shared__ float mu[K * D];
-    __shared__ int32_t asg[128];
-    __shared__ int32_t cnt[K];
-    __shared__ float row[kSelectMaxBlocks];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int64_t pr = blockIdx.x;                                 // pair within this launch
-    const int64_t bh = a.head0 + pr / a.pairs_per_head;
-    const int p = (int)(pr % a.pairs_per_head);
-    const int n = 2 * p + 1 < a.nB ? 128 : 64;
+// d'AB-Attention", first item).  A workgroup of 16 waves serves two pairs of query
+// blocks of one (batch, head) (128 queries a pair; an odd last block alone); waves
+// 8P .. 8P + 7 serve pair P.
+//  - Lloyd's k-means with 8 clusters and 4 rounds, started from the queries at
+//    positions n*c/8.  Assignment: each query is split over 4 lanes (D/4
+//    dimensions each, in registers); the squared distances to the 8 centroids, fp32
+//    sums of (x - mu)^2 over the lane's dimensions and then over the 4 lanes, pick
+//    the nearest, ties to the lower cluster.  Update: the cluster sums are the
+//    product onehot^T X on v_mfma_f32_16x16x32_bf16 (0/1 and the bf16 queries are
+//    exact operands, fp32 accumulation); a centroid becomes its cluster's sum over
+//    its count, and an empty cluster keeps its centroid.  The weights are the last
+//    assignment's shares.
+//  - Scores of the 16 centroids on every key block mean, S = mu . Kbar * scale, on
+//    the same MFMA with each centroid split into three bf16 parts (hi, mid, lo) and
+//    the key means in their two (hi, lo): the five products that reach 2^-24.
+//  - Wave 8P + c: softmax of centroid c on its register row (max, then the sum),
+//    weighted by w_c.  The pair's row is the sum of its 8 weighted rows, added in
+//    cluster order through LDS 256 keys at a time, and stored in log2 units for the
+//    cut.
+template <int D, int NE>
+__global__ __launch_bounds__(1024) void ibcs_mix_kernel(IbcsArgs a) {
+    constexpr int K = kIbcsClusters, DP = D / 4, KB = D / 32, NCH = NE / 4;
+    constexpr int QW = 3 * D + 8;                                   // bf16 per centroid row: hi | mid | lo, pad
+    constexpr int QBYTES = 2 * 128 * D * 2;                         // the two pairs' queries
+    constexpr int SBYTES = 16 * QW * 2 + 2 * kSelRows * kStageStride * 4;
+    constexpr int BIG = QBYTES > SBYTES ? QBYTES : SBYTES;
+    static_assert(K == 8 && D % 32 == 0 && (2 * 128 * D / 8) % 1024 == 0, "layout");
+    __shared__ __attribute__((aligned(16))) unsigned char big[BIG];
+    __shared__ float mu[2][K][D];
+    __shared__ int32_t asg[2][128];
+    __shared__ int32_t cnt[2][K];
+    __bf16 *qs = reinterpret_cast<__bf16 *>(big);                   // [2][128][D], during the k-means
+    __bf16 *qf = reinterpret_cast<__bf16 *>(big);                   // [16][QW], afterwards
+    float *stage = reinterpret_cast<float *>(big + 16 * QW * 2);    // [2][16][kStageStride]
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int P = wave >> 3, w8 = wave & 7;
+    const int gph = (a.pairs_per_head + 1) / 2;
+    const int64_t bh = a.head0 + blockIdx.x / gph;
+    const int p0 = 2 * (int)(blockIdx.x % gph);
+    const int np = p0 + 1 < a.pairs_per_head ? 2 : 1;               // pairs in this workgroup
     const int64_t N = (int64_t)a.nB * 64;
-    const __bf16 *qg = a.q + (bh * N + (int64_t)128 * p) * D;
+    auto pair_n = [&](int pp) { return 2 * (p0 + pp) + 1 < a.nB ? 128 : 64; };
     {
-        // all of this thread's loads in flight before the stores
-        constexpr int PER = 128 * D / 8 / 512;
+        // the pairs' queries, all of this thread's loads in flight before the stores
+        constexpr int PER = 2 * 128 * D / 8 / 1024, PP = 128 * D / 8;
         uint4 tmp[PER];
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
-            const int e = t + 512 * u;
-            tmp[u] = e < n * D / 8 ? reinterpret_cast<const uint4 *>(qg)[e] : uint4{0u, 0u, 0u, 0u};
+            const int e = t + 1024 * u, pp = e / PP, r = e % PP;
+            const bool ok = pp < np && r < pair_n(pp) * D / 8;
+            tmp[u] = ok ? reinterpret_cast<const uint4 *>(a.q + (bh * N + (int64_t)128 * (p0 + pp)) * D)[r]
+                        : uint4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int u = 0; u < PER; ++u) reinterpret_cast<uint4 *>(qs)[t + 512 * u] = tmp[u];
+        for (int u = 0; u < PER; ++u) reinterpret_cast<uint4 *>(qs)[t + 1024 * u] = tmp[u];
     }
     __syncthreads();
-    for (int e = t; e < K * D; e += blockDim.x) mu[e] = (float)qs[((n * (e / D)) / K) * D + e % D];
-    uint32_t x[D / 2];                                              // this lane's query as bf16 pairs (t < n)
-    if (t < n) {
+
+    // ---- k-means of pair P: lane (q, part) holds query q's dimensions part*DP ..
+    const int tp = t & 511, q = tp >> 2, part = tp & 3;
+    const int n = pair_n(P);
+    float x[DP];
+    {
+        const uint4 *src = reinterpret_cast<const uint4 *>(qs + (P * 128 + q) * D + part * DP);
 #pragma unroll
-        for (int w = 0; w < D / 2; ++w) x[w] = reinterpret_cast<const uint32_t *>(qs)[t * (D / 2) + w];
+        for (int u = 0; u < DP / 8; ++u) {
+            const uint4 w = src[u];
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                x[8 * u + 2 * k] = bf16_lo(ws[k]);
+                x[8 * u + 2 * k + 1] = bf16_hi(ws[k]);
+            }
+        }
+    }
+    for (int e = tp; e < K * D; e += 512) {
+        const int c = e / D, dd = e % D;
+        mu[P][c][dd] = (float)qs[(P * 128 + (n * c) / K) * D + dd];
     }
     __syncthreads();
-    for (int it = 0; it < kIbcsIters; ++it) {
-        if (t < n) {
-            int best = 0;
-            float bd = INFINITY;
 #pragma unroll 1
+    for (int it = 0; it < kIbcsIters; ++it) {
+        float dist[K];
+#pragma unroll
+        for (int c = 0; c < K; ++c) {
+            const float *m = &mu[P][c][part * DP];
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < DP; ++i) {
+                const float df = x[i] - m[i];
+                acc = __builtin_fmaf(df, df, acc);
+            }
+            dist[c] = acc;
+        }
+#pragma unroll
+        for (int c = 0; c < K; ++c) {
+            dist[c] += __shfl_xor(dist[c], 1, 64);
+            dist[c] += __shfl_xor(dist[c], 2, 64);
+        }
+        int best = 0;
+        float bd = dist[0];
+#pragma unroll
+        for (int c = 1; c < K; ++c)
+            if (dist[c] < bd) {
+                bd = dist[c];
+                best = c;
+            }
+        if (part == 0) asg[P][q] = q < n ? best : -1;
+        __syncthreads();
+        if (w8 == 0) {
+#pragma unroll
             for (int c = 0; c < K; ++c) {
-                float d2 = 0.f;
-#pragma unroll
-                for (int w = 0; w < D / 2; ++w) {
-                    const float d0 = bf16_lo(x[w]) - mu[c * D + 2 * w], d1 = bf16_hi(x[w]) - mu[c * D + 2 * w + 1];
-                    d2 = __builtin_fmaf(d0, d0, d2);
-                    d2 = __builtin_fmaf(d1, d1, d2);
-                }
-                if (d2 < bd) {
-                    bd = d2;
-                    best = c;
-                }
-            }
-            asg[t] = best;
-        }
-        __syncthreads();
-        // new centroids: thread (c, dd) sums its cluster's queries in query order
-        float nv[(K * D + 511) / 512];
-        int nc[(K * D + 511) / 512];
-#pragma unroll
-        for (int u = 0; u < (K * D + 511) / 512; ++u) {
-            const int e = t + 512 * u;
-            nv[u] = 0.f;
-            nc[u] = 0;
-            if (e < K * D) {
-                const int c = e / D, dd = e % D;
-                float sum = 0.f;
-                int m = 0;
-#pragma unroll 16
-                for (int q = 0; q < n; ++q) {
-                    const bool in = asg[q] == c;
-                    sum += in ? (float)qs[q * D + dd] : 0.f;
-                    m += in ? 1 : 0;
-                }
-                nv[u] = m > 0 ? sum / (float)m : mu[e];
-                nc[u] = m;
+                const int m = __popcll(__ballot(asg[P][lane] == c)) + __popcll(__ballot(asg[P][64 + lane] == c));
+                if (lane == 0) cnt[P][c] = m;
             }
         }
-        __syncthreads();
+        // cluster sums of dimensions 16 w8 .. 16 w8 + 15: row = cluster (0 .. 15, 8 .. 15
+        // empty), k = query, column = dimension
+        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+        const int cl = lane & 15, kq = lane >> 4, dim = 16 * w8 + (lane & 15);
+        if (16 * w8 < D) {
 #pragma unroll
-        for (int u = 0; u < (K * D + 511) / 512; ++u) {
-            const int e = t + 512 * u;
-            if (e < K * D) {
-                mu[e] = nv[u];
-                if (e % D == 0) cnt[e / D] = nc[u];
+            for (int ks = 0; ks < 4; ++ks) {
+                const int qb = 32 * ks + 8 * kq;
+                bf16x8 oh, xb;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    oh[i] = asg[P][qb + i] == cl ? (__bf16)1.f : (__bf16)0.f;
+                    xb[i] = qs[(P * 128 + qb + i) * D + dim];
+                }
+                sum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oh, xb, sum, 0, 0, 0);
+            }
+        }
+        __syncthreads();            // counts written; every read of the old centroids done
+        if (16 * w8 < D) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = 4 * kq + i;
+                if (c < K && cnt[P][c] > 0) mu[P][c][dim] = sum[i] / (float)cnt[P][c];
             }
         }
         __syncthreads();
     }
-    // wave c: softmax of centroid c over all key blocks (an online pass for the max
-    // and the sum, then a second pass that adds the weighted terms), added to the
-    // pair's row in cluster order.  Key means are staged 64 at a time in LDS with
-    // coalesced loads, rows padded to D/2 + 1 words (hi and lo halves as packed
-    // bf16 pairs) so that the lane-per-key reads hit distinct banks.
-    const int c = wave;
-    const float wgt = (float)cnt[c] / (float)n;
-    const __bf16 *kb = a.kbar + (bh * a.nB) * (2 * D);
-    const float *mc = mu + c * D;                                   // this wave's centroid (LDS, broadcast reads)
-    constexpr int KW = D + 1;                                       // words per staged key (hi|lo pairs + pad)
-    uint32_t *kst = qbuf;                                           // the query buffer is free by now
-    const int nvc = a.nBp >> 6;
-    auto stage = [&](int e) {
-        // 64 key means = 64 * D words: 16-byte loads, all in flight before the stores
-        constexpr int PER = 64 * D / 4 / 512;
-        const uint4 *src = reinterpret_cast<const uint4 *>(kb + (int64_t)(64 * e) * (2 * D));
-        const int nk = a.nB - 64 * e < 64 ? a.nB - 64 * e : 64;
-        uint4 tmp[PER];
+    const float wgt = (float)cnt[P][w8] / (float)n;                  // this wave's centroid weight
+
+    // ---- centroid rows as three bf16 parts (the query buffer is free)
+    for (int e = t; e < 16 * D; e += 1024) {
+        const int r = e / D, dd = e % D;
+        const float v = (r >> 3) < np ? mu[r >> 3][r & 7][dd] : 0.f;
+        const __bf16 h = (__bf16)v;
+        const float r1 = v - (float)h;
+        const __bf16 m = (__bf16)r1;
+        qf[r * QW + dd] = h;
+        qf[r * QW + D + dd] = m;
+        qf[r * QW + 2 * D + dd] = (__bf16)(r1 - (float)m);
+    }
+    __syncthreads();
+
+    // ---- scores, chunk by chunk, into the register row of wave 8P + c (as in the
+    //      selection: 16 rows x 16 keys per wave and chunk, parked in the LDS stage)
+    const int ii = lane & 15, kq = lane >> 4;
+    const __bf16 *ks = a.kbar + (bh * a.nB) * (2 * D);
+    float s[NE];
 #pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int g4 = t + 512 * u;                            // 16-byte piece: key g4 / (D/4)
-            tmp[u] = g4 < nk * D / 4 ? src[g4] : uint4{0u, 0u, 0u, 0u};
-        }
-        __syncthreads();                                           // the previous stage's readers are done
+    for (int cc = 0; cc < NCH; ++cc) {
+        bf16x8 kh[KB], kl[KB];
+        const int jj = kSelChunk * cc + 16 * wave + ii;
+        const __bf16 *kr = ks + (int64_t)(jj < a.nB ? jj : 0) * (2 * D) + 8 * kq;   // (padding keys read row 0)
 #pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int g4 = t + 512 * u, key = g4 / (D / 4), w0 = 4 * (g4 % (D / 4));
-            uint32_t *dst = kst + key * KW + w0;
-            dst[0] = tmp[u].x;
-            dst[1] = tmp[u].y;
-            dst[2] = tmp[u].z;
-            dst[3] = tmp[u].w;
+        for (int kb = 0; kb < KB; ++kb) {
+            kh[kb] = *reinterpret_cast<const bf16x8 *>(kr + 32 * kb);
+            kl[kb] = *reinterpret_cast<const bf16x8 *>(kr + D + 32 * kb);
         }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const __bf16 *qrow = qf + ii * QW + 8 * kq;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const bf16x8 qh = *reinterpret_cast<const bf16x8 *>(qrow + 32 * kb);
+            const bf16x8 qm = *reinterpret_cast<const bf16x8 *>(qrow + D + 32 * kb);
+            const bf16x8 ql = *reinterpret_cast<const bf16x8 *>(qrow + 2 * D + 32 * kb);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql, kh[kb], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qm, kl[kb], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qm, kh[kb], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kl[kb], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kh[kb], acc, 0, 0, 0);
+        }
+        // acc[e] = S[row 4 kq + e][key 256 cc + 16 wave + ii]
+        float *st = stage + (cc & 1) * kSelRows * kStageStride;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st[(4 * kq + e) * kStageStride + 16 * wave + ii] = acc[e] * a.scale_log2;
         __syncthreads();
-    };
-    auto score = [&](int e) {
-        const uint32_t *kr = kst + lane * KW;
-        float acc = 0.f;
 #pragma unroll
-        for (int dd = 0; dd < D; dd += 2) {
-            const uint32_t h = kr[dd / 2], l = kr[D / 2 + dd / 2];
-            acc = __builtin_fmaf(mc[dd], bf16_lo(h) + bf16_lo(l), acc);
-            acc = __builtin_fmaf(mc[dd + 1], bf16_hi(h) + bf16_hi(l), acc);
-        }
-        return acc * a.scale_log2;
-    };
-    float mx = -INFINITY, z = 0.f;
-    for (int e = 0; e < nvc; ++e) {
-        stage(e);
-        if (64 * e + lane < a.nB) {
-            const float v = score(e);
-            if (v > mx) {
-                z = z * __builtin_amdgcn_exp2f(mx - v) + 1.f;
-                mx = v;
-            } else {
-                z += __builtin_amdgcn_exp2f(v - mx);
-            }
+        for (int t4 = 0; t4 < 4; ++t4) {
+            const float v = st[wave * kStageStride + 64 * t4 + lane];
+            s[4 * cc + t4] = kSelChunk * cc + 64 * t4 + lane < a.nB ? v : -INFINITY;
         }
     }
+
+    // ---- softmax of this wave's centroid, weighted; the pair's row in cluster order
+    float mx = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < NE; ++c) mx = fmaxf(mx, s[c]);
     const float gmx = wave_max_u(mx);
-    z = wave_sum_u(mx == -INFINITY ? 0.f : z * __builtin_amdgcn_exp2f(mx - gmx));
-    const float f = wgt / z;
-    // second pass: each wave's weighted terms for the staged keys, added in cluster order
-    for (int e = 0; e < nvc; ++e) {
-        stage(e);
-        const int j = 64 * e + lane;
-        const float term = j < a.nB ? f * __builtin_amdgcn_exp2f(score(e) - gmx) : 0.f;
-        for (int cc = 0; cc < K; ++cc) {
-            if (c == cc && j < a.nB) row[j] = (cc == 0 ? 0.f : row[j]) + term;
-            __syncthreads();
+    float z = 0.f;
+#pragma unroll
+    for (int c = 0; c < NE; ++c) z += __builtin_amdgcn_exp2f(s[c] - gmx);
+    const float f = wgt / wave_sum_u(z);
+    float *T = stage;                                               // [16][kStageStride]
+    __syncthreads();                                                // every wave has read its last stage
+#pragma unroll
+    for (int e = 0; e < NCH; ++e) {
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4)
+            T[wave * kStageStride + 64 * t4 + lane] = f * __builtin_amdgcn_exp2f(s[4 * e + t4] - gmx);
+        __syncthreads();
+        if (t < 512) {
+            const int pp = t >> 8, k = t & 255, j = kSelChunk * e + k;
+            if (pp < np && j < a.nB) {
+                float sum = 0.f;
+#pragma unroll
+                for (int c = 0; c < K; ++c) sum += T[(8 * pp + c) * kStageStride + k];
+                a.rows[((bh - a.head0) * a.pairs_per_head + p0 + pp) * a.nBp + j] =
+                    sum > 0.f ? __log2f(sum) : -INFINITY;
+            }
         }
+        __syncthreads();
     }
-    float *dst = a.rows + pr * a.nBp;
-    for (int j = t; j < a.nB; j += blockDim.x) dst[j] = row[j] > 0.f ? __log2f(row[j]) : -INFINITY;
+}
+
+template <int D, int NCH> static void launch_ibcs_nch(const IbcsArgs &a, dim3 g, int nch, hipStream_t s) {
+    if constexpr (NCH <= kSelectMaxBlocks / kSelChunk) {
+        if (nch == NCH) {
+            ibcs_mix_kernel<D, 4 * NCH><<<g, dim3(1024), 0, s>>>(a);
+            return;
+        }
+        launch_ibcs_nch<D, NCH + 1>(a, g, nch, s);
+    }
 }
 
 int launch_ibcs_mix(const IbcsArgs &a, int64_t heads, int d, hipStream_t s) {
-    const dim3 g((unsigned)(heads * a.pairs_per_head)), b(512);
+    if (a.nBp > kSelectMaxBlocks) return -1;
+    const dim3 g((unsigned)(heads * ((a.pairs_per_head + 1) / 2)));
+    const int nch = (a.nB + kSelChunk - 1) / kSelChunk;
     if (d == 128)
-        ibcs_mix_kernel<128><<<g, b, 0, s>>>(a);
+        launch_ibcs_nch<128, 1>(a, g, nch, s);
     else
-        ibcs_mix_kernel<64><<<g, b, 0, s>>>(a);
+        launch_ibcs_nch<64, 1>(a, g, nch, s);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
