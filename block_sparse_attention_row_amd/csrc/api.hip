@@ -60,7 +60,10 @@ int64_t groups_per_head(const Dims &d) { return (d.nB + kGroupRows - 1) / kGroup
 int64_t n_groups(const Dims &d) { return d.B * d.H * groups_per_head(d); }
 
 int64_t n_pairs(const Dims &d) { return d.B * d.H * ((d.nB + 1) / 2); }
-int64_t max_slots(const Dims &d) { return n_pairs(d) * 4 < kMaxSlots ? n_pairs(d) * 4 : kMaxSlots; }
+int64_t long_slots(const Dims &d) { return n_pairs(d) * 4 < kLongSlots ? n_pairs(d) * 4 : kLongSlots; }
+int64_t max_slots(const Dims &d) {
+    return long_slots(d) + (n_pairs(d) >= 2 * kResidentPairs ? (int64_t)kTailPairs * kTailPieces : 0);
+}
 
 struct Layout {
     int64_t thr, kbar, status, ticket;                                   // selection
@@ -274,6 +277,7 @@ int32_t forward_impl(const sparse_attn_shape *shape, const void *q, const void *
     a.plan.part_o = (float *)(ws + L.part_o);
     a.plan.part_lse = (float *)(ws + L.part_lse);
     a.plan.max_slots = (int32_t)max_slots(d);
+    a.plan.long_slots = (int32_t)long_slots(d);
     if (launch_attention(a, shape->dtype, (int)d.D, (hipStream_t)stream)) return SPARSE_ATTN_HIP_ERROR;
     return SPARSE_ATTN_OK;
 }

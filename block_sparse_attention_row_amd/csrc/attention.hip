@@ -162,19 +162,26 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     const int t = threadIdx.x, lane = t & 63, hh = lane >> 5, l32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int grp = wave >> 1;                    // 0: first query block of the pair, 1: second
-    // work item: the first max_slots workgroups take the pieces of split pairs (so that
-    // long work starts first), the rest take whole pairs that were not split
-    const int64_t ms = a.plan.max_slots;
+    // work item: the first long_slots workgroups take the pieces of long rows (so that
+    // long work starts first), the next n_pairs take whole pairs that were not split,
+    // and the last ones the pieces of the last round's pairs (so that the launch ends
+    // on short items)
+    const int64_t ls = a.plan.long_slots, bid = blockIdx.x;
     int64_t pair;
     SplitItem it = {};
-    const bool split = (int64_t)blockIdx.x < ms;
-    if (split) {
-        if ((int64_t)blockIdx.x >= a.plan.counts[0]) return;
-        it = a.plan.items[blockIdx.x];
+    bool split = true;
+    if (bid < ls) {
+        if (bid >= a.plan.counts[0]) return;
+        it = a.plan.items[bid];
         pair = it.pair;
-    } else {
-        pair = xcd_chunk_remap<256>(blockIdx.x - ms, a.n_pairs);
+    } else if (bid < ls + a.n_pairs) {
+        split = false;
+        pair = xcd_chunk_remap<256>(bid - ls, a.n_pairs);
         if (a.plan.pair_flag[pair]) return;
+    } else {
+        if (bid - ls - a.n_pairs >= a.plan.counts[3]) return;
+        it = a.plan.items[bid - a.n_pairs];
+        pair = it.pair;
     }
     const int64_t bh = pair / a.pairs_per_head;
     const int i0 = (int)(pair % a.pairs_per_head) * 2;
@@ -481,7 +488,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
             if (e > L) need += (e + L - 1) / L;
         }
         need = block_sum64(need, red);
-        if (need <= P.max_slots) break;
+        if (need <= P.long_slots) break;
         L *= 2;
     }
     int32_t base = 0, mbase = 0;
@@ -522,10 +529,55 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
         base += tot_ns;
         mbase += tot_sp;
     }
+    // the last round's pairs (the last T in dispatch order, unless already cut), in
+    // kTailPieces pieces each when every piece keeps 16 tiles
+    __syncthreads();   // every pair_flag above is written
+    static_assert(kTailPairs <= 1024, "one pass");
+    const int64_t T = a.n_pairs >= 2 * kResidentPairs
+                          ? min((int64_t)kTailPairs, (int64_t)(P.max_slots - P.long_slots) / kTailPieces)
+                          : 0;
+    int32_t tail = 0;
+    {
+        int64_t p = 0, bA = 0, eA = 0, bB = 0, eB = 0;
+        int32_t ns = 0;
+        if (t < T) {
+            p = xcd_chunk_remap<256>(a.n_pairs - T + t, a.n_pairs);
+            if (P.pair_flag[p] == 0) {
+                pair_ranges(a, p, bA, eA, bB, eB);
+                ns = max(eA - bA, eB - bB) >= 16 * kTailPieces ? kTailPieces : 0;
+            }
+        }
+        int32_t tot_ns, tot_sp;
+        const int32_t excl = block_scan32(ns, scan, tot_ns);
+        const int32_t mex = block_scan32(ns > 0 ? 1 : 0, scan, tot_sp);
+        if (ns) {
+            const int32_t first = P.long_slots + excl;
+            P.pair_flag[p] = first + 1;
+            int32_t *me = P.merge + 3 * (int64_t)(mbase + mex);
+            me[0] = (int32_t)p;
+            me[1] = first;
+            me[2] = ns;
+            for (int32_t sI = 0; sI < ns; ++sI) {
+                SplitItem it;
+                it.pair = (int32_t)p;
+                it.slot = first + sI;
+                it.a0 = (int32_t)(bA + (eA - bA) * sI / ns);
+                it.a1 = (int32_t)(bA + (eA - bA) * (sI + 1) / ns);
+                it.ra = (int32_t)bA;
+                it.b0 = (int32_t)(bB + (eB - bB) * sI / ns);
+                it.b1 = (int32_t)(bB + (eB - bB) * (sI + 1) / ns);
+                it.rb = (int32_t)bB;
+                P.items[first + sI] = it;
+            }
+        }
+        tail = tot_ns;
+        mbase += tot_sp;
+    }
     if (t == 0) {
         P.counts[0] = base;
         P.counts[1] = mbase;
         P.counts[2] = (int32_t)L;
+        P.counts[3] = tail;
     }
 }
 
@@ -694,6 +746,8 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
 
 int launch_attention(const AttnArgs &a, int dtype, int d, hipStream_t s) {
     const dim3 pgrid((unsigned)(a.plan.max_slots + a.n_pairs)), pblock(256), grid((unsigned)a.rows), block(128);
+    // (long_slots workgroups of long-row pieces, n_pairs of whole pairs, then max_slots -
+    // long_slots of last-round pieces)
     const dim3 mgrid((unsigned)a.plan.max_slots), mblock(512);
     if (dtype == 1) {
         plan_kernel<<<1, 1024, 0, s>>>(a);

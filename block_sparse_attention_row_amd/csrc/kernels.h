@@ -77,6 +77,9 @@ int launch_ibcs_mix(const IbcsArgs &a, int64_t heads, int d, hipStream_t s);
 // row); pieces run first, write normalised partial outputs and their log-sum-exp
 // to partial slots, and a merge kernel combines them.  L follows the total work
 // over the workgroups resident at once, so that no work item outlasts the rest.
+// With at least two rounds of pairs, the pairs dispatched last (the last round)
+// are cut into kTailPieces pieces as well, which run after every whole pair: the
+// launch then ends on short items instead of a part-filled round of whole pairs.
 struct SplitItem {
     int32_t pair, slot;          // query-block pair, partial slot
     int32_t a0, a1, ra;          // row A entries [a0, a1); the row's first entry ra
@@ -84,15 +87,19 @@ struct SplitItem {
 };
 constexpr int kResidentPairs = 512;   // attention workgroups resident at once (256 CUs x 2)
 constexpr int kMinPiece = 64;         // shortest piece (tiles)
-constexpr int kMaxSlots = 512;        // partial slots at most
+constexpr int kLongSlots = 512;       // partial slots of long-row pieces at most
+constexpr int kTailPairs = 384;       // pairs of the last round cut into pieces (3/4 of the resident pairs)
+constexpr int kTailPieces = 4;        // pieces per such pair (a pair needs 16 tiles per piece)
+constexpr int kMaxSlots = kLongSlots + kTailPairs * kTailPieces;   // partial slots at most
 struct SplitPlan {
-    SplitItem *items;        // [max_slots] pieces, in pair order
-    int32_t *counts;         // [0] pieces, [1] split pairs, [2] piece length L
+    SplitItem *items;        // [max_slots] pieces: long-row pieces from 0, last-round pieces from long_slots
+    int32_t *counts;         // [0] long-row pieces, [1] split pairs, [2] piece length L, [3] last-round pieces
     int32_t *pair_flag;      // [n_pairs] 0: not split, else first slot + 1
     int32_t *merge;          // [max_slots][3] pair, first slot, pieces (one entry per split pair)
     float *part_o;           // [max_slots][2 blocks][D][64 queries] normalised partial outputs
     float *part_lse;         // [max_slots][2 blocks][64] partial log2-sum-exp (scaled-score units)
-    int32_t max_slots;
+    int32_t max_slots;       // partial slots
+    int32_t long_slots;      // of which the first long_slots serve long-row pieces
 };
 
 struct AttnArgs {

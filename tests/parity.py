@@ -249,6 +249,42 @@ def sample_rows(wl: Workload, thr: np.ndarray, n_heads=2, n_blocks=32, seed=1):
     return np.array(rows, dtype=np.int64)
 
 
+# The bf16 forward's launch order (host-side mirror, for choosing test rows): whole
+# pairs are dispatched in the order of xcd_chunk_remap<256>, and with at least two
+# rounds of resident pairs (512) the last 384 of them are cut into pieces that run
+# at the end of the launch.
+def _xcd_remap(bid, n, x8=8):
+    x, k = bid % x8, bid // x8
+    per, rem = n // x8, n % x8
+    return x * per + min(x, rem) + k
+
+
+def _xcd_chunk_remap(bid, n, c=256, x8=8):
+    full = n // (x8 * c) * (x8 * c)
+    if bid >= full:
+        return full + _xcd_remap(bid - full, n - full)
+    x, k = bid % x8, bid // x8
+    return (k // c) * (x8 * c) + x * c + k % c
+
+
+def last_round_rows(wl: Workload, n_pairs_picked=6):
+    """Query blocks (global rows, batch 0 first) of some pairs the forward cuts into
+    last-round pieces; empty when the workload has fewer than two rounds of pairs."""
+    pph = (wl.blocks + 1) // 2
+    n = wl.batch * wl.heads * pph
+    if n < 2 * 512:
+        return np.zeros(0, dtype=np.int64)
+    picks = np.linspace(n - 384, n - 1, n_pairs_picked).round().astype(np.int64)
+    rows = []
+    for b in picks:
+        p = _xcd_chunk_remap(int(b), n)
+        bh, i = divmod(p, pph)
+        rows.append(bh * wl.blocks + 2 * i)
+        if 2 * i + 1 < wl.blocks:
+            rows.append(bh * wl.blocks + 2 * i + 1)
+    return np.array(rows, dtype=np.int64)
+
+
 def flops_kept(nnz: int, d: int) -> float:
     return 4.0 * 64 * 64 * d * nnz
 

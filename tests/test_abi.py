@@ -58,7 +58,7 @@ def test_capacity_and_workspace_formulas():
     expect = al(expect + 4 * rows)
     expect = al(expect + 4 * 12 * ((nB + 15) // 16))     # kept-block totals per 16-row group
     pairs = 12 * ((nB + 1) // 2)
-    slots = min(512, 4 * pairs)                           # attention row splitting
+    slots = min(512, 4 * pairs) + (384 * 4 if pairs >= 2 * 512 else 0)   # long-row and last-round pieces
     expect = al(expect + 32 * slots)                      # pieces
     expect = al(expect + 16)                              # plan counts
     expect = al(expect + 4 * pairs)                       # per-pair split flags

@@ -4,7 +4,8 @@ fp32 one in test_gpu_parity.py), in the launch configuration bench.py times.
 Selection: every row of every head is compared with the oracle under the
 mask rule in parity.py.  Attention: sampled query blocks (2 heads x 32 blocks,
 drawn with rng(1); for the jittered-threshold workload the heads with the
-lowest and highest threshold) under the oracle's block list, and the same
+lowest and highest threshold, and 12 blocks of pairs the forward cuts into
+last-round pieces) under the oracle's block list, and the same
 rows under the GPU's own block list where the two masks agree.  Backward (bf16):
 dQ, dK, dV over the whole block list with the upstream gradient on six of the
 sampled rows (see _backward_sampled).
@@ -63,7 +64,8 @@ def test_full_size_workload(name):
     _log("mask: " + P.fmt(rep))
     assert rep.unexcused == 0 and rep.window_missing == 0 and rep.invariant_fail == 0
 
-    sample = P.sample_rows(wl, thr)
+    # sampled blocks, plus blocks of pairs that the forward cuts into last-round pieces
+    sample = np.unique(np.concatenate([P.sample_rows(wl, thr), P.last_round_rows(wl)]))
     orp, oci = oracle.csr_from_mask(keep != 0)
     out_o, lse_o = P.gpu_forward(wl, qd, kd, vd, orp, oci)
     err, lerr = P.compare_rows(wl, out_o, lse_o, q32, k32, v32, orp, oci, sample)
