@@ -181,6 +181,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     } else {
         if (bid - ls - a.n_pairs >= a.plan.counts[3]) return;
         it = a.plan.items[bid - a.n_pairs];
+        if (it.pair < 0) return;      // a last-round pair that was not cut
         pair = it.pair;
     }
     const int64_t bh = pair / a.pairs_per_head;
@@ -530,11 +531,15 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
         mbase += tot_sp;
     }
     // the last round's pairs (the last T in dispatch order, unless already cut), in
-    // kTailPieces pieces each when every piece keeps 16 tiles
+    // kTailPieces pieces each when every piece keeps 16 tiles.  Their items are laid
+    // out by dispatch position so that each piece runs on the XCD that would have
+    // run its whole pair (workgroups are dealt to the XCDs round-robin): piece s of
+    // tail pair t sits at position 8 (kTailPieces (t / 8) + s) + t % 8, and an uncut
+    // pair leaves empty items there.  The partial slots stay consecutive per pair.
     __syncthreads();   // every pair_flag above is written
-    static_assert(kTailPairs <= 1024, "one pass");
+    static_assert(kTailPairs <= 1024 && kTailPairs % 8 == 0, "one pass, whole rounds of XCDs");
     const int64_t T = a.n_pairs >= 2 * kResidentPairs
-                          ? min((int64_t)kTailPairs, (int64_t)(P.max_slots - P.long_slots) / kTailPieces)
+                          ? min((int64_t)kTailPairs, (int64_t)(P.max_slots - P.long_slots) / kTailPieces) / 8 * 8
                           : 0;
     int32_t tail = 0;
     {
@@ -550,27 +555,32 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
         int32_t tot_ns, tot_sp;
         const int32_t excl = block_scan32(ns, scan, tot_ns);
         const int32_t mex = block_scan32(ns > 0 ? 1 : 0, scan, tot_sp);
-        if (ns) {
+        if (t < T) {
             const int32_t first = P.long_slots + excl;
-            P.pair_flag[p] = first + 1;
-            int32_t *me = P.merge + 3 * (int64_t)(mbase + mex);
-            me[0] = (int32_t)p;
-            me[1] = first;
-            me[2] = ns;
-            for (int32_t sI = 0; sI < ns; ++sI) {
-                SplitItem it;
-                it.pair = (int32_t)p;
-                it.slot = first + sI;
-                it.a0 = (int32_t)(bA + (eA - bA) * sI / ns);
-                it.a1 = (int32_t)(bA + (eA - bA) * (sI + 1) / ns);
-                it.ra = (int32_t)bA;
-                it.b0 = (int32_t)(bB + (eB - bB) * sI / ns);
-                it.b1 = (int32_t)(bB + (eB - bB) * (sI + 1) / ns);
-                it.rb = (int32_t)bB;
-                P.items[first + sI] = it;
+            if (ns) {
+                P.pair_flag[p] = first + 1;
+                int32_t *me = P.merge + 3 * (int64_t)(mbase + mex);
+                me[0] = (int32_t)p;
+                me[1] = first;
+                me[2] = ns;
+            }
+            for (int32_t sI = 0; sI < kTailPieces; ++sI) {
+                SplitItem it = {};
+                it.pair = -1;
+                if (sI < ns) {
+                    it.pair = (int32_t)p;
+                    it.slot = first + sI;
+                    it.a0 = (int32_t)(bA + (eA - bA) * sI / ns);
+                    it.a1 = (int32_t)(bA + (eA - bA) * (sI + 1) / ns);
+                    it.ra = (int32_t)bA;
+                    it.b0 = (int32_t)(bB + (eB - bB) * sI / ns);
+                    it.b1 = (int32_t)(bB + (eB - bB) * (sI + 1) / ns);
+                    it.rb = (int32_t)bB;
+                }
+                P.items[P.long_slots + 8 * (kTailPieces * (t / 8) + sI) + t % 8] = it;
             }
         }
-        tail = tot_ns;
+        tail = (int32_t)(T * kTailPieces);
         mbase += tot_sp;
     }
     if (t == 0) {
