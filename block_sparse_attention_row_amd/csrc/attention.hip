@@ -532,10 +532,13 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
     }
     // the last round's pairs (the last T in dispatch order, unless already cut), in
     // kTailPieces pieces each when every piece keeps 16 tiles.  Their items are laid
-    // out by dispatch position so that each piece runs on the XCD that would have
-    // run its whole pair (workgroups are dealt to the XCDs round-robin): piece s of
-    // tail pair t sits at position 8 (kTailPieces (t / 8) + s) + t % 8, and an uncut
-    // pair leaves empty items there.  The partial slots stay consecutive per pair.
+    // out by dispatch position: piece s of tail pair t sits at position
+    // 8 (s (T / 8) + t / 8) + t % 8, so that it runs on the XCD that would have run
+    // its whole pair (workgroups are dealt to the XCDs round-robin), and an XCD runs
+    // the first pieces of its pairs, then the second ones, and so on: pieces that
+    // run together walk the same part of the key range and share the L2, as whole
+    // pairs do.  An uncut pair leaves empty items; the partial slots stay
+    // consecutive per pair.
     __syncthreads();   // every pair_flag above is written
     static_assert(kTailPairs <= 1024 && kTailPairs % 8 == 0, "one pass, whole rounds of XCDs");
     const int64_t T = a.n_pairs >= 2 * kResidentPairs
@@ -577,7 +580,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
                     it.b1 = (int32_t)(bB + (eB - bB) * (sI + 1) / ns);
                     it.rb = (int32_t)bB;
                 }
-                P.items[P.long_slots + 8 * (kTailPieces * (t / 8) + sI) + t % 8] = it;
+                P.items[P.long_slots + 8 * (sI * (T / 8) + t / 8) + t % 8] = it;
             }
         }
         tail = (int32_t)(T * kTailPieces);
