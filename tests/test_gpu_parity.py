@@ -183,6 +183,33 @@ def test_long_rows_are_split_and_merged():
     assert err <= P.TOL["bf16"] and lerr <= P.LSE_TOL["bf16"]
 
 
+def test_long_rows_and_last_round_pieces_together():
+    """1,024 pairs (two rounds of 512 resident workgroups): rows of 64-140 tiles, so
+    the last 384 pairs in dispatch order are cut into quarter pieces, and a few rows
+    of 480 tiles, cut as long rows (the per-workgroup share is ~240 tiles).  Long
+    rows, rows of last-round pairs and random rows are compared with the oracle."""
+    wl = small_workload("rounds", 4, 128, (8, 8, 8), "bf16", seed=31)
+    q, k, v, _ = make_inputs(wl, "A")
+    qd, kd, vd = P.to_device(q, k, v)
+    nB = wl.blocks
+    assert nB == 512 and wl.heads * nB // 2 == 1024
+    rows = wl.heads * nB
+    rng = np.random.default_rng(11)
+    lens = rng.integers(64, 141, rows)
+    long_rows = np.array([3, 700, 1301, 2047])
+    lens[long_rows] = 480
+    mask = np.zeros((rows, nB), dtype=bool)
+    for r in range(rows):
+        mask[r, rng.choice(nB, size=int(lens[r]), replace=False)] = True
+    orp, oci = oracle.csr_from_mask(mask)
+    out, lse = P.gpu_forward(wl, qd, kd, vd, orp, oci)
+    tail = P.last_round_rows(wl)
+    assert len(tail) == 12
+    check = np.unique(np.concatenate([long_rows, long_rows ^ 1, tail, rng.choice(rows, 8, replace=False)]))
+    err, lerr = P.compare_rows(wl, out, lse, q, k, v, orp, oci, check)
+    assert err <= P.TOL["bf16"] and lerr <= P.LSE_TOL["bf16"]
+
+
 @pytest.mark.parametrize("dtype,d,grid,tile", [("bf16", 128, (3, 16, 24), (1, 8, 8)),
                                                  ("f32", 64, (4, 8, 16), (2, 4, 8)),
                                                  ("bf16", 64, (2, 32, 8), (1, 8, 8))])
