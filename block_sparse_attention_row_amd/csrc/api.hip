@@ -266,6 +266,7 @@ int32_t forward_impl(const sparse_attn_shape *shape, const void *q, const void *
     a.lse = lse;
     a.rows = d.rows;
     a.pairs_per_head = (int32_t)((d.nB + 1) / 2);
+    a.pair_stride = d.nT >= 2 ? (int32_t)(d.nTy * d.nTx) : 1;   // frame-neighbour pairs
     a.n_pairs = n_pairs(d);
     a.nB = (int32_t)d.nB;
     a.scale_log2 = effective_scale(shape) * kLog2e;

@@ -141,8 +141,9 @@ __device__ __forceinline__ void tile_scores_probs(const char *K, const bf16x8 *q
     }
 }
 
-// Workgroup of 4 waves = a pair of neighbouring query blocks of one (batch, head);
-// waves 2g and 2g+1 own queries 0-31 and 32-63 of block g.  The pair walks the
+// Workgroup of 4 waves = a pair of query blocks of one (batch, head), neighbours in
+// time (pair_blocks); waves 2g and 2g+1 own queries 0-31 and 32-63 of block g of
+// the pair.  The pair walks the
 // union of its two ascending CSR rows; each union tile is loaded once and computed
 // by the waves whose row keeps it.  The walk is software-pipelined one tile deep:
 // while the scores of tile j+1 are formed on MFMA, the softmax of tile j runs on
@@ -185,7 +186,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         pair = it.pair;
     }
     const int64_t bh = pair / a.pairs_per_head;
-    const int i0 = (int)(pair % a.pairs_per_head) * 2;
+    int32_t blk_a, blk_b;
+    pair_blocks((int32_t)(pair % a.pairs_per_head), a.pair_stride, a.nB, blk_a, blk_b);
     const int64_t N = (int64_t)a.nB * 64;
     const char *kg = (const char *)a.k + bh * N * ROWB + 16 * wave * ROWB;
     const char *vg = (const char *)a.v + bh * N * ROWB + 16 * wave * ROWB;
@@ -193,8 +195,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     const float c = a.scale_log2;
 
     // CSR ranges of the two rows (the second may not exist when nB is odd)
-    const int64_t rowA = bh * a.nB + i0;
-    const bool hasB = i0 + 1 < a.nB;
+    const int64_t rowA = bh * a.nB + blk_a, rowB = bh * a.nB + blk_b;
+    const bool hasB = blk_b >= 0;
+    const int blk = grp && hasB ? blk_b : blk_a;   // this wave's query block
     auto clamp_range = [&](int64_t r, int64_t &b, int64_t &e) {
         b = rp[r];
         e = rp[r + 1];
@@ -228,12 +231,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         lastB = prefix_max(it.rb, begB);
     } else {
         clamp_range(rowA, begA, endA);
-        if (hasB) clamp_range(rowA + 1, begB, endB);
+        if (hasB) clamp_range(rowB, begB, endB);
     }
     const bool has_row = grp == 0 || hasB;
 
     // Q fragments (B operand of S^T): query 32*(wave&1) + l32 of this wave's block, d = 16c + 8hh .. +7
-    const __bf16 *qg = (const __bf16 *)a.q + (bh * N + (int64_t)(i0 + grp) * 64) * D;
+    const __bf16 *qg = (const __bf16 *)a.q + (bh * N + (int64_t)blk * 64) * D;
     bf16x8 qf[D / 16];
 #pragma unroll
     for (int cq = 0; cq < D / 16; ++cq)
@@ -415,7 +418,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
                 l_tot > 0.f ? (BIAS ? m_run : m_run * c) + __log2f(l_tot) : -INFINITY;
         return;
     }
-    const int64_t qrow = bh * N + (int64_t)(i0 + grp) * 64 + 32 * (wave & 1) + l32;
+    const int64_t qrow = bh * N + (int64_t)blk * 64 + 32 * (wave & 1) + l32;
     __bf16 *og = (__bf16 *)a.out + qrow * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -444,10 +447,11 @@ __device__ __forceinline__ void row_range(const AttnArgs &a, int64_t r, int64_t 
 __device__ __forceinline__ void pair_ranges(const AttnArgs &a, int64_t p, int64_t &bA, int64_t &eA, int64_t &bB,
                                             int64_t &eB) {
     const int64_t bh = p / a.pairs_per_head;
-    const int i0 = (int)(p % a.pairs_per_head) * 2;
-    row_range(a, bh * a.nB + i0, bA, eA);
+    int32_t blk_a, blk_b;
+    pair_blocks((int32_t)(p % a.pairs_per_head), a.pair_stride, a.nB, blk_a, blk_b);
+    row_range(a, bh * a.nB + blk_a, bA, eA);
     bB = eB = 0;
-    if (i0 + 1 < a.nB) row_range(a, bh * a.nB + i0 + 1, bB, eB);
+    if (blk_b >= 0) row_range(a, bh * a.nB + blk_b, bB, eB);
 }
 
 // Sum over the 1024 threads of the workgroup, returned to every thread.
@@ -607,10 +611,12 @@ __global__ __launch_bounds__(512) void merge_kernel(AttnArgs a) {
     const int first = me[1], ns = me[2];
     const int t = threadIdx.x, q = t & 63, dq = (t >> 6) & 3, g = t >> 8;
     const int64_t bh = pair / a.pairs_per_head;
-    const int i0 = (int)(pair % a.pairs_per_head) * 2;
-    if (i0 + g >= a.nB) return;
+    int32_t blk_a, blk_b;
+    pair_blocks((int32_t)(pair % a.pairs_per_head), a.pair_stride, a.nB, blk_a, blk_b);
+    const int32_t blk = g ? blk_b : blk_a;
+    if (blk < 0) return;
     const int64_t N = (int64_t)a.nB * 64;
-    const int64_t qrow = bh * N + (int64_t)(i0 + g) * 64 + q;
+    const int64_t qrow = bh * N + (int64_t)blk * 64 + q;
     const float *pl = a.plan.part_lse + ((int64_t)first * 2 + g) * 64 + q;   // piece s at pl[128 s]
     float mx = -INFINITY;
     for (int sI = 0; sI < ns; ++sI) mx = fmaxf(mx, pl[128 * sI]);

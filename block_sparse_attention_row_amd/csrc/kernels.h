@@ -102,6 +102,25 @@ struct SplitPlan {
     int32_t long_slots;      // of which the first long_slots serve long-row pieces
 };
 
+// Query-block pairs of the bf16 forward.  Blocks are frame-major (b = t S + s with
+// S blocks per frame), and neighbouring frames keep nearly the same key blocks, so
+// a pair is two frame-neighbours: pair p < (nT / 2) S of a head is
+// (2u S + s, (2u + 1) S + s), u = p / S, s = p mod S; an odd last frame pairs its
+// own blocks side by side ((nT - 1) S + 2 s', + 1; the last one alone when S is
+// odd).  Either way a head has ceil(nB / 2) pairs.  S = 1 gives (2p, 2p + 1).
+__host__ __device__ inline void pair_blocks(int32_t p, int32_t S, int32_t nB, int32_t &blk_a, int32_t &blk_b) {
+    const int32_t nT = nB / S, full = (nT / 2) * S;
+    if (p < full) {
+        const int32_t u = p / S, s = p - u * S;
+        blk_a = 2 * u * S + s;
+        blk_b = blk_a + S;
+    } else {
+        const int32_t s2 = p - full;
+        blk_a = (nT - 1) * S + 2 * s2;
+        blk_b = 2 * s2 + 1 < S ? blk_a + 1 : -1;
+    }
+}
+
 struct AttnArgs {
     const void *q, *k, *v;
     const int32_t *row_ptr, *col_idx;
@@ -113,6 +132,7 @@ struct AttnArgs {
     int64_t n_pairs;          // B*H*pairs_per_head (query-block pairs of the bf16 kernel)
     int32_t pairs_per_head;   // ceil(nB / 2)
     int32_t nB;
+    int32_t pair_stride;      // S of pair_blocks: blocks per frame, or 1
     float scale_log2;         // softmax scale * log2(e)
     SplitPlan plan;           // bf16 path only
 };

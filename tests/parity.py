@@ -267,6 +267,24 @@ def _xcd_chunk_remap(bid, n, c=256, x8=8):
     return (k // c) * (x8 * c) + x * c + k % c
 
 
+def pair_blocks(p, s, nb):
+    """Blocks of query-block pair p of a head in the forward: frame-neighbours (stride
+    s = blocks per frame), an odd last frame side by side; -1 for no second block."""
+    nt = nb // s
+    full = (nt // 2) * s
+    if p < full:
+        u, r = divmod(p, s)
+        return 2 * u * s + r, 2 * u * s + r + s
+    s2 = p - full
+    a = (nt - 1) * s + 2 * s2
+    return a, (a + 1 if 2 * s2 + 1 < s else -1)
+
+
+def pair_stride(wl: Workload):
+    nt, ny, nx = wl.block_grid
+    return ny * nx if nt >= 2 else 1
+
+
 def last_round_rows(wl: Workload, n_pairs_picked=6):
     """Query blocks (global rows, batch 0 first) of some pairs the forward cuts into
     last-round pieces; empty when the workload has fewer than two rounds of pairs."""
@@ -279,9 +297,10 @@ def last_round_rows(wl: Workload, n_pairs_picked=6):
     for b in picks:
         p = _xcd_chunk_remap(int(b), n)
         bh, i = divmod(p, pph)
-        rows.append(bh * wl.blocks + 2 * i)
-        if 2 * i + 1 < wl.blocks:
-            rows.append(bh * wl.blocks + 2 * i + 1)
+        ba, bb = pair_blocks(i, pair_stride(wl), wl.blocks)
+        rows.append(bh * wl.blocks + ba)
+        if bb >= 0:
+            rows.append(bh * wl.blocks + bb)
     return np.array(rows, dtype=np.int64)
 
 

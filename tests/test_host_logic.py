@@ -1,5 +1,6 @@
-"""Host-side logic of bench.py (no GPU): the one-GPU guard, the HBM-traffic record
-and the check that ties a stored traffic figure to its kernel source and workload."""
+"""Host-side logic with no GPU: bench.py's one-GPU guard, its HBM-traffic record and
+the check that ties a stored traffic figure to its kernel source and workload, and
+the forward's query-block pairing as mirrored by the tests."""
 import csv
 import hashlib
 import json
@@ -63,3 +64,22 @@ def test_stored_traffic_needs_the_same_source_and_workload(tmp_path, monkeypatch
     assert bench.stored_traffic("wan13b_480p") is None        # kernel changed since the counters
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
     assert bench.stored_traffic("wan13b_480p") is None
+
+
+@pytest.mark.parametrize("nt,s", [(20, 24), (21, 60), (7, 15), (3, 3), (1, 24), (480, 1), (105, 1), (2, 1)])
+def test_forward_pairs_cover_every_block_once(nt, s):
+    """The host mirror of the forward's query-block pairs (tests/parity.py) is a
+    partition of the blocks into ceil(nB/2) pairs of frame-neighbours (side by side in
+    an odd last frame)."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import parity as P
+    nb = nt * s
+    stride = s if nt >= 2 else 1
+    seen = []
+    for p in range((nb + 1) // 2):
+        a, b = P.pair_blocks(p, stride, nb)
+        seen.append(a)
+        if b >= 0:
+            seen.append(b)
+            assert b == a + stride or (a // stride == nt - 1 and b == a + 1)
+    assert sorted(seen) == list(range(nb))
