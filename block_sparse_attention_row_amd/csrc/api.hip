@@ -528,6 +528,7 @@ int32_t sparse_attn_backward(const sparse_attn_shape *shape, const void *q, cons
     b.args.dn = (float *)(ws + L.dn);
     b.args.n_pairs = n_pairs(d);
     b.args.pairs_per_head = (int32_t)((d.nB + 1) / 2);
+    b.args.pair_stride = d.nT >= 2 ? (int32_t)(d.nTy * d.nTx) : 1;   // frame-neighbour pairs
     b.args.nB = (int32_t)d.nB;
     b.args.scale = effective_scale(shape);
     b.args.scale_log2 = b.args.scale * kLog2e;

@@ -13,7 +13,8 @@
 //           S^T = K Q^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T;
 //   dV, dK  a pair of key blocks walks the transposed list (query tiles streamed):
 //           S = Q K^T, P, dP = dO V^T, dS, then dV^T += dO^T P and dK^T += Q^T dS.
-// Each is the forward's tile machinery with other operands: the streamed tile is
+// Pairs are neighbours in time, as in the forward (pair_blocks).  Each pass is the
+// forward's tile machinery with other operands: the streamed tile is
 // the A operand of the scores and, read transposed, of the output product; the
 // pair's own rows sit in registers as the B operand.  The transposed list (for
 // every key block, the query blocks that keep it, ascending) is built from row
@@ -160,15 +161,16 @@ __global__ __launch_bounds__(256, MODE == kDKV && D == 128 ? 1 : 2) void bwd_ker
     const int grp = wave >> 1, half = wave & 1;   // block of the pair, 32-row half of the block
     const int64_t pair = xcd_chunk_remap<256>(blockIdx.x, a.n_pairs);
     const int64_t bh = pair / a.pairs_per_head;
-    const int i0 = (int)(pair % a.pairs_per_head) * 2;
+    int32_t blk_a, blk_b;   // the pair's two blocks, neighbours in time (pair_blocks)
+    pair_blocks((int32_t)(pair % a.pairs_per_head), a.pair_stride, a.nB, blk_a, blk_b);
     const int64_t N = (int64_t)a.nB * 64;
     // streamed tiles: key tiles K, V for dQ; query tiles Q, dO for dV and dK
     const char *t1g = (const char *)(MODE == kDQ ? a.k : a.q) + bh * N * ROWB + 16 * wave * ROWB;
     const char *t2g = (const char *)(MODE == kDQ ? a.v : a.dout) + bh * N * ROWB + 16 * wave * ROWB;
     const float c = a.scale_log2;
 
-    const int64_t rowA = bh * a.nB + i0;
-    const bool hasB = i0 + 1 < a.nB;
+    const int64_t rowA = bh * a.nB + blk_a, rowB = bh * a.nB + blk_b;
+    const bool hasB = blk_b >= 0;
     auto clamp_range = [&](int64_t r, int64_t &b, int64_t &e) {
         b = a.ptr[r];
         e = a.ptr[r + 1];
@@ -178,12 +180,12 @@ __global__ __launch_bounds__(256, MODE == kDKV && D == 128 ? 1 : 2) void bwd_ker
     };
     int64_t begA, endA, begB = 0, endB = 0;
     clamp_range(rowA, begA, endA);
-    if (hasB) clamp_range(rowA + 1, begB, endB);
+    if (hasB) clamp_range(rowB, begB, endB);
     const bool has_row = grp == 0 || hasB;
 
     // the pair's own rows, B operands of the score products: queries and dO (dQ), keys
-    // (dV), keys and V (dK); row 32 half + l32 of block i0 + grp, d = 16 cq + 8 hh ..
-    const int64_t own = bh * N + (int64_t)(i0 + grp) * 64 + 32 * half + l32;
+    // (dV), keys and V (dK); row 32 half + l32 of the pair's block grp, d = 16 cq + 8 hh ..
+    const int64_t own = bh * N + (int64_t)(grp && hasB ? blk_b : blk_a) * 64 + 32 * half + l32;
     const __bf16 *o1 = (const __bf16 *)(MODE == kDQ ? a.q : a.k) + own * D;
     const __bf16 *o2 = (const __bf16 *)(MODE == kDQ ? a.dout : a.v) + own * D;
     bf16x8 f1[D / 16], f2[D / 16];

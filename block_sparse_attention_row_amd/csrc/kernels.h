@@ -174,6 +174,7 @@ struct BwdArgs {
     void *grad2;                  // second gradient of the fused dV + dK pass (dK; grad is dV)
     int64_t n_pairs;              // B*H*ceil(nB/2) pairs of blocks
     int32_t pairs_per_head, nB;
+    int32_t pair_stride;          // S of pair_blocks (blocks per frame, or 1)
     float scale_log2, scale;
 };
 struct BwdLaunch {
