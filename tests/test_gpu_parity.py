@@ -36,6 +36,8 @@ SMALL = [
     ("bf16_d128_page", 3, 128, (4, 6, 8), "bf16", 0.9, (-1, -1, -1), "page", None, 1),
     ("bf16_d128_dense", 2, 128, (2, 3, 3), "bf16", 1.0, (-1, -1, -1), "A", None, 1),
     ("bf16_d128_one_block", 2, 128, (1, 1, 1), "bf16", 0.5, (-1, -1, -1), "A", None, 1),
+    # one frame of 35 blocks: the forward pairs blocks side by side, the last alone
+    ("bf16_d128_one_frame", 2, 128, (1, 5, 7), "bf16", 0.85, (-1, -1, -1), "A", None, 1),
 ]
 
 
