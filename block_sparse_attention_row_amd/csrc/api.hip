@@ -90,7 +90,7 @@ Layout layout(const Dims &d) {
     l.thr = off;
     off = align_up(off + 4 * d.H, kAlign);
     l.kbar = off;
-    off = align_up(off + 4 * d.B * d.H * d.nB * d.D, kAlign);
+    off = align_up(off + 4 * d.B * d.H * groups_per_head(d) * kGroupRows * d.D, kAlign);   // key means, 16-key groups
     l.status = off;
     off = align_up(off + 8 * n_groups(d), kAlign);
     l.ticket = off;
@@ -210,7 +210,7 @@ int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_sel
             tmp[i] = params->head_thresholds ? params->head_thresholds[h0 + i] : params->threshold;
         if (launch_fill_thresholds(tmp, n, thr + h0, s)) return SPARSE_ATTN_HIP_ERROR;
     }
-    if (launch_pool_keys(k, kbar, d.B * d.H * d.nB, shape->dtype, (int)d.D, side, s)) return SPARSE_ATTN_HIP_ERROR;
+    if (launch_pool_keys(k, kbar, d.B * d.H * d.nB, d.nB, shape->dtype, (int)d.D, side, s)) return SPARSE_ATTN_HIP_ERROR;
 
     SelectArgs a;
     a.q = q;
@@ -333,7 +333,7 @@ int32_t sparse_attn_select_sip(const sparse_attn_shape *shape, const sparse_attn
     side.status = status;
     side.n_status = n_groups(d);
     side.ticket = ticket;
-    if (launch_pool_keys(k, kbar, d.B * d.H * d.nB, shape->dtype, (int)d.D, side, s)) return SPARSE_ATTN_HIP_ERROR;
+    if (launch_pool_keys(k, kbar, d.B * d.H * d.nB, d.nB, shape->dtype, (int)d.D, side, s)) return SPARSE_ATTN_HIP_ERROR;
 
     SelectArgs a = {};
     a.q = q;
@@ -402,7 +402,7 @@ int32_t sparse_attn_select_ibcs(const sparse_attn_shape *shape, const sparse_att
             tmp[i] = params->head_thresholds ? params->head_thresholds[h0 + i] : params->threshold;
         if (launch_fill_thresholds(tmp, n, thr + h0, s)) return SPARSE_ATTN_HIP_ERROR;
     }
-    if (launch_pool_keys(k, kbar, d.B * d.H * d.nB, shape->dtype, (int)d.D, side, s)) return SPARSE_ATTN_HIP_ERROR;
+    if (launch_pool_keys(k, kbar, d.B * d.H * d.nB, d.nB, shape->dtype, (int)d.D, side, s)) return SPARSE_ATTN_HIP_ERROR;
 
     IbcsArgs m;
     m.q = (const __bf16 *)q;

@@ -16,6 +16,16 @@ struct ThrChunk {
 // ceil(nB/16)).  Each group's kept-block total feeds the CSR prefix.
 constexpr int kGroupRows = 16;
 
+// Key block means are stored in the B-operand order of v_mfma_f32_16x16x32_bf16, 16
+// key blocks to a group, groups padded per (batch, head): group g of head bh starts at
+// element (bh * ceil(nB / 16) + g) * 32 D; inside it, part p (0: hi = bf16(x), 1: lo =
+// bf16(x - hi)), k-block kb and lane L = ii + 16 kq hold the 8 elements 32 kb + 8 kq ..
+// 32 kb + 8 kq + 7 of key block 16 g + ii, at element p * 16 D + 512 kb + 8 L.  Every
+// operand load of a wave is then one contiguous 1 KiB run.
+__host__ __device__ constexpr int64_t kbar_group(int64_t bh, int64_t groups_per_head, int64_t g, int D) {
+    return (bh * groups_per_head + g) * 32 * D;
+}
+
 // Side job done by the pooling kernel for the selection that follows.
 struct PoolSide {
     ThrChunk thr;             // first thresholds, by value
@@ -38,7 +48,7 @@ constexpr int kSelectMaxBlocks = 4096;
 
 struct SelectArgs {
     const void *q;            // [BH*N][D] queries in the input dtype (tile-major)
-    const __bf16 *kbar;       // [BH*nB][2][D] key block means as bf16 pairs (hi, then lo)
+    const __bf16 *kbar;       // key block means as bf16 pairs, in fragment order (kbar_group)
     const float *thr;         // [H] thresholds (device)
     uint64_t *status;         // [n_groups] look-back words (zeroed by the pooling kernel)
     uint32_t *ticket;         // group ticket counter (zeroed by the pooling kernel)
@@ -64,7 +74,7 @@ struct SelectArgs {
 constexpr int kIbcsClusters = 8, kIbcsIters = 4;
 struct IbcsArgs {
     const __bf16 *q;          // [BH*N][D] queries (bf16, tile-major)
-    const __bf16 *kbar;       // [BH*nB][2][D] key block means (hi | lo)
+    const __bf16 *kbar;       // key block means (hi | lo), in fragment order (kbar_group)
     float *rows;              // [heads][pairs][nBp]: log2 of the mixture row of each pair
     int64_t head0;            // first (batch, head) of this launch
     int32_t nB, nBp, pairs_per_head;
@@ -146,7 +156,7 @@ struct ReorderArgs {
 };
 int launch_reorder(const void *src, void *dst, const ReorderArgs &a, int64_t tiles, hipStream_t s);
 
-int launch_pool_keys(const void *k, __bf16 *kbar, int64_t nblocks, int dtype, int d, const PoolSide &side,
+int launch_pool_keys(const void *k, __bf16 *kbar, int64_t nblocks, int32_t nB, int dtype, int d, const PoolSide &side,
                      hipStream_t s);
 int launch_fill_thresholds(const float *host_thr, int n, float *dst, hipStream_t s);
 int launch_select(const SelectArgs &a, int d, int dtype, hipStream_t s);

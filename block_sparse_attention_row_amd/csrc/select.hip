@@ -74,13 +74,30 @@ template <typename T, int D, int BATCH> struct BlockPool {
         *reinterpret_cast<bv *>(row + col(lane)) = hi;
         *reinterpret_cast<bv *>(row + D + col(lane)) = lo;
     }
+    // the same pair in the key means' fragment order (kbar_group): lane's columns
+    // col .. col+VEC-1 share one k-block kb and one 8-column slice kq
+    static __device__ __forceinline__ void store_frag(const float (&x)[VEC], __bf16 *group, int ii, int lane) {
+        typedef __attribute__((ext_vector_type(VEC))) float fv;
+        typedef __attribute__((ext_vector_type(VEC))) __bf16 bv;
+        fv xv, r;
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) xv[c] = x[c];
+        const bv hi = __builtin_convertvector(xv, bv);
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) r[c] = xv[c] - (float)hi[c];
+        const bv lo = __builtin_convertvector(r, bv);
+        const int d0 = col(lane), kb = d0 / 32, kq = (d0 % 32) / 8;
+        __bf16 *at = group + 512 * kb + 8 * (ii + 16 * kq) + d0 % 8;
+        *reinterpret_cast<bv *>(at) = hi;
+        *reinterpret_cast<bv *>(at + 16 * D) = lo;
+    }
 };
 
-// Key block means, one wave per block.  Side jobs for the selection that follows:
+// Key block means, one wave per block, stored in fragment order (kbar_group).  Side jobs for the selection that follows:
 // the first ThrChunk::kMax thresholds, and zeroing its ticket and look-back words.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ k, __bf16 *__restrict__ kbar,
-                                                   int64_t nblocks, PoolSide side) {
+                                                   int64_t nblocks, int32_t nB, PoolSide side) {
     const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (blockIdx.x == 0 && (int)threadIdx.x < side.n_thr) side.thr_dst[threadIdx.x] = side.thr.v[threadIdx.x];
     for (int64_t i = gt; i < side.n_status; i += (int64_t)gridDim.x * blockDim.x) side.status[i] = 0;
@@ -91,7 +108,9 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ k, __bf
     if (blk >= nblocks) return;
     float x[P::VEC];
     P::mean(k + blk * kTokensPerBlock * D, lane, x);
-    if (lane < P::LPR) P::store_split(x, kbar + blk * (2 * D), lane);
+    const int64_t bh = blk / nB;
+    const int j = (int)(blk - bh * nB);
+    if (lane < P::LPR) P::store_frag(x, kbar + kbar_group(bh, (nB + 15) / 16, j / 16, D), j % 16, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -422,7 +441,7 @@ __global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
     const uint32_t bh = g / (uint32_t)a.groups_per_head;
     const int i0 = (int)(g - bh * (uint32_t)a.groups_per_head) * kSelRows;
     const int nrows = min(kSelRows, a.nB - i0);
-    const __bf16 *ks = a.kbar + ((int64_t)bh * a.nB) * (2 * D);
+    const __bf16 *ks = a.kbar + kbar_group(bh, a.groups_per_head, 0, D);
     const float thr = a.thr[bh % (uint32_t)a.H];
 
     const int ii = lane & 15, kq = lane >> 4;
@@ -437,14 +456,16 @@ __global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
         }
     } else {
     bf16x8 kh[2][KB], kl[2][KB];
-    // keys past nB read row 0 (in bounds); their scores land on padding columns
+    // the 16 keys of group 16 cc + wave, one contiguous 1 KiB run per load; groups past
+    // the head's last read its first (in bounds), and keys past nB inside the last
+    // group read its padding: their scores land on padding columns
     auto load_k = [&](int cc, int slot) {
-        const int jj = kSelChunk * cc + 16 * wave + ii;
-        const __bf16 *kr = ks + (int64_t)(jj < a.nB ? jj : 0) * (2 * D) + 8 * kq;
+        const int gg = (kSelChunk / 16) * cc + wave;
+        const __bf16 *kr = ks + (int64_t)(gg < a.groups_per_head ? gg : 0) * (32 * D) + 8 * lane;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            kh[slot][kb] = *reinterpret_cast<const bf16x8 *>(kr + 32 * kb);
-            kl[slot][kb] = *reinterpret_cast<const bf16x8 *>(kr + D + 32 * kb);
+            kh[slot][kb] = *reinterpret_cast<const bf16x8 *>(kr + 512 * kb);
+            kl[slot][kb] = *reinterpret_cast<const bf16x8 *>(kr + 16 * D + 512 * kb);
         }
     };
     // ---- the group's pooled queries (hi | lo), one query block per wave
@@ -548,17 +569,17 @@ __global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-int launch_pool_keys(const void *k, __bf16 *kbar, int64_t nblocks, int dtype, int d, const PoolSide &side,
+int launch_pool_keys(const void *k, __bf16 *kbar, int64_t nblocks, int32_t nB, int dtype, int d, const PoolSide &side,
                      hipStream_t s) {
     const dim3 grid((unsigned)((nblocks + 3) / 4)), block(256);
     if (dtype == 1 && d == 128)
-        pool_kernel<__bf16, 128><<<grid, block, 0, s>>>((const __bf16 *)k, kbar, nblocks, side);
+        pool_kernel<__bf16, 128><<<grid, block, 0, s>>>((const __bf16 *)k, kbar, nblocks, nB, side);
     else if (dtype == 1 && d == 64)
-        pool_kernel<__bf16, 64><<<grid, block, 0, s>>>((const __bf16 *)k, kbar, nblocks, side);
+        pool_kernel<__bf16, 64><<<grid, block, 0, s>>>((const __bf16 *)k, kbar, nblocks, nB, side);
     else if (dtype == 0 && d == 128)
-        pool_kernel<float, 128><<<grid, block, 0, s>>>((const float *)k, kbar, nblocks, side);
+        pool_kernel<float, 128><<<grid, block, 0, s>>>((const float *)k, kbar, nblocks, nB, side);
     else
-        pool_kernel<float, 64><<<grid, block, 0, s>>>((const float *)k, kbar, nblocks, side);
+        pool_kernel<float, 64><<<grid, block, 0, s>>>((const float *)k, kbar, nblocks, nB, side);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -764,17 +785,18 @@ __global__ __launch_bounds__(1024) void ibcs_mix_kernel(IbcsArgs a) {
     // ---- scores, chunk by chunk, into the register row of wave 8P + c (as in the
     //      selection: 16 rows x 16 keys per wave and chunk, parked in the LDS stage)
     const int ii = lane & 15, kq = lane >> 4;
-    const __bf16 *ks = a.kbar + (bh * a.nB) * (2 * D);
+    const int32_t kgph = (a.nB + 15) / 16;   // key groups per head
+    const __bf16 *ks = a.kbar + kbar_group(bh, kgph, 0, D);
     float s[NE];
 #pragma unroll
     for (int cc = 0; cc < NCH; ++cc) {
         bf16x8 kh[KB], kl[KB];
-        const int jj = kSelChunk * cc + 16 * wave + ii;
-        const __bf16 *kr = ks + (int64_t)(jj < a.nB ? jj : 0) * (2 * D) + 8 * kq;   // (padding keys read row 0)
+        const int gg = (kSelChunk / 16) * cc + wave;   // key group (padding groups read the first)
+        const __bf16 *kr = ks + (int64_t)(gg < kgph ? gg : 0) * (32 * D) + 8 * lane;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            kh[kb] = *reinterpret_cast<const bf16x8 *>(kr + 32 * kb);
-            kl[kb] = *reinterpret_cast<const bf16x8 *>(kr + D + 32 * kb);
+            kh[kb] = *reinterpret_cast<const bf16x8 *>(kr + 512 * kb);
+            kl[kb] = *reinterpret_cast<const bf16x8 *>(kr + 16 * D + 512 * kb);
         }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         const __bf16 *qrow = qf + ii * QW + 8 * kq;

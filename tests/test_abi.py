@@ -51,7 +51,7 @@ def test_capacity_and_workspace_formulas():
     expect = 0
     al = lambda x: (x + 255) // 256 * 256
     expect = al(expect + 4 * 12)
-    expect = al(expect + 4 * rows * 128)                  # key block means (bf16 hi | lo)
+    expect = al(expect + 4 * 12 * ((nB + 15) // 16) * 16 * 128)   # key block means (bf16 hi | lo), 16-key groups
     expect = al(expect + 8 * 12 * ((nB + 15) // 16))      # selection look-back words per 16-row group
     expect = al(expect + 16)                              # selection ticket counter
     expect = al(expect + 8 * rows * (nbp // 64))
