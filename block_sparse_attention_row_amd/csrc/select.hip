@@ -155,12 +155,79 @@ template <int D> constexpr size_t select_lds_bytes() {
            (size_t)kSelRows * 256 * 4;
 }
 
+// Pivot steps of the cut over an array of keys v (the register row, or the bracket
+// compacted out of it; zeros are inert).  The key bracket (lo, hi] keeps
+//   Mhi = mass(key > hi) < thr*Z <= Mlo = mass(key > lo),
+// with clo, chi the counts of keys above lo and hi; mass and count of the keys above
+// the array's own range come in as m0, c0.  Each step splits the bracket at a pivot,
+// at one compare/select/add per element plus a wave sum; the compare masks'
+// popcounts count the keys.  Pivots alternate between regula falsi on the values
+// (the mass above a value is linear in the value when the e_j are spread evenly in
+// log scale) and halving the key range, which bounds the steps.  Steps run while the
+// bracket holds more than `stop` keys and more than one key value.
+template <int N>
+__device__ __forceinline__ void pivot_steps(const float (&v)[N], float thrz, float m0, uint32_t c0, uint32_t stop,
+                                            uint32_t &lo, uint32_t &hi, float &Mlo, float &Mhi, uint32_t &clo,
+                                            uint32_t &chi, int &step) {
+#pragma unroll 1
+    for (; clo - chi > stop && hi - lo > 1; ++step) {
+        uint32_t p;
+        if (step < 2 || (step & 1) == 0) {
+            const float vlo = __uint_as_float(lo), vhi = __uint_as_float(hi);
+            const float f = (thrz - Mhi) / (Mlo - Mhi);
+            p = __float_as_uint(vhi - f * (vhi - vlo));
+            p = min(max(p, lo + 1u), hi - 1u);
+        } else {
+            p = lo + ((hi - lo) >> 1);
+        }
+        float acc = 0.f;
+        uint32_t cnt = c0;
+#pragma unroll
+        for (int c = 0; c < N; ++c) {
+            const bool gt = __float_as_uint(v[c]) > p;
+            acc += gt ? v[c] : 0.f;
+            cnt += (uint32_t)__popcll(__ballot(gt));
+        }
+        const float A = m0 + wave_sum_u(acc);
+        if (A < thrz) {
+            hi = p;
+            Mhi = A;
+            chi = cnt;
+        } else {
+            lo = p;
+            Mlo = A;
+            clo = cnt;
+        }
+    }
+}
+
+// The keys of v inside (lo, hi], in index order, to dst (LDS); returns how many.
+template <int N>
+__device__ __forceinline__ uint32_t compact_bracket(const float (&v)[N], uint32_t lo, uint32_t hi, uint32_t *dst) {
+    uint32_t base = 0;
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+        const uint32_t u = __float_as_uint(v[c]);
+        const bool in = u > lo && u <= hi;
+        const uint64_t m = __ballot(in);
+        if (in) dst[base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = u;
+        base += (uint32_t)__popcll(m);
+    }
+    return base;
+}
+
+// Quotient of j by d for j, d <= 4096: j * ceil(2^24 / d) / 2^24 is exact while
+// j (d - 1) < 2^24.  m24 = ceil(2^24 / d) is formed once per wave.
+__device__ __forceinline__ uint32_t div_small(uint32_t j, uint32_t m24) { return __umulhi(j << 8, m24); }
+
 // The cut of row i (threshold thr), run by one wave on its register row s (scaled
 // scores, -inf for padding keys).  Returns the row's bitmask (lane c holds the word
-// of key blocks 64c .. 64c+63) and its count.
+// of key blocks 64c .. 64c+63) and its count.  `bracket` is 512 words of LDS for this
+// wave, `hist_all` holds 256 words per wave.
 template <int NE>
-__device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], float *hist_all, int i, float thr,
-                                           int lane, uint64_t &word, int32_t &count_out) {
+__device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], float *hist_all, uint32_t *bracket,
+                                           int i, float thr, int lane, uint64_t &word, int32_t &count_out) {
+    constexpr int NC = 8;                  // compacted bracket: 8 words a lane, 512 keys
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool keep_all = !(thr < 1.f);
     uint32_t *list = reinterpret_cast<uint32_t *>(hist_all + wave * 256);   // up to 64 keys of the bracket
@@ -185,64 +252,43 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
     const float thrz = thr * Z;
 
     // Crossing value v* and the mass M strictly above it.  Keys are the fp32 bit
-    // patterns of the e_j (order-preserving for e >= 0).  The key bracket (lo, hi]
-    // keeps  Mhi = mass(key > hi) < thr*Z <= Mlo = mass(key > lo);  each step splits it
-    // at a pivot and costs one compare/select/add per element plus a wave sum; the
-    // compare masks' popcounts track how many elements the bracket holds.  Pivots
-    // alternate between regula falsi on the values (the mass above a value is linear
-    // in the value when the e_j are spread evenly in log scale) and halving the key
-    // range, which bounds the steps.  Once at most 64 elements remain they are
-    // compacted to LDS, sorted across the lanes, and the crossing is read off their
-    // prefix sums.
+    // patterns of the e_j (order-preserving for e >= 0).  Pivot steps over the row
+    // until the bracket holds at most 512 keys; on long rows those are then compacted
+    // (through LDS) into NC words a lane and the steps go on over them.  Once at most
+    // 64 keys remain they are compacted to LDS, sorted across the lanes, and the
+    // crossing is read off their prefix sums.
     uint32_t vstar = 0x3f800000u;
     float M = 0.f;
     if (!keep_all) {
         uint32_t lo = wave_min_u32(kmin), hi = 0x3f800000u;   // every e_j <= 1, the row max is exactly 1
         float Mhi = 0.f, Mlo = Z;
         uint32_t clo = npos, chi = 0;                         // counts of key > lo, key > hi
-#pragma unroll 1
-        for (int step = 0; clo - chi > 64 && hi - lo > 1; ++step) {
-            uint32_t p;
-            if (step < 2 || (step & 1) == 0) {
-                const float vlo = __uint_as_float(lo), vhi = __uint_as_float(hi);
-                const float f = (thrz - Mhi) / (Mlo - Mhi);
-                p = __float_as_uint(vhi - f * (vhi - vlo));
-                p = min(max(p, lo + 1u), hi - 1u);
-            } else {
-                p = lo + ((hi - lo) >> 1);
-            }
-            float acc = 0.f;
-            uint32_t cnt = 0;
+        int step = 0;
+        bool packed = false;
+        float t[NC];
+        if constexpr (NE > NC) {
+            pivot_steps(s, thrz, 0.f, 0u, 64u * NC, lo, hi, Mlo, Mhi, clo, chi, step);
+            if (clo - chi > 64 && hi - lo > 1) {
+                const float m0 = Mhi;
+                const uint32_t c0 = chi, n = compact_bracket(s, lo, hi, bracket);
+                wave_lds_sync();
 #pragma unroll
-            for (int c = 0; c < NE; ++c) {
-                const bool gt = __float_as_uint(s[c]) > p;
-                acc += gt ? s[c] : 0.f;
-                cnt += (uint32_t)__popcll(__ballot(gt));
+                for (int w = 0; w < NC; ++w)
+                    t[w] = (uint32_t)(64 * w + lane) < n ? __uint_as_float(bracket[64 * w + lane]) : 0.f;
+                wave_lds_sync();
+                pivot_steps(t, thrz, m0, c0, 64u, lo, hi, Mlo, Mhi, clo, chi, step);
+                packed = true;
             }
-            const float A = wave_sum_u(acc);
-            if (A < thrz) {
-                hi = p;
-                Mhi = A;
-                chi = cnt;
-            } else {
-                lo = p;
-                Mlo = A;
-                clo = cnt;
-            }
+        } else {
+            pivot_steps(s, thrz, 0.f, 0u, 64u, lo, hi, Mlo, Mhi, clo, chi, step);
         }
         vstar = hi;       // a single key left in the bracket: v* = hi, M = Mhi
         M = Mhi;
         if (clo - chi <= 64 && clo > chi) {
-            uint32_t base = 0;
-#pragma unroll
-            for (int c = 0; c < NE; ++c) {
-                const uint32_t u = __float_as_uint(s[c]);
-                const bool in = u > lo && u <= hi;
-                const uint64_t m = __ballot(in);
-                if (in)
-                    list[base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = u;
-                base += (uint32_t)__popcll(m);
-            }
+            if (packed)
+                compact_bracket(t, lo, hi, list);
+            else
+                compact_bracket(s, lo, hi, list);
             wave_lds_sync();
             const uint32_t n = clo - chi;
             uint32_t u = (uint32_t)lane < n ? list[lane] : 0u;
@@ -268,9 +314,15 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
     }
 
     // ---- kept = key above v*, or equal to v* with M + (its rank among the equal
-    //      keys, by index) * v* below thr*Z, or inside the window
+    //      keys, by index) * v* below thr*Z, or inside the window: frames form a
+    //      contiguous range of j, rows and columns come from exact small quotients
     const int nTyx = a.nTy * a.nTx;
     const int ti = i / nTyx, yi = (i / a.nTx) % a.nTy, xi = i % a.nTx;
+    const int nT = a.nB / nTyx;
+    const int jlo = max(ti - a.wt, 0) * nTyx;                                  // frames in reach
+    const int jhi = ((a.wt >= nT - ti ? nT - 1 : ti + a.wt) + 1) * nTyx;
+    const uint32_t m_x = (0x1000000u + (uint32_t)a.nTx - 1u) / (uint32_t)a.nTx;
+    const uint32_t m_y = (0x1000000u + (uint32_t)a.nTy - 1u) / (uint32_t)a.nTy;
     const float vstar_f = __uint_as_float(vstar);
     uint32_t ties_before = 0, count = 0, wlo = 0, whi = 0;
 #pragma unroll
@@ -291,8 +343,10 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
             }
         }
         if (a.window) {
-            const int tj = j / nTyx, yj = (j / a.nTx) % a.nTy, xj = j % a.nTx;
-            m |= __ballot(j < a.nB && abs(tj - ti) <= a.wt && abs(yj - yi) <= a.wh && abs(xj - xi) <= a.ww);
+            const uint32_t row = div_small((uint32_t)j, m_x);                 // j / nTx
+            const int xj = j - (int)row * a.nTx;
+            const int yj = (int)row - (int)div_small(row, m_y) * a.nTy;      // (j / nTx) % nTy
+            m |= __ballot(j >= jlo && j < jhi && abs(yj - yi) <= a.wh && abs(xj - xi) <= a.ww);
         }
         count += (uint32_t)__popcll(m);
         if (lane == c) {
@@ -510,12 +564,15 @@ __global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
             s[4 * cc + t] = kSelChunk * cc + 64 * t + lane < a.nB ? v : -INFINITY;   // padding keys
         }
     }
+    __syncthreads();   // every wave has its row: the cut reuses the stage
     }
     uint64_t word = 0;
     int32_t count = 0;
     float sigma = 0.f, tcap = 0.f;
     if (wave < nrows) {
-        if constexpr (MODE != 1) select_cut<NE>(a, s, hist_all, i0 + wave, thr, lane, word, count);
+        if constexpr (MODE != 1)
+            select_cut<NE>(a, s, hist_all, reinterpret_cast<uint32_t *>(stage) + 512 * wave, i0 + wave, thr, lane, word,
+                           count);
         else sip_cut<NE>(a, s, (int64_t)bh * a.nB + i0 + wave, lane, word, count, sigma, tcap);
     }
     if (lane == 0) wave_count[wave] = count;

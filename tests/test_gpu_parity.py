@@ -84,6 +84,31 @@ def test_small_select_and_forward(case):
     assert err2 <= tol and lerr2 <= ltol
 
 
+LONG_ROWS = [
+    # name, heads, d, block grid, thr, window, reading, head-thr range: rows of more than 512
+    # blocks (the cut's bracket is compacted), block counts that are not whole 16-key groups
+    ("d128_756", 2, 128, (3, 12, 21), 0.8, (-1, -1, -1), "A", None),
+    ("d64_720_window", 2, 64, (2, 18, 20), 0.7, (1, 1, 1), "B", None),
+    ("d128_1080_window_headthr", 3, 128, (4, 15, 18), 0.9, (1, 2, 2), "A", (0.6, 0.95)),
+]
+
+
+@pytest.mark.parametrize("case", LONG_ROWS, ids=[c[0] for c in LONG_ROWS])
+def test_long_row_selection_matches_oracle(case):
+    """Selection on rows longer than 512 blocks, every row against the oracle."""
+    name, H, d, bg, thr, win, reading, hr = case
+    wl = small_workload(name, H, d, bg, "bf16", threshold=thr, window=win, head_threshold_range=hr, seed=19)
+    print(f"\n[case] long rows {name} blocks={wl.blocks}", flush=True)
+    q, k, _, thr_h = make_inputs(wl, reading)
+    qd, kd = P.to_device(q, k)
+    rp, ci = P.gpu_select(wl, qd, kd, thr_h)
+    gmask = P.check_csr(rp, ci, wl.blocks)
+    qbar, kbar, keep = P.oracle_select_full(wl, q, k, thr_h)
+    rep = P.compare_masks(gmask, keep, qbar, kbar, wl, thr_h)
+    print(P.fmt(rep), flush=True)
+    assert rep.unexcused == 0 and rep.window_missing == 0 and rep.invariant_fail == 0
+
+
 def test_threshold_one_is_dense_attention():
     wl = small_workload("dense", 2, 128, (2, 2, 3), "bf16", threshold=1.0, seed=3)
     q, k, v, thr = make_inputs(wl, "B")
