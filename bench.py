@@ -231,6 +231,42 @@ def main():
     reo_gbs = 2 * qd.numel() * elt / (reo_ms_med * 1e-3) / 1e9
     del reo
 
+    # raster-ordered Q and K: the two reorders followed by the selection, against the
+    # selection on raster inputs with the reorder fused into the pooling (same block
+    # list and tile-major copies); interleaved repetitions, each after the sweep
+    raster = None
+    if not args.no_select_timing:
+        qr = B.sparse_attn_from_tiles(shape, qd, stream=stream)
+        kr = B.sparse_attn_from_tiles(shape, kd, stream=stream)
+        qt, kt = torch.empty_like(qd), torch.empty_like(kd)
+        rbufs = B.alloc_buffers(shape, dev)
+        kw = dict(threshold=float(np.float32(wl.threshold)), head_thresholds=head_thr, window=wl.window,
+                  buffers=rbufs, stream=stream)
+
+        def separate():
+            B.sparse_attn_to_tiles(shape, qr, qt, stream=stream)
+            B.sparse_attn_to_tiles(shape, kr, kt, stream=stream)
+            B.sparse_attn_select(shape, qt, kt, **kw)
+
+        def fused():
+            B.sparse_attn_select_raster(shape, qr, kr, qt, kt, **kw)
+        times = {"separate": [], "fused": []}
+        for _ in range(7):
+            for name, fn in (("separate", separate), ("fused", fused)):
+                flush.sum()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                torch.cuda.synchronize()
+                times[name].append(a.elapsed_time(b))
+        med = {n: sorted(v)[len(v) // 2] for n, v in times.items()}
+        r_bytes = 4 * qd.numel() * elt + 4 * (rows + 1) + 4 * nnz      # Q, K read and written, CSR
+        r_gbs = r_bytes / (med["fused"] * 1e-3) / 1e9
+        raster = {"reorder_then_select_ms": round(med["separate"], 4), "fused_ms": round(med["fused"], 4),
+                  "bytes": r_bytes, "fused_GB_s": round(r_gbs, 1), "fused_frac_hbm_peak": round(r_gbs / PEAK_HBM_GBS, 4)}
+        del qr, kr, qt, kt, rbufs
+
     # backward over the selected block list (bf16): dQ over the rows, dK and dV over the
     # transposed list; FLOPs counted as the five algorithmic products (S, dP, dV, dQ, dK)
     bwd = None
@@ -416,6 +452,7 @@ def main():
         },
         "reorder_to_tiles": {"ms": round(reo_ms_med, 4), "GB_s": round(reo_gbs, 1),
                              "frac_hbm_peak": round(reo_gbs / PEAK_HBM_GBS, 4)},
+        "raster_select": raster,
         "dense_forward_ms": round(dense_ms_med, 4),
         "speedup_vs_dense": {
             "forward": round(dense_ms_med / attn_ms_avg, 3),

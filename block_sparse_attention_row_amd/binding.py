@@ -41,6 +41,7 @@ EXPORTED = (
     "sparse_attn_full_csr",
     "sparse_attn_to_tiles",
     "sparse_attn_from_tiles",
+    "sparse_attn_select_raster",
 )
 
 
@@ -115,6 +116,8 @@ def lib():
         L.sparse_attn_backward.restype = ctypes.c_int32
         L.sparse_attn_full_csr.argtypes = [SP, P, P, I64, P]
         L.sparse_attn_full_csr.restype = ctypes.c_int32
+        L.sparse_attn_select_raster.argtypes = [SP, ctypes.POINTER(SelectParams), P, P, P, P, P, P, I64, P, I64, P]
+        L.sparse_attn_select_raster.restype = ctypes.c_int32
         for name in ("sparse_attn_to_tiles", "sparse_attn_from_tiles"):
             getattr(L, name).argtypes = [SP, P, P, P]
             getattr(L, name).restype = ctypes.c_int32
@@ -207,6 +210,28 @@ def sparse_attn_select(shape: Shape, q, k, threshold: float = 0.9,
                                   _ptr(bufs.workspace), bufs.workspace.numel(), _stream(stream))
     _check(st, "sparse_attn_select")
     return bufs.row_ptr, bufs.col_idx
+
+
+def sparse_attn_select_raster(shape: Shape, q, k, q_tiles=None, k_tiles=None, threshold: float = 0.9,
+                              head_thresholds: Optional[Sequence[float]] = None, window=(-1, -1, -1),
+                              buffers: Optional[Buffers] = None, stream=None):
+    """The selection on raster-ordered q, k, with the tile-major copies written on the way;
+    returns (row_ptr, col_idx, q_tiles, k_tiles)."""
+    import torch
+    bufs = buffers or alloc_buffers(shape, q.device)
+    q_tiles = torch.empty_like(q) if q_tiles is None else q_tiles
+    k_tiles = torch.empty_like(k) if k_tiles is None else k_tiles
+    ht = None
+    if head_thresholds is not None:
+        arr = (ctypes.c_float * shape.heads)(*[float(x) for x in head_thresholds])
+        ht = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
+    params = SelectParams(float(threshold), ht, *(int(w) for w in window))
+    st = lib().sparse_attn_select_raster(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(q_tiles),
+                                         _ptr(k_tiles), _ptr(bufs.row_ptr), _ptr(bufs.col_idx),
+                                         bufs.col_idx.numel(), _ptr(bufs.workspace), bufs.workspace.numel(),
+                                         _stream(stream))
+    _check(st, "sparse_attn_select_raster")
+    return bufs.row_ptr, bufs.col_idx, q_tiles, k_tiles
 
 
 def sparse_attn_select_ibcs(shape: Shape, q, k, threshold: float = 0.9,

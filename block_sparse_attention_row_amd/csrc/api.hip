@@ -66,7 +66,7 @@ int64_t max_slots(const Dims &d) {
 }
 
 struct Layout {
-    int64_t thr, kbar, status, ticket;                                   // selection
+    int64_t thr, kbar, qbar, status, ticket;                             // selection
     int64_t bits, counts, groups;                                        // external masks
     int64_t items, plan_counts, pair_flag, merge, part_o, part_lse;      // attention row splitting
     int64_t col_ptr, lse2, dn;                                           // backward
@@ -91,6 +91,8 @@ Layout layout(const Dims &d) {
     off = align_up(off + 4 * d.H, kAlign);
     l.kbar = off;
     off = align_up(off + 4 * d.B * d.H * groups_per_head(d) * kGroupRows * d.D, kAlign);   // key means, 16-key groups
+    l.qbar = off;
+    off = align_up(off + 4 * d.B * d.H * d.nB * d.D, kAlign);   // query means (raster selection)
     l.status = off;
     off = align_up(off + 8 * n_groups(d), kAlign);
     l.ticket = off;
@@ -167,13 +169,39 @@ int64_t sparse_attn_workspace_size(const sparse_attn_shape *shape) {
     return layout(d).total;
 }
 
-int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_select_params *params, const void *q,
+static ReorderArgs reorder_args(const sparse_attn_shape *shape, const Dims &d, int inverse) {
+    const int64_t rowb = d.D * (shape->dtype == SPARSE_ATTN_BF16 ? 2 : 4);
+    ReorderArgs a;
+    a.nB = (int32_t)d.nB;
+    a.nTy = d.nTy;
+    a.nTx = d.nTx;
+    a.tt = shape->tile_t;
+    a.th = shape->tile_h;
+    a.tw = shape->tile_w;
+    a.gh = shape->grid_h;
+    a.gw = shape->grid_w;
+    a.row_log2 = 0;
+    while ((16LL << a.row_log2) < rowb) ++a.row_log2;
+    a.inverse = inverse;
+    return a;
+}
+
+// The CDF selection.  q_tiles == k_tiles == null: q and k are tile-major and the
+// selection pools them.  Otherwise q and k are in raster order: they are copied to
+// q_tiles / k_tiles in tile-major order and their block means are formed by that copy.
+static int32_t select_impl(const sparse_attn_shape *shape, const sparse_attn_select_params *params, const void *q,
                            const void *k, int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity,
-                           void *workspace, int64_t workspace_bytes, void *stream) {
+                           void *workspace, int64_t workspace_bytes, void *stream, void *q_tiles, void *k_tiles) {
     Dims d;
     int32_t st = check_shape(shape, &d);
     if (st) return st;
     if (!params || !q || !k || !row_ptr || !col_idx || !workspace) return SPARSE_ATTN_INVALID_ARGUMENT;
+    const bool raster = q_tiles != nullptr || k_tiles != nullptr;
+    if (raster) {
+        if (!q_tiles || !k_tiles || q_tiles == k_tiles || q_tiles == q || q_tiles == k || k_tiles == q ||
+            k_tiles == k || !aligned(q_tiles, 16) || !aligned(k_tiles, 16))
+            return SPARSE_ATTN_INVALID_ARGUMENT;
+    }
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(row_ptr, 4) || !aligned(col_idx, 4) ||
         !aligned(workspace, 16))
         return SPARSE_ATTN_INVALID_ARGUMENT;
@@ -210,10 +238,28 @@ int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_sel
             tmp[i] = params->head_thresholds ? params->head_thresholds[h0 + i] : params->threshold;
         if (launch_fill_thresholds(tmp, n, thr + h0, s)) return SPARSE_ATTN_HIP_ERROR;
     }
-    if (launch_pool_keys(k, kbar, d.B * d.H * d.nB, d.nB, shape->dtype, (int)d.D, side, s)) return SPARSE_ATTN_HIP_ERROR;
+    __bf16 *qbar = nullptr;
+    if (raster) {
+        qbar = (__bf16 *)(ws + L.qbar);
+        ReorderPoolArgs rp;
+        rp.a = reorder_args(shape, d, 0);
+        rp.k_src = k;
+        rp.q_src = q;
+        rp.k_dst = k_tiles;
+        rp.q_dst = q_tiles;
+        rp.kbar = kbar;
+        rp.qbar = qbar;
+        rp.tiles = d.B * d.H * d.nB;
+        rp.gph = (int32_t)groups_per_head(d);
+        rp.side = side;
+        if (launch_reorder_pool(rp, shape->dtype, (int)d.D, s)) return SPARSE_ATTN_HIP_ERROR;
+    } else if (launch_pool_keys(k, kbar, d.B * d.H * d.nB, d.nB, shape->dtype, (int)d.D, side, s)) {
+        return SPARSE_ATTN_HIP_ERROR;
+    }
 
-    SelectArgs a;
-    a.q = q;
+    SelectArgs a = {};
+    a.q = raster ? q_tiles : q;
+    a.qbar = qbar;
     a.kbar = kbar;
     a.thr = thr;
     a.status = status;
@@ -235,6 +281,22 @@ int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_sel
     a.scale_log2 = effective_scale(shape) * kLog2e;
     if (launch_select(a, (int)d.D, shape->dtype, s)) return SPARSE_ATTN_HIP_ERROR;
     return SPARSE_ATTN_OK;
+}
+
+int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_select_params *params, const void *q,
+                           const void *k, int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity,
+                           void *workspace, int64_t workspace_bytes, void *stream) {
+    return select_impl(shape, params, q, k, row_ptr, col_idx, col_capacity, workspace, workspace_bytes, stream,
+                       nullptr, nullptr);
+}
+
+int32_t sparse_attn_select_raster(const sparse_attn_shape *shape, const sparse_attn_select_params *params,
+                                  const void *q, const void *k, void *q_tiles, void *k_tiles, int32_t *row_ptr,
+                                  int32_t *col_idx, int64_t col_capacity, void *workspace, int64_t workspace_bytes,
+                                  void *stream) {
+    if (!q_tiles || !k_tiles) return SPARSE_ATTN_INVALID_ARGUMENT;
+    return select_impl(shape, params, q, k, row_ptr, col_idx, col_capacity, workspace, workspace_bytes, stream,
+                       q_tiles, k_tiles);
 }
 
 }  // extern "C"
@@ -573,19 +635,7 @@ static int32_t reorder(const sparse_attn_shape *shape, const void *src, void *ds
     if (st) return st;
     if (!src || !dst || src == dst) return SPARSE_ATTN_INVALID_ARGUMENT;
     if (!aligned(src, 16) || !aligned(dst, 16)) return SPARSE_ATTN_INVALID_ARGUMENT;
-    const int64_t rowb = d.D * (shape->dtype == SPARSE_ATTN_BF16 ? 2 : 4);
-    ReorderArgs a;
-    a.nB = (int32_t)d.nB;
-    a.nTy = d.nTy;
-    a.nTx = d.nTx;
-    a.tt = shape->tile_t;
-    a.th = shape->tile_h;
-    a.tw = shape->tile_w;
-    a.gh = shape->grid_h;
-    a.gw = shape->grid_w;
-    a.row_log2 = 0;
-    while ((16LL << a.row_log2) < rowb) ++a.row_log2;
-    a.inverse = inverse;
+    const ReorderArgs a = reorder_args(shape, d, inverse);
     if (launch_reorder(src, dst, a, d.B * d.H * d.nB, (hipStream_t)stream)) return SPARSE_ATTN_HIP_ERROR;
     return SPARSE_ATTN_OK;
 }

@@ -49,6 +49,8 @@ constexpr int kSelectMaxBlocks = 4096;
 struct SelectArgs {
     const void *q;            // [BH*N][D] queries in the input dtype (tile-major)
     const __bf16 *kbar;       // key block means as bf16 pairs, in fragment order (kbar_group)
+    const __bf16 *qbar;       // null: the selection pools Q itself; else [BH*nB][2][D] query
+                              // block means as bf16 pairs (hi, then lo), formed by the reorder
     const float *thr;         // [H] thresholds (device)
     uint64_t *status;         // [n_groups] look-back words (zeroed by the pooling kernel)
     uint32_t *ticket;         // group ticket counter (zeroed by the pooling kernel)
@@ -155,6 +157,19 @@ struct ReorderArgs {
     int32_t inverse;               // 0: raster -> tile-major, 1: tile-major -> raster
 };
 int launch_reorder(const void *src, void *dst, const ReorderArgs &a, int64_t tiles, hipStream_t s);
+// Raster -> tile-major copies of K and Q plus their block means (keys in fragment
+// order, kbar_group with gph groups a head; queries as [hi | lo] rows), and the
+// selection's side jobs.  One launch of 2 * tiles workgroups.
+struct ReorderPoolArgs {
+    ReorderArgs a;
+    const void *k_src, *q_src;
+    void *k_dst, *q_dst;
+    __bf16 *kbar, *qbar;
+    int64_t tiles;            // B * H * nB
+    int32_t gph;
+    PoolSide side;
+};
+int launch_reorder_pool(const ReorderPoolArgs &p, int dtype, int d, hipStream_t s);
 
 int launch_pool_keys(const void *k, __bf16 *kbar, int64_t nblocks, int32_t nB, int dtype, int d, const PoolSide &side,
                      hipStream_t s);

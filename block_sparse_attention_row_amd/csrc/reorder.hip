@@ -36,6 +36,104 @@ __global__ __launch_bounds__(256) void reorder_kernel(const u32x4 *__restrict__ 
     }
 }
 
+// Raster -> tile-major copy of K and Q with each tile's mean formed on the way (the
+// selection's "Sous-echantillonnage" fused into the reorder): one workgroup per tile,
+// the key tiles first, then the query tiles.  Thread t moves the 16-byte pieces t,
+// t + 256, .. of the tile, which all hold the same column slice (256 is a multiple of
+// the pieces per token row), sums them in fp32, and the sums of the threads that
+// share a slice meet in LDS.  The mean goes out as a bf16 pair (hi = bf16(x), lo =
+// bf16(x - hi)): for keys in the fragment order of kbar_group, for queries as a
+// [hi | lo] row per block.  Side jobs for the selection that follows, as in the
+// pooling kernel.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void reorder_pool_kernel(ReorderPoolArgs p) {
+    constexpr int VEC = 16 / (int)sizeof(T), PR = D / VEC;   // elements per piece, pieces per token row
+    constexpr int PER = 64 * PR, IT = PER / 256, SHARE = 256 / PR;
+    static_assert(PER % 256 == 0 && 256 % PR == 0, "pieces per thread");
+    __shared__ float red[SHARE][PR][VEC + 1];
+    const int t = threadIdx.x;
+    const ReorderArgs &a = p.a;
+    const int64_t gt = (int64_t)blockIdx.x * blockDim.x + t;
+    if (blockIdx.x == 0 && t < p.side.n_thr) p.side.thr_dst[t] = p.side.thr.v[t];
+    for (int64_t i = gt; i < p.side.n_status; i += (int64_t)gridDim.x * blockDim.x) p.side.status[i] = 0;
+    if (gt == 0) *p.side.ticket = 0u;
+    const bool keys = (int64_t)blockIdx.x < p.tiles;
+    const int64_t b = keys ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - p.tiles;   // tile over B*H*nB
+    const u32x4 *s4 = reinterpret_cast<const u32x4 *>(keys ? p.k_src : p.q_src);
+    u32x4 *d4 = reinterpret_cast<u32x4 *>(keys ? p.k_dst : p.q_dst);
+    const int64_t bh = b / a.nB;
+    const int blk = (int)(b - bh * a.nB);
+    const int bt = blk / (a.nTy * a.nTx), by = (blk / a.nTx) % a.nTy, bx = blk % a.nTx;
+    const int64_t N = (int64_t)a.nB * 64;
+    const int tyx = a.th * a.tw;
+    const int off = t % PR;                                   // the same slice for every piece of this thread
+    u32x4 buf[IT];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const int u = (256 * i + t) / PR;                     // token inside the tile
+        const int ut = u / tyx, uy = (u / a.tw) % a.th, ux = u % a.tw;
+        const int64_t tok = ((int64_t)(bt * a.tt + ut) * a.gh + (by * a.th + uy)) * a.gw + (bx * a.tw + ux);
+        buf[i] = s4[(bh * N + tok) * PR + off];
+    }
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        d4[(bh * N + (int64_t)blk * 64) * PR + 256 * i + t] = buf[i];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if constexpr (sizeof(T) == 2) {
+                acc[2 * c] += bf16_lo(buf[i][c]);
+                acc[2 * c + 1] += bf16_hi(buf[i][c]);
+            } else {
+                acc[c] += __uint_as_float(buf[i][c]);
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) red[t / PR][off][e] = acc[e];
+    __syncthreads();
+    if (t >= PR) return;
+    typedef __attribute__((ext_vector_type(VEC))) float fv;
+    typedef __attribute__((ext_vector_type(VEC))) __bf16 bv;
+    fv xv, rv;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        float v = 0.f;
+        for (int g = 0; g < SHARE; ++g) v += red[g][t][e];
+        xv[e] = v * (1.f / 64.f);
+    }
+    const bv hi = __builtin_convertvector(xv, bv);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) rv[e] = xv[e] - (float)hi[e];
+    const bv lo = __builtin_convertvector(rv, bv);
+    const int d0 = t * VEC;                                   // this thread's columns d0 .. d0 + VEC - 1
+    if (keys) {
+        const int kb = d0 / 32, kq = (d0 % 32) / 8;
+        __bf16 *at = p.kbar + kbar_group(bh, p.gph, blk / 16, D) + 512 * kb + 8 * (blk % 16 + 16 * kq) + d0 % 8;
+        *reinterpret_cast<bv *>(at) = hi;
+        *reinterpret_cast<bv *>(at + 16 * D) = lo;
+    } else {
+        __bf16 *row = p.qbar + (bh * a.nB + blk) * (2 * D);
+        *reinterpret_cast<bv *>(row + d0) = hi;
+        *reinterpret_cast<bv *>(row + D + d0) = lo;
+    }
+}
+
+int launch_reorder_pool(const ReorderPoolArgs &p, int dtype, int d, hipStream_t s) {
+    const dim3 g((unsigned)(2 * p.tiles)), blk(256);
+    if (dtype == 1 && d == 128)
+        reorder_pool_kernel<__bf16, 128><<<g, blk, 0, s>>>(p);
+    else if (dtype == 1 && d == 64)
+        reorder_pool_kernel<__bf16, 64><<<g, blk, 0, s>>>(p);
+    else if (dtype == 0 && d == 128)
+        reorder_pool_kernel<float, 128><<<g, blk, 0, s>>>(p);
+    else
+        reorder_pool_kernel<float, 64><<<g, blk, 0, s>>>(p);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_reorder(const void *src, void *dst, const ReorderArgs &a, int64_t tiles, hipStream_t s) {
     const dim3 g((unsigned)tiles), blk(256);
     if (a.row_log2 == 3)

@@ -10,6 +10,8 @@
 //                         Hybride avec STA": OR with a static box window; and the
 //                         "Expansion" into row_ptr / col_idx, whose offsets come
 //                         from a look-back over the groups' totals.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -522,10 +524,17 @@ __global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
             kl[slot][kb] = *reinterpret_cast<const bf16x8 *>(kr + 16 * D + 512 * kb);
         }
     };
-    // ---- the group's pooled queries (hi | lo), one query block per wave
+    // ---- the group's pooled queries (hi | lo), one query block per wave: pooled here,
+    //      or copied from the means the reorder formed
     {
         __bf16 *qrow = qf + wave * qf_stride<D>();
-        if (wave < nrows) {
+        if (a.qbar != nullptr) {
+            using QV = std::conditional_t<D == 128, uint2, uint32_t>;   // 2D bf16 over the 64 lanes
+            const QV v =
+                wave < nrows ? reinterpret_cast<const QV *>(a.qbar + ((int64_t)bh * a.nB + i0 + wave) * (2 * D))[lane]
+                             : QV{};
+            reinterpret_cast<QV *>(qrow)[lane] = v;
+        } else if (wave < nrows) {
             float x[QP::VEC];
             const T *qb = reinterpret_cast<const T *>(a.q) + (((int64_t)bh * a.nB + i0 + wave) * kTokensPerBlock) * D;
             QP::mean(qb, lane, x);

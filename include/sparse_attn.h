@@ -318,6 +318,26 @@ int32_t sparse_attn_full_csr(const sparse_attn_shape *shape, int32_t *row_ptr, i
 int32_t sparse_attn_to_tiles(const sparse_attn_shape *shape, const void *src, void *dst, void *stream);
 int32_t sparse_attn_from_tiles(const sparse_attn_shape *shape, const void *src, void *dst, void *stream);
 
+/*
+ * sparse_attn_select on raster-order inputs, with the reorder fused into the
+ * pooling: Q and K are copied to tile-major order exactly as sparse_attn_to_tiles
+ * does, and each tile's mean (the "Sous-echantillonnage" step of the NABLA summary
+ * page, section "Methodologie : NABLA") is formed by that copy, so the selection
+ * reads Q and K once in all.  The block list equals the one sparse_attn_select
+ * gives on the tile-major copies, up to fp32 summation order in the means (which
+ * moves only blocks whose cumulative mass lies at the threshold).
+ *
+ *   q, k          device, [B, H, N, d] in shape->dtype, raster order.
+ *   q_tiles, k_tiles  device, same size, written: the tile-major copies, ready for
+ *               sparse_attn_forward.  Four distinct, non-overlapping buffers.
+ *   params, row_ptr, col_idx, col_capacity, workspace: as in sparse_attn_select.
+ * Errors as in sparse_attn_select and sparse_attn_to_tiles.
+ */
+int32_t sparse_attn_select_raster(const sparse_attn_shape *shape, const sparse_attn_select_params *params,
+                                  const void *q, const void *k, void *q_tiles, void *k_tiles,
+                                  int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity,
+                                  void *workspace, int64_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

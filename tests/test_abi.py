@@ -52,6 +52,7 @@ def test_capacity_and_workspace_formulas():
     al = lambda x: (x + 255) // 256 * 256
     expect = al(expect + 4 * 12)
     expect = al(expect + 4 * 12 * ((nB + 15) // 16) * 16 * 128)   # key block means (bf16 hi | lo), 16-key groups
+    expect = al(expect + 4 * rows * 128)                  # query block means (raster selection)
     expect = al(expect + 8 * 12 * ((nB + 15) // 16))      # selection look-back words per 16-row group
     expect = al(expect + 16)                              # selection ticket counter
     expect = al(expect + 8 * rows * (nbp // 64))
@@ -122,6 +123,27 @@ def _select(shape, thr=0.9, head_thr=None, q=A, k=A, rp=A, ci=A, cap=None, ws=A,
 ])
 def test_select_rejects_before_launch(kw, status):
     assert _select(_shape(), **kw) == status
+
+
+def _select_raster(shape, qt=2 * A, kt=3 * A, cap=None, wsb=None):
+    params = B.SelectParams(0.9, None, -1, -1, -1)
+    cap = B.sparse_attn_csr_capacity(shape) if cap is None else cap
+    wsb = B.sparse_attn_workspace_size(shape) if wsb is None else wsb
+    return B.lib().sparse_attn_select_raster(ctypes.byref(shape), ctypes.byref(params), A, A, qt, kt, A, A, cap, A,
+                                             wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qt=None), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(kt=None), B.SPARSE_ATTN_INVALID_ARGUMENT),
+    (dict(qt=2 * A, kt=2 * A), B.SPARSE_ATTN_INVALID_ARGUMENT),    # one buffer for both copies
+    (dict(qt=A), B.SPARSE_ATTN_INVALID_ARGUMENT),                  # copy over its own input
+    (dict(kt=3 * A + 8), B.SPARSE_ATTN_INVALID_ARGUMENT),          # misaligned
+    (dict(cap=10), B.SPARSE_ATTN_CAPACITY),
+    (dict(wsb=1024), B.SPARSE_ATTN_WORKSPACE),
+])
+def test_raster_select_rejects_before_launch(kw, status):
+    assert _select_raster(_shape(), **kw) == status
 
 
 def test_select_rejects_bad_head_threshold():

@@ -255,6 +255,40 @@ def test_token_reorder_matches_oracle(dtype, d, grid, tile):
     assert torch.equal(z.cpu(), x)
 
 
+RASTER = [
+    # name, heads, d, block grid, dtype, thr, window, reading, head-thr range
+    ("bf16_d128", 2, 128, (3, 5, 7), "bf16", 0.85, (-1, -1, -1), "A", None),
+    ("f32_d64_window", 2, 64, (2, 3, 5), "f32", 0.9, (1, 1, 1), "B", None),
+    ("bf16_d64_window", 3, 64, (2, 4, 6), "bf16", 0.7, (1, 1, 1), "B", None),
+    ("bf16_d128_756_headthr", 2, 128, (3, 12, 21), "bf16", 0.8, (-1, -1, -1), "A", (0.6, 0.9)),
+]
+
+
+@pytest.mark.parametrize("case", RASTER, ids=[c[0] for c in RASTER])
+def test_raster_selection(case):
+    """The selection on raster inputs: tile-major copies bit-equal to the inputs of the
+    tiled path, and the block list against the oracle (differences only at the CDF
+    boundary)."""
+    name, H, d, bg, dt, thr, win, reading, hr = case
+    wl = small_workload(name, H, d, bg, dt, threshold=thr, window=win, head_threshold_range=hr, seed=23)
+    print(f"\n[case] raster selection {name} blocks={wl.blocks}", flush=True)
+    q, k, _, thr_h = make_inputs(wl, reading)
+    qd, kd = P.to_device(q, k)
+    shape = P.shape_for(wl)
+    qr, kr = B.sparse_attn_from_tiles(shape, qd), B.sparse_attn_from_tiles(shape, kd)
+    head_thr = None if hr is None else [float(x) for x in thr_h]
+    rp, ci, qt, kt = B.sparse_attn_select_raster(shape, qr, kr, threshold=float(np.float32(wl.threshold)),
+                                                 head_thresholds=head_thr, window=win)
+    torch.cuda.synchronize()
+    assert torch.equal(qt, qd) and torch.equal(kt, kd)
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    gmask = P.check_csr(rp_h, ci[:int(rp_h[-1])].cpu().numpy(), wl.blocks)
+    qbar, kbar, keep = P.oracle_select_full(wl, q, k, thr_h)
+    rep = P.compare_masks(gmask, keep, qbar, kbar, wl, thr_h)
+    print(P.fmt(rep), flush=True)
+    assert rep.unexcused == 0 and rep.window_missing == 0 and rep.invariant_fail == 0
+
+
 def test_full_csr_is_the_dense_block_list():
     """The dense block list equals the oracle's CSR of an all-true mask (integer work:
     bit-exact), and attention over it is dense attention."""
