@@ -69,6 +69,7 @@ struct Layout {
     int64_t thr, kbar, qbar, status, ticket;                             // selection
     int64_t bits, counts, groups;                                        // external masks
     int64_t items, plan_counts, pair_flag, merge, part_o, part_lse;      // attention row splitting
+    int64_t part_b;                                                      // backward: second partial rows
     int64_t col_ptr, lse2, dn;                                           // backward
     int64_t mix;                                                         // clustering selector rows
     int64_t total;
@@ -116,6 +117,8 @@ Layout layout(const Dims &d) {
     off = align_up(off + 4 * ms * 2 * 64 * d.D, kAlign);
     l.part_lse = off;
     off = align_up(off + 4 * ms * 2 * 64, kAlign);
+    l.part_b = off;
+    off = align_up(off + 4 * ms * 2 * 64 * d.D, kAlign);
     l.col_ptr = off;
     off = align_up(off + 4 * (d.rows + 1), kAlign);
     l.lse2 = off;                                   // lse2 then dn: one direct load reaches both
@@ -594,6 +597,16 @@ int32_t sparse_attn_backward(const sparse_attn_shape *shape, const void *q, cons
     b.args.nB = (int32_t)d.nB;
     b.args.scale = effective_scale(shape);
     b.args.scale_log2 = b.args.scale * kLog2e;
+    b.args.plan.items = (SplitItem *)(ws + L.items);
+    b.args.plan.counts = (int32_t *)(ws + L.plan_counts);
+    b.args.plan.pair_flag = (int32_t *)(ws + L.pair_flag);
+    b.args.plan.merge = (int32_t *)(ws + L.merge);
+    b.args.plan.part_o = nullptr;
+    b.args.plan.part_lse = nullptr;
+    b.args.plan.max_slots = (int32_t)max_slots(d);
+    b.args.plan.long_slots = (int32_t)long_slots(d);
+    b.args.part = (float *)(ws + L.part_o);
+    b.args.part2 = (float *)(ws + L.part_b);
     b.out = out;
     b.lse = lse;
     b.lse2 = (float *)(ws + L.lse2);

@@ -763,6 +763,11 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
     if (a.lse && hh == 0) a.lse[qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
+int launch_plan(const AttnArgs &a, hipStream_t s) {
+    plan_kernel<<<1, 1024, 0, s>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_attention(const AttnArgs &a, int dtype, int d, hipStream_t s) {
     const dim3 pgrid((unsigned)(a.plan.max_slots + a.n_pairs)), pblock(256), grid((unsigned)a.rows), block(128);
     // (long_slots workgroups of long-row pieces, n_pairs of whole pairs, then max_slots -

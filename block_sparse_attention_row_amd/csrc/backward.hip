@@ -159,7 +159,26 @@ __global__ __launch_bounds__(256, MODE == kDKV && D == 128 ? 1 : 2) void bwd_ker
     const int t = threadIdx.x, lane = t & 63, hh = lane >> 5, l32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int grp = wave >> 1, half = wave & 1;   // block of the pair, 32-row half of the block
-    const int64_t pair = xcd_chunk_remap<256>(blockIdx.x, a.n_pairs);
+    // work item, as in the forward: long-row pieces, then whole pairs that were not
+    // split, then the last round's pieces
+    const int64_t ls = a.plan.long_slots, bid = blockIdx.x;
+    int64_t pair;
+    SplitItem it = {};
+    bool split = true;
+    if (bid < ls) {
+        if (bid >= a.plan.counts[0]) return;
+        it = a.plan.items[bid];
+        pair = it.pair;
+    } else if (bid < ls + a.n_pairs) {
+        split = false;
+        pair = xcd_chunk_remap<256>(bid - ls, a.n_pairs);
+        if (a.plan.pair_flag[pair]) return;
+    } else {
+        if (bid - ls - a.n_pairs >= a.plan.counts[3]) return;
+        it = a.plan.items[bid - a.n_pairs];
+        if (it.pair < 0) return;      // a last-round pair that was not cut
+        pair = it.pair;
+    }
     const int64_t bh = pair / a.pairs_per_head;
     int32_t blk_a, blk_b;   // the pair's two blocks, neighbours in time (pair_blocks)
     pair_blocks((int32_t)(pair % a.pairs_per_head), a.pair_stride, a.nB, blk_a, blk_b);
@@ -179,8 +198,33 @@ __global__ __launch_bounds__(256, MODE == kDKV && D == 128 ? 1 : 2) void bwd_ker
         if (e < b) e = b;
     };
     int64_t begA, endA, begB = 0, endB = 0;
-    clamp_range(rowA, begA, endA);
-    if (hasB) clamp_range(rowB, begB, endB);
+    int lastA = -1, lastB = -1;
+    if (split) {
+        begA = it.a0;
+        endA = it.a1;
+        begB = it.b0;
+        endB = it.b1;
+        // the whole-list walk would arrive at the piece with the largest valid block
+        // of the entries before it as its last one
+        auto prefix_max = [&](int64_t from, int64_t to) {
+            int m = -1;
+            for (int64_t i = from + lane; i < to; i += 64) {
+                const int cc = a.idx[i];
+                if (cc >= 0 && cc < a.nB) m = cc > m ? cc : m;
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const int u = __shfl_xor(m, o, 64);
+                m = u > m ? u : m;
+            }
+            return __builtin_amdgcn_readfirstlane(m);
+        };
+        lastA = prefix_max(it.ra, begA);
+        lastB = prefix_max(it.rb, begB);
+    } else {
+        clamp_range(rowA, begA, endA);
+        if (hasB) clamp_range(rowB, begB, endB);
+    }
     const bool has_row = grp == 0 || hasB;
 
     // the pair's own rows, B operands of the score products: queries and dO (dQ), keys
@@ -206,7 +250,6 @@ __global__ __launch_bounds__(256, MODE == kDKV && D == 128 ? 1 : 2) void bwd_ker
     int winA = window(baseA, endA), nxtA = window(baseA + 64, endA);
     int winB = window(baseB, endB), nxtB = window(baseB + 64, endB);
     __builtin_amdgcn_s_waitcnt(0x0f70);
-    int lastA = -1, lastB = -1;
     auto peek = [&](int64_t &base, int &pos, int &win, int &nxt, int64_t e, int last) {
         while (base + pos < e) {
             if (pos == 64) {
@@ -328,6 +371,24 @@ __global__ __launch_bounds__(256, MODE == kDKV && D == 128 ? 1 : 2) void bwd_ker
     if (!has_row) return;
     // lane owns row 32 half + l32 of its block, d = 32 dt + 8 rr + 4 hh + {0..3}
     const float mult = MODE == kDKV ? 1.f : a.scale;
+    if (split) {
+        // piece of a split pair: its scaled fp32 partial rows, summed by bwd_merge_kernel
+        const int64_t at = ((int64_t)it.slot * 2 + grp) * (64 * D) + (32 * half + l32) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                f32x4 w, w2;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    w[e] = acc[dt][4 * rr + e] * mult;
+                    w2[e] = acc2[dt][4 * rr + e] * a.scale;
+                }
+                *reinterpret_cast<f32x4 *>(a.part + at + 32 * dt + 8 * rr + 4 * hh) = w;
+                if constexpr (MODE == kDKV) *reinterpret_cast<f32x4 *>(a.part2 + at + 32 * dt + 8 * rr + 4 * hh) = w2;
+            }
+        return;
+    }
     __bf16 *og = (__bf16 *)a.grad + own * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -349,6 +410,36 @@ __global__ __launch_bounds__(256, MODE == kDKV && D == 128 ? 1 : 2) void bwd_ker
                 for (int e = 0; e < 4; ++e) w[e] = acc2[dt][4 * rr + e] * a.scale;
                 *reinterpret_cast<bf16x4 *>(og2 + 32 * dt + 8 * rr + 4 * hh) = __builtin_convertvector(w, bf16x4);
             }
+    }
+}
+
+// Gradient rows of the split pairs: the sum of their pieces' partial rows, in piece
+// order (deterministic), to bf16; grad2 from part2 when `two`.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_merge_kernel(BwdArgs a, int two) {
+    const int m = blockIdx.x;
+    if (m >= a.plan.counts[1]) return;
+    const int32_t *me = a.plan.merge + 3 * (int64_t)m;
+    const int64_t pair = me[0];
+    const int first = me[1], ns = me[2];
+    const int64_t bh = pair / a.pairs_per_head;
+    int32_t blk_a, blk_b;
+    pair_blocks((int32_t)(pair % a.pairs_per_head), a.pair_stride, a.nB, blk_a, blk_b);
+    const int64_t N = (int64_t)a.nB * 64;
+    for (int g = 0; g < 2; ++g) {
+        const int32_t blk = g ? blk_b : blk_a;
+        if (blk < 0) continue;
+        const int64_t orow = (bh * N + (int64_t)blk * 64) * D;
+        for (int i = threadIdx.x; i < 64 * D / 4; i += blockDim.x) {
+            f32x4 s = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
+            for (int p = 0; p < ns; ++p) {
+                const int64_t src = ((int64_t)(first + p) * 2 + g) * (64 * D) + 4 * i;
+                s += *reinterpret_cast<const f32x4 *>(a.part + src);
+                if (two) s2 += *reinterpret_cast<const f32x4 *>(a.part2 + src);
+            }
+            *reinterpret_cast<bf16x4 *>((__bf16 *)a.grad + orow + 4 * i) = __builtin_convertvector(s, bf16x4);
+            if (two) *reinterpret_cast<bf16x4 *>((__bf16 *)a.grad2 + orow + 4 * i) = __builtin_convertvector(s2, bf16x4);
+        }
     }
 }
 
@@ -376,16 +467,38 @@ int launch_backward(const BwdLaunch &L, hipStream_t s) {
     csc.ptr = L.col_ptr;
     csc.idx = L.t_idx;
     csc.idx_count = L.col_count;
-    const dim3 g((unsigned)L.args.n_pairs), b(256);
+    const dim3 g((unsigned)(L.args.plan.max_slots + L.args.n_pairs)), b(256), mg((unsigned)L.args.plan.max_slots);
     BwdArgs cdkv = csc;
     cdkv.grad = L.dv;
     cdkv.grad2 = L.dk;
+    // each pass: the forward's plan over the list it walks, the pass, the merge of its pieces
+    auto plan = [&](const BwdArgs &w) {
+        AttnArgs pa = {};
+        pa.row_ptr = w.ptr;
+        pa.col_idx = w.idx;
+        pa.col_count = w.idx_count;
+        pa.n_pairs = w.n_pairs;
+        pa.pairs_per_head = w.pairs_per_head;
+        pa.nB = w.nB;
+        pa.pair_stride = w.pair_stride;
+        pa.plan = w.plan;
+        return launch_plan(pa, s);
+    };
+    if (plan(csr)) return -1;
     if (L.d == 128) {
         bwd_kernel<128, kDQ><<<g, b, 0, s>>>(csr);
-        bwd_kernel<128, kDKV><<<g, b, 0, s>>>(cdkv);
+        bwd_merge_kernel<128><<<mg, b, 0, s>>>(csr, 0);
     } else {
         bwd_kernel<64, kDQ><<<g, b, 0, s>>>(csr);
+        bwd_merge_kernel<64><<<mg, b, 0, s>>>(csr, 0);
+    }
+    if (plan(cdkv)) return -1;
+    if (L.d == 128) {
+        bwd_kernel<128, kDKV><<<g, b, 0, s>>>(cdkv);
+        bwd_merge_kernel<128><<<mg, b, 0, s>>>(cdkv, 1);
+    } else {
         bwd_kernel<64, kDKV><<<g, b, 0, s>>>(cdkv);
+        bwd_merge_kernel<64><<<mg, b, 0, s>>>(cdkv, 1);
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -201,6 +201,11 @@ struct BwdArgs {
     int32_t pairs_per_head, nB;
     int32_t pair_stride;          // S of pair_blocks (blocks per frame, or 1)
     float scale_log2, scale;
+    // pieces of long pairs and of the last round (the forward's plan over the list
+    // walked): each piece writes its partial gradient rows, fp32 and scaled, to
+    // part[slot][block of the pair][64][d] (and the dK part to part2); a merge adds them
+    SplitPlan plan;
+    float *part, *part2;
 };
 struct BwdLaunch {
     BwdArgs args;                 // fields common to the gradient passes
@@ -219,5 +224,8 @@ struct BwdLaunch {
 int launch_backward(const BwdLaunch &L, hipStream_t s);
 
 int launch_attention(const AttnArgs &a, int dtype, int d, hipStream_t s);   // bf16: plan, attention, merge
+// The work plan of the bf16 forward (long-row and last-round pieces) over the CSR view
+// in a (row_ptr, col_idx, col_count, pair fields, plan); also used by the backward.
+int launch_plan(const AttnArgs &a, hipStream_t s);
 
 }  // namespace sattn

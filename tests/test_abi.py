@@ -66,6 +66,7 @@ def test_capacity_and_workspace_formulas():
     expect = al(expect + 12 * slots)                      # merge list
     expect = al(expect + 4 * slots * 2 * 64 * 128)        # partial outputs (fp32)
     expect = al(expect + 4 * slots * 2 * 64)              # partial log-sum-exp
+    expect = al(expect + 4 * slots * 2 * 64 * 128)        # backward: second partial rows (dK)
     expect = al(expect + 4 * (rows + 1))                  # backward: transposed row pointers
     expect = al(expect + 4 * rows * 64)                   # backward: lse in log2 units
     expect = al(expect + 4 * rows * 64)                   # backward: dO . O
