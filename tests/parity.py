@@ -315,3 +315,38 @@ def fmt(rep: MaskReport) -> str:
 
 def scale_of(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+def backward_sampled(wl, shape, qd, kd, vd, lse, q32, k32, v32, orp, oci, sample, log=print):
+    """The backward at full size over the oracle's whole block list, with the upstream
+    gradient nonzero only on a few sampled query-block rows: the gradients are linear
+    in it and a row with dO = 0 adds exact zeros, so every gradient entry comes from
+    those rows, which the oracle computes under the block list cut down to them.  Both
+    sides take D = dO . O from the oracle's forward output of those rows, in bf16."""
+    nB, d = wl.blocks, wl.head_dim
+    rows_s = np.sort(sample[:: max(1, len(sample) // 6)][:6])
+    o_ref, _ = oracle.attention_rows(q32, k32, v32, orp, oci, rows_s)
+    o_in = torch.zeros(q32.shape, dtype=torch.bfloat16).reshape(-1, 64, d)
+    dout = torch.zeros_like(o_in)
+    gen = torch.Generator().manual_seed(12)
+    o_in[rows_s] = torch.as_tensor(o_ref).to(torch.bfloat16)
+    dout[rows_s] = torch.randn((len(rows_s), 64, d), generator=gen).to(torch.bfloat16)
+    o_in, dout = o_in.reshape(q32.shape), dout.reshape(q32.shape)
+    rpd = torch.as_tensor(orp.astype(np.int32)).cuda()
+    cid = torch.as_tensor(oci).cuda()
+    dq, dk, dv = B.sparse_attn_backward(shape, qd, kd, vd, o_in.cuda(), lse, dout.cuda(), rpd, cid)
+    torch.cuda.synchronize()
+    log(f"backward done on the GPU; oracle over rows {rows_s.tolist()}")
+    keep = np.zeros(len(orp) - 1, dtype=bool)
+    keep[rows_s] = True
+    lens = np.diff(orp)
+    rp_s = np.concatenate([[0], np.cumsum(np.where(keep, lens, 0))])
+    ci_s = np.concatenate([oci[orp[r]:orp[r + 1]] for r in rows_s])
+    rq, rk, rv = oracle.attention_backward(q32, k32, v32, dout.float().numpy(), rp_s, ci_s, out=o_in.float().numpy())
+    errs = []
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        g = got.float().cpu().numpy()
+        assert np.all(g[ref == 0] == 0), name          # rows with dO = 0 add exact zeros
+        errs.append(float(np.abs(g - ref).max() / np.abs(ref).max()))
+    log(f"backward, {len(rows_s)} sampled rows: rel err dq {errs[0]:.3e} dk {errs[1]:.3e} dv {errs[2]:.3e}")
+    assert max(errs[:2]) <= BWD_TOL_DQK and errs[2] <= BWD_TOL_DV

@@ -237,6 +237,30 @@ def test_long_rows_and_last_round_pieces_together():
     assert err <= P.TOL["bf16"] and lerr <= P.LSE_TOL["bf16"]
 
 
+def test_backward_long_rows_and_last_round_pieces():
+    """The backward on 1,024 pairs with long rows: both passes cut long pairs and the
+    last round into pieces whose partial rows a merge adds.  dO is nonzero only on
+    sampled rows (long rows, rows of last-round pairs, random rows), so every gradient
+    entry comes from them, and the oracle computes all of dQ, dK, dV from those rows."""
+    wl = small_workload("bwd_rounds", 4, 128, (8, 8, 8), "bf16", seed=37)
+    q, k, v, _ = make_inputs(wl, "A")
+    qd, kd, vd = P.to_device(q, k, v)
+    nB = wl.blocks
+    rows = wl.heads * nB
+    rng = np.random.default_rng(13)
+    lens = rng.integers(64, 141, rows)
+    long_rows = np.array([5, 900, 1500, 2046])
+    lens[long_rows] = 480
+    mask = np.zeros((rows, nB), dtype=bool)
+    for r in range(rows):
+        mask[r, rng.choice(nB, size=int(lens[r]), replace=False)] = True
+    orp, oci = oracle.csr_from_mask(mask)
+    _, lse = P.gpu_forward(wl, qd, kd, vd, orp, oci)
+    q32, k32, v32 = (t.float().numpy() for t in (q, k, v))
+    sample = np.unique(np.concatenate([long_rows, P.last_round_rows(wl), rng.choice(rows, 4, replace=False)]))
+    P.backward_sampled(wl, P.shape_for(wl), qd, kd, vd, lse, q32, k32, v32, orp, oci, sample)
+
+
 @pytest.mark.parametrize("dtype,d,grid,tile", [("bf16", 128, (3, 16, 24), (1, 8, 8)),
                                                  ("f32", 64, (4, 8, 16), (2, 4, 8)),
                                                  ("bf16", 64, (2, 32, 8), (1, 8, 8))])
