@@ -3,9 +3,10 @@
 A step is one pass of the whole path over one batch of synthetic input:
 sparse_attn_select (pooling, pooled softmax, CDF cut, CSR) followed by
 sparse_attn_forward (block-sparse flash attention over the kept tiles).
-The workload is the Wan2.1-1.3B-480p-like layer: batch 1, 12 heads, d=128,
-bf16, grid 20x32x48 (30,720 tokens, 480 blocks of 1x8x8), threshold 0.9,
-inputs from the seeded generator (reading A).
+The default workload is the largest configuration, the long-video layer:
+batch 1, 12 heads, d=128, bf16, grid 64x48x80 (245,760 tokens, 3,840 blocks
+of 1x8x8), per-head thresholds U(0.6, 0.8), inputs from the seeded generator
+(reading A).  --workload picks another one.
 
 Prints one JSON line.  `value` is the effective TFLOP/s of the whole step on
 kept tiles, 4*64*64*d*nnz / t_step.  `roofline` is for the attention
@@ -14,7 +15,8 @@ with HIP events on the stream it runs on.  `cpu_baseline` times the CPU
 oracle on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
-    python bench.py --pmc-summary DIR   # HBM traffic from rocprofv3 --pmc runs
+    python bench.py --pmc-summary DIR --workload W   # HBM traffic from rocprofv3 --pmc runs
+    python bench.py --trace-summary DIR --steps K --warmup W   # kernel durations from a --kernel-trace run
 """
 from __future__ import annotations
 
@@ -33,10 +35,17 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_wan13b_480p.json")
-ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_row_amd", "csrc", "attention.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "block_sparse_attention_row_amd", "csrc")
+ATTN_SRC = os.path.join(CSRC, "attention.hip")
+SEL_SRC = os.path.join(CSRC, "select.hip")
 ATTN_KERNEL = "attn_bf16_kernel"
 COPY_BYTES = 1 << 30
+DEFAULT_WORKLOAD = "long_video"
+
+
+def traffic_file(workload):
+    return os.path.join(PROFILES, f"traffic_{workload}.json")
 
 
 def _sha(path):
@@ -49,7 +58,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="wan13b_480p")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--reading", default="A")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
@@ -67,6 +76,7 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB read + 1 GiB write kernel (torch.neg) for rocprofv3 counter scaling")
     ap.add_argument("--pmc-summary", metavar="DIR", help="summarise rocprofv3 --pmc output and exit")
+    ap.add_argument("--trace-summary", metavar="DIR", help="summarise a rocprofv3 --kernel-trace run and exit")
     return ap.parse_args()
 
 
@@ -85,8 +95,9 @@ def _read_counter_csv(pattern, counter):
     return out
 
 
-def pmc_summary(d):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel, scaled by a 1 GiB copy."""
+def pmc_summary(d, workload):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention and selection kernels,
+    scaled by what the same counters read for a plain 1 GiB copy."""
     fetch = _read_counter_csv(os.path.join(d, "fetch", "**", "*counter_collection.csv"), "FETCH_SIZE")
     write = _read_counter_csv(os.path.join(d, "write", "**", "*counter_collection.csv"), "WRITE_SIZE")
 
@@ -96,32 +107,82 @@ def pmc_summary(d):
 
     copy_key = "neg_kernel"            # torch.neg over COPY_BYTES: reads and writes COPY_BYTES once
     cf, cw = pick(fetch, copy_key), pick(write, copy_key)
-    # the plain attention kernel (the instantiation with logit offsets serves other calls)
-    af, aw = pick(fetch, ATTN_KERNEL, "true>"), pick(write, ATTN_KERNEL, "true>")
     kib = COPY_BYTES / 1024.0
-    rec = {
-        "kernel": ATTN_KERNEL,
-        "attention_source_sha256": _sha(ATTN_SRC),
-        "fetch_kib_per_dispatch": af, "write_kib_per_dispatch": aw,
-        "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_expected_kib": kib,
-        "fetch_scale": (kib / cf) if cf else None, "write_scale": (kib / cw) if cw else None,
-    }
-    if af and aw and cf and cw:
-        rec["hbm_bytes_per_dispatch"] = af * 1024.0 * rec["fetch_scale"] + aw * 1024.0 * rec["write_scale"]
+    fs = (kib / cf) if cf else None
+    ws = (kib / cw) if cw else None
+    rec = {"workload": workload, "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_expected_kib": kib,
+           "fetch_scale": fs, "write_scale": ws,
+           "attention_source_sha256": _sha(ATTN_SRC), "selection_source_sha256": _sha(SEL_SRC), "kernels": {}}
+    # the plain attention kernel (the instantiation with logit offsets serves other calls), the key
+    # pooling and the CDF selection (MODE 0 of select_emit_kernel)
+    for label, key, excl in ((ATTN_KERNEL, ATTN_KERNEL, "true>"), ("pool_kernel", "pool_kernel", None),
+                             ("select_emit_kernel", "select_emit_kernel", None)):
+        if label == "select_emit_kernel":
+            f = pick({n: v for n, v in fetch.items() if n.rstrip().endswith("0>")}, key)
+            w = pick({n: v for n, v in write.items() if n.rstrip().endswith("0>")}, key)
+        else:
+            f, w = pick(fetch, key, excl), pick(write, key, excl)
+        k = {"fetch_kib_per_dispatch": f, "write_kib_per_dispatch": w}
+        if f and w and fs and ws:
+            k["hbm_bytes_per_dispatch"] = f * 1024.0 * fs + w * 1024.0 * ws
+        rec["kernels"][label] = k
     print(json.dumps(rec, indent=1))
     return rec
 
 
 def stored_traffic(workload):
+    """(attention bytes, selection bytes) per launch from the stored counter summary, or
+    None for each when absent or taken on a different kernel source."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(traffic_file(workload)))
     except (OSError, ValueError):
-        return None
-    if rec.get("attention_source_sha256") != _sha(ATTN_SRC):
-        return None            # kernel changed since the counters were taken
+        return None, None
     if rec.get("workload") != workload:
-        return None            # the counters were taken on another workload
-    return rec.get("hbm_bytes_per_dispatch")
+        return None, None
+    ks = rec.get("kernels", {})
+    attn = ks.get(ATTN_KERNEL, {}).get("hbm_bytes_per_dispatch")
+    if rec.get("attention_source_sha256") != _sha(ATTN_SRC):
+        attn = None            # the kernel changed since the counters were taken
+    sel = None
+    if rec.get("selection_source_sha256") == _sha(SEL_SRC):
+        a = ks.get("pool_kernel", {}).get("hbm_bytes_per_dispatch")
+        b = ks.get("select_emit_kernel", {}).get("hbm_bytes_per_dispatch")
+        sel = (a + b) if (a and b) else None
+    return attn, sel
+
+
+def trace_summary(d, steps, warmup):
+    """Per-kernel durations from rocprofv3 --kernel-trace CSV files, as a markdown table;
+    for the attention kernel also the dispatches of the timed steps alone (the plain
+    kernel's dispatches warmup .. warmup + steps - 1: bench.py's warm-up steps come
+    first and the timed steps next)."""
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+    by = {}
+    for t0, t1, name in rows:
+        by.setdefault(name, []).append((t1 - t0) / 1000.0)
+
+    def stats(v):
+        s = sorted(v)
+        return len(v), sum(v) / len(v), s[len(s) // 2], s[0], s[-1], sum(v) / 1000.0
+    out = ["| kernel | calls | avg us | median us | min us | max us | total ms |", "|---|---|---|---|---|---|---|"]
+    for name, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        n, a, m, lo, hi, tot = stats(v)
+        short = name.split("(")[0][:90]
+        out.append(f"| `{short}` | {n} | {a:.1f} | {m:.1f} | {lo:.1f} | {hi:.1f} | {tot:.2f} |")
+    plain = [v for name, v in by.items() if ATTN_KERNEL in name and "true>" not in name]
+    if plain:
+        timed = plain[0][warmup:warmup + steps]
+        if timed:
+            n, a, m, lo, hi, _ = stats(timed)
+            out.append("")
+            out.append(f"Timed steps only (`{ATTN_KERNEL}`, plain, dispatches {warmup} .. {warmup + steps - 1}): "
+                       f"{n} calls, avg {a:.1f} us, median {m:.1f} us, min {lo:.1f} us, max {hi:.1f} us.")
+    print("\n".join(out))
 
 
 # ---------------------------------------------------------------------------- GPU bench
@@ -129,7 +190,10 @@ def stored_traffic(workload):
 def main():
     args = parse()
     if args.pmc_summary:
-        pmc_summary(args.pmc_summary)
+        pmc_summary(args.pmc_summary, args.workload)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.steps, args.warmup)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -419,7 +483,7 @@ def main():
         sched = {"dense_steps": args.dense_steps, "reselect_every": K, "ms_per_step": round(1e3 * t_s, 4),
                  "TFLOP_s": round(4.0 * 64 * 64 * wl.head_dim * tiles / args.steps / t_s / 1e12, 2)}
 
-    traffic = stored_traffic(wl.name)
+    traffic, sel_traffic = stored_traffic(wl.name)
     rec = {
         "metric": "effective TFLOP/s on kept tiles (select + forward step)",
         "value": round(value, 2),
@@ -448,7 +512,7 @@ def main():
         "attention_tflops_pct_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
         "selection": {
             "ms": round(sel_ms_med, 4), "bytes": sel_bytes, "GB_s": round(sel_gbs, 1),
-            "frac_hbm_peak": round(sel_gbs / PEAK_HBM_GBS, 4),
+            "frac_hbm_peak": round(sel_gbs / PEAK_HBM_GBS, 4), "traffic": sel_traffic,
         },
         "reorder_to_tiles": {"ms": round(reo_ms_med, 4), "GB_s": round(reo_gbs, 1),
                              "frac_hbm_peak": round(reo_gbs / PEAK_HBM_GBS, 4)},
@@ -472,33 +536,75 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
+def _host_info():
+    try:
+        n_aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n_aff = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    omp = os.environ.get("OMP_NUM_THREADS")
+    threads = int(omp) if omp and omp.isdigit() else n_aff
+    return {"nproc": n_aff, "cpu_model": model, "omp_num_threads": omp, "threads": threads}
+
+
+def sample_blocks(wl, thr, n_heads=2, n_blocks=32, seed=1):
+    """The oracle's sample: 2 heads x 32 query blocks drawn with rng(1); with per-head
+    thresholds, the heads of the lowest and the highest threshold."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    if wl.head_threshold_range is not None:
+        heads = [int(np.argmin(thr)), int(np.argmax(thr))]
+    else:
+        heads = sorted(rng.choice(wl.heads, size=min(n_heads, wl.heads), replace=False).tolist())
+    rows = []
+    for h in heads:
+        blocks = np.sort(rng.choice(wl.blocks, size=min(n_blocks, wl.blocks), replace=False))
+        rows.extend((h * wl.blocks + blocks).tolist())        # batch 0
+    return np.array(rows, dtype=np.int64), heads
+
+
 def cpu_baseline(wl, q, k, v, thr, bufs, target_s):
-    """The CPU oracle timed on a bounded sample of the same workload (rank 0, one GPU)."""
+    """The CPU oracle, as it stands, on the host cores of the GPU machine (rank 0, one GPU):
+    the whole selection (pooling, pooled softmax, CDF cut, window) on every row, and the
+    attention of a sample of query blocks (2 heads x 32 blocks, rng(1)) under the GPU's
+    block list; the per-block time extrapolated to the whole step, labelled as such."""
     import numpy as np
     import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    host = _host_info()
     rows = wl.batch * wl.heads * wl.blocks
     rp = bufs.row_ptr.cpu().numpy().astype(np.int64)
     ci = bufs.col_idx[:int(rp[-1])].cpu().numpy()
-    # time a probe of 64 query blocks (the oracle runs rows in parallel), then size the
-    # sample to about target_s seconds
-    rng = np.random.default_rng(1)
-    order = rng.permutation(rows)
-    probe = min(64, rows // 2)
+    q32, k32 = q.float().numpy(), k.float().numpy()
     t0 = time.perf_counter()
-    oracle.attention_rows(q, k, v, rp, ci, order[:probe])
-    per = max(time.perf_counter() - t0, 1e-3) / max(probe, 1)
-    n = int(min(rows - probe, max(2, target_s / per)))
-    sample = order[probe:probe + n]
+    qbar, kbar = oracle.pool(q32), oracle.pool(k32)
+    oracle.select_rows(qbar, kbar, wl.heads, wl.block_grid, thr.astype(np.float64), wl.window)
+    t_sel = time.perf_counter() - t0
+    del q32, k32
+    sample, heads = sample_blocks(wl, thr)
     t0 = time.perf_counter()
     oracle.attention_rows(q, k, v, rp, ci, sample)
     t = time.perf_counter() - t0
     tiles = int(np.sum(rp[sample + 1] - rp[sample]))
     tflops = 4.0 * 64 * 64 * wl.head_dim * tiles / t / 1e12
-    return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 oracle attention over {n} of {rows} query blocks ({tiles} kept tiles, "
-                      f"{t:.1f} s) under the GPU's block list; full-step extrapolation "
-                      f"{t * rows / n:.0f} s"}
+    per_block = t / len(sample)
+    # the full step extrapolated by kept tiles (rows differ in length across heads)
+    full_attn = t * float(rp[-1]) / max(tiles, 1)
+    return {"value": tflops, "unit": "TFLOP/s", "cores": host["threads"], "kind": "oracle",
+            "sample": f"fp64 oracle: full selection of all {rows} query blocks ({t_sel:.1f} s); attention of "
+                      f"{len(sample)} query blocks (heads {heads} x 32 blocks, rng(1); {tiles} kept tiles, "
+                      f"{t:.1f} s) under the GPU's block list",
+            "selection_s": round(t_sel, 3), "attention_s_per_query_block": round(per_block, 4),
+            "extrapolated_full_step_s": round(t_sel + full_attn, 1),
+            "extrapolation": "selection measured in full; attention scaled from the sample by kept tiles",
+            **host}
 
 
 if __name__ == "__main__":

@@ -24,12 +24,14 @@ SPARSE_ATTN_UNSUPPORTED = -2
 SPARSE_ATTN_CAPACITY = -3
 SPARSE_ATTN_WORKSPACE = -4
 SPARSE_ATTN_HIP_ERROR = -5
+SPARSE_ATTN_LOOKBACK_FAULT = -6
 
 EXPORTED = (
     "sparse_attn_version",
     "sparse_attn_status_string",
     "sparse_attn_csr_capacity",
     "sparse_attn_workspace_size",
+    "sparse_attn_select_check",
     "sparse_attn_select",
     "sparse_attn_select_sip",
     "sparse_attn_select_ibcs",
@@ -98,6 +100,8 @@ def lib():
         L.sparse_attn_csr_capacity.restype = I64
         L.sparse_attn_workspace_size.argtypes = [SP]
         L.sparse_attn_workspace_size.restype = I64
+        L.sparse_attn_select_check.argtypes = [SP, P, I64, P]
+        L.sparse_attn_select_check.restype = ctypes.c_int32
         L.sparse_attn_select.argtypes = [SP, ctypes.POINTER(SelectParams), P, P, P, P, I64, P, I64, P]
         L.sparse_attn_select.restype = ctypes.c_int32
         L.sparse_attn_select_sip.argtypes = [SP, ctypes.POINTER(SipParams), P, P, P, P, P, I64, P, I64, P]
@@ -174,6 +178,86 @@ def _check(status: int, where: str):
         raise SparseAttnError(status, where)
 
 
+# ---------------------------------------------------------------- tensor checks
+# The C-ABI takes raw pointers and trusts them; a tensor of the wrong dtype, size or
+# layout would make the kernels read or write outside it.  These checks run before
+# every call that takes tensors and raise ValueError without touching the device.
+
+def _dims(shape: Shape):
+    n = shape.grid_t * shape.grid_h * shape.grid_w
+    vol = max(shape.tile_t * shape.tile_h * shape.tile_w, 1)
+    nb = n // vol
+    return n, nb, shape.batch * shape.heads * nb
+
+
+def _elem_dtype(shape: Shape):
+    import torch
+    return {SPARSE_ATTN_F32: torch.float32, SPARSE_ATTN_BF16: torch.bfloat16}.get(shape.dtype)
+
+
+def _req(t, name: str, dtype, numel: Optional[int] = None, min_numel: Optional[int] = None, device=None,
+         check_device: bool = True):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} must hold at least {min_numel} elements, got {t.numel()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not check_device:
+        return
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
+
+
+def _req_tokens(shape: Shape, **tensors):
+    """[B, H, N, d] operands in the shape's dtype, all on the first one's device."""
+    n, _, _ = _dims(shape)
+    want = shape.batch * shape.heads * n * shape.head_dim
+    dt = _elem_dtype(shape)
+    for name, t in tensors.items():           # form first, then the devices
+        if t is not None:
+            _req(t, name, dt, numel=want, check_device=False)
+    dev = None
+    for name, t in tensors.items():
+        if t is not None:
+            _req(t, name, dt, numel=want, device=dev)
+            dev = t.device
+    return dev
+
+
+def _req_csr(shape: Shape, row_ptr, col_idx, device, capacity: bool = False):
+    import torch
+    _, nb, rows = _dims(shape)
+    _req(row_ptr, "row_ptr", torch.int32, min_numel=rows + 1, device=device)
+    _req(col_idx, "col_idx", torch.int32, min_numel=rows * nb if capacity else None, device=device)
+
+
+def _req_lse(shape: Shape, lse, device):
+    import torch
+    if lse is not None:
+        n, _, _ = _dims(shape)
+        _req(lse, "lse", torch.float32, numel=shape.batch * shape.heads * n, device=device)
+
+
+def _req_buffers(shape: Shape, bufs: "Buffers", device):
+    import torch
+    _req_csr(shape, bufs.row_ptr, bufs.col_idx, device, capacity=True)
+    _req(bufs.workspace, "workspace", torch.uint8, device=device)
+
+
+def _req_workspace(ws, device):
+    import torch
+    if ws is not None:
+        _req(ws, "workspace", torch.uint8, device=device)
+
+
 @dataclass
 class Buffers:
     """Caller-owned device buffers for one shape (the library allocates nothing)."""
@@ -199,7 +283,9 @@ def sparse_attn_select(shape: Shape, q, k, threshold: float = 0.9,
                        head_thresholds: Optional[Sequence[float]] = None, window=(-1, -1, -1),
                        buffers: Optional[Buffers] = None, stream=None) -> Tuple[object, object]:
     """Run the selection; returns (row_ptr, col_idx) views of the caller-owned buffers."""
+    dev = _req_tokens(shape, q=q, k=k)
     bufs = buffers or alloc_buffers(shape, q.device)
+    _req_buffers(shape, bufs, dev)
     ht = None
     if head_thresholds is not None:
         arr = (ctypes.c_float * shape.heads)(*[float(x) for x in head_thresholds])
@@ -218,9 +304,12 @@ def sparse_attn_select_raster(shape: Shape, q, k, q_tiles=None, k_tiles=None, th
     """The selection on raster-ordered q, k, with the tile-major copies written on the way;
     returns (row_ptr, col_idx, q_tiles, k_tiles)."""
     import torch
+    dev = _req_tokens(shape, q=q, k=k)
     bufs = buffers or alloc_buffers(shape, q.device)
     q_tiles = torch.empty_like(q) if q_tiles is None else q_tiles
     k_tiles = torch.empty_like(k) if k_tiles is None else k_tiles
+    _req_tokens(shape, q=q, k=k, q_tiles=q_tiles, k_tiles=k_tiles)
+    _req_buffers(shape, bufs, dev)
     ht = None
     if head_thresholds is not None:
         arr = (ctypes.c_float * shape.heads)(*[float(x) for x in head_thresholds])
@@ -238,7 +327,9 @@ def sparse_attn_select_ibcs(shape: Shape, q, k, threshold: float = 0.9,
                             head_thresholds: Optional[Sequence[float]] = None, window=(-1, -1, -1),
                             buffers: Optional[Buffers] = None, stream=None) -> Tuple[object, object]:
     """The clustering selector with NABLA's CDF cut; returns (row_ptr, col_idx)."""
+    dev = _req_tokens(shape, q=q, k=k)
     bufs = buffers or alloc_buffers(shape, q.device)
+    _req_buffers(shape, bufs, dev)
     ht = None
     if head_thresholds is not None:
         arr = (ctypes.c_float * shape.heads)(*[float(x) for x in head_thresholds])
@@ -256,11 +347,12 @@ def sparse_attn_select_sip(shape: Shape, q, k, budget: float, seed: int = 0, buf
     """Sampling with inclusion probabilities; returns (row_ptr, col_idx, col_bias), the
     first two views of the caller-owned buffers, col_bias fp32 of their capacity."""
     import torch
+    dev = _req_tokens(shape, q=q, k=k)
     bufs = buffers or alloc_buffers(shape, q.device)
+    _req_buffers(shape, bufs, dev)
     if col_bias is None:
         col_bias = torch.empty(bufs.col_idx.numel(), dtype=torch.float32, device=q.device)
-    if col_bias.numel() < bufs.col_idx.numel() or col_bias.dtype != torch.float32:
-        raise ValueError("col_bias must be float32 with the capacity of col_idx")
+    _req(col_bias, "col_bias", torch.float32, min_numel=bufs.col_idx.numel(), device=dev)
     params = SipParams(float(budget), int(seed) & 0xFFFFFFFFFFFFFFFF)
     st = lib().sparse_attn_select_sip(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k),
                                       _ptr(bufs.row_ptr), _ptr(bufs.col_idx), _ptr(col_bias), bufs.col_idx.numel(),
@@ -273,6 +365,7 @@ def sparse_attn_forward(shape: Shape, q, k, v, row_ptr, col_idx, out=None, lse=N
                         workspace=None, stream=None):
     """Block-sparse attention; returns out (and lse when requested)."""
     import torch
+    dev = _req_tokens(shape, q=q, k=k, v=v)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
@@ -280,6 +373,10 @@ def sparse_attn_forward(shape: Shape, q, k, v, row_ptr, col_idx, out=None, lse=N
         lse = torch.empty(B, H, N, dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = torch.empty(sparse_attn_workspace_size(shape), dtype=torch.uint8, device=q.device)
+    _req_tokens(shape, q=q, out=out)
+    _req_csr(shape, row_ptr, col_idx, dev)
+    _req_lse(shape, lse, dev)
+    _req_workspace(workspace, dev)
     st = lib().sparse_attn_forward(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr), _ptr(col_idx),
                                    col_idx.numel(), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                    _stream(stream))
@@ -291,8 +388,8 @@ def sparse_attn_forward_biased(shape: Shape, q, k, v, row_ptr, col_idx, col_bias
                                want_lse: bool = False, workspace=None, stream=None):
     """Block-sparse attention with a logit offset per col_idx entry (fp32 col_bias)."""
     import torch
-    if col_bias.numel() < col_idx.numel() or col_bias.dtype != torch.float32:
-        raise ValueError("col_bias must be float32 with one value per col_idx entry")
+    dev = _req_tokens(shape, q=q, k=k, v=v)
+    _req(col_bias, "col_bias", torch.float32, min_numel=col_idx.numel(), device=dev)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
@@ -300,6 +397,10 @@ def sparse_attn_forward_biased(shape: Shape, q, k, v, row_ptr, col_idx, col_bias
         lse = torch.empty(B, H, N, dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = torch.empty(sparse_attn_workspace_size(shape), dtype=torch.uint8, device=q.device)
+    _req_tokens(shape, q=q, out=out)
+    _req_csr(shape, row_ptr, col_idx, dev)
+    _req_lse(shape, lse, dev)
+    _req_workspace(workspace, dev)
     st = lib().sparse_attn_forward_biased(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr),
                                           _ptr(col_idx), _ptr(col_bias), col_idx.numel(), _ptr(out), _ptr(lse),
                                           _ptr(workspace), workspace.numel(), _stream(stream))
@@ -311,6 +412,7 @@ def sparse_attn_radial_csr(shape: Shape, r0: float, gamma: float, lam: int = 0, 
                            device=None, stream=None):
     """DynamicRad's radial window as a block list -> (row_ptr, col_idx)."""
     bufs = buffers or alloc_buffers(shape, device or "cuda")
+    _req_buffers(shape, bufs, bufs.workspace.device)
     params = RadialParams(float(r0), float(gamma), int(lam))
     st = lib().sparse_attn_radial_csr(ctypes.byref(shape), ctypes.byref(params), _ptr(bufs.row_ptr),
                                       _ptr(bufs.col_idx), bufs.col_idx.numel(), _ptr(bufs.workspace),
@@ -321,7 +423,11 @@ def sparse_attn_radial_csr(shape: Shape, r0: float, gamma: float, lam: int = 0, 
 
 def sparse_attn_mask_to_csr(shape: Shape, block_mask, buffers: Optional[Buffers] = None, stream=None):
     """Dense uint8 block mask [B, H, nB, nB] -> (row_ptr, col_idx)."""
+    import torch
+    _, nb, rows = _dims(shape)
+    _req(block_mask, "block_mask", torch.uint8, numel=rows * nb)
     bufs = buffers or alloc_buffers(shape, block_mask.device)
+    _req_buffers(shape, bufs, block_mask.device)
     st = lib().sparse_attn_mask_to_csr(ctypes.byref(shape), _ptr(block_mask), _ptr(bufs.row_ptr),
                                        _ptr(bufs.col_idx), bufs.col_idx.numel(), _ptr(bufs.workspace),
                                        bufs.workspace.numel(), _stream(stream))
@@ -334,14 +440,19 @@ def sparse_attn_backward(shape: Shape, q, k, v, out, lse, dout, row_ptr, col_idx
     """Gradients (dq, dk, dv) of sparse_attn_forward for the upstream gradient dout
     (written into `grads` = (dq, dk, dv) when given)."""
     import torch
+    dev = _req_tokens(shape, q=q, k=k, v=v, out=out, dout=dout)
+    _req_csr(shape, row_ptr, col_idx, dev)
+    if lse is None:
+        raise ValueError("lse is required")
+    _req_lse(shape, lse, dev)
     ws = workspace if workspace is not None else torch.empty(sparse_attn_workspace_size(shape), dtype=torch.uint8,
                                                               device=q.device)
+    _req_workspace(ws, dev)
     cc = col_idx.numel()
     t_idx = t_idx if t_idx is not None else torch.empty(max(cc, 1), dtype=torch.int32, device=q.device)
+    _req(t_idx, "t_idx", torch.int32, min_numel=cc, device=dev)
     dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-    for g in (dq, dk, dv):
-        if g.shape != q.shape or g.dtype != q.dtype or g.device != q.device or not g.is_contiguous():
-            raise ValueError("gradient outputs must be contiguous tensors like q")
+    _req_tokens(shape, q=q, dq=dq, dk=dk, dv=dv)
     st = lib().sparse_attn_backward(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
                                     _ptr(row_ptr), _ptr(col_idx), cc, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(t_idx),
                                     _ptr(ws), ws.numel(), _stream(stream))
@@ -352,6 +463,7 @@ def sparse_attn_backward(shape: Shape, q, k, v, out, lse, dout, row_ptr, col_idx
 def sparse_attn_full_csr(shape: Shape, buffers: Optional[Buffers] = None, device=None, stream=None):
     """The dense block list (every query block keeps every key block) -> (row_ptr, col_idx)."""
     bufs = buffers or alloc_buffers(shape, device or "cuda")
+    _req_csr(shape, bufs.row_ptr, bufs.col_idx, bufs.row_ptr.device, capacity=True)
     st = lib().sparse_attn_full_csr(ctypes.byref(shape), _ptr(bufs.row_ptr), _ptr(bufs.col_idx), bufs.col_idx.numel(),
                                     _stream(stream))
     _check(st, "sparse_attn_full_csr")
@@ -362,6 +474,7 @@ def sparse_attn_to_tiles(shape: Shape, src, dst=None, stream=None):
     """Raster-ordered [B, H, N, d] -> tile-major (a new tensor unless dst is given)."""
     import torch
     dst = torch.empty_like(src) if dst is None else dst
+    _req_tokens(shape, src=src, dst=dst)
     _check(lib().sparse_attn_to_tiles(ctypes.byref(shape), _ptr(src), _ptr(dst), _stream(stream)),
            "sparse_attn_to_tiles")
     return dst
@@ -371,6 +484,17 @@ def sparse_attn_from_tiles(shape: Shape, src, dst=None, stream=None):
     """Tile-major [B, H, N, d] -> raster order (a new tensor unless dst is given)."""
     import torch
     dst = torch.empty_like(src) if dst is None else dst
+    _req_tokens(shape, src=src, dst=dst)
     _check(lib().sparse_attn_from_tiles(ctypes.byref(shape), _ptr(src), _ptr(dst), _stream(stream)),
            "sparse_attn_from_tiles")
     return dst
+
+
+def sparse_attn_select_check(shape: Shape, workspace, stream=None) -> int:
+    """Status of the last selection on `workspace` (waits for the stream):
+    SPARSE_ATTN_OK, or SPARSE_ATTN_LOOKBACK_FAULT when a row group gave up in its
+    CSR look-back (its row_ptr entries are then -1)."""
+    import torch
+    _req(workspace, "workspace", torch.uint8)
+    return int(lib().sparse_attn_select_check(ctypes.byref(shape), _ptr(workspace), workspace.numel(),
+                                              _stream(stream)))

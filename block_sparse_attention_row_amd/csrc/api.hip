@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "../../include/sparse_attn.h"
 #include "common.h"
@@ -133,6 +134,16 @@ Layout layout(const Dims &d) {
 
 bool bad_thr(float t) { return !(t > 0.f); }   // also rejects NaN
 
+// Polls of the selection's look-back before it gives up: kSpinCap, or the value of
+// SPARSE_ATTN_LOOKBACK_SPIN_CAP (a debugging knob; 0 gives up at the first poll).
+uint32_t lookback_spin_cap() {
+    const char *e = getenv("SPARSE_ATTN_LOOKBACK_SPIN_CAP");
+    if (!e || !*e) return kSpinCap;
+    char *end = nullptr;
+    const unsigned long v = strtoul(e, &end, 10);
+    return (end && *end == 0 && v <= kSpinCap) ? (uint32_t)v : kSpinCap;
+}
+
 int32_t emit_csr(const Dims &d, uint64_t *bits, int32_t *counts, int32_t *groups, int32_t *row_ptr,
                  int32_t *col_idx, hipStream_t st) {
     if (launch_emit(bits, counts, groups, d.rows, (int32_t)d.nB, (int32_t)d.nW, row_ptr, col_idx, st))
@@ -154,6 +165,7 @@ const char *sparse_attn_status_string(int32_t status) {
     case SPARSE_ATTN_CAPACITY: return "col_idx capacity below the worst case B*H*nB*nB";
     case SPARSE_ATTN_WORKSPACE: return "workspace smaller than sparse_attn_workspace_size";
     case SPARSE_ATTN_HIP_ERROR: return "HIP kernel launch failed";
+    case SPARSE_ATTN_LOOKBACK_FAULT: return "a selection gave up waiting in its CSR look-back; its block list is invalid";
     default: return "unknown status";
     }
 }
@@ -170,6 +182,22 @@ int64_t sparse_attn_workspace_size(const sparse_attn_shape *shape) {
     const int32_t st = check_shape(shape, &d);
     if (st) return st;
     return layout(d).total;
+}
+
+int32_t sparse_attn_select_check(const sparse_attn_shape *shape, const void *workspace, int64_t workspace_bytes,
+                                 void *stream) {
+    Dims d;
+    const int32_t st = check_shape(shape, &d);
+    if (st) return st;
+    if (!workspace || !aligned(workspace, 16)) return SPARSE_ATTN_INVALID_ARGUMENT;
+    const Layout L = layout(d);
+    if (workspace_bytes < L.total) return SPARSE_ATTN_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    uint32_t word = 0;
+    const uint32_t *fault = (const uint32_t *)((const char *)workspace + L.ticket) + 1;
+    if (hipMemcpyAsync(&word, fault, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess) return SPARSE_ATTN_HIP_ERROR;
+    if (hipStreamSynchronize(s) != hipSuccess) return SPARSE_ATTN_HIP_ERROR;
+    return word ? SPARSE_ATTN_LOOKBACK_FAULT : SPARSE_ATTN_OK;
 }
 
 static ReorderArgs reorder_args(const sparse_attn_shape *shape, const Dims &d, int inverse) {
@@ -267,6 +295,8 @@ static int32_t select_impl(const sparse_attn_shape *shape, const sparse_attn_sel
     a.thr = thr;
     a.status = status;
     a.ticket = ticket;
+    a.fault = ticket + 1;
+    a.spin_cap = lookback_spin_cap();
     a.row_ptr = row_ptr;
     a.col_idx = col_idx;
     a.rows = d.rows;
@@ -406,6 +436,8 @@ int32_t sparse_attn_select_sip(const sparse_attn_shape *shape, const sparse_attn
     a.thr = (const float *)(ws + L.thr);
     a.status = status;
     a.ticket = ticket;
+    a.fault = ticket + 1;
+    a.spin_cap = lookback_spin_cap();
     a.row_ptr = row_ptr;
     a.col_idx = col_idx;
     a.rows = d.rows;
@@ -483,6 +515,8 @@ int32_t sparse_attn_select_ibcs(const sparse_attn_shape *shape, const sparse_att
     a.thr = thr;
     a.status = status;
     a.ticket = ticket;
+    a.fault = ticket + 1;
+    a.spin_cap = lookback_spin_cap();
     a.row_ptr = row_ptr;
     a.col_idx = col_idx;
     a.rows = d.rows;

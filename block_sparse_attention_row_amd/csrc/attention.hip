@@ -682,9 +682,13 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
         for (int v = 0; v < 16; ++v) acc_o[i][v] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
+    // entries out of range, repeated or below the last accepted column are skipped,
+    // exactly as in the bf16 walk
+    int last = -1;
     for (int e = 0; e < ntile; ++e) {
         const int col = a.col_idx[beg + e];
-        if ((unsigned)col >= (unsigned)a.nB) continue;
+        if (col <= last || col >= a.nB) continue;
+        last = col;
         __syncthreads();
         const float *kt = kg + (int64_t)col * 64 * D;
         const float *vt = vg + (int64_t)col * 64 * D;

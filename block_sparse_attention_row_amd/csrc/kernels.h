@@ -33,13 +33,16 @@ struct PoolSide {
     int32_t n_thr;            // thresholds in `thr` (<= ThrChunk::kMax)
     uint64_t *status;         // look-back words of the selection that follows, zeroed here
     int64_t n_status;
-    uint32_t *ticket;         // its ticket counter, zeroed here
+    uint32_t *ticket;         // its ticket counter ([0]) and look-back fault word ([1]), zeroed here
 };
 
 // Look-back word of a row group: 0 until published, then kStatAgg | the group's
 // kept-block total, finally kStatPre | the inclusive prefix of the totals up to and
-// including the group.  Waits on these words give up after kSpinCap polls (they end
-// in microseconds when every earlier group runs, which the ticket order ensures).
+// including the group.  Waits on these words give up after spin_cap polls (kSpinCap
+// unless the caller lowers it; they end in microseconds when every earlier group
+// runs, which the ticket order ensures).  A group that gives up sets the fault word
+// (ticket[1] = 1) and writes -1 as the row_ptr entry of each of its rows, so that the
+// block list it leaves fails every validity check instead of looking plausible.
 constexpr uint64_t kStatAgg = 1ull << 62, kStatPre = 2ull << 62, kStatFlags = 3ull << 62;
 constexpr uint32_t kSpinCap = 1u << 22;
 
@@ -54,6 +57,8 @@ struct SelectArgs {
     const float *thr;         // [H] thresholds (device)
     uint64_t *status;         // [n_groups] look-back words (zeroed by the pooling kernel)
     uint32_t *ticket;         // group ticket counter (zeroed by the pooling kernel)
+    uint32_t *fault;          // look-back fault word (ticket + 1, zeroed with it)
+    uint32_t spin_cap;        // polls of one look-back before it gives up
     int32_t *row_ptr;         // [rows + 1]
     int32_t *col_idx;         // [nnz]
     int64_t rows;             // BH * nB

@@ -56,7 +56,10 @@ __global__ __launch_bounds__(256) void reorder_pool_kernel(ReorderPoolArgs p) {
     const int64_t gt = (int64_t)blockIdx.x * blockDim.x + t;
     if (blockIdx.x == 0 && t < p.side.n_thr) p.side.thr_dst[t] = p.side.thr.v[t];
     for (int64_t i = gt; i < p.side.n_status; i += (int64_t)gridDim.x * blockDim.x) p.side.status[i] = 0;
-    if (gt == 0) *p.side.ticket = 0u;
+    if (gt == 0) {
+        p.side.ticket[0] = 0u;
+        p.side.ticket[1] = 0u;
+    }
     const bool keys = (int64_t)blockIdx.x < p.tiles;
     const int64_t b = keys ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - p.tiles;   // tile over B*H*nB
     const u32x4 *s4 = reinterpret_cast<const u32x4 *>(keys ? p.k_src : p.q_src);

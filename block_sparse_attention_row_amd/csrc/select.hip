@@ -103,7 +103,10 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ k, __bf
     const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (blockIdx.x == 0 && (int)threadIdx.x < side.n_thr) side.thr_dst[threadIdx.x] = side.thr.v[threadIdx.x];
     for (int64_t i = gt; i < side.n_status; i += (int64_t)gridDim.x * blockDim.x) side.status[i] = 0;
-    if (gt == 0) *side.ticket = 0u;
+    if (gt == 0) {
+        side.ticket[0] = 0u;
+        side.ticket[1] = 0u;
+    }
     using P = BlockPool<T, D, 16>;
     const int lane = threadIdx.x & 63;
     const int64_t blk = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
@@ -433,13 +436,18 @@ __device__ __forceinline__ void sip_cut(const SelectArgs &a, const float (&s)[NE
 // groups before the current position are read at once and summed up to the nearest
 // one that carries a prefix; while one of those has published nothing yet the wave
 // polls again.  Every group before g holds an earlier ticket, so it is running or
-// done and publishes its total without waiting on anyone; the polls end.
-__device__ __forceinline__ int64_t group_lookback(uint64_t *status, int64_t g, int64_t total, int lane) {
+// done and publishes its total without waiting on anyone; the polls end.  After
+// spin_cap polls the wave gives up: it counts the missing totals as 0 (so that the
+// offsets of later groups can only come out low, never past the end of col_idx) and
+// reports that it gave up through `gave_up`.
+__device__ __forceinline__ int64_t group_lookback(uint64_t *status, int64_t g, int64_t total, int lane,
+                                                  uint32_t spin_cap, bool &gave_up) {
     if (lane == 0)
         __hip_atomic_store(status + g, (g == 0 ? kStatPre : kStatAgg) | (uint64_t)total, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     int64_t base = 0, p = g - 1;
     uint32_t polls = 0;
+    gave_up = false;
     while (p >= 0) {
         const int64_t idx = p - lane;
         const uint64_t w = idx >= 0 ? __hip_atomic_load(status + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
@@ -448,10 +456,12 @@ __device__ __forceinline__ int64_t group_lookback(uint64_t *status, int64_t g, i
         const uint64_t pre = __ballot(f == kStatPre);
         const int first = pre ? __builtin_ctzll(pre) : 64;       // nearest group carrying a prefix
         const uint64_t upto = first >= 63 ? ~0ull : ((2ull << first) - 1);
-        if ((__ballot(f == 0) & upto) && ++polls < kSpinCap) {
+        const bool missing = (__ballot(f == 0) & upto) != 0;
+        if (missing && ++polls < spin_cap) {
             __builtin_amdgcn_s_sleep(1);
             continue;
         }
+        gave_up = gave_up || missing;
         const int v = lane <= first && f != 0 ? (int)(w & ~kStatFlags) : 0;
         base += wave_sum_i(v);
         if (first < 64) break;
@@ -488,6 +498,7 @@ __global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
     __shared__ uint32_t s_ticket;
     __shared__ int32_t wave_count[kSelRows];
     __shared__ int64_t s_base;
+    __shared__ int32_t s_gave_up;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -590,14 +601,27 @@ __global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
     // ---- offsets: the group's by look-back, then the rows' within the group
     if (wave == 0) {
         const int32_t total = wave_sum_i(lane < kSelRows ? wave_count[lane] : 0);
-        const int64_t base = group_lookback(a.status, g, total, lane);
-        if (lane == 0) s_base = base;
+        bool gave_up;
+        const int64_t base = group_lookback(a.status, g, total, lane, a.spin_cap, gave_up);
+        if (lane == 0) {
+            s_base = base;
+            s_gave_up = gave_up;
+            if (gave_up) __hip_atomic_store(a.fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     __syncthreads();
     if (wave >= nrows) return;
+    const int64_t row = (int64_t)bh * a.nB + i0 + wave;
+    if (s_gave_up) {
+        // the offset is unknown: poison the group's rows and write no columns
+        if (lane == 0) {
+            a.row_ptr[row] = -1;
+            if (row == a.rows - 1) a.row_ptr[a.rows] = -1;
+        }
+        return;
+    }
     int32_t before = 0;
     for (int w = 0; w < wave; ++w) before += wave_count[w];
-    const int64_t row = (int64_t)bh * a.nB + i0 + wave;
     int32_t pos = (int32_t)s_base + before;
     if (lane == 0) {
         a.row_ptr[row] = pos;

@@ -24,7 +24,8 @@
  *     and keeps no state between calls; scratch space comes in through
  *     `workspace` (see sparse_attn_workspace_size).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
- *     and runs asynchronously: no call synchronises the host.  Concurrent
+ *     and runs asynchronously: no call synchronises the host, except the
+ *     debugging check sparse_attn_select_check.  Concurrent
  *     calls are safe as long as they do not share output or workspace
  *     buffers.
  *   - Return value: SPARSE_ATTN_OK (0) or a negative status.  Every argument
@@ -54,6 +55,8 @@ extern "C" {
 #define SPARSE_ATTN_CAPACITY (-3)         /* col_idx shorter than the worst case B*H*nB*nB      */
 #define SPARSE_ATTN_WORKSPACE (-4)        /* workspace smaller than sparse_attn_workspace_size  */
 #define SPARSE_ATTN_HIP_ERROR (-5)        /* a kernel launch failed                             */
+#define SPARSE_ATTN_LOOKBACK_FAULT (-6)   /* a selection gave up in its CSR look-back (see
+                                             sparse_attn_select_check)                          */
 
 /*
  * Problem shape.  head_dim must be 64 or 128; the tile must hold 64 tokens
@@ -107,6 +110,25 @@ int64_t sparse_attn_csr_capacity(const sparse_attn_shape *shape);
  * the shape is invalid.
  */
 int64_t sparse_attn_workspace_size(const sparse_attn_shape *shape);
+
+/*
+ * Outcome of the last selection (sparse_attn_select, _select_raster, _select_sip or
+ * _select_ibcs) that used `workspace`, for callers that want to confirm a block
+ * list before using it.  The selections chain the CSR offsets of their row groups
+ * through a look-back whose waits are bounded; a group that runs out of polls
+ * writes -1 as the row_ptr entry of each of its rows (so the block list fails any
+ * validity check) and sets a fault word in the workspace.  This call reads that
+ * word: it enqueues a 4-byte device-to-host copy on `stream` and, unlike every
+ * other entry point, waits for the stream to finish.
+ *   Returns SPARSE_ATTN_OK, SPARSE_ATTN_LOOKBACK_FAULT, or an argument status
+ *   (checked on the host first, as everywhere).
+ * The wait is 2^22 polls.  The environment variable SPARSE_ATTN_LOOKBACK_SPIN_CAP
+ * (a decimal count, at most 2^22, read by each selection call) lowers it, so that
+ * tests can drive the give-up path without hanging anything; 0 gives up at the
+ * first unpublished word.
+ */
+int32_t sparse_attn_select_check(const sparse_attn_shape *shape, const void *workspace, int64_t workspace_bytes,
+                                 void *stream);
 
 /*
  * Dynamic block selection (pooling, reduced attention map, CDF cut, window

@@ -58,9 +58,10 @@ def kmeans(x: np.ndarray, k: int = K_CLUSTERS, iters: int = ITERS):
     return mu, w, gap
 
 
-def mixture_scores(q, k, heads: int, scale: Optional[float] = None):
+def mixture_scores(q, k, heads: int, scale: Optional[float] = None, iters: int = ITERS):
     """p~ [B*H*nB, nB] (the pair's row for both of its blocks) and the smallest
-    assignment gap per pair [B*H, ceil(nB/2)]."""
+    assignment gap per pair [B*H, ceil(nB/2)].  `iters`: k-means rounds (the reading
+    is ITERS; other counts serve tests that show the round count matters)."""
     q = np.asarray(q, dtype=np.float64)
     kb = pool(k)                                   # [B, H, nB, d] fp64
     *lead, N, d = q.shape
@@ -75,7 +76,7 @@ def mixture_scores(q, k, heads: int, scale: Optional[float] = None):
     for bh in range(BH):
         for p in range(npairs):
             t0, t1 = 128 * p, min(128 * p + 128, N)
-            mu, w, gaps[bh, p] = kmeans(qf[bh, t0:t1])
+            mu, w, gaps[bh, p] = kmeans(qf[bh, t0:t1], iters=iters)
             s = mu @ kf[bh].T * sc                 # [8, nB]
             e = np.exp(s - s.max(axis=1, keepdims=True))
             row = (w[:, None] * e / e.sum(axis=1, keepdims=True)).sum(axis=0)
@@ -99,9 +100,9 @@ def cdf_keep(p: np.ndarray, thr: float) -> np.ndarray:
     return keep
 
 
-def select_ibcs(q, k, heads: int, thr: float, scale: Optional[float] = None):
+def select_ibcs(q, k, heads: int, thr: float, scale: Optional[float] = None, iters: int = ITERS):
     """(keep [rows, nB], row_ptr, col_idx, p~ [rows, nB], gaps [B*H, pairs])."""
-    pt, gaps = mixture_scores(q, k, heads, scale)
+    pt, gaps = mixture_scores(q, k, heads, scale, iters)
     keep = cdf_keep(pt, thr)
     row_ptr, col_idx = csr_from_mask(keep)
     return keep, row_ptr, col_idx, pt, gaps

@@ -5,15 +5,21 @@ Mask rule (selection).  Where GPU and oracle disagree on block j of a row,
 with p, E the oracle's probabilities and exclusive CDF mass and c the
 oracle's crossing block (the last block it keeps in CDF order):
   R1  excused if |E(j) - thr| <= 1e-4;
-  R2  excused if |p_j - p_c| <= 1e-5 * p_c (a rank swap of near-equal blocks
-      at the cut);
-window blocks are never excused.  On rows that disagree, the GPU's kept set
-must still hold mass >= thr - 1e-4 and stay minimal (mass minus its smallest
-block < thr + 1e-4) when the window is off.
+  R2  excused (when R1 does not excuse it) if |p_j - p_c| <= 1e-5 * p_c: a rank
+      swap of near-equal blocks at the cut, which moves E(j) by a whole p_c;
+window blocks are never excused.  On every row that disagrees, the GPU's CDF
+set (the oracle's CDF set with the differing blocks toggled: those are never
+window blocks) must hold mass >= thr - 1e-4, stay minimal (mass minus its
+smallest block < thr + 1e-4), and hold the oracle set's mass to within 1e-4;
+the last bound is what keeps an R2 swap a harmless one.  The counts (R1 only,
+R2 only, blocks inside the R1 band over all rows, the largest mass deviation)
+are returned, and written as JSON to $SPARSE_ATTN_PARITY_DIR when it is set.
 """
 from __future__ import annotations
 
+import json
 import math
+import os
 from dataclasses import dataclass
 
 import numpy as np
@@ -31,15 +37,17 @@ TOL = {"bf16": 2e-2, "f32": 1e-4}
 # relative error in the normaliser; fp32 keeps fp32 weights.
 LSE_TOL = {"bf16": 5e-3, "f32": 1e-4}
 # Backward (bf16): max |GPU - oracle| over max |oracle|, per gradient.  The kernels
-# round P (for dV) and dS (for dQ, dK) to bf16 before the MFMA products: unit
-# roundoff u = 2^-9 = 1.95e-3 per term.  dV = sum_n P dO has nonnegative weights, so
-# its error stays near u: BWD_TOL_DV = 2.5u.  Each row of dS sums to zero
+# round P (for dV) and dS (for dQ, dK) to bf16 before the MFMA products.  bf16 keeps
+# 8 significand bits, so its unit roundoff (half an ulp of 1) is u = 2^-8 = 3.9e-3
+# per rounded term.  dV = sum_n P dO has nonnegative weights, so the roundings of P
+# (relative, at most u each, of random sign) average out and its error stays below
+# u times max |dV|: BWD_TOL_DV = 1.28u = 5e-3.  Each row of dS sums to zero
 # (sum_m P (dP - D) = D - D), so dQ = scale sum_m dS k_m cancels the keys' common part
 # and dK likewise; the rounding error scales with sum |dS| |k| instead, which was 5-9
 # times max |dQ| on the test inputs (checked by an fp64 emulation of the roundings,
 # which gives the GPU's errors to within a few percent).  When the oracle recomputes O
 # exactly while the kernels read the bf16 forward output, D = dO . O carries a further
-# |dO| |O| u, passed into dS the same way.  BWD_TOL_DQK = 10u covers both.
+# |dO| |O| u, passed into dS the same way.  BWD_TOL_DQK = 5.1u = 2e-2 covers both.
 BWD_TOL_DV = 5e-3
 BWD_TOL_DQK = 2e-2
 
@@ -73,8 +81,10 @@ def gpu_select(wl: Workload, q, k, thr, window=None, bufs=None):
     shape = shape_for(wl)
     win = wl.window if window is None else window
     head_thr = None if wl.head_threshold_range is None else [float(x) for x in thr]
+    bufs = bufs or B.alloc_buffers(shape, q.device)
     rp, ci = B.sparse_attn_select(shape, q, k, threshold=float(np.float32(wl.threshold)),
                                   head_thresholds=head_thr, window=win, buffers=bufs)
+    assert B.sparse_attn_select_check(shape, bufs.workspace) == B.SPARSE_ATTN_OK
     torch.cuda.synchronize()
     rp_h = rp.cpu().numpy().astype(np.int64)
     nnz = int(rp_h[-1])
@@ -87,25 +97,30 @@ class MaskReport:
     rows: int
     diff_rows: int
     diff_blocks: int
-    r1: int
-    r2: int
+    r1: int                  # differing blocks excused by R1
+    r2: int                  # differing blocks excused by R2 only
     unexcused: int
     window_missing: int
     invariant_fail: int
+    band: int = -1           # blocks inside the R1 band over all rows (-1: not counted)
+    mass_dev: float = 0.0    # largest |GPU CDF-set mass - oracle CDF-set mass| on differing rows
+
+    def as_dict(self):
+        return dict(self.__dict__)
 
 
 def compare_masks(gpu_mask: np.ndarray, keep: np.ndarray, qbar, kbar, wl: Workload, thr: np.ndarray,
-                  window=None) -> MaskReport:
+                  window=None, band: int = -1) -> MaskReport:
     """gpu_mask, keep: [rows, nB]; keep is the oracle's (bit0 CDF, bit1 window)."""
     win = wl.window if window is None else window
     nB = keep.shape[1]
     oracle_mask = keep != 0
     diff = np.nonzero((gpu_mask != oracle_mask).any(axis=1))[0]
     r1 = r2 = unexc = wmiss = inv = nblk = 0
+    mass_dev = 0.0
     if len(diff):
         kk, p, E = oracle.select_rows(qbar, kbar, wl.heads, wl.block_grid, thr.astype(np.float64), win,
                                       rows=diff, stats=True)
-        window_on = all(w >= 0 for w in win)
         for n, r in enumerate(diff):
             t = float(thr[(r // nB) % wl.heads])
             cdf = (kk[n] & 1) != 0
@@ -114,7 +129,8 @@ def compare_masks(gpu_mask: np.ndarray, keep: np.ndarray, qbar, kbar, wl: Worklo
             else:
                 c = int(np.argmax(np.where(cdf, E[n], -1.0)))
                 pc = p[n, c]
-            for j in np.nonzero(gpu_mask[r] != oracle_mask[r])[0]:
+            dj = np.nonzero(gpu_mask[r] != oracle_mask[r])[0]
+            for j in dj:
                 nblk += 1
                 if kk[n, j] & 2:
                     wmiss += 1
@@ -125,18 +141,54 @@ def compare_masks(gpu_mask: np.ndarray, keep: np.ndarray, qbar, kbar, wl: Worklo
                     r2 += 1
                 else:
                     unexc += 1
-            if not window_on and t < 1.0:
-                kp = p[n][gpu_mask[r]]
-                if not (kp.sum() >= t - R1_BAND and kp.sum() - kp.min() < t + R1_BAND):
+            if t < 1.0:
+                # the GPU's CDF set: the oracle's with the differing (non-window) blocks toggled
+                g = cdf.copy()
+                g[dj] = ~g[dj]
+                kp = p[n][g]
+                m = float(kp.sum()) if kp.size else 0.0
+                if not (kp.size and m >= t - R1_BAND and m - kp.min() < t + R1_BAND):
                     inv += 1
-    return MaskReport(gpu_mask.shape[0], len(diff), nblk, r1, r2, unexc, wmiss, inv)
+                mass_dev = max(mass_dev, abs(m - float(p[n][cdf].sum())))
+    return MaskReport(gpu_mask.shape[0], len(diff), nblk, r1, r2, unexc, wmiss, inv, band, mass_dev)
 
 
-def oracle_select_full(wl: Workload, q, k, thr):
+def mask_ok(rep: MaskReport) -> bool:
+    return (rep.unexcused == 0 and rep.window_missing == 0 and rep.invariant_fail == 0
+            and rep.mass_dev <= R1_BAND)
+
+
+def record_masks(label: str, rep: MaskReport, **extra):
+    """Print the mask report and, with $SPARSE_ATTN_PARITY_DIR set, keep it as JSON."""
+    print(f"[masks] {label}: {fmt(rep)}", flush=True)
+    d = os.environ.get("SPARSE_ATTN_PARITY_DIR")
+    if d:
+        os.makedirs(d, exist_ok=True)
+        rec = dict(label=label, **rep.as_dict(), **extra)
+        with open(os.path.join(d, f"masks_{label}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+
+
+def oracle_select_full(wl: Workload, q, k, thr, window=None, count_band: bool = False, chunk: int = 2048):
+    """The oracle's selection for every row: (qbar, kbar, keep) and, with count_band,
+    also the number of blocks whose exclusive mass lies within R1_BAND of the
+    threshold (the blocks R1 could excuse), counted chunk by chunk."""
+    win = wl.window if window is None else window
     qbar = oracle.pool(q)
     kbar = oracle.pool(k)
-    keep = oracle.select_rows(qbar, kbar, wl.heads, wl.block_grid, thr.astype(np.float64), wl.window)
-    return qbar, kbar, keep
+    th = thr.astype(np.float64)
+    if not count_band:
+        return qbar, kbar, oracle.select_rows(qbar, kbar, wl.heads, wl.block_grid, th, win)
+    rows = wl.batch * wl.heads * wl.blocks
+    keep = np.empty((rows, wl.blocks), dtype=np.uint8)
+    band = 0
+    for r0 in range(0, rows, chunk):
+        rr = np.arange(r0, min(rows, r0 + chunk))
+        kk, _, E = oracle.select_rows(qbar, kbar, wl.heads, wl.block_grid, th, win, rows=rr, stats=True)
+        keep[rr] = kk
+        t = th[(rr // wl.blocks) % wl.heads][:, None]
+        band += int(((np.abs(E - t) <= R1_BAND) & (t < 1.0)).sum())
+    return qbar, kbar, keep, band
 
 
 def gpu_forward(wl: Workload, q, k, v, row_ptr, col_idx, want_lse=True):
@@ -309,8 +361,9 @@ def flops_kept(nnz: int, d: int) -> float:
 
 
 def fmt(rep: MaskReport) -> str:
-    return (f"rows={rep.rows} diff_rows={rep.diff_rows} diff_blocks={rep.diff_blocks} R1={rep.r1} R2={rep.r2} "
-            f"unexcused={rep.unexcused} window_missing={rep.window_missing} invariant_fail={rep.invariant_fail}")
+    return (f"rows={rep.rows} diff_rows={rep.diff_rows} diff_blocks={rep.diff_blocks} R1={rep.r1} R2only={rep.r2} "
+            f"unexcused={rep.unexcused} window_missing={rep.window_missing} invariant_fail={rep.invariant_fail} "
+            f"band={rep.band} mass_dev={rep.mass_dev:.2e}")
 
 
 def scale_of(d: int) -> float:

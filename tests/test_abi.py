@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert B.sparse_attn_version() == 10000
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6):
         assert B.status_string(st) and B.status_string(st) != "unknown status"
     assert B.status_string(-99) == "unknown status"
 
@@ -309,3 +309,73 @@ def test_select_ibcs_rejects_before_launch():
     assert f(ctypes.byref(s), ctypes.byref(ok), A, A, A, A, cap - 1, A, wsb, None) == B.SPARSE_ATTN_CAPACITY
     assert f(ctypes.byref(s), ctypes.byref(ok), A, A, A, A, cap, A, wsb - 1, None) == B.SPARSE_ATTN_WORKSPACE
     assert f(ctypes.byref(s), ctypes.byref(ok), None, A, A, A, cap, A, wsb, None) == B.SPARSE_ATTN_INVALID_ARGUMENT
+
+
+
+# ---------------------------------------------------------------- binding checks
+# Every call that takes tensors checks them against the shape first (dtype, size,
+# contiguity, device) and raises ValueError without touching the GPU.
+
+def _small():
+    return B.make_shape(1, 2, 64, (2, 8, 16), "bf16")      # N = 256, nB = 4
+
+
+def _tok(dtype=None, n=None):
+    import torch
+    return torch.zeros(n if n is not None else 2 * 256 * 64, dtype=dtype or torch.bfloat16)
+
+
+def test_binding_rejects_wrong_dtype_before_any_call():
+    import torch
+    s = _small()
+    with pytest.raises(ValueError, match="must be torch.bfloat16"):
+        B.sparse_attn_select(s, _tok(torch.float32), _tok())
+    with pytest.raises(ValueError, match="must be torch.bfloat16"):
+        B.sparse_attn_forward(s, _tok(), _tok(torch.float16), _tok(), None, None)
+
+
+def test_binding_rejects_wrong_size_and_layout():
+    import torch
+    s = _small()
+    with pytest.raises(ValueError, match="must hold 32768 elements"):
+        B.sparse_attn_select(s, _tok(n=100), _tok())
+    nc = torch.zeros(2 * 64, 256, dtype=torch.bfloat16).t()        # right size, not contiguous
+    with pytest.raises(ValueError, match="contiguous"):
+        B.sparse_attn_forward(s, nc, _tok(), _tok(), None, None)
+
+
+def test_binding_rejects_host_tensors():
+    s = _small()
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.sparse_attn_select(s, _tok(), _tok())
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.sparse_attn_to_tiles(s, _tok(), _tok())
+
+
+def test_binding_rejects_bad_csr_and_lse():
+    import torch
+    s = _small()
+    ok = dict(dtype=torch.int32)
+    # the dtype checks come before the device check, so host tensors reach them
+    with pytest.raises(ValueError, match="row_ptr must be torch.int32"):
+        B._req_csr(s, torch.zeros(9, dtype=torch.int64), torch.zeros(4, **ok), None)
+    with pytest.raises(ValueError, match="at least 9 elements"):
+        B._req_csr(s, torch.zeros(8, **ok), torch.zeros(4, **ok), None)
+    with pytest.raises(ValueError, match="at least 32 elements"):
+        B._req(torch.zeros(31, **ok), "col_idx", torch.int32, min_numel=32)
+    with pytest.raises(ValueError, match="lse must be torch.float32"):
+        B._req_lse(s, torch.zeros(512, dtype=torch.float64), None)
+    with pytest.raises(ValueError, match="lse must hold 512 elements"):
+        B._req_lse(s, torch.zeros(511, dtype=torch.float32), None)
+
+
+def test_select_check_rejects_bad_arguments_on_the_host():
+    L = B.lib()
+    s = _small()
+    ws = B.sparse_attn_workspace_size(s)
+    assert L.sparse_attn_select_check(ctypes.byref(s), None, ws, None) == B.SPARSE_ATTN_INVALID_ARGUMENT
+    assert L.sparse_attn_select_check(ctypes.byref(s), 16, ws - 1, None) == B.SPARSE_ATTN_WORKSPACE
+    assert L.sparse_attn_select_check(ctypes.byref(s), 8, ws, None) == B.SPARSE_ATTN_INVALID_ARGUMENT
+    bad = B.make_shape(1, 2, 96, (2, 8, 16), "bf16")
+    assert L.sparse_attn_select_check(ctypes.byref(bad), 16, ws, None) == B.SPARSE_ATTN_UNSUPPORTED
+    assert "look-back" in B.status_string(B.SPARSE_ATTN_LOOKBACK_FAULT)

@@ -57,10 +57,10 @@ def test_small_select_and_forward(case):
     # selection: GPU mask vs oracle mask under the excuse rules
     rp, ci = P.gpu_select(wl, qd, kd, thr)
     gmask = P.check_csr(rp, ci, wl.blocks)
-    qbar, kbar, keep = P.oracle_select_full(wl, q, k, thr)
-    rep = P.compare_masks(gmask, keep, qbar, kbar, wl, thr)
-    print(P.fmt(rep), flush=True)
-    assert rep.unexcused == 0 and rep.window_missing == 0 and rep.invariant_fail == 0
+    qbar, kbar, keep, band = P.oracle_select_full(wl, q, k, thr, count_band=True)
+    rep = P.compare_masks(gmask, keep, qbar, kbar, wl, thr, band=band)
+    P.record_masks(f"small_{wl.name}_{reading}", rep)
+    assert P.mask_ok(rep), P.fmt(rep)
 
     # forward under the oracle's CSR, every row
     orp, oci = oracle.csr_from_mask(keep != 0)
@@ -103,10 +103,10 @@ def test_long_row_selection_matches_oracle(case):
     qd, kd = P.to_device(q, k)
     rp, ci = P.gpu_select(wl, qd, kd, thr_h)
     gmask = P.check_csr(rp, ci, wl.blocks)
-    qbar, kbar, keep = P.oracle_select_full(wl, q, k, thr_h)
-    rep = P.compare_masks(gmask, keep, qbar, kbar, wl, thr_h)
-    print(P.fmt(rep), flush=True)
-    assert rep.unexcused == 0 and rep.window_missing == 0 and rep.invariant_fail == 0
+    qbar, kbar, keep, band = P.oracle_select_full(wl, q, k, thr_h, count_band=True)
+    rep = P.compare_masks(gmask, keep, qbar, kbar, wl, thr_h, band=band)
+    P.record_masks(f"long_rows_{name}", rep)
+    assert P.mask_ok(rep), P.fmt(rep)
 
 
 def test_threshold_one_is_dense_attention():
@@ -147,9 +147,13 @@ def test_external_mask_empty_rows_and_roundtrip():
     assert torch.all(torch.isneginf(l[[0, 7, rows - 1]]))
 
 
-def test_forward_skips_out_of_order_and_out_of_range_columns():
-    wl = small_workload("order", 2, 128, (2, 2, 4), "bf16", seed=13)
-    q, k, v, _ = make_inputs(wl, "B")
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_forward_skips_out_of_order_and_out_of_range_columns(dtype):
+    """Both dtypes skip entries that are out of range, repeated or below the row's last
+    accepted column: the output over the polluted list equals, bit for bit, the output
+    over the clean one."""
+    wl = small_workload("order", 2, 128 if dtype == "bf16" else 64, (2, 2, 4), dtype, seed=13)
+    q, k, v, _ = make_inputs(wl, "B" if dtype == "bf16" else "A")
     qd, kd, vd = P.to_device(q, k, v)
     nB = wl.blocks
     rows = wl.heads * nB
@@ -159,7 +163,7 @@ def test_forward_skips_out_of_order_and_out_of_range_columns():
     orp, oci = oracle.csr_from_mask(mask)
     out_a, lse_a = P.gpu_forward(wl, qd, kd, vd, orp, oci)
     err, lerr = P.compare_rows(wl, out_a, lse_a, q, k, v, orp, oci, np.arange(rows))
-    assert err <= P.TOL["bf16"] and lerr <= P.LSE_TOL["bf16"]
+    assert err <= P.TOL[dtype] and lerr <= P.LSE_TOL[dtype]
     # entries out of range, repeated or below the previous entry are skipped
     rp2 = [0]
     ci2 = []
@@ -307,10 +311,10 @@ def test_raster_selection(case):
     assert torch.equal(qt, qd) and torch.equal(kt, kd)
     rp_h = rp.cpu().numpy().astype(np.int64)
     gmask = P.check_csr(rp_h, ci[:int(rp_h[-1])].cpu().numpy(), wl.blocks)
-    qbar, kbar, keep = P.oracle_select_full(wl, q, k, thr_h)
-    rep = P.compare_masks(gmask, keep, qbar, kbar, wl, thr_h)
-    print(P.fmt(rep), flush=True)
-    assert rep.unexcused == 0 and rep.window_missing == 0 and rep.invariant_fail == 0
+    qbar, kbar, keep, band = P.oracle_select_full(wl, q, k, thr_h, count_band=True)
+    rep = P.compare_masks(gmask, keep, qbar, kbar, wl, thr_h, band=band)
+    P.record_masks(f"raster_{name}", rep)
+    assert P.mask_ok(rep), P.fmt(rep)
 
 
 def test_full_csr_is_the_dense_block_list():
@@ -441,11 +445,49 @@ def test_ibcs_selection_matches_oracle(d, grid, thr, reading):
     print(f"ibcs d={d} nB={nB}: kept {int(gmask.sum())} (oracle {int(keep.sum())}), differing {ndiff}, "
           f"excused {nexc}, unexcused {nunx}, near-tie rows {int(skip.sum())} (differing there {near_diff})", flush=True)
     assert nunx == 0
-    assert np.all(mass >= thr - 1e-3)
+    # the kept mass on the oracle's p~: within the R1 band of the threshold where the
+    # clustering matches; a near-tie pair may cluster differently on the GPU, which moves
+    # p~ itself, so only a looser 1e-3 holds there
+    assert np.all(mass[~skip] >= thr - 1e-4) and np.all(mass[skip] >= thr - 1e-3)
     # both blocks of a pair share the row
     for r in range(0, wl.heads * nB - 1):
         if (r % nB) % 2 == 0 and (r % nB) + 1 < nB:
             assert np.array_equal(gmask[r], gmask[r + 1])
+
+
+def test_ibcs_runs_four_kmeans_rounds():
+    """The kernel's k-means round count, pinned through the block list.  Every pair of
+    query blocks holds the hand-derived chain of the k-means golden case (shifted by
+    -9 along the first axis, so that the two moving centroids take opposite signs)
+    and its six frozen groups along the second axis, where the keys are zero (they add
+    a uniform share).  Key block j is c_j along the first axis, c_j distinct multiples
+    of 1/8.  The mixture's order then depends on where the two centroids sit, and on
+    the oracle the block lists after 1, 2, 3, 5 and 6 rounds all differ from the one
+    after 4; the GPU's must equal the 4-round list exactly (every cumulative mass is
+    more than 1e-2 from the threshold and neighbouring p~ differ by > 7e-4 relative,
+    far above the kernel's rounding)."""
+    from oracle import ibcs
+    from .test_oracle_pins import _kmeans_chain_golden
+    x, _ = _kmeans_chain_golden()
+    nB, d, thr, scale = 32, 128, 0.5, 0.25
+    q = np.zeros((1, 1, nB * 64, d), dtype=np.float32)
+    for p in range(nB // 2):
+        q[0, 0, 128 * p:128 * p + 32, 0] = x[:32, 0] - 9.0
+        q[0, 0, 128 * p + 32:128 * p + 128, 1] = x[32:, 0]
+    c = (np.arange(nB) - 15.5) / 8.0
+    np.random.default_rng(5).shuffle(c)
+    k = np.zeros((1, 1, nB * 64, d), dtype=np.float32)
+    k[0, 0, :, 0] = np.repeat(c, 64)
+    masks = {it: ibcs.select_ibcs(q, k, 1, thr, scale=scale, iters=it)[0] for it in (1, 2, 3, 4, 5, 6)}
+    assert all((masks[it] != masks[4]).any() for it in (1, 2, 3, 5, 6))
+    shape = B.make_shape(1, 1, d, (1, 32, 64), "bf16", scale)
+    qd = torch.as_tensor(q).to(torch.bfloat16).cuda()
+    kd = torch.as_tensor(k).to(torch.bfloat16).cuda()
+    rp, ci = B.sparse_attn_select_ibcs(shape, qd, kd, threshold=thr)
+    torch.cuda.synchronize()
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    gmask = P.check_csr(rp_h, ci[:int(rp_h[-1])].cpu().numpy(), nB)
+    assert np.array_equal(gmask, masks[4])
 
 
 def _backward_case(wl, reading, mask=None, seed=0):
@@ -579,10 +621,10 @@ def test_tiny_workload_full():
     qd, kd, vd = P.to_device(q, k, v)
     rp, ci = P.gpu_select(wl, qd, kd, thr)
     gmask = P.check_csr(rp, ci, wl.blocks)
-    qbar, kbar, keep = P.oracle_select_full(wl, q, k, thr)
-    rep = P.compare_masks(gmask, keep, qbar, kbar, wl, thr)
-    print(P.fmt(rep), flush=True)
-    assert rep.unexcused == 0
+    qbar, kbar, keep, band = P.oracle_select_full(wl, q, k, thr, count_band=True)
+    rep = P.compare_masks(gmask, keep, qbar, kbar, wl, thr, band=band)
+    P.record_masks("tiny_f32_A", rep)
+    assert P.mask_ok(rep), P.fmt(rep)
     orp, oci = oracle.csr_from_mask(keep != 0)
     out, lse = P.gpu_forward(wl, qd, kd, vd, orp, oci)
     err, lerr = P.compare_rows(wl, out, lse, q, k, v, orp, oci, np.arange(wl.blocks))
@@ -609,3 +651,38 @@ def test_radial_csr_matches_oracle(grid, tile, heads, r0, gamma, lam):
     nnz = int(orp[-1])
     assert np.array_equal(rp.cpu().numpy(), orp.astype(np.int32))
     assert np.array_equal(ci[:nnz].cpu().numpy(), oci)
+
+
+def test_lookback_give_up_is_reported(monkeypatch):
+    """With the look-back's wait cut to zero polls, a row group that finds an earlier
+    group's total still unpublished gives up at once.  Either no group had to wait (the
+    check says OK and the block list equals the normal one) or the check reports the
+    fault and row_ptr holds -1 entries: the list is never silently wrong.  Every access
+    stays in bounds either way (a group that gives up writes no columns, and missing
+    totals only make later offsets smaller).  A normal selection on the same workspace
+    then clears the fault."""
+    wl = WORKLOADS["wan13b_480p"].with_(heads=4)
+    q, k, _, thr = make_inputs(wl, "A")
+    qd, kd = P.to_device(q, k)
+    shape = P.shape_for(wl)
+    ref_rp, ref_ci = P.gpu_select(wl, qd, kd, thr)
+    bufs = B.alloc_buffers(shape)
+    faults = 0
+    monkeypatch.setenv("SPARSE_ATTN_LOOKBACK_SPIN_CAP", "0")
+    for _ in range(3):
+        B.sparse_attn_select(shape, qd, kd, threshold=wl.threshold, buffers=bufs)
+        st = B.sparse_attn_select_check(shape, bufs.workspace)
+        rp = bufs.row_ptr.cpu().numpy().astype(np.int64)
+        if st == B.SPARSE_ATTN_OK:
+            assert np.array_equal(rp, ref_rp)
+            assert np.array_equal(bufs.col_idx[:int(rp[-1])].cpu().numpy(), ref_ci)
+        else:
+            assert st == B.SPARSE_ATTN_LOOKBACK_FAULT
+            assert (rp == -1).any()
+            faults += 1
+    print(f"give-ups reported in {faults} of 3 selections", flush=True)
+    monkeypatch.delenv("SPARSE_ATTN_LOOKBACK_SPIN_CAP")
+    B.sparse_attn_select(shape, qd, kd, threshold=wl.threshold, buffers=bufs)
+    assert B.sparse_attn_select_check(shape, bufs.workspace) == B.SPARSE_ATTN_OK
+    rp = bufs.row_ptr.cpu().numpy().astype(np.int64)
+    assert np.array_equal(rp, ref_rp)

@@ -733,3 +733,47 @@ def test_cdf_keep_against_pairwise_brute_force():
         for r in range(p.shape[0]):
             assert np.array_equal(keep[r], brute.cdf_keep_pairwise(p[r], thr).astype(bool))
     assert ibcs.cdf_keep(p, 1.0).all()
+
+
+def _kmeans_chain_golden():
+    chain, rounds = None, {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", "kmeans_chain.txt")) as f:
+        for line in f:
+            tok = line.split()
+            if not tok or tok[0].startswith("#"):
+                continue
+            if tok[0] == "chain":
+                chain = [float(v) for v in tok[1:]]
+            elif tok[0] == "rounds":
+                r, a, b, c, d, n0, n1 = (int(v) for v in tok[1:])
+                rounds[r] = (a / b, c / d, n0, n1)
+    x = np.zeros((128, 3))
+    x[:32, 0] = chain
+    for g in range(2, 8):
+        x[16 * g:16 * g + 16, 0] = 1024.0 * g
+    return x, rounds
+
+
+def test_kmeans_round_count_against_hand_derived_chain():
+    """The k-means runs exactly ITERS = 4 rounds: on a chain that moves in every one of
+    its first nine rounds, the oracle's centroids and weights equal the hand-derived
+    values after round 4 (tests/golden/kmeans_chain.txt), and running 1, 2, 3 or 5
+    rounds gives the hand-derived values of those rounds, which all differ from
+    round 4's.  The tie of the first round (three points at the midpoint) goes to
+    the lower cluster."""
+    from oracle import ibcs
+    x, rounds = _kmeans_chain_golden()
+    assert ibcs.ITERS == 4
+    for r, (m0, m1, n0, n1) in rounds.items():
+        mu, w, gap = ibcs.kmeans(x, iters=r)
+        assert abs(mu[0, 0] - m0) <= 1e-12 and abs(mu[1, 0] - m1) <= 1e-12, r
+        assert np.all(mu[:, 1:] == 0.0)
+        assert np.array_equal(mu[2:, 0], 1024.0 * np.arange(2, 8))
+        assert w[0] * 128 == n0 and w[1] * 128 == n1 and np.all(w[2:] * 128 == 16)
+        if r != 4:
+            assert (m0, m1) != rounds[4][:2]
+    mu, w, gap = ibcs.kmeans(x)
+    m0, m1, n0, n1 = rounds[4]
+    assert abs(mu[0, 0] - m0) <= 1e-12 and abs(mu[1, 0] - m1) <= 1e-12
+    assert w[0] * 128 == n0 and w[1] * 128 == n1
+    assert gap == 0.0                                  # the first round's tie
