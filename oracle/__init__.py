@@ -50,9 +50,9 @@ def _load():
         P = ctypes.c_void_p
         I = ctypes.c_int64
         D = ctypes.c_double
-        lib.oracle_pool.argtypes = [P, I, I, I, P]
+        lib.oracle_pool.argtypes = [P, I, I, I, P, I, P]
         lib.oracle_select_rows.argtypes = [P, P, I, I, I, P, I, D, P, I, I, I, I, I, I, P, P, P]
-        lib.oracle_attention_rows.argtypes = [P, P, P, I, I, I, P, P, P, P, I, D, P, P, P]
+        lib.oracle_attention_rows.argtypes = [P, P, P, I, I, I, P, P, P, P, P, I, D, P, P, P]
         lib.oracle_attention_backward.argtypes = [P, P, P, P, P, I, I, I, I, P, P, D, P, P, P]
         for f in (lib.oracle_pool, lib.oracle_select_rows, lib.oracle_attention_rows, lib.oracle_attention_backward):
             f.restype = None
@@ -76,16 +76,29 @@ def default_scale(head_dim: int) -> float:
     return 1.0 / float(np.sqrt(head_dim))
 
 
-def pool(x, tpb: int = TOKENS_PER_BLOCK) -> np.ndarray:
-    """Block means: x [..., N, d] -> [..., N/tpb, d] in fp64."""
+def pool(x, tpb: int = TOKENS_PER_BLOCK, valid: Optional[np.ndarray] = None) -> np.ndarray:
+    """Block means: x [..., N, d] -> [..., N/tpb, d] in fp64.  `valid` ([N] bool, the
+    same for every head): only those tokens are averaged (padding of partial tiles)."""
     x = _f32(x)
     *lead, n, d = x.shape
     if n % tpb:
         raise ValueError("token count must be a whole number of blocks")
     nblk = int(np.prod(lead, dtype=np.int64)) * (n // tpb)
+    vb = _valid(valid, n)
     out = np.empty((nblk, d), dtype=np.float64)
-    _load().oracle_pool(_ptr(x), nblk, tpb, d, _ptr(out))
+    _load().oracle_pool(_ptr(x), nblk, tpb, d, _ptr(vb), n // tpb, _ptr(out))
     return out.reshape(*lead, n // tpb, d)
+
+
+def _valid(valid, n):
+    if valid is None:
+        return None
+    vb = np.ascontiguousarray(np.asarray(valid, dtype=bool), dtype=np.uint8)
+    if vb.shape != (n,):
+        raise ValueError(f"valid must have one entry per token slot ({n})")
+    if not vb.reshape(-1, TOKENS_PER_BLOCK).any(axis=1).all():
+        raise ValueError("every block needs at least one valid token")
+    return vb
 
 
 def select_rows(qbar: np.ndarray, kbar: np.ndarray, heads: int, block_grid: Sequence[int],
@@ -147,37 +160,60 @@ def attention_backward(q, k, v, dout, row_ptr, col_idx, scale: Optional[float] =
     return dq, dk, dv
 
 
+def block_grid(grid: Sequence[int], tile: Sequence[int]):
+    """Tiles along t, y, x: ceil(grid / tile) (a last partial tile counts as a tile)."""
+    return tuple(-(-int(g) // int(s)) for g, s in zip(grid, tile))
+
+
 def tile_order(grid: Sequence[int], tile: Sequence[int]) -> np.ndarray:
-    """perm[i] = raster index of the token at tile-major position i.
+    """perm[i] = raster index of the token at tile-major position i, or -1 for padding.
 
     NABLA summary page, section "Methodologie : NABLA", item "Fractal Flattening":
-    the tokens of each spatial patch are made contiguous.  Raster token (t, y, x) sits
-    at (t * H + y) * W + x; tile-major position i belongs to block b = i // V
-    (V = tile volume), b = (bt * nTy + by) * nTx + bx, and is the (i mod V)-th token of
-    that tile in row-major order.
+    the tokens of each spatial patch are made contiguous, whatever the global size of
+    the video.  Raster token (t, y, x) sits at (t * H + y) * W + x; tile-major position
+    i belongs to block b = i // V (V = tile volume), b = (bt * nTy + by) * nTx + bx over
+    the ceil(grid / tile) tiles, and is the (i mod V)-th slot of that tile in row-major
+    order.  A slot whose coordinates fall beyond the grid (a partial tile at the far
+    edge of t, y or x) is padding.
     """
     T, H, W = (int(g) for g in grid)
     tt, th, tw = (int(s) for s in tile)
     vol = tt * th * tw
-    nTy, nTx = H // th, W // tw
-    i = np.arange(T * H * W, dtype=np.int64)
+    nT, nTy, nTx = block_grid(grid, tile)
+    i = np.arange(nT * nTy * nTx * vol, dtype=np.int64)
     b, u = i // vol, i % vol
     bt, by, bx = b // (nTy * nTx), (b // nTx) % nTy, b % nTx
     ut, uy, ux = u // (th * tw), (u // tw) % th, u % tw
-    return ((bt * tt + ut) * H + (by * th + uy)) * W + (bx * tw + ux)
+    t, y, x = bt * tt + ut, by * th + uy, bx * tw + ux
+    ok = (t < T) & (y < H) & (x < W)
+    return np.where(ok, (t * H + y) * W + x, -1)
+
+
+def token_valid(grid: Sequence[int], tile: Sequence[int]) -> np.ndarray:
+    """[nB * V] bool: which tile-major slots hold a token of the grid (not padding)."""
+    return tile_order(grid, tile) >= 0
 
 
 def to_tiles(x, grid, tile) -> np.ndarray:
-    """Raster-ordered [..., N, d] -> tile-major (same dtype, exact)."""
+    """Raster-ordered [..., N, d] -> tile-major [..., nB * V, d] (same dtype, exact; padding
+    slots are zero)."""
     a = x.numpy() if hasattr(x, "numpy") else np.asarray(x)
-    return a[..., tile_order(grid, tile), :]
+    perm = tile_order(grid, tile)
+    out = np.zeros(a.shape[:-2] + (len(perm), a.shape[-1]), dtype=a.dtype)
+    ok = perm >= 0
+    out[..., ok, :] = a[..., perm[ok], :]
+    return out
 
 
 def from_tiles(x, grid, tile) -> np.ndarray:
-    """Tile-major [..., N, d] -> raster order (the inverse of to_tiles)."""
+    """Tile-major [..., nB * V, d] -> raster order [..., N, d] (the inverse of to_tiles;
+    padding slots are dropped)."""
     a = x.numpy() if hasattr(x, "numpy") else np.asarray(x)
-    out = np.empty_like(a)
-    out[..., tile_order(grid, tile), :] = a
+    perm = tile_order(grid, tile)
+    T, H, W = (int(g) for g in grid)
+    out = np.empty(a.shape[:-2] + (T * H * W, a.shape[-1]), dtype=a.dtype)
+    ok = perm >= 0
+    out[..., perm[ok], :] = a[..., ok, :]
     return out
 
 
@@ -191,10 +227,11 @@ def csr_from_mask(mask: np.ndarray):
     return row_ptr, col_idx
 
 
-def select(q, k, heads: int, block_grid, thresholds, window=(-1, -1, -1), scale=None):
-    """Full selection for every row: returns (mask bool [B*H*nB, nB], row_ptr, col_idx)."""
-    qbar = pool(q)
-    kbar = pool(k)
+def select(q, k, heads: int, block_grid, thresholds, window=(-1, -1, -1), scale=None, valid=None):
+    """Full selection for every row: returns (mask bool [B*H*nB, nB], row_ptr, col_idx).
+    `valid`: the token slots that are not padding (partial tiles), as in pool()."""
+    qbar = pool(q, valid=valid)
+    kbar = pool(k, valid=valid)
     keep = select_rows(qbar, kbar, heads, block_grid, thresholds, window, scale)
     mask = keep != 0
     row_ptr, col_idx = csr_from_mask(mask)
@@ -202,13 +239,15 @@ def select(q, k, heads: int, block_grid, thresholds, window=(-1, -1, -1), scale=
 
 
 def attention_rows(q, k, v, row_ptr, col_idx, rows, scale: Optional[float] = None,
-                   tpb: int = TOKENS_PER_BLOCK, weights: bool = False, bias=None):
+                   tpb: int = TOKENS_PER_BLOCK, weights: bool = False, bias=None, valid=None):
     """Exact attention of every token of the listed query-block rows over its kept tiles.
 
     q, k, v: [B, H, N, d]; row_ptr/col_idx: CSR over rows r = bh * nB + i.
     Returns out [nrows, tpb, d] fp64 and lse [nrows, tpb] (natural log), plus
     the per-token weight sums with ``weights``.  ``bias``: optional logit offset per
-    col_idx entry, added to the scaled logits of all keys of that block.
+    col_idx entry, added to the scaled logits of all keys of that block.  ``valid``:
+    [N] bool, the token slots that are not padding (partial tiles); padding keys get no
+    weight and padding queries O = 0, LSE = -inf.
     """
     q, k, v = _f32(q), _f32(k), _f32(v)
     *lead, n, d = q.shape
@@ -223,7 +262,8 @@ def attention_rows(q, k, v, row_ptr, col_idx, rows, scale: Optional[float] = Non
     lse = np.empty((len(rows), tpb), dtype=np.float64)
     ws = np.empty((len(rows), tpb), dtype=np.float64) if weights else None
     sc = default_scale(d) if scale is None else float(scale)
-    _load().oracle_attention_rows(_ptr(q), _ptr(k), _ptr(v), nB, tpb, d, _ptr(rp), _ptr(ci), _ptr(b),
+    vb = _valid(valid, n)
+    _load().oracle_attention_rows(_ptr(q), _ptr(k), _ptr(v), nB, tpb, d, _ptr(rp), _ptr(ci), _ptr(b), _ptr(vb),
                                   _ptr(rows), len(rows), sc, _ptr(out), _ptr(lse), _ptr(ws))
     if weights:
         return out, lse, ws

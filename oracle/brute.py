@@ -11,6 +11,9 @@ Each one reaches the same result by a different route than the oracle:
   mask is expanded to a token-level N x N mask, disallowed logits are set to
   -inf and an ordinary dense softmax runs over the whole key axis.
 * ``dense_attention``: textbook softmax attention, used for thr >= 1.
+* ``raster_block_mask_attention``: the same literal expansion on a raster-ordered
+  grid that need not be a whole number of tiles: every token's block is found
+  from its own (t, y, x) coordinates, with no tile-major reordering or padding.
 * ``window_count``: the number of blocks in a clipped box window, as a product
   of per-axis interval lengths.
 """
@@ -73,3 +76,29 @@ def window_count(i: int, block_grid, window) -> int:
     for c, r, size in ((t, window[0], nT), (y, window[1], nTy), (x, window[2], nTx)):
         n *= min(size - 1, c + r) - max(0, c - r) + 1
     return n
+
+
+def raster_block_of(grid, tile) -> np.ndarray:
+    """Block index of every raster token (t, y, x): (t // tt, y // th, x // tw) over the
+    ceil(grid / tile) blocks."""
+    T, H, W = grid
+    tt, th, tw = tile
+    nTy, nTx = -(-H // th), -(-W // tw)
+    t, y, x = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    return (((t // tt) * nTy + (y // th)) * nTx + (x // tw)).reshape(-1)
+
+
+def raster_block_mask_attention(q, k, v, grid, tile, block_mask: np.ndarray, scale: float):
+    """Masked dense attention of raster-ordered tokens [N, d] (one head): token n may
+    attend to token m iff block_mask[block(n), block(m)], blocks taken from the tokens'
+    grid coordinates (fp64).  Returns out [N, d] and lse [N]."""
+    blk = raster_block_of(grid, tile)
+    allowed = np.asarray(block_mask, dtype=bool)[blk[:, None], blk[None, :]]
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    s = np.where(allowed, (q @ k.T) * scale, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=1, keepdims=True)
+    return (e / z) @ v, (m + np.log(z))[:, 0]

@@ -39,16 +39,25 @@
 #include <stdlib.h>
 #include <string.h>
 
-/* Sous-echantillonnage: xbar[b][c] = (1/tpb) * sum over the tpb tokens of block b of x[token][c]. */
-void oracle_pool(const float *x, int64_t nblocks, int64_t tpb, int64_t d, double *xbar)
+/*
+ * Sous-echantillonnage: xbar[b][c] = mean over the tokens of block b of x[token][c].
+ * valid (optional, [nB * tpb], the same for every head): the tokens of a partial
+ * tile that lie beyond the grid are padding; only the valid ones are averaged.  With
+ * valid == NULL every token counts (mean over tpb).
+ */
+void oracle_pool(const float *x, int64_t nblocks, int64_t tpb, int64_t d, const uint8_t *valid, int64_t nB,
+                 double *xbar)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t b = 0; b < nblocks; ++b) {
+        const uint8_t *vb = valid ? valid + (b % nB) * tpb : NULL;
+        int64_t n = 0;
+        for (int64_t t = 0; t < tpb; ++t) n += vb ? (vb[t] != 0) : 1;
         for (int64_t c = 0; c < d; ++c) {
             double s = 0.0;
             for (int64_t t = 0; t < tpb; ++t)
-                s += (double)x[(b * tpb + t) * d + c];
-            xbar[b * d + c] = s / (double)tpb;
+                if (!vb || vb[t]) s += (double)x[(b * tpb + t) * d + c];
+            xbar[b * d + c] = s / (double)n;
         }
     }
 }
@@ -155,11 +164,13 @@ void oracle_select_rows(const double *qbar, const double *kbar, int64_t H, int64
  * key of that entry's block: the logit offset by which AB-Attention's sampling
  * ("SIP", section "Les trois techniques d'AB-Attention" of the AB-Attention
  * page) weighs a kept block by the inverse of its inclusion probability.
+ * valid (optional, [nB * tpb], the same for every head): padding tokens of partial
+ * tiles take no part as keys, and a padding query token gets O = 0, LSE = -inf.
  */
 void oracle_attention_rows(const float *q, const float *k, const float *v, int64_t nB, int64_t tpb,
                            int64_t d, const int64_t *row_ptr, const int32_t *col_idx,
-                           const double *col_bias, const int64_t *rows, int64_t nrows, double scale,
-                           double *out, double *lse, double *w_sum)
+                           const double *col_bias, const uint8_t *valid, const int64_t *rows, int64_t nrows,
+                           double scale, double *out, double *lse, double *w_sum)
 {
     const int64_t N = nB * tpb;
 #pragma omp parallel
@@ -175,7 +186,7 @@ void oracle_attention_rows(const float *q, const float *k, const float *v, int64
                 const int64_t beg = row_ptr[r], end = row_ptr[r + 1];
                 double *o = out + (kr * tpb + t) * d;
                 const int64_t m_count = (end - beg) * tpb;
-                if (m_count == 0) {
+                if (m_count == 0 || (valid && !valid[i * tpb + t])) {
                     for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
                     lse[kr * tpb + t] = -INFINITY;
                     if (w_sum) w_sum[kr * tpb + t] = 0.0;
@@ -186,6 +197,10 @@ void oracle_attention_rows(const float *q, const float *k, const float *v, int64
                 for (int64_t e = beg; e < end; ++e) {
                     const int64_t j = col_idx[e];
                     for (int64_t u = 0; u < tpb; ++u, ++m) {
+                        if (valid && !valid[j * tpb + u]) {        /* padding key: no weight */
+                            logit[m] = -INFINITY;
+                            continue;
+                        }
                         const float *km = k + (bh * N + j * tpb + u) * d;
                         double a = 0.0;
                         for (int64_t c = 0; c < d; ++c) a += (double)qn[c] * (double)km[c];

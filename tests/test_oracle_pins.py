@@ -777,3 +777,85 @@ def test_kmeans_round_count_against_hand_derived_chain():
     assert abs(mu[0, 0] - m0) <= 1e-12 and abs(mu[1, 0] - m1) <= 1e-12
     assert w[0] * 128 == n0 and w[1] * 128 == n1
     assert gap == 0.0                                  # the first round's tie
+
+
+
+# ---------------------------------------------------------------- partial tiles
+# Grids that are not a whole number of tiles (NABLA summary page, "Fractal Flattening":
+# patches are grouped whatever the global size of the video): the last tile along y or
+# x holds fewer tokens, and its remaining slots in the tile-major layout are padding.
+
+PARTIAL = [((2, 12, 20), (1, 8, 8)), ((3, 9, 17), (1, 8, 8)), ((5, 8, 8), (4, 4, 4)), ((2, 13, 11), (1, 8, 8))]
+
+
+@pytest.mark.parametrize("grid,tile", PARTIAL)
+def test_partial_tile_order_counts(grid, tile):
+    """Every raster token appears exactly once; a tile holds prod(min(tile, rest of the
+    grid)) tokens along each axis (closed form), the rest of its slots are padding."""
+    perm = oracle.tile_order(grid, tile)
+    nT, nTy, nTx = oracle.block_grid(grid, tile)
+    assert len(perm) == nT * nTy * nTx * 64
+    assert np.array_equal(np.sort(perm[perm >= 0]), np.arange(np.prod(grid)))
+    valid = oracle.token_valid(grid, tile).reshape(-1, 64)
+    for b in range(nT * nTy * nTx):
+        bt, by, bx = b // (nTy * nTx), (b // nTx) % nTy, b % nTx
+        n = (min(tile[0], grid[0] - bt * tile[0]) * min(tile[1], grid[1] - by * tile[1])
+             * min(tile[2], grid[2] - bx * tile[2]))
+        assert valid[b].sum() == n
+
+
+@pytest.mark.parametrize("grid,tile", PARTIAL)
+def test_partial_tiles_round_trip_and_pool(grid, tile):
+    """to_tiles / from_tiles invert each other and pad with zeros; the pooled mean of a
+    partial tile is the mean of the grid tokens inside it, taken here by slicing the
+    raster grid directly (no tile-major order involved)."""
+    T, H, W = grid
+    x = _rand((2, T * H * W, 8), 61)
+    xt = oracle.to_tiles(x, grid, tile)
+    valid = oracle.token_valid(grid, tile)
+    assert np.all(xt[:, ~valid] == 0)
+    assert np.array_equal(oracle.from_tiles(xt, grid, tile), x)
+    pooled = oracle.pool(xt, valid=valid)
+    nT, nTy, nTx = oracle.block_grid(grid, tile)
+    xr = x.astype(np.float64).reshape(2, T, H, W, 8)
+    for b in range(nT * nTy * nTx):
+        bt, by, bx = b // (nTy * nTx), (b // nTx) % nTy, b % nTx
+        sl = xr[:, bt * tile[0]:(bt + 1) * tile[0], by * tile[1]:(by + 1) * tile[1], bx * tile[2]:(bx + 1) * tile[2]]
+        assert np.allclose(pooled[:, b], sl.reshape(2, -1, 8).mean(axis=1), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("grid,tile", PARTIAL[:3])
+def test_partial_tile_walk_matches_raster_bruteforce(grid, tile):
+    """The tile walk over the padded tile-major layout, with padding keys left out and
+    padding queries zero, equals masked dense attention on the raster grid whose mask
+    comes from each token's own block coordinates."""
+    T, H, W = grid
+    n, d = T * H * W, 16
+    q, k, v = (_rand((1, 1, n, d), s) for s in (62, 63, 64))
+    qt, kt, vt = (oracle.to_tiles(a, grid, tile) for a in (q, k, v))
+    # padding slots hold junk: it must not matter
+    valid = oracle.token_valid(grid, tile)
+    for a in (qt, kt, vt):
+        a[..., ~valid, :] = 7.0
+    nB = int(np.prod(oracle.block_grid(grid, tile)))
+    mask = np.random.default_rng(65).random((nB, nB)) < 0.6
+    mask[np.arange(nB), np.arange(nB)] = True
+    rp, ci = oracle.csr_from_mask(mask)
+    sc = 1.0 / math.sqrt(d)
+    out, lse = oracle.attention_rows(qt, kt, vt, rp, ci, np.arange(nB), scale=sc, valid=valid)
+    ref, ref_lse = brute.raster_block_mask_attention(q[0, 0], k[0, 0], v[0, 0], grid, tile, mask, sc)
+    perm = oracle.tile_order(grid, tile)
+    got = out.reshape(-1, d)
+    got_l = lse.reshape(-1)
+    assert np.allclose(got[valid], ref[perm[valid]], rtol=0, atol=1e-12)
+    assert np.allclose(got_l[valid], ref_lse[perm[valid]], rtol=0, atol=1e-12)
+    assert np.all(got[~valid] == 0) and np.all(np.isneginf(got_l[~valid]))
+
+
+def test_whole_tiles_need_no_padding():
+    """A grid of whole tiles has no padding slot and the same order as before."""
+    grid, tile = (2, 16, 24), (1, 8, 8)
+    perm = oracle.tile_order(grid, tile)
+    assert (perm >= 0).all() and len(perm) == 2 * 16 * 24
+    x = _rand((1, len(perm), 4), 66)
+    assert np.array_equal(oracle.pool(x), oracle.pool(x, valid=oracle.token_valid(grid, tile)))
