@@ -337,6 +337,7 @@ def main():
     if wl.dtype == "bf16" and not args.no_backward:
         rp, ci = select()
         forward(rp, ci)
+        ci = ci[:nnz]                      # the backward's transposed list holds one entry per listed one
         gen = torch.Generator(device=dev).manual_seed(5)
         dout = torch.randn(qd.shape, generator=gen, device=dev).to(qd.dtype)
         grads = tuple(torch.empty_like(qd) for _ in range(3))

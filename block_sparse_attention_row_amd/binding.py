@@ -183,11 +183,21 @@ def _check(status: int, where: str):
 # layout would make the kernels read or write outside it.  These checks run before
 # every call that takes tensors and raise ValueError without touching the device.
 
+def _block_grid(shape: Shape):
+    ceil = lambda g, t: -(-g // max(t, 1))
+    return ceil(shape.grid_t, shape.tile_t), ceil(shape.grid_h, shape.tile_h), ceil(shape.grid_w, shape.tile_w)
+
+
 def _dims(shape: Shape):
-    n = shape.grid_t * shape.grid_h * shape.grid_w
-    vol = max(shape.tile_t * shape.tile_h * shape.tile_w, 1)
-    nb = n // vol
-    return n, nb, shape.batch * shape.heads * nb
+    """(tile-major token slots per head, blocks per head, rows): a grid that is not a
+    whole number of tiles ends in partial tiles, whose padding slots count as slots."""
+    nt, ny, nx = _block_grid(shape)
+    nb = nt * ny * nx
+    return nb * 64, nb, shape.batch * shape.heads * nb
+
+
+def _raster_tokens(shape: Shape):
+    return shape.grid_t * shape.grid_h * shape.grid_w
 
 
 def _elem_dtype(shape: Shape):
@@ -216,20 +226,34 @@ def _req(t, name: str, dtype, numel: Optional[int] = None, min_numel: Optional[i
         raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
 
 
-def _req_tokens(shape: Shape, **tensors):
-    """[B, H, N, d] operands in the shape's dtype, all on the first one's device."""
+def _req_tokens(shape: Shape, raster=(), **tensors):
+    """[B, H, N, d] operands in the shape's dtype, all on the first one's device: N is
+    the tile-major slot count, or the raster token count for the names in `raster`."""
     n, _, _ = _dims(shape)
     want = shape.batch * shape.heads * n * shape.head_dim
+    want_r = shape.batch * shape.heads * _raster_tokens(shape) * shape.head_dim
     dt = _elem_dtype(shape)
     for name, t in tensors.items():           # form first, then the devices
         if t is not None:
-            _req(t, name, dt, numel=want, check_device=False)
+            _req(t, name, dt, numel=want_r if name in raster else want, check_device=False)
     dev = None
     for name, t in tensors.items():
         if t is not None:
-            _req(t, name, dt, numel=want, device=dev)
+            _req(t, name, dt, numel=want_r if name in raster else want, device=dev)
             dev = t.device
     return dev
+
+
+def _tiles_like(shape: Shape, src):
+    """A tile-major tensor for the raster tensor src (same leading dims and d)."""
+    import torch
+    n, _, _ = _dims(shape)
+    return torch.empty(*src.shape[:-2], n, src.shape[-1], dtype=src.dtype, device=src.device)
+
+
+def _raster_like(shape: Shape, src):
+    import torch
+    return torch.empty(*src.shape[:-2], _raster_tokens(shape), src.shape[-1], dtype=src.dtype, device=src.device)
 
 
 def _req_csr(shape: Shape, row_ptr, col_idx, device, capacity: bool = False):
@@ -272,8 +296,7 @@ def alloc_buffers(shape: Shape, device="cuda") -> Buffers:
     cap = sparse_attn_csr_capacity(shape)
     if ws < 0 or cap < 0:
         raise SparseAttnError(min(ws, cap), "shape")
-    nb = shape.grid_t * shape.grid_h * shape.grid_w // 64
-    rows = shape.batch * shape.heads * nb
+    _, nb, rows = _dims(shape)
     return Buffers(torch.empty(ws, dtype=torch.uint8, device=device),
                    torch.empty(rows + 1, dtype=torch.int32, device=device),
                    torch.empty(cap, dtype=torch.int32, device=device))
@@ -303,12 +326,11 @@ def sparse_attn_select_raster(shape: Shape, q, k, q_tiles=None, k_tiles=None, th
                               buffers: Optional[Buffers] = None, stream=None):
     """The selection on raster-ordered q, k, with the tile-major copies written on the way;
     returns (row_ptr, col_idx, q_tiles, k_tiles)."""
-    import torch
-    dev = _req_tokens(shape, q=q, k=k)
+    dev = _req_tokens(shape, raster=("q", "k"), q=q, k=k)
     bufs = buffers or alloc_buffers(shape, q.device)
-    q_tiles = torch.empty_like(q) if q_tiles is None else q_tiles
-    k_tiles = torch.empty_like(k) if k_tiles is None else k_tiles
-    _req_tokens(shape, q=q, k=k, q_tiles=q_tiles, k_tiles=k_tiles)
+    q_tiles = _tiles_like(shape, q) if q_tiles is None else q_tiles
+    k_tiles = _tiles_like(shape, k) if k_tiles is None else k_tiles
+    _req_tokens(shape, raster=("q", "k"), q=q, k=k, q_tiles=q_tiles, k_tiles=k_tiles)
     _req_buffers(shape, bufs, dev)
     ht = None
     if head_thresholds is not None:
@@ -471,20 +493,20 @@ def sparse_attn_full_csr(shape: Shape, buffers: Optional[Buffers] = None, device
 
 
 def sparse_attn_to_tiles(shape: Shape, src, dst=None, stream=None):
-    """Raster-ordered [B, H, N, d] -> tile-major (a new tensor unless dst is given)."""
-    import torch
-    dst = torch.empty_like(src) if dst is None else dst
-    _req_tokens(shape, src=src, dst=dst)
+    """Raster-ordered [B, H, T*H*W, d] -> tile-major [B, H, nB*64, d] (a new tensor unless
+    dst is given; padding slots of partial tiles are written as zeros)."""
+    dst = _tiles_like(shape, src) if dst is None else dst
+    _req_tokens(shape, raster=("src",), src=src, dst=dst)
     _check(lib().sparse_attn_to_tiles(ctypes.byref(shape), _ptr(src), _ptr(dst), _stream(stream)),
            "sparse_attn_to_tiles")
     return dst
 
 
 def sparse_attn_from_tiles(shape: Shape, src, dst=None, stream=None):
-    """Tile-major [B, H, N, d] -> raster order (a new tensor unless dst is given)."""
-    import torch
-    dst = torch.empty_like(src) if dst is None else dst
-    _req_tokens(shape, src=src, dst=dst)
+    """Tile-major [B, H, nB*64, d] -> raster order [B, H, T*H*W, d] (a new tensor unless
+    dst is given; padding slots are dropped)."""
+    dst = _raster_like(shape, src) if dst is None else dst
+    _req_tokens(shape, raster=("dst",), src=src, dst=dst)
     _check(lib().sparse_attn_from_tiles(ctypes.byref(shape), _ptr(src), _ptr(dst), _stream(stream)),
            "sparse_attn_from_tiles")
     return dst
@@ -498,3 +520,4 @@ def sparse_attn_select_check(shape: Shape, workspace, stream=None) -> int:
     _req(workspace, "workspace", torch.uint8)
     return int(lib().sparse_attn_select_check(ctypes.byref(shape), _ptr(workspace), workspace.numel(),
                                               _stream(stream)))
+

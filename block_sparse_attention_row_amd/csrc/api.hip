@@ -21,7 +21,9 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 struct Dims {
     int64_t B, H, D, N, nB, nBp, nW, rows;
+    int64_t Nr;                 // raster tokens per head, grid_t * grid_h * grid_w (<= N)
     int32_t nT, nTy, nTx;
+    bool partial;               // the grid ends in partial tiles along some axis
 };
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -35,22 +37,38 @@ int32_t check_shape(const sparse_attn_shape *s, Dims *d) {
     if (s->dtype != SPARSE_ATTN_F32 && s->dtype != SPARSE_ATTN_BF16) return SPARSE_ATTN_UNSUPPORTED;
     if (s->head_dim != 64 && s->head_dim != 128) return SPARSE_ATTN_UNSUPPORTED;
     if ((int64_t)s->tile_t * s->tile_h * s->tile_w != 64) return SPARSE_ATTN_UNSUPPORTED;
-    if (s->grid_t % s->tile_t || s->grid_h % s->tile_h || s->grid_w % s->tile_w) return SPARSE_ATTN_UNSUPPORTED;
     if (!isfinite(s->scale) || s->scale < 0.f) return SPARSE_ATTN_INVALID_ARGUMENT;
     d->B = s->batch;
     d->H = s->heads;
     d->D = s->head_dim;
-    d->nT = s->grid_t / s->tile_t;
-    d->nTy = s->grid_h / s->tile_h;
-    d->nTx = s->grid_w / s->tile_w;
-    d->N = (int64_t)s->grid_t * s->grid_h * s->grid_w;
+    // ceil(grid / tile) tiles; the last along an axis may be partial
+    d->nT = (s->grid_t + s->tile_t - 1) / s->tile_t;
+    d->nTy = (s->grid_h + s->tile_h - 1) / s->tile_h;
+    d->nTx = (s->grid_w + s->tile_w - 1) / s->tile_w;
+    d->partial = (s->grid_t % s->tile_t) || (s->grid_h % s->tile_h) || (s->grid_w % s->tile_w);
+    d->Nr = (int64_t)s->grid_t * s->grid_h * s->grid_w;
     d->nB = (int64_t)d->nT * d->nTy * d->nTx;
+    d->N = d->nB * 64;
     d->nBp = align_up(d->nB, 64);
     d->nW = d->nBp / 64;
     d->rows = d->B * d->H * d->nB;
     // row_ptr / col_idx are int32: the worst-case nnz must fit.
     if (d->rows > INT32_MAX / d->nB) return SPARSE_ATTN_UNSUPPORTED;
     return SPARSE_ATTN_OK;
+}
+
+SlotGeo slot_geo(const sparse_attn_shape *s, const Dims &d) {
+    SlotGeo g;
+    g.nTy = d.nTy;
+    g.nTx = d.nTx;
+    g.tt = s->tile_t;
+    g.th = s->tile_h;
+    g.tw = s->tile_w;
+    g.gt = s->grid_t;
+    g.gh = s->grid_h;
+    g.gw = s->grid_w;
+    g.partial = d.partial ? 1 : 0;
+    return g;
 }
 
 float effective_scale(const sparse_attn_shape *s) {
@@ -68,11 +86,13 @@ int64_t max_slots(const Dims &d) {
 
 struct Layout {
     int64_t thr, kbar, qbar, status, ticket;                             // selection
+    int64_t kbar64, qbar64, knorm;                                       // selection: exact means
     int64_t bits, counts, groups;                                        // external masks
     int64_t items, plan_counts, pair_flag, merge, part_o, part_lse;      // attention row splitting
     int64_t part_b;                                                      // backward: second partial rows
     int64_t col_ptr, lse2, dn;                                           // backward
     int64_t mix;                                                         // clustering selector rows
+    int64_t slot_mask;                                                   // partial tiles: token slots per block
     int64_t total;
 };
 
@@ -99,6 +119,12 @@ Layout layout(const Dims &d) {
     off = align_up(off + 8 * n_groups(d), kAlign);
     l.ticket = off;
     off = align_up(off + 16, kAlign);
+    l.kbar64 = off;
+    off = align_up(off + 8 * d.B * d.H * d.nB * d.D, kAlign);   // exact key means
+    l.knorm = off;
+    off = align_up(off + 4 * d.B * d.H * d.nB, kAlign);         // their norms
+    l.qbar64 = off;
+    off = align_up(off + 8 * d.B * d.H * d.nB * d.D, kAlign);   // exact query means (raster selection)
     l.bits = off;
     off = align_up(off + 8 * d.rows * d.nW, kAlign);
     l.counts = off;
@@ -128,6 +154,8 @@ Layout layout(const Dims &d) {
     off = align_up(off + 4 * d.rows * 64, kAlign);
     l.mix = off;
     off = align_up(off + 4 * ibcs_heads_per_launch(d) * ibcs_row_floats(d), kAlign);
+    l.slot_mask = off;
+    off = align_up(off + 8 * d.nB, kAlign);
     l.total = off;
     return l;
 }
@@ -209,32 +237,42 @@ static ReorderArgs reorder_args(const sparse_attn_shape *shape, const Dims &d, i
     a.tt = shape->tile_t;
     a.th = shape->tile_h;
     a.tw = shape->tile_w;
+    a.gt = shape->grid_t;
     a.gh = shape->grid_h;
     a.gw = shape->grid_w;
+    a.nr = d.Nr;
     a.row_log2 = 0;
     while ((16LL << a.row_log2) < rowb) ++a.row_log2;
     a.inverse = inverse;
     return a;
 }
 
-// The CDF selection.  q_tiles == k_tiles == null: q and k are tile-major and the
-// selection pools them.  Otherwise q and k are in raster order: they are copied to
-// q_tiles / k_tiles in tile-major order and their block means are formed by that copy.
-static int32_t select_impl(const sparse_attn_shape *shape, const sparse_attn_select_params *params, const void *q,
-                           const void *k, int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity,
-                           void *workspace, int64_t workspace_bytes, void *stream, void *q_tiles, void *k_tiles) {
-    Dims d;
+// Device memory the CDF selection works in: per-head thresholds, the key block means,
+// the query block means (raster inputs only), the look-back words and the ticket with
+// the fault word after it.
+struct SelectScratch {
+    float *thr;
+    __bf16 *kbar, *qbar;
+    double *kbar64, *qbar64;
+    float *knorm;
+    uint64_t *status;
+    uint32_t *ticket;
+};
+
+// Argument checks of the CDF selection that do not involve the workspace.
+static int32_t select_checks(const sparse_attn_shape *shape, const sparse_attn_select_params *params, const void *q,
+                             const void *k, int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity, void *q_tiles,
+                             void *k_tiles, Dims &d) {
     int32_t st = check_shape(shape, &d);
     if (st) return st;
-    if (!params || !q || !k || !row_ptr || !col_idx || !workspace) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (!params || !q || !k || !row_ptr || !col_idx) return SPARSE_ATTN_INVALID_ARGUMENT;
     const bool raster = q_tiles != nullptr || k_tiles != nullptr;
     if (raster) {
         if (!q_tiles || !k_tiles || q_tiles == k_tiles || q_tiles == q || q_tiles == k || k_tiles == q ||
             k_tiles == k || !aligned(q_tiles, 16) || !aligned(k_tiles, 16))
             return SPARSE_ATTN_INVALID_ARGUMENT;
     }
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(row_ptr, 4) || !aligned(col_idx, 4) ||
-        !aligned(workspace, 16))
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(row_ptr, 4) || !aligned(col_idx, 4))
         return SPARSE_ATTN_INVALID_ARGUMENT;
     if (d.nBp > kSelectMaxBlocks) return SPARSE_ATTN_UNSUPPORTED;   // a row is held in registers
     if (bad_thr(params->threshold)) return SPARSE_ATTN_INVALID_ARGUMENT;
@@ -242,15 +280,19 @@ static int32_t select_impl(const sparse_attn_shape *shape, const sparse_attn_sel
         for (int64_t h = 0; h < d.H; ++h)
             if (bad_thr(params->head_thresholds[h])) return SPARSE_ATTN_INVALID_ARGUMENT;
     if (col_capacity < d.rows * d.nB) return SPARSE_ATTN_CAPACITY;
-    const Layout L = layout(d);
-    if (workspace_bytes < L.total) return SPARSE_ATTN_WORKSPACE;
+    return SPARSE_ATTN_OK;
+}
 
+// The CDF selection's launches, once every argument has been checked.  q_tiles ==
+// k_tiles == null: q and k are tile-major and the selection pools them.  Otherwise q
+// and k are in raster order: they are copied to q_tiles / k_tiles in tile-major order
+// and their block means are formed by that copy.
+static int32_t select_launch(const sparse_attn_shape *shape, const sparse_attn_select_params *params, const Dims &d,
+                             const void *q, const void *k, int32_t *row_ptr, int32_t *col_idx,
+                             const SelectScratch &w, void *stream, void *q_tiles, void *k_tiles) {
+    const bool raster = q_tiles != nullptr;
     hipStream_t s = (hipStream_t)stream;
-    char *ws = (char *)workspace;
-    float *thr = (float *)(ws + L.thr);
-    __bf16 *kbar = (__bf16 *)(ws + L.kbar);
-    uint64_t *status = (uint64_t *)(ws + L.status);
-    uint32_t *ticket = (uint32_t *)(ws + L.ticket);
+    float *thr = w.thr;
 
     // thresholds: the first ThrChunk::kMax travel with the pooling kernel, any others
     // through small fill kernels
@@ -259,9 +301,9 @@ static int32_t select_impl(const sparse_attn_shape *shape, const sparse_attn_sel
     for (int i = 0; i < side.n_thr; ++i)
         side.thr.v[i] = params->head_thresholds ? params->head_thresholds[i] : params->threshold;
     side.thr_dst = thr;
-    side.status = status;
+    side.status = w.status;
     side.n_status = n_groups(d);
-    side.ticket = ticket;
+    side.ticket = w.ticket;
     for (int64_t h0 = ThrChunk::kMax; h0 < d.H; h0 += ThrChunk::kMax) {
         float tmp[ThrChunk::kMax];
         const int n = (int)((d.H - h0) < ThrChunk::kMax ? (d.H - h0) : ThrChunk::kMax);
@@ -269,33 +311,39 @@ static int32_t select_impl(const sparse_attn_shape *shape, const sparse_attn_sel
             tmp[i] = params->head_thresholds ? params->head_thresholds[h0 + i] : params->threshold;
         if (launch_fill_thresholds(tmp, n, thr + h0, s)) return SPARSE_ATTN_HIP_ERROR;
     }
-    __bf16 *qbar = nullptr;
     if (raster) {
-        qbar = (__bf16 *)(ws + L.qbar);
         ReorderPoolArgs rp;
         rp.a = reorder_args(shape, d, 0);
         rp.k_src = k;
         rp.q_src = q;
         rp.k_dst = k_tiles;
         rp.q_dst = q_tiles;
-        rp.kbar = kbar;
-        rp.qbar = qbar;
+        rp.kbar = w.kbar;
+        rp.qbar = w.qbar;
+        rp.kbar64 = w.kbar64;
+        rp.qbar64 = w.qbar64;
+        rp.knorm = w.knorm;
         rp.tiles = d.B * d.H * d.nB;
         rp.gph = (int32_t)groups_per_head(d);
         rp.side = side;
         if (launch_reorder_pool(rp, shape->dtype, (int)d.D, s)) return SPARSE_ATTN_HIP_ERROR;
-    } else if (launch_pool_keys(k, kbar, d.B * d.H * d.nB, d.nB, shape->dtype, (int)d.D, side, s)) {
+    } else if (launch_pool_keys(k, w.kbar, w.kbar64, w.knorm, d.B * d.H * d.nB, d.nB, shape->dtype, (int)d.D, side,
+                                slot_geo(shape, d), s)) {
         return SPARSE_ATTN_HIP_ERROR;
     }
 
     SelectArgs a = {};
     a.q = raster ? q_tiles : q;
-    a.qbar = qbar;
-    a.kbar = kbar;
+    a.qbar = raster ? w.qbar : nullptr;
+    a.qbar64 = raster ? w.qbar64 : nullptr;
+    a.kbar = w.kbar;
+    a.kbar64 = w.kbar64;
+    a.knorm = w.knorm;
+    a.geo = slot_geo(shape, d);
     a.thr = thr;
-    a.status = status;
-    a.ticket = ticket;
-    a.fault = ticket + 1;
+    a.status = w.status;
+    a.ticket = w.ticket;
+    a.fault = w.ticket + 1;
     a.spin_cap = lookback_spin_cap();
     a.row_ptr = row_ptr;
     a.col_idx = col_idx;
@@ -314,6 +362,28 @@ static int32_t select_impl(const sparse_attn_shape *shape, const sparse_attn_sel
     a.scale_log2 = effective_scale(shape) * kLog2e;
     if (launch_select(a, (int)d.D, shape->dtype, s)) return SPARSE_ATTN_HIP_ERROR;
     return SPARSE_ATTN_OK;
+}
+
+static int32_t select_impl(const sparse_attn_shape *shape, const sparse_attn_select_params *params, const void *q,
+                           const void *k, int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity,
+                           void *workspace, int64_t workspace_bytes, void *stream, void *q_tiles, void *k_tiles) {
+    Dims d;
+    int32_t st = select_checks(shape, params, q, k, row_ptr, col_idx, col_capacity, q_tiles, k_tiles, d);
+    if (st) return st;
+    if (!workspace || !aligned(workspace, 16)) return SPARSE_ATTN_INVALID_ARGUMENT;
+    const Layout L = layout(d);
+    if (workspace_bytes < L.total) return SPARSE_ATTN_WORKSPACE;
+    char *ws = (char *)workspace;
+    SelectScratch w;
+    w.thr = (float *)(ws + L.thr);
+    w.kbar = (__bf16 *)(ws + L.kbar);
+    w.qbar = (__bf16 *)(ws + L.qbar);
+    w.kbar64 = (double *)(ws + L.kbar64);
+    w.qbar64 = (double *)(ws + L.qbar64);
+    w.knorm = (float *)(ws + L.knorm);
+    w.status = (uint64_t *)(ws + L.status);
+    w.ticket = (uint32_t *)(ws + L.ticket);
+    return select_launch(shape, params, d, q, k, row_ptr, col_idx, w, stream, q_tiles, k_tiles);
 }
 
 int32_t sparse_attn_select(const sparse_attn_shape *shape, const sparse_attn_select_params *params, const void *q,
@@ -349,7 +419,7 @@ int32_t forward_impl(const sparse_attn_shape *shape, const void *q, const void *
     const Layout L = layout(d);
     if (workspace_bytes < L.total) return SPARSE_ATTN_WORKSPACE;
 
-    AttnArgs a;
+    AttnArgs a = {};
     a.q = q;
     a.k = k;
     a.v = v;
@@ -374,6 +444,11 @@ int32_t forward_impl(const sparse_attn_shape *shape, const void *q, const void *
     a.plan.part_lse = (float *)(ws + L.part_lse);
     a.plan.max_slots = (int32_t)max_slots(d);
     a.plan.long_slots = (int32_t)long_slots(d);
+    a.geo = slot_geo(shape, d);
+    if (d.partial && shape->dtype == SPARSE_ATTN_BF16) {
+        a.slot_mask_w = (uint64_t *)(ws + L.slot_mask);
+        a.slot_mask = a.slot_mask_w;
+    }
     if (launch_attention(a, shape->dtype, (int)d.D, (hipStream_t)stream)) return SPARSE_ATTN_HIP_ERROR;
     return SPARSE_ATTN_OK;
 }
@@ -428,7 +503,9 @@ int32_t sparse_attn_select_sip(const sparse_attn_shape *shape, const sparse_attn
     side.status = status;
     side.n_status = n_groups(d);
     side.ticket = ticket;
-    if (launch_pool_keys(k, kbar, d.B * d.H * d.nB, d.nB, shape->dtype, (int)d.D, side, s)) return SPARSE_ATTN_HIP_ERROR;
+    if (launch_pool_keys(k, kbar, (double *)(ws + L.kbar64), (float *)(ws + L.knorm), d.B * d.H * d.nB, d.nB,
+                         shape->dtype, (int)d.D, side, slot_geo(shape, d), s))
+        return SPARSE_ATTN_HIP_ERROR;
 
     SelectArgs a = {};
     a.q = q;
@@ -449,6 +526,7 @@ int32_t sparse_attn_select_sip(const sparse_attn_shape *shape, const sparse_attn
     a.nTy = d.nTy;
     a.nTx = d.nTx;
     a.window = 0;
+    a.geo = slot_geo(shape, d);
     a.scale_log2 = effective_scale(shape) * kLog2e;
     a.budget = params->budget;
     a.seed = params->seed;
@@ -464,6 +542,7 @@ int32_t sparse_attn_select_ibcs(const sparse_attn_shape *shape, const sparse_att
     int32_t st = check_shape(shape, &d);
     if (st) return st;
     if (shape->dtype != SPARSE_ATTN_BF16) return SPARSE_ATTN_UNSUPPORTED;
+    if (d.partial) return SPARSE_ATTN_UNSUPPORTED;   // the 128-token clusters take whole tiles
     if (!params || !q || !k || !row_ptr || !col_idx || !workspace) return SPARSE_ATTN_INVALID_ARGUMENT;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(row_ptr, 4) || !aligned(col_idx, 4) ||
         !aligned(workspace, 16))
@@ -499,7 +578,9 @@ int32_t sparse_attn_select_ibcs(const sparse_attn_shape *shape, const sparse_att
             tmp[i] = params->head_thresholds ? params->head_thresholds[h0 + i] : params->threshold;
         if (launch_fill_thresholds(tmp, n, thr + h0, s)) return SPARSE_ATTN_HIP_ERROR;
     }
-    if (launch_pool_keys(k, kbar, d.B * d.H * d.nB, d.nB, shape->dtype, (int)d.D, side, s)) return SPARSE_ATTN_HIP_ERROR;
+    if (launch_pool_keys(k, kbar, (double *)(ws + L.kbar64), (float *)(ws + L.knorm), d.B * d.H * d.nB, d.nB,
+                         shape->dtype, (int)d.D, side, slot_geo(shape, d), s))
+        return SPARSE_ATTN_HIP_ERROR;
 
     IbcsArgs m;
     m.q = (const __bf16 *)q;
@@ -608,6 +689,7 @@ int32_t sparse_attn_backward(const sparse_attn_shape *shape, const void *q, cons
     if (st) return st;
     if (shape->dtype != SPARSE_ATTN_BF16) return SPARSE_ATTN_UNSUPPORTED;
     if (d.nB > kSelectMaxBlocks) return SPARSE_ATTN_UNSUPPORTED;   // a row's bitmask is held in LDS
+    if (d.partial) return SPARSE_ATTN_UNSUPPORTED;                  // whole tiles only
     if (!q || !k || !v || !out || !lse || !dout || !row_ptr || !dq || !dk || !dv || !workspace)
         return SPARSE_ATTN_INVALID_ARGUMENT;
     if (col_count < 0 || (col_count > 0 && (!col_idx || !t_idx))) return SPARSE_ATTN_INVALID_ARGUMENT;

@@ -100,6 +100,20 @@ __device__ __forceinline__ float tile_commit(const f32x16 *acc_s, float c, float
     return lt;
 }
 
+// Scores of a key tile whose block is cut by the grid edge (a partial tile): its
+// padding slots get -inf, so they take no weight.  km: bit u set for the slots that
+// are grid tokens; accumulator v of half kt of this lane holds key 32 kt + 8 (v / 4) +
+// 4 hh + v % 4 (the 32x32 MFMA output layout, keys along its rows).
+__device__ __forceinline__ void mask_keys(f32x16 *sc, uint64_t km, int hh) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int key = 32 * kt + 8 * (v >> 2) + 4 * hh + (v & 3);
+            if (!((km >> key) & 1ull)) sc[kt][v] = -INFINITY;
+        }
+}
+
 // Scores of the next tile (MFMA) interleaved with the probabilities of the current
 // one (VALU): each score MFMA is grouped with an equal share of the softmax work, and the K reads run two MFMAs ahead.
 template <int D>
@@ -332,6 +346,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     float m_run = -INFINITY, l_run = 0.f;
     FragOffsets<D> fo;
     fo.init(lane);
+    // partial tiles: the per-block slot masks the plan wrote (null when every tile is whole)
+    auto mask_tile = [&](f32x16 *sc, int col) {
+        if (a.slot_mask != nullptr) {
+            const uint64_t km = a.slot_mask[__builtin_amdgcn_readfirstlane(col)];
+            if (km != ~0ull) mask_keys(sc, km, hh);
+        }
+    };
 
     // tiles j (scores pending), j+1 (K resident), j+2 (lookahead)
     int col0, col1, col2;
@@ -346,7 +367,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         if (col1 != kNone) issue_k(col1, 1);
         wait_vmcnt<0>();
         __syncthreads();
-        if (mine0) tile_scores<D>(Ks, qf, fo, sa);
+        if (mine0) {
+            tile_scores<D>(Ks, qf, fo, sa);
+            mask_tile(sa, col0);
+        }
     }
     // One pipeline step for tile j with j & 1 == BJ: the scores of tile j are in sc,
     // those of tile j+1 go to sn; buffer offsets are compile-time constants.
@@ -377,6 +401,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         } else if (mine0) {
             tile_probs(sc, c, mc, lacc, pf);
         }
+        if (mine1) mask_tile(sn, col1);
         if constexpr (!BIAS) {
             if (mine0) l_run += tile_commit<NDT>(sc, c, m_run, l_run, lt, acc_o, pf);
         }
@@ -400,9 +425,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     }
 
     if (!has_row) return;
-    // epilogue: normalise and store; lane owns query l32, d = 32 dt + 8 rr + 4 hh + {0..3}
+    // epilogue: normalise and store; lane owns query l32, d = 32 dt + 8 rr + 4 hh + {0..3}.
+    // A padding slot of a partial tile gets O = 0 and LSE = -inf.
     const float l_tot = pair_sum(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const bool qvalid =
+        a.slot_mask == nullptr || ((a.slot_mask[blk] >> (32 * (wave & 1) + l32)) & 1ull);
+    const float inv = (l_tot > 0.f && qvalid) ? 1.f / l_tot : 0.f;
     if (split) {
         // piece of a split pair: the normalised partial output and its log2-sum-exp
         const int q = 32 * (wave & 1) + l32;
@@ -412,10 +440,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) po[(32 * dt + 8 * rr + 4 * hh + e) * 64 + q] = acc_o[dt][4 * rr + e] * inv;
+                for (int e = 0; e < 4; ++e)
+                    po[(32 * dt + 8 * rr + 4 * hh + e) * 64 + q] = qvalid ? acc_o[dt][4 * rr + e] * inv : 0.f;
         if (hh == 0)
             a.plan.part_lse[((int64_t)it.slot * 2 + grp) * 64 + q] =
-                l_tot > 0.f ? (BIAS ? m_run : m_run * c) + __log2f(l_tot) : -INFINITY;
+                (l_tot > 0.f && qvalid) ? (BIAS ? m_run : m_run * c) + __log2f(l_tot) : -INFINITY;
         return;
     }
     const int64_t qrow = bh * N + (int64_t)blk * 64 + 32 * (wave & 1) + l32;
@@ -426,11 +455,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         for (int rr = 0; rr < 4; ++rr) {
             f32x4 w;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = acc_o[dt][4 * rr + e] * inv;
+            for (int e = 0; e < 4; ++e) w[e] = qvalid ? acc_o[dt][4 * rr + e] * inv : 0.f;
             *reinterpret_cast<bf16x4 *>(og + 32 * dt + 8 * rr + 4 * hh) = __builtin_convertvector(w, bf16x4);
         }
     if (a.lse && hh == 0)
-        a.lse[qrow] = l_tot > 0.f ? ((BIAS ? m_run : m_run * c) + __log2f(l_tot)) * kLn2 : -INFINITY;
+        a.lse[qrow] = (l_tot > 0.f && qvalid) ? ((BIAS ? m_run : m_run * c) + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -476,6 +505,14 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
     __shared__ int32_t scan[16];
     const SplitPlan &P = a.plan;
     const int t = threadIdx.x;
+    // which slots of each block are grid tokens, for grids that end in partial tiles
+    if (a.slot_mask != nullptr) {
+        for (int b = t; b < a.nB; b += 1024) {
+            uint64_t m = 0;
+            for (int u = 0; u < 64; ++u) m |= (uint64_t)slot_valid(a.geo, b, u) << u;
+            a.slot_mask_w[b] = m;
+        }
+    }
     auto est_of = [&](int64_t p) {
         int64_t bA, eA, bB, eB;
         pair_ranges(a, p, bA, eA, bB, eB);
@@ -685,10 +722,13 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
     // entries out of range, repeated or below the last accepted column are skipped,
     // exactly as in the bf16 walk
     int last = -1;
+    const bool partial = a.geo.partial != 0;
     for (int e = 0; e < ntile; ++e) {
         const int col = a.col_idx[beg + e];
         if (col <= last || col >= a.nB) continue;
         last = col;
+        // padding slots of a partial key tile take no weight
+        const uint64_t km = partial ? __ballot(slot_valid(a.geo, col, lane)) : ~0ull;
         __syncthreads();
         const float *kt = kg + (int64_t)col * 64 * D;
         const float *vt = vg + (int64_t)col * 64 * D;
@@ -712,6 +752,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
                 acc_s[kt2] = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[(32 * kt2 + l32) * KS + 2 * c + hh], qf[c],
                                                                   acc_s[kt2], 0, 0, 0);
         }
+        if (km != ~0ull) mask_keys(acc_s, km, hh);
         float mt = -INFINITY;
 #pragma unroll
         for (int kt2 = 0; kt2 < 2; ++kt2)
@@ -752,7 +793,8 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const bool qvalid = !partial || slot_valid(a.geo, (int32_t)(row % a.nB), 32 * wave + l32);
+    const float inv = (l_tot > 0.f && qvalid) ? 1.f / l_tot : 0.f;
     const int64_t qrow = bh * N + (row % a.nB) * 64 + 32 * wave + l32;
     float *og = (float *)a.out + qrow * D;
 #pragma unroll
@@ -761,10 +803,11 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
         for (int rr = 0; rr < 4; ++rr) {
             f32x4 w;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) w[s] = acc_o[dt][4 * rr + s] * inv;
+            for (int s = 0; s < 4; ++s) w[s] = qvalid ? acc_o[dt][4 * rr + s] * inv : 0.f;
             *reinterpret_cast<f32x4 *>(og + 32 * dt + 8 * rr + 4 * hh) = w;
         }
-    if (a.lse && hh == 0) a.lse[qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (a.lse && hh == 0)
+        a.lse[qrow] = (l_tot > 0.f && qvalid) ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 int launch_plan(const AttnArgs &a, hipStream_t s) {

@@ -6,6 +6,24 @@
 
 namespace sattn {
 
+// Geometry of the tile-major slots.  Blocks are the ceil(grid / tile) tiles of the
+// token grid, frame-block outermost; slot u of a block is (u / (th tw), (u / tw) % th,
+// u % tw) inside its tile, and it holds a grid token iff those coordinates fall inside
+// the grid.  Only the last tile along an axis can be partial; when no tile is
+// (`partial` == 0) every slot is a token.
+struct SlotGeo {
+    int32_t nTy, nTx;         // tiles along y and x
+    int32_t tt, th, tw;       // tile
+    int32_t gt, gh, gw;       // token grid
+    int32_t partial;          // some tile is cut by the grid edge
+};
+// Whether slot u of block b holds a grid token.
+__host__ __device__ inline bool slot_valid(const SlotGeo &g, int32_t b, int32_t u) {
+    const int32_t bt = b / (g.nTy * g.nTx), by = (b / g.nTx) % g.nTy, bx = b % g.nTx;
+    const int32_t ut = u / (g.th * g.tw), uy = (u / g.tw) % g.th, ux = u % g.tw;
+    return bt * g.tt + ut < g.gt && by * g.th + uy < g.gh && bx * g.tw + ux < g.gw;
+}
+
 struct ThrChunk {
     static constexpr int kMax = 256;
     float v[kMax];
@@ -49,11 +67,23 @@ constexpr uint32_t kSpinCap = 1u << 22;
 // Longest row the selection holds in registers (64 words of 64 key blocks).
 constexpr int kSelectMaxBlocks = 4096;
 
+// Exact rescoring of near-ties at the cut: the scores' error bound is
+// kScoreEps * scale * log2(e) * |qbar| * max_j |kbar_j| (split-bf16 products and fp32
+// accumulation: 3 * 2^-16 per product plus 384 * 2^-24 of accumulation, below 2^-13);
+// the blocks whose probability lies within that bound of the crossing value are
+// ordered again by their exact fp64 scores, when there are at most kRefineMax of them.
+constexpr float kScoreEps = 0x1p-13f;
+constexpr int kRefineMax = 64;
+
 struct SelectArgs {
     const void *q;            // [BH*N][D] queries in the input dtype (tile-major)
     const __bf16 *kbar;       // key block means as bf16 pairs, in fragment order (kbar_group)
+    const double *kbar64;     // [BH*nB][D] exact key block means
+    const float *knorm;       // [BH*nB] Euclidean norms of the key block means
+    SlotGeo geo;              // which slots of the query blocks are tokens
     const __bf16 *qbar;       // null: the selection pools Q itself; else [BH*nB][2][D] query
                               // block means as bf16 pairs (hi, then lo), formed by the reorder
+    const double *qbar64;     // with qbar: [BH*nB][D] exact query block means
     const float *thr;         // [H] thresholds (device)
     uint64_t *status;         // [n_groups] look-back words (zeroed by the pooling kernel)
     uint32_t *ticket;         // group ticket counter (zeroed by the pooling kernel)
@@ -151,13 +181,20 @@ struct AttnArgs {
     int32_t nB;
     int32_t pair_stride;      // S of pair_blocks: blocks per frame, or 1
     float scale_log2;         // softmax scale * log2(e)
+    SlotGeo geo;              // padding slots of partial tiles: no weight as keys, zero output as queries
+    // bf16 path with partial tiles: per-block masks of the slots that are grid tokens,
+    // written by the plan kernel (slot_mask_w) and read by the attention (slot_mask);
+    // null when every tile is whole
+    const uint64_t *slot_mask;
+    uint64_t *slot_mask_w;
     SplitPlan plan;           // bf16 path only
 };
 
 struct ReorderArgs {
     int32_t nB, nTy, nTx;          // blocks per head, block grid (t implied)
     int32_t tt, th, tw;            // tile
-    int32_t gh, gw;                // token grid height and width
+    int32_t gt, gh, gw;            // token grid
+    int64_t nr;                    // raster tokens per head, gt * gh * gw (<= 64 nB: partial tiles pad)
     int32_t row_log2;              // log2 of the 16-byte pieces per token row
     int32_t inverse;               // 0: raster -> tile-major, 1: tile-major -> raster
 };
@@ -170,14 +207,16 @@ struct ReorderPoolArgs {
     const void *k_src, *q_src;
     void *k_dst, *q_dst;
     __bf16 *kbar, *qbar;
+    double *kbar64, *qbar64;  // [BH*nB][D] exact means
+    float *knorm;             // [BH*nB] norms of the key means
     int64_t tiles;            // B * H * nB
     int32_t gph;
     PoolSide side;
 };
 int launch_reorder_pool(const ReorderPoolArgs &p, int dtype, int d, hipStream_t s);
 
-int launch_pool_keys(const void *k, __bf16 *kbar, int64_t nblocks, int32_t nB, int dtype, int d, const PoolSide &side,
-                     hipStream_t s);
+int launch_pool_keys(const void *k, __bf16 *kbar, double *kbar64, float *knorm, int64_t nblocks, int32_t nB, int dtype,
+                     int d, const PoolSide &side, const SlotGeo &geo, hipStream_t s);
 int launch_fill_thresholds(const float *host_thr, int n, float *dst, hipStream_t s);
 int launch_select(const SelectArgs &a, int d, int dtype, hipStream_t s);
 int launch_select_sip(const SelectArgs &a, int d, hipStream_t s);

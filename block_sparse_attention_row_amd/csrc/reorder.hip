@@ -28,11 +28,16 @@ __global__ __launch_bounds__(256) void reorder_kernel(const u32x4 *__restrict__ 
         const int c = 256 * i + threadIdx.x;
         const int u = c >> RL, off = c & ((1 << RL) - 1);
         const int ut = u / tyx, uy = (u / a.tw) % a.th, ux = u % a.tw;
-        const int64_t tok = ((int64_t)(bt * a.tt + ut) * a.gh + (by * a.th + uy)) * a.gw + (bx * a.tw + ux);
-        const int64_t r = ((bh * N + tok) << RL) + off;
+        const int t0 = bt * a.tt + ut, y0 = by * a.th + uy, x0 = bx * a.tw + ux;
+        const bool in = t0 < a.gt && y0 < a.gh && x0 < a.gw;       // else a partial tile's padding slot
+        const int64_t tok = ((int64_t)t0 * a.gh + y0) * a.gw + x0;
+        const int64_t r = ((bh * a.nr + tok) << RL) + off;
         const int64_t t = tile0 + c;
-        if (a.inverse) dst[r] = src[t];
-        else dst[t] = src[r];
+        if (a.inverse) {
+            if (in) dst[r] = src[t];
+        } else {
+            dst[t] = in ? src[r] : u32x4{0u, 0u, 0u, 0u};
+        }
     }
 }
 
@@ -50,7 +55,7 @@ __global__ __launch_bounds__(256) void reorder_pool_kernel(ReorderPoolArgs p) {
     constexpr int VEC = 16 / (int)sizeof(T), PR = D / VEC;   // elements per piece, pieces per token row
     constexpr int PER = 64 * PR, IT = PER / 256, SHARE = 256 / PR;
     static_assert(PER % 256 == 0 && 256 % PR == 0, "pieces per thread");
-    __shared__ float red[SHARE][PR][VEC + 1];
+    __shared__ double red[SHARE][PR][VEC + 1];
     const int t = threadIdx.x;
     const ReorderArgs &a = p.a;
     const int64_t gt = (int64_t)blockIdx.x * blockDim.x + t;
@@ -71,41 +76,64 @@ __global__ __launch_bounds__(256) void reorder_pool_kernel(ReorderPoolArgs p) {
     const int tyx = a.th * a.tw;
     const int off = t % PR;                                   // the same slice for every piece of this thread
     u32x4 buf[IT];
+    int cnt = 0;                                              // grid tokens among this thread's slots
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
         const int u = (256 * i + t) / PR;                     // token inside the tile
         const int ut = u / tyx, uy = (u / a.tw) % a.th, ux = u % a.tw;
-        const int64_t tok = ((int64_t)(bt * a.tt + ut) * a.gh + (by * a.th + uy)) * a.gw + (bx * a.tw + ux);
-        buf[i] = s4[(bh * N + tok) * PR + off];
+        const int t0 = bt * a.tt + ut, y0 = by * a.th + uy, x0 = bx * a.tw + ux;
+        const bool in = t0 < a.gt && y0 < a.gh && x0 < a.gw;  // else a partial tile's padding slot
+        const int64_t tok = ((int64_t)t0 * a.gh + y0) * a.gw + x0;
+        buf[i] = in ? s4[(bh * a.nr + tok) * PR + off] : u32x4{0u, 0u, 0u, 0u};
+        cnt += in ? 1 : 0;
     }
-    float acc[VEC];
+    // sums in fp64: exact for 64 bf16 values, so the means are exact
+    double acc[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
         d4[(bh * N + (int64_t)blk * 64) * PR + 256 * i + t] = buf[i];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             if constexpr (sizeof(T) == 2) {
-                acc[2 * c] += bf16_lo(buf[i][c]);
-                acc[2 * c + 1] += bf16_hi(buf[i][c]);
+                acc[2 * c] += (double)bf16_lo(buf[i][c]);
+                acc[2 * c + 1] += (double)bf16_hi(buf[i][c]);
             } else {
-                acc[c] += __uint_as_float(buf[i][c]);
+                acc[c] += (double)__uint_as_float(buf[i][c]);
             }
         }
     }
 #pragma unroll
     for (int e = 0; e < VEC; ++e) red[t / PR][off][e] = acc[e];
+    red[t / PR][off][VEC] = (double)cnt;
     __syncthreads();
     if (t >= PR) return;
+    double ntok = 0.0;                                        // tokens of the tile (64 unless partial)
+    for (int g = 0; g < SHARE; ++g) ntok += red[g][t][VEC];
     typedef __attribute__((ext_vector_type(VEC))) float fv;
     typedef __attribute__((ext_vector_type(VEC))) __bf16 bv;
     fv xv, rv;
+    double x64[VEC];
+    float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-        float v = 0.f;
+        double v = 0.0;
         for (int g = 0; g < SHARE; ++g) v += red[g][t][e];
-        xv[e] = v * (1.f / 64.f);
+        x64[e] = ntok == 64.0 ? v * (1.0 / 64.0) : v / ntok;
+        xv[e] = (float)x64[e];
+        ss += xv[e] * xv[e];
+    }
+    {
+        double *m64 = (keys ? p.kbar64 : p.qbar64) + (bh * a.nB + blk) * D + t * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; e += 2) *reinterpret_cast<double2 *>(m64 + e) = double2{x64[e], x64[e + 1]};
+    }
+    if (keys) {
+        // the key mean's norm: the PR threads of the first wave hold its slices
+#pragma unroll
+        for (int o = 1; o < PR; o <<= 1) ss += __shfl_xor(ss, o, 64);
+        if (t == 0) p.knorm[bh * a.nB + blk] = sqrtf(ss);
     }
     const bv hi = __builtin_convertvector(xv, bv);
 #pragma unroll

@@ -19,9 +19,11 @@ namespace sattn {
 
 // ---------------------------------------------------------------------------
 // Pooling of one 64-token block by one wave: the block is 64*D contiguous elements;
-// each lane streams 16-byte chunks (BATCH loads in flight), accumulates in fp32, and
+// each lane streams 16-byte chunks (BATCH loads in flight), accumulates in Acc, and
 // the lanes that share a column slice are combined with xor-shuffles.  Lanes
-// 0 .. LPR-1 end up with the VEC means of columns col .. col+VEC-1.
+// 0 .. LPR-1 end up with the VEC means of columns col .. col+VEC-1.  With Acc =
+// double the means are exact (a sum of 64 bf16 values, or of 64 fp32 values of
+// moderate spread, is exact in fp64, and the division by 64 is a power of two).
 template <typename T, int D, int BATCH> struct BlockPool {
     static constexpr int VEC = 16 / sizeof(T);
     static constexpr int LPR = D / VEC;               // lanes covering one token row
@@ -29,28 +31,39 @@ template <typename T, int D, int BATCH> struct BlockPool {
     static constexpr int ITER = kTokensPerBlock / RPW;
     static constexpr int B = ITER < BATCH ? ITER : BATCH;
     static __device__ __forceinline__ int col(int lane) { return (lane % LPR) * VEC; }
-    static __device__ __forceinline__ void mean(const T *blk, int lane, float (&x)[VEC]) {
+    // `valid`: bit u set when slot u of the block is a grid token (a partial tile's
+    // padding slots are skipped and the mean divides by the token count)
+    template <typename Acc>
+    static __device__ __forceinline__ void mean(const T *blk, int lane, Acc (&x)[VEC], uint64_t valid = ~0ull) {
         const u32x4 *p = reinterpret_cast<const u32x4 *>(blk + (lane / LPR) * D + col(lane));
         constexpr int STEP = RPW * D * (int)sizeof(T) / 16;   // u32x4 units between iterations
-        float acc[VEC];
+        Acc acc[VEC];
 #pragma unroll
-        for (int c = 0; c < VEC; ++c) acc[c] = 0.f;
+        for (int c = 0; c < VEC; ++c) acc[c] = 0;
 #pragma unroll
         for (int b0 = 0; b0 < ITER; b0 += B) {
             u32x4 buf[B];
 #pragma unroll
             for (int it = 0; it < B; ++it) buf[it] = p[(b0 + it) * STEP];
+            if (valid != ~0ull) {
+#pragma unroll
+                for (int it = 0; it < B; ++it)
+                    if (!((valid >> (lane / LPR + RPW * (b0 + it))) & 1ull)) buf[it] = u32x4{0u, 0u, 0u, 0u};
+            }
 #pragma unroll
             for (int it = 0; it < B; ++it) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     if constexpr (sizeof(T) == 2) {
-                        acc[2 * c] += bf16_lo(buf[it][c]);
-                        acc[2 * c + 1] += bf16_hi(buf[it][c]);
+                        acc[2 * c] += (Acc)bf16_lo(buf[it][c]);
+                        acc[2 * c + 1] += (Acc)bf16_hi(buf[it][c]);
                     } else {
-                        acc[c] += __uint_as_float(buf[it][c]);
+                        acc[c] += (Acc)__uint_as_float(buf[it][c]);
                     }
                 }
+                // one load's conversions at a time: the fp64 temporaries of all loads
+                // at once would not fit the register budget
+                if constexpr (sizeof(Acc) == 8) __builtin_amdgcn_sched_barrier(0);
             }
         }
 #pragma unroll
@@ -58,8 +71,24 @@ template <typename T, int D, int BATCH> struct BlockPool {
 #pragma unroll
             for (int c = 0; c < VEC; ++c) acc[c] += __shfl_xor(acc[c], o, 64);
         }
+        if (valid == ~0ull) {
 #pragma unroll
-        for (int c = 0; c < VEC; ++c) x[c] = acc[c] * (1.f / 64.f);
+            for (int c = 0; c < VEC; ++c) x[c] = acc[c] * (Acc)(1.0 / 64.0);
+        } else {
+            const Acc n = (Acc)__popcll(valid);
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) x[c] = acc[c] / n;
+        }
+    }
+    // the exact means, for the selection's exact rescoring of near-ties
+    static __device__ __forceinline__ void store64(const double (&x)[VEC], double *row, int lane) {
+#pragma unroll
+        for (int c = 0; c < VEC; c += 2)
+            *reinterpret_cast<double2 *>(row + col(lane) + c) = double2{x[c], x[c + 1]};
+    }
+    static __device__ __forceinline__ void to_f32(const double (&x)[VEC], float (&y)[VEC]) {
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) y[c] = (float)x[c];
     }
     // the fp32 means as bf16 pairs, hi = bf16(x) and lo = bf16(x - hi): the operand
     // form of the split-bf16 score products ([hi: D][lo: D] per block)
@@ -99,7 +128,8 @@ template <typename T, int D, int BATCH> struct BlockPool {
 // the first ThrChunk::kMax thresholds, and zeroing its ticket and look-back words.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ k, __bf16 *__restrict__ kbar,
-                                                   int64_t nblocks, int32_t nB, PoolSide side) {
+                                                   double *__restrict__ kbar64, float *__restrict__ knorm,
+                                                   int64_t nblocks, int32_t nB, PoolSide side, SlotGeo geo) {
     const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (blockIdx.x == 0 && (int)threadIdx.x < side.n_thr) side.thr_dst[threadIdx.x] = side.thr.v[threadIdx.x];
     for (int64_t i = gt; i < side.n_status; i += (int64_t)gridDim.x * blockDim.x) side.status[i] = 0;
@@ -111,11 +141,23 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ k, __bf
     const int lane = threadIdx.x & 63;
     const int64_t blk = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
     if (blk >= nblocks) return;
-    float x[P::VEC];
-    P::mean(k + blk * kTokensPerBlock * D, lane, x);
     const int64_t bh = blk / nB;
     const int j = (int)(blk - bh * nB);
-    if (lane < P::LPR) P::store_frag(x, kbar + kbar_group(bh, (nB + 15) / 16, j / 16, D), j % 16, lane);
+    const uint64_t valid = geo.partial ? __ballot(slot_valid(geo, j, lane)) : ~0ull;
+    double x64[P::VEC];
+    float x[P::VEC];
+    P::mean(k + blk * kTokensPerBlock * D, lane, x64, valid);
+    P::to_f32(x64, x);
+    // the mean's Euclidean norm (for the scores' error bound)
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < P::VEC; ++c) ss += lane < P::LPR ? x[c] * x[c] : 0.f;
+    ss = wave_sum_u(ss);
+    if (lane < P::LPR) {
+        P::store_frag(x, kbar + kbar_group(bh, (nB + 15) / 16, j / 16, D), j % 16, lane);
+        P::store64(x64, kbar64 + blk * D, lane);
+    }
+    if (lane == 0) knorm[blk] = sqrtf(ss);
 }
 
 // ---------------------------------------------------------------------------
@@ -157,7 +199,56 @@ constexpr int kStageStride = kSelChunk + 4;   // padded: the 16x16 tile stores a
 template <int D> constexpr int qf_stride() { return 2 * D + 8; }   // bf16; 16 B pad per row
 template <int D> constexpr size_t select_lds_bytes() {
     return (size_t)kSelRows * qf_stride<D>() * 2 + (size_t)2 * kSelRows * kStageStride * 4 +
-           (size_t)kSelRows * 256 * 4;
+           (size_t)kSelRows * 256 * 4 + (size_t)kSelRows * D * 8;
+}
+
+// Exact order of the near-ties at the cut.  The band is the set of blocks whose
+// probability lies within the scores' error bound of the crossing value: `list` holds
+// its nb block indices in ascending order, `cdf` (word c in lane c) the blocks the cut
+// keeps, m of them in the band, with 2 <= nb <= kRefineMax and 0 < m < nb (otherwise
+// nothing is ambiguous).  The band's blocks
+// are scored again in fp64 from the exact means (qrow: this row's query mean in LDS;
+// k64: the head's key means) and the m best of them by exact score (ties to the lower
+// index) replace the cut's choice among them.  Every block outside the band is
+// ordered correctly against every block inside it, so this is the cut of the exact
+// scores wherever the kept count m is itself settled (it can change only when the
+// threshold lies within the band's spread of mass, i.e. at the boundary).
+template <int D>
+__device__ __forceinline__ uint64_t refine_band(uint64_t cdf, int nb, int m, const double *qrow, const double *k64,
+                                                const uint32_t *list, int lane) {
+    static_assert(D % 64 == 0, "whole dimensions per lane");
+    constexpr int DPL = D / 64;
+    const int my_j = lane < nb ? (int)list[lane] : 0x7fffffff;
+    double q[DPL];
+#pragma unroll
+    for (int u = 0; u < DPL; ++u) q[u] = qrow[DPL * lane + u];
+    double my_s = 0.0;
+    for (int n = 0; n < nb; ++n) {
+        const int j = __builtin_amdgcn_readfirstlane((int)list[n]);
+        const double *kr = k64 + (int64_t)j * D + DPL * lane;
+        double part = 0.0;
+#pragma unroll
+        for (int u = 0; u < DPL; ++u) part = __builtin_fma(q[u], kr[u], part);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+        if (lane == n) my_s = part;
+    }
+    // rank by (exact score descending, index ascending); the m best are kept
+    int rank = 0;
+    for (int n = 0; n < nb; ++n) {
+        const double sn = __shfl(my_s, n, 64);
+        const int jn = __shfl(my_j, n, 64);
+        rank += (sn > my_s || (sn == my_s && jn < my_j)) ? 1 : 0;
+    }
+    const uint64_t keep = __ballot(lane < nb && rank < m);
+    for (int n = 0; n < nb; ++n) {
+        const int jn = __builtin_amdgcn_readfirstlane((int)list[n]);
+        if (lane == (jn >> 6)) {
+            const uint64_t bit = 1ull << (jn & 63);
+            cdf = ((keep >> n) & 1ull) ? (cdf | bit) : (cdf & ~bit);
+        }
+    }
+    return cdf;
 }
 
 // Pivot steps of the cut over an array of keys v (the register row, or the bracket
@@ -229,9 +320,10 @@ __device__ __forceinline__ uint32_t div_small(uint32_t j, uint32_t m24) { return
 // scores, -inf for padding keys).  Returns the row's bitmask (lane c holds the word
 // of key blocks 64c .. 64c+63) and its count.  `bracket` is 512 words of LDS for this
 // wave, `hist_all` holds 256 words per wave.
-template <int NE>
+template <int NE, int D>
 __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], float *hist_all, uint32_t *bracket,
-                                           int i, float thr, int lane, uint64_t &word, int32_t &count_out) {
+                                           int i, float thr, int lane, uint64_t &word, int32_t &count_out,
+                                           const double *qrow, const double *k64, float band_rel) {
     constexpr int NC = 8;                  // compacted bracket: 8 words a lane, 512 keys
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool keep_all = !(thr < 1.f);
@@ -329,11 +421,17 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
     const uint32_t m_x = (0x1000000u + (uint32_t)a.nTx - 1u) / (uint32_t)a.nTx;
     const uint32_t m_y = (0x1000000u + (uint32_t)a.nTy - 1u) / (uint32_t)a.nTy;
     const float vstar_f = __uint_as_float(vstar);
-    uint32_t ties_before = 0, count = 0, wlo = 0, whi = 0;
+    // the band of near-ties around v* (band_rel < 0: no exact rescoring); the main pass
+    // only counts the band and the kept blocks in it
+    const bool refine = !keep_all && band_rel >= 0.f && qrow != nullptr;
+    const float blo = vstar_f * (1.f - band_rel), bhi = vstar_f * (1.f + band_rel);
+    uint32_t ties_before = 0;
+    int nbl = 0, mbl = 0;                  // this lane's band and kept-in-band counts
+    uint64_t cdf_word = 0, win_word = 0;
 #pragma unroll
     for (int c = 0; c < NE; ++c) {
         const int j = 64 * c + lane;
-        uint64_t m;
+        uint64_t m, mw = 0;
         if (keep_all) {
             m = __ballot(j < a.nB);
         } else {
@@ -346,21 +444,46 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
                 m |= __ballot(u == vstar && M + (float)rank * vstar_f < thrz);
                 ties_before += (uint32_t)__popcll(tb);
             }
+            if (refine) {
+                const bool inb = s[c] >= blo && s[c] <= bhi && s[c] > 0.f;
+                nbl += inb ? 1 : 0;
+                mbl += (inb && ((m >> lane) & 1ull)) ? 1 : 0;
+            }
         }
         if (a.window) {
             const uint32_t row = div_small((uint32_t)j, m_x);                 // j / nTx
             const int xj = j - (int)row * a.nTx;
             const int yj = (int)row - (int)div_small(row, m_y) * a.nTy;      // (j / nTx) % nTy
-            m |= __ballot(j >= jlo && j < jhi && abs(yj - yi) <= a.wh && abs(xj - xi) <= a.ww);
+            mw = __ballot(j >= jlo && j < jhi && abs(yj - yi) <= a.wh && abs(xj - xi) <= a.ww);
         }
-        count += (uint32_t)__popcll(m);
         if (lane == c) {
-            wlo = (uint32_t)m;
-            whi = (uint32_t)(m >> 32);
+            cdf_word = m;
+            win_word = mw;
         }
     }
-    word = ((uint64_t)whi << 32) | wlo;
-    count_out = (int32_t)count;
+    if (refine) {
+        const int nb = wave_sum_i(nbl), mb = wave_sum_i(mbl);
+        if (nb >= 2 && nb <= kRefineMax && mb > 0 && mb < nb) {
+            // the band's indices, ascending, into this wave's LDS list
+            const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+            uint32_t *list = reinterpret_cast<uint32_t *>(hist_all) + 256 * wave;
+            uint32_t base = 0;
+#pragma unroll
+            for (int c = 0; c < NE; ++c) {
+                const bool in = s[c] >= blo && s[c] <= bhi && s[c] > 0.f;
+                const uint64_t bm = __ballot(in);
+                if (in)
+                    list[base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u))] =
+                        (uint32_t)(64 * c + lane);
+                base += (uint32_t)__popcll(bm);
+            }
+            wave_lds_sync();
+            cdf_word = refine_band<D>(cdf_word, nb, mb, qrow, k64, list, lane);
+            wave_lds_sync();
+        }
+    }
+    word = cdf_word | win_word;
+    count_out = (int32_t)wave_sum_i(__popcll(word));
 }
 
 // Uniform in [0, 1) for block j of row r: the top 24 bits of output r * nB + j + 1
@@ -483,22 +606,26 @@ __device__ __forceinline__ int64_t group_lookback(uint64_t *status, int64_t g, i
 // on rows given in log2 units (mix_rows, one per pair of query blocks: the
 // clustering selector), with no pooling or scores of its own.
 template <typename T, int D, int NE, int MODE>
-__global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
+__device__ __forceinline__ void select_emit_body(const SelectArgs &a) {
     static_assert(NE % 4 == 0 && NE <= 64, "NE: register row length in 64-key words");
     constexpr int KB = D / 32;                     // k-blocks of one 16x16x32 product
     constexpr int NCH = NE / 4;                    // score chunks
     // registers for the next chunk's operands where they fit; at NE <= 8 two
     // workgroups share a CU instead
     constexpr bool kPrefetch = NE > 8 && NE <= 32;
-    using QP = BlockPool<T, D, 8>;
+    // the CDF selection pools its queries in fp64 (exact means for the near-tie
+    // rescoring), with fewer loads in flight to stay within the register budget
+    using QP = BlockPool<T, D, MODE == 0 ? 4 : 8>;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     __bf16 *qf = reinterpret_cast<__bf16 *>(smem_raw);                              // [16][2D+8]
     float *stage = reinterpret_cast<float *>(smem_raw + (size_t)kSelRows * qf_stride<D>() * 2);  // [2][16][260]
     float *hist_all = stage + 2 * kSelRows * kStageStride;                          // [16][256]
+    double *q64 = reinterpret_cast<double *>(hist_all + kSelRows * 256);            // [16][D] exact query means
     __shared__ uint32_t s_ticket;
     __shared__ int32_t wave_count[kSelRows];
     __shared__ int64_t s_base;
     __shared__ int32_t s_gave_up;
+    __shared__ float s_kmax[kSelRows];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -535,6 +662,16 @@ __global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
             kl[slot][kb] = *reinterpret_cast<const bf16x8 *>(kr + 16 * D + 512 * kb);
         }
     };
+    // ---- the largest key-mean norm of the head (for the scores' error bound), each
+    //      wave over a slice of the head's key blocks
+    if constexpr (MODE == 0) {
+        const int per = (a.nB + kSelRows - 1) / kSelRows;
+        float mx = 0.f;
+        for (int j = wave * per + lane; j < min(a.nB, (wave + 1) * per); j += 64)
+            mx = fmaxf(mx, a.knorm[(int64_t)bh * a.nB + j]);
+        mx = wave_max_u(mx);
+        if (lane == 0) s_kmax[wave] = mx;
+    }
     // ---- the group's pooled queries (hi | lo), one query block per wave: pooled here,
     //      or copied from the means the reorder formed
     {
@@ -545,10 +682,25 @@ __global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
                 wave < nrows ? reinterpret_cast<const QV *>(a.qbar + ((int64_t)bh * a.nB + i0 + wave) * (2 * D))[lane]
                              : QV{};
             reinterpret_cast<QV *>(qrow)[lane] = v;
+            if constexpr (MODE == 0) {
+                if (wave < nrows) {
+                    const double *src = a.qbar64 + ((int64_t)bh * a.nB + i0 + wave) * D;
+#pragma unroll
+                    for (int u = 0; u < D / 64; ++u) q64[wave * D + (D / 64) * lane + u] = src[(D / 64) * lane + u];
+                }
+            }
         } else if (wave < nrows) {
             float x[QP::VEC];
             const T *qb = reinterpret_cast<const T *>(a.q) + (((int64_t)bh * a.nB + i0 + wave) * kTokensPerBlock) * D;
-            QP::mean(qb, lane, x);
+            const uint64_t valid = a.geo.partial ? __ballot(slot_valid(a.geo, i0 + wave, lane)) : ~0ull;
+            if constexpr (MODE == 0) {
+                double x64[QP::VEC];
+                QP::mean(qb, lane, x64, valid);
+                QP::to_f32(x64, x);
+                if (lane < QP::LPR) QP::store64(x64, q64 + wave * D, lane);
+            } else {
+                QP::mean(qb, lane, x, valid);
+            }
             if (lane < QP::LPR) QP::store_split(x, qrow, lane);
         } else if (lane < 2 * D / 8) {
             reinterpret_cast<uint4 *>(qrow)[lane] = uint4{0u, 0u, 0u, 0u};
@@ -590,10 +742,30 @@ __global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
     int32_t count = 0;
     float sigma = 0.f, tcap = 0.f;
     if (wave < nrows) {
-        if constexpr (MODE != 1)
-            select_cut<NE>(a, s, hist_all, reinterpret_cast<uint32_t *>(stage) + 512 * wave, i0 + wave, thr, lane, word,
-                           count);
-        else sip_cut<NE>(a, s, (int64_t)bh * a.nB + i0 + wave, lane, word, count, sigma, tcap);
+        if constexpr (MODE == 0) {
+            // half-width of the near-tie band, relative: twice the score bound (the row
+            // max carries one too) in log2 units, plus the exponential's own rounding
+            float kmax = 0.f;
+#pragma unroll
+            for (int w = 0; w < kSelRows; ++w) kmax = fmaxf(kmax, s_kmax[w]);
+            const double *qrow = q64 + wave * D;
+            float qq = 0.f;
+#pragma unroll
+            for (int u = 0; u < D / 64; ++u) {
+                const float x = (float)qrow[(D / 64) * lane + u];
+                qq += x * x;
+            }
+            const float qn = sqrtf(wave_sum_u(qq));
+            const float band_rel =
+                __builtin_amdgcn_exp2f(2.f * kScoreEps * a.scale_log2 * qn * kmax * 1.01f) - 1.f + 0x1p-20f;
+            select_cut<NE, D>(a, s, hist_all, reinterpret_cast<uint32_t *>(stage) + 512 * wave, i0 + wave, thr, lane,
+                              word, count, qrow, a.kbar64 + (int64_t)bh * a.nB * D, band_rel);
+        } else if constexpr (MODE == 2) {
+            select_cut<NE, D>(a, s, hist_all, reinterpret_cast<uint32_t *>(stage) + 512 * wave, i0 + wave, thr, lane,
+                              word, count, nullptr, nullptr, -1.f);
+        } else {
+            sip_cut<NE>(a, s, (int64_t)bh * a.nB + i0 + wave, lane, word, count, sigma, tcap);
+        }
     }
     if (lane == 0) wave_count[wave] = count;
     __syncthreads();
@@ -658,18 +830,25 @@ __global__ __launch_bounds__(1024) void select_emit_kernel(SelectArgs a) {
     }
 }
 
+// Rows of up to 512 key blocks (NE <= 8) fit in 64 registers, and two workgroups then
+// share a CU (8 waves per SIMD); longer rows take the whole register budget of one.
+template <typename T, int D, int NE, int MODE>
+__global__ __launch_bounds__(1024, NE <= 8 ? 8 : 4) void select_emit_kernel(SelectArgs a) {
+    select_emit_body<T, D, NE, MODE>(a);
+}
+
 // ---------------------------------------------------------------------------
-int launch_pool_keys(const void *k, __bf16 *kbar, int64_t nblocks, int32_t nB, int dtype, int d, const PoolSide &side,
-                     hipStream_t s) {
+int launch_pool_keys(const void *k, __bf16 *kbar, double *kbar64, float *knorm, int64_t nblocks, int32_t nB, int dtype,
+                     int d, const PoolSide &side, const SlotGeo &geo, hipStream_t s) {
     const dim3 grid((unsigned)((nblocks + 3) / 4)), block(256);
     if (dtype == 1 && d == 128)
-        pool_kernel<__bf16, 128><<<grid, block, 0, s>>>((const __bf16 *)k, kbar, nblocks, nB, side);
+        pool_kernel<__bf16, 128><<<grid, block, 0, s>>>((const __bf16 *)k, kbar, kbar64, knorm, nblocks, nB, side, geo);
     else if (dtype == 1 && d == 64)
-        pool_kernel<__bf16, 64><<<grid, block, 0, s>>>((const __bf16 *)k, kbar, nblocks, nB, side);
+        pool_kernel<__bf16, 64><<<grid, block, 0, s>>>((const __bf16 *)k, kbar, kbar64, knorm, nblocks, nB, side, geo);
     else if (dtype == 0 && d == 128)
-        pool_kernel<float, 128><<<grid, block, 0, s>>>((const float *)k, kbar, nblocks, nB, side);
+        pool_kernel<float, 128><<<grid, block, 0, s>>>((const float *)k, kbar, kbar64, knorm, nblocks, nB, side, geo);
     else
-        pool_kernel<float, 64><<<grid, block, 0, s>>>((const float *)k, kbar, nblocks, nB, side);
+        pool_kernel<float, 64><<<grid, block, 0, s>>>((const float *)k, kbar, kbar64, knorm, nblocks, nB, side, geo);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -20,7 +20,9 @@ Recipe (one field per batch, head and channel):
 * ``K = Q + 0.5 * N(0, 1)`` with independent noise, ``V ~ N(0, 1)``;
 * tokens are then put in tile-major order: frame-block outermost, then tile
   row, then tile column, then row-major inside the ``tile_t x tile_h x tile_w``
-  tile, so that block ``b`` is tokens ``[64 b, 64 b + 64)``;
+  tile, so that block ``b`` is tokens ``[64 b, 64 b + 64)``; on a grid that is not
+  a whole number of tiles the last tiles are partial and their slots beyond the
+  grid hold zeros;
 * finally the arrays are cast to the workload's dtype (the cast values are
   what every consumer sees).
 
@@ -70,7 +72,16 @@ class Workload:
 
     @property
     def block_grid(self) -> Tuple[int, int, int]:
-        return tuple(g // s for g, s in zip(self.grid, self.tile))
+        return tuple(-(-g // s) for g, s in zip(self.grid, self.tile))
+
+    @property
+    def partial(self) -> bool:
+        return any(g % s for g, s in zip(self.grid, self.tile))
+
+    @property
+    def slots(self) -> int:
+        """Token slots of a head in tile-major order (nB * 64, padding included)."""
+        return self.blocks * 64
 
     @property
     def blocks(self) -> int:
@@ -127,9 +138,15 @@ def _smooth_valid(x: torch.Tensor, taps: np.ndarray) -> torch.Tensor:
 
 
 def tile_major(x: torch.Tensor, grid, tile) -> torch.Tensor:
-    """[..., d, T, H, W] field -> [..., N, d] tokens in tile-major order."""
+    """[..., d, T, H, W] field -> [..., nB * V, d] tokens in tile-major order.  When the
+    grid is not a whole number of tiles, the last tile along an axis is partial and its
+    slots beyond the grid hold zeros (padding)."""
     t, h, w = grid
     tt, th, tw = tile
+    pt, ph, pw = (-(-t // tt)) * tt, (-(-h // th)) * th, (-(-w // tw)) * tw
+    if (pt, ph, pw) != (t, h, w):
+        x = torch.nn.functional.pad(x, (0, pw - w, 0, ph - h, 0, pt - t))
+        t, h, w = pt, ph, pw
     lead = x.shape[:-4]
     d = x.shape[-4]
     x = x.reshape(*lead, d, t // tt, tt, h // th, th, w // tw, tw)
@@ -159,9 +176,6 @@ def make_inputs(wl: Workload, reading: str = "A", threads: Optional[int] = None)
     """
     if reading not in ("A", "B", "page"):
         raise ValueError(f"unknown reading {reading!r}")
-    for g, s in zip(wl.grid, wl.tile):
-        if g % s:
-            raise ValueError(f"grid {wl.grid} is not a whole number of {wl.tile} tiles")
     B, H, d = wl.batch, wl.heads, wl.head_dim
     T, Hh, W = wl.grid
     taps = gaussian_taps(wl.sigma)
@@ -171,7 +185,7 @@ def make_inputs(wl: Workload, reading: str = "A", threads: Optional[int] = None)
         std = math.sqrt(float(np.sum(taps * taps)) ** 3)
         amp = (4.0 if reading == "B" else 1.4) / std
     tdt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
-    N = wl.tokens
+    N = wl.slots                      # tile-major slots (== tokens for whole tiles)
     q = torch.empty(B, H, N, d, dtype=tdt)
     k = torch.empty(B, H, N, d, dtype=tdt)
     v = torch.empty(B, H, N, d, dtype=tdt)
@@ -206,8 +220,10 @@ def make_inputs(wl: Workload, reading: str = "A", threads: Optional[int] = None)
 
 def small_workload(name: str, heads: int, head_dim: int, block_grid, dtype: str = "bf16",
                    sigma: float = 2.0, threshold: float = 0.9, window=(-1, -1, -1),
-                   head_threshold_range=None, seed: int = 0) -> Workload:
-    """A test-sized workload with the given block grid (tiles 1x8x8)."""
+                   head_threshold_range=None, seed: int = 0, grid=None) -> Workload:
+    """A test-sized workload with the given block grid (tiles 1x8x8), or with the given
+    token grid (which may end in partial tiles)."""
     bt, by, bx = block_grid
-    return Workload(name, 1, heads, head_dim, (bt, 8 * by, 8 * bx), dtype, sigma, threshold,
+    g = (bt, 8 * by, 8 * bx) if grid is None else tuple(grid)
+    return Workload(name, 1, heads, head_dim, g, dtype, sigma, threshold,
                     head_threshold_range=head_threshold_range, window=tuple(window), seed=seed)

@@ -14,9 +14,18 @@
  * attention is then run over the kept 64 x 64 tiles only ("Expansion").
  *
  * Conventions shared by every entry point
- *   - Tensors are dense row-major [B, H, N, d] with N = grid_t*grid_h*grid_w;
- *     block b of a head is tokens [64 b, 64 b + 64).  Element type is given
- *     by shape->dtype (fp32 or bf16); q, k, v and out share it.
+ *   - Tensors are dense row-major [B, H, N, d].  The blocks are the
+ *     nT x nTy x nTx = ceil(grid / tile) tiles of the token grid, frame-block
+ *     outermost, and a tile-major tensor has N = 64 nB slots: block b of a head
+ *     is slots [64 b, 64 b + 64), row-major inside its tile.  On a grid that is
+ *     not a whole number of tiles (item "Fractal Flattening": patches whatever the
+ *     global size of the video), the last tile along an axis is partial and its
+ *     slots beyond the grid are padding: their contents must be finite but do not
+ *     matter (sparse_attn_to_tiles writes zeros); pooling leaves them out, the
+ *     attention gives them no weight as keys, and as queries they get O = 0 and
+ *     LSE = -inf.  Raster tensors (sparse_attn_to_tiles and friends) have
+ *     N = grid_t*grid_h*grid_w.  Element type is given by shape->dtype (fp32 or
+ *     bf16); q, k, v and out share it.
  *   - All pointers named as device pointers must point to device memory (or
  *     memory the device can address) and be 16-byte aligned.  Host pointers
  *     are read during the call only and are not retained.
@@ -58,9 +67,12 @@ extern "C" {
 #define SPARSE_ATTN_LOOKBACK_FAULT (-6)   /* a selection gave up in its CSR look-back (see
                                              sparse_attn_select_check)                          */
 
+
 /*
  * Problem shape.  head_dim must be 64 or 128; the tile must hold 64 tokens
- * (only 1 x 8 x 8 is implemented) and divide the grid exactly.  scale is the
+ * (1 x 8 x 8 in the video workloads; any tile_t x tile_h x tile_w of volume 64
+ * works) and need not divide the grid (see partial tiles above; the clustering
+ * selector and the backward take whole tiles only).  scale is the
  * softmax scale of both the pooled scores and the attention; it must be
  * finite and >= 0, and 0 means 1/sqrt(head_dim).  The worst-case block
  * count B*H*nB*nB (nB = blocks per head) must fit in int32.
@@ -193,7 +205,7 @@ int32_t sparse_attn_select_sip(const sparse_attn_shape *shape, const sparse_attn
  * blocks of the pair keep the blocks NABLA's CDF rule keeps on p~ (threshold,
  * per-head thresholds and window as in sparse_attn_select).
  *
- *   Arguments as in sparse_attn_select.  bf16 only, nB <= 4096
+ *   Arguments as in sparse_attn_select.  bf16 only, nB <= 4096, whole tiles
  *   (SPARSE_ATTN_UNSUPPORTED otherwise).
  */
 int32_t sparse_attn_select_ibcs(const sparse_attn_shape *shape, const sparse_attn_select_params *params,
@@ -288,7 +300,7 @@ int32_t sparse_attn_radial_csr(const sparse_attn_shape *shape, const sparse_attn
                                void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
- * Backward of sparse_attn_forward (bf16 only and nB <= 4096; SPARSE_ATTN_UNSUPPORTED
+ * Backward of sparse_attn_forward (bf16 only, nB <= 4096, whole tiles; SPARSE_ATTN_UNSUPPORTED
  * otherwise):
  * the gradients for training (NABLA summary page, "Methodologie : NABLA" and its
  * training results).  With P the forward's softmax weights (recovered from lse)
@@ -334,8 +346,9 @@ int32_t sparse_attn_full_csr(const sparse_attn_shape *shape, int32_t *row_ptr, i
  *   raster      token (t, y, x) at index (t * grid_h + y) * grid_w + x.
  *   tile-major  block b = (bt * nTy + by) * nTx + bx holds tokens [64 b, 64 b + 64):
  *               the tile_t x tile_h x tile_w tile at (bt, by, bx), row-major inside.
- * sparse_attn_to_tiles: raster -> tile-major; sparse_attn_from_tiles: the inverse.
- * The grid must divide into whole tiles (SPARSE_ATTN_UNSUPPORTED otherwise).
+ * sparse_attn_to_tiles: raster [B, H, grid_t*grid_h*grid_w, d] -> tile-major
+ * [B, H, 64 nB, d], padding slots of partial tiles written as zeros;
+ * sparse_attn_from_tiles: the inverse (padding slots dropped).
  */
 int32_t sparse_attn_to_tiles(const sparse_attn_shape *shape, const void *src, void *dst, void *stream);
 int32_t sparse_attn_from_tiles(const sparse_attn_shape *shape, const void *src, void *dst, void *stream);
@@ -349,8 +362,8 @@ int32_t sparse_attn_from_tiles(const sparse_attn_shape *shape, const void *src, 
  * gives on the tile-major copies, up to fp32 summation order in the means (which
  * moves only blocks whose cumulative mass lies at the threshold).
  *
- *   q, k          device, [B, H, N, d] in shape->dtype, raster order.
- *   q_tiles, k_tiles  device, same size, written: the tile-major copies, ready for
+ *   q, k          device, [B, H, grid_t*grid_h*grid_w, d] in shape->dtype, raster order.
+ *   q_tiles, k_tiles  device, [B, H, 64 nB, d], written: the tile-major copies, ready for
  *               sparse_attn_forward.  Four distinct, non-overlapping buffers.
  *   params, row_ptr, col_idx, col_capacity, workspace: as in sparse_attn_select.
  * Errors as in sparse_attn_select and sparse_attn_to_tiles.

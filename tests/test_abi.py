@@ -55,6 +55,9 @@ def test_capacity_and_workspace_formulas():
     expect = al(expect + 4 * rows * 128)                  # query block means (raster selection)
     expect = al(expect + 8 * 12 * ((nB + 15) // 16))      # selection look-back words per 16-row group
     expect = al(expect + 16)                              # selection ticket counter
+    expect = al(expect + 8 * rows * 128)                  # exact key means (fp64)
+    expect = al(expect + 4 * rows)                        # their norms
+    expect = al(expect + 8 * rows * 128)                  # exact query means (raster selection)
     expect = al(expect + 8 * rows * (nbp // 64))
     expect = al(expect + 4 * rows)
     expect = al(expect + 4 * 12 * ((nB + 15) // 16))     # kept-block totals per 16-row group
@@ -72,13 +75,13 @@ def test_capacity_and_workspace_formulas():
     expect = al(expect + 4 * rows * 64)                   # backward: dO . O
     per_head = 4 * ((nB + 1) // 2) * nbp                  # clustering selector: a row per query-block pair
     expect = al(expect + min(12, max(1, (64 << 20) // per_head)) * per_head)
+    expect = al(expect + 8 * nB)                          # partial tiles: token slots per block
     assert B.sparse_attn_workspace_size(s) == expect
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), B.SPARSE_ATTN_UNSUPPORTED),
     (dict(dtype=7), B.SPARSE_ATTN_UNSUPPORTED),
-    (dict(grid=(20, 30, 48)), B.SPARSE_ATTN_UNSUPPORTED),          # not a whole number of 8x8 tiles
     (dict(tile=(1, 4, 8)), B.SPARSE_ATTN_UNSUPPORTED),             # 32-token tile
     (dict(batch=0), B.SPARSE_ATTN_INVALID_ARGUMENT),
     (dict(heads=-1), B.SPARSE_ATTN_INVALID_ARGUMENT),
@@ -204,8 +207,6 @@ def test_reorder_rejects_before_launch(fn):
     assert f(ctypes.byref(s), A, A, None) == B.SPARSE_ATTN_INVALID_ARGUMENT          # same buffer
     assert f(ctypes.byref(s), A, A + 8, None) == B.SPARSE_ATTN_INVALID_ARGUMENT      # misaligned
     assert f(ctypes.byref(s), None, A, None) == B.SPARSE_ATTN_INVALID_ARGUMENT
-    bad = _shape(grid=(20, 30, 48))                                                  # partial tiles
-    assert f(ctypes.byref(bad), A, A + 4096, None) == B.SPARSE_ATTN_UNSUPPORTED
 
 
 def test_full_csr_rejects_before_launch():
@@ -379,3 +380,29 @@ def test_select_check_rejects_bad_arguments_on_the_host():
     bad = B.make_shape(1, 2, 96, (2, 8, 16), "bf16")
     assert L.sparse_attn_select_check(ctypes.byref(bad), 16, ws, None) == B.SPARSE_ATTN_UNSUPPORTED
     assert "look-back" in B.status_string(B.SPARSE_ATTN_LOOKBACK_FAULT)
+
+
+def test_partial_tiles_size_by_ceil_grid():
+    """A grid that is not a whole number of tiles has ceil(grid / tile) tiles, the last
+    ones partial: 20 x 30 x 45 tokens in 1 x 8 x 8 tiles give 20 x 4 x 6 = 480 blocks,
+    whose tile-major tensors hold 64 * 480 slots a head."""
+    s = _shape(grid=(20, 30, 45))
+    nB = 480
+    assert B.sparse_attn_csr_capacity(s) == 12 * nB * nB
+    assert B.sparse_attn_workspace_size(s) == B.sparse_attn_workspace_size(_shape(grid=(20, 32, 48)))
+    assert B._dims(s) == (64 * nB, nB, 12 * nB)
+    assert B._raster_tokens(s) == 20 * 30 * 45
+
+
+def test_partial_tiles_refused_where_whole_tiles_are_needed():
+    """The clustering selector (128-token clusters of whole tiles) and the backward take
+    whole tiles only: SPARSE_ATTN_UNSUPPORTED on the host, before any launch."""
+    L = B.lib()
+    s = _shape(grid=(20, 30, 45))
+    ws = B.sparse_attn_workspace_size(s)
+    cap = B.sparse_attn_csr_capacity(s)
+    params = B.SelectParams(0.9, None, -1, -1, -1)
+    assert L.sparse_attn_select_ibcs(ctypes.byref(s), ctypes.byref(params), A, A, A, A, cap, A, ws,
+                                     None) == B.SPARSE_ATTN_UNSUPPORTED
+    assert L.sparse_attn_backward(ctypes.byref(s), A, A, A, A, A, A, A, A, cap, A, A, A, A, A, ws,
+                                  None) == B.SPARSE_ATTN_UNSUPPORTED

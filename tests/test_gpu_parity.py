@@ -686,3 +686,77 @@ def test_lookback_give_up_is_reported(monkeypatch):
     assert B.sparse_attn_select_check(shape, bufs.workspace) == B.SPARSE_ATTN_OK
     rp = bufs.row_ptr.cpu().numpy().astype(np.int64)
     assert np.array_equal(rp, ref_rp)
+
+
+
+# ---------------------------------------------------------------- partial tiles
+# Grids that are not a whole number of tiles: the last tile along y or x is partial,
+# and its slots beyond the grid are padding (filled here with junk, which must not
+# matter).
+
+PARTIAL = [
+    # name, heads, d, token grid, dtype, thr, window, reading
+    ("bf16_d128_2x12x20", 2, 128, (2, 12, 20), "bf16", 0.85, (-1, -1, -1), "A"),
+    ("f32_d64_3x13x11", 1, 64, (3, 13, 11), "f32", 0.9, (-1, -1, -1), "A"),
+    ("bf16_d64_4x9x17_window", 2, 64, (4, 9, 17), "bf16", 0.7, (1, 1, 1), "B"),
+    ("bf16_d128_5x20x36_page", 3, 128, (5, 20, 36), "bf16", 0.9, (-1, -1, -1), "page"),
+]
+
+
+def _junk_padding(wl, *ts):
+    valid = torch.as_tensor(P.valid_of(wl))
+    for t in ts:
+        t[..., ~valid, :] = 7.0
+    return ts
+
+
+@pytest.mark.parametrize("case", PARTIAL, ids=[c[0] for c in PARTIAL])
+def test_partial_tiles_select_and_forward(case):
+    name, H, d, grid, dt, thr, win, reading = case
+    wl = small_workload(name, H, d, (0, 0, 0), dt, threshold=thr, window=win, seed=71, grid=grid)
+    assert wl.partial
+    print(f"\n[case] partial tiles {name} blocks={wl.blocks} tokens={wl.tokens} slots={wl.slots}", flush=True)
+    q, k, v, thr_h = make_inputs(wl, reading)
+    q, k, v = _junk_padding(wl, q, k, v)
+    qd, kd, vd = P.to_device(q, k, v)
+    rp, ci = P.gpu_select(wl, qd, kd, thr_h)
+    gmask = P.check_csr(rp, ci, wl.blocks)
+    qbar, kbar, keep, band = P.oracle_select_full(wl, q, k, thr_h, count_band=True)
+    rep = P.compare_masks(gmask, keep, qbar, kbar, wl, thr_h, band=band)
+    P.record_masks(f"partial_{name}", rep)
+    assert P.mask_ok(rep), P.fmt(rep)
+    orp, oci = oracle.csr_from_mask(keep != 0)
+    out, lse = P.gpu_forward(wl, qd, kd, vd, orp, oci)
+    rows = np.arange(wl.heads * wl.blocks)
+    err, lerr = P.compare_rows(wl, out, lse, q, k, v, orp, oci, rows)
+    print(f"forward max|err|={err:.3e} lse max|err|={lerr:.3e}", flush=True)
+    tol = P.TOL[dt] if reading == "A" or dt == "bf16" else 1e-3
+    assert err <= tol and lerr <= (P.LSE_TOL[dt] if reading == "A" or dt == "bf16" else 1e-3)
+    valid = torch.as_tensor(P.valid_of(wl))
+    assert torch.all(out.cpu()[..., ~valid, :] == 0)
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64)])
+def test_partial_tiles_reorder_and_raster_selection(dt, d):
+    """to_tiles / from_tiles on a grid with partial tiles are bit-exact against the
+    oracle's index map (zeros in the padding slots), and the selection on raster inputs
+    writes the same tile-major copies and keeps the oracle's blocks."""
+    wl = small_workload("partial_raster", 2, d, (0, 0, 0), dt, threshold=0.85, seed=72, grid=(3, 11, 21))
+    q, k, _, thr = make_inputs(wl, "A")
+    shape = P.shape_for(wl)
+    qr = torch.as_tensor(oracle.from_tiles(q, wl.grid, wl.tile)).cuda()
+    kr = torch.as_tensor(oracle.from_tiles(k, wl.grid, wl.tile)).cuda()
+    qt = B.sparse_attn_to_tiles(shape, qr)
+    back = B.sparse_attn_from_tiles(shape, qt)
+    torch.cuda.synchronize()
+    assert torch.equal(qt.cpu(), torch.as_tensor(oracle.to_tiles(qr.cpu(), wl.grid, wl.tile)))
+    assert torch.equal(qt.cpu(), q) and torch.equal(back, qr)
+    rp, ci, qt2, kt2 = B.sparse_attn_select_raster(shape, qr, kr, threshold=float(np.float32(wl.threshold)))
+    torch.cuda.synchronize()
+    assert torch.equal(qt2.cpu(), q) and torch.equal(kt2.cpu(), k)
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    gmask = P.check_csr(rp_h, ci[:int(rp_h[-1])].cpu().numpy(), wl.blocks)
+    qbar, kbar, keep, band = P.oracle_select_full(wl, q, k, thr, count_band=True)
+    rep = P.compare_masks(gmask, keep, qbar, kbar, wl, thr, band=band)
+    P.record_masks(f"partial_raster_{dt}", rep)
+    assert P.mask_ok(rep), P.fmt(rep)
