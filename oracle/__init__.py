@@ -51,8 +51,8 @@ def _load():
         I = ctypes.c_int64
         D = ctypes.c_double
         lib.oracle_pool.argtypes = [P, I, I, I, P, I, P]
-        lib.oracle_select_rows.argtypes = [P, P, I, I, I, P, I, D, P, I, I, I, I, I, I, P, P, P]
-        lib.oracle_attention_rows.argtypes = [P, P, P, I, I, I, P, P, P, P, P, I, D, P, P, P]
+        lib.oracle_select_rows.argtypes = [P, P, I, I, I, I, P, I, D, P, I, I, I, I, I, I, P, P, P]
+        lib.oracle_attention_rows.argtypes = [P, P, P, I, I, I, I, P, P, P, P, P, I, D, P, P, P]
         lib.oracle_attention_backward.argtypes = [P, P, P, P, P, I, I, I, I, P, P, D, P, P, P]
         for f in (lib.oracle_pool, lib.oracle_select_rows, lib.oracle_attention_rows, lib.oracle_attention_backward):
             f.restype = None
@@ -106,13 +106,16 @@ def select_rows(qbar: np.ndarray, kbar: np.ndarray, heads: int, block_grid: Sequ
                 rows: Optional[np.ndarray] = None, stats: bool = False):
     """Reduced map, CDF cut and window for the listed rows.
 
-    qbar, kbar: pooled [B, H, nB, d] (fp64).  thresholds: scalar or [H].
-    Returns ``keep`` [nrows, nB] uint8 (bit 0: CDF rule, bit 1: window) and,
+    qbar: pooled [B, H, nB, d], kbar: pooled [B, H, nK, d] (fp64; nK == nB for the
+    square map, or the 4-token key blocks of AB-Attention's fine selection, where no
+    window applies).  thresholds: scalar or [H].
+    Returns ``keep`` [nrows, nK] uint8 (bit 0: CDF rule, bit 1: window) and,
     with ``stats``, the probabilities ``p`` and the exclusive CDF mass ``E``.
     """
     qbar = np.ascontiguousarray(qbar, dtype=np.float64)
     kbar = np.ascontiguousarray(kbar, dtype=np.float64)
     *lead, nB, d = qbar.shape
+    nK = kbar.shape[-2]
     bh = int(np.prod(lead, dtype=np.int64))
     nT, nTy, nTx = (int(g) for g in block_grid)
     if nT * nTy * nTx != nB:
@@ -123,12 +126,12 @@ def select_rows(qbar: np.ndarray, kbar: np.ndarray, heads: int, block_grid: Sequ
     if rows is None:
         rows = np.arange(bh * nB, dtype=np.int64)
     rows = np.ascontiguousarray(rows, dtype=np.int64)
-    keep = np.zeros((len(rows), nB), dtype=np.uint8)
-    p = np.empty((len(rows), nB), dtype=np.float64) if stats else None
-    E = np.empty((len(rows), nB), dtype=np.float64) if stats else None
+    keep = np.zeros((len(rows), nK), dtype=np.uint8)
+    p = np.empty((len(rows), nK), dtype=np.float64) if stats else None
+    E = np.empty((len(rows), nK), dtype=np.float64) if stats else None
     sc = default_scale(d) if scale is None else float(scale)
     wt, wh, ww = (int(w) for w in window)
-    _load().oracle_select_rows(_ptr(qbar), _ptr(kbar), heads, nB, d, _ptr(rows), len(rows), sc,
+    _load().oracle_select_rows(_ptr(qbar), _ptr(kbar), heads, nB, nK, d, _ptr(rows), len(rows), sc,
                                _ptr(thr), nT, nTy, nTx, wt, wh, ww, _ptr(keep), _ptr(p), _ptr(E))
     if stats:
         return keep, p, E
@@ -239,7 +242,8 @@ def select(q, k, heads: int, block_grid, thresholds, window=(-1, -1, -1), scale=
 
 
 def attention_rows(q, k, v, row_ptr, col_idx, rows, scale: Optional[float] = None,
-                   tpb: int = TOKENS_PER_BLOCK, weights: bool = False, bias=None, valid=None):
+                   tpb: int = TOKENS_PER_BLOCK, weights: bool = False, bias=None, valid=None,
+                   key_tokens: Optional[int] = None):
     """Exact attention of every token of the listed query-block rows over its kept tiles.
 
     q, k, v: [B, H, N, d]; row_ptr/col_idx: CSR over rows r = bh * nB + i.
@@ -247,7 +251,8 @@ def attention_rows(q, k, v, row_ptr, col_idx, rows, scale: Optional[float] = Non
     the per-token weight sums with ``weights``.  ``bias``: optional logit offset per
     col_idx entry, added to the scaled logits of all keys of that block.  ``valid``:
     [N] bool, the token slots that are not padding (partial tiles); padding keys get no
-    weight and padding queries O = 0, LSE = -inf.
+    weight and padding queries O = 0, LSE = -inf.  ``key_tokens``: tokens per key block
+    (default tpb; 4 for AB-Attention's 4-token key blocks, col_idx then indexing them).
     """
     q, k, v = _f32(q), _f32(k), _f32(v)
     *lead, n, d = q.shape
@@ -263,8 +268,34 @@ def attention_rows(q, k, v, row_ptr, col_idx, rows, scale: Optional[float] = Non
     ws = np.empty((len(rows), tpb), dtype=np.float64) if weights else None
     sc = default_scale(d) if scale is None else float(scale)
     vb = _valid(valid, n)
-    _load().oracle_attention_rows(_ptr(q), _ptr(k), _ptr(v), nB, tpb, d, _ptr(rp), _ptr(ci), _ptr(b), _ptr(vb),
+    tk = tpb if key_tokens is None else int(key_tokens)
+    if n % tk or (vb is not None and tk != tpb):
+        raise ValueError("key blocks must tile the tokens (and padding needs whole tiles as key blocks)")
+    _load().oracle_attention_rows(_ptr(q), _ptr(k), _ptr(v), nB, tpb, tk, d, _ptr(rp), _ptr(ci), _ptr(b), _ptr(vb),
                                   _ptr(rows), len(rows), sc, _ptr(out), _ptr(lse), _ptr(ws))
     if weights:
         return out, lse, ws
     return out, lse
+
+
+# ---------------------------------------------------------------- AB-Attention's fine selection
+KEY_BLOCK_4 = 4
+
+
+def select_fine(q, k, heads: int, thresholds, key_tokens: int = KEY_BLOCK_4, scale=None, stats: bool = False):
+    """AB-Attention page, section "Les trois techniques d'AB-Attention", third technique:
+    key blocks of `key_tokens` (4) tokens, selected per 64-token query block.  Reading:
+    the query blocks are NABLA's 64-token means, the key blocks the means of `key_tokens`
+    consecutive tile-major tokens (half a row of an 8 x 8 tile); each row is the softmax
+    of the pooled scores over all key blocks of the head, cut by NABLA's CDF rule.
+    Returns (keep bool [B*H*nB, nK], row_ptr, col_idx) -- col_idx indexes key blocks --
+    plus (p, E) with ``stats``."""
+    qbar = pool(q)
+    kbar = pool(k, tpb=key_tokens)
+    *lead, nB, _ = qbar.shape
+    r = select_rows(qbar, kbar, heads, (1, 1, nB), thresholds, (-1, -1, -1), scale, stats=stats)
+    keep = (r[0] if stats else r) != 0
+    row_ptr, col_idx = csr_from_mask(keep)
+    if stats:
+        return keep, row_ptr, col_idx, r[1], r[2]
+    return keep, row_ptr, col_idx

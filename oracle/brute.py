@@ -46,16 +46,18 @@ def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
     return (e / z) @ v, (m + np.log(z))[..., 0]
 
 
-def token_mask_attention(q, k, v, block_mask: np.ndarray, scale: float, tpb: int = 64):
+def token_mask_attention(q, k, v, block_mask: np.ndarray, scale: float, tpb: int = 64, key_tokens=None):
     """Masked dense attention with the block mask expanded to tokens (fp64).
 
-    q, k, v: [N, d] for one head; block_mask: [nB, nB] bool.
+    q, k, v: [N, d] for one head; block_mask: [nB, nK] bool, query blocks of tpb
+    tokens, key blocks of key_tokens (default tpb) tokens.
     Rows with no allowed key give O = 0 and LSE = -inf.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
-    tok = np.kron(np.asarray(block_mask, dtype=np.int8), np.ones((tpb, tpb), dtype=np.int8)).astype(bool)
+    tk = tpb if key_tokens is None else key_tokens
+    tok = np.kron(np.asarray(block_mask, dtype=np.int8), np.ones((tpb, tk), dtype=np.int8)).astype(bool)
     s = np.where(tok, (q @ k.T) * scale, -np.inf)
     out = np.zeros((q.shape[0], v.shape[1]))
     lse = np.full(q.shape[0], -np.inf)

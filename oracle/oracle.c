@@ -79,13 +79,16 @@ static int by_prob_desc(const void *a, const void *b)
 /*
  * Attention Reduite + Seuil CDF + union with the window, for a list of rows.
  *
- * qbar, kbar: pooled vectors [BH][nB][d] (fp64).  A row index r = bh * nB + i
- * names query block i of batch-head bh; its head is bh % H.
+ * qbar: pooled query blocks [BH][nB][d], kbar: pooled key blocks [BH][nK][d] (fp64;
+ * nK == nB for NABLA's square map, nK = 16 nB for AB-Attention's 4-token key blocks,
+ * "Les trois techniques d'AB-Attention", third technique).  A row index
+ * r = bh * nB + i names query block i of batch-head bh; its head is bh % H.  The
+ * window applies to the square map only.
  * keep[k][j] (k-th listed row) receives bit 0 when the CDF rule keeps j and
  * bit 1 when the window contains j.  p_out / E_out (optional, [nrows][nB])
  * receive the row's probabilities and the exclusive mass E(j) in CDF order.
  */
-void oracle_select_rows(const double *qbar, const double *kbar, int64_t H, int64_t nB, int64_t d,
+void oracle_select_rows(const double *qbar, const double *kbar, int64_t H, int64_t nB, int64_t nK, int64_t d,
                         const int64_t *rows, int64_t nrows, double scale, const double *thr_head,
                         int64_t nT, int64_t nTy, int64_t nTx, int64_t wt, int64_t wh, int64_t ww,
                         uint8_t *keep, double *p_out, double *E_out)
@@ -93,50 +96,50 @@ void oracle_select_rows(const double *qbar, const double *kbar, int64_t H, int64
     (void)nT;
 #pragma omp parallel
     {
-        double *s = (double *)malloc(sizeof(double) * (size_t)nB);
-        prob_idx *ord = (prob_idx *)malloc(sizeof(prob_idx) * (size_t)nB);
+        double *s = (double *)malloc(sizeof(double) * (size_t)nK);
+        prob_idx *ord = (prob_idx *)malloc(sizeof(prob_idx) * (size_t)nK);
 #pragma omp for schedule(dynamic, 4)
         for (int64_t k = 0; k < nrows; ++k) {
             const int64_t r = rows[k];
             const int64_t bh = r / nB, i = r % nB;
             const double thr = thr_head[bh % H];
             const double *qi = qbar + (bh * nB + i) * d;
-            uint8_t *kr = keep + k * nB;
+            uint8_t *kr = keep + k * nK;
 
             /* reduced attention map row: scaled dot products, then a softmax over all key blocks */
             double mx = -INFINITY;
-            for (int64_t j = 0; j < nB; ++j) {
-                const double *kj = kbar + (bh * nB + j) * d;
+            for (int64_t j = 0; j < nK; ++j) {
+                const double *kj = kbar + (bh * nK + j) * d;
                 double acc = 0.0;
                 for (int64_t c = 0; c < d; ++c) acc += qi[c] * kj[c];
                 s[j] = acc * scale;
                 if (s[j] > mx) mx = s[j];
             }
             double z = 0.0;
-            for (int64_t j = 0; j < nB; ++j) {
+            for (int64_t j = 0; j < nK; ++j) {
                 s[j] = exp(s[j] - mx);
                 z += s[j];
             }
-            for (int64_t j = 0; j < nB; ++j) s[j] /= z;
+            for (int64_t j = 0; j < nK; ++j) s[j] /= z;
 
             /* CDF: walk the blocks from the most probable; keep while the mass before is below thr */
-            for (int64_t j = 0; j < nB; ++j) {
+            for (int64_t j = 0; j < nK; ++j) {
                 ord[j].p = s[j];
                 ord[j].j = j;
             }
-            qsort(ord, (size_t)nB, sizeof(prob_idx), by_prob_desc);
+            qsort(ord, (size_t)nK, sizeof(prob_idx), by_prob_desc);
             double before = 0.0;
-            for (int64_t n = 0; n < nB; ++n) {
+            for (int64_t n = 0; n < nK; ++n) {
                 const int64_t j = ord[n].j;
                 kr[j] = (thr >= 1.0 || before < thr) ? 1 : 0;
-                if (E_out) E_out[k * nB + j] = before;
+                if (E_out) E_out[k * nK + j] = before;
                 before += ord[n].p;
             }
             if (p_out)
-                for (int64_t j = 0; j < nB; ++j) p_out[k * nB + j] = s[j];
+                for (int64_t j = 0; j < nK; ++j) p_out[k * nK + j] = s[j];
 
             /* static window around the query block, in block coordinates (t, y, x) */
-            if (wt >= 0 && wh >= 0 && ww >= 0) {
+            if (wt >= 0 && wh >= 0 && ww >= 0 && nK == nB) {
                 const int64_t ti = i / (nTy * nTx), yi = (i / nTx) % nTy, xi = i % nTx;
                 for (int64_t j = 0; j < nB; ++j) {
                     const int64_t tj = j / (nTy * nTx), yj = (j / nTx) % nTy, xj = j % nTx;
@@ -153,7 +156,9 @@ void oracle_select_rows(const double *qbar, const double *kbar, int64_t H, int64
 /*
  * Exact attention over the kept tiles (Expansion): for every token n of query
  * block i, softmax over all tokens of the key blocks listed in the CSR row of
- * (bh, i), then the weighted sum of V.
+ * (bh, i), then the weighted sum of V.  Query blocks hold tpb tokens, key blocks
+ * tk (tk == tpb for NABLA's tiles; tk = 4 for AB-Attention's 4-token key blocks,
+ * whose kept blocks the kernel gathers into full tiles).
  *
  * q, k, v: [BH][nB*tpb][d] float32 (the exact values the GPU sees).
  * row_ptr/col_idx: CSR over rows r = bh * nB + i.  For each listed row, out
@@ -167,7 +172,7 @@ void oracle_select_rows(const double *qbar, const double *kbar, int64_t H, int64
  * valid (optional, [nB * tpb], the same for every head): padding tokens of partial
  * tiles take no part as keys, and a padding query token gets O = 0, LSE = -inf.
  */
-void oracle_attention_rows(const float *q, const float *k, const float *v, int64_t nB, int64_t tpb,
+void oracle_attention_rows(const float *q, const float *k, const float *v, int64_t nB, int64_t tpb, int64_t tk,
                            int64_t d, const int64_t *row_ptr, const int32_t *col_idx,
                            const double *col_bias, const uint8_t *valid, const int64_t *rows, int64_t nrows,
                            double scale, double *out, double *lse, double *w_sum)
@@ -185,7 +190,7 @@ void oracle_attention_rows(const float *q, const float *k, const float *v, int64
                 const float *qn = q + (bh * N + i * tpb + t) * d;
                 const int64_t beg = row_ptr[r], end = row_ptr[r + 1];
                 double *o = out + (kr * tpb + t) * d;
-                const int64_t m_count = (end - beg) * tpb;
+                const int64_t m_count = (end - beg) * tk;
                 if (m_count == 0 || (valid && !valid[i * tpb + t])) {
                     for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
                     lse[kr * tpb + t] = -INFINITY;
@@ -196,12 +201,12 @@ void oracle_attention_rows(const float *q, const float *k, const float *v, int64
                 int64_t m = 0;
                 for (int64_t e = beg; e < end; ++e) {
                     const int64_t j = col_idx[e];
-                    for (int64_t u = 0; u < tpb; ++u, ++m) {
-                        if (valid && !valid[j * tpb + u]) {        /* padding key: no weight */
+                    for (int64_t u = 0; u < tk; ++u, ++m) {
+                        if (valid && !valid[j * tk + u]) {          /* padding key: no weight */
                             logit[m] = -INFINITY;
                             continue;
                         }
-                        const float *km = k + (bh * N + j * tpb + u) * d;
+                        const float *km = k + (bh * N + j * tk + u) * d;
                         double a = 0.0;
                         for (int64_t c = 0; c < d; ++c) a += (double)qn[c] * (double)km[c];
                         logit[m] = a * scale + (col_bias ? col_bias[e] : 0.0);
@@ -218,8 +223,8 @@ void oracle_attention_rows(const float *q, const float *k, const float *v, int64
                 m = 0;
                 for (int64_t e = beg; e < end; ++e) {
                     const int64_t j = col_idx[e];
-                    for (int64_t u = 0; u < tpb; ++u, ++m) {
-                        const float *vm = v + (bh * N + j * tpb + u) * d;
+                    for (int64_t u = 0; u < tk; ++u, ++m) {
+                        const float *vm = v + (bh * N + j * tk + u) * d;
                         const double w = logit[m] / z;
                         wsum += w;
                         for (int64_t c = 0; c < d; ++c) acc[c] += w * (double)vm[c];

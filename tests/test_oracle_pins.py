@@ -859,3 +859,62 @@ def test_whole_tiles_need_no_padding():
     assert (perm >= 0).all() and len(perm) == 2 * 16 * 24
     x = _rand((1, len(perm), 4), 66)
     assert np.array_equal(oracle.pool(x), oracle.pool(x, valid=oracle.token_valid(grid, tile)))
+
+
+
+# ---------------------------------------------------------------- 4-token key blocks (AB-Attention)
+# AB-Attention page, "Les trois techniques d'AB-Attention", third technique: key and
+# value blocks of 4 tokens, the kept ones gathered by index into full tiles.
+
+def test_four_token_blocks_of_a_whole_tile_equal_the_tile():
+    """Listing all 16 four-token blocks of a 64-token tile gives the same attention as
+    listing the tile itself."""
+    rng = np.random.default_rng(81)
+    nB, d = 6, 32
+    q, k, v = (_rand((1, 2, nB * 64, d), s) for s in (82, 83, 84))
+    mask = rng.random((2 * nB, nB)) < 0.5
+    mask[:, 0] = True
+    rp, ci = oracle.csr_from_mask(mask)
+    fine = np.repeat(mask, 16, axis=1)                      # block j -> sub-blocks 16 j .. 16 j + 15
+    rp4, ci4 = oracle.csr_from_mask(fine)
+    rows = np.arange(2 * nB)
+    o, l = oracle.attention_rows(q, k, v, rp, ci, rows)
+    o4, l4 = oracle.attention_rows(q, k, v, rp4, ci4, rows, key_tokens=4)
+    assert np.allclose(o4, o, rtol=0, atol=1e-12) and np.allclose(l4, l, rtol=0, atol=1e-12)
+
+
+def test_four_token_gather_matches_token_mask_bruteforce():
+    rng = np.random.default_rng(85)
+    nB, d = 5, 16
+    q, k, v = (_rand((1, 1, nB * 64, d), s) for s in (86, 87, 88))
+    mask = rng.random((nB, nB * 16)) < 0.3
+    mask[2] = False                                          # an empty row
+    rp, ci = oracle.csr_from_mask(mask)
+    sc = 1.0 / math.sqrt(d)
+    out, lse = oracle.attention_rows(q, k, v, rp, ci, np.arange(nB), scale=sc, key_tokens=4)
+    ref, ref_lse = brute.token_mask_attention(q[0, 0], k[0, 0], v[0, 0], mask, sc, tpb=64, key_tokens=4)
+    assert np.allclose(out.reshape(-1, d), ref, rtol=0, atol=1e-12)
+    assert np.array_equal(np.isneginf(lse.reshape(-1)), np.isneginf(ref_lse))
+    fin = np.isfinite(ref_lse)
+    assert np.allclose(lse.reshape(-1)[fin], ref_lse[fin], rtol=0, atol=1e-12)
+
+
+def test_fine_selection_against_pairwise_cdf():
+    """The rows of the 4-token selection are the CDF rule (pairwise brute force) on the
+    softmax of 64-token query means against 4-token key means, both taken here by
+    reshape-means; thr >= 1 keeps every key block."""
+    nB, d, H = 4, 16, 2
+    q = _rand((1, H, nB * 64, d), 89, 0.5)
+    k = _rand((1, H, nB * 64, d), 90, 0.5)
+    thr = np.array([0.6, 0.85])
+    keep, rp, ci = oracle.select_fine(q, k, H, thr)
+    assert keep.shape == (H * nB, nB * 16)
+    qb = q.astype(np.float64).reshape(H, nB, 64, d).mean(axis=2)
+    kb = k.astype(np.float64).reshape(H, nB * 16, 4, d).mean(axis=2)
+    for h in range(H):
+        s = qb[h] @ kb[h].T / math.sqrt(d)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        for i in range(nB):
+            assert np.array_equal(keep[h * nB + i], brute.cdf_keep_pairwise(p[i], thr[h]).astype(bool))
+    assert oracle.select_fine(q, k, H, 1.0)[0].all()
