@@ -37,6 +37,7 @@ EXPORTED = (
     "sparse_attn_select_ibcs",
     "sparse_attn_forward",
     "sparse_attn_forward_biased",
+    "sparse_attn_forward_gather",
     "sparse_attn_mask_to_csr",
     "sparse_attn_radial_csr",
     "sparse_attn_backward",
@@ -111,6 +112,8 @@ def lib():
         L.sparse_attn_forward.argtypes = [SP, P, P, P, P, P, I64, P, P, P, I64, P]
         L.sparse_attn_forward.restype = ctypes.c_int32
         L.sparse_attn_forward_biased.argtypes = [SP, P, P, P, P, P, P, I64, P, P, P, I64, P]
+        L.sparse_attn_forward_gather.argtypes = [SP, P, P, P, P, P, I64, P, P, P, I64, P]
+        L.sparse_attn_forward_gather.restype = ctypes.c_int32
         L.sparse_attn_forward_biased.restype = ctypes.c_int32
         L.sparse_attn_mask_to_csr.argtypes = [SP, P, P, P, I64, P, I64, P]
         L.sparse_attn_mask_to_csr.restype = ctypes.c_int32
@@ -403,6 +406,30 @@ def sparse_attn_forward(shape: Shape, q, k, v, row_ptr, col_idx, out=None, lse=N
                                    col_idx.numel(), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                    _stream(stream))
     _check(st, "sparse_attn_forward")
+    return (out, lse) if (want_lse or lse is not None) else out
+
+
+def sparse_attn_forward_gather(shape: Shape, q, k, v, row_ptr, col_idx, out=None, lse=None, want_lse: bool = False,
+                               workspace=None, stream=None):
+    """Block-sparse attention over 4-token key blocks (col_idx in [0, 16 nB)), gathered
+    into full tiles by the kernel; returns out (and lse when requested)."""
+    import torch
+    dev = _req_tokens(shape, q=q, k=k, v=v)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        B, H, N, _ = q.shape
+        lse = torch.empty(B, H, N, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(sparse_attn_workspace_size(shape), dtype=torch.uint8, device=q.device)
+    _req_tokens(shape, q=q, out=out)
+    _req_csr(shape, row_ptr, col_idx, dev)
+    _req_lse(shape, lse, dev)
+    _req_workspace(workspace, dev)
+    st = lib().sparse_attn_forward_gather(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr), _ptr(col_idx),
+                                          col_idx.numel(), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                          _stream(stream))
+    _check(st, "sparse_attn_forward_gather")
     return (out, lse) if (want_lse or lse is not None) else out
 
 

@@ -16,6 +16,7 @@ namespace {
 using namespace sattn;
 
 constexpr int64_t kAlign = 256;
+constexpr int64_t kFineBlocks = 16;     // 4-token key blocks per 64-token tile
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -405,9 +406,11 @@ int32_t sparse_attn_select_raster(const sparse_attn_shape *shape, const sparse_a
 }  // extern "C"
 
 namespace {
+// kpt: key blocks per 64-key tile named by col_idx (1: tiles; 16: 4-token blocks,
+// gathered into tiles by the bf16 kernel).
 int32_t forward_impl(const sparse_attn_shape *shape, const void *q, const void *k, const void *v,
                      const int32_t *row_ptr, const int32_t *col_idx, const float *col_bias, int64_t col_count,
-                     void *out, float *lse, void *workspace, int64_t workspace_bytes, void *stream) {
+                     void *out, float *lse, void *workspace, int64_t workspace_bytes, void *stream, int32_t kpt = 1) {
     Dims d;
     int32_t st = check_shape(shape, &d);
     if (st) return st;
@@ -434,6 +437,8 @@ int32_t forward_impl(const sparse_attn_shape *shape, const void *q, const void *
     a.pair_stride = d.nT >= 2 ? (int32_t)(d.nTy * d.nTx) : 1;   // frame-neighbour pairs
     a.n_pairs = n_pairs(d);
     a.nB = (int32_t)d.nB;
+    a.nK = (int32_t)(d.nB * kpt);
+    a.kpt = kpt;
     a.scale_log2 = effective_scale(shape) * kLog2e;
     char *ws = (char *)workspace;
     a.plan.items = (SplitItem *)(ws + L.items);
@@ -462,6 +467,18 @@ int32_t sparse_attn_forward(const sparse_attn_shape *shape, const void *q, const
                             float *lse, void *workspace, int64_t workspace_bytes, void *stream) {
     return forward_impl(shape, q, k, v, row_ptr, col_idx, nullptr, col_count, out, lse, workspace, workspace_bytes,
                         stream);
+}
+
+int32_t sparse_attn_forward_gather(const sparse_attn_shape *shape, const void *q, const void *k, const void *v,
+                                   const int32_t *row_ptr, const int32_t *col_idx, int64_t col_count, void *out,
+                                   float *lse, void *workspace, int64_t workspace_bytes, void *stream) {
+    Dims d;
+    const int32_t st = check_shape(shape, &d);
+    if (st) return st;
+    if (shape->dtype != SPARSE_ATTN_BF16 || d.partial) return SPARSE_ATTN_UNSUPPORTED;
+    if (d.nB * kFineBlocks > INT32_MAX) return SPARSE_ATTN_UNSUPPORTED;
+    return forward_impl(shape, q, k, v, row_ptr, col_idx, nullptr, col_count, out, lse, workspace, workspace_bytes,
+                        stream, kFineBlocks);
 }
 
 int32_t sparse_attn_forward_biased(const sparse_attn_shape *shape, const void *q, const void *k, const void *v,
@@ -778,3 +795,4 @@ int32_t sparse_attn_from_tiles(const sparse_attn_shape *shape, const void *src, 
 }
 
 }  // extern "C"
+

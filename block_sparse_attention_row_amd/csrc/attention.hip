@@ -101,17 +101,32 @@ __device__ __forceinline__ float tile_commit(const f32x16 *acc_s, float c, float
 }
 
 // Scores of a key tile whose block is cut by the grid edge (a partial tile): its
-// padding slots get -inf, so they take no weight.  km: bit u set for the slots that
-// are grid tokens; accumulator v of half kt of this lane holds key 32 kt + 8 (v / 4) +
+// padding slots get kMaskedScore, so they take no weight.  The value is finite: with
+// the running max still at -inf on a row's first tile, -inf - (-inf) would be NaN, and
+// the device code is compiled without NaN semantics (the first tile's rescale is
+// triggered by an infinite row sum instead).  km: bit u set for the slots that are
+// grid tokens; accumulator v of half kt of this lane holds key 32 kt + 8 (v / 4) +
 // 4 hh + v % 4 (the 32x32 MFMA output layout, keys along its rows).
+constexpr float kMaskedScore = -0x1p100f;
 __device__ __forceinline__ void mask_keys(f32x16 *sc, uint64_t km, int hh) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int key = 32 * kt + 8 * (v >> 2) + 4 * hh + (v & 3);
-            if (!((km >> key) & 1ull)) sc[kt][v] = -INFINITY;
+            if (!((km >> key) & 1ull)) sc[kt][v] = kMaskedScore;
         }
+}
+
+// Bit e of m (e < 16) set -> nibble e of the result all ones: the 4 keys of entry e
+// of a gathered tile.
+__device__ __forceinline__ uint64_t spread_nibbles(uint32_t m) {
+    uint64_t x = m & 0xffffu;
+    x = (x | (x << 24)) & 0x000000ff000000ffull;
+    x = (x | (x << 12)) & 0x000f000f000f000full;
+    x = (x | (x << 6)) & 0x0303030303030303ull;
+    x = (x | (x << 3)) & 0x1111111111111111ull;
+    return x * 0xfull;
 }
 
 // Scores of the next tile (MFMA) interleaved with the probabilities of the current
@@ -167,8 +182,21 @@ __device__ __forceinline__ void tile_scores_probs(const char *K, const bf16x8 *q
 // BIAS: every block-list entry carries a logit offset (col_bias, natural-log units)
 // that is added to the scores of its tile; the running max is then tracked in log2
 // units, including the offset.
-template <int D, bool BIAS>
+//
+// GATHER: the block list names 4-token key blocks (AB-Attention page, section "Les
+// trois techniques d'AB-Attention", third technique).  The pair walks the union of its
+// two rows 16 entries at a time, and the 16 blocks of a step are gathered by index
+// into one 64-key tile: each wave's direct loads cover 4 consecutive tile rows per
+// 16-row group, exactly one block, so a block's address is the load's scalar base
+// (no copy, no permutation of the tokens).  A wave masks the keys of entries its own
+// row does not keep, and those past the list's end.
+//
+// MASKED: the grid ends in partial tiles; the keys of their padding slots are masked
+// and padding queries get O = 0, LSE = -inf (a separate instantiation, so that the
+// plain walk carries none of it).
+template <int D, bool BIAS, bool GATHER, bool MASKED>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
+    static_assert(!(BIAS && GATHER) && !(GATHER && MASKED), "combinations that are not built");
     using G = TileGeo<D>;
     constexpr int ROWB = G::ROWB, SLOTS = G::SLOTS, RPI = G::RPI, IPW = G::IPW, NDT = G::NDT, TILEB = G::TILEB;
     __shared__ __attribute__((aligned(1024))) char Ks[2 * TILEB];
@@ -203,8 +231,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     int32_t blk_a, blk_b;
     pair_blocks((int32_t)(pair % a.pairs_per_head), a.pair_stride, a.nB, blk_a, blk_b);
     const int64_t N = (int64_t)a.nB * 64;
-    const char *kg = (const char *)a.k + bh * N * ROWB + 16 * wave * ROWB;
-    const char *vg = (const char *)a.v + bh * N * ROWB + 16 * wave * ROWB;
+    const char *kgh = (const char *)a.k + bh * N * ROWB, *vgh = (const char *)a.v + bh * N * ROWB;
+    const char *kg = kgh + 16 * wave * ROWB;
+    const char *vg = vgh + 16 * wave * ROWB;
     const_i32 *rp = (const_i32 *)a.row_ptr;
     const float c = a.scale_log2;
 
@@ -232,7 +261,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
             int m = -1;
             for (int64_t i = from + lane; i < to; i += 64) {
                 const int cc = a.col_idx[i];
-                if (cc >= 0 && cc < a.nB) m = cc > m ? cc : m;
+                if (cc >= 0 && cc < a.nK) m = cc > m ? cc : m;
             }
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1) {
@@ -269,19 +298,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     }
     const uint32_t ks0 = (uint32_t)(uintptr_t)(lds_char *)Ks + 16 * wave * ROWB;
     const uint32_t vs0 = (uint32_t)(uintptr_t)(lds_char *)Vs + 16 * wave * ROWB;
-    // (the column is wave-uniform by construction; readfirstlane states it for the
-    // scalar base operand of the direct load)
-    auto issue_k = [&](int col, int buf) {
-        const int64_t cu = __builtin_amdgcn_readfirstlane(col);
-#pragma unroll
-        for (int i = 0; i < IPW; ++i) dma16(ks0 + buf * TILEB + RPI * i * ROWB, voff[i], kg + cu * TILEB);
-    };
-    auto issue_v = [&](int col, int buf) {
-        const int64_t cu = __builtin_amdgcn_readfirstlane(col);
-#pragma unroll
-        for (int i = 0; i < IPW; ++i) dma16(vs0 + buf * TILEB + RPI * i * ROWB, voff[i], vg + cu * TILEB);
-    };
-
     // merged walk over the two rows' ascending lists (entries out of range or not
     // ascending are skipped).  Each row's upcoming entries sit in a VGPR window (lane
     // l holds entry base + l) read with v_readlane; the following window is loaded
@@ -313,7 +329,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
                 }
             }
             const int cc = __builtin_amdgcn_readlane(win, pos);
-            if (cc > last && cc < a.nB) return cc;
+            if (cc > last && cc < a.nK) return cc;
             ++pos;
         }
         return kNone;
@@ -346,14 +362,25 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     float m_run = -INFINITY, l_run = 0.f;
     FragOffsets<D> fo;
     fo.init(lane);
-    // partial tiles: the per-block slot masks the plan wrote (null when every tile is whole)
+    // partial tiles: the per-block slot masks the plan wrote
     auto mask_tile = [&](f32x16 *sc, int col) {
-        if (a.slot_mask != nullptr) {
+        if constexpr (MASKED) {
             const uint64_t km = a.slot_mask[__builtin_amdgcn_readfirstlane(col)];
             if (km != ~0ull) mask_keys(sc, km, hh);
         }
     };
 
+    if constexpr (!GATHER) {
+    auto issue_k = [&](int col, int buf) {
+        const int64_t cu = __builtin_amdgcn_readfirstlane(col);
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) dma16(ks0 + buf * TILEB + RPI * i * ROWB, voff[i], kg + cu * TILEB);
+    };
+    auto issue_v = [&](int col, int buf) {
+        const int64_t cu = __builtin_amdgcn_readfirstlane(col);
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) dma16(vs0 + buf * TILEB + RPI * i * ROWB, voff[i], vg + cu * TILEB);
+    };
     // tiles j (scores pending), j+1 (K resident), j+2 (lookahead)
     int col0, col1, col2;
     bool mine0, mine1, mine2;
@@ -424,12 +451,128 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         step(std::integral_constant<int, 1>{}, sb, sa);
     }
 
+    } else {
+    // The units of the gathered walk: chunks of up to 16 union entries, gathered into
+    // one tile each.
+    struct Unit {
+        int cols;         // lane e holds entry e's block (padded with the last one)
+        bool mine;        // this wave's row keeps some entry of the chunk
+        int n;            // entries in the chunk (0 past the end)
+        uint64_t km;      // keys of this wave's entries
+    };
+    auto next_unit = [&](Unit &u) {
+        {
+            u.n = 0;
+            u.cols = 0;
+            uint32_t my = 0;
+            int lastc = 0;
+            for (int e = 0; e < 16; ++e) {
+                int col;
+                bool mine;
+                float beta;
+                next_union(col, mine, beta);
+                if (col == kNone) break;
+                u.cols = lane == e ? col : u.cols;
+                my |= (uint32_t)mine << e;
+                lastc = col;
+                u.n = e + 1;
+            }
+            // entries past the chunk's end repeat its last block (in range and
+            // non-decreasing); their keys are masked
+            u.cols = lane >= u.n ? lastc : u.cols;
+            u.mine = my != 0;
+            u.km = spread_nibbles(my);
+        }
+    };
+    // direct loads of a unit into tile buffer buf
+    auto issue_u = [&](const char *gw, const char *gh, uint32_t lds0, const Unit &u, int buf) {
+        (void)gw;
+        if constexpr (RPI == 4) {
+            // load i of wave w covers tile rows 16 w + 4 i .. + 3: entry 4 w + i
+#pragma unroll
+            for (int i = 0; i < IPW; ++i) {
+                const int j = __builtin_amdgcn_readlane(u.cols, 4 * wave + i);
+                dma16(lds0 + buf * TILEB + RPI * i * ROWB, voff[i], gh + (int64_t)(4 * (j - i)) * ROWB);
+            }
+        } else {
+            // RPI == 8: load i covers entries 4 w + 2 i (lanes 0-31) and 4 w + 2 i + 1 (32-63)
+            static_assert(RPI == 8, "4-token entries per direct load");
+#pragma unroll
+            for (int i = 0; i < IPW; ++i) {
+                const int jlo = __builtin_amdgcn_readlane(u.cols, 4 * wave + 2 * i);
+                const int jhi = __builtin_amdgcn_readlane(u.cols, 4 * wave + 2 * i + 1);
+                const uint32_t v = voff[i] + (hh ? (uint32_t)(4 * (jhi - jlo - 1) * ROWB) : 0u);
+                dma16(lds0 + buf * TILEB + RPI * i * ROWB, v, gh + (int64_t)(4 * (jlo - 2 * i)) * ROWB);
+            }
+        }
+    };
+    auto live = [&](const Unit &u) { return u.n != 0; };
+    auto mask_u = [&](f32x16 *sc, const Unit &u) {
+        if (u.km != ~0ull) mask_keys(sc, u.km, hh);
+    };
+
+    // units j (scores pending), j+1 (K resident), j+2 (lookahead)
+    Unit u0, u1, u2;
+    next_unit(u0);
+    next_unit(u1);
+    f32x16 sa[2], sb[2];
+    if (live(u0)) {
+        issue_u(kg, kgh, ks0, u0, 0);
+        issue_u(vg, vgh, vs0, u0, 0);
+        if (live(u1)) issue_u(kg, kgh, ks0, u1, 1);
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (u0.mine) {
+            tile_scores<D>(Ks, qf, fo, sa);
+            mask_u(sa, u0);
+        }
+    }
+    // One pipeline step for unit j with j & 1 == BJ: the scores of unit j are in sc,
+    // those of unit j+1 go to sn; buffer offsets are compile-time constants.
+    auto step = [&](auto bj_tag, f32x16 *sc, f32x16 *sn) {
+        constexpr int BJ = decltype(bj_tag)::value;
+        wait_vmcnt<0>();            // this wave's part of K(j+1) and V(j) has landed
+        next_unit(u2);              // (after the wait: a window load never waits on tile loads)
+        __syncthreads();            // ... and everyone's; K(j) and V(j-1) are free
+        if (live(u2)) issue_u(kg, kgh, ks0, u2, BJ);
+        if (live(u1)) issue_u(vg, vgh, vs0, u1, BJ ^ 1);
+
+        const bool mine0 = u0.mine, mine1 = u1.mine;
+        float lt = 0.f;
+        const float mc = mine0 ? m_run * c : 0.f;
+        bf16x8 pf[4];
+        float &lacc = lt;
+        if (mine0 && mine1) {
+            tile_scores_probs<D>(Ks + (BJ ^ 1) * TILEB, qf, fo, sn, sc, c, mc, lacc, pf);
+        } else if (mine1) {
+            tile_scores<D>(Ks + (BJ ^ 1) * TILEB, qf, fo, sn);
+        } else if (mine0) {
+            tile_probs(sc, c, mc, lacc, pf);
+        }
+        if (mine1) mask_u(sn, u1);
+        if (mine0) l_run += tile_commit<NDT>(sc, c, m_run, l_run, lt, acc_o, pf);
+        // P V is MFMA work only: the wave runs it at raised priority, so that the
+        // SIMD's other wave fills the matrix unit's gaps with its softmax instead of
+        // delaying these MFMAs
+        __builtin_amdgcn_s_setprio(1);
+        if (mine0) tile_pv<D>(Vs + BJ * TILEB, pf, fo, acc_o);
+        __builtin_amdgcn_s_setprio(0);
+        u0 = u1;
+        u1 = u2;
+    };
+    while (live(u0)) {
+        step(std::integral_constant<int, 0>{}, sa, sb);
+        if (!live(u0)) break;
+        step(std::integral_constant<int, 1>{}, sb, sa);
+    }
+
+    }
     if (!has_row) return;
     // epilogue: normalise and store; lane owns query l32, d = 32 dt + 8 rr + 4 hh + {0..3}.
     // A padding slot of a partial tile gets O = 0 and LSE = -inf.
     const float l_tot = pair_sum(l_run);
-    const bool qvalid =
-        a.slot_mask == nullptr || ((a.slot_mask[blk] >> (32 * (wave & 1) + l32)) & 1ull);
+    bool qvalid = true;
+    if constexpr (MASKED) qvalid = (a.slot_mask[blk] >> (32 * (wave & 1) + l32)) & 1ull;
     const float inv = (l_tot > 0.f && qvalid) ? 1.f / l_tot : 0.f;
     if (split) {
         // piece of a split pair: the normalised partial output and its log2-sum-exp
@@ -516,7 +659,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
     auto est_of = [&](int64_t p) {
         int64_t bA, eA, bB, eB;
         pair_ranges(a, p, bA, eA, bB, eB);
-        return max(eA - bA, eB - bB);
+        return (max(eA - bA, eB - bB) + a.kpt - 1) / a.kpt;   // tiles (gathered chunks of kpt entries)
     };
     int64_t tot = 0;
     for (int64_t p = t; p < a.n_pairs; p += 1024) tot += est_of(p);
@@ -540,7 +683,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
         int32_t ns = 0;
         if (p < a.n_pairs) {
             pair_ranges(a, p, bA, eA, bB, eB);
-            const int64_t e = max(eA - bA, eB - bB);
+            const int64_t e = (max(eA - bA, eB - bB) + a.kpt - 1) / a.kpt;
             ns = e > L ? (int32_t)((e + L - 1) / L) : 0;
         }
         int32_t tot_ns, tot_sp;
@@ -593,7 +736,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
             p = xcd_chunk_remap<256>(a.n_pairs - T + t, a.n_pairs);
             if (P.pair_flag[p] == 0) {
                 pair_ranges(a, p, bA, eA, bB, eB);
-                ns = max(eA - bA, eB - bB) >= 16 * kTailPieces ? kTailPieces : 0;
+                ns = max(eA - bA, eB - bB) >= (int64_t)16 * kTailPieces * a.kpt ? kTailPieces : 0;
             }
         }
         int32_t tot_ns, tot_sp;
@@ -822,14 +965,20 @@ int launch_attention(const AttnArgs &a, int dtype, int d, hipStream_t s) {
     const dim3 mgrid((unsigned)a.plan.max_slots), mblock(512);
     if (dtype == 1) {
         plan_kernel<<<1, 1024, 0, s>>>(a);
-        const bool bias = a.col_bias != nullptr;
+        const bool bias = a.col_bias != nullptr, gather = a.kpt > 1, masked = a.slot_mask != nullptr;
         if (d == 128) {
-            if (bias) attn_bf16_kernel<128, true><<<pgrid, pblock, 0, s>>>(a);
-            else attn_bf16_kernel<128, false><<<pgrid, pblock, 0, s>>>(a);
+            if (gather) attn_bf16_kernel<128, false, true, false><<<pgrid, pblock, 0, s>>>(a);
+            else if (bias && masked) attn_bf16_kernel<128, true, false, true><<<pgrid, pblock, 0, s>>>(a);
+            else if (bias) attn_bf16_kernel<128, true, false, false><<<pgrid, pblock, 0, s>>>(a);
+            else if (masked) attn_bf16_kernel<128, false, false, true><<<pgrid, pblock, 0, s>>>(a);
+            else attn_bf16_kernel<128, false, false, false><<<pgrid, pblock, 0, s>>>(a);
             merge_kernel<128><<<mgrid, mblock, 0, s>>>(a);
         } else {
-            if (bias) attn_bf16_kernel<64, true><<<pgrid, pblock, 0, s>>>(a);
-            else attn_bf16_kernel<64, false><<<pgrid, pblock, 0, s>>>(a);
+            if (gather) attn_bf16_kernel<64, false, true, false><<<pgrid, pblock, 0, s>>>(a);
+            else if (bias && masked) attn_bf16_kernel<64, true, false, true><<<pgrid, pblock, 0, s>>>(a);
+            else if (bias) attn_bf16_kernel<64, true, false, false><<<pgrid, pblock, 0, s>>>(a);
+            else if (masked) attn_bf16_kernel<64, false, false, true><<<pgrid, pblock, 0, s>>>(a);
+            else attn_bf16_kernel<64, false, false, false><<<pgrid, pblock, 0, s>>>(a);
             merge_kernel<64><<<mgrid, mblock, 0, s>>>(a);
         }
     } else if (dtype == 0 && d == 128)

@@ -480,6 +480,8 @@ int launch_backward(const BwdLaunch &L, hipStream_t s) {
         pa.n_pairs = w.n_pairs;
         pa.pairs_per_head = w.pairs_per_head;
         pa.nB = w.nB;
+        pa.nK = w.nB;
+        pa.kpt = 1;
         pa.pair_stride = w.pair_stride;
         pa.plan = w.plan;
         return launch_plan(pa, s);

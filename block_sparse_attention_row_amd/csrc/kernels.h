@@ -179,6 +179,8 @@ struct AttnArgs {
     int64_t n_pairs;          // B*H*pairs_per_head (query-block pairs of the bf16 kernel)
     int32_t pairs_per_head;   // ceil(nB / 2)
     int32_t nB;
+    int32_t nK;               // key blocks per head that col_idx may name: nB, or 16 nB for 4-token blocks
+    int32_t kpt;              // key blocks per 64-key tile: 1, or 16 (4-token blocks gathered into tiles)
     int32_t pair_stride;      // S of pair_blocks: blocks per frame, or 1
     float scale_log2;         // softmax scale * log2(e)
     SlotGeo geo;              // padding slots of partial tiles: no weight as keys, zero output as queries

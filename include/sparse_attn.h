@@ -263,6 +263,26 @@ int32_t sparse_attn_forward_biased(const sparse_attn_shape *shape, const void *q
                                    void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * sparse_attn_forward over a list of 4-token key blocks: AB-Attention's fine
+ * selection on coarse hardware (AB-Attention page, section "Les trois techniques
+ * d'AB-Attention", third technique): key and value blocks of 4 tokens, and the kernel
+ * gathers the kept ones by index into full 64-key tiles for the matrix cores, with no
+ * copy or permutation of the tokens.
+ *
+ *   row_ptr     as in sparse_attn_forward: one row per 64-token query block.
+ *   col_idx     device, int32 [col_count]: 4-token key-block indices in [0, 16 nB)
+ *               (key block j is tile-major tokens [4 j, 4 j + 4), half a row of an
+ *               8 x 8 tile), ascending per row; out-of-range, repeated or descending
+ *               entries are skipped as in sparse_attn_forward.
+ *   Everything else as in sparse_attn_forward: for each query token, the softmax over
+ *   the tokens of its row's 4-token blocks, applied to V.
+ * bf16 and whole tiles only (SPARSE_ATTN_UNSUPPORTED otherwise).
+ */
+int32_t sparse_attn_forward_gather(const sparse_attn_shape *shape, const void *q, const void *k, const void *v,
+                                   const int32_t *row_ptr, const int32_t *col_idx, int64_t col_count, void *out,
+                                   float *lse, void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
  * External block mask to CSR (the path that accepts a caller's mask, e.g. a
  * static window or a mask reused from an earlier step).
  *

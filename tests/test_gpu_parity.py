@@ -744,12 +744,18 @@ def test_partial_tiles_reorder_and_raster_selection(dt, d):
     wl = small_workload("partial_raster", 2, d, (0, 0, 0), dt, threshold=0.85, seed=72, grid=(3, 11, 21))
     q, k, _, thr = make_inputs(wl, "A")
     shape = P.shape_for(wl)
-    qr = torch.as_tensor(oracle.from_tiles(q, wl.grid, wl.tile)).cuda()
-    kr = torch.as_tensor(oracle.from_tiles(k, wl.grid, wl.tile)).cuda()
+    def moved(x, f):
+        # the oracle's index maps move bit patterns: bf16 travels as int16 (numpy has no bf16)
+        if x.dtype == torch.bfloat16:
+            return torch.as_tensor(f(x.view(torch.int16), wl.grid, wl.tile)).view(torch.bfloat16)
+        return torch.as_tensor(f(x, wl.grid, wl.tile))
+
+    qr = moved(q, oracle.from_tiles).cuda()
+    kr = moved(k, oracle.from_tiles).cuda()
     qt = B.sparse_attn_to_tiles(shape, qr)
     back = B.sparse_attn_from_tiles(shape, qt)
     torch.cuda.synchronize()
-    assert torch.equal(qt.cpu(), torch.as_tensor(oracle.to_tiles(qr.cpu(), wl.grid, wl.tile)))
+    assert torch.equal(qt.cpu(), moved(qr.cpu(), oracle.to_tiles))
     assert torch.equal(qt.cpu(), q) and torch.equal(back, qr)
     rp, ci, qt2, kt2 = B.sparse_attn_select_raster(shape, qr, kr, threshold=float(np.float32(wl.threshold)))
     torch.cuda.synchronize()
@@ -760,3 +766,68 @@ def test_partial_tiles_reorder_and_raster_selection(dt, d):
     rep = P.compare_masks(gmask, keep, qbar, kbar, wl, thr, band=band)
     P.record_masks(f"partial_raster_{dt}", rep)
     assert P.mask_ok(rep), P.fmt(rep)
+
+
+
+# ---------------------------------------------------------------- 4-token key blocks (AB-Attention)
+
+GATHER = [
+    # name, heads, d, block grid, thr, reading
+    ("d128", 2, 128, (2, 3, 4), 0.8, "A"),
+    ("d64_page", 3, 64, (3, 2, 5), 0.9, "page"),
+    ("d128_B_odd", 2, 128, (3, 3, 3), 0.9, "B"),
+]
+
+
+@pytest.mark.parametrize("case", GATHER, ids=[c[0] for c in GATHER])
+def test_gather_forward_matches_oracle(case):
+    """Attention over the oracle's 4-token key blocks, gathered into tiles by the kernel,
+    against the oracle's attention over the same blocks, every query block."""
+    name, H, d, bg, thr, reading = case
+    wl = small_workload("gather_" + name, H, d, bg, "bf16", threshold=thr, seed=91)
+    q, k, v, _ = make_inputs(wl, reading)
+    qd, kd, vd = P.to_device(q, k, v)
+    keep, orp, oci = oracle.select_fine(q, k, H, thr)
+    shape = P.shape_for(wl)
+    rp = torch.as_tensor(orp.astype(np.int32)).cuda()
+    ci = torch.as_tensor(oci).cuda()
+    out = torch.full_like(qd, float("nan"))
+    lse = torch.full(qd.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+    B.sparse_attn_forward_gather(shape, qd, kd, vd, rp, ci, out=out, lse=lse)
+    torch.cuda.synchronize()
+    rows = np.arange(H * wl.blocks)
+    ref, ref_lse = oracle.attention_rows(q, k, v, orp, oci, rows, key_tokens=4)
+    got = out.float().cpu().reshape(-1, 64, d).numpy()
+    got_l = lse.cpu().reshape(-1, 64).numpy()
+    err = float(np.abs(got - ref).max())
+    lerr = float(np.abs(got_l - ref_lse).max())
+    print(f"gather {name}: kept {int(keep.sum())} of {keep.size} 4-token blocks, max|err|={err:.3e} lse {lerr:.3e}",
+          flush=True)
+    assert err <= P.TOL["bf16"] and lerr <= P.LSE_TOL["bf16"]
+
+
+def test_gather_of_whole_tiles_equals_the_tile_forward():
+    """Listing all 16 four-token blocks of each kept tile gathers exactly the tile: the
+    output is bit-identical to the tile forward over the tile list.  Junk entries (out of
+    range, repeated, descending) are skipped as in the tile forward."""
+    wl = small_workload("gather_tiles", 2, 128, (3, 2, 4), "bf16", threshold=0.8, seed=92)
+    q, k, v, thr = make_inputs(wl, "A")
+    qd, kd, vd = P.to_device(q, k, v)
+    qbar, kbar, keep = P.oracle_select_full(wl, q, k, thr)
+    orp, oci = oracle.csr_from_mask(keep != 0)
+    out_t, lse_t = P.gpu_forward(wl, qd, kd, vd, orp, oci)
+    fine = np.repeat(keep != 0, 16, axis=1)
+    frp, fci = oracle.csr_from_mask(fine)
+    rows = len(frp) - 1
+    rp2, ci2 = [0], []
+    for r in range(rows):
+        seg = fci[frp[r]:frp[r + 1]].tolist()
+        ci2 += [-3] + seg[:1] + seg[:1] + seg[1:] + [seg[0], 16 * wl.blocks + 5]
+        rp2.append(len(ci2))
+    shape = P.shape_for(wl)
+    out_g = torch.full_like(qd, float("nan"))
+    lse_g = torch.full(qd.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+    B.sparse_attn_forward_gather(shape, qd, kd, vd, torch.as_tensor(np.array(rp2, np.int32)).cuda(),
+                                 torch.as_tensor(np.array(ci2, np.int32)).cuda(), out=out_g, lse=lse_g)
+    torch.cuda.synchronize()
+    assert torch.equal(out_g, out_t) and torch.equal(lse_g, lse_t)
