@@ -25,6 +25,8 @@ SPARSE_ATTN_CAPACITY = -3
 SPARSE_ATTN_WORKSPACE = -4
 SPARSE_ATTN_HIP_ERROR = -5
 SPARSE_ATTN_LOOKBACK_FAULT = -6
+SPARSE_ATTN_SCRATCH = -7
+SPARSE_ATTN_SCRATCH_BYTES = 96 << 20
 
 EXPORTED = (
     "sparse_attn_version",
@@ -45,6 +47,8 @@ EXPORTED = (
     "sparse_attn_to_tiles",
     "sparse_attn_from_tiles",
     "sparse_attn_select_raster",
+    "sparse_attn_select_noalloc",
+    "sparse_attn_select_noalloc_bytes",
 )
 
 
@@ -125,6 +129,10 @@ def lib():
         L.sparse_attn_full_csr.restype = ctypes.c_int32
         L.sparse_attn_select_raster.argtypes = [SP, ctypes.POINTER(SelectParams), P, P, P, P, P, P, I64, P, I64, P]
         L.sparse_attn_select_raster.restype = ctypes.c_int32
+        L.sparse_attn_select_noalloc.argtypes = [SP, ctypes.POINTER(SelectParams), P, P, P, P, I64, P]
+        L.sparse_attn_select_noalloc.restype = ctypes.c_int32
+        L.sparse_attn_select_noalloc_bytes.argtypes = [SP]
+        L.sparse_attn_select_noalloc_bytes.restype = I64
         for name in ("sparse_attn_to_tiles", "sparse_attn_from_tiles"):
             getattr(L, name).argtypes = [SP, P, P, P]
             getattr(L, name).restype = ctypes.c_int32
@@ -548,3 +556,25 @@ def sparse_attn_select_check(shape: Shape, workspace, stream=None) -> int:
     return int(lib().sparse_attn_select_check(ctypes.byref(shape), _ptr(workspace), workspace.numel(),
                                               _stream(stream)))
 
+
+def sparse_attn_select_noalloc_bytes(shape: Shape) -> int:
+    return int(lib().sparse_attn_select_noalloc_bytes(ctypes.byref(shape)))
+
+
+def sparse_attn_select_noalloc(shape: Shape, q, k, row_ptr, col_idx, threshold: float = 0.9,
+                               head_thresholds: Optional[Sequence[float]] = None, window=(-1, -1, -1),
+                               stream=None):
+    """The selection with its scratch in the library's static device array (no
+    workspace); writes the caller's row_ptr and col_idx (capacity B*H*nB*nB) and
+    returns them."""
+    dev = _req_tokens(shape, q=q, k=k)
+    _req_csr(shape, row_ptr, col_idx, dev, capacity=True)
+    ht = None
+    if head_thresholds is not None:
+        arr = (ctypes.c_float * shape.heads)(*[float(x) for x in head_thresholds])
+        ht = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
+    params = SelectParams(float(threshold), ht, *(int(w) for w in window))
+    st = lib().sparse_attn_select_noalloc(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k),
+                                          _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _stream(stream))
+    _check(st, "sparse_attn_select_noalloc")
+    return row_ptr, col_idx

@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "../../include/sparse_attn.h"
 #include "common.h"
 #include "kernels.h"
@@ -195,6 +197,7 @@ const char *sparse_attn_status_string(int32_t status) {
     case SPARSE_ATTN_WORKSPACE: return "workspace smaller than sparse_attn_workspace_size";
     case SPARSE_ATTN_HIP_ERROR: return "HIP kernel launch failed";
     case SPARSE_ATTN_LOOKBACK_FAULT: return "a selection gave up waiting in its CSR look-back; its block list is invalid";
+    case SPARSE_ATTN_SCRATCH: return "the shape needs more than the allocation-free selection's 96 MiB static scratch";
     default: return "unknown status";
     }
 }
@@ -796,3 +799,96 @@ int32_t sparse_attn_from_tiles(const sparse_attn_shape *shape, const void *src, 
 
 }  // extern "C"
 
+// ---------------------------------------------------------------------------
+// Allocation-free selection.  The CDF selection's scratch (thresholds, key block
+// means, look-back words, ticket and fault word) lives in a static device array
+// instead of a caller's workspace.  Each GPU holds its own copy of the array at its
+// own address, which hipGetSymbolAddress returns with that device current; host code
+// uses only that address (the array's name on the host is a stand-in, not a device
+// address).  Every call on one GPU shares its array; the pooling kernel clears the
+// look-back words, the ticket and the fault word at the start of each call.
+static __device__ __align__(256) unsigned char scratch[SPARSE_ATTN_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int64_t kScratchBytes = SPARSE_ATTN_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of the scratch array, looked up once per device.
+int32_t device_scratch(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SPARSE_ATTN_HIP_ERROR;
+    if (dev < 0 || dev >= kMaxDevices) return SPARSE_ATTN_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SPARSE_ATTN_HIP_ERROR;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SPARSE_ATTN_OK;
+}
+
+// The selection's part of the workspace, packed: thresholds, key means, look-back
+// words, ticket.
+struct ScratchLayout {
+    int64_t thr, kbar, kbar64, knorm, status, ticket, total;
+};
+ScratchLayout scratch_layout(const Dims &d) {
+    ScratchLayout l;
+    int64_t off = 0;
+    l.thr = off;
+    off = align_up(off + 4 * d.H, kAlign);
+    l.kbar = off;
+    off = align_up(off + 4 * d.B * d.H * groups_per_head(d) * kGroupRows * d.D, kAlign);
+    l.kbar64 = off;
+    off = align_up(off + 8 * d.B * d.H * d.nB * d.D, kAlign);
+    l.knorm = off;
+    off = align_up(off + 4 * d.B * d.H * d.nB, kAlign);
+    l.status = off;
+    off = align_up(off + 8 * n_groups(d), kAlign);
+    l.ticket = off;
+    off = align_up(off + 16, kAlign);
+    l.total = off;
+    return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t sparse_attn_select_noalloc_bytes(const sparse_attn_shape *shape) {
+    Dims d;
+    const int32_t st = check_shape(shape, &d);
+    if (st) return st;
+    return scratch_layout(d).total;
+}
+
+int32_t sparse_attn_select_noalloc(const sparse_attn_shape *shape, const sparse_attn_select_params *params,
+                                   const void *q, const void *k, int32_t *row_ptr, int32_t *col_idx,
+                                   int64_t col_capacity, void *stream) {
+    Dims d;
+    int32_t st = select_checks(shape, params, q, k, row_ptr, col_idx, col_capacity, nullptr, nullptr, d);
+    if (st) return st;
+    const ScratchLayout L = scratch_layout(d);
+    if (L.total > kScratchBytes) return SPARSE_ATTN_SCRATCH;
+    void *base = nullptr;
+    st = device_scratch(&base);
+    if (st) return st;
+    char *ws = (char *)base;
+    SelectScratch w;
+    w.thr = (float *)(ws + L.thr);
+    w.kbar = (__bf16 *)(ws + L.kbar);
+    w.qbar = nullptr;
+    w.kbar64 = (double *)(ws + L.kbar64);
+    w.qbar64 = nullptr;
+    w.knorm = (float *)(ws + L.knorm);
+    w.status = (uint64_t *)(ws + L.status);
+    w.ticket = (uint32_t *)(ws + L.ticket);
+    return select_launch(shape, params, d, q, k, row_ptr, col_idx, w, stream, nullptr, nullptr);
+}
+
+}  // extern "C"

@@ -66,7 +66,10 @@ extern "C" {
 #define SPARSE_ATTN_HIP_ERROR (-5)        /* a kernel launch failed                             */
 #define SPARSE_ATTN_LOOKBACK_FAULT (-6)   /* a selection gave up in its CSR look-back (see
                                              sparse_attn_select_check)                          */
+#define SPARSE_ATTN_SCRATCH (-7)          /* shape too large for sparse_attn_select_noalloc      */
 
+/* Size of the static device scratch of sparse_attn_select_noalloc (96 MiB). */
+#define SPARSE_ATTN_SCRATCH_BYTES (96ll << 20)
 
 /*
  * Problem shape.  head_dim must be 64 or 128; the tile must hold 64 tokens
@@ -392,6 +395,35 @@ int32_t sparse_attn_select_raster(const sparse_attn_shape *shape, const sparse_a
                                   const void *q, const void *k, void *q_tiles, void *k_tiles,
                                   int32_t *row_ptr, int32_t *col_idx, int64_t col_capacity,
                                   void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * sparse_attn_select without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  It computes exactly what sparse_attn_select computes, with the same
+ * kernels; their scratch (per-head thresholds, key block means, look-back words,
+ * ticket, and the exact fp64 key means with their norms) lives in a static device
+ * array of SPARSE_ATTN_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends.  The call allocates
+ * and frees nothing.
+ *
+ *   Arguments as in sparse_attn_select, minus the workspace.  The current device's
+ *   array is used, so `stream` must belong to the current device.
+ *   Returns SPARSE_ATTN_SCRATCH when the shape needs more scratch than the array
+ *   holds (sparse_attn_select_noalloc_bytes > SPARSE_ATTN_SCRATCH_BYTES; the
+ *   workloads of up to 12 heads x 3,840 blocks or 40 heads x 1,260 blocks at
+ *   d = 128 fit), and otherwise the statuses of sparse_attn_select.
+ *   All calls on one GPU share its array, which keeps the last call's contents:
+ *   calls that overlap on one GPU (different streams or threads without ordering
+ *   between them) race and must not be issued.  sparse_attn_select_check does not
+ *   apply (it reads a workspace).
+ */
+int32_t sparse_attn_select_noalloc(const sparse_attn_shape *shape, const sparse_attn_select_params *params,
+                                   const void *q, const void *k, int32_t *row_ptr, int32_t *col_idx,
+                                   int64_t col_capacity, void *stream);
+
+/* Bytes of the static scratch sparse_attn_select_noalloc needs for this shape, or a
+   negative status for an invalid shape. */
+int64_t sparse_attn_select_noalloc_bytes(const sparse_attn_shape *shape);
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert B.sparse_attn_version() == 10000
-    for st in (0, -1, -2, -3, -4, -5, -6):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert B.status_string(st) and B.status_string(st) != "unknown status"
     assert B.status_string(-99) == "unknown status"
 
@@ -380,6 +380,31 @@ def test_select_check_rejects_bad_arguments_on_the_host():
     bad = B.make_shape(1, 2, 96, (2, 8, 16), "bf16")
     assert L.sparse_attn_select_check(ctypes.byref(bad), 16, ws, None) == B.SPARSE_ATTN_UNSUPPORTED
     assert "look-back" in B.status_string(B.SPARSE_ATTN_LOOKBACK_FAULT)
+
+
+def test_noalloc_selection_rejects_what_its_scratch_cannot_hold():
+    """The allocation-free selection checks the shape against its static scratch on the
+    host: 64 heads of 3,840 blocks at d = 128 need ~380 MB of key means and are refused
+    with SPARSE_ATTN_SCRATCH before any HIP call (the pointers are never touched)."""
+    L = B.lib()
+    params = B.SelectParams(0.9, None, -1, -1, -1)
+    big = B.make_shape(1, 64, 128, (64, 48, 80), "bf16")
+    assert B.sparse_attn_select_noalloc_bytes(big) > B.SPARSE_ATTN_SCRATCH_BYTES
+    cap = B.sparse_attn_csr_capacity(big)
+    assert L.sparse_attn_select_noalloc(ctypes.byref(big), ctypes.byref(params), 16, 16, 16, 16, cap,
+                                        None) == B.SPARSE_ATTN_SCRATCH
+    # the five workloads fit
+    for grid, heads in (((20, 32, 48), 12), ((21, 48, 80), 40), ((32, 48, 80), 24), ((64, 48, 80), 12)):
+        s = B.make_shape(1, heads, 128, grid, "bf16")
+        assert 0 < B.sparse_attn_select_noalloc_bytes(s) <= B.SPARSE_ATTN_SCRATCH_BYTES
+    # the usual argument checks come first
+    small = _small()
+    assert L.sparse_attn_select_noalloc(ctypes.byref(small), ctypes.byref(params), None, 16, 16, 16,
+                                        B.sparse_attn_csr_capacity(small), None) == B.SPARSE_ATTN_INVALID_ARGUMENT
+    assert L.sparse_attn_select_noalloc(ctypes.byref(small), ctypes.byref(params), 16, 16, 16, 16,
+                                        B.sparse_attn_csr_capacity(small) - 1, None) == B.SPARSE_ATTN_CAPACITY
+    assert "static scratch" in B.status_string(B.SPARSE_ATTN_SCRATCH)
+
 
 
 def test_partial_tiles_size_by_ceil_grid():
