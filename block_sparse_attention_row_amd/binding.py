@@ -40,6 +40,9 @@ EXPORTED = (
     "sparse_attn_forward",
     "sparse_attn_forward_biased",
     "sparse_attn_forward_gather",
+    "sparse_attn_select_fine",
+    "sparse_attn_fine_csr_capacity",
+    "sparse_attn_fine_workspace_size",
     "sparse_attn_mask_to_csr",
     "sparse_attn_radial_csr",
     "sparse_attn_backward",
@@ -118,6 +121,12 @@ def lib():
         L.sparse_attn_forward_biased.argtypes = [SP, P, P, P, P, P, P, I64, P, P, P, I64, P]
         L.sparse_attn_forward_gather.argtypes = [SP, P, P, P, P, P, I64, P, P, P, I64, P]
         L.sparse_attn_forward_gather.restype = ctypes.c_int32
+        L.sparse_attn_select_fine.argtypes = [SP, ctypes.POINTER(SelectParams), P, P, P, P, I64, P, I64, P]
+        L.sparse_attn_select_fine.restype = ctypes.c_int32
+        L.sparse_attn_fine_csr_capacity.argtypes = [SP]
+        L.sparse_attn_fine_csr_capacity.restype = I64
+        L.sparse_attn_fine_workspace_size.argtypes = [SP]
+        L.sparse_attn_fine_workspace_size.restype = I64
         L.sparse_attn_forward_biased.restype = ctypes.c_int32
         L.sparse_attn_mask_to_csr.argtypes = [SP, P, P, P, I64, P, I64, P]
         L.sparse_attn_mask_to_csr.restype = ctypes.c_int32
@@ -439,6 +448,45 @@ def sparse_attn_forward_gather(shape: Shape, q, k, v, row_ptr, col_idx, out=None
                                           _stream(stream))
     _check(st, "sparse_attn_forward_gather")
     return (out, lse) if (want_lse or lse is not None) else out
+
+
+def sparse_attn_fine_csr_capacity(shape: Shape) -> int:
+    return int(lib().sparse_attn_fine_csr_capacity(ctypes.byref(shape)))
+
+
+def sparse_attn_fine_workspace_size(shape: Shape) -> int:
+    return int(lib().sparse_attn_fine_workspace_size(ctypes.byref(shape)))
+
+
+def sparse_attn_select_fine(shape: Shape, q, k, threshold: float = 0.9,
+                            head_thresholds: Optional[Sequence[float]] = None, row_ptr=None, col_idx=None,
+                            workspace=None, stream=None):
+    """Selection of 4-token key blocks per 64-token query block; returns (row_ptr,
+    col_idx) with col_idx indexing 4-token blocks (capacity B*H*nB*16nB)."""
+    import torch
+    dev = _req_tokens(shape, q=q, k=k)
+    rows = _dims(shape)[2]
+    cap = sparse_attn_fine_csr_capacity(shape)
+    _check(cap if cap < 0 else 0, "sparse_attn_fine_csr_capacity")
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=q.device)
+    if col_idx is None:
+        col_idx = torch.empty(cap, dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(sparse_attn_fine_workspace_size(shape), dtype=torch.uint8, device=q.device)
+    _req(row_ptr, "row_ptr", torch.int32, min_numel=rows + 1, device=dev)
+    _req(col_idx, "col_idx", torch.int32, min_numel=cap, device=dev)
+    _req_workspace(workspace, dev)
+    ht = None
+    if head_thresholds is not None:
+        arr = (ctypes.c_float * shape.heads)(*[float(x) for x in head_thresholds])
+        ht = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
+    params = SelectParams(float(threshold), ht, -1, -1, -1)
+    st = lib().sparse_attn_select_fine(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(row_ptr),
+                                       _ptr(col_idx), col_idx.numel(), _ptr(workspace), workspace.numel(),
+                                       _stream(stream))
+    _check(st, "sparse_attn_select_fine")
+    return row_ptr, col_idx
 
 
 def sparse_attn_forward_biased(shape: Shape, q, k, v, row_ptr, col_idx, col_bias, out=None, lse=None,

@@ -800,6 +800,133 @@ int32_t sparse_attn_from_tiles(const sparse_attn_shape *shape, const void *src, 
 }  // extern "C"
 
 // ---------------------------------------------------------------------------
+// Selection of 4-token key blocks (AB-Attention's fine blocks) per 64-token query
+// block, with NABLA's CDF cut.  Its workspace: thresholds, the fp32 key-block means
+// in planes of 4 columns and their norms, look-back words, ticket and fault word.
+namespace {
+
+constexpr int64_t kFineMaxBlocks = 512;   // nB: 8 words of 64 keys a lane per wave
+
+struct FineLayout {
+    int64_t thr, kf, knorm, status, ticket, total;
+};
+
+int64_t fine_groups(const Dims &d) { return d.B * d.H * ((d.nB + fine_rows(fine_words(d.nB * kFineBlocks)) - 1) /
+                                                          fine_rows(fine_words(d.nB * kFineBlocks))); }
+
+FineLayout fine_layout(const Dims &d) {
+    const int64_t nK = d.nB * kFineBlocks;
+    FineLayout l;
+    int64_t off = 0;
+    l.thr = off;
+    off = align_up(off + 4 * d.H, kAlign);
+    l.kf = off;
+    off = align_up(off + 4 * d.B * d.H * nK * d.D, kAlign);
+    l.knorm = off;
+    off = align_up(off + 4 * d.B * d.H * nK, kAlign);
+    l.status = off;
+    off = align_up(off + 8 * fine_groups(d), kAlign);
+    l.ticket = off;
+    off = align_up(off + 16, kAlign);
+    l.total = off;
+    return l;
+}
+
+// Shape checks of the fine selection: bf16, whole tiles, nB <= kFineMaxBlocks, and a
+// worst case of rows * 16 nB entries that int32 offsets can address.
+int32_t fine_shape(const sparse_attn_shape *shape, Dims &d) {
+    const int32_t st = check_shape(shape, &d);
+    if (st) return st;
+    if (shape->dtype != SPARSE_ATTN_BF16 || d.partial || d.nB > kFineMaxBlocks) return SPARSE_ATTN_UNSUPPORTED;
+    if (d.rows > INT32_MAX / (d.nB * kFineBlocks)) return SPARSE_ATTN_UNSUPPORTED;
+    return SPARSE_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t sparse_attn_fine_csr_capacity(const sparse_attn_shape *shape) {
+    Dims d;
+    const int32_t st = fine_shape(shape, d);
+    return st ? st : d.rows * d.nB * kFineBlocks;
+}
+
+int64_t sparse_attn_fine_workspace_size(const sparse_attn_shape *shape) {
+    Dims d;
+    const int32_t st = fine_shape(shape, d);
+    return st ? st : fine_layout(d).total;
+}
+
+int32_t sparse_attn_select_fine(const sparse_attn_shape *shape, const sparse_attn_select_params *params,
+                                const void *q, const void *k, int32_t *row_ptr, int32_t *col_idx,
+                                int64_t col_capacity, void *workspace, int64_t workspace_bytes, void *stream) {
+    Dims d;
+    int32_t st = fine_shape(shape, d);
+    if (st) return st;
+    if (!params || !q || !k || !row_ptr || !col_idx || !workspace) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(row_ptr, 4) || !aligned(col_idx, 4) || !aligned(workspace, 16))
+        return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (bad_thr(params->threshold)) return SPARSE_ATTN_INVALID_ARGUMENT;
+    if (params->head_thresholds)
+        for (int64_t h = 0; h < d.H; ++h)
+            if (bad_thr(params->head_thresholds[h])) return SPARSE_ATTN_INVALID_ARGUMENT;
+    // the window is a box in 64-token block coordinates: not defined for 4-token blocks
+    if (params->win_t >= 0 && params->win_h >= 0 && params->win_w >= 0) return SPARSE_ATTN_UNSUPPORTED;
+    const int64_t nK = d.nB * kFineBlocks;
+    if (col_capacity < d.rows * nK) return SPARSE_ATTN_CAPACITY;
+    const FineLayout L = fine_layout(d);
+    if (workspace_bytes < L.total) return SPARSE_ATTN_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    float *thr = (float *)(ws + L.thr);
+    PoolSide side;
+    side.n_thr = (int32_t)(d.H < ThrChunk::kMax ? d.H : ThrChunk::kMax);
+    for (int i = 0; i < side.n_thr; ++i)
+        side.thr.v[i] = params->head_thresholds ? params->head_thresholds[i] : params->threshold;
+    side.thr_dst = thr;
+    side.status = (uint64_t *)(ws + L.status);
+    side.n_status = fine_groups(d);
+    side.ticket = (uint32_t *)(ws + L.ticket);
+    for (int64_t h0 = ThrChunk::kMax; h0 < d.H; h0 += ThrChunk::kMax) {
+        float tmp[ThrChunk::kMax];
+        const int n = (int)((d.H - h0) < ThrChunk::kMax ? (d.H - h0) : ThrChunk::kMax);
+        for (int i = 0; i < n; ++i)
+            tmp[i] = params->head_thresholds ? params->head_thresholds[h0 + i] : params->threshold;
+        if (launch_fill_thresholds(tmp, n, thr + h0, s)) return SPARSE_ATTN_HIP_ERROR;
+    }
+    float *kf = (float *)(ws + L.kf);
+    float *knorm = (float *)(ws + L.knorm);
+    if (launch_fine_pool((const __bf16 *)k, kf, knorm, nK, d.B * d.H * nK, (int)d.D, side, s))
+        return SPARSE_ATTN_HIP_ERROR;
+    const int W = fine_words(nK), R = fine_rows(W);
+    FineArgs a = {};
+    a.q = (const __bf16 *)q;
+    a.k = (const __bf16 *)k;
+    a.kf = kf;
+    a.knorm = knorm;
+    a.thr = thr;
+    a.status = side.status;
+    a.ticket = side.ticket;
+    a.fault = side.ticket + 1;
+    a.spin_cap = lookback_spin_cap();
+    a.row_ptr = row_ptr;
+    a.col_idx = col_idx;
+    a.rows = d.rows;
+    a.groups_per_head = (int32_t)((d.nB + R - 1) / R);
+    a.n_groups = fine_groups(d);
+    a.H = (int32_t)d.H;
+    a.nB = (int32_t)d.nB;
+    a.nK = (int32_t)nK;
+    a.S = (int32_t)((nK + kFineWaves - 1) / kFineWaves);
+    a.scale_log2 = effective_scale(shape) * kLog2e;
+    if (launch_fine_select(a, (int)d.D, s)) return SPARSE_ATTN_HIP_ERROR;
+    return SPARSE_ATTN_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
 // Allocation-free selection.  The CDF selection's scratch (thresholds, key block
 // means, look-back words, ticket and fault word) lives in a static device array
 // instead of a caller's workspace.  Each GPU holds its own copy of the array at its

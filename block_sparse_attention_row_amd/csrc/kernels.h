@@ -108,6 +108,34 @@ struct SelectArgs {
     const float *mix_rows;
     int64_t head0;
 };
+// Selection of 4-token key blocks (nK = 16 nB per head) for each 64-token query
+// block: a workgroup of kFineWaves waves takes R query blocks of one head by ticket;
+// wave w holds the scores of keys [w S, w S + S) of all R rows (W words of 64 a lane).
+constexpr int kFineWaves = 16;
+struct FineArgs {
+    const __bf16 *q;          // [BH*N][D] queries (bf16, tile-major)
+    const __bf16 *k;          // [BH*N][D] keys (bf16, tile-major): the exact rescoring
+    const float *kf;          // [BH][D/4][nK][4] fp32 means of the 4-token key blocks
+    const float *knorm;       // [BH*nK] their Euclidean norms
+    const float *thr;         // [H] thresholds (device)
+    uint64_t *status;         // [n_groups] look-back words (zeroed by the pooling kernel)
+    uint32_t *ticket;         // group ticket counter (zeroed by the pooling kernel)
+    uint32_t *fault;          // look-back fault word (ticket + 1)
+    uint32_t spin_cap;
+    int32_t *row_ptr;         // [rows + 1]
+    int32_t *col_idx;         // [nnz]: key-block indices in [0, nK)
+    int64_t rows;             // BH * nB
+    int64_t n_groups;         // BH * groups_per_head
+    int32_t groups_per_head;  // ceil(nB / R)
+    int32_t H, nB, nK, S;     // heads, query blocks, key blocks, keys per wave slice
+    float scale_log2;
+};
+int fine_words(int64_t nK);   // W
+int fine_rows(int W);         // R
+int launch_fine_pool(const __bf16 *k, float *kf, float *knorm, int64_t nK, int64_t nkeys, int d, const PoolSide &side,
+                     hipStream_t s);
+int launch_fine_select(const FineArgs &a, int d, hipStream_t s);
+
 constexpr int kIbcsClusters = 8, kIbcsIters = 4;
 struct IbcsArgs {
     const __bf16 *q;          // [BH*N][D] queries (bf16, tile-major)

@@ -286,6 +286,41 @@ int32_t sparse_attn_forward_gather(const sparse_attn_shape *shape, const void *q
                                    float *lse, void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * Selection of 4-token key blocks for each 64-token query block: AB-Attention's
+ * fine key/value blocks (AB-Attention page, section "Les trois techniques
+ * d'AB-Attention", third technique), chosen with NABLA's rule (NABLA summary page,
+ * section "Methodologie : NABLA": "Sous-echantillonnage", "Attention Reduite",
+ * "Seuil CDF").  For query block i of head h: qbar_i = mean of its 64 tokens,
+ * kbar_j = mean of tile-major key tokens [4 j, 4 j + 4) for j in [0, 16 nB), scores
+ * qbar_i . kbar_j * scale, softmax over all 16 nB key blocks of the head, and the
+ * blocks kept in descending probability while the mass before them is below the
+ * threshold (ties to the lower index; threshold >= 1 keeps every block).  The
+ * near-ties at the cut are ordered by their exact scores, as in sparse_attn_select.
+ * The list feeds sparse_attn_forward_gather.
+ *
+ *   q, k         device bf16 [B, H, N, head_dim], tile-major, 16-byte aligned.
+ *   params       threshold / head_thresholds as in sparse_attn_select; the window
+ *                must be off (it is a box of 64-token blocks): UNSUPPORTED otherwise.
+ *   row_ptr      device int32 [B*H*nB + 1]; col_idx device int32 [col_capacity], with
+ *                col_capacity >= sparse_attn_fine_csr_capacity (B*H*nB*16nB);
+ *                4-token key-block indices, ascending per row.
+ *   workspace    device, >= sparse_attn_fine_workspace_size bytes.
+ * bf16, whole tiles and nB <= 512 only (SPARSE_ATTN_UNSUPPORTED otherwise).  A
+ * selection that gives up in its look-back writes -1 into the row_ptr entries of
+ * the rows it could not place, so that the list fails every validity check.
+ */
+int32_t sparse_attn_select_fine(const sparse_attn_shape *shape, const sparse_attn_select_params *params,
+                                const void *q, const void *k, int32_t *row_ptr, int32_t *col_idx,
+                                int64_t col_capacity, void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Worst-case col_idx entries of sparse_attn_select_fine (B*H*nB*16nB), or a negative
+   status when the shape is unsupported. */
+int64_t sparse_attn_fine_csr_capacity(const sparse_attn_shape *shape);
+
+/* Workspace bytes of sparse_attn_select_fine, or a negative status. */
+int64_t sparse_attn_fine_workspace_size(const sparse_attn_shape *shape);
+
+/*
  * External block mask to CSR (the path that accepts a caller's mask, e.g. a
  * static window or a mask reused from an earlier step).
  *

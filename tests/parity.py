@@ -110,9 +110,11 @@ class MaskReport:
 
 def compare_masks(gpu_mask: np.ndarray, keep: np.ndarray, qbar, kbar, wl: Workload, thr: np.ndarray,
                   window=None, band: int = -1) -> MaskReport:
-    """gpu_mask, keep: [rows, nB]; keep is the oracle's (bit0 CDF, bit1 window)."""
+    """gpu_mask, keep: [rows, nK]; keep is the oracle's (bit0 CDF, bit1 window).  kbar
+    holds the key blocks of the rows: nK = nB (64-token blocks) or 16 nB (4-token
+    blocks, with the window off)."""
     win = wl.window if window is None else window
-    nB = keep.shape[1]
+    nB = wl.blocks      # query blocks per head: row r belongs to head (r // nB) % H
     oracle_mask = keep != 0
     diff = np.nonzero((gpu_mask != oracle_mask).any(axis=1))[0]
     r1 = r2 = unexc = wmiss = inv = nblk = 0

@@ -431,3 +431,34 @@ def test_partial_tiles_refused_where_whole_tiles_are_needed():
                                      None) == B.SPARSE_ATTN_UNSUPPORTED
     assert L.sparse_attn_backward(ctypes.byref(s), A, A, A, A, A, A, A, A, cap, A, A, A, A, A, ws,
                                   None) == B.SPARSE_ATTN_UNSUPPORTED
+
+
+def test_fine_selection_sizes_and_host_checks():
+    """The 4-token selection's sizes, and the shapes and arguments it refuses on the
+    host before any HIP call (no GPU needed: no pointer is touched)."""
+    L = B.lib()
+    s = B.make_shape(1, 12, 128, (20, 32, 48), "bf16")          # nB = 480, nK = 7680
+    rows = 12 * 480
+    assert B.sparse_attn_fine_csr_capacity(s) == rows * 7680
+    ws = B.sparse_attn_fine_workspace_size(s)
+    # thresholds, fp32 key means and norms, look-back words of 8-row groups, ticket
+    assert ws >= 4 * 12 * 7680 * 128 + 4 * 12 * 7680 + 8 * 12 * 60 + 16
+    params = B.SelectParams(0.9, None, -1, -1, -1)
+    cap = rows * 7680
+    ok = (ctypes.byref(s), ctypes.byref(params), 16, 16, 16, 16, cap, 16, ws, None)
+    # unsupported: fp32, partial tiles, more than 512 blocks, a window
+    for bad in (B.make_shape(1, 1, 128, (2, 8, 8), "f32"), B.make_shape(1, 1, 128, (2, 12, 20), "bf16"),
+                B.make_shape(1, 1, 128, (9, 64, 64), "bf16")):   # 576 blocks
+        assert B.sparse_attn_fine_csr_capacity(bad) == B.SPARSE_ATTN_UNSUPPORTED
+        assert L.sparse_attn_select_fine(ctypes.byref(bad), ctypes.byref(params), 16, 16, 16, 16, 1 << 40, 16,
+                                         1 << 40, None) == B.SPARSE_ATTN_UNSUPPORTED
+    win = B.SelectParams(0.9, None, 1, 1, 1)
+    assert L.sparse_attn_select_fine(ctypes.byref(s), ctypes.byref(win), 16, 16, 16, 16, cap, 16, ws,
+                                     None) == B.SPARSE_ATTN_UNSUPPORTED
+    # argument checks
+    assert L.sparse_attn_select_fine(ctypes.byref(s), ctypes.byref(params), None, 16, 16, 16, cap, 16, ws,
+                                     None) == B.SPARSE_ATTN_INVALID_ARGUMENT
+    assert L.sparse_attn_select_fine(ctypes.byref(s), ctypes.byref(B.SelectParams(0.0, None, -1, -1, -1)), 16, 16,
+                                     16, 16, cap, 16, ws, None) == B.SPARSE_ATTN_INVALID_ARGUMENT
+    assert L.sparse_attn_select_fine(*ok[:6], cap - 1, *ok[7:]) == B.SPARSE_ATTN_CAPACITY
+    assert L.sparse_attn_select_fine(*ok[:8], ws - 1, None) == B.SPARSE_ATTN_WORKSPACE

@@ -831,3 +831,84 @@ def test_gather_of_whole_tiles_equals_the_tile_forward():
                                  torch.as_tensor(np.array(ci2, np.int32)).cuda(), out=out_g, lse=lse_g)
     torch.cuda.synchronize()
     assert torch.equal(out_g, out_t) and torch.equal(lse_g, lse_t)
+
+
+FINE = [
+    # name, heads, d, block grid (nB), thr, reading, per-head threshold range
+    ("d128_A_nB24", 2, 128, (2, 3, 4), 0.8, "A", None),            # 1 word a lane
+    ("d64_page_nB30", 3, 64, (3, 2, 5), 0.9, "page", None),
+    ("d128_B_nB27", 2, 128, (3, 3, 3), 0.9, "B", None),
+    ("d128_headthr_nB96", 3, 128, (2, 6, 8), 0.7, "A", (0.5, 0.95)),   # 2 words, ragged rows
+    ("d128_page_nB200", 2, 128, (2, 10, 10), 0.85, "page", None),      # 4 words
+    ("d64_A_nB480", 1, 64, (5, 8, 12), 0.9, "A", None),                 # 8 words
+    ("d128_keepall_nB40", 2, 128, (2, 4, 5), 1.0, "A", None),           # threshold 1: every block
+]
+
+
+def _fine_case(case):
+    name, H, d, bg, thr, reading, hr = case
+    wl = small_workload("fine_" + name, H, d, bg, "bf16", threshold=thr, head_threshold_range=hr, seed=93)
+    q, k, v, th = make_inputs(wl, reading)
+    return wl, q, k, v, th
+
+
+@pytest.mark.parametrize("case", FINE, ids=[c[0] for c in FINE])
+def test_fine_selection_matches_oracle(case):
+    """4-token key blocks selected per 64-token query block on the GPU against the
+    oracle's fine selection: every row, the mask rule of the 64-token selection (R1
+    only, no R2-only differences), a valid CSR of ascending 4-token indices."""
+    wl, q, k, _, th = _fine_case(case)
+    qd, kd = P.to_device(q, k)
+    shape = P.shape_for(wl)
+    head_thr = None if wl.head_threshold_range is None else [float(x) for x in th]
+    rp, ci = B.sparse_attn_select_fine(shape, qd, kd, threshold=float(np.float32(wl.threshold)),
+                                       head_thresholds=head_thr)
+    torch.cuda.synchronize()
+    nK = 16 * wl.blocks
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    gmask = P.check_csr(rp_h, ci[:int(rp_h[-1])].cpu().numpy(), nK)
+    keep, _, _ = oracle.select_fine(q, k, wl.heads, th.astype(np.float64))
+    qbar = oracle.pool(q)
+    kbar = oracle.pool(k, tpb=4)
+    rep = P.compare_masks(gmask, keep.astype(np.uint8), qbar, kbar, wl, th, window=(-1, -1, -1))
+    P.record_masks(f"fine_{case[0]}", rep)
+    assert P.mask_ok(rep), P.fmt(rep)
+    if wl.threshold >= 1.0:
+        assert int(rp_h[-1]) == wl.heads * wl.blocks * nK
+
+
+def test_fine_selection_feeds_the_gather_forward():
+    """The GPU's own 4-token list through sparse_attn_forward_gather, against the
+    oracle's attention over that same list, every query block."""
+    wl, q, k, v, th = _fine_case(("e2e_nB60", 2, 128, (3, 4, 5), 0.85, "page", None))
+    qd, kd, vd = P.to_device(q, k, v)
+    shape = P.shape_for(wl)
+    rp, ci = B.sparse_attn_select_fine(shape, qd, kd, threshold=float(np.float32(wl.threshold)))
+    out, lse = B.sparse_attn_forward_gather(shape, qd, kd, vd, rp, ci, want_lse=True)
+    torch.cuda.synchronize()
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    ci_h = ci[:int(rp_h[-1])].cpu().numpy()
+    rows = np.arange(wl.heads * wl.blocks)
+    ref, ref_lse = oracle.attention_rows(q, k, v, rp_h, ci_h, rows, key_tokens=4)
+    err = float(np.abs(out.float().cpu().reshape(-1, 64, wl.head_dim).numpy() - ref).max())
+    lerr = float(np.abs(lse.cpu().reshape(-1, 64).numpy() - ref_lse).max())
+    print(f"fine e2e: nnz {int(rp_h[-1])} of {rows.size * 16 * wl.blocks}, max|err|={err:.3e} lse {lerr:.3e}",
+          flush=True)
+    assert err <= P.TOL["bf16"] and lerr <= P.LSE_TOL["bf16"]
+
+
+def test_fine_selection_uniform_rows_keep_the_lowest_indices():
+    """Q = 0: every score is 0, so each row is uniform over its 16 nB key blocks and
+    the rule keeps ceil(thr * nK) of them, the lowest indices (all ties)."""
+    wl, q, k, _, _ = _fine_case(("uniform_nB64", 1, 128, (1, 8, 8), 0.75, "A", None))
+    q = torch.zeros_like(q)
+    qd, kd = P.to_device(q, k)
+    shape = P.shape_for(wl)
+    rp, ci = B.sparse_attn_select_fine(shape, qd, kd, threshold=0.75)
+    torch.cuda.synchronize()
+    nK = 16 * wl.blocks
+    want = int(np.ceil(0.75 * nK))
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    assert np.all(np.diff(rp_h) == want)
+    ci_h = ci[:int(rp_h[-1])].cpu().numpy().reshape(wl.blocks, want)
+    assert np.all(ci_h == np.arange(want)[None, :])
