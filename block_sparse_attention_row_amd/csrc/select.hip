@@ -215,41 +215,41 @@ template <int D> constexpr size_t select_lds_bytes() {
 // scores wherever the kept count m is itself settled (it can change only when the
 // threshold lies within the band's spread of mass, i.e. at the boundary).
 template <int D>
-__device__ __forceinline__ uint64_t refine_band(uint64_t cdf, int nb, int m, const double *qrow, const double *k64,
-                                                const uint32_t *list, int lane) {
-    static_assert(D % 64 == 0, "whole dimensions per lane");
-    constexpr int DPL = D / 64;
+__device__ __forceinline__ void refine_band(uint64_t *cdf_bits, int nb, int m, const double *qrow, const double *k64,
+                                            const uint32_t *list, int lane) {
+    static_assert(D % 16 == 0, "whole double2 loads");
     const int my_j = lane < nb ? (int)list[lane] : 0x7fffffff;
-    double q[DPL];
-#pragma unroll
-    for (int u = 0; u < DPL; ++u) q[u] = qrow[DPL * lane + u];
+    // lane n scores band block list[n]: its whole key-mean row at once (independent
+    // loads, so the band costs one memory latency, not nb), against the query row in
+    // LDS (broadcast reads)
     double my_s = 0.0;
-    for (int n = 0; n < nb; ++n) {
-        const int j = __builtin_amdgcn_readfirstlane((int)list[n]);
-        const double *kr = k64 + (int64_t)j * D + DPL * lane;
-        double part = 0.0;
-#pragma unroll
-        for (int u = 0; u < DPL; ++u) part = __builtin_fma(q[u], kr[u], part);
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-        if (lane == n) my_s = part;
+    if (lane < nb) {
+        const double2 *kr = reinterpret_cast<const double2 *>(k64 + (int64_t)my_j * D);
+        const double2 *qr = reinterpret_cast<const double2 *>(qrow);
+        double acc0 = 0.0, acc1 = 0.0;
+#pragma unroll 16
+        for (int u = 0; u < D / 2; ++u) {
+            const double2 kv = kr[u], qv = qr[u];
+            acc0 = __builtin_fma(qv.x, kv.x, acc0);
+            acc1 = __builtin_fma(qv.y, kv.y, acc1);
+        }
+        my_s = acc0 + acc1;
     }
-    // rank by (exact score descending, index ascending); the m best are kept
+    // rank by (exact score descending, index ascending); the m best are kept, and
+    // lane n sets or clears its block's bit in the row's LDS mask words
     int rank = 0;
     for (int n = 0; n < nb; ++n) {
         const double sn = __shfl(my_s, n, 64);
         const int jn = __shfl(my_j, n, 64);
         rank += (sn > my_s || (sn == my_s && jn < my_j)) ? 1 : 0;
     }
-    const uint64_t keep = __ballot(lane < nb && rank < m);
-    for (int n = 0; n < nb; ++n) {
-        const int jn = __builtin_amdgcn_readfirstlane((int)list[n]);
-        if (lane == (jn >> 6)) {
-            const uint64_t bit = 1ull << (jn & 63);
-            cdf = ((keep >> n) & 1ull) ? (cdf | bit) : (cdf & ~bit);
-        }
+    if (lane < nb) {
+        const unsigned long long bit = 1ull << (my_j & 63);
+        if (rank < m)
+            atomicOr(reinterpret_cast<unsigned long long *>(cdf_bits + (my_j >> 6)), bit);
+        else
+            atomicAnd(reinterpret_cast<unsigned long long *>(cdf_bits + (my_j >> 6)), ~bit);
     }
-    return cdf;
 }
 
 // Pivot steps of the cut over an array of keys v (the register row, or the bracket
@@ -320,7 +320,10 @@ __device__ __forceinline__ uint32_t div_small(uint32_t j, uint32_t m24) { return
 // The cut of row i (threshold thr), run by one wave on its register row s (scaled
 // scores, -inf for padding keys).  Returns the row's bitmask (lane c holds the word
 // of key blocks 64c .. 64c+63) and its count.  `bracket` is 512 words of LDS for this
-// wave, `hist_all` holds 256 words per wave.
+// wave (the compacted bracket, then the band's block list); `hist_all` holds 256
+// words per wave: the row's mask words (CDF cut at [0, NE), window at [64, 64 + NE)
+// as 64-bit words), written by one lane as they are formed, so that no per-word
+// mask has to stay in scalar registers.
 template <int NE, int D>
 __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], float *hist_all, uint32_t *bracket,
                                            int i, float thr, int lane, uint64_t &word, int32_t &count_out,
@@ -328,7 +331,9 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
     constexpr int NC = 8;                  // compacted bracket: 8 words a lane, 512 keys
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool keep_all = !(thr < 1.f);
-    uint32_t *list = reinterpret_cast<uint32_t *>(hist_all + wave * 256);   // up to 64 keys of the bracket
+    uint32_t *list = bracket;                                                // up to 64 keys of the bracket
+    uint64_t *cdf_bits = reinterpret_cast<uint64_t *>(hist_all + wave * 256);   // [NE] CDF words, then [NE] window
+    uint64_t *win_bits = cdf_bits + 64;
 
     // e_j = 2^(s_j - max) in place (0 for padding), Z, the smallest positive key and
     // how many keys are positive
@@ -337,14 +342,15 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
     for (int c = 0; c < NE; ++c) mx = fmaxf(mx, s[c]);
     mx = wave_max_u(mx);
     float z = 0.f;
-    uint32_t kmin = 0xffffffffu, npos = 0;
+    uint32_t kmin = 0xffffffffu;
+    int npos_l = 0;                                          // this lane's positive keys
 #pragma unroll
     for (int c = 0; c < NE; ++c) {
         const float pe = __builtin_amdgcn_exp2f(s[c] - mx);
         s[c] = pe;
         z += pe;
         kmin = min(kmin, __float_as_uint(pe) - 1u);         // padding (0) wraps to the top
-        npos += (uint32_t)__popcll(__ballot(pe > 0.f));
+        npos_l += pe > 0.f ? 1 : 0;
     }
     const float Z = wave_sum_u(z);
     const float thrz = thr * Z;
@@ -360,7 +366,7 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
     if (!keep_all) {
         uint32_t lo = wave_min_u32(kmin), hi = 0x3f800000u;   // every e_j <= 1, the row max is exactly 1
         float Mhi = 0.f, Mlo = Z;
-        uint32_t clo = npos, chi = 0;                         // counts of key > lo, key > hi
+        uint32_t clo = (uint32_t)wave_sum_i(npos_l), chi = 0; // counts of key > lo, key > hi
         int step = 0;
         bool packed = false;
         float t[NC];
@@ -428,7 +434,6 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
     const float blo = vstar_f * (1.f - band_rel), bhi = vstar_f * (1.f + band_rel);
     uint32_t ties_before = 0;
     int nbl = 0, mbl = 0;                  // this lane's band and kept-in-band counts
-    uint64_t cdf_word = 0, win_word = 0;
 #pragma unroll
     for (int c = 0; c < NE; ++c) {
         const int j = 64 * c + lane;
@@ -457,17 +462,15 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
             const int yj = (int)row - (int)div_small(row, m_y) * a.nTy;      // (j / nTx) % nTy
             mw = __ballot(j >= jlo && j < jhi && abs(yj - yi) <= a.wh && abs(xj - xi) <= a.ww);
         }
-        if (lane == c) {
-            cdf_word = m;
-            win_word = mw;
+        if (lane == 0) {
+            cdf_bits[c] = m;
+            win_bits[c] = mw;
         }
     }
     if (refine) {
         const int nb = wave_sum_i(nbl), mb = wave_sum_i(mbl);
         if (nb >= 2 && nb <= kRefineMax && mb > 0 && mb < nb) {
             // the band's indices, ascending, into this wave's LDS list
-            const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-            uint32_t *list = reinterpret_cast<uint32_t *>(hist_all) + 256 * wave;
             uint32_t base = 0;
 #pragma unroll
             for (int c = 0; c < NE; ++c) {
@@ -479,11 +482,12 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
                 base += (uint32_t)__popcll(bm);
             }
             wave_lds_sync();
-            cdf_word = refine_band<D>(cdf_word, nb, mb, qrow, k64, list, lane);
-            wave_lds_sync();
+            refine_band<D>(cdf_bits, nb, mb, qrow, k64, list, lane);
         }
     }
-    word = cdf_word | win_word;
+    wave_lds_sync();
+    // word c of the row to lane c
+    word = lane < NE ? (cdf_bits[lane] | win_bits[lane]) : 0ull;
     count_out = (int32_t)wave_sum_i(__popcll(word));
 }
 
