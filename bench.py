@@ -82,6 +82,16 @@ def parse():
 
 # ---------------------------------------------------------------------------- counters
 
+def is_plain_attention(name):
+    """The plain bf16 attention kernel: attn_bf16_kernel<D, ...> with every flag after D
+    false (no logit offsets, no 4-token gather, no partial-tile masking)."""
+    at = name.find(ATTN_KERNEL + "<")
+    if at < 0:
+        return False
+    args = name[at + len(ATTN_KERNEL) + 1:].split(">")[0].split(",")
+    return all(a.strip() == "false" for a in args[1:])
+
+
 def _read_counter_csv(pattern, counter):
     """Per-dispatch counter values by kernel name from rocprofv3 counter_collection.csv files."""
     out = {}
@@ -115,13 +125,16 @@ def pmc_summary(d, workload):
            "attention_source_sha256": _sha(ATTN_SRC), "selection_source_sha256": _sha(SEL_SRC), "kernels": {}}
     # the plain attention kernel (the instantiation with logit offsets serves other calls), the key
     # pooling and the CDF selection (MODE 0 of select_emit_kernel)
-    for label, key, excl in ((ATTN_KERNEL, ATTN_KERNEL, "true>"), ("pool_kernel", "pool_kernel", None),
-                             ("select_emit_kernel", "select_emit_kernel", None)):
+    for label, key in ((ATTN_KERNEL, ATTN_KERNEL), ("pool_kernel", "pool_kernel"),
+                       ("select_emit_kernel", "select_emit_kernel")):
         if label == "select_emit_kernel":
             f = pick({n: v for n, v in fetch.items() if n.rstrip().endswith("0>")}, key)
             w = pick({n: v for n, v in write.items() if n.rstrip().endswith("0>")}, key)
+        elif label == ATTN_KERNEL:
+            f = pick({n: v for n, v in fetch.items() if is_plain_attention(n)}, key)
+            w = pick({n: v for n, v in write.items() if is_plain_attention(n)}, key)
         else:
-            f, w = pick(fetch, key, excl), pick(write, key, excl)
+            f, w = pick(fetch, key), pick(write, key)
         k = {"fetch_kib_per_dispatch": f, "write_kib_per_dispatch": w}
         if f and w and fs and ws:
             k["hbm_bytes_per_dispatch"] = f * 1024.0 * fs + w * 1024.0 * ws
@@ -174,7 +187,7 @@ def trace_summary(d, steps, warmup):
         n, a, m, lo, hi, tot = stats(v)
         short = name.split("(")[0][:90]
         out.append(f"| `{short}` | {n} | {a:.1f} | {m:.1f} | {lo:.1f} | {hi:.1f} | {tot:.2f} |")
-    plain = [v for name, v in by.items() if ATTN_KERNEL in name and "true>" not in name]
+    plain = [v for name, v in by.items() if is_plain_attention(name)]
     if plain:
         timed = plain[0][warmup:warmup + steps]
         if timed:

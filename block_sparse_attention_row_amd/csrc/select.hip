@@ -317,13 +317,20 @@ __device__ __forceinline__ uint32_t compact_bracket(const float (&v)[N], uint32_
 // j (d - 1) < 2^24.  m24 = ceil(2^24 / d) is formed once per wave.
 __device__ __forceinline__ uint32_t div_small(uint32_t j, uint32_t m24) { return __umulhi(j << 8, m24); }
 
+// f(std::integral_constant<int, I>) for I = B .. E-1, in order, at compile time.
+template <int B, int E, typename F> __device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // The cut of row i (threshold thr), run by one wave on its register row s (scaled
 // scores, -inf for padding keys).  Returns the row's bitmask (lane c holds the word
 // of key blocks 64c .. 64c+63) and its count.  `bracket` is 512 words of LDS for this
 // wave (the compacted bracket, then the band's block list); `hist_all` holds 256
-// words per wave: the row's mask words (CDF cut at [0, NE), window at [64, 64 + NE)
-// as 64-bit words), written by one lane as they are formed, so that no per-word
-// mask has to stay in scalar registers.
+// words per wave: the row's 64-bit mask words while the band's exact order sets or
+// clears their bits.
 template <int NE, int D>
 __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], float *hist_all, uint32_t *bracket,
                                            int i, float thr, int lane, uint64_t &word, int32_t &count_out,
@@ -332,8 +339,7 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool keep_all = !(thr < 1.f);
     uint32_t *list = bracket;                                                // up to 64 keys of the bracket
-    uint64_t *cdf_bits = reinterpret_cast<uint64_t *>(hist_all + wave * 256);   // [NE] CDF words, then [NE] window
-    uint64_t *win_bits = cdf_bits + 64;
+    uint64_t *cdf_bits = reinterpret_cast<uint64_t *>(hist_all + wave * 256);   // [NE] words (band rescoring)
 
     // e_j = 2^(s_j - max) in place (0 for padding), Z, the smallest positive key and
     // how many keys are positive
@@ -418,28 +424,22 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
     }
 
     // ---- kept = key above v*, or equal to v* with M + (its rank among the equal
-    //      keys, by index) * v* below thr*Z, or inside the window: frames form a
-    //      contiguous range of j, rows and columns come from exact small quotients
-    const int nTyx = a.nTy * a.nTx;
-    const int ti = i / nTyx, yi = (i / a.nTx) % a.nTy, xi = i % a.nTx;
-    const int nT = a.nB / nTyx;
-    const int jlo = max(ti - a.wt, 0) * nTyx;                                  // frames in reach
-    const int jhi = ((a.wt >= nT - ti ? nT - 1 : ti + a.wt) + 1) * nTyx;
-    const uint32_t m_x = (0x1000000u + (uint32_t)a.nTx - 1u) / (uint32_t)a.nTx;
-    const uint32_t m_y = (0x1000000u + (uint32_t)a.nTy - 1u) / (uint32_t)a.nTy;
+    //      keys, by index) * v* below thr*Z.  Each 64-block word goes to LDS from
+    //      one lane as it is formed, so that no per-word mask stays live in scalar
+    //      registers; lane c reads word c back at the end.
     const float vstar_f = __uint_as_float(vstar);
     // the band of near-ties around v* (band_rel < 0: no exact rescoring); the main pass
-    // only counts the band and the kept blocks in it
+    // only counts the band and the kept blocks in it, by popcounts of wave masks
     const bool refine = !keep_all && band_rel >= 0.f && qrow != nullptr;
     const float blo = vstar_f * (1.f - band_rel), bhi = vstar_f * (1.f + band_rel);
-    uint32_t ties_before = 0;
-    int nbl = 0, mbl = 0;                  // this lane's band and kept-in-band counts
-#pragma unroll
-    for (int c = 0; c < NE; ++c) {
-        const int j = 64 * c + lane;
-        uint64_t m, mw = 0;
+    // as bit patterns (blo_u >= 1 leaves out the padding, whose e is 0)
+    const uint32_t blo_u = blo > 0.f ? max(__float_as_uint(blo), 1u) : 1u, bhi_u = __float_as_uint(bhi);
+    uint32_t ties_before = 0, nb = 0, mb = 0;
+    static_for<0, NE>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        uint64_t m;
         if (keep_all) {
-            m = __ballot(j < a.nB);
+            m = __ballot(64 * c + lane < a.nB);
         } else {
             const uint32_t u = __float_as_uint(s[c]);
             m = __ballot(u > vstar);
@@ -451,43 +451,57 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
                 ties_before += (uint32_t)__popcll(tb);
             }
             if (refine) {
-                const bool inb = s[c] >= blo && s[c] <= bhi && s[c] > 0.f;
-                nbl += inb ? 1 : 0;
-                mbl += (inb && ((m >> lane) & 1ull)) ? 1 : 0;
+                const uint64_t bm = __ballot(u >= blo_u && u <= bhi_u);
+                nb += (uint32_t)__popcll(bm);
+                mb += (uint32_t)__popcll(bm & m);
             }
         }
-        if (a.window) {
-            const uint32_t row = div_small((uint32_t)j, m_x);                 // j / nTx
-            const int xj = j - (int)row * a.nTx;
-            const int yj = (int)row - (int)div_small(row, m_y) * a.nTy;      // (j / nTx) % nTy
-            mw = __ballot(j >= jlo && j < jhi && abs(yj - yi) <= a.wh && abs(xj - xi) <= a.ww);
-        }
-        if (lane == 0) {
-            cdf_bits[c] = m;
-            win_bits[c] = mw;
-        }
-    }
-    if (refine) {
-        const int nb = wave_sum_i(nbl), mb = wave_sum_i(mbl);
-        if (nb >= 2 && nb <= kRefineMax && mb > 0 && mb < nb) {
-            // the band's indices, ascending, into this wave's LDS list
-            uint32_t base = 0;
+        if (lane == 0) cdf_bits[c] = m;
+    });
+    if (refine && nb >= 2 && nb <= (uint32_t)kRefineMax && mb > 0 && mb < nb) {
+        // the band's indices, ascending, into this wave's LDS list; the row's words to
+        // LDS, where the exact order of the band sets or clears their bits
+        uint32_t base = 0;
 #pragma unroll
-            for (int c = 0; c < NE; ++c) {
-                const bool in = s[c] >= blo && s[c] <= bhi && s[c] > 0.f;
-                const uint64_t bm = __ballot(in);
-                if (in)
-                    list[base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u))] =
-                        (uint32_t)(64 * c + lane);
-                base += (uint32_t)__popcll(bm);
-            }
-            wave_lds_sync();
-            refine_band<D>(cdf_bits, nb, mb, qrow, k64, list, lane);
+        for (int c = 0; c < NE; ++c) {
+            const uint32_t u = __float_as_uint(s[c]);
+            const bool in = u >= blo_u && u <= bhi_u;
+            const uint64_t bm = __ballot(in);
+            if (in)
+                list[base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u))] =
+                    (uint32_t)(64 * c + lane);
+            base += (uint32_t)__popcll(bm);
         }
+        wave_lds_sync();
+        refine_band<D>(cdf_bits, (int)nb, (int)mb, qrow, k64, list, lane);
     }
     wave_lds_sync();
     // word c of the row to lane c
-    word = lane < NE ? (cdf_bits[lane] | win_bits[lane]) : 0ull;
+    uint64_t cdf_word = lane < NE ? cdf_bits[lane] : 0ull;
+    // ---- the window, ORed in: frames form a contiguous range of j, rows and columns
+    //      come from exact small quotients
+    if (a.window) {
+        const int nTyx = a.nTy * a.nTx;
+        const int ti = i / nTyx, yi = (i / a.nTx) % a.nTy, xi = i % a.nTx;
+        const int nT = a.nB / nTyx;
+        const int jlo = max(ti - a.wt, 0) * nTyx;                                  // frames in reach
+        const int jhi = ((a.wt >= nT - ti ? nT - 1 : ti + a.wt) + 1) * nTyx;
+        const uint32_t m_x = (0x1000000u + (uint32_t)a.nTx - 1u) / (uint32_t)a.nTx;
+        const uint32_t m_y = (0x1000000u + (uint32_t)a.nTy - 1u) / (uint32_t)a.nTy;
+        wave_lds_sync();      // every lane has read its word: the window's words reuse the array
+        static_for<0, NE>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            const int j = 64 * c + lane;
+            const uint32_t row = div_small((uint32_t)j, m_x);                 // j / nTx
+            const int xj = j - (int)row * a.nTx;
+            const int yj = (int)row - (int)div_small(row, m_y) * a.nTy;      // (j / nTx) % nTy
+            const uint64_t mw = __ballot(j >= jlo && j < jhi && abs(yj - yi) <= a.wh && abs(xj - xi) <= a.ww);
+            if (lane == 0) cdf_bits[c] = mw;
+        });
+        wave_lds_sync();
+        if (lane < NE) cdf_word |= cdf_bits[lane];
+    }
+    word = cdf_word;
     count_out = (int32_t)wave_sum_i(__popcll(word));
 }
 
@@ -579,8 +593,9 @@ __device__ __forceinline__ void select_emit_body(const SelectArgs &a) {
     // workgroups share a CU instead
     constexpr bool kPrefetch = NE > 8 && NE <= 32;
     // the CDF selection pools its queries in fp64 (exact means for the near-tie
-    // rescoring), with fewer loads in flight to stay within the register budget
-    using QP = BlockPool<T, D, MODE == 0 ? 4 : 8>;
+    // rescoring); rows of up to 512 blocks run at 64 VGPRs and keep 4 loads a lane in
+    // flight, longer rows (128 VGPRs, free while the scores do not exist yet) all 16
+    using QP = BlockPool<T, D, MODE == 0 ? (NE <= 8 ? 4 : 16) : 8>;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     __bf16 *qf = reinterpret_cast<__bf16 *>(smem_raw);                              // [16][2D+8]
     float *stage = reinterpret_cast<float *>(smem_raw + (size_t)kSelRows * qf_stride<D>() * 2);  // [2][16][260]

@@ -34,19 +34,20 @@ def _write_counters(path, counter, rows):
 
 def test_pmc_summary_scales_by_the_copy_kernel(tmp_path):
     kib = bench.COPY_BYTES / 1024.0
-    attn = "void sattn::attn_bf16_kernel<128, false>(sattn::AttnArgs)"
-    biased = "void sattn::attn_bf16_kernel<128, true>(sattn::AttnArgs)"
+    attn = "void sattn::attn_bf16_kernel<128, false, false, false>(sattn::AttnArgs)"
+    biased = "void sattn::attn_bf16_kernel<128, true, false, false>(sattn::AttnArgs)"
+    gathered = "void sattn::attn_bf16_kernel<128, false, true, false>(sattn::AttnArgs)"
     pool = "void sattn::pool_kernel<__bf16, 128>(__bf16 const*, __bf16*, long, int, sattn::PoolSide)"
     sel = "sattn::select_emit_kernel<bf16, 128, 60, 0>"
     sip = "sattn::select_emit_kernel<bf16, 128, 60, 1>"
     copy = "void at::native::vectorized_elementwise_kernel<4, neg_kernel>"
     # the copy reads and writes 1 GiB but the counters read half of it on fetch
     _write_counters(str(tmp_path / "fetch" / "a" / "run_counter_collection.csv"), "FETCH_SIZE",
-                    [(copy, kib / 2), (attn, 1000.0), (attn, 1200.0), (biased, 9.0e9), (pool, 50.0),
-                     (sel, 70.0), (sip, 9.0e9)])
+                    [(copy, kib / 2), (attn, 1000.0), (attn, 1200.0), (biased, 9.0e9), (gathered, 9.0e9),
+                     (pool, 50.0), (sel, 70.0), (sip, 9.0e9)])
     _write_counters(str(tmp_path / "write" / "a" / "run_counter_collection.csv"), "WRITE_SIZE",
-                    [(copy, kib), (attn, 300.0), (attn, 300.0), (biased, 9.0e9), (pool, 5.0), (sel, 7.0),
-                     (sip, 9.0e9)])
+                    [(copy, kib), (attn, 300.0), (attn, 300.0), (biased, 9.0e9), (gathered, 9.0e9), (pool, 5.0),
+                     (sel, 7.0), (sip, 9.0e9)])
     rec = bench.pmc_summary(str(tmp_path), "long_video")
     assert rec["fetch_scale"] == pytest.approx(2.0)
     assert rec["write_scale"] == pytest.approx(1.0)
@@ -85,11 +86,15 @@ def test_stored_traffic_needs_the_same_source_and_workload(tmp_path, monkeypatch
 def test_trace_summary_separates_the_timed_steps(tmp_path, capsys):
     path = tmp_path / "x" / "run_kernel_trace.csv"
     os.makedirs(path.parent)
-    attn = "void sattn::attn_bf16_kernel<128, false>(sattn::AttnArgs)"
+    attn = "void sattn::attn_bf16_kernel<128, false, false, false>(sattn::AttnArgs)"
+    biased = "void sattn::attn_bf16_kernel<128, true, false, false>(sattn::AttnArgs)"
     rows = []
     t = 0
     for i, dur_us in enumerate([900, 800, 240, 241, 239, 500]):      # 2 warm-ups, 3 timed, 1 later call
         rows.append({"Kernel_Name": attn, "Start_Timestamp": t, "End_Timestamp": t + dur_us * 1000})
+        t += 10 ** 7
+    for dur_us in (70, 71):                                           # the biased kernel is not the plain one
+        rows.append({"Kernel_Name": biased, "Start_Timestamp": t, "End_Timestamp": t + dur_us * 1000})
         t += 10 ** 7
     with open(path, "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
@@ -98,6 +103,14 @@ def test_trace_summary_separates_the_timed_steps(tmp_path, capsys):
     bench.trace_summary(str(tmp_path), steps=3, warmup=2)
     out = capsys.readouterr().out
     assert "3 calls, avg 240.0 us, median 240.0 us, min 239.0 us, max 241.0 us" in out
+
+
+def test_plain_attention_kernel_names():
+    assert bench.is_plain_attention("void sattn::attn_bf16_kernel<128, false, false, false>(sattn::AttnArgs)")
+    assert bench.is_plain_attention("sattn::attn_bf16_kernel<64, false>")
+    for flags in ("true, false, false", "false, true, false", "false, false, true"):
+        assert not bench.is_plain_attention(f"void sattn::attn_bf16_kernel<128, {flags}>(sattn::AttnArgs)")
+    assert not bench.is_plain_attention("void sattn::pool_kernel<__bf16, 128>(...)")
 
 
 def test_cpu_baseline_sample_is_two_heads_of_32_blocks():
