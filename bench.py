@@ -27,6 +27,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -66,6 +67,8 @@ def parse():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-sip", action="store_true", help="skip the sampling-selection timing")
     ap.add_argument("--no-ibcs", action="store_true", help="skip the clustering-selector timing")
+    ap.add_argument("--no-fine", action="store_true",
+                    help="skip the 4-token key-block path (selection and gathered forward, 480p-sized inputs)")
     ap.add_argument("--sip-budget", type=float, default=0.1,
                     help="sampling selection: expected kept key blocks per row, as a fraction of the blocks")
     ap.add_argument("--no-select-timing", action="store_true", help="skip the separate selection timing")
@@ -82,14 +85,49 @@ def parse():
 
 # ---------------------------------------------------------------------------- counters
 
+def kernel_ident(name):
+    """The kernel's function name, from a demangled ("void ns::name<...>(...)") or an
+    Itanium-mangled ("_ZN5sattn11pool_kernelI...") kernel name."""
+    if name.startswith("_ZN"):
+        i, ident = 3, None
+        while i < len(name) and name[i].isdigit():
+            j = i
+            while j < len(name) and name[j].isdigit():
+                j += 1
+            n = int(name[i:j])
+            ident, i = name[j:j + n], j + n
+        return ident
+    return name.split("(")[0].split("<")[0].split("::")[-1].split()[-1]
+
+
+def template_args(name):
+    """Integer and boolean template arguments of a kernel name, in order (demangled or
+    mangled: Li<n>E and Lb<0|1>E)."""
+    if name.startswith("_ZN"):
+        return [int(v) for v in re.findall(r"L[ib](\d+)E", name)]
+    inner = name.split("<", 1)[1].rsplit(">", 1)[0] if "<" in name else ""
+    out = []
+    for a in inner.split(","):
+        a = a.strip()
+        if a in ("true", "false"):
+            out.append(1 if a == "true" else 0)
+        elif a.lstrip("-").isdigit():
+            out.append(int(a))
+    return out
+
+
 def is_plain_attention(name):
     """The plain bf16 attention kernel: attn_bf16_kernel<D, ...> with every flag after D
     false (no logit offsets, no 4-token gather, no partial-tile masking)."""
-    at = name.find(ATTN_KERNEL + "<")
-    if at < 0:
+    if kernel_ident(name) != ATTN_KERNEL:
         return False
-    args = name[at + len(ATTN_KERNEL) + 1:].split(">")[0].split(",")
-    return all(a.strip() == "false" for a in args[1:])
+    return all(v == 0 for v in template_args(name)[1:])
+
+
+def is_cdf_selection(name):
+    """select_emit_kernel<T, D, NE, 0>: NABLA's CDF selection (MODE 0)."""
+    args = template_args(name)
+    return kernel_ident(name) == "select_emit_kernel" and bool(args) and args[-1] == 0
 
 
 def _read_counter_csv(pattern, counter):
@@ -111,12 +149,13 @@ def pmc_summary(d, workload):
     fetch = _read_counter_csv(os.path.join(d, "fetch", "**", "*counter_collection.csv"), "FETCH_SIZE")
     write = _read_counter_csv(os.path.join(d, "write", "**", "*counter_collection.csv"), "WRITE_SIZE")
 
-    def pick(table, key, exclude=None):
-        vals = [v for n, vs in table.items() if key in n and not (exclude and exclude in n) for v in vs]
+    def pick(table, match):
+        vals = [v for n, vs in table.items() if match(n) for v in vs]
         return sum(vals) / len(vals) if vals else None
 
-    copy_key = "neg_kernel"            # torch.neg over COPY_BYTES: reads and writes COPY_BYTES once
-    cf, cw = pick(fetch, copy_key), pick(write, copy_key)
+    def is_copy(n):                    # torch.neg over COPY_BYTES: reads and writes COPY_BYTES once
+        return "neg_kernel" in n
+    cf, cw = pick(fetch, is_copy), pick(write, is_copy)
     kib = COPY_BYTES / 1024.0
     fs = (kib / cf) if cf else None
     ws = (kib / cw) if cw else None
@@ -125,16 +164,9 @@ def pmc_summary(d, workload):
            "attention_source_sha256": _sha(ATTN_SRC), "selection_source_sha256": _sha(SEL_SRC), "kernels": {}}
     # the plain attention kernel (the instantiation with logit offsets serves other calls), the key
     # pooling and the CDF selection (MODE 0 of select_emit_kernel)
-    for label, key in ((ATTN_KERNEL, ATTN_KERNEL), ("pool_kernel", "pool_kernel"),
-                       ("select_emit_kernel", "select_emit_kernel")):
-        if label == "select_emit_kernel":
-            f = pick({n: v for n, v in fetch.items() if n.rstrip().endswith("0>")}, key)
-            w = pick({n: v for n, v in write.items() if n.rstrip().endswith("0>")}, key)
-        elif label == ATTN_KERNEL:
-            f = pick({n: v for n, v in fetch.items() if is_plain_attention(n)}, key)
-            w = pick({n: v for n, v in write.items() if is_plain_attention(n)}, key)
-        else:
-            f, w = pick(fetch, key), pick(write, key)
+    for label, match in ((ATTN_KERNEL, is_plain_attention), ("pool_kernel", lambda n: kernel_ident(n) == "pool_kernel"),
+                         ("select_emit_kernel", is_cdf_selection)):
+        f, w = pick(fetch, match), pick(write, match)
         k = {"fetch_kib_per_dispatch": f, "write_kib_per_dispatch": w}
         if f and w and fs and ws:
             k["hbm_bytes_per_dispatch"] = f * 1024.0 * fs + w * 1024.0 * ws
@@ -449,6 +481,63 @@ def main():
                 "frac_hbm_peak": round(ibytes / (ims_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         del ibufs
 
+    # AB-Attention's 4-token key blocks: the selection over 16 nB key blocks a row and the
+    # forward that gathers the kept blocks into tiles, on the 480p-sized workload (the
+    # 4-token selection serves rows of up to 512 query blocks)
+    fine = None
+    if not args.no_fine:
+        fwl = WORKLOADS["wan13b_480p"]
+        fq, fk, fv, _ = make_inputs(fwl, args.reading)
+        fqd, fkd, fvd = fq.to(dev), fk.to(dev), fv.to(dev)
+        del fq, fk, fv
+        fshape = B.make_shape(fwl.batch, fwl.heads, fwl.head_dim, fwl.grid, fwl.dtype, 0.0, fwl.tile)
+        fthr = float(np.float32(fwl.threshold))
+        fws = torch.empty(B.sparse_attn_fine_workspace_size(fshape), dtype=torch.uint8, device=dev)
+        frows = fwl.batch * fwl.heads * fwl.blocks
+        frp = torch.empty(frows + 1, dtype=torch.int32, device=dev)
+        fci = torch.empty(B.sparse_attn_fine_csr_capacity(fshape), dtype=torch.int32, device=dev)
+        fout = torch.empty_like(fqd)
+        fwsa = torch.empty(B.sparse_attn_workspace_size(fshape), dtype=torch.uint8, device=dev)
+
+        def fine_select():
+            return B.sparse_attn_select_fine(fshape, fqd, fkd, threshold=fthr, row_ptr=frp, col_idx=fci,
+                                             workspace=fws, stream=stream)
+
+        def fine_forward():
+            B.sparse_attn_forward_gather(fshape, fqd, fkd, fvd, frp, fci, out=fout, workspace=fwsa, stream=stream)
+        fine_select()
+        fine_forward()
+        torch.cuda.synchronize()
+        fnnz = int(frp[-1].item())
+        fsel, ffw = [], []
+        for _ in range(10):
+            flush.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fine_select()
+            b.record(stream)
+            torch.cuda.synchronize()
+            fsel.append(a.elapsed_time(b))
+        for _ in range(10):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fine_forward()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ffw.append(a.elapsed_time(b))
+        fsel_med, ffw_med = sorted(fsel)[5], sorted(ffw)[5]
+        nK = 16 * fwl.blocks
+        fbytes = 2 * fqd.numel() * fqd.element_size() + 4 * (frows + 1) + 4 * fnnz
+        fflops = 4.0 * 64 * 4 * fwl.head_dim * fnnz        # 64 queries x 4 keys per kept block
+        fine = {"workload": fwl.name, "key_blocks_per_row": nK, "nnz_key_blocks": fnnz,
+                "kept_fraction": round(fnnz / (frows * nK), 4),
+                "select_ms": round(fsel_med, 4), "select_GB_s": round(fbytes / (fsel_med * 1e-3) / 1e9, 1),
+                "select_frac_hbm_peak": round(fbytes / (fsel_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "forward_ms": round(ffw_med, 4),
+                "forward_TFLOP_s": round(fflops / (ffw_med * 1e-3) / 1e12, 2),
+                "forward_frac_bf16_peak": round(fflops / (ffw_med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del fqd, fkd, fvd, fws, fci, fout, fwsa
+
     # dense reference: the same forward kernel over the full CSR (every tile kept)
     full_bufs = B.alloc_buffers(shape, dev)
     full_rp, full_ci = B.sparse_attn_full_csr(shape, full_bufs, stream=stream)
@@ -543,6 +632,8 @@ def main():
         rec["sip"] = sip
     if ibcs is not None:
         rec["ibcs"] = ibcs
+    if fine is not None:
+        rec["fine_4token"] = fine
     if sched is not None:
         rec["denoise_schedule"] = sched
     if not args.no_cpu_baseline:

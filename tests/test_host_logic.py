@@ -37,6 +37,8 @@ def test_pmc_summary_scales_by_the_copy_kernel(tmp_path):
     attn = "void sattn::attn_bf16_kernel<128, false, false, false>(sattn::AttnArgs)"
     biased = "void sattn::attn_bf16_kernel<128, true, false, false>(sattn::AttnArgs)"
     gathered = "void sattn::attn_bf16_kernel<128, false, true, false>(sattn::AttnArgs)"
+    fine_pool = "_ZN5sattn16fine_pool_kernelILi128EEEvPKDF16bPfS3_llNS_8PoolSideE"     # not the key pooling
+    sel_mangled = "_ZN5sattn18select_emit_kernelIDF16bLi128ELi60ELi0EEEvNS_10SelectArgsE"
     pool = "void sattn::pool_kernel<__bf16, 128>(__bf16 const*, __bf16*, long, int, sattn::PoolSide)"
     sel = "sattn::select_emit_kernel<bf16, 128, 60, 0>"
     sip = "sattn::select_emit_kernel<bf16, 128, 60, 1>"
@@ -44,10 +46,10 @@ def test_pmc_summary_scales_by_the_copy_kernel(tmp_path):
     # the copy reads and writes 1 GiB but the counters read half of it on fetch
     _write_counters(str(tmp_path / "fetch" / "a" / "run_counter_collection.csv"), "FETCH_SIZE",
                     [(copy, kib / 2), (attn, 1000.0), (attn, 1200.0), (biased, 9.0e9), (gathered, 9.0e9),
-                     (pool, 50.0), (sel, 70.0), (sip, 9.0e9)])
+                     (pool, 50.0), (fine_pool, 9.0e9), (sel, 70.0), (sel_mangled, 70.0), (sip, 9.0e9)])
     _write_counters(str(tmp_path / "write" / "a" / "run_counter_collection.csv"), "WRITE_SIZE",
                     [(copy, kib), (attn, 300.0), (attn, 300.0), (biased, 9.0e9), (gathered, 9.0e9), (pool, 5.0),
-                     (sel, 7.0), (sip, 9.0e9)])
+                     (fine_pool, 9.0e9), (sel, 7.0), (sel_mangled, 7.0), (sip, 9.0e9)])
     rec = bench.pmc_summary(str(tmp_path), "long_video")
     assert rec["fetch_scale"] == pytest.approx(2.0)
     assert rec["write_scale"] == pytest.approx(1.0)
