@@ -108,13 +108,21 @@ __device__ __forceinline__ float tile_commit(const f32x16 *acc_s, float c, float
 // grid tokens; accumulator v of half kt of this lane holds key 32 kt + 8 (v / 4) +
 // 4 hh + v % 4 (the 32x32 MFMA output layout, keys along its rows).
 constexpr float kMaskedScore = -0x1p100f;
+// km is wave-uniform: the lanes that keep element (kt, v) form a scalar lane mask
+// (lanes 0-31 hold key b of the element, lanes 32-63 key b + 4), applied by one
+// select each, with no per-lane shifts of the 64-bit key mask.
 __device__ __forceinline__ void mask_keys(f32x16 *sc, uint64_t km, int hh) {
+    (void)hh;
+    km = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(km >> 32)) << 32) |
+         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)km);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int key = 32 * kt + 8 * (v >> 2) + 4 * hh + (v & 3);
-            if (!((km >> key) & 1ull)) sc[kt][v] = kMaskedScore;
+            const int b = 32 * kt + 8 * (v >> 2) + (v & 3);
+            const uint64_t lanes = (((km >> b) & 1ull) ? 0x00000000ffffffffull : 0ull) |
+                                   (((km >> (b + 4)) & 1ull) ? 0xffffffff00000000ull : 0ull);
+            sc[kt][v] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? sc[kt][v] : kMaskedScore;
         }
 }
 
@@ -127,6 +135,24 @@ __device__ __forceinline__ uint64_t spread_nibbles(uint32_t m) {
     x = (x | (x << 6)) & 0x0303030303030303ull;
     x = (x | (x << 3)) & 0x1111111111111111ull;
     return x * 0xfull;
+}
+
+// LDS writes of some lanes made visible to the other lanes of the wave.
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Inclusive prefix max over lanes 0 .. 31 of values >= -1 (lanes 32-63: unspecified),
+// by row shifts within each 16-lane row and lane 15 carried into the second row.
+__device__ __forceinline__ int prefix_max32(int v, int lane) {
+    v = max(v, __builtin_amdgcn_update_dpp(-1, v, kDppShr1, 0xF, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(-1, v, kDppShr2, 0xF, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(-1, v, kDppShr4, 0xF, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(-1, v, kDppShr8, 0xF, 0xF, false));
+    const int r15 = __builtin_amdgcn_readlane(v, 15);
+    return (lane >= 16 && lane < 32) ? max(v, r15) : v;
 }
 
 // Scores of the next tile (MFMA) interleaved with the probabilities of the current
@@ -452,37 +478,114 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     }
 
     } else {
-    // The units of the gathered walk: chunks of up to 16 union entries, gathered into
-    // one tile each.
+    // The units of the gathered walk: the next up-to-16 entries of the union of the
+    // pair's two rows, gathered into one tile each.  Each row keeps a buffer of its next
+    // valid entries in a VGPR (lane l: the l-th next one, kNone past them), topped up 32
+    // raw entries at a time from a window loaded one top-up ahead; the skip rule of the
+    // tile walk (an entry counts if it is in range and above every earlier counted
+    // entry) applies to a whole window at once through a prefix max.  A unit's entries
+    // are then placed by rank: candidate i of row A lands at position i + (row B's
+    // first 16 candidates below it), a candidate of row B likewise, and an entry both
+    // rows hold once (from A).  Unseen entries of either row are larger than every
+    // placed one, since each buffer holds at least 16 entries or the whole rest of its
+    // row.
     struct Unit {
         int cols;         // lane e holds entry e's block (padded with the last one)
-        bool mine;        // this wave's row keeps some entry of the chunk
-        int n;            // entries in the chunk (0 past the end)
+        bool mine;        // this wave's row keeps some entry of the unit
+        int n;            // entries in the unit (0 past the end)
         uint64_t km;      // keys of this wave's entries
     };
-    auto next_unit = [&](Unit &u) {
-        {
-            u.n = 0;
-            u.cols = 0;
-            uint32_t my = 0;
-            int lastc = 0;
-            for (int e = 0; e < 16; ++e) {
-                int col;
-                bool mine;
-                float beta;
-                next_union(col, mine, beta);
-                if (col == kNone) break;
-                u.cols = lane == e ? col : u.cols;
-                my |= (uint32_t)mine << e;
-                lastc = col;
-                u.n = e + 1;
-            }
-            // entries past the chunk's end repeat its last block (in range and
-            // non-decreasing); their keys are masked
-            u.cols = lane >= u.n ? lastc : u.cols;
-            u.mine = my != 0;
-            u.km = spread_nibbles(my);
+    struct RowBuf {
+        int buf;          // lane l: the l-th next counted entry, kNone past cnt
+        int cnt;
+        int raw;          // lanes 0-31: raw entries next .. next + 31 (kNone past end)
+        int64_t next, end;
+        int last;         // the last counted entry (the skip rule's running max)
+    };
+    __shared__ int ubuf[4][32];           // per wave: unit columns [16], then flags [16]
+    int *ucol = ubuf[wave], *ufl = ubuf[wave] + 16;
+    auto raw_window = [&](int64_t base, int64_t e) { return lane < 32 && base + lane < e ? cv[base + lane] : kNone; };
+    auto topup = [&](RowBuf &r) {
+        while (r.cnt <= 32 && r.next < r.end) {
+            const int v = lane < 32 ? r.raw : kNone;
+            const bool inr = v >= 0 && v < a.nK;
+            const int incl = prefix_max32(inr ? v : -1, lane);
+            const int r15 = __builtin_amdgcn_readlane(incl, 15);
+            int ex = __builtin_amdgcn_update_dpp(-1, incl, kDppShr1, 0xF, 0xF, false);
+            ex = lane == 16 ? r15 : ex;
+            ex = max(ex, r.last);
+            const bool ok = lane < 32 && inr && v > ex;
+            const uint64_t om = __ballot(ok);
+            const int k = __popcll(om);
+            // the counted entries to lanes cnt .. cnt + k - 1 in order, the others to the
+            // remaining lanes (a permutation of the 64 lanes)
+            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(om >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)om, 0u));
+            const int to = ok ? r.cnt + below : (r.cnt + k + (lane - below)) & 63;
+            const int pushed = __builtin_amdgcn_ds_permute(to * 4, v);
+            r.buf = (lane >= r.cnt && lane < r.cnt + k) ? pushed : r.buf;
+            r.cnt += k;
+            r.last = max(r.last, __builtin_amdgcn_readlane(incl, 31));
+            r.next += 32;
+            r.raw = raw_window(r.next, r.end);
         }
+    };
+    auto consume = [&](RowBuf &r, int t) {
+        const int sh = __builtin_amdgcn_ds_bpermute(((lane + t) & 63) * 4, r.buf);
+        r.buf = lane + t < 64 ? sh : kNone;
+        r.cnt -= t;
+    };
+    RowBuf RA{kNone, 0, raw_window(begA, endA), begA, endA, lastA};
+    RowBuf RB{kNone, 0, raw_window(begB, endB), begB, endB, lastB};
+    auto next_unit = [&](Unit &u) {
+        topup(RA);
+        topup(RB);
+        const int xa = RA.buf, xbv = RB.buf;
+        // this lane's candidate: lanes 0-15 row A's first 16, lanes 16-31 row B's
+        const int xbs = __builtin_amdgcn_ds_bpermute(((lane - 16) & 63) * 4, xbv);
+        const bool isA = lane < 16, isB = lane >= 16 && lane < 32;
+        const int x = isA ? xa : (isB ? xbs : kNone);
+        // in one pass over the other row's 16 candidates: how many lie below this lane's
+        // candidate, and whether one equals it (an entry both rows hold)
+        int below_other = 0;
+        bool dup = false;
+#pragma unroll 2
+        for (int q = 0; q < 16; ++q) {
+            const int other = isA ? __builtin_amdgcn_readlane(xbv, q) : __builtin_amdgcn_readlane(xa, q);
+            below_other += other < x ? 1 : 0;
+            dup |= x != kNone && other == x;
+        }
+        // an entry both rows hold is placed once, as row A's: row A's count drops the
+        // row-B copies of such entries below it (one for each row-A entry below it that
+        // row B holds too), row B's candidates held by A are not placed
+        const uint64_t dam = __ballot(isA && dup);
+        const int dup_below = __builtin_amdgcn_mbcnt_hi((uint32_t)(dam >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)dam, 0u));
+        const int rank = isA ? below_other - dup_below : below_other;
+        // row B's own candidates (not held by A) by their order among themselves
+        const uint64_t om = __ballot(isB && !dup);
+        const int bown = __builtin_amdgcn_mbcnt_hi((uint32_t)(om >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)om, 0u));
+        const int pos = isA ? lane + rank : bown + rank;
+        const bool take = x != kNone && pos < 16 && (isA || (isB && !dup));
+        if (lane < 16) ufl[lane] = 0;
+        wave_lds_fence();
+        if (take) {
+            ucol[pos] = x;
+            ufl[pos] = isA ? (dup ? 3 : 1) : 2;
+        }
+        wave_lds_fence();
+        const int col = lane < 16 ? ucol[lane] : 0;
+        const int fl = lane < 16 ? ufl[lane] : 0;
+        const uint64_t present = __ballot(fl != 0);
+        u.n = __popcll(present);
+        const int lastc = u.n ? __builtin_amdgcn_readlane(col, u.n - 1) : 0;
+        u.cols = lane < u.n ? col : lastc;
+        const uint32_t my = (uint32_t)__ballot(lane < 16 && (fl & (grp ? 2 : 1)));
+        u.mine = my != 0;
+        u.km = spread_nibbles(my);
+        // both rows move past the unit's last entry
+        const int tA = __popcll(__ballot(isA && x != kNone && u.n && x <= lastc));
+        const int tB = __popcll(__ballot(isB && x != kNone && u.n && x <= lastc));
+        consume(RA, tA);
+        consume(RB, tB);
     };
     // direct loads of a unit into tile buffer buf
     auto issue_u = [&](const char *gw, const char *gh, uint32_t lds0, const Unit &u, int buf) {

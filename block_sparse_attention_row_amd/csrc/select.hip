@@ -642,6 +642,18 @@ __device__ __forceinline__ void select_emit_body(const SelectArgs &a) {
             kl[slot][kb] = *reinterpret_cast<const bf16x8 *>(kr + 16 * D + 512 * kb);
         }
     };
+    // one part of the group: the hi parts (lo = false) or the lo parts
+    auto load_k_part = [&](int cc, int slot, bool lo) {
+        const int gg = (kSelChunk / 16) * cc + wave;
+        const __bf16 *kr = ks + (int64_t)(gg < a.groups_per_head ? gg : 0) * (32 * D) + 8 * lane;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            if (lo)
+                kl[slot][kb] = *reinterpret_cast<const bf16x8 *>(kr + 16 * D + 512 * kb);
+            else
+                kh[slot][kb] = *reinterpret_cast<const bf16x8 *>(kr + 512 * kb);
+        }
+    };
     // ---- the largest key-mean norm of the head (for the scores' error bound), each
     //      wave over a slice of the head's key blocks
     if constexpr (MODE == 0) {
@@ -696,15 +708,34 @@ __device__ __forceinline__ void select_emit_body(const SelectArgs &a) {
         if (kPrefetch && cc + 1 < NCH) load_k(cc + 1, cur ^ 1);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         const __bf16 *qrow = qf + ii * qf_stride<D>() + 8 * kq;
+        if constexpr (kPrefetch) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const bf16x8 qh = *reinterpret_cast<const bf16x8 *>(qrow + 32 * kb);
-            const bf16x8 ql = *reinterpret_cast<const bf16x8 *>(qrow + D + 32 * kb);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql, kh[cur][kb], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kl[cur][kb], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kh[cur][kb], acc, 0, 0, 0);
+            for (int kb = 0; kb < KB; ++kb) {
+                const bf16x8 qh = *reinterpret_cast<const bf16x8 *>(qrow + 32 * kb);
+                const bf16x8 ql = *reinterpret_cast<const bf16x8 *>(qrow + D + 32 * kb);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql, kh[cur][kb], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kl[cur][kb], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kh[cur][kb], acc, 0, 0, 0);
+            }
+        } else {
+            // the products with the K hi parts first: those registers then take the next
+            // chunk's hi parts while the products with the lo parts run, and the lo parts
+            // follow; the loads get the lo products, the stage and the barrier ahead of use
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const bf16x8 qh = *reinterpret_cast<const bf16x8 *>(qrow + 32 * kb);
+                const bf16x8 ql = *reinterpret_cast<const bf16x8 *>(qrow + D + 32 * kb);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql, kh[0][kb], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kh[0][kb], acc, 0, 0, 0);
+            }
+            if (cc + 1 < NCH) load_k_part(cc + 1, 0, false);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const bf16x8 qh = *reinterpret_cast<const bf16x8 *>(qrow + 32 * kb);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kl[0][kb], acc, 0, 0, 0);
+            }
+            if (cc + 1 < NCH) load_k_part(cc + 1, 0, true);
         }
-        if (!kPrefetch && cc + 1 < NCH) load_k(cc + 1, 0);
         // acc[e] = S[row 4*kq + e][key 256*cc + 16*wave + ii]
         float *st = stage + (cc & 1) * kSelRows * kStageStride;
 #pragma unroll

@@ -833,6 +833,38 @@ def test_gather_of_whole_tiles_equals_the_tile_forward():
     assert torch.equal(out_g, out_t) and torch.equal(lse_g, lse_t)
 
 
+def test_gather_forward_long_lists_and_last_round_pieces():
+    """1,024 pairs of query blocks (so the plan cuts the last round of pairs into pieces)
+    over random 4-token lists, a few rows far longer than the rest (cut into long-row
+    pieces): sampled query blocks of both kinds, and random ones, against the oracle's
+    attention over the same list."""
+    wl = small_workload("gather_long", 1, 128, (16, 8, 16), "bf16", threshold=0.9, seed=94)
+    q, k, v, _ = make_inputs(wl, "A")
+    qd, kd, vd = P.to_device(q, k, v)
+    nK = 16 * wl.blocks
+    rng = np.random.default_rng(95)
+    keep = rng.random((wl.blocks, nK)) < 0.03
+    long_rows = rng.choice(wl.blocks, 6, replace=False)
+    keep[long_rows] = rng.random((6, nK)) < 0.7
+    keep[np.arange(wl.blocks), rng.integers(0, nK, wl.blocks)] = True       # no empty row
+    orp, oci = oracle.csr_from_mask(keep)
+    shape = P.shape_for(wl)
+    out, lse = B.sparse_attn_forward_gather(shape, qd, kd, vd, torch.as_tensor(orp.astype(np.int32)).cuda(),
+                                            torch.as_tensor(oci).cuda(), want_lse=True)
+    torch.cuda.synchronize()
+    tail = P.last_round_rows(wl)
+    assert tail.size > 0
+    rows = np.unique(np.concatenate([tail, long_rows, rng.choice(wl.blocks, 8, replace=False)]))
+    ref, ref_lse = oracle.attention_rows(q, k, v, orp, oci, rows, key_tokens=4)
+    got = out.float().cpu().reshape(-1, 64, wl.head_dim).numpy()[rows]
+    got_l = lse.cpu().reshape(-1, 64).numpy()[rows]
+    err = float(np.abs(got - ref).max())
+    lerr = float(np.abs(got_l - ref_lse).max())
+    print(f"gather long: nnz {len(oci)}, {rows.size} query blocks checked, max|err|={err:.3e} lse {lerr:.3e}",
+          flush=True)
+    assert err <= P.TOL["bf16"] and lerr <= P.LSE_TOL["bf16"]
+
+
 FINE = [
     # name, heads, d, block grid (nB), thr, reading, per-head threshold range
     ("d128_A_nB24", 2, 128, (2, 3, 4), 0.8, "A", None),            # 1 word a lane
