@@ -53,7 +53,7 @@ def _load():
         lib.oracle_pool.argtypes = [P, I, I, I, P, I, P]
         lib.oracle_select_rows.argtypes = [P, P, I, I, I, I, P, I, D, P, I, I, I, I, I, I, P, P, P]
         lib.oracle_attention_rows.argtypes = [P, P, P, I, I, I, I, P, P, P, P, P, I, D, P, P, P]
-        lib.oracle_attention_backward.argtypes = [P, P, P, P, P, I, I, I, I, P, P, D, P, P, P]
+        lib.oracle_attention_backward.argtypes = [P, P, P, P, P, I, I, I, I, P, P, P, D, P, P, P]
         for f in (lib.oracle_pool, lib.oracle_select_rows, lib.oracle_attention_rows, lib.oracle_attention_backward):
             f.restype = None
         _lib = lib
@@ -139,12 +139,13 @@ def select_rows(qbar: np.ndarray, kbar: np.ndarray, heads: int, block_grid: Sequ
 
 
 def attention_backward(q, k, v, dout, row_ptr, col_idx, scale: Optional[float] = None,
-                       tpb: int = TOKENS_PER_BLOCK, out=None):
+                       tpb: int = TOKENS_PER_BLOCK, out=None, valid=None):
     """Gradients (dq, dk, dv) [B, H, N, d] fp64 of the block-sparse attention for the
     upstream gradient dout, from their definition (see oracle.c).  row_ptr/col_idx: a
     valid CSR (ascending, in-range columns) over rows r = bh * nB + i.  `out`: the
     forward output as stored (e.g. rounded to bf16), used for D = dO . O; None
-    recomputes it in fp64."""
+    recomputes it in fp64.  `valid`: [N] bool, the token slots that are not padding
+    (partial tiles); padding slots get zero gradients and no weight as keys."""
     q, k, v, g = _f32(q), _f32(k), _f32(v), _f32(dout)
     o = None if out is None else _f32(out)
     if o is not None and o.shape != q.shape:
@@ -158,8 +159,11 @@ def attention_backward(q, k, v, dout, row_ptr, col_idx, scale: Optional[float] =
     dk = np.empty(q.shape, dtype=np.float64)
     dv = np.empty(q.shape, dtype=np.float64)
     sc = default_scale(d) if scale is None else float(scale)
-    _load().oracle_attention_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o), BH, nB, tpb, d, _ptr(rp), _ptr(ci), sc,
-                                      _ptr(dq), _ptr(dk), _ptr(dv))
+    vb = None if valid is None else np.ascontiguousarray(np.asarray(valid, dtype=bool), dtype=np.uint8)
+    if vb is not None and (vb.shape != (n,) or not vb.reshape(-1, tpb).any(axis=1).all()):
+        raise ValueError("valid needs one entry per token slot and a token in every block")
+    _load().oracle_attention_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o), BH, nB, tpb, d, _ptr(rp), _ptr(ci),
+                                      _ptr(vb), sc, _ptr(dq), _ptr(dk), _ptr(dv))
     return dq, dk, dv
 
 

@@ -252,13 +252,16 @@ void oracle_attention_rows(const float *q, const float *k, const float *v, int64
  * D_n is the product of dO_n with the forward output.  A caller that holds that
  * output, rounded as it was stored, passes it as `out` [BH][N][d] and D_n uses it;
  * with out == NULL, O_n is recomputed here in fp64.
+ * Partial tiles (`valid` [N], NULL when every slot is a token): the sums over n
+ * and m above run over token slots only, so padding slots get zero gradients
+ * and take no part in any other token's.
  * One head at a time (heads in parallel); within a head the rows are visited in
  * order, so the sums over n are in a fixed order.  Outputs are fp64 [BH][N][d].
  */
 void oracle_attention_backward(const float *q, const float *k, const float *v, const float *dout,
                                const float *out, int64_t BH, int64_t nB, int64_t tpb, int64_t d,
-                               const int64_t *row_ptr, const int32_t *col_idx, double scale, double *dq,
-                               double *dk, double *dv)
+                               const int64_t *row_ptr, const int32_t *col_idx, const uint8_t *valid,
+                               double scale, double *dq, double *dk, double *dv)
 {
     const int64_t N = nB * tpb;
 #pragma omp parallel
@@ -276,29 +279,39 @@ void oracle_attention_backward(const float *q, const float *k, const float *v, c
                 if (mc == 0) continue;
                 for (int64_t t = 0; t < tpb; ++t) {
                     const int64_t n = i * tpb + t;
+                    if (valid && !valid[n]) continue;               /* padding query: no gradient */
                     const float *qn = qh + n * d, *gn = gh + n * d;
-                    /* weights P_nm over the kept tokens, in kept order */
+                    /* weights P_nm over the kept tokens, in kept order (padding keys: none) */
                     double mx = -INFINITY;
                     int64_t m = 0;
                     for (int64_t e = beg; e < end; ++e)
                         for (int64_t u = 0; u < tpb; ++u, ++m) {
-                            const float *km = kh + (col_idx[e] * tpb + u) * d;
+                            const int64_t mt = col_idx[e] * tpb + u;
+                            if (valid && !valid[mt]) {
+                                w[m] = 0.0;
+                                continue;
+                            }
+                            const float *km = kh + mt * d;
                             double a = 0.0;
                             for (int64_t c = 0; c < d; ++c) a += (double)qn[c] * (double)km[c];
                             w[m] = a * scale;
                             if (w[m] > mx) mx = w[m];
                         }
                     double z = 0.0;
-                    for (int64_t mm = 0; mm < mc; ++mm) {
-                        w[mm] = exp(w[mm] - mx);
-                        z += w[mm];
-                    }
+                    m = 0;
+                    for (int64_t e = beg; e < end; ++e)
+                        for (int64_t u = 0; u < tpb; ++u, ++m) {
+                            if (valid && !valid[col_idx[e] * tpb + u]) continue;
+                            w[m] = exp(w[m] - mx);
+                            z += w[m];
+                        }
                     for (int64_t mm = 0; mm < mc; ++mm) w[mm] /= z;
                     /* O_n and D_n */
                     for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
                     m = 0;
                     for (int64_t e = beg; e < end; ++e)
                         for (int64_t u = 0; u < tpb; ++u, ++m) {
+                            if (valid && !valid[col_idx[e] * tpb + u]) continue;
                             const float *vm = vh + (col_idx[e] * tpb + u) * d;
                             for (int64_t c = 0; c < d; ++c) o[c] += w[m] * (double)vm[c];
                         }
@@ -311,6 +324,7 @@ void oracle_attention_backward(const float *q, const float *k, const float *v, c
                     for (int64_t e = beg; e < end; ++e)
                         for (int64_t u = 0; u < tpb; ++u, ++m) {
                             const int64_t mt = col_idx[e] * tpb + u;
+                            if (valid && !valid[mt]) continue;
                             const float *vm = vh + mt * d, *km = kh + mt * d;
                             double dp = 0.0;
                             for (int64_t c = 0; c < d; ++c) dp += (double)gn[c] * (double)vm[c];

@@ -852,6 +852,50 @@ def test_partial_tile_walk_matches_raster_bruteforce(grid, tile):
     assert np.all(got[~valid] == 0) and np.all(np.isneginf(got_l[~valid]))
 
 
+def test_backward_partial_tiles_match_raster_finite_differences():
+    """Partial tiles in the backward: on the padded tile-major layout (junk in every
+    padding slot, dO included) the gradients are zero at padding slots, and at token
+    slots equal central differences of sum(dO * O) with O the masked dense attention
+    on the raster grid (blocks from each token's grid coordinates, no tile-major order)."""
+    grid, tile = (1, 9, 10), (1, 8, 8)
+    n, d = 90, 4
+    q, k, v, g = (_rand((n, d), s).astype(np.float64) for s in (81, 82, 83, 84))
+    nB = int(np.prod(oracle.block_grid(grid, tile)))
+    mask = np.random.default_rng(85).random((nB, nB)) < 0.6
+    mask[np.arange(nB), np.arange(nB)] = True
+    mask[1, 3] = mask[3, 1] = True
+    rp, ci = oracle.csr_from_mask(mask)
+    sc = 0.45
+    valid = oracle.token_valid(grid, tile)
+    tiled = [oracle.to_tiles(a.astype(np.float32)[None, None], grid, tile) for a in (q, k, v, g)]
+    for a in tiled:
+        a[..., ~valid, :] = 7.0
+    dq, dk, dv = oracle.attention_backward(*tiled, rp, ci, scale=sc, valid=valid)
+    for gr in (dq, dk, dv):
+        assert np.all(gr[0, 0, ~valid] == 0)
+    perm = oracle.tile_order(grid, tile)
+
+    def loss(qq, kk, vv):
+        o, _ = brute.raster_block_mask_attention(qq, kk, vv, grid, tile, mask, sc)
+        return float(np.sum(g.astype(np.float32).astype(np.float64) * o))
+
+    q32, k32, v32 = (a.astype(np.float32).astype(np.float64) for a in (q, k, v))
+    h = 1e-6
+    for name, grad in (("q", dq), ("k", dk), ("v", dv)):
+        num = np.empty((n, d))
+        for i in range(n):
+            for c in range(d):
+                args = {"q": q32.copy(), "k": k32.copy(), "v": v32.copy()}
+                args[name][i, c] += h
+                lp = loss(args["q"], args["k"], args["v"])
+                args[name][i, c] -= 2 * h
+                lm = loss(args["q"], args["k"], args["v"])
+                num[i, c] = (lp - lm) / (2 * h)
+        got = np.empty((n, d))
+        got[perm[valid]] = grad[0, 0][valid]
+        assert np.abs(got - num).max() <= 1e-6 * max(1.0, np.abs(num).max()), name
+
+
 def test_whole_tiles_need_no_padding():
     """A grid of whole tiles has no padding slot and the same order as before."""
     grid, tile = (2, 16, 24), (1, 8, 8)
