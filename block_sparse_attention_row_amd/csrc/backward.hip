@@ -13,7 +13,11 @@
 //           S^T = K Q^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T;
 //   dV, dK  a pair of key blocks walks the transposed list (query tiles streamed):
 //           S = Q K^T, P, dP = dO V^T, dS, then dV^T += dO^T P and dK^T += Q^T dS.
-// Pairs are neighbours in time, as in the forward (pair_blocks).  Each pass is the
+// Pairs are neighbours in time, as in the forward (pair_blocks).  Partial tiles
+// (MASKED): padding queries carry lse2 = +inf from the prep kernel, so every P of
+// theirs is 0 and they neither receive nor pass on gradient; the dQ pass masks the
+// padding keys of the key tiles it streams, and the dV/dK pass writes zero rows for
+// the padding keys it owns.  Each pass is the
 // forward's tile machinery with other operands: the streamed tile is
 // the A operand of the scores and, read transposed, of the output product; the
 // pair's own rows sit in registers as the B operand.  The transposed list (for
@@ -28,7 +32,9 @@
 namespace sattn {
 
 // ---------------------------------------------------------------------------
-// D_n = dO_n . O_n and lse_n in log2 units, one token per D/8 lanes.
+// D_n = dO_n . O_n and lse_n in log2 units, one token per D/8 lanes.  A token whose
+// LSE is -inf (a padding query, or a query block that keeps no tile) gets lse2 = +inf,
+// so that every softmax weight recovered for it in the passes is 0.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16 *__restrict__ o, const __bf16 *__restrict__ dout,
                                                        const float *__restrict__ lse, float *__restrict__ lse2,
@@ -47,7 +53,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16 *__restrict_
     for (int off = 1; off < LPT; off <<= 1) acc += __shfl_xor(acc, off, 64);
     if (tok < ntok && lane % LPT == 0) {
         dn[tok] = acc;
-        lse2[tok] = lse[tok] * kLog2e;
+        const float l = lse[tok];
+        lse2[tok] = l == -INFINITY ? INFINITY : l * kLog2e;
     }
 }
 
@@ -148,7 +155,7 @@ enum BwdMode { kDQ = 0, kDKV = 1 };
 // kDKV: dV and dK in one walk of the transposed list (S and dP once per tile, four
 // products; 8% faster at d = 128 than a dV pass and a dK pass that each form S);
 // at d = 128 its two d-wide accumulators take one wave per SIMD.
-template <int D, int MODE>
+template <int D, int MODE, bool MASKED>
 __global__ __launch_bounds__(256, MODE == kDKV && D == 128 ? 1 : 2) void bwd_kernel(BwdArgs a) {
     using G = TileGeo<D>;
     constexpr int ROWB = G::ROWB, SLOTS = G::SLOTS, RPI = G::RPI, IPW = G::IPW, NDT = G::NDT, TILEB = G::TILEB;
@@ -325,6 +332,11 @@ __global__ __launch_bounds__(256, MODE == kDKV && D == 128 ? 1 : 2) void bwd_ker
         const float *ax = aux[BJ];
         f32x16 s[2], dp[2];
         tile_scores<D>(T1, f1, fo, s);
+        if constexpr (MASKED && MODE == kDQ) {
+            // padding keys of a partial key tile: no weight (dP needs no mask, P = 0 there)
+            const uint64_t km = a.slot_mask[__builtin_amdgcn_readfirstlane(col0)];
+            if (km != ~0ull) mask_keys(s, km, hh);
+        }
         tile_scores<D>(T2, f2, fo, dp);
         bf16x8 pf[4], pf2[4];           // pf2: dS of the fused pass (pf holds P there)
 #pragma unroll
@@ -371,6 +383,18 @@ __global__ __launch_bounds__(256, MODE == kDKV && D == 128 ? 1 : 2) void bwd_ker
     if (!has_row) return;
     // lane owns row 32 half + l32 of its block, d = 32 dt + 8 rr + 4 hh + {0..3}
     const float mult = MODE == kDKV ? 1.f : a.scale;
+    if constexpr (MASKED && MODE == kDKV) {
+        // a padding key of the pair's own block: zero dV and dK rows
+        if (!((a.slot_mask[grp && hasB ? blk_b : blk_a] >> (32 * half + l32)) & 1ull)) {
+#pragma unroll
+            for (int i = 0; i < NDT; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    acc[i][v] = 0.f;
+                    acc2[i][v] = 0.f;
+                }
+        }
+    }
     if (split) {
         // piece of a split pair: its scaled fp32 partial rows, summed by bwd_merge_kernel
         const int64_t at = ((int64_t)it.slot * 2 + grp) * (64 * D) + (32 * half + l32) * D;
@@ -472,8 +496,14 @@ int launch_backward(const BwdLaunch &L, hipStream_t s) {
     cdkv.grad = L.dv;
     cdkv.grad2 = L.dk;
     // each pass: the forward's plan over the list it walks, the pass, the merge of its pieces
-    auto plan = [&](const BwdArgs &w) {
+    auto plan = [&](const BwdArgs &w, bool masks) {
         AttnArgs pa = {};
+        if (masks && L.slot_mask_w != nullptr) {
+            // the first plan also writes the slot masks of partial tiles
+            pa.geo = L.geo;
+            pa.slot_mask_w = L.slot_mask_w;
+            pa.slot_mask = L.slot_mask_w;
+        }
         pa.row_ptr = w.ptr;
         pa.col_idx = w.idx;
         pa.col_count = w.idx_count;
@@ -486,20 +516,25 @@ int launch_backward(const BwdLaunch &L, hipStream_t s) {
         pa.plan = w.plan;
         return launch_plan(pa, s);
     };
-    if (plan(csr)) return -1;
+    const bool masked = L.args.slot_mask != nullptr;
+    if (plan(csr, true)) return -1;
     if (L.d == 128) {
-        bwd_kernel<128, kDQ><<<g, b, 0, s>>>(csr);
+        if (masked) bwd_kernel<128, kDQ, true><<<g, b, 0, s>>>(csr);
+        else bwd_kernel<128, kDQ, false><<<g, b, 0, s>>>(csr);
         bwd_merge_kernel<128><<<mg, b, 0, s>>>(csr, 0);
     } else {
-        bwd_kernel<64, kDQ><<<g, b, 0, s>>>(csr);
+        if (masked) bwd_kernel<64, kDQ, true><<<g, b, 0, s>>>(csr);
+        else bwd_kernel<64, kDQ, false><<<g, b, 0, s>>>(csr);
         bwd_merge_kernel<64><<<mg, b, 0, s>>>(csr, 0);
     }
-    if (plan(cdkv)) return -1;
+    if (plan(cdkv, false)) return -1;
     if (L.d == 128) {
-        bwd_kernel<128, kDKV><<<g, b, 0, s>>>(cdkv);
+        if (masked) bwd_kernel<128, kDKV, true><<<g, b, 0, s>>>(cdkv);
+        else bwd_kernel<128, kDKV, false><<<g, b, 0, s>>>(cdkv);
         bwd_merge_kernel<128><<<mg, b, 0, s>>>(cdkv, 1);
     } else {
-        bwd_kernel<64, kDKV><<<g, b, 0, s>>>(cdkv);
+        if (masked) bwd_kernel<64, kDKV, true><<<g, b, 0, s>>>(cdkv);
+        else bwd_kernel<64, kDKV, false><<<g, b, 0, s>>>(cdkv);
         bwd_merge_kernel<64><<<mg, b, 0, s>>>(cdkv, 1);
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;

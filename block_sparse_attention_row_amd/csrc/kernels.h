@@ -280,9 +280,14 @@ struct BwdArgs {
     // part[slot][block of the pair][64][d] (and the dK part to part2); a merge adds them
     SplitPlan plan;
     float *part, *part2;
+    // partial tiles: per-block masks of the slots that are grid tokens (written by the
+    // plan of the first pass), or null when every tile is whole
+    const uint64_t *slot_mask;
 };
 struct BwdLaunch {
     BwdArgs args;                 // fields common to the gradient passes
+    SlotGeo geo;                  // partial tiles: which slots are grid tokens
+    uint64_t *slot_mask_w;        // workspace [nB] for their masks, or null (whole tiles)
     const void *out;
     const float *lse;
     float *lse2, *dn;             // workspace

@@ -137,4 +137,30 @@ __device__ __forceinline__ void tile_pv(const char *V, const bf16x8 *pf, const F
     }
 }
 
+// Scores of a key tile whose block is cut by the grid edge (a partial tile): its
+// padding slots get kMaskedScore, so they take no weight.  The value is finite: with
+// the running max still at -inf on a row's first tile, -inf - (-inf) would be NaN, and
+// the device code is compiled without NaN semantics (the first tile's rescale is
+// triggered by an infinite row sum instead).  km: bit u set for the slots that are
+// grid tokens; accumulator v of half kt of this lane holds key 32 kt + 8 (v / 4) +
+// 4 hh + v % 4 (the 32x32 MFMA output layout, keys along its rows).
+constexpr float kMaskedScore = -0x1p100f;
+// km is wave-uniform: the lanes that keep element (kt, v) form a scalar lane mask
+// (lanes 0-31 hold key b of the element, lanes 32-63 key b + 4), applied by one
+// select each, with no per-lane shifts of the 64-bit key mask.
+__device__ __forceinline__ void mask_keys(f32x16 *sc, uint64_t km, int hh) {
+    (void)hh;
+    km = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(km >> 32)) << 32) |
+         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)km);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int b = 32 * kt + 8 * (v >> 2) + (v & 3);
+            const uint64_t lanes = (((km >> b) & 1ull) ? 0x00000000ffffffffull : 0ull) |
+                                   (((km >> (b + 4)) & 1ull) ? 0xffffffff00000000ull : 0ull);
+            sc[kt][v] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? sc[kt][v] : kMaskedScore;
+        }
+}
+
 }  // namespace sattn

@@ -75,7 +75,7 @@ extern "C" {
  * Problem shape.  head_dim must be 64 or 128; the tile must hold 64 tokens
  * (1 x 8 x 8 in the video workloads; any tile_t x tile_h x tile_w of volume 64
  * works) and need not divide the grid (see partial tiles above; the clustering
- * selector and the backward take whole tiles only).  scale is the
+ * selector takes whole tiles only).  scale is the
  * softmax scale of both the pooled scores and the attention; it must be
  * finite and >= 0, and 0 means 1/sqrt(head_dim).  The worst-case block
  * count B*H*nB*nB (nB = blocks per head) must fit in int32.
@@ -358,7 +358,7 @@ int32_t sparse_attn_radial_csr(const sparse_attn_shape *shape, const sparse_attn
                                void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
- * Backward of sparse_attn_forward (bf16 only, nB <= 4096, whole tiles; SPARSE_ATTN_UNSUPPORTED
+ * Backward of sparse_attn_forward (bf16 only, nB <= 4096; SPARSE_ATTN_UNSUPPORTED
  * otherwise):
  * the gradients for training (NABLA summary page, "Methodologie : NABLA" and its
  * training results).  With P the forward's softmax weights (recovered from lse)
@@ -371,7 +371,8 @@ int32_t sparse_attn_radial_csr(const sparse_attn_shape *shape, const sparse_attn
  *   dout        device, [B, H, N, d] bf16: dL/dout.
  *   row_ptr, col_idx, col_count: the block list the forward used (same rules).
  *   dq, dk, dv  device, [B, H, N, d] bf16, fully written (zeros where no tile
- *               reaches a row).
+ *               reaches a row, and at the padding slots of partial tiles, which
+ *               take no part in any other token's gradient).
  *   t_idx       device int32 [col_count], caller-owned scratch: receives the
  *               transposed block list (for each key block, the query blocks
  *               that keep it, ascending).

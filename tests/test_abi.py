@@ -420,8 +420,10 @@ def test_partial_tiles_size_by_ceil_grid():
 
 
 def test_partial_tiles_refused_where_whole_tiles_are_needed():
-    """The clustering selector (128-token clusters of whole tiles) and the backward take
-    whole tiles only: SPARSE_ATTN_UNSUPPORTED on the host, before any launch."""
+    """The clustering selector (128-token clusters of whole tiles) takes whole tiles
+    only: SPARSE_ATTN_UNSUPPORTED on the host, before any launch.  The backward takes
+    partial tiles: on such a grid it passes the shape checks and stops at the null
+    pointer (no launch)."""
     L = B.lib()
     s = _shape(grid=(20, 30, 45))
     ws = B.sparse_attn_workspace_size(s)
@@ -429,8 +431,8 @@ def test_partial_tiles_refused_where_whole_tiles_are_needed():
     params = B.SelectParams(0.9, None, -1, -1, -1)
     assert L.sparse_attn_select_ibcs(ctypes.byref(s), ctypes.byref(params), A, A, A, A, cap, A, ws,
                                      None) == B.SPARSE_ATTN_UNSUPPORTED
-    assert L.sparse_attn_backward(ctypes.byref(s), A, A, A, A, A, A, A, A, cap, A, A, A, A, A, ws,
-                                  None) == B.SPARSE_ATTN_UNSUPPORTED
+    assert L.sparse_attn_backward(ctypes.byref(s), None, A, A, A, A, A, A, A, cap, A, A, A, A, A, ws,
+                                  None) == B.SPARSE_ATTN_INVALID_ARGUMENT
 
 
 def test_fine_selection_sizes_and_host_checks():

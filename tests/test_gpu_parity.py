@@ -570,6 +570,39 @@ def test_backward_empty_rows_unused_keys_and_skipped_entries():
     assert torch.equal(dq2, dq) and torch.equal(dk2, dk) and torch.equal(dv2, dv)
 
 
+@pytest.mark.parametrize("name,d,grid,thr,reading", [("bf16_d128_2x12x20", 128, (2, 12, 20), 0.8, "A"),
+                                                      ("bf16_d64_3x13x11_B", 64, (3, 13, 11), 0.9, "B")])
+def test_backward_partial_tiles(name, d, grid, thr, reading):
+    """Partial tiles in the backward: dQ, dK, dV against the oracle with the same token
+    validity, junk in every padding slot of Q, K, V and dO; padding slots get exact
+    zeros in all three gradients."""
+    wl = small_workload("bwd_partial_" + name, 2, d, (0, 0, 0), "bf16", threshold=thr, seed=73, grid=grid)
+    assert wl.partial
+    print(f"\n[case] backward partial tiles {name} blocks={wl.blocks} slots={wl.slots}", flush=True)
+    q, k, v, _ = make_inputs(wl, reading)
+    gen = torch.Generator().manual_seed(74)
+    g = torch.randn(q.shape, generator=gen).to(torch.bfloat16)
+    q, k, v, g = _junk_padding(wl, q, k, v, g)
+    valid = P.valid_of(wl)
+    qd, kd, vd = P.to_device(q, k, v)
+    shape = P.shape_for(wl)
+    qbar, kbar = oracle.pool(q, valid=valid), oracle.pool(k, valid=valid)
+    mask = oracle.select_rows(qbar, kbar, wl.heads, wl.block_grid, float(wl.threshold)) != 0
+    orp, oci = oracle.csr_from_mask(mask)
+    out, lse = P.gpu_forward(wl, qd, kd, vd, orp, oci)
+    rpd = torch.as_tensor(orp.astype(np.int32)).cuda()
+    cid = torch.as_tensor(oci).cuda()
+    dq, dk, dv = B.sparse_attn_backward(shape, qd, kd, vd, out, lse, g.cuda(), rpd, cid)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward(q, k, v, g, orp, oci, valid=valid)
+    errs = [_rel_err(x, r) for x, r in ((dq, rq), (dk, rk), (dv, rv))]
+    print(f"backward partial rel err dq {errs[0]:.3e} dk {errs[1]:.3e} dv {errs[2]:.3e}", flush=True)
+    assert max(errs[:2]) <= P.BWD_TOL_DQK and errs[2] <= P.BWD_TOL_DV
+    vt = torch.as_tensor(valid)
+    for gr in (dq, dk, dv):
+        assert torch.all(gr.cpu()[..., ~vt, :] == 0)
+
+
 def test_deterministic_and_no_nan():
     wl = small_workload("det", 3, 128, (3, 4, 5), "bf16", threshold=0.8, window=(1, 1, 1), seed=17)
     q, k, v, thr = make_inputs(wl, "A")
