@@ -97,7 +97,8 @@ def kernel_ident(name):
             n = int(name[i:j])
             ident, i = name[j:j + n], j + n
         return ident
-    return name.split("(")[0].split("<")[0].split("::")[-1].split()[-1]
+    head = name.split("<")[0].split("(")[0].split("::")[-1].split()
+    return head[-1] if head else ""
 
 
 def template_args(name):

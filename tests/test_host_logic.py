@@ -113,6 +113,9 @@ def test_plain_attention_kernel_names():
     for flags in ("true, false, false", "false, true, false", "false, false, true"):
         assert not bench.is_plain_attention(f"void sattn::attn_bf16_kernel<128, {flags}>(sattn::AttnArgs)")
     assert not bench.is_plain_attention("void sattn::pool_kernel<__bf16, 128>(...)")
+    # library kernels whose names carry no identifier before the parameters
+    for odd in ("void at::native::(anonymous namespace)::fill_kernel(float*)", "void (anonymous)", "", "()"):
+        assert not bench.is_plain_attention(odd) and not bench.is_cdf_selection(odd)
 
 
 def test_cpu_baseline_sample_is_two_heads_of_32_blocks():
