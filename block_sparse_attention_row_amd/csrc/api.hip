@@ -707,7 +707,6 @@ int32_t sparse_attn_backward(const sparse_attn_shape *shape, const void *q, cons
     Dims d;
     int32_t st = check_shape(shape, &d);
     if (st) return st;
-    if (shape->dtype != SPARSE_ATTN_BF16) return SPARSE_ATTN_UNSUPPORTED;
     if (d.nB > kSelectMaxBlocks) return SPARSE_ATTN_UNSUPPORTED;   // a row's bitmask is held in LDS
     if (!q || !k || !v || !out || !lse || !dout || !row_ptr || !dq || !dk || !dv || !workspace)
         return SPARSE_ATTN_INVALID_ARGUMENT;
@@ -743,7 +742,9 @@ int32_t sparse_attn_backward(const sparse_attn_shape *shape, const void *q, cons
     b.args.part = (float *)(ws + L.part_o);
     b.args.part2 = (float *)(ws + L.part_b);
     b.geo = slot_geo(shape, d);
-    b.slot_mask_w = d.partial ? (uint64_t *)(ws + L.slot_mask) : nullptr;
+    b.args.geo = b.geo;
+    b.f32 = shape->dtype == SPARSE_ATTN_F32;
+    b.slot_mask_w = (d.partial && !b.f32) ? (uint64_t *)(ws + L.slot_mask) : nullptr;
     b.args.slot_mask = b.slot_mask_w;
     b.out = out;
     b.lse = lse;

@@ -468,11 +468,248 @@ __global__ __launch_bounds__(256) void bwd_merge_kernel(BwdArgs a, int two) {
 }
 
 // ---------------------------------------------------------------------------
+// fp32 inputs: the same gradients with fp32 MFMA (v_mfma_f32_32x32x2_f32), in the plain
+// form of the fp32 forward: one workgroup of 2 waves per block (32 rows a wave), one
+// tile at a time through LDS, no pieces.  As in that forward, the k = 2 of each MFMA
+// makes the score accumulators the operand of the next product element by element:
+// accumulator v of half h of a lane holds tile row 32 h + 8 (v / 4) + 4 hh + v % 4
+// against the lane's own row l32, which is the k = hh slot of that product.
+
+// D_n = dO_n . O_n and lse2 (lse in log2 units, -inf turned to +inf), one token a thread.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_f32_kernel(const float *__restrict__ o, const float *__restrict__ dout,
+                                                           const float *__restrict__ lse, float *__restrict__ lse2,
+                                                           float *__restrict__ dn, int64_t ntok) {
+    const int64_t tok = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (tok >= ntok) return;
+    const f32x4 *x = reinterpret_cast<const f32x4 *>(o + tok * D);
+    const f32x4 *g = reinterpret_cast<const f32x4 *>(dout + tok * D);
+    float acc = 0.f;
+#pragma unroll 4
+    for (int c = 0; c < D / 4; ++c) {
+        const f32x4 a = x[c], b = g[c];
+        acc += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+    }
+    dn[tok] = acc;
+    const float l = lse[tok];
+    lse2[tok] = l == -INFINITY ? INFINITY : l * kLog2e;
+}
+
+// dQ: block row `row` walks its kept key tiles (the forward's skip rule).
+//   S^T = K Q^T, dP^T = V dO^T, P = 2^(S c - lse2), dS = P (dP - D), dQ^T += K^T dS^T.
+template <int D>
+__global__ __launch_bounds__(128) void bwd_dq_f32_kernel(BwdArgs a, int64_t rows) {
+    constexpr int KS = D + 1, NDT = D / 32;
+    __shared__ float Ks[64 * KS];
+    __shared__ float Vs[64 * KS];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, hh = lane >> 5, l32 = lane & 31;
+    const int64_t row = xcd_remap(blockIdx.x, rows);
+    const int64_t bh = row / a.nB;
+    const int64_t N = (int64_t)a.nB * 64;
+    const int64_t qrow = bh * N + (row % a.nB) * 64 + 32 * wave + l32;
+    const float *kg = (const float *)a.k + bh * N * D;
+    const float *vg = (const float *)a.v + bh * N * D;
+    float qf[D / 2], gf[D / 2];
+#pragma unroll
+    for (int c = 0; c < D / 2; ++c) {
+        qf[c] = ((const float *)a.q)[qrow * D + 2 * c + hh];
+        gf[c] = ((const float *)a.dout)[qrow * D + 2 * c + hh];
+    }
+    const float l2 = a.lse2[qrow], dq = a.dn[qrow];
+    f32x16 acc[NDT];
+#pragma unroll
+    for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+
+    int64_t beg = a.ptr[row], end = a.ptr[row + 1];
+    end = end < a.idx_count ? end : a.idx_count;
+    beg = beg < 0 ? 0 : beg;
+    const bool partial = a.geo.partial != 0;
+    int last = -1;
+    for (int64_t e = beg; e < end; ++e) {
+        const int col = a.idx[e];
+        if (col <= last || col >= a.nB) continue;
+        last = col;
+        const uint64_t km = partial ? __ballot(slot_valid(a.geo, col, lane)) : ~0ull;
+        __syncthreads();
+        const float *kt = kg + (int64_t)col * 64 * D, *vt = vg + (int64_t)col * 64 * D;
+        for (int c = t; c < 64 * D / 4; c += 128) {
+            const f32x4 kv = *reinterpret_cast<const f32x4 *>(kt + 4 * c);
+            const f32x4 vv = *reinterpret_cast<const f32x4 *>(vt + 4 * c);
+            const int key = (4 * c) / D, d4 = (4 * c) % D;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                Ks[key * KS + d4 + u] = kv[u];
+                Vs[key * KS + d4 + u] = vv[u];
+            }
+        }
+        __syncthreads();
+        f32x16 sc[2], dp[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                sc[h][v] = 0.f;
+                dp[h][v] = 0.f;
+            }
+#pragma unroll
+            for (int c = 0; c < D / 2; ++c) {
+                sc[h] = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[(32 * h + l32) * KS + 2 * c + hh], qf[c], sc[h], 0, 0, 0);
+                dp[h] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[(32 * h + l32) * KS + 2 * c + hh], gf[c], dp[h], 0, 0, 0);
+            }
+        }
+        if (km != ~0ull) mask_keys(sc, km, hh);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[h][v], a.scale_log2, -l2));
+                sc[h][v] = p * (dp[h][v] - dq);
+            }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int key = 32 * h + 8 * (v >> 2) + 4 * hh + (v & 3);
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[key * KS + 32 * dt + l32], sc[h][v], acc[dt], 0, 0, 0);
+            }
+    }
+    float *og = (float *)a.grad + qrow * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            f32x4 w;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) w[u] = acc[dt][4 * rr + u] * a.scale;
+            *reinterpret_cast<f32x4 *>(og + 32 * dt + 8 * rr + 4 * hh) = w;
+        }
+}
+
+// dV and dK: key block `row` walks the query blocks that keep it (the transposed list).
+//   S = Q K^T, dP = dO V^T, P, dS as above; dV^T += dO^T P, dK^T += Q^T dS.
+template <int D>
+__global__ __launch_bounds__(128) void bwd_dkv_f32_kernel(BwdArgs a, int64_t rows) {
+    constexpr int KS = D + 1, NDT = D / 32;
+    __shared__ float Qs[64 * KS];
+    __shared__ float Gs[64 * KS];
+    __shared__ float Ls[64], Dd[64];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, hh = lane >> 5, l32 = lane & 31;
+    const int64_t row = xcd_remap(blockIdx.x, rows);
+    const int64_t bh = row / a.nB;
+    const int64_t N = (int64_t)a.nB * 64;
+    const int32_t kb = (int32_t)(row % a.nB);
+    const int64_t krow = bh * N + (int64_t)kb * 64 + 32 * wave + l32;
+    const float *qg = (const float *)a.q + bh * N * D;
+    const float *gg = (const float *)a.dout + bh * N * D;
+    float kf[D / 2], vf[D / 2];
+#pragma unroll
+    for (int c = 0; c < D / 2; ++c) {
+        kf[c] = ((const float *)a.k)[krow * D + 2 * c + hh];
+        vf[c] = ((const float *)a.v)[krow * D + 2 * c + hh];
+    }
+    f32x16 adv[NDT], adk[NDT];
+#pragma unroll
+    for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            adv[i][v] = 0.f;
+            adk[i][v] = 0.f;
+        }
+    int64_t beg = a.ptr[row], end = a.ptr[row + 1];
+    end = end < a.idx_count ? end : a.idx_count;
+    beg = beg < 0 ? 0 : beg;
+    for (int64_t e = beg; e < end; ++e) {
+        const int qb = a.idx[e];          // the transposed list holds valid, ascending blocks
+        __syncthreads();
+        const int64_t q0 = (int64_t)qb * 64;
+        const float *qt = qg + q0 * D, *gt = gg + q0 * D;
+        for (int c = t; c < 64 * D / 4; c += 128) {
+            const f32x4 qv = *reinterpret_cast<const f32x4 *>(qt + 4 * c);
+            const f32x4 gv = *reinterpret_cast<const f32x4 *>(gt + 4 * c);
+            const int r = (4 * c) / D, d4 = (4 * c) % D;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                Qs[r * KS + d4 + u] = qv[u];
+                Gs[r * KS + d4 + u] = gv[u];
+            }
+        }
+        if (t < 64) {
+            Ls[t] = a.lse2[bh * N + q0 + t];
+            Dd[t] = a.dn[bh * N + q0 + t];
+        }
+        __syncthreads();
+        f32x16 sc[2], dp[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                sc[h][v] = 0.f;
+                dp[h][v] = 0.f;
+            }
+#pragma unroll
+            for (int c = 0; c < D / 2; ++c) {
+                sc[h] = __builtin_amdgcn_mfma_f32_32x32x2f32(Qs[(32 * h + l32) * KS + 2 * c + hh], kf[c], sc[h], 0, 0, 0);
+                dp[h] = __builtin_amdgcn_mfma_f32_32x32x2f32(Gs[(32 * h + l32) * KS + 2 * c + hh], vf[c], dp[h], 0, 0, 0);
+            }
+        }
+        // P and dS of query 32 h + 8 (v / 4) + 4 hh + v % 4 against this lane's key
+        // (padding queries carry lse2 = +inf: P = 0)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int qi = 32 * h + 8 * (v >> 2) + 4 * hh + (v & 3);
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[h][v], a.scale_log2, -Ls[qi]));
+                sc[h][v] = p;
+                dp[h][v] = p * (dp[h][v] - Dd[qi]);
+            }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int qi = 32 * h + 8 * (v >> 2) + 4 * hh + (v & 3);
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    adv[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(Gs[qi * KS + 32 * dt + l32], sc[h][v], adv[dt], 0, 0, 0);
+                    adk[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(Qs[qi * KS + 32 * dt + l32], dp[h][v], adk[dt], 0, 0, 0);
+                }
+            }
+    }
+    // a padding key of a partial tile: zero rows
+    const bool valid = !a.geo.partial || slot_valid(a.geo, kb, 32 * wave + l32);
+    float *ov = (float *)a.grad + krow * D, *ok = (float *)a.grad2 + krow * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            f32x4 wv, wk;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                wv[u] = valid ? adv[dt][4 * rr + u] : 0.f;
+                wk[u] = valid ? adk[dt][4 * rr + u] * a.scale : 0.f;
+            }
+            *reinterpret_cast<f32x4 *>(ov + 32 * dt + 8 * rr + 4 * hh) = wv;
+            *reinterpret_cast<f32x4 *>(ok + 32 * dt + 8 * rr + 4 * hh) = wk;
+        }
+}
+
+// ---------------------------------------------------------------------------
 int launch_backward(const BwdLaunch &L, hipStream_t s) {
     const int64_t ntok = L.rows * 64;
     const int tpw = 64 / (L.d / 8);
     const dim3 pg((unsigned)((ntok + 4 * tpw - 1) / (4 * tpw))), pb(256);
-    if (L.d == 128)
+    const bool f32 = L.f32;
+    if (f32) {
+        const dim3 fg((unsigned)((ntok + 255) / 256));
+        if (L.d == 128)
+            bwd_prep_f32_kernel<128><<<fg, pb, 0, s>>>((const float *)L.out, (const float *)L.args.dout, L.lse, L.lse2, L.dn, ntok);
+        else
+            bwd_prep_f32_kernel<64><<<fg, pb, 0, s>>>((const float *)L.out, (const float *)L.args.dout, L.lse, L.lse2, L.dn, ntok);
+    } else if (L.d == 128)
         bwd_prep_kernel<128><<<pg, pb, 0, s>>>((const __bf16 *)L.out, (const __bf16 *)L.args.dout, L.lse, L.lse2, L.dn, ntok);
     else
         bwd_prep_kernel<64><<<pg, pb, 0, s>>>((const __bf16 *)L.out, (const __bf16 *)L.args.dout, L.lse, L.lse2, L.dn, ntok);
@@ -495,6 +732,18 @@ int launch_backward(const BwdLaunch &L, hipStream_t s) {
     BwdArgs cdkv = csc;
     cdkv.grad = L.dv;
     cdkv.grad2 = L.dk;
+    if (f32) {
+        // one workgroup per block, no pieces
+        const dim3 rg((unsigned)L.rows), rb(128);
+        if (L.d == 128) {
+            bwd_dq_f32_kernel<128><<<rg, rb, 0, s>>>(csr, L.rows);
+            bwd_dkv_f32_kernel<128><<<rg, rb, 0, s>>>(cdkv, L.rows);
+        } else {
+            bwd_dq_f32_kernel<64><<<rg, rb, 0, s>>>(csr, L.rows);
+            bwd_dkv_f32_kernel<64><<<rg, rb, 0, s>>>(cdkv, L.rows);
+        }
+        return hipGetLastError() == hipSuccess ? 0 : -1;
+    }
     // each pass: the forward's plan over the list it walks, the pass, the merge of its pieces
     auto plan = [&](const BwdArgs &w, bool masks) {
         AttnArgs pa = {};

@@ -283,6 +283,7 @@ struct BwdArgs {
     // partial tiles: per-block masks of the slots that are grid tokens (written by the
     // plan of the first pass), or null when every tile is whole
     const uint64_t *slot_mask;
+    SlotGeo geo;                  // the same slots from the grid (fp32 passes)
 };
 struct BwdLaunch {
     BwdArgs args;                 // fields common to the gradient passes
@@ -299,6 +300,7 @@ struct BwdLaunch {
     void *dq, *dk, *dv;
     int64_t rows, BH;
     int32_t nB, nW, d;
+    bool f32;                     // fp32 tensors (else bf16)
 };
 int launch_backward(const BwdLaunch &L, hipStream_t s);
 

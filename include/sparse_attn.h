@@ -358,7 +358,7 @@ int32_t sparse_attn_radial_csr(const sparse_attn_shape *shape, const sparse_attn
                                void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
- * Backward of sparse_attn_forward (bf16 only, nB <= 4096; SPARSE_ATTN_UNSUPPORTED
+ * Backward of sparse_attn_forward (bf16 or fp32, nB <= 4096; SPARSE_ATTN_UNSUPPORTED
  * otherwise):
  * the gradients for training (NABLA summary page, "Methodologie : NABLA" and its
  * training results).  With P the forward's softmax weights (recovered from lse)
@@ -366,18 +366,20 @@ int32_t sparse_attn_radial_csr(const sparse_attn_shape *shape, const sparse_attn
  *   dV = P^T dO,  dS = P o (dO V^T - rowsum(dO o O)),  dQ = scale dS K,
  *   dK = scale dS^T Q.
  *
- *   q, k, v, out  device, [B, H, N, d] bf16: the forward's inputs and output.
+ *   q, k, v, out  device, [B, H, N, d] in shape->dtype: the forward's inputs and output.
  *   lse         device fp32 [B, H, N]: the forward's log-sum-exp (required).
- *   dout        device, [B, H, N, d] bf16: dL/dout.
+ *   dout        device, [B, H, N, d] in shape->dtype: dL/dout.
  *   row_ptr, col_idx, col_count: the block list the forward used (same rules).
- *   dq, dk, dv  device, [B, H, N, d] bf16, fully written (zeros where no tile
+ *   dq, dk, dv  device, [B, H, N, d] in shape->dtype, fully written (zeros where no tile
  *               reaches a row, and at the padding slots of partial tiles, which
  *               take no part in any other token's gradient).
  *   t_idx       device int32 [col_count], caller-owned scratch: receives the
  *               transposed block list (for each key block, the query blocks
  *               that keep it, ascending).
  *   workspace   as in sparse_attn_forward.
- * The result is deterministic (no atomics; fixed summation order).
+ * The result is deterministic (no atomics; fixed summation order).  bf16 rounds P
+ * and dS to bf16 for its MFMA products; fp32 keeps them fp32 (fp32 MFMA), with one
+ * workgroup per block and no splitting of long rows.
  */
 int32_t sparse_attn_backward(const sparse_attn_shape *shape, const void *q, const void *k, const void *v,
                              const void *out, const float *lse, const void *dout, const int32_t *row_ptr,

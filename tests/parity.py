@@ -49,6 +49,12 @@ LSE_TOL = {"bf16": 5e-3, "f32": 1e-4}
 # |dO| |O| u, passed into dS the same way.  BWD_TOL_DQK = 5.1u = 2e-2 covers both.
 BWD_TOL_DV = 5e-3
 BWD_TOL_DQK = 2e-2
+# Backward (fp32): P and dS stay fp32 (u = 2^-24 per rounding, v_exp_f32 within a few
+# ulps), so the errors are those of fp32 sums over the kept keys, times the same
+# cancellation factor of up to ~9 in dQ and dK, and D taken from the fp32 forward
+# output (1e-4 absolute, TOL["f32"]) when the oracle recomputes O in fp64.  One bound
+# for all three gradients: the fp32 forward's, 1e-4 of max |ref|.
+BWD_TOL_F32 = 1e-4
 
 
 def to_device(*ts):

@@ -228,7 +228,8 @@ def test_backward_rejects_before_launch():
         x = dict(ok, **kw)
         return f(ctypes.byref(x.pop("shape", s)), x["q"], x["k"], x["v"], x["o"], x["lse"], x["g"], x["rp"], x["ci"],
                  x["cc"], x["dq"], x["dk"], x["dv"], x["ti"], x["ws"], x["wsb"], None)
-    assert call(shape=_shape(dtype="f32")) == B.SPARSE_ATTN_UNSUPPORTED
+    # fp32 passes the dtype check and stops at the missing lse, like bf16
+    assert call(shape=_shape(dtype="f32"), lse=None) == B.SPARSE_ATTN_INVALID_ARGUMENT
     assert call(lse=None) == B.SPARSE_ATTN_INVALID_ARGUMENT
     assert call(ti=None) == B.SPARSE_ATTN_INVALID_ARGUMENT
     assert call(dk=A + 4) == B.SPARSE_ATTN_INVALID_ARGUMENT

@@ -603,6 +603,43 @@ def test_backward_partial_tiles(name, d, grid, thr, reading):
         assert torch.all(gr.cpu()[..., ~vt, :] == 0)
 
 
+@pytest.mark.parametrize("name,d,grid,bgrid,thr,reading", [
+    ("f32_d64", 64, None, (2, 3, 5), 0.9, "A"),
+    ("f32_d128_B", 128, None, (3, 4, 3), 0.8, "B"),
+    ("f32_d64_partial_3x13x11", 64, (3, 13, 11), (0, 0, 0), 0.85, "A"),
+])
+def test_backward_f32(name, d, grid, bgrid, thr, reading):
+    """The fp32 backward (fp32 MFMA, one workgroup per block) against the oracle on the
+    same block list: whole tiles at d = 64 and 128 (odd block counts), and a grid with
+    partial tiles (junk in every padding slot; exact zeros there)."""
+    wl = small_workload("bwd_f32_" + name, 2, d, bgrid, "f32", threshold=thr, seed=75, grid=grid)
+    print(f"\n[case] fp32 backward {name} blocks={wl.blocks} slots={wl.slots}", flush=True)
+    q, k, v, _ = make_inputs(wl, reading)
+    gen = torch.Generator().manual_seed(76)
+    g = torch.randn(q.shape, generator=gen, dtype=torch.float32)
+    valid = P.valid_of(wl)
+    if valid is not None:
+        q, k, v, g = _junk_padding(wl, q, k, v, g)
+    qd, kd, vd = P.to_device(q, k, v)
+    shape = P.shape_for(wl)
+    qbar, kbar = oracle.pool(q, valid=valid), oracle.pool(k, valid=valid)
+    mask = oracle.select_rows(qbar, kbar, wl.heads, wl.block_grid, float(wl.threshold)) != 0
+    orp, oci = oracle.csr_from_mask(mask)
+    out, lse = P.gpu_forward(wl, qd, kd, vd, orp, oci)
+    rpd = torch.as_tensor(orp.astype(np.int32)).cuda()
+    cid = torch.as_tensor(oci).cuda()
+    dq, dk, dv = B.sparse_attn_backward(shape, qd, kd, vd, out, lse, g.cuda(), rpd, cid)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward(q, k, v, g, orp, oci, valid=valid)
+    errs = [_rel_err(x, r) for x, r in ((dq, rq), (dk, rk), (dv, rv))]
+    print(f"fp32 backward rel err dq {errs[0]:.3e} dk {errs[1]:.3e} dv {errs[2]:.3e}", flush=True)
+    assert max(errs) <= P.BWD_TOL_F32
+    if valid is not None:
+        vt = torch.as_tensor(valid)
+        for gr in (dq, dk, dv):
+            assert torch.all(gr.cpu()[..., ~vt, :] == 0)
+
+
 def test_deterministic_and_no_nan():
     wl = small_workload("det", 3, 128, (3, 4, 5), "bf16", threshold=0.8, window=(1, 1, 1), seed=17)
     q, k, v, thr = make_inputs(wl, "A")
