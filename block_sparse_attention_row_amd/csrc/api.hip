@@ -488,7 +488,6 @@ int32_t sparse_attn_forward_biased(const sparse_attn_shape *shape, const void *q
                                    const int32_t *row_ptr, const int32_t *col_idx, const float *col_bias,
                                    int64_t col_count, void *out, float *lse, void *workspace,
                                    int64_t workspace_bytes, void *stream) {
-    if (shape && shape->dtype != SPARSE_ATTN_BF16) return SPARSE_ATTN_UNSUPPORTED;
     if (col_count > 0 && !col_bias) return SPARSE_ATTN_INVALID_ARGUMENT;
     // an empty list has no offsets to apply: the plain kernel gives the same result
     return forward_impl(shape, q, k, v, row_ptr, col_idx, col_count > 0 ? col_bias : nullptr, col_count, out, lse,
@@ -501,7 +500,6 @@ int32_t sparse_attn_select_sip(const sparse_attn_shape *shape, const sparse_attn
     Dims d;
     int32_t st = check_shape(shape, &d);
     if (st) return st;
-    if (shape->dtype != SPARSE_ATTN_BF16) return SPARSE_ATTN_UNSUPPORTED;
     if (!params || !q || !k || !row_ptr || !col_idx || !col_bias || !workspace) return SPARSE_ATTN_INVALID_ARGUMENT;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(row_ptr, 4) || !aligned(col_idx, 4) || !aligned(col_bias, 4) ||
         !aligned(workspace, 16))
@@ -551,7 +549,7 @@ int32_t sparse_attn_select_sip(const sparse_attn_shape *shape, const sparse_attn
     a.budget = params->budget;
     a.seed = params->seed;
     a.col_bias = col_bias;
-    if (launch_select_sip(a, (int)d.D, s)) return SPARSE_ATTN_HIP_ERROR;
+    if (launch_select_sip(a, (int)d.D, shape->dtype, s)) return SPARSE_ATTN_HIP_ERROR;
     return SPARSE_ATTN_OK;
 }
 

@@ -906,8 +906,10 @@ __global__ __launch_bounds__(512) void merge_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // fp32 inputs, fp32 MFMA (v_mfma_f32_32x32x2_f32).  Same structure; with
 // k = 2 per instruction the S^T accumulators map one-to-one onto the P^T
-// operand, so V stays row-major in LDS.
-template <int D>
+// operand, so V stays row-major in LDS.  BIAS: each list entry's logit offset
+// (col_bias, natural-log units) is added to the scaled scores of its tile before the
+// tile's max, so the online softmax takes it in exactly.
+template <int D, bool BIAS>
 __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
     constexpr int KS = D + 1;
     constexpr int VS = D;
@@ -973,12 +975,13 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs a) {
                                                                   acc_s[kt2], 0, 0, 0);
         }
         if (km != ~0ull) mask_keys(acc_s, km, hh);
+        const float beta = BIAS ? a.col_bias[beg + e] * kLog2e : 0.f;
         float mt = -INFINITY;
 #pragma unroll
         for (int kt2 = 0; kt2 < 2; ++kt2)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                acc_s[kt2][v] *= a.scale_log2;
+                acc_s[kt2][v] = BIAS ? __builtin_fmaf(acc_s[kt2][v], a.scale_log2, beta) : acc_s[kt2][v] * a.scale_log2;
                 mt = fmaxf(mt, acc_s[kt2][v]);
             }
         mt = pair_max(mt);
@@ -1058,10 +1061,14 @@ int launch_attention(const AttnArgs &a, int dtype, int d, hipStream_t s) {
             else attn_bf16_kernel<64, false, false, false><<<pgrid, pblock, 0, s>>>(a);
             merge_kernel<64><<<mgrid, mblock, 0, s>>>(a);
         }
-    } else if (dtype == 0 && d == 128)
-        attn_f32_kernel<128><<<grid, block, 0, s>>>(a);
+    } else if (dtype == 0 && d == 128 && a.col_bias != nullptr)
+        attn_f32_kernel<128, true><<<grid, block, 0, s>>>(a);
+    else if (dtype == 0 && d == 64 && a.col_bias != nullptr)
+        attn_f32_kernel<64, true><<<grid, block, 0, s>>>(a);
+    else if (dtype == 0 && d == 128)
+        attn_f32_kernel<128, false><<<grid, block, 0, s>>>(a);
     else
-        attn_f32_kernel<64><<<grid, block, 0, s>>>(a);
+        attn_f32_kernel<64, false><<<grid, block, 0, s>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

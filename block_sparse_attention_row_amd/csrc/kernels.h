@@ -249,7 +249,7 @@ int launch_pool_keys(const void *k, __bf16 *kbar, double *kbar64, float *knorm, 
                      int d, const PoolSide &side, const SlotGeo &geo, hipStream_t s);
 int launch_fill_thresholds(const float *host_thr, int n, float *dst, hipStream_t s);
 int launch_select(const SelectArgs &a, int d, int dtype, hipStream_t s);
-int launch_select_sip(const SelectArgs &a, int d, hipStream_t s);
+int launch_select_sip(const SelectArgs &a, int d, int dtype, hipStream_t s);
 int launch_select_rows(const SelectArgs &a, int64_t groups, hipStream_t s);
 int launch_mask_bits(const uint8_t *mask, int64_t bh, int32_t nB, int32_t nW, uint64_t *bits, int32_t *counts,
                      int32_t *group_sums, hipStream_t s);

@@ -1172,13 +1172,17 @@ int launch_select_rows(const SelectArgs &a, int64_t groups, hipStream_t s) {
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_select_sip(const SelectArgs &a, int d, hipStream_t s) {
+int launch_select_sip(const SelectArgs &a, int d, int dtype, hipStream_t s) {
     if (a.nBp > kSelectMaxBlocks) return -1;
     const int nch = (a.nB + kSelChunk - 1) / kSelChunk;
-    if (d == 128)
+    if (dtype == 1 && d == 128)
         launch_select_nch<__bf16, 128, 1, 1>(a, nch, s);
-    else
+    else if (dtype == 1)
         launch_select_nch<__bf16, 64, 1, 1>(a, nch, s);
+    else if (d == 128)
+        launch_select_nch<float, 128, 1, 1>(a, nch, s);
+    else
+        launch_select_nch<float, 64, 1, 1>(a, nch, s);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -188,7 +188,7 @@ typedef struct {
  *   q, k, row_ptr, col_idx, col_capacity, workspace: as in sparse_attn_select.
  *   col_bias    device, fp32 [col_capacity]; entries [0, nnz) are written,
  *               aligned with col_idx.
- * bf16 only, nB <= 4096 (SPARSE_ATTN_UNSUPPORTED otherwise); a budget that is
+ * bf16 or fp32, nB <= 4096 (SPARSE_ATTN_UNSUPPORTED otherwise); a budget that is
  * not a finite positive number is SPARSE_ATTN_INVALID_ARGUMENT.
  */
 int32_t sparse_attn_select_sip(const sparse_attn_shape *shape, const sparse_attn_sip_params *params,
@@ -257,8 +257,8 @@ int32_t sparse_attn_forward(const sparse_attn_shape *shape, const void *q, const
  *               aligned with col_idx (skipped entries' offsets are ignored).
  *               NULL is allowed only when col_count == 0.
  *   lse         as in sparse_attn_forward, including the offsets.
- * Everything else as in sparse_attn_forward.  bf16 only
- * (SPARSE_ATTN_UNSUPPORTED otherwise).
+ * Everything else as in sparse_attn_forward (bf16 or fp32; the fp32 kernel adds the
+ * offsets to a tile's scaled scores before taking its max).
  */
 int32_t sparse_attn_forward_biased(const sparse_attn_shape *shape, const void *q, const void *k,
                                    const void *v, const int32_t *row_ptr, const int32_t *col_idx,

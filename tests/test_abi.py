@@ -244,7 +244,8 @@ def test_forward_biased_rejects_before_launch():
 
     def call(shape=None, cb=A, cc=100, ws=A, w=None):
         return f(ctypes.byref(shape or s), A, A, A, A, A, cb, cc, A, None, ws, wsb if w is None else w, None)
-    assert call(shape=_shape(dtype="f32")) == B.SPARSE_ATTN_UNSUPPORTED
+    # fp32 passes the dtype check and stops at the missing offsets, like bf16
+    assert call(shape=_shape(dtype="f32"), cb=None) == B.SPARSE_ATTN_INVALID_ARGUMENT
     assert call(cb=None) == B.SPARSE_ATTN_INVALID_ARGUMENT            # offsets needed for a non-empty list
     assert call(cb=A + 2) == B.SPARSE_ATTN_INVALID_ARGUMENT           # misaligned
     assert call(cc=-1) == B.SPARSE_ATTN_INVALID_ARGUMENT
@@ -274,8 +275,9 @@ def test_select_sip_rejects_before_launch(kw, status):
     assert _sip(_shape(), **kw) == status
 
 
-def test_select_sip_rejects_fp32_and_too_many_blocks():
-    assert _sip(_shape(dtype="f32")) == B.SPARSE_ATTN_UNSUPPORTED
+def test_select_sip_takes_fp32_and_rejects_too_many_blocks():
+    # fp32 passes the dtype check and stops at the bad budget, like bf16
+    assert _sip(_shape(dtype="f32"), budget=0.0) == B.SPARSE_ATTN_INVALID_ARGUMENT
     assert _sip(_shape(heads=1, grid=(65, 64, 64))) == B.SPARSE_ATTN_UNSUPPORTED
 
 
