@@ -559,7 +559,6 @@ int32_t sparse_attn_select_ibcs(const sparse_attn_shape *shape, const sparse_att
     Dims d;
     int32_t st = check_shape(shape, &d);
     if (st) return st;
-    if (shape->dtype != SPARSE_ATTN_BF16) return SPARSE_ATTN_UNSUPPORTED;
     if (d.partial) return SPARSE_ATTN_UNSUPPORTED;   // the 128-token clusters take whole tiles
     if (!params || !q || !k || !row_ptr || !col_idx || !workspace) return SPARSE_ATTN_INVALID_ARGUMENT;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(row_ptr, 4) || !aligned(col_idx, 4) ||
@@ -601,7 +600,7 @@ int32_t sparse_attn_select_ibcs(const sparse_attn_shape *shape, const sparse_att
         return SPARSE_ATTN_HIP_ERROR;
 
     IbcsArgs m;
-    m.q = (const __bf16 *)q;
+    m.q = q;
     m.kbar = kbar;
     m.rows = rows;
     m.nB = (int32_t)d.nB;
@@ -639,7 +638,7 @@ int32_t sparse_attn_select_ibcs(const sparse_attn_shape *shape, const sparse_att
         const int64_t nh = BH - h0 < hpl ? BH - h0 : hpl;
         m.head0 = h0;
         a.head0 = h0;
-        if (launch_ibcs_mix(m, nh, (int)d.D, s)) return SPARSE_ATTN_HIP_ERROR;
+        if (launch_ibcs_mix(m, nh, (int)d.D, shape->dtype, s)) return SPARSE_ATTN_HIP_ERROR;
         if (launch_select_rows(a, nh * groups_per_head(d), s)) return SPARSE_ATTN_HIP_ERROR;
     }
     return SPARSE_ATTN_OK;

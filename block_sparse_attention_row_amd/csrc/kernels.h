@@ -138,14 +138,14 @@ int launch_fine_select(const FineArgs &a, int d, hipStream_t s);
 
 constexpr int kIbcsClusters = 8, kIbcsIters = 4;
 struct IbcsArgs {
-    const __bf16 *q;          // [BH*N][D] queries (bf16, tile-major)
+    const void *q;            // [BH*N][D] queries (bf16 or fp32, tile-major)
     const __bf16 *kbar;       // key block means (hi | lo), in fragment order (kbar_group)
     float *rows;              // [heads][pairs][nBp]: log2 of the mixture row of each pair
     int64_t head0;            // first (batch, head) of this launch
     int32_t nB, nBp, pairs_per_head;
     float scale_log2;
 };
-int launch_ibcs_mix(const IbcsArgs &a, int64_t heads, int d, hipStream_t s);
+int launch_ibcs_mix(const IbcsArgs &a, int64_t heads, int d, int dtype, hipStream_t s);
 
 // Row splitting of the bf16 attention.  Pairs of query blocks whose rows hold more
 // than L tiles are cut into pieces of at most about L tiles (by position in each

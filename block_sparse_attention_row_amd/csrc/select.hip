@@ -921,19 +921,24 @@ int launch_select(const SelectArgs &a, int d, int dtype, hipStream_t s) {
 //    weighted by w_c.  The pair's row is the sum of its 8 weighted rows, added in
 //    cluster order through LDS 256 keys at a time, and stored in log2 units for the
 //    cut.
-template <int D, int NE>
+// QT = float (fp32 queries): they are staged in fp32, the k-means runs on their exact
+// values, and the cluster sums take each value as three bf16 parts (hi, mid, lo),
+// which hold an fp32 value exactly (away from the bottom of the exponent range), in
+// three one-hot products.
+template <typename QT, int D, int NE>
 __global__ __launch_bounds__(1024) void ibcs_mix_kernel(IbcsArgs a) {
     constexpr int K = kIbcsClusters, DP = D / 4, KB = D / 32, NCH = NE / 4;
     constexpr int QW = 3 * D + 8;                                   // bf16 per centroid row: hi | mid | lo, pad
-    constexpr int QBYTES = 2 * 128 * D * 2;                         // the two pairs' queries
+    constexpr int QBYTES = 2 * 128 * D * (int)sizeof(QT);            // the two pairs' queries
     constexpr int SBYTES = 16 * QW * 2 + 2 * kSelRows * kStageStride * 4;
     constexpr int BIG = QBYTES > SBYTES ? QBYTES : SBYTES;
-    static_assert(K == 8 && D % 32 == 0 && (2 * 128 * D / 8) % 1024 == 0, "layout");
+    constexpr int V16 = 16 / (int)sizeof(QT);                        // elements per 16-byte load
+    static_assert(K == 8 && D % 32 == 0 && (2 * 128 * D / V16) % 1024 == 0, "layout");
     __shared__ __attribute__((aligned(16))) unsigned char big[BIG];
     __shared__ float mu[2][K][D];
     __shared__ int32_t asg[2][128];
     __shared__ int32_t cnt[2][K];
-    __bf16 *qs = reinterpret_cast<__bf16 *>(big);                   // [2][128][D], during the k-means
+    QT *qs = reinterpret_cast<QT *>(big);                             // [2][128][D], during the k-means
     __bf16 *qf = reinterpret_cast<__bf16 *>(big);                   // [16][QW], afterwards
     float *stage = reinterpret_cast<float *>(big + 16 * QW * 2);    // [2][16][kStageStride]
 
@@ -947,18 +952,24 @@ __global__ __launch_bounds__(1024) void ibcs_mix_kernel(IbcsArgs a) {
     const int64_t N = (int64_t)a.nB * 64;
     auto pair_n = [&](int pp) { return 2 * (p0 + pp) + 1 < a.nB ? 128 : 64; };
     {
-        // the pairs' queries, all of this thread's loads in flight before the stores
-        constexpr int PER = 2 * 128 * D / 8 / 1024, PP = 128 * D / 8;
-        uint4 tmp[PER];
+        // the pairs' queries, a batch of this thread's loads in flight before its stores
+        // (fp32: two batches, so that the staging registers stay those of bf16)
+        constexpr int PER = 2 * 128 * D / V16 / 1024, PP = 128 * D / V16;
+        constexpr int BAT = PER < 4 ? PER : 4;
+        const QT *qg = reinterpret_cast<const QT *>(a.q);
 #pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int e = t + 1024 * u, pp = e / PP, r = e % PP;
-            const bool ok = pp < np && r < pair_n(pp) * D / 8;
-            tmp[u] = ok ? reinterpret_cast<const uint4 *>(a.q + (bh * N + (int64_t)128 * (p0 + pp)) * D)[r]
-                        : uint4{0u, 0u, 0u, 0u};
+        for (int u0 = 0; u0 < PER; u0 += BAT) {
+            uint4 tmp[BAT];
+#pragma unroll
+            for (int u = 0; u < BAT; ++u) {
+                const int e = t + 1024 * (u0 + u), pp = e / PP, r = e % PP;
+                const bool ok = pp < np && r < pair_n(pp) * D / V16;
+                tmp[u] = ok ? reinterpret_cast<const uint4 *>(qg + (bh * N + (int64_t)128 * (p0 + pp)) * D)[r]
+                            : uint4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < BAT; ++u) reinterpret_cast<uint4 *>(qs)[t + 1024 * (u0 + u)] = tmp[u];
         }
-#pragma unroll
-        for (int u = 0; u < PER; ++u) reinterpret_cast<uint4 *>(qs)[t + 1024 * u] = tmp[u];
     }
     __syncthreads();
 
@@ -966,7 +977,7 @@ __global__ __launch_bounds__(1024) void ibcs_mix_kernel(IbcsArgs a) {
     const int tp = t & 511, q = tp >> 2, part = tp & 3;
     const int n = pair_n(P);
     float x[DP];
-    {
+    if constexpr (sizeof(QT) == 2) {
         const uint4 *src = reinterpret_cast<const uint4 *>(qs + (P * 128 + q) * D + part * DP);
 #pragma unroll
         for (int u = 0; u < DP / 8; ++u) {
@@ -977,6 +988,14 @@ __global__ __launch_bounds__(1024) void ibcs_mix_kernel(IbcsArgs a) {
                 x[8 * u + 2 * k] = bf16_lo(ws[k]);
                 x[8 * u + 2 * k + 1] = bf16_hi(ws[k]);
             }
+        }
+    } else {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(qs + (P * 128 + q) * D + part * DP);
+#pragma unroll
+        for (int u = 0; u < DP / 4; ++u) {
+            const f32x4 w = src[u];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) x[4 * u + k] = w[k];
         }
     }
     for (int e = tp; e < K * D; e += 512) {
@@ -1028,13 +1047,28 @@ __global__ __launch_bounds__(1024) void ibcs_mix_kernel(IbcsArgs a) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int qb = 32 * ks + 8 * kq;
-                bf16x8 oh, xb;
+                bf16x8 oh;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    oh[i] = asg[P][qb + i] == cl ? (__bf16)1.f : (__bf16)0.f;
-                    xb[i] = qs[(P * 128 + qb + i) * D + dim];
+                for (int i = 0; i < 8; ++i) oh[i] = asg[P][qb + i] == cl ? (__bf16)1.f : (__bf16)0.f;
+                if constexpr (sizeof(QT) == 2) {
+                    bf16x8 xb;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) xb[i] = qs[(P * 128 + qb + i) * D + dim];
+                    sum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oh, xb, sum, 0, 0, 0);
+                } else {
+                    bf16x8 xh, xm, xl;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float v = qs[(P * 128 + qb + i) * D + dim];
+                        xh[i] = (__bf16)v;
+                        const float r1 = v - (float)xh[i];
+                        xm[i] = (__bf16)r1;
+                        xl[i] = (__bf16)(r1 - (float)xm[i]);
+                    }
+                    sum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oh, xh, sum, 0, 0, 0);
+                    sum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oh, xm, sum, 0, 0, 0);
+                    sum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oh, xl, sum, 0, 0, 0);
                 }
-                sum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oh, xb, sum, 0, 0, 0);
             }
         }
         __syncthreads();            // counts written; every read of the old centroids done
@@ -1134,24 +1168,29 @@ __global__ __launch_bounds__(1024) void ibcs_mix_kernel(IbcsArgs a) {
     }
 }
 
-template <int D, int NCH> static void launch_ibcs_nch(const IbcsArgs &a, dim3 g, int nch, hipStream_t s) {
+template <typename T, int D, int NCH>
+static void launch_ibcs_nch(const IbcsArgs &a, dim3 g, int nch, hipStream_t s) {
     if constexpr (NCH <= kSelectMaxBlocks / kSelChunk) {
         if (nch == NCH) {
-            ibcs_mix_kernel<D, 4 * NCH><<<g, dim3(1024), 0, s>>>(a);
+            ibcs_mix_kernel<T, D, 4 * NCH><<<g, dim3(1024), 0, s>>>(a);
             return;
         }
-        launch_ibcs_nch<D, NCH + 1>(a, g, nch, s);
+        launch_ibcs_nch<T, D, NCH + 1>(a, g, nch, s);
     }
 }
 
-int launch_ibcs_mix(const IbcsArgs &a, int64_t heads, int d, hipStream_t s) {
+int launch_ibcs_mix(const IbcsArgs &a, int64_t heads, int d, int dtype, hipStream_t s) {
     if (a.nBp > kSelectMaxBlocks) return -1;
     const dim3 g((unsigned)(heads * ((a.pairs_per_head + 1) / 2)));
     const int nch = (a.nB + kSelChunk - 1) / kSelChunk;
-    if (d == 128)
-        launch_ibcs_nch<128, 1>(a, g, nch, s);
+    if (dtype == 1 && d == 128)
+        launch_ibcs_nch<__bf16, 128, 1>(a, g, nch, s);
+    else if (dtype == 1)
+        launch_ibcs_nch<__bf16, 64, 1>(a, g, nch, s);
+    else if (d == 128)
+        launch_ibcs_nch<float, 128, 1>(a, g, nch, s);
     else
-        launch_ibcs_nch<64, 1>(a, g, nch, s);
+        launch_ibcs_nch<float, 64, 1>(a, g, nch, s);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

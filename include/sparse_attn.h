@@ -208,7 +208,7 @@ int32_t sparse_attn_select_sip(const sparse_attn_shape *shape, const sparse_attn
  * blocks of the pair keep the blocks NABLA's CDF rule keeps on p~ (threshold,
  * per-head thresholds and window as in sparse_attn_select).
  *
- *   Arguments as in sparse_attn_select.  bf16 only, nB <= 4096, whole tiles
+ *   Arguments as in sparse_attn_select.  bf16 or fp32, nB <= 4096, whole tiles
  *   (SPARSE_ATTN_UNSUPPORTED otherwise).
  */
 int32_t sparse_attn_select_ibcs(const sparse_attn_shape *shape, const sparse_attn_select_params *params,

@@ -306,9 +306,10 @@ def test_select_ibcs_rejects_before_launch():
     cap = B.sparse_attn_csr_capacity(s)
     wsb = B.sparse_attn_workspace_size(s)
     ok = B.SelectParams(0.9, None, -1, -1, -1)
-    assert f(ctypes.byref(_shape(dtype="f32")), ctypes.byref(ok), A, A, A, A, cap, A, wsb, None) == \
-        B.SPARSE_ATTN_UNSUPPORTED
     bad = B.SelectParams(0.0, None, -1, -1, -1)
+    # fp32 passes the dtype check and stops at the bad threshold, like bf16
+    assert f(ctypes.byref(_shape(dtype="f32")), ctypes.byref(bad), A, A, A, A, cap, A, wsb, None) == \
+        B.SPARSE_ATTN_INVALID_ARGUMENT
     assert f(ctypes.byref(s), ctypes.byref(bad), A, A, A, A, cap, A, wsb, None) == B.SPARSE_ATTN_INVALID_ARGUMENT
     assert f(ctypes.byref(s), ctypes.byref(ok), A, A, A, A, cap - 1, A, wsb, None) == B.SPARSE_ATTN_CAPACITY
     assert f(ctypes.byref(s), ctypes.byref(ok), A, A, A, A, cap, A, wsb - 1, None) == B.SPARSE_ATTN_WORKSPACE

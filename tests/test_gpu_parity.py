@@ -421,13 +421,15 @@ def test_sip_budget_of_all_blocks_keeps_everything():
     assert torch.all(cb[:rows * nB] == 0)
 
 
-@pytest.mark.parametrize("d,grid,thr,reading", [(128, (3, 4, 5), 0.8, "A"), (64, (2, 3, 5), 0.9, "B"),
-                                               (128, (2, 8, 18), 0.7, "A")])
-def test_ibcs_selection_matches_oracle(d, grid, thr, reading):
+@pytest.mark.parametrize("d,grid,thr,reading,dt", [(128, (3, 4, 5), 0.8, "A", "bf16"), (64, (2, 3, 5), 0.9, "B", "bf16"),
+                                                  (128, (2, 8, 18), 0.7, "A", "bf16"), (64, (3, 4, 5), 0.8, "A", "f32"),
+                                                  (128, (2, 8, 18), 0.7, "B", "f32")])
+def test_ibcs_selection_matches_oracle(d, grid, thr, reading, dt):
     """The clustering selector against the oracle: block lists equal except at the CDF
-    boundary, and pairs with near-tied k-means assignments checked for validity."""
+    boundary, and pairs with near-tied k-means assignments checked for validity; bf16
+    and fp32 queries."""
     from oracle import ibcs
-    wl = small_workload("ibcs", 2, d, grid, "bf16", threshold=thr, seed=61)
+    wl = small_workload("ibcs", 2, d, grid, dt, threshold=thr, seed=61)
     q, k, _, _ = make_inputs(wl, reading)
     qd, kd = P.to_device(q, k)
     rp, ci = B.sparse_attn_select_ibcs(P.shape_for(wl), qd, kd, threshold=thr)
