@@ -421,7 +421,8 @@ def backward_sampled(wl, shape, qd, kd, vd, lse, q32, k32, v32, orp, oci, sample
     lens = np.diff(orp)
     rp_s = np.concatenate([[0], np.cumsum(np.where(keep, lens, 0))])
     ci_s = np.concatenate([oci[orp[r]:orp[r + 1]] for r in rows_s])
-    rq, rk, rv = oracle.attention_backward(q32, k32, v32, dout.float().numpy(), rp_s, ci_s, out=o_in.float().numpy())
+    rq, rk, rv = oracle.attention_backward(q32, k32, v32, dout.float().numpy(), rp_s, ci_s, out=o_in.float().numpy(),
+                                           valid=valid_of(wl))
     errs = []
     for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         g = got.float().cpu().numpy()

@@ -88,6 +88,44 @@ def test_full_size_workload(name):
         P.backward_sampled(wl, shape, qd, kd, vd, lse_o, q32, k32, v32, orp, oci, sample, log=_log)
 
 
+@pytest.mark.timeout(600)
+def test_full_size_partial_tiles():
+    """A grid of the 480p workload's size that is not a whole number of tiles
+    (20 x 30 x 45 tokens in 1 x 8 x 8 tiles: 480 blocks, the last row and column of
+    tiles partial), junk in every padding slot: every mask row against the oracle,
+    sampled query blocks of the forward under the oracle's list (padding slots O = 0),
+    and the sampled backward (padding slots zero gradients)."""
+    from block_sparse_attention_row_amd.synth import Workload
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    wl = Workload("partial_480p", 1, 12, 128, (20, 30, 45), "bf16", 2.0, 0.9, seed=23)
+    assert wl.partial and wl.blocks == 480
+    _log(f"[case] {wl.name}: drawing inputs (grid {wl.grid}, {wl.blocks} blocks)")
+    q, k, v, thr = make_inputs(wl, "A")
+    valid = torch.as_tensor(P.valid_of(wl))
+    for t in (q, k, v):
+        t[..., ~valid, :] = 7.0
+    qd, kd, vd = P.to_device(q, k, v)
+    shape = P.shape_for(wl)
+    rp_h, ci_h = P.gpu_select(wl, qd, kd, thr)
+    gmask = P.check_csr(rp_h, ci_h, wl.blocks)
+    rows = wl.batch * wl.heads * wl.blocks
+    _log(f"GPU selection done: nnz={int(rp_h[-1])} kept={rp_h[-1] / (rows * wl.blocks):.4f}")
+    q32, k32, v32 = (t.float().numpy() for t in (q, k, v))
+    qbar, kbar, keep, band = P.oracle_select_full(wl, q32, k32, thr, count_band=True)
+    rep = P.compare_masks(gmask, keep, qbar, kbar, wl, thr, band=band)
+    P.record_masks(wl.name, rep, nnz=int(rp_h[-1]), oracle_nnz=int((keep != 0).sum()))
+    assert P.mask_ok(rep), P.fmt(rep)
+    orp, oci = oracle.csr_from_mask(keep != 0)
+    sample = np.unique(np.concatenate([P.sample_rows(wl, thr), P.last_round_rows(wl)]))
+    out_o, lse_o = P.gpu_forward(wl, qd, kd, vd, orp, oci)
+    err, lerr = P.compare_rows(wl, out_o, lse_o, q32, k32, v32, orp, oci, sample)
+    _log(f"forward (oracle CSR), {len(sample)} sampled blocks: max|err|={err:.3e} lse max|err|={lerr:.3e}")
+    assert err <= P.TOL[wl.dtype] and lerr <= P.LSE_TOL[wl.dtype]
+    assert torch.all(out_o.cpu()[..., ~valid, :] == 0)
+    P.backward_sampled(wl, shape, qd, kd, vd, lse_o, q32, k32, v32, orp, oci, sample, log=_log)
+
+
 OTHER_READINGS = [(n, r) for n in ("wan13b_480p", "long_video") for r in ("B", "page")]
 
 
