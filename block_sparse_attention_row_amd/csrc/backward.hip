@@ -154,7 +154,11 @@ enum BwdMode { kDQ = 0, kDKV = 1 };
 
 // kDKV: dV and dK in one walk of the transposed list (S and dP once per tile, four
 // products; 8% faster at d = 128 than a dV pass and a dK pass that each form S);
-// at d = 128 its two d-wide accumulators take one wave per SIMD.
+// at d = 128 its two d-wide accumulators take one wave per SIMD, so there its tile
+// runs in phases with the softmax work beside the MFMAs and the fragment reads
+// kDkvAhead MFMAs ahead of use (dkv_tile below); at d = 64 (two waves per SIMD) the
+// other wave covers that work.
+constexpr int kDkvAhead = 6;
 template <int D, int MODE, bool MASKED>
 __global__ __launch_bounds__(256, MODE == kDKV && D == 128 ? 1 : 2) void bwd_kernel(BwdArgs a) {
     using G = TileGeo<D>;
@@ -321,6 +325,117 @@ __global__ __launch_bounds__(256, MODE == kDKV && D == 128 ? 1 : 2) void bwd_ker
     next_union(col0, mine0);
     if (col0 != kNone) issue(col0, 0);
 
+    // One tile of the fused dV/dK pass, as three MFMA phases with the softmax work
+    // spread over them (the wave has its SIMD to itself, so VALU work beside no MFMA
+    // leaves the matrix unit idle): S; then dP beside P (S complete), two of P's
+    // elements after each MFMA; then dV^T += dO^T P beside dS (dP complete); then
+    // dK^T += Q^T dS.  Fragment reads run kDkvAhead MFMAs ahead and consecutive MFMAs
+    // use different accumulators.  Formulas and summation orders are those of the
+    // unphased form, so the gradients are the same bit for bit.
+    auto dkv_tile = [&](const char *T1, const char *T2, const float *ax, f32x16 *s, f32x16 *dp, bf16x8 *pf,
+                        bf16x8 *pf2) {
+        constexpr int NC = D / 16, NM = 2 * NC, PER = 32 / NM, AH = kDkvAhead, RR = 2 * AH;
+        constexpr int NDT2 = TileGeo<D>::NDT, NV = 4 * NDT2, PERV = 32 / NV;
+        // lse2 and D of the 64 streamed rows this lane's elements belong to
+        float l2v[32], ddv[32];
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            const f32x4 lo_l = *reinterpret_cast<const f32x4 *>(ax + 16 * kc + 4 * hh);
+            const f32x4 hi_l = *reinterpret_cast<const f32x4 *>(ax + 16 * kc + 8 + 4 * hh);
+            const f32x4 lo_d = *reinterpret_cast<const f32x4 *>(ax + 64 + 16 * kc + 4 * hh);
+            const f32x4 hi_d = *reinterpret_cast<const f32x4 *>(ax + 64 + 16 * kc + 8 + 4 * hh);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                l2v[8 * kc + e] = lo_l[e];
+                l2v[8 * kc + 4 + e] = hi_l[e];
+                ddv[8 * kc + e] = lo_d[e];
+                ddv[8 * kc + 4 + e] = hi_d[e];
+            }
+        }
+        // S (alternating key halves)
+        {
+            auto frag = [&](int i) { return fo.kfrag(T1, i & 1, i >> 1); };
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                s[0][v] = 0.f;
+                s[1][v] = 0.f;
+            }
+            bf16x8 kf[RR];
+#pragma unroll
+            for (int j = 0; j < AH; ++j) kf[j] = frag(j);
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+                if (i + AH < NM) kf[(i + AH) % RR] = frag(i + AH);
+                s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % RR], f1[i >> 1], s[i & 1], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // dP beside P (fp32 P kept in s for dS)
+        {
+            auto frag = [&](int i) { return fo.kfrag(T2, i & 1, i >> 1); };
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                dp[0][v] = 0.f;
+                dp[1][v] = 0.f;
+            }
+            bf16x8 kf[RR];
+#pragma unroll
+            for (int j = 0; j < AH; ++j) kf[j] = frag(j);
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+                if (i + AH < NM) kf[(i + AH) % RR] = frag(i + AH);
+                dp[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % RR], f2[i >> 1], dp[i & 1], 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < PER; ++u) {
+                    const int e = PER * i + u, kc = e >> 3;
+                    const int q = 8 * (kc & 1) + (e & 7);
+                    s[kc >> 1][q] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kc >> 1][q], c, -l2v[e]));
+                    if ((e & 7) == 7) {
+                        f32x8 pv;
+#pragma unroll
+                        for (int w = 0; w < 8; ++w) pv[w] = s[kc >> 1][8 * (kc & 1) + w];
+                        pf[kc] = __builtin_convertvector(pv, bf16x8);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // dV^T += dO^T P beside dS, then dK^T += Q^T dS
+        {
+            auto frag = [&](const char *T, int i) { return fo.vfrag(T, i / NDT2, i % NDT2); };
+            bf16x8 vf[RR];
+#pragma unroll
+            for (int j = 0; j < AH; ++j) vf[j] = frag(T2, j);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                if (i + AH < NV) vf[(i + AH) % RR] = frag(T2, i + AH);
+                acc[i % NDT2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % RR], pf[i / NDT2], acc[i % NDT2], 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < PERV; ++u) {
+                    const int e = PERV * i + u, kc = e >> 3;
+                    const int q = 8 * (kc & 1) + (e & 7);
+                    s[kc >> 1][q] = s[kc >> 1][q] * (dp[kc >> 1][q] - ddv[e]);
+                    if ((e & 7) == 7) {
+                        f32x8 pv;
+#pragma unroll
+                        for (int w = 0; w < 8; ++w) pv[w] = s[kc >> 1][8 * (kc & 1) + w];
+                        pf2[kc] = __builtin_convertvector(pv, bf16x8);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int j = 0; j < AH; ++j) vf[j] = frag(T1, j);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                if (i + AH < NV) vf[(i + AH) % RR] = frag(T1, i + AH);
+                acc2[i % NDT2] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % RR], pf2[i / NDT2], acc2[i % NDT2], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+
     auto step = [&](auto bj_tag) {
         constexpr int BJ = decltype(bj_tag)::value;
         wait_vmcnt<0>();            // this wave's part of tile j has landed
@@ -331,6 +446,11 @@ __global__ __launch_bounds__(256, MODE == kDKV && D == 128 ? 1 : 2) void bwd_ker
         const char *T1 = T1s + BJ * TILEB, *T2 = T2s + BJ * TILEB;
         const float *ax = aux[BJ];
         f32x16 s[2], dp[2];
+        bf16x8 pf[4], pf2[4];           // pf2: dS of the fused pass (pf holds P there)
+        if constexpr (MODE == kDKV && D == 128) {
+            dkv_tile(T1, T2, ax, s, dp, pf, pf2);
+            return;
+        }
         tile_scores<D>(T1, f1, fo, s);
         if constexpr (MASKED && MODE == kDQ) {
             // padding keys of a partial key tile: no weight (dP needs no mask, P = 0 there)
@@ -338,7 +458,6 @@ __global__ __launch_bounds__(256, MODE == kDKV && D == 128 ? 1 : 2) void bwd_ker
             if (km != ~0ull) mask_keys(s, km, hh);
         }
         tile_scores<D>(T2, f2, fo, dp);
-        bf16x8 pf[4], pf2[4];           // pf2: dS of the fused pass (pf holds P there)
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
             f32x4 lo_l, hi_l, lo_d, hi_d;   // lse2, D of the 8 streamed rows of this chunk (dV, dK)
