@@ -430,3 +430,56 @@ def backward_sampled(wl, shape, qd, kd, vd, lse, q32, k32, v32, orp, oci, sample
         errs.append(float(np.abs(g - ref).max() / np.abs(ref).max()))
     log(f"backward, {len(rows_s)} sampled rows: rel err dq {errs[0]:.3e} dk {errs[1]:.3e} dv {errs[2]:.3e}")
     assert max(errs[:2]) <= BWD_TOL_DQK and errs[2] <= BWD_TOL_DV
+
+
+# ------------------------------------------------------------- mask record summary
+_SUMMARY_HEAD = """# Mask parity records (GPU selection against the fp64 oracle)
+
+Every row of every listed case: the GPU's block list against the oracle's.  `diff` = blocks on which the two
+differ; `R1` = differences excused because the oracle's exclusive mass E(j) lies within 1e-4 of the threshold;
+`R2` = differences only a near-tie rule would excuse (|p_j - p_c| <= 1e-5 p_c) -- counted, never accepted;
+`unexcused` must be 0; `window missing` = window blocks the GPU left out (must be 0); `invariant` = rows
+whose GPU set fails kept mass >= thr - 1e-4 or minimality (must be 0); `band` = blocks within R1's band over
+all rows (where R1 could excuse a difference), counted on the full-size cases; `nnz` = kept tiles, GPU / oracle.
+
+Made from the JSON records of a GPU suite run (from the repository root on an MI355X, after building in-tree):
+
+```
+SPARSE_ATTN_PARITY_DIR=<out> python -u -m pytest tests/ -x -v -m gpu --timeout 900 --timeout-method thread
+python -m tests.parity --summary <out> > profiles/parity_masks.md
+```
+
+Full-size cases are the five workloads (and the B and page-like readings of two of them, and `partial_480p`: a
+20 x 30 x 45 token grid, 480 blocks whose last tile row and column are partial); `fine_*` is the
+selection of 4-token key blocks (16 nB key blocks a row).
+"""
+
+
+def summarize(directory: str) -> str:
+    """The markdown table of every masks_*.json record in `directory`."""
+    import glob
+    recs = []
+    for path in sorted(glob.glob(os.path.join(directory, "masks_*.json"))):
+        with open(path) as f:
+            recs.append(json.load(f))
+    lines = [_SUMMARY_HEAD, "| case | rows | diff rows | diff | R1 | R2 | unexcused | window missing | invariant | band | nnz |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in sorted(recs, key=lambda r: r["label"]):
+        band = r.get("band", -1)
+        nnz = f"{r['nnz']} / {r['oracle_nnz']}" if "nnz" in r and "oracle_nnz" in r else "-"
+        lines.append(f"| {r['label']} | {r['rows']} | {r['diff_rows']} | {r['diff_blocks']} | {r['r1']} | {r['r2']} | "
+                     f"{r['unexcused']} | {r['window_missing']} | {r['invariant_fail']} | "
+                     f"{band if band >= 0 else '-'} | {nnz} |")
+    tot = {k: sum(r[k] for r in recs) for k in ("diff_blocks", "r1", "r2", "unexcused", "window_missing", "invariant_fail")}
+    lines.append("")
+    lines.append(f"{len(recs)} cases; over all of them: {tot['diff_blocks']} differing blocks, {tot['r1']} excused by R1, "
+                 f"{tot['r2']} R2-only, {tot['unexcused']} unexcused, {tot['window_missing']} window blocks missing, "
+                 f"{tot['invariant_fail']} invariant failures.")
+    return "\n".join(lines) + "\n"
+
+
+if __name__ == "__main__":
+    import argparse
+    ap = argparse.ArgumentParser(description="summaries of the GPU parity records")
+    ap.add_argument("--summary", required=True, help="directory of masks_*.json records")
+    print(summarize(ap.parse_args().summary), end="")
