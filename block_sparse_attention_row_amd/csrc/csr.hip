@@ -133,22 +133,22 @@ __global__ __launch_bounds__(256) void emit_kernel(const uint64_t *__restrict__ 
         row_ptr[row] = pos;
         if (row == rows - 1) row_ptr[rows] = pos + counts[row];
     }
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    // per word, the lanes whose bit is set (the word as the execution mask) store their
+    // column at the running offset plus the set bits below them
     const uint64_t *b = bits + row * nW;
+    int32_t *const dst = col_idx + __builtin_amdgcn_readfirstlane(pos);
+    uint32_t off = 0;
     for (int w0 = 0; w0 < nW; w0 += 64) {
         const uint64_t mine_w = (w0 + lane < nW) ? b[w0 + lane] : 0ull;
-        const int cnt = __popcll(mine_w);
-        const int incl = wave_incl_scan_i(cnt, lane);
-        const int excl = incl - cnt;
         const int nw = min(64, nW - w0);
         for (int e = 0; e < nw; ++e) {
             const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine_w, e);
             const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine_w >> 32), e);
             const uint64_t m = ((uint64_t)hi << 32) | lo;
-            const int off = __builtin_amdgcn_readlane(excl, e);
-            if ((m >> lane) & 1ull) col_idx[pos + off + __popcll(m & lt_mask)] = (w0 + e) * 64 + lane;
+            if (__builtin_amdgcn_inverse_ballot_w64(m))
+                dst[__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, off))] = (w0 + e) * 64 + lane;
+            off += (uint32_t)__popcll(m);
         }
-        pos += __builtin_amdgcn_readlane(incl, 63);
     }
 }
 

@@ -305,9 +305,11 @@ __device__ __forceinline__ uint32_t compact_bracket(const float (&v)[N], uint32_
 #pragma unroll
     for (int c = 0; c < N; ++c) {
         const uint32_t u = __float_as_uint(v[c]);
-        const bool in = u > lo && u <= hi;
-        const uint64_t m = __ballot(in);
-        if (in) dst[base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = u;
+        // the mask straight from the two compares (no per-lane bool in between), and the
+        // stores under it
+        const uint64_t m = __ballot(u > lo) & __ballot(u <= hi);
+        if (__builtin_amdgcn_inverse_ballot_w64(m))
+            dst[__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, base))] = u;
         base += (uint32_t)__popcll(m);
     }
     return base;
@@ -451,7 +453,7 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
                 ties_before += (uint32_t)__popcll(tb);
             }
             if (refine) {
-                const uint64_t bm = __ballot(u >= blo_u && u <= bhi_u);
+                const uint64_t bm = __ballot(u >= blo_u) & __ballot(u <= bhi_u);
                 nb += (uint32_t)__popcll(bm);
                 mb += (uint32_t)__popcll(bm & m);
             }
@@ -465,10 +467,9 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
 #pragma unroll
         for (int c = 0; c < NE; ++c) {
             const uint32_t u = __float_as_uint(s[c]);
-            const bool in = u >= blo_u && u <= bhi_u;
-            const uint64_t bm = __ballot(in);
-            if (in)
-                list[base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u))] =
+            const uint64_t bm = __ballot(u >= blo_u) & __ballot(u <= bhi_u);
+            if (__builtin_amdgcn_inverse_ballot_w64(bm))
+                list[__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, base))] =
                     (uint32_t)(64 * c + lane);
             base += (uint32_t)__popcll(bm);
         }
@@ -810,33 +811,38 @@ __device__ __forceinline__ void select_emit_body(const SelectArgs &a) {
         a.row_ptr[row] = pos;
         if (row == a.rows - 1) a.row_ptr[a.rows] = pos + count;
     }
-    // ---- kept columns, ascending: word e of the row sits in lane e
+    // ---- kept columns, ascending: word e of the row sits in lane e.  Per word the
+    //      lanes whose bit is set (the word itself as the execution mask) store their
+    //      column at the word's offset plus the set bits below them; the offset runs
+    //      on in a scalar register.
     const int nvc = a.nBp >> 6;
-    const int cnt = __popcll(word);
-    const int excl = wave_incl_scan_i(cnt, lane) - cnt;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int32_t pos_s = __builtin_amdgcn_readfirstlane(pos);
+    int32_t *const dst = a.col_idx + pos_s;
+    uint32_t off = 0;
     if constexpr (MODE != 1) {
         for (int e = 0; e < nvc; ++e) {
             const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)word, e);
             const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(word >> 32), e);
             const uint64_t m = ((uint64_t)hi << 32) | lo;
-            const int off = __builtin_amdgcn_readlane(excl, e);
-            if ((m >> lane) & 1ull) a.col_idx[pos + off + __popcll(m & lt_mask)] = 64 * e + lane;
+            if (__builtin_amdgcn_inverse_ballot_w64(m))
+                dst[__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, off))] = 64 * e + lane;
+            off += (uint32_t)__popcll(m);
         }
     } else {
         // the register row is indexed by the word, so the loop runs at compile time
+        float *const bdst = a.col_bias + pos_s;
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
             if (e >= nvc) break;
             const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)word, e);
             const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(word >> 32), e);
             const uint64_t m = ((uint64_t)hi << 32) | lo;
-            const int off = __builtin_amdgcn_readlane(excl, e);
-            if ((m >> lane) & 1ull) {
-                const int at = pos + off + __popcll(m & lt_mask);
-                a.col_idx[at] = 64 * e + lane;
-                a.col_bias[at] = s[e] >= sigma ? 0.f : (tcap - s[e]) * kLn2;   // -ln(pi)
+            if (__builtin_amdgcn_inverse_ballot_w64(m)) {
+                const uint32_t at = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, off));
+                dst[at] = 64 * e + lane;
+                bdst[at] = s[e] >= sigma ? 0.f : (tcap - s[e]) * kLn2;   // -ln(pi)
             }
+            off += (uint32_t)__popcll(m);
         }
     }
 }
