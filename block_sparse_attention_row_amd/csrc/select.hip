@@ -509,8 +509,9 @@ __device__ __forceinline__ void select_cut(const SelectArgs &a, float (&s)[NE], 
 // Uniform in [0, 1) for block j of row r: the top 24 bits of output r * nB + j + 1
 // of the SplitMix64 stream seeded with `seed` (state advanced by the golden gamma,
 // output through the variant-13 murmur3 finaliser), times 2^-24.
-__device__ __forceinline__ float splitmix_uniform(uint64_t seed, uint64_t counter) {
-    uint64_t z = seed + counter * 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kSplitmixGamma = 0x9E3779B97F4A7C15ull;
+// the output function applied to the state z = seed + counter * gamma
+__device__ __forceinline__ float splitmix_out(uint64_t z) {
     z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
     z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
     z ^= z >> 31;
@@ -531,7 +532,8 @@ __device__ __forceinline__ float splitmix_uniform(uint64_t seed, uint64_t counte
 // bitmask word (as select_cut), the count, sigma and t (sigma = -inf: keep all).
 template <int NE>
 __device__ __forceinline__ void sip_cut(const SelectArgs &a, const float (&s)[NE], int64_t row, int lane,
-                                        uint64_t &word, int32_t &count_out, float &sigma_out, float &t_out) {
+                                        uint64_t *wbits, uint64_t &word, int32_t &count_out, float &sigma_out,
+                                        float &t_out) {
     float sigma = INFINITY, t = INFINITY;
     if (a.budget < (float)a.nB) {
         uint32_t ncap = 0;
@@ -555,20 +557,23 @@ __device__ __forceinline__ void sip_cut(const SelectArgs &a, const float (&s)[NE
     } else {
         sigma = -INFINITY;
     }
-    uint32_t count = 0, wlo = 0, whi = 0;
+    // the generator's state for key j = 64c + lane, seed + (row nB + j + 1) gamma, steps
+    // by 64 gamma from one word to the next (the same value mod 2^64).  Each word goes
+    // to LDS from one lane as it is formed (no mask stays live in scalar registers),
+    // and lane c reads word c back.
+    uint64_t z = a.seed + ((uint64_t)row * (uint64_t)a.nB + (uint64_t)lane + 1ull) * kSplitmixGamma;
+    uint32_t count = 0;
 #pragma unroll
     for (int c = 0; c < NE; ++c) {
         const int j = 64 * c + lane;
         const float pi = s[c] >= sigma ? 1.f : __builtin_amdgcn_exp2f(s[c] - t);
-        const bool keep = j < a.nB && splitmix_uniform(a.seed, (uint64_t)row * a.nB + j + 1) < pi;
-        const uint64_t m = __ballot(keep);
+        const uint64_t m = __ballot(j < a.nB) & __ballot(splitmix_out(z) < pi);
+        z += 64ull * kSplitmixGamma;
         count += (uint32_t)__popcll(m);
-        if (lane == c) {
-            wlo = (uint32_t)m;
-            whi = (uint32_t)(m >> 32);
-        }
+        if (lane == 0) wbits[c] = m;
     }
-    word = ((uint64_t)whi << 32) | wlo;
+    wave_lds_sync();
+    word = lane < NE ? wbits[lane] : 0ull;
     count_out = (int32_t)count;
     sigma_out = sigma;
     t_out = t;
@@ -776,7 +781,8 @@ __device__ __forceinline__ void select_emit_body(const SelectArgs &a) {
             select_cut<NE, D>(a, s, hist_all, reinterpret_cast<uint32_t *>(stage) + 512 * wave, i0 + wave, thr, lane,
                               word, count, nullptr, nullptr, -1.f);
         } else {
-            sip_cut<NE>(a, s, (int64_t)bh * a.nB + i0 + wave, lane, word, count, sigma, tcap);
+            sip_cut<NE>(a, s, (int64_t)bh * a.nB + i0 + wave, lane,
+                        reinterpret_cast<uint64_t *>(hist_all + wave * 256), word, count, sigma, tcap);
         }
     }
     if (lane == 0) wave_count[wave] = count;
