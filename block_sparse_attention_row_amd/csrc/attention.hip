@@ -100,17 +100,6 @@ __device__ __forceinline__ float tile_commit(const f32x16 *acc_s, float c, float
     return lt;
 }
 
-// Bit e of m (e < 16) set -> nibble e of the result all ones: the 4 keys of entry e
-// of a gathered tile.
-__device__ __forceinline__ uint64_t spread_nibbles(uint32_t m) {
-    uint64_t x = m & 0xffffu;
-    x = (x | (x << 24)) & 0x000000ff000000ffull;
-    x = (x | (x << 12)) & 0x000f000f000f000full;
-    x = (x | (x << 6)) & 0x0303030303030303ull;
-    x = (x | (x << 3)) & 0x1111111111111111ull;
-    return x * 0xfull;
-}
-
 // LDS writes of some lanes made visible to the other lanes of the wave.
 __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -467,7 +456,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         int cols;         // lane e holds entry e's block (padded with the last one)
         bool mine;        // this wave's row keeps some entry of the unit
         int n;            // entries in the unit (0 past the end)
-        uint64_t km;      // keys of this wave's entries
+        uint32_t em;      // this wave's entries (bit e: entry e)
     };
     struct RowBuf {
         int buf;          // lane l: the l-th next counted entry, kNone past cnt
@@ -554,7 +543,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         u.cols = lane < u.n ? col : lastc;
         const uint32_t my = (uint32_t)__ballot(lane < 16 && (fl & (grp ? 2 : 1)));
         u.mine = my != 0;
-        u.km = spread_nibbles(my);
+        u.em = my;
         // both rows move past the unit's last entry
         const int tA = __popcll(__ballot(isA && x != kNone && u.n && x <= lastc));
         const int tB = __popcll(__ballot(isB && x != kNone && u.n && x <= lastc));
@@ -585,7 +574,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     };
     auto live = [&](const Unit &u) { return u.n != 0; };
     auto mask_u = [&](f32x16 *sc, const Unit &u) {
-        if (u.km != ~0ull) mask_keys(sc, u.km, hh);
+        if (u.em != 0xffffu) mask_entries(sc, u.em);
     };
 
     // units j (scores pending), j+1 (K resident), j+2 (lookahead)

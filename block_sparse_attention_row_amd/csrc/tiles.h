@@ -163,4 +163,22 @@ __device__ __forceinline__ void mask_keys(f32x16 *sc, uint64_t km, int hh) {
         }
 }
 
+// The same for a tile gathered from 4-token entries (entry e = keys 4e .. 4e + 3): em,
+// wave-uniform, has bit e set for the entries kept.  Accumulator v of half kt holds key
+// 32 kt + 8 (v / 4) + 4 hh + v % 4, i.e. entry 2 g + hh with g = 4 kt + v / 4, so the
+// four accumulators of one g share one lane mask (entry 2 g in lanes 0-31, entry 2 g + 1
+// in lanes 32-63): eight masks for the tile's 32 selects.
+__device__ __forceinline__ void mask_entries(f32x16 *sc, uint32_t em) {
+    em = (uint32_t)__builtin_amdgcn_readfirstlane((int)em);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+        const uint64_t lanes = (((em >> (2 * g)) & 1u) ? 0x00000000ffffffffull : 0ull) |
+                               (((em >> (2 * g + 1)) & 1u) ? 0xffffffff00000000ull : 0ull);
+        const bool keep = __builtin_amdgcn_inverse_ballot_w64(lanes);
+#pragma unroll
+        for (int v = 4 * (g & 3); v < 4 * (g & 3) + 4; ++v)
+            sc[g >> 2][v] = keep ? sc[g >> 2][v] : kMaskedScore;
+    }
+}
+
 }  // namespace sattn
