@@ -100,11 +100,11 @@ __device__ __forceinline__ float tile_commit(const f32x16 *acc_s, float c, float
     return lt;
 }
 
-// LDS writes of some lanes made visible to the other lanes of the wave.
-__device__ __forceinline__ void wave_lds_fence() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// One compare-exchange stage of a bitonic merge over lanes 0-31 (ascending): lane l
+// and lane l ^ J exchange through a swizzle, the lower lane keeps the smaller key.
+template <int J> __device__ __forceinline__ uint32_t merge_stage(uint32_t key, int lane) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_ds_swizzle((int)key, (J << 10) | 0x1f);
+    return (lane & J) ? max(key, o) : min(key, o);
 }
 
 // Inclusive prefix max over lanes 0 .. 31 of values >= -1 (lanes 32-63: unspecified),
@@ -446,12 +446,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     // valid entries in a VGPR (lane l: the l-th next one, kNone past them), topped up 32
     // raw entries at a time from a window loaded one top-up ahead; the skip rule of the
     // tile walk (an entry counts if it is in range and above every earlier counted
-    // entry) applies to a whole window at once through a prefix max.  A unit's entries
-    // are then placed by rank: candidate i of row A lands at position i + (row B's
-    // first 16 candidates below it), a candidate of row B likewise, and an entry both
-    // rows hold once (from A).  Unseen entries of either row are larger than every
-    // placed one, since each buffer holds at least 16 entries or the whole rest of its
-    // row.
+    // entry) applies to a whole window at once through a prefix max.  A unit is then
+    // the 16 smallest distinct entries of the two rows' first 16 candidates, merged
+    // across the lanes (a bitonic merge), an entry both rows hold taken once.  Unseen
+    // entries of either row are larger than every placed one, since each buffer holds
+    // at least 16 entries or the whole rest of its row.
+    // above every 4-token column (nK <= 16 * 4096); twice it plus one fits 32 bits
+    constexpr int kGatherSentinel = 0x3fffffff;
     struct Unit {
         int cols;         // lane e holds entry e's block (padded with the last one)
         bool mine;        // this wave's row keeps some entry of the unit
@@ -465,8 +466,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         int64_t next, end;
         int last;         // the last counted entry (the skip rule's running max)
     };
-    __shared__ int ubuf[4][32];           // per wave: unit columns [16], then flags [16]
-    int *ucol = ubuf[wave], *ufl = ubuf[wave] + 16;
     auto raw_window = [&](int64_t base, int64_t e) { return lane < 32 && base + lane < e ? cv[base + lane] : kNone; };
     auto topup = [&](RowBuf &r) {
         while (r.cnt <= 32 && r.next < r.end) {
@@ -503,40 +502,40 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         topup(RA);
         topup(RB);
         const int xa = RA.buf, xbv = RB.buf;
-        // this lane's candidate: lanes 0-15 row A's first 16, lanes 16-31 row B's
-        const int xbs = __builtin_amdgcn_ds_bpermute(((lane - 16) & 63) * 4, xbv);
+        // lanes 0-15 take row A's first 16 candidates, lanes 16-31 row B's
         const bool isA = lane < 16, isB = lane >= 16 && lane < 32;
-        const int x = isA ? xa : (isB ? xbs : kNone);
-        // in one pass over the other row's 16 candidates: how many lie below this lane's
-        // candidate, and whether one equals it (an entry both rows hold)
-        int below_other = 0;
-        bool dup = false;
-#pragma unroll 2
-        for (int q = 0; q < 16; ++q) {
-            const int other = isA ? __builtin_amdgcn_readlane(xbv, q) : __builtin_amdgcn_readlane(xa, q);
-            below_other += other < x ? 1 : 0;
-            dup |= x != kNone && other == x;
-        }
-        // an entry both rows hold is placed once, as row A's: row A's count drops the
-        // row-B copies of such entries below it (one for each row-A entry below it that
-        // row B holds too), row B's candidates held by A are not placed
-        const uint64_t dam = __ballot(isA && dup);
-        const int dup_below = __builtin_amdgcn_mbcnt_hi((uint32_t)(dam >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)dam, 0u));
-        const int rank = isA ? below_other - dup_below : below_other;
-        // row B's own candidates (not held by A) by their order among themselves
-        const uint64_t om = __ballot(isB && !dup);
-        const int bown = __builtin_amdgcn_mbcnt_hi((uint32_t)(om >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)om, 0u));
-        const int pos = isA ? lane + rank : bown + rank;
-        const bool take = x != kNone && pos < 16 && (isA || (isB && !dup));
-        if (lane < 16) ufl[lane] = 0;
-        wave_lds_fence();
-        if (take) {
-            ucol[pos] = x;
-            ufl[pos] = isA ? (dup ? 3 : 1) : 2;
-        }
-        wave_lds_fence();
-        const int col = lane < 16 ? ucol[lane] : 0;
-        const int fl = lane < 16 ? ufl[lane] : 0;
+        // the 32 candidates in merged order: row B's reversed behind row A's form one
+        // bitonic sequence over lanes 0-31, which five compare-exchange stages sort.  The
+        // keys are 2 x value + row (kNone as a value above every column), so that of an
+        // entry both rows hold, row A's copy comes first.
+        // (the lane exchanges are swizzles and wave shifts with immediate patterns, so
+        // that no per-lane address vector stays live across the walk)
+        const int xrev = __builtin_amdgcn_ds_swizzle(xbv, kSwizzleXor31);   // lane 16 + i: B[15 - i]
+        const int xv = isA ? xa : (isB ? xrev : kNone);
+        uint32_t key = ((uint32_t)min(xv, kGatherSentinel) << 1) | (isB ? 1u : 0u);
+        key = merge_stage<16>(key, lane);
+        key = merge_stage<8>(key, lane);
+        key = merge_stage<4>(key, lane);
+        key = merge_stage<2>(key, lane);
+        key = merge_stage<1>(key, lane);
+        const int val = (int)(key >> 1);
+        const bool fromB = key & 1u;
+        // an entry both rows hold: row A's copy is followed by row B's, which is dropped
+        const uint32_t kprev = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)key, kDppWaveShr1, 0xF, 0xF, false);
+        const uint32_t knext = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)key, kDppWaveShl1, 0xF, 0xF, false);
+        const bool dupB = fromB && lane > 0 && (kprev >> 1) == (uint32_t)val;
+        const bool dupA = !fromB && lane < 31 && (knext >> 1) == (uint32_t)val;
+        const bool keep = lane < 32 && val < kGatherSentinel && !dupB;
+        const uint64_t km = __ballot(keep);
+        const int nk = __popcll(km);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(km >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)km, 0u));
+        // the kept entries to lanes 0 .. nk-1 in order, the others to the remaining lanes
+        // (a permutation of the 64 lanes); lane e < 16 then holds entry e (value, row flags)
+        const int to = keep ? below : (nk + (lane - below)) & 63;
+        const int flag = fromB ? 2 : (dupA ? 3 : 1);
+        const int packed = __builtin_amdgcn_ds_permute(to * 4, val * 4 + flag);
+        const int col = lane < 16 && lane < nk ? packed >> 2 : 0;
+        const int fl = lane < 16 && lane < nk ? (packed & 3) : 0;
         const uint64_t present = __ballot(fl != 0);
         u.n = __popcll(present);
         const int lastc = u.n ? __builtin_amdgcn_readlane(col, u.n - 1) : 0;
@@ -545,8 +544,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         u.mine = my != 0;
         u.em = my;
         // both rows move past the unit's last entry
-        const int tA = __popcll(__ballot(isA && x != kNone && u.n && x <= lastc));
-        const int tB = __popcll(__ballot(isB && x != kNone && u.n && x <= lastc));
+        const int tA = __popcll(__ballot(lane < 16 && xa != kNone && u.n && xa <= lastc));
+        const int tB = __popcll(__ballot(lane < 16 && xbv != kNone && u.n && xbv <= lastc));
         consume(RA, tA);
         consume(RB, tB);
     };

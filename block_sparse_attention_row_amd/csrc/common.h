@@ -89,6 +89,10 @@ constexpr int kDppXor2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
 constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+constexpr int kDppWaveShl1 = 0x130;  // lane l takes lane l + 1 (whole wave)
+constexpr int kDppWaveShr1 = 0x138;  // lane l takes lane l - 1 (whole wave)
+// ds_swizzle bit mode within 32-lane groups (and 0x1f, or 0, xor 31): lane l takes 31 - l
+constexpr int kSwizzleXor31 = (31 << 10) | 0x1f;
 
 __device__ __forceinline__ float lane_value(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
