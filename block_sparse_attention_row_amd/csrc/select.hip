@@ -835,11 +835,12 @@ __device__ __forceinline__ void select_emit_body(const SelectArgs &a) {
             off += (uint32_t)__popcll(m);
         }
     } else {
-        // the register row is indexed by the word, so the loop runs at compile time
+        // the register row is indexed by the word, so the loop runs at compile time (a
+        // test rather than an exit keeps it unrolled, and the row in registers)
         float *const bdst = a.col_bias + pos_s;
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
-            if (e >= nvc) break;
+            if (e >= nvc) continue;
             const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)word, e);
             const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(word >> 32), e);
             const uint64_t m = ((uint64_t)hi << 32) | lo;
