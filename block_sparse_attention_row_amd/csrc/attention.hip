@@ -533,7 +533,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         // (a permutation of the 64 lanes); lane e < 16 then holds entry e (value, row flags)
         const int to = keep ? below : (nk + (lane - below)) & 63;
         const int flag = fromB ? 2 : (dupA ? 3 : 1);
-        const int packed = __builtin_amdgcn_ds_permute(to * 4, val * 4 + flag);
+        const int packed = __builtin_amdgcn_ds_permute(to * 4, (int)((uint32_t)val * 4u + (uint32_t)flag));
         const int col = lane < 16 && lane < nk ? packed >> 2 : 0;
         const int fl = lane < 16 && lane < nk ? (packed & 3) : 0;
         const uint64_t present = __ballot(fl != 0);
