@@ -937,6 +937,38 @@ def test_gather_forward_long_lists_and_last_round_pieces():
     assert err <= P.TOL["bf16"] and lerr <= P.LSE_TOL["bf16"]
 
 
+
+@pytest.mark.parametrize("layout", ["same", "interleaved"])
+def test_gather_units_of_shared_and_interleaved_rows(layout):
+    """Rows whose 4-token lists are identical for every query block (each entry of a pair's
+    walk held by both rows, so every position of a unit merges two copies), or split by
+    frame parity into even and odd key blocks (the two rows of a frame-neighbour pair then
+    alternate entry by entry): every query block against the oracle's attention."""
+    wl = small_workload("gather_" + layout, 1, 128, (4, 2, 3), "bf16", seed=96)
+    q, k, v, _ = make_inputs(wl, "A")
+    qd, kd, vd = P.to_device(q, k, v)
+    nB, nK = wl.blocks, 16 * wl.blocks
+    rng = np.random.default_rng(97)
+    base = rng.random(nK) < 0.6
+    keep = np.zeros((nB, nK), dtype=bool)
+    per_frame = nB // wl.block_grid[0]
+    for i in range(nB):
+        if layout == "same":
+            keep[i] = base
+        else:
+            keep[i, (i // per_frame) % 2::2] = True
+    orp, oci = oracle.csr_from_mask(keep)
+    shape = P.shape_for(wl)
+    out, lse = B.sparse_attn_forward_gather(shape, qd, kd, vd, torch.as_tensor(orp.astype(np.int32)).cuda(),
+                                            torch.as_tensor(oci).cuda(), want_lse=True)
+    torch.cuda.synchronize()
+    rows = np.arange(nB)
+    ref, ref_lse = oracle.attention_rows(q, k, v, orp, oci, rows, key_tokens=4)
+    err = float(np.abs(out.float().cpu().reshape(-1, 64, wl.head_dim).numpy() - ref).max())
+    lerr = float(np.abs(lse.cpu().reshape(-1, 64).numpy() - ref_lse).max())
+    print(f"gather {layout}: nnz {len(oci)}, max|err|={err:.3e} lse {lerr:.3e}", flush=True)
+    assert err <= P.TOL["bf16"] and lerr <= P.LSE_TOL["bf16"]
+
 FINE = [
     # name, heads, d, block grid (nB), thr, reading, per-head threshold range
     ("d128_A_nB24", 2, 128, (2, 3, 4), 0.8, "A", None),            # 1 word a lane
