@@ -595,12 +595,12 @@ __device__ __forceinline__ void select_emit_body(const SelectArgs &a) {
     static_assert(NE % 4 == 0 && NE <= 64, "NE: register row length in 64-key words");
     constexpr int KB = D / 32;                     // k-blocks of one 16x16x32 product
     constexpr int NCH = NE / 4;                    // score chunks
-    // registers for the next chunk's operands where they fit; at NE <= 8 two
-    // workgroups share a CU instead
+    // registers for the next chunk's operands where they fit (at NE <= 8 the chunks are
+    // few and the prefetch measured no faster)
     constexpr bool kPrefetch = NE > 8 && NE <= 32;
     // the CDF selection pools its queries in fp64 (exact means for the near-tie
-    // rescoring); rows of up to 512 blocks run at 64 VGPRs and keep 4 loads a lane in
-    // flight, longer rows (128 VGPRs, free while the scores do not exist yet) all 16
+    // rescoring); rows of up to 512 blocks keep 4 loads a lane in flight, longer rows
+    // (registers free while the scores do not exist yet) all 16
     using QP = BlockPool<T, D, MODE == 0 ? (NE <= 8 ? 4 : 16) : 8>;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     __bf16 *qf = reinterpret_cast<__bf16 *>(smem_raw);                              // [16][2D+8]
@@ -854,10 +854,11 @@ __device__ __forceinline__ void select_emit_body(const SelectArgs &a) {
     }
 }
 
-// Rows of up to 512 key blocks (NE <= 8) fit in 64 registers, and two workgroups then
-// share a CU (8 waves per SIMD); longer rows take the whole register budget of one.
+// One workgroup a CU (up to 128 VGPRs a wave).  Rows of up to 512 key blocks would fit
+// two workgroups a CU at 64 VGPRs, but the fp64 pooling then spills (88 B of scratch a
+// lane), and one unspilled workgroup a CU measured faster (480p: 84 -> 75 us).
 template <typename T, int D, int NE, int MODE>
-__global__ __launch_bounds__(1024, NE <= 8 ? 8 : 4) void select_emit_kernel(SelectArgs a) {
+__global__ __launch_bounds__(1024, 4) void select_emit_kernel(SelectArgs a) {
     select_emit_body<T, D, NE, MODE>(a);
 }
 
